@@ -1,0 +1,405 @@
+"""CPU oracle of the dropless top-k Mixture-of-Experts SwiGLU FFN layer.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the package's ``smoke()`` check and
+the ``cpu_baseline`` leg of the benchmark may import this module.  It shares
+no code with the HIP path and the HIP path never calls it.
+
+The layer computes, for every token x_n (a row of x [N, H]):
+
+    y_n = sum_k g_{n,k} * FFN_{e_{n,k}}(x_n)
+
+with router logits l = x.W_r (+ b), the K experts e_{n,0..K-1} of largest
+logit, renormalised gates g, and SwiGLU experts
+FFN_e(v) = (silu(v.W_gate[e]) * (v.W_up[e])).W_down[e].
+
+Sources (page titles; the text of each page is what is followed):
+  * "MoE computation principle and execution process: from Router scoring to
+    expert parallelism and load balancing" (icman.com.cn): section 2.1 (router
+    logits x.W_r with W_r [H, E]), 2.2 (softmax, top-K, renormalise the K
+    selected weights; gradient only through the continuous weights), 2.3
+    (SwiGLU expert silu(gate) * up then down projection; weighted sum over the
+    K selected experts), 2.4 (tiny example shapes and init).
+  * "MoE technical analysis: from theory to practice" (intelliparadigm.com):
+    section 2.1 (SwiGLU FeedForward without biases, silu on the w1 branch),
+    2.3 (top-k on the gate logits, softmax over the K values, per-expert loop
+    with an index_add_ combine).
+  * "MegaBlocks - architecture and principles" (ai-reference-codex): section
+    2.1 / 2.3 (dropless metadata: sort by expert, histogram, cumsum into bins;
+    gather, expert MLP, weighted scatter with a top-k sum), section 4 (sort
+    only on the expert-id key; gather and scatter are each other's backward).
+  * "MoK: high-performance Megakernel for deterministic training of large MoE
+    models" (jsqmd.com): section 3.1/3.3 (gating, top-k, index_add combine),
+    section 4.3 and 6.2 (deterministic top-k and sort, identical reruns).
+  * "MoonEP: how Moonshot AI solved the imbalance problem in MoE models"
+    (aikraft.ru): section 01 (the maxvio skew metric).
+
+Readings where the pages are silent or ambiguous (each also listed in the
+design notes of the repository):
+  * top-K is taken on the logits with the order (logit descending, expert id
+    ascending); slot k of a token is its rank in that order;
+  * gates are the softmax over the K selected logits, which equals the full
+    softmax renormalised over the K selected experts;
+  * sorting by expert is stable in the flat index f = n*K + k;
+  * no bias in the experts; the optional logit bias b [E] is a constant input
+    that changes both selection and gate values and gets no gradient;
+  * weights are stored for x.W: W_gate, W_up [E, H, F], W_down [E, F, H];
+  * unselected router logits get exactly zero gradient.
+
+Precision.  All arithmetic is float64.  ``store`` selects where values are
+rounded, to mirror the storage precision of a device implementation:
+  * "f64": no rounding (exact mode);
+  * "f32": every tensor that is stored between steps is rounded to float32;
+  * "bf16": every activation tensor stored between steps (xs, G, U, A, ys, y,
+    dys, dG, dU, dxs, dx) is rounded to bfloat16 with round-to-nearest-even;
+    gates, dgates and dlogits are rounded to float32; logits, the expert
+    partial sums and all weight gradients stay float64.
+
+Parity pins: see tests/test_oracle_pins.py (brute-force per-token
+evaluation, library routines for the metadata, closed-form special cases,
+central finite differences, and autograd of an independent dense-masked
+formulation).
+"""
+from __future__ import annotations
+
+import math
+from typing import Callable, Optional
+
+import numpy as np
+
+STORE_TYPES = ("f64", "f32", "bf16")
+
+
+# --------------------------------------------------------------------------
+# rounding helpers
+# --------------------------------------------------------------------------
+
+def as_f64(a) -> np.ndarray:
+    """Convert a torch tensor (any float dtype) or array to a float64 ndarray."""
+    if a is None:
+        return None
+    if hasattr(a, "detach"):
+        a = a.detach().to("cpu")
+        if str(a.dtype) in ("torch.bfloat16", "torch.float16"):
+            import torch
+            a = a.to(torch.float32)
+        a = a.numpy()
+    return np.asarray(a, dtype=np.float64)
+
+
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value (ties to even).
+
+    bfloat16 keeps the sign, the 8-bit exponent and the top 7 mantissa bits
+    of a float32; in float64 terms it keeps the top 7 of 52 mantissa bits,
+    so the low 45 bits are rounded away.
+    """
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    u = a.view(np.uint64)
+    keep_lsb = (u >> np.uint64(45)) & np.uint64(1)
+    r = (u + (np.uint64(1) << np.uint64(44)) - np.uint64(1) + keep_lsb) & ~((np.uint64(1) << np.uint64(45)) - np.uint64(1))
+    out = r.view(np.float64)
+    # values beyond the bfloat16 range become +-inf, as a float32 cast would
+    return out.astype(np.float32).astype(np.float64)
+
+
+def rho(a: np.ndarray, store: str) -> np.ndarray:
+    """Storage rounding of an activation tensor."""
+    if store == "f64":
+        return a
+    if store == "f32":
+        return a.astype(np.float32).astype(np.float64)
+    if store == "bf16":
+        return round_bf16(a)
+    raise ValueError(store)
+
+
+def rho32(a: np.ndarray, store: str) -> np.ndarray:
+    """Storage rounding of a tensor kept in float32 (gates and router grads)."""
+    if store == "f64":
+        return a
+    return a.astype(np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# router (icman 2.1, 2.2; intelliparadigm 2.3)
+# --------------------------------------------------------------------------
+
+def router_logits(x: np.ndarray, w_r: np.ndarray, bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """Router logits l = x.W_r (+ b): one score per (token, expert)."""
+    l = x @ w_r
+    if bias is not None:
+        l = l + bias[None, :]
+    return l
+
+
+def topk_experts(logits: np.ndarray, K: int) -> np.ndarray:
+    """The K experts of largest logit per token, ordered (logit desc, id asc).
+
+    A stable sort of the negated logits keeps equal logits in ascending
+    expert-id order, which is the tie-break.
+    """
+    order = np.argsort(-logits, axis=1, kind="stable")
+    return np.ascontiguousarray(order[:, :K]).astype(np.int32)
+
+
+def gates_topk_softmax(logits: np.ndarray, topk: np.ndarray) -> np.ndarray:
+    """Gates as the softmax over the K selected logits (intelliparadigm 2.3)."""
+    sel = np.take_along_axis(logits, topk.astype(np.int64), axis=1)
+    z = np.exp(sel - sel[:, :1])
+    return z / z.sum(axis=1, keepdims=True)
+
+
+def gates_renormalised_softmax(logits: np.ndarray, topk: np.ndarray) -> np.ndarray:
+    """Gates as the full softmax over E renormalised over the K selected (icman 2.2)."""
+    m = logits.max(axis=1, keepdims=True)
+    p = np.exp(logits - m)
+    p = p / p.sum(axis=1, keepdims=True)
+    sel = np.take_along_axis(p, topk.astype(np.int64), axis=1)
+    return sel / sel.sum(axis=1, keepdims=True)
+
+
+# --------------------------------------------------------------------------
+# dropless routing metadata (MegaBlocks 2.1 / 2.3, section 4)
+# --------------------------------------------------------------------------
+
+def routing_metadata(topk: np.ndarray, E: int):
+    """Histogram, cumsum bins and the stable sort of the flat assignment.
+
+    Returns (counts [E], offsets [E+1], sorted_flat [NK], inv [NK]) where
+    offsets is the exclusive cumsum of counts (offsets[1:] are the inclusive
+    bins), sorted_flat[i] is the flat index f = n*K + k of the i-th row of
+    the expert-grouped order (stable in f), and inv[f] is the row of f.
+    """
+    flat = topk.reshape(-1).astype(np.int64)
+    counts = np.bincount(flat, minlength=E).astype(np.int64)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    sorted_flat = np.argsort(flat, kind="stable").astype(np.int64)
+    inv = np.empty_like(sorted_flat)
+    inv[sorted_flat] = np.arange(sorted_flat.size, dtype=np.int64)
+    return counts, offsets, sorted_flat, inv
+
+
+def tile_list(counts: np.ndarray, offsets: np.ndarray, tile_m: int) -> np.ndarray:
+    """Row tiles of the grouped GEMM: (expert, first row, rows) per tile.
+
+    Experts ascending; each expert's rows [offsets[e], offsets[e+1]) are cut
+    into ceil(counts[e] / tile_m) tiles of tile_m rows, the last one ragged.
+    Padding exists only as tile granularity, never in memory.
+    """
+    tiles = []
+    for e in range(counts.size):
+        c = int(counts[e])
+        t = 0
+        while t * tile_m < c:
+            tiles.append((e, int(offsets[e]) + t * tile_m, min(tile_m, c - t * tile_m)))
+            t += 1
+    return np.asarray(tiles, dtype=np.int64).reshape(-1, 3)
+
+
+def maxvio(counts: np.ndarray, N: int, K: int, E: int) -> float:
+    """max_e(T_e / T_bar) - 1 with T_bar = N*K/E (MoonEP section 01)."""
+    tbar = N * K / E
+    return float(np.max(counts) / tbar - 1.0)
+
+
+# --------------------------------------------------------------------------
+# SwiGLU expert (icman 2.3; intelliparadigm 2.1)
+# --------------------------------------------------------------------------
+
+def silu(z: np.ndarray) -> np.ndarray:
+    return z / (1.0 + np.exp(-z))
+
+
+def sigmoid(z: np.ndarray) -> np.ndarray:
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def swiglu_expert(xs: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray, store: str):
+    """One expert on its rows: G = xs.Wg, U = xs.Wu, A = silu(G)*U, ys = A.Wd."""
+    G = rho(xs @ wg, store)
+    U = rho(xs @ wu, store)
+    A = rho(silu(G) * U, store)
+    ys = rho(A @ wd, store)
+    return G, U, A, ys
+
+
+# --------------------------------------------------------------------------
+# whole layer
+# --------------------------------------------------------------------------
+
+def forward(x, w_r, w_gate, w_up, w_down, K: int, bias=None, store: str = "bf16", tile_m: int = 128):
+    """Forward pass of the layer; returns every intermediate in a dict.
+
+    Steps in the pages' order: logits, top-K, gates, metadata (histogram,
+    cumsum, stable sort), gather, per-expert SwiGLU on the expert's rows,
+    gate-weighted index_add combine back to token order.
+    """
+    assert store in STORE_TYPES
+    x = as_f64(x)
+    w_r = as_f64(w_r)
+    bias = as_f64(bias)
+    wg_all, wu_all, wd_all = as_f64(w_gate), as_f64(w_up), as_f64(w_down)
+    N, H = x.shape
+    E = w_r.shape[1]
+    F = wg_all.shape[2]
+
+    logits = router_logits(x, w_r, bias)
+    topk = topk_experts(logits, K)
+    gates = rho32(gates_topk_softmax(logits, topk), store)
+    counts, offsets, sorted_flat, inv = routing_metadata(topk, E)
+    tiles = tile_list(counts, offsets, tile_m)
+
+    tok = sorted_flat // K
+    xs = x[tok]
+    NK = N * K
+    G = np.zeros((NK, F))
+    U = np.zeros((NK, F))
+    A = np.zeros((NK, F))
+    ys = np.zeros((NK, H))
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        G[r0:r1], U[r0:r1], A[r0:r1], ys[r0:r1] = swiglu_expert(xs[r0:r1], wg_all[e], wu_all[e], wd_all[e], store)
+
+    # index_add-style combine: each expert adds its gate-weighted rows into
+    # the tokens they came from
+    y = np.zeros((N, H))
+    gflat = gates.reshape(-1)
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        f = sorted_flat[r0:r1]
+        np.add.at(y, f // K, gflat[f][:, None] * ys[r0:r1])
+    y = rho(y, store)
+    return dict(x=x, w_r=w_r, bias=bias, w_gate=wg_all, w_up=wu_all, w_down=wd_all, K=K, store=store,
+                logits=logits, topk=topk, gates=gates, counts=counts, offsets=offsets,
+                sorted_flat=sorted_flat, inv=inv, tiles=tiles, xs=xs, G=G, U=U, A=A, ys=ys, y=y)
+
+
+def backward(fwd: dict, dy) -> dict:
+    """Backward pass given the forward intermediates and dL/dy.
+
+    combine backward (gather of dy weighted by the gate, and the gate
+    gradient as a dot product), expert backward with the SwiGLU derivative,
+    router backward through the softmax over the selected logits only, and
+    the gather backward (sum of the K rows of each token) plus the router's
+    input gradient.
+    """
+    store = fwd["store"]
+    K = fwd["K"]
+    dy = as_f64(dy)
+    x, w_r = fwd["x"], fwd["w_r"]
+    N, H = x.shape
+    E = w_r.shape[1]
+    F = fwd["w_gate"].shape[2]
+    NK = N * K
+    sorted_flat, inv, offsets = fwd["sorted_flat"], fwd["inv"], fwd["offsets"]
+    gates, topk = fwd["gates"], fwd["topk"]
+    gflat = gates.reshape(-1)
+    tok = sorted_flat // K
+
+    # combine backward
+    dys = rho(gflat[sorted_flat][:, None] * dy[tok], store)
+    ys_tok = fwd["ys"][inv.reshape(N, K)]                 # [N, K, H]
+    dgates = rho32(np.einsum("nh,nkh->nk", dy, ys_tok), store)
+
+    # expert backward
+    dG = np.zeros((NK, F))
+    dU = np.zeros((NK, F))
+    dxs = np.zeros((NK, H))
+    dw_gate = np.zeros_like(fwd["w_gate"])
+    dw_up = np.zeros_like(fwd["w_up"])
+    dw_down = np.zeros_like(fwd["w_down"])
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        G, U, A = fwd["G"][r0:r1], fwd["U"][r0:r1], fwd["A"][r0:r1]
+        xs = fwd["xs"][r0:r1]
+        d = dys[r0:r1]
+        dA = d @ fwd["w_down"][e].T
+        sg = sigmoid(G)
+        dG[r0:r1] = rho(dA * U * sg * (1.0 + G * (1.0 - sg)), store)
+        dU[r0:r1] = rho(dA * (G * sg), store)
+        dxs[r0:r1] = rho(dG[r0:r1] @ fwd["w_gate"][e].T + dU[r0:r1] @ fwd["w_up"][e].T, store)
+        dw_gate[e] = xs.T @ dG[r0:r1]
+        dw_up[e] = xs.T @ dU[r0:r1]
+        dw_down[e] = A.T @ d
+
+    # router backward: only the selected logits receive a gradient
+    s = np.sum(gates * dgates, axis=1, keepdims=True)
+    dsel = rho32(gates * (dgates - s), store)
+    dlogits = np.zeros((N, E))
+    np.put_along_axis(dlogits, topk.astype(np.int64), dsel, axis=1)
+
+    # gather backward (sum over each token's K rows) + router input gradient
+    dx = dxs[inv.reshape(N, K)].sum(axis=1) + dlogits @ w_r.T
+    dx = rho(dx, store)
+    dw_r = x.T @ dlogits
+    return dict(dys=dys, dgates=dgates, dG=dG, dU=dU, dxs=dxs, dlogits=dlogits, dx=dx, dw_r=dw_r,
+                dw_gate=dw_gate, dw_up=dw_up, dw_down=dw_down)
+
+
+# --------------------------------------------------------------------------
+# one token at a time (for sampled checks at sizes where the whole layer is
+# too slow on the CPU)
+# --------------------------------------------------------------------------
+
+ExpertFn = Callable[[int], tuple]
+
+
+def token_forward(xn, w_r, bias, expert_weights: ExpertFn, K: int, store: str = "bf16") -> dict:
+    """Forward of one token: its K experts, gates, expert rows and output.
+
+    ``expert_weights(e)`` returns (W_gate[e], W_up[e], W_down[e]).
+    """
+    xn = as_f64(xn).reshape(1, -1)
+    l = router_logits(xn, as_f64(w_r), as_f64(bias))
+    top = topk_experts(l, K)
+    g = rho32(gates_topk_softmax(l, top), store)[0]
+    rows = []
+    y = np.zeros(xn.shape[1])
+    for k in range(K):
+        wg, wu, wd = (as_f64(w) for w in expert_weights(int(top[0, k])))
+        G, U, A, ys = swiglu_expert(xn, wg, wu, wd, store)
+        rows.append(dict(G=G[0], U=U[0], A=A[0], ys=ys[0]))
+        y = y + g[k] * ys[0]
+    return dict(logits=l[0], topk=top[0], gates=g, rows=rows, y=rho(y, store))
+
+
+def token_backward(tf: dict, dyn, w_r, expert_weights: ExpertFn, store: str = "bf16") -> dict:
+    """Backward of one token given its token_forward result and dL/dy_n.
+
+    Every quantity here depends on the token alone: dys, dgates, the expert
+    row gradients dG, dU, dxs, the router gradient and dx_n.
+    """
+    dyn = as_f64(dyn).reshape(-1)
+    w_r = as_f64(w_r)
+    K = tf["topk"].size
+    g = tf["gates"]
+    dg = np.zeros(K)
+    dxs_sum = np.zeros_like(dyn)
+    out_rows = []
+    for k in range(K):
+        r = tf["rows"][k]
+        dg[k] = float(dyn @ r["ys"])
+        wg, wu, wd = (as_f64(w) for w in expert_weights(int(tf["topk"][k])))
+        dys = rho(g[k] * dyn, store)
+        dA = dys @ wd.T
+        G, U = r["G"], r["U"]
+        sg = sigmoid(G)
+        dG = rho(dA * U * sg * (1.0 + G * (1.0 - sg)), store)
+        dU = rho(dA * (G * sg), store)
+        dxs = rho(dG @ wg.T + dU @ wu.T, store)
+        dxs_sum = dxs_sum + dxs
+        out_rows.append(dict(dys=dys, dG=dG, dU=dU, dxs=dxs))
+    dg = rho32(dg, store)
+    s = float(np.sum(g * dg))
+    dsel = rho32(g * (dg - s), store)
+    dl = np.zeros(w_r.shape[1])
+    dl[tf["topk"].astype(np.int64)] = dsel
+    dx = rho(dxs_sum + w_r @ dl, store)
+    return dict(dgates=dg, dlogits=dl, rows=out_rows, dx=dx)
