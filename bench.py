@@ -1,0 +1,239 @@
+"""Benchmark of the dropless top-k MoE layer (forward + backward) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c1]
+
+A step is one pass of the whole layer over one batch of synthetic input:
+route, routing metadata, gather, gate/up and down grouped GEMMs, combine,
+and (for configurations with a backward) the combine, router, expert and
+gather backward passes.  Inputs are resident in HBM before the timed
+region; W untimed warm-up steps run first, then exactly K timed steps
+bracketed by torch.cuda.synchronize().
+
+Prints one JSON line: throughput in tokens/s (value), the per-stage
+breakdown from an untimed event-instrumented pass, the grouped-GEMM rate as
+a fraction of the bf16 MFMA peak, a roofline entry for the dominant kernel
+(its duration measured with HIP events on the launch stream during the timed
+steps), and the CPU oracle timed on the host as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+# profiles/ summaries of the dominant kernel's HBM counters: (FETCH_SIZE,
+# WRITE_SIZE) KiB per dispatch, already scaled by the copy-kernel factor;
+# filled from rocprofv3 --pmc runs of this same benchmark (None until taken).
+TRAFFIC_BYTES = {}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", default="c1")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--seed", type=int, default=0)
+    return p.parse_args()
+
+
+def stage_flops(cfg):
+    hf = cfg.H * cfg.F * cfg.NK
+    return {"gate_up": 4 * hf, "down": 2 * hf, "dact": 2 * hf, "dx": 4 * hf, "dw": 6 * hf}
+
+
+def stage_bytes(cfg):
+    """Algorithmic HBM bytes of the row-movement and metadata stages."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    N, NK, H, E, K = cfg.N, cfg.NK, cfg.H, cfg.E, cfg.K
+    return {
+        "route": N * H * e + H * E * e + N * K * 8,
+        "meta": NK * 4 * 3 + NK * 8 + (2 * E + 1) * 4,
+        "permute": (N + NK) * H * e + NK * 4,           # read each token once (cached), write NK rows
+        "combine": (NK + N) * H * e + NK * 8,
+        "combine_bwd": (N + 2 * NK) * H * e + NK * 12,
+        "permute_bwd": (NK + N) * H * e + NK * 8 + N * K * 4,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this layer runs on one GPU; --gpus {args.gpus} is not supported "
+              "(no sharding or collectives are built)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from mixture_experts_layer_sort_amd import _lib as L
+    from mixture_experts_layer_sort_amd.layer import MoELayerRunner
+    from moe_workloads import get_config, make_inputs
+
+    cfg = get_config(args.config)
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    big = cfg.E * cfg.H * cfg.F * 3 * 2 > 8 * 2 ** 30
+    if big:
+        # generate the weights expert by expert on the device (same recipe and
+        # seeds, device generator): the host copy would be tens of GB
+        inp = make_inputs(cfg, args.seed, device=dev, with_dy=cfg.backward)
+    else:
+        cpu = make_inputs(cfg, args.seed, with_dy=cfg.backward)
+        inp = {k: (None if v is None else v.to(dev)) for k, v in cpu.items()}
+    torch.cuda.synchronize()
+    r = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, dev, backward=cfg.backward)
+    d = r.d
+    x, w_r, wg, wu, wd, bias, dy = (inp[k] for k in ("x", "w_r", "w_gate", "w_up", "w_down", "bias", "dy"))
+    stream = torch.cuda.current_stream()
+
+    def stages():
+        yield "route", lambda: L.moe_route(d, x, w_r, bias, r.topk, r.gates, stream)
+        yield "meta", lambda: L.moe_permute_meta(d, r.topk, r.sorted_flat, r.inv, r.counts, r.offsets, r.tiles,
+                                                 r.num_tiles, r.meta_ws, stream)
+        yield "permute", lambda: L.moe_permute(d, x, r.sorted_flat, r.xs, stream)
+        yield "gate_up", lambda: L.moe_ffn_gate_up(d, r.xs, wg, wu, r.tiles, r.num_tiles, r.g, r.u, r.act, stream)
+        yield "down", lambda: L.moe_ffn_down(d, r.act, wd, r.tiles, r.num_tiles, r.ys, stream)
+        yield "combine", lambda: L.moe_combine(d, r.ys, r.gates, r.inv, r.y, stream)
+        if cfg.backward:
+            yield "combine_bwd", lambda: L.moe_combine_bwd(d, dy, r.ys, r.gates, r.inv, r.dys, r.dgates, stream)
+            yield "route_bwd", lambda: L.moe_route_bwd(d, x, r.topk, r.gates, r.dgates, r.dlogits, r.dw_r,
+                                                       r.route_ws, stream)
+            yield "dact", lambda: L.moe_ffn_bwd_dact(d, r.dys, wd, r.g, r.u, r.tiles, r.num_tiles, r.dg, r.du, stream)
+            yield "dx", lambda: L.moe_ffn_bwd_dx(d, r.dg, r.du, wg, wu, r.tiles, r.num_tiles, r.dxs, stream)
+            yield "dw", lambda: L.moe_ffn_bwd_dw(d, r.xs, r.act, r.dys, r.dg, r.du, r.offsets, r.dw_gate, r.dw_up,
+                                                 r.dw_down, stream)
+            yield "permute_bwd", lambda: L.moe_permute_bwd(d, r.dxs, r.inv, r.topk, r.dlogits, w_r, r.dx, r.perm_ws,
+                                                           stream)
+
+    def step(ev=None, only=None):
+        for name, fn in stages():
+            if ev is not None and (only is None or name == only):
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn()
+                b.record(stream)
+                ev.setdefault(name, []).append((a, b))
+            else:
+                fn()
+
+    # warm-up (untimed)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # untimed per-stage breakdown
+    ev = {}
+    for _ in range(max(3, min(10, args.steps))):
+        step(ev)
+    torch.cuda.synchronize()
+    stage_ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
+    fl = stage_flops(cfg)
+    gemm_ms = sum(stage_ms[k] for k in fl if k in stage_ms)
+    gemm_flops = sum(v for k, v in fl.items() if k in stage_ms)
+    dominant = max(stage_ms, key=stage_ms.get)
+
+    # timed region: exactly K steps; events only around the dominant kernel
+    ev_dom = {}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(ev_dom, only=dominant)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    dom_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_dom[dominant]]))
+    tokens_per_s = cfg.N * args.steps / (t1 - t0)
+
+    if dominant in fl:
+        achieved = fl[dominant] / (dom_ms * 1e-3) / 1e12
+        roof = {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "algorithmic_flops_per_launch": fl[dominant], "launch_ms": round(dom_ms, 5)}
+    else:
+        byt = stage_bytes(cfg)[dominant]
+        achieved = byt / (dom_ms * 1e-3) / 1e9
+        roof = {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "algorithmic_bytes_per_launch": byt, "launch_ms": round(dom_ms, 5)}
+    roof["traffic"] = TRAFFIC_BYTES.get((cfg.name, dominant))
+
+    counts = r.counts.cpu().numpy().astype(np.float64)
+    tbar = cfg.NK / cfg.E
+    maxvio = float(counts.max() / tbar - 1.0)
+
+    hbm = {}
+    for k, b in stage_bytes(cfg).items():
+        if k in stage_ms and stage_ms[k] > 0:
+            hbm[k] = round(b / (stage_ms[k] * 1e-3) / 1e9, 1)
+
+    cpu_base = None
+    if not args.no_cpu_baseline and not big:
+        cpu_base = cpu_baseline(cfg, cpu)
+
+    out = {
+        "metric": "MoE layer tokens/sec fwd+bwd; grouped-GEMM % of bf16 MFMA peak",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.description, "N": cfg.N, "H": cfg.H, "F": cfg.F, "E": cfg.E, "K": cfg.K,
+                   "backward": cfg.backward, "parallelism": "single GPU", "maxvio": round(maxvio, 4),
+                   "empty_experts": int((counts == 0).sum())},
+        "grouped_gemm": {"tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 2),
+                         "frac_of_bf16_peak": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "ms": round(gemm_ms, 4), "algorithmic_flops": gemm_flops},
+        "stages_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "stages_hbm_gbs": hbm,
+        "roofline": roof,
+        "cpu_baseline": cpu_base,
+        "host": {"cpu": platform.processor() or platform.machine(), "cores": os.cpu_count()},
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(cfg, cpu):
+    """The oracle (as it stands) on the host: whole-layer passes over the
+    workload's first S tokens, repeated until about 10 s have passed."""
+    import torch
+
+    from oracle import moe_oracle as O
+    threads = torch.get_num_threads()
+    S = min(cfg.N, 16384)
+    x = cpu["x"][:S]
+    dy = cpu["dy"][:S] if cpu["dy"] is not None else None
+    store = "bf16" if cfg.dtype == "bf16" else "f32"
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        f = O.forward(x, cpu["w_r"], cpu["w_gate"], cpu["w_up"], cpu["w_down"], cfg.K, bias=cpu["bias"], store=store)
+        if dy is not None:
+            O.backward(f, dy)
+        passes += 1
+        if time.perf_counter() - t0 > 10.0 or passes >= 5:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(S * passes / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {S} tokens of the workload, {passes} whole-layer pass(es) "
+                      f"({'fwd+bwd' if dy is not None else 'fwd'}), float64 NumPy, {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,225 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) dropless top-k Mixture-of-Experts
+ * SwiGLU FFN layer, forward and backward, on one GPU.
+ *
+ * The layer (for a token x_n, a row of x [N, H]):
+ *     l_n   = x_n . W_r (+ b)                       router logits, W_r [H, E]
+ *     e_n,k = the K experts of largest logit, ordered (logit desc, id asc)
+ *     g_n,k = softmax over the K selected logits     renormalised gates
+ *     y_n   = sum_k g_n,k * FFN_{e_n,k}(x_n)
+ *     FFN_e(v) = (silu(v . W_gate[e]) * (v . W_up[e])) . W_down[e]
+ * Sources: "MoE computation principle and execution process: from Router
+ * scoring to expert parallelism and load balancing" (icman.com.cn) sections
+ * 2.1-2.3; "MoE technical analysis: from theory to practice"
+ * (intelliparadigm.com) sections 2.1 and 2.3; dropless routing metadata and
+ * the gather / grouped GEMM / weighted scatter structure from "MegaBlocks -
+ * architecture and principles" (ai-reference-codex) sections 2.1 and 2.3.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor argument is a caller-owned DEVICE pointer to a contiguous
+ *    row-major buffer with the shape stated below, aligned to 16 bytes.
+ *    The library never allocates, frees or keeps device memory between
+ *    calls; scratch memory comes only through (ws, ws_bytes), sized by
+ *    moe_workspace_bytes().
+ *  - "act" tensors (x, xs, G, U, A, ys, y, dy, dys, dG, dU, dxs, dx) and the
+ *    weights (W_r, W_gate, W_up, W_down) have the element type dims->dtype:
+ *    MOE_BF16 (bfloat16 storage, float32 accumulation, round-to-nearest-even
+ *    on every store) or MOE_F32.  gates, dgates, dlogits, the logit bias and
+ *    every weight gradient (dW_r, dW_gate, dW_up, dW_down) are float32.
+ *  - Index tensors are int32.
+ *  - All work is enqueued on `stream`; no call synchronises the stream or
+ *    copies device memory to the host (num_tiles stays on the device).
+ *  - Results are bitwise reproducible run to run: no floating-point atomics,
+ *    every reduction has a fixed order and every output element has one
+ *    owner.
+ *  - Return value: MOE_OK, or a negative moe_status.  Arguments are checked
+ *    on the host before anything is enqueued; on error nothing is enqueued.
+ *    MOE_EHIP reports a launch error from the HIP runtime.  Faults inside a
+ *    kernel surface at the caller's next synchronisation.
+ *  - N == 0 is valid: the call returns MOE_OK and enqueues nothing (weight
+ *    gradient outputs are then left untouched).
+ *  - Limits: 1 <= E <= 256, 1 <= K <= min(E, 8), H and F multiples of 128,
+ *    N*K < 2^31, N*E < 2^31.
+ */
+#ifndef MOE_MI355X_MOE_H_
+#define MOE_MI355X_MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+/* Rows per tile of the grouped-GEMM tile list built by moe_permute_meta. */
+#define MOE_TILE_M 128
+#define MOE_MAX_EXPERTS 256
+#define MOE_MAX_TOPK 8
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,       /* bad shape, null or misaligned pointer */
+  MOE_EUNSUPPORTED = -2, /* outside the limits above, or unknown dtype */
+  MOE_EWORKSPACE = -3,   /* workspace missing or smaller than required */
+  MOE_EHIP = -4          /* the HIP runtime reported a launch error */
+} moe_status;
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Entry points that take a workspace (argument of moe_workspace_bytes). */
+typedef enum moe_entry {
+  MOE_ENTRY_PERMUTE_META = 1,
+  MOE_ENTRY_ROUTE_BWD = 2,
+  MOE_ENTRY_PERMUTE_BWD = 3
+} moe_entry;
+
+/* Problem sizes: N tokens, hidden size H, expert FFN size F, E experts,
+ * K experts per token, dtype a moe_dtype.  NK = N*K routed rows. */
+typedef struct moe_dims {
+  int64_t N, H, F, E, K;
+  int32_t dtype;
+  int32_t reserved; /* must be 0 */
+} moe_dims;
+
+/* ABI version of the loaded library (MOE_ABI_VERSION it was built with). */
+int moe_abi_version(void);
+
+/* Static English text of a status code (never NULL). */
+const char* moe_status_str(int status);
+
+/* Capacity, in tiles, of the tile list: floor((NK + E*(MOE_TILE_M-1)) /
+ * MOE_TILE_M), an upper bound of sum_e ceil(count_e / MOE_TILE_M) for any
+ * routing.  The tiles buffer holds 3 int32 per tile.  Returns -1 on invalid
+ * dims. */
+int64_t moe_max_tiles(const moe_dims* d);
+
+/* Workspace bytes needed by `entry` (a moe_entry) for these dims; 0 if the
+ * entry needs none; (size_t)-1 on invalid dims or entry. */
+size_t moe_workspace_bytes(const moe_dims* d, int32_t entry);
+
+/* ---------------------------------------------------------------- forward */
+
+/* Router: logits l = x.W_r (+ logit_bias), top-K by (logit desc, expert id
+ * asc), gates = softmax over the K selected logits (icman sections 2.1 and
+ * 2.2; intelliparadigm section 2.3).  Logits are accumulated in float32 and
+ * not stored.
+ *   x [N,H] act; w_r [H,E] act; logit_bias [E] f32 or NULL (a constant that
+ *   changes selection and gate values);
+ *   topk_idx [N,K] int32 out (slot k = rank k); gates [N,K] f32 out. */
+int moe_route(const moe_dims* d, const void* x, const void* w_r, const float* logit_bias, int32_t* topk_idx,
+              float* gates, hipStream_t stream);
+
+/* Dropless routing metadata from the flat assignment f = n*K + k (MegaBlocks
+ * sections 2.1, 2.3 and 4: sort by expert id, histogram, cumsum into bins):
+ *   counts [E]      rows per expert (histogram);
+ *   offsets [E+1]   exclusive cumsum of counts, offsets[E] = NK;
+ *   sorted_flat [NK] flat indices grouped by expert, ascending f within an
+ *                   expert (a stable sort on the expert id);
+ *   inv [NK]        inv[f] = row of f in the grouped order;
+ *   tiles [3*moe_max_tiles] (expert, first row, rows) per MOE_TILE_M-row tile,
+ *                   experts ascending; only the first *num_tiles are written;
+ *   num_tiles [1]   number of tiles, on the device.
+ * topk_idx [N,K] int32 in, every value in [0,E).  ws: MOE_ENTRY_PERMUTE_META. */
+int moe_permute_meta(const moe_dims* d, const int32_t* topk_idx, int32_t* sorted_flat, int32_t* inv, int32_t* counts,
+                     int32_t* offsets, int32_t* tiles, int32_t* num_tiles, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/* Permuting gather: xs[i] = x[sorted_flat[i] / K]  (MegaBlocks section 2.1).
+ *   x [N,H] act in; sorted_flat [NK] in; xs [NK,H] act out. */
+int moe_permute(const moe_dims* d, const void* x, const int32_t* sorted_flat, void* xs, hipStream_t stream);
+
+/* Grouped SwiGLU experts over the tile list (icman section 2.3;
+ * intelliparadigm section 2.1), for every row i of expert e:
+ *   G[i] = xs[i].W_gate[e], U[i] = xs[i].W_up[e]    (stored rounded),
+ *   A[i] = silu(G[i]) * U[i]                         (from the rounded G, U),
+ *   ys[i] = A[i].W_down[e].
+ *   xs [NK,H]; w_gate, w_up [E,H,F]; w_down [E,F,H]; tiles/num_tiles from
+ *   moe_permute_meta; g_save, u_save [NK,F] out or both NULL (forward only);
+ *   act [NK,F] out (A, needed by the backward); ys [NK,H] out.
+ * Calls moe_ffn_gate_up then moe_ffn_down. */
+int moe_expert_ffn(const moe_dims* d, const void* xs, const void* w_gate, const void* w_up, const void* w_down,
+                   const int32_t* tiles, const int32_t* num_tiles, void* g_save, void* u_save, void* act, void* ys,
+                   hipStream_t stream);
+
+/* First grouped GEMM of moe_expert_ffn: G, U and A = silu(G)*U. */
+int moe_ffn_gate_up(const moe_dims* d, const void* xs, const void* w_gate, const void* w_up, const int32_t* tiles,
+                    const int32_t* num_tiles, void* g_save, void* u_save, void* act, hipStream_t stream);
+
+/* Second grouped GEMM of moe_expert_ffn: ys = A.W_down[e]. */
+int moe_ffn_down(const moe_dims* d, const void* act, const void* w_down, const int32_t* tiles,
+                 const int32_t* num_tiles, void* ys, hipStream_t stream);
+
+/* Gate-weighted combine back to token order (MegaBlocks section 2.1:
+ * weighted scatter with a sum over the top-k; icman section 2.3):
+ *   y[n] = sum_{k=0..K-1} gates[n,k] * ys[inv[n*K+k]], k ascending, float32
+ *   accumulation, one rounding.
+ *   ys [NK,H]; gates [N,K]; inv [NK]; y [N,H] out. */
+int moe_combine(const moe_dims* d, const void* ys, const float* gates, const int32_t* inv, void* y,
+                hipStream_t stream);
+
+/* --------------------------------------------------------------- backward */
+
+/* Backward of the combine (the backward of a weighted scatter is a weighted
+ * gather, MegaBlocks section 4):
+ *   dys[inv[n*K+k]] = gates[n,k] * dy[n];
+ *   dgates[n,k] = <dy[n], ys[inv[n*K+k]]> (float32, fixed reduction order).
+ *   dy [N,H]; ys [NK,H]; gates [N,K]; inv [NK]; dys [NK,H] out;
+ *   dgates [N,K] out. */
+int moe_combine_bwd(const moe_dims* d, const void* dy, const void* ys, const float* gates, const int32_t* inv,
+                    void* dys, float* dgates, hipStream_t stream);
+
+/* Router backward through the softmax over the selected logits only (icman
+ * section 2.2: the gradient flows through the continuous gate weights):
+ *   s_n = sum_k gates[n,k]*dgates[n,k];
+ *   dlogits[n,e_k] = gates[n,k]*(dgates[n,k] - s_n), 0 for unselected e;
+ *   dw_r = x^T . dlogits (fixed partition of the tokens, fixed-order sum).
+ *   x [N,H]; topk_idx, gates, dgates [N,K]; dlogits [N,E] f32 out;
+ *   dw_r [H,E] f32 out.  ws: MOE_ENTRY_ROUTE_BWD. */
+int moe_route_bwd(const moe_dims* d, const void* x, const int32_t* topk_idx, const float* gates,
+                  const float* dgates, float* dlogits, float* dw_r, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Backward of the grouped SwiGLU experts, for every row i of expert e:
+ *   dA = dys[i].W_down[e]^T; s = sigmoid(G[i]);
+ *   dG[i] = dA*U[i]*s*(1 + G[i]*(1-s)), dU[i] = dA*G[i]*s   (stored rounded);
+ *   dxs[i] = dG[i].W_gate[e]^T + dU[i].W_up[e]^T;
+ *   dW_gate[e] = xs_e^T.dG_e, dW_up[e] = xs_e^T.dU_e, dW_down[e] = A_e^T.dys_e
+ *   (float32, rows summed in ascending order inside each tile; experts with
+ *   no rows get exact zeros).
+ *   dys, xs [NK,H]; w_gate, w_up [E,H,F]; w_down [E,F,H]; g_save, u_save,
+ *   act [NK,F] from moe_expert_ffn; offsets, tiles, num_tiles from
+ *   moe_permute_meta; dg, du [NK,F] out; dxs [NK,H] out; dw_gate, dw_up
+ *   [E,H,F] f32 out; dw_down [E,F,H] f32 out.
+ * Calls moe_ffn_bwd_dact, moe_ffn_bwd_dx and moe_ffn_bwd_dw. */
+int moe_expert_ffn_bwd(const moe_dims* d, const void* dys, const void* xs, const void* w_gate, const void* w_up,
+                       const void* w_down, const void* g_save, const void* u_save, const void* act,
+                       const int32_t* offsets, const int32_t* tiles, const int32_t* num_tiles, void* dg, void* du,
+                       void* dxs, float* dw_gate, float* dw_up, float* dw_down, hipStream_t stream);
+
+/* dA = dys.W_down[e]^T with the SwiGLU derivative applied: writes dG, dU. */
+int moe_ffn_bwd_dact(const moe_dims* d, const void* dys, const void* w_down, const void* g_save, const void* u_save,
+                     const int32_t* tiles, const int32_t* num_tiles, void* dg, void* du, hipStream_t stream);
+
+/* dxs = dG.W_gate[e]^T + dU.W_up[e]^T. */
+int moe_ffn_bwd_dx(const moe_dims* d, const void* dg, const void* du, const void* w_gate, const void* w_up,
+                   const int32_t* tiles, const int32_t* num_tiles, void* dxs, hipStream_t stream);
+
+/* The three weight gradients, one owner per output tile. */
+int moe_ffn_bwd_dw(const moe_dims* d, const void* xs, const void* act, const void* dys, const void* dg,
+                   const void* du, const int32_t* offsets, float* dw_gate, float* dw_up, float* dw_down,
+                   hipStream_t stream);
+
+/* Backward of the gather plus the router's input gradient:
+ *   dx[n] = sum_k dxs[inv[n*K+k]] + sum_k dlogits[n,e_k] * W_r[:,e_k],
+ *   k ascending, float32 accumulation, one rounding.
+ *   dxs [NK,H]; inv [NK]; topk_idx [N,K]; dlogits [N,E] f32; w_r [H,E];
+ *   dx [N,H] out.  ws: MOE_ENTRY_PERMUTE_BWD (holds W_r transposed). */
+int moe_permute_bwd(const moe_dims* d, const void* dxs, const int32_t* inv, const int32_t* topk_idx,
+                    const float* dlogits, const void* w_r, void* dx, void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_MOE_H_ */

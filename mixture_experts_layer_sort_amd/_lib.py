@@ -1,0 +1,210 @@
+"""ctypes binding of the C ABI in include/moe.h (argument marshalling only).
+
+Each function here has the name of the C entry point it calls and takes
+torch tensors (device memory) instead of raw pointers; every step of the
+layer runs in the HIP library.  There is no fallback: if the library is not
+built or cannot be loaded, ``lib()`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libmoe_mi355x.so"
+LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
+MOE_F32, MOE_BF16 = 0, 1
+MOE_ENTRY_PERMUTE_META, MOE_ENTRY_ROUTE_BWD, MOE_ENTRY_PERMUTE_BWD = 1, 2, 3
+MOE_TILE_M = 128
+
+# Every exported symbol with (restype, argtypes); the tests check this list
+# against include/moe.h and against the built library.
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_SZ = ctypes.c_size_t
+
+
+class moe_dims(ctypes.Structure):
+    _fields_ = [("N", _I64), ("H", _I64), ("F", _I64), ("E", _I64), ("K", _I64), ("dtype", _I32), ("reserved", _I32)]
+
+
+_DP = ctypes.POINTER(moe_dims)
+
+SIGNATURES = {
+    "moe_abi_version": (ctypes.c_int, []),
+    "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_max_tiles": (_I64, [_DP]),
+    "moe_workspace_bytes": (_SZ, [_DP, _I32]),
+    "moe_route": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P]),
+    "moe_permute_meta": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_permute": (ctypes.c_int, [_DP, _P, _P, _P, _P]),
+    "moe_expert_ffn": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_ffn_gate_up": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_ffn_down": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P]),
+    "moe_combine": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P]),
+    "moe_combine_bwd": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_route_bwd": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_expert_ffn_bwd": (ctypes.c_int, [_DP] + [_P] * 17 + [_P]),
+    "moe_ffn_bwd_dact": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_ffn_bwd_dx": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_ffn_bwd_dw": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_permute_bwd": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+}
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = lib().moe_status_str(status).decode() if _LIB is not None else str(status)
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+def lib(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load (once) and return the HIP library; raises if it is not built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with mixture_experts_layer_sort_amd.build "
+                           "(there is no CPU fallback)")
+    h = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(h, name)
+        fn.restype = res
+        fn.argtypes = args
+    _LIB = h
+    return h
+
+
+def dims(N: int, H: int, F: int, E: int, K: int, dtype: int) -> moe_dims:
+    return moe_dims(N, H, F, E, K, dtype, 0)
+
+
+def dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return MOE_BF16
+    if t == torch.float32:
+        return MOE_F32
+    raise ValueError(f"unsupported dtype {t}")
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("tensor arguments must be device (cuda) tensors")
+    if not t.is_contiguous():
+        raise ValueError("tensor arguments must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _call(name: str, *args):
+    st = getattr(lib(), name)(*args)
+    if st != MOE_OK:
+        raise MoEError(name, st)
+
+
+def moe_abi_version() -> int:
+    return lib().moe_abi_version()
+
+
+def moe_status_str(status: int) -> str:
+    return lib().moe_status_str(status).decode()
+
+
+def moe_max_tiles(d: moe_dims) -> int:
+    return lib().moe_max_tiles(ctypes.byref(d))
+
+
+def moe_workspace_bytes(d: moe_dims, entry: int) -> int:
+    return lib().moe_workspace_bytes(ctypes.byref(d), entry)
+
+
+def moe_route(d, x, w_r, logit_bias, topk_idx, gates, stream=None):
+    _call("moe_route", ctypes.byref(d), _ptr(x), _ptr(w_r), _ptr(logit_bias), _ptr(topk_idx), _ptr(gates),
+          _stream(stream))
+
+
+def moe_permute_meta(d, topk_idx, sorted_flat, inv, counts, offsets, tiles, num_tiles, ws, stream=None):
+    _call("moe_permute_meta", ctypes.byref(d), _ptr(topk_idx), _ptr(sorted_flat), _ptr(inv), _ptr(counts),
+          _ptr(offsets), _ptr(tiles), _ptr(num_tiles), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+          _stream(stream))
+
+
+def moe_permute(d, x, sorted_flat, xs, stream=None):
+    _call("moe_permute", ctypes.byref(d), _ptr(x), _ptr(sorted_flat), _ptr(xs), _stream(stream))
+
+
+def moe_expert_ffn(d, xs, w_gate, w_up, w_down, tiles, num_tiles, g_save, u_save, act, ys, stream=None):
+    _call("moe_expert_ffn", ctypes.byref(d), _ptr(xs), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(tiles),
+          _ptr(num_tiles), _ptr(g_save), _ptr(u_save), _ptr(act), _ptr(ys), _stream(stream))
+
+
+def moe_ffn_gate_up(d, xs, w_gate, w_up, tiles, num_tiles, g_save, u_save, act, stream=None):
+    _call("moe_ffn_gate_up", ctypes.byref(d), _ptr(xs), _ptr(w_gate), _ptr(w_up), _ptr(tiles), _ptr(num_tiles),
+          _ptr(g_save), _ptr(u_save), _ptr(act), _stream(stream))
+
+
+def moe_ffn_down(d, act, w_down, tiles, num_tiles, ys, stream=None):
+    _call("moe_ffn_down", ctypes.byref(d), _ptr(act), _ptr(w_down), _ptr(tiles), _ptr(num_tiles), _ptr(ys),
+          _stream(stream))
+
+
+def moe_combine(d, ys, gates, inv, y, stream=None):
+    _call("moe_combine", ctypes.byref(d), _ptr(ys), _ptr(gates), _ptr(inv), _ptr(y), _stream(stream))
+
+
+def moe_combine_bwd(d, dy, ys, gates, inv, dys, dgates, stream=None):
+    _call("moe_combine_bwd", ctypes.byref(d), _ptr(dy), _ptr(ys), _ptr(gates), _ptr(inv), _ptr(dys), _ptr(dgates),
+          _stream(stream))
+
+
+def moe_route_bwd(d, x, topk_idx, gates, dgates, dlogits, dw_r, ws, stream=None):
+    _call("moe_route_bwd", ctypes.byref(d), _ptr(x), _ptr(topk_idx), _ptr(gates), _ptr(dgates), _ptr(dlogits),
+          _ptr(dw_r), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+
+
+def moe_expert_ffn_bwd(d, dys, xs, w_gate, w_up, w_down, g_save, u_save, act, offsets, tiles, num_tiles, dg, du,
+                       dxs, dw_gate, dw_up, dw_down, stream=None):
+    _call("moe_expert_ffn_bwd", ctypes.byref(d), _ptr(dys), _ptr(xs), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+          _ptr(g_save), _ptr(u_save), _ptr(act), _ptr(offsets), _ptr(tiles), _ptr(num_tiles), _ptr(dg), _ptr(du),
+          _ptr(dxs), _ptr(dw_gate), _ptr(dw_up), _ptr(dw_down), _stream(stream))
+
+
+def moe_ffn_bwd_dact(d, dys, w_down, g_save, u_save, tiles, num_tiles, dg, du, stream=None):
+    _call("moe_ffn_bwd_dact", ctypes.byref(d), _ptr(dys), _ptr(w_down), _ptr(g_save), _ptr(u_save), _ptr(tiles),
+          _ptr(num_tiles), _ptr(dg), _ptr(du), _stream(stream))
+
+
+def moe_ffn_bwd_dx(d, dg, du, w_gate, w_up, tiles, num_tiles, dxs, stream=None):
+    _call("moe_ffn_bwd_dx", ctypes.byref(d), _ptr(dg), _ptr(du), _ptr(w_gate), _ptr(w_up), _ptr(tiles),
+          _ptr(num_tiles), _ptr(dxs), _stream(stream))
+
+
+def moe_ffn_bwd_dw(d, xs, act, dys, dg, du, offsets, dw_gate, dw_up, dw_down, stream=None):
+    _call("moe_ffn_bwd_dw", ctypes.byref(d), _ptr(xs), _ptr(act), _ptr(dys), _ptr(dg), _ptr(du), _ptr(offsets),
+          _ptr(dw_gate), _ptr(dw_up), _ptr(dw_down), _stream(stream))
+
+
+def moe_permute_bwd(d, dxs, inv, topk_idx, dlogits, w_r, dx, ws, stream=None):
+    _call("moe_permute_bwd", ctypes.byref(d), _ptr(dxs), _ptr(inv), _ptr(topk_idx), _ptr(dlogits), _ptr(w_r),
+          _ptr(dx), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))

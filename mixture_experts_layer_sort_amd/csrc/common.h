@@ -1,0 +1,123 @@
+// Device helpers shared by the HIP kernels of the MoE layer (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+typedef uint16_t bf16_t;  // bfloat16 storage (upper half of a float32)
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) { return __uint_as_float(uint32_t(v) << 16); }
+
+// float32 -> bfloat16, round to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return bf16_t((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return bf16_t(u >> 16);
+}
+
+// Element-type traits: loads return float, stores round to the type.
+template <typename T> struct Elt;
+template <> struct Elt<float> {
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ float to_f32(float v) { return v; }
+  static __device__ __forceinline__ float from_f32(float v) { return v; }
+};
+template <> struct Elt<bf16_t> {
+  static __device__ __forceinline__ float load(const bf16_t* p) { return bf16_to_f32(*p); }
+  static __device__ __forceinline__ float to_f32(bf16_t v) { return bf16_to_f32(v); }
+  static __device__ __forceinline__ bf16_t from_f32(float v) { return f32_to_bf16(v); }
+};
+
+// 16-byte vector of elements of type T, converted to / from float.
+template <typename T> struct Vec16;
+template <> struct Vec16<float> {
+  static constexpr int n = 4;
+  static __device__ __forceinline__ void load(const float* p, float* out) {
+    float4 v = *reinterpret_cast<const float4*>(p);
+    out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+  }
+  static __device__ __forceinline__ void store(float* p, const float* in) {
+    *reinterpret_cast<float4*>(p) = make_float4(in[0], in[1], in[2], in[3]);
+  }
+};
+template <> struct Vec16<bf16_t> {
+  static constexpr int n = 8;
+  static __device__ __forceinline__ void load(const bf16_t* p, float* out) {
+    uint4 v = *reinterpret_cast<const uint4*>(p);
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ void store(bf16_t* p, const float* in) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = uint32_t(f32_to_bf16(in[2 * i])) | (uint32_t(f32_to_bf16(in[2 * i + 1])) << 16);
+    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+
+__device__ __forceinline__ float wave_sum(float v) {
+  // fixed butterfly order: bitwise reproducible
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+__device__ __forceinline__ float sigmoid_f32(float g) { return 1.0f / (1.0f + __expf(-g)); }
+
+}  // namespace moe
+
+// Host-side launch helpers (defined in the kernel sources).
+namespace moe_launch {
+struct Dims {
+  int64_t N, H, F, E, K;
+  int dtype;
+  int64_t NK() const { return N * K; }
+};
+int64_t max_tiles(const Dims& d);
+size_t route_bwd_chunks(const Dims& d);
+
+hipError_t route(const Dims& d, const void* x, const void* w_r, const float* bias, int32_t* topk, float* gates,
+                 hipStream_t s);
+hipError_t permute_meta(const Dims& d, const int32_t* topk, int32_t* sorted_flat, int32_t* inv, int32_t* counts,
+                        int32_t* offsets, int32_t* tiles, int32_t* num_tiles, void* ws, hipStream_t s);
+size_t permute_meta_ws(const Dims& d);
+hipError_t permute(const Dims& d, const void* x, const int32_t* sorted_flat, void* xs, hipStream_t s);
+hipError_t combine(const Dims& d, const void* ys, const float* gates, const int32_t* inv, void* y, hipStream_t s);
+hipError_t combine_bwd(const Dims& d, const void* dy, const void* ys, const float* gates, const int32_t* inv,
+                       void* dys, float* dgates, hipStream_t s);
+hipError_t route_bwd(const Dims& d, const void* x, const int32_t* topk, const float* gates, const float* dgates,
+                     float* dlogits, float* dw_r, void* ws, hipStream_t s);
+size_t route_bwd_ws(const Dims& d);
+hipError_t permute_bwd(const Dims& d, const void* dxs, const int32_t* inv, const int32_t* topk, const float* dlogits,
+                       const void* w_r, void* dx, void* ws, hipStream_t s);
+size_t permute_bwd_ws(const Dims& d);
+
+hipError_t ffn_gate_up(const Dims& d, const void* xs, const void* wg, const void* wu, const int32_t* tiles,
+                       const int32_t* num_tiles, void* g, void* u, void* a, hipStream_t s);
+hipError_t ffn_down(const Dims& d, const void* a, const void* wd, const int32_t* tiles, const int32_t* num_tiles,
+                    void* ys, hipStream_t s);
+hipError_t ffn_bwd_dact(const Dims& d, const void* dys, const void* wd, const void* g, const void* u,
+                        const int32_t* tiles, const int32_t* num_tiles, void* dg, void* du, hipStream_t s);
+hipError_t ffn_bwd_dx(const Dims& d, const void* dg, const void* du, const void* wg, const void* wu,
+                      const int32_t* tiles, const int32_t* num_tiles, void* dxs, hipStream_t s);
+hipError_t ffn_bwd_dw(const Dims& d, const void* xs, const void* a, const void* dys, const void* dg, const void* du,
+                      const int32_t* offsets, float* dwg, float* dwu, float* dwd, hipStream_t s);
+}  // namespace moe_launch

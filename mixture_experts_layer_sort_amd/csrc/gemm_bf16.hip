@@ -1,0 +1,446 @@
+// bf16 MFMA grouped GEMMs of the SwiGLU experts, forward and backward, for
+// CDNA4 (gfx950, v_mfma_f32_32x32x16_bf16, float32 accumulation).
+//
+// Every expert's rows form one group of a grouped GEMM (one launch covers
+// all experts; "MoE computation principle and execution process",
+// section 3.4, merges same-expert tokens into one large GEMM; the dropless
+// grouped GEMM without padding in memory is the grouped path of "MegaBlocks -
+// architecture and principles", sections 2.1 and 2.3).  The row groups are
+// read from the device-built tile list (expert, first row, rows), so no host
+// synchronisation is needed: the grid is sized for the largest possible tile
+// count and workgroups past the real count return at once.
+//
+// Workgroup tile 128 x 128, K step 64, 256 threads = 4 waves in a 2 x 2
+// arrangement, 64 x 64 per wave (2 x 2 MFMA 32x32x16 per 16-deep k step).
+// Operand tiles live in LDS as [128 rows][64 k] bf16 (128 B per row, eight
+// 16-byte chunks) with the chunk index XOR-swizzled by the row, so that both
+// the MFMA fragment reads (8 consecutive rows, same chunk) and the staging
+// writes are free of bank conflicts.  An operand whose K index is contiguous
+// in memory is copied in 16-byte vectors; an operand whose M or N index is
+// contiguous (the weights in the forward, both operands of the weight
+// gradients) is loaded as 4(k) x 8(mn) blocks and transposed in registers
+// before it is written to LDS.  The next K tile is prefetched into registers
+// while the current one is multiplied.
+//
+// Determinism: every output element has exactly one owning workgroup and its
+// K loop runs in ascending order.
+#include "common.h"
+
+namespace {
+using namespace moe;
+
+constexpr int BM = 128, BN = 128, BK = 64, NT = 256;
+constexpr int kTileBytes = BM * BK * 2;  // one operand tile in LDS
+
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return (row * 8 + (chunk ^ ((row ^ (row >> 3)) & 7))) * 16;
+}
+
+// 128 rows x 64 k of a row-major matrix whose k index is contiguous.
+struct LoadKC {
+  uint4 v[4];
+  __device__ __forceinline__ void load(const bf16_t* base, int64_t ld, int rows_valid) {
+    const int c = threadIdx.x & 7, r0 = threadIdx.x >> 3;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int r = r0 + 32 * i;
+      if (r < rows_valid)
+        v[i] = *reinterpret_cast<const uint4*>(base + (int64_t)r * ld + c * 8);
+      else
+        v[i] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void store(char* lds) const {
+    const int c = threadIdx.x & 7, r0 = threadIdx.x >> 3;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(lds + swz(r0 + 32 * i, c)) = v[i];
+  }
+};
+
+// 64 k-rows x 128 mn-columns of a row-major matrix whose mn index is
+// contiguous, stored to LDS transposed as [mn][k].
+struct LoadMN {
+  uint4 v[4];
+  __device__ __forceinline__ void load(const bf16_t* base, int64_t ld, int k_valid) {
+    const int mc = threadIdx.x & 15, kg = threadIdx.x >> 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int k = kg * 4 + j;
+      if (k < k_valid)
+        v[j] = *reinterpret_cast<const uint4*>(base + (int64_t)k * ld + mc * 8);
+      else
+        v[j] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void store(char* lds) const {
+    const int mc = threadIdx.x & 15, kg = threadIdx.x >> 4;
+    uint32_t w[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w[j][0] = v[j].x; w[j][1] = v[j].y; w[j][2] = v[j].z; w[j][3] = v[j].w;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int q = i >> 1;
+      uint32_t lo, hi;
+      if ((i & 1) == 0) {
+        lo = (w[0][q] & 0xffffu) | (w[1][q] << 16);
+        hi = (w[2][q] & 0xffffu) | (w[3][q] << 16);
+      } else {
+        lo = (w[0][q] >> 16) | (w[1][q] & 0xffff0000u);
+        hi = (w[2][q] >> 16) | (w[3][q] & 0xffff0000u);
+      }
+      const int row = mc * 8 + i;
+      *reinterpret_cast<uint2*>(lds + swz(row, kg >> 1) + (kg & 1) * 8) = make_uint2(lo, hi);
+    }
+  }
+};
+
+// One 64-deep K step of the 64 x 64 wave tile: acc[mi][ni] += A . B^T.
+__device__ __forceinline__ void mma_tile(const char* ldsA, const char* ldsB, f32x16_t (&acc)[2][2], int wm, int wn) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int kk = 0; kk < BK / 16; ++kk) {
+    const int chunk = kk * 2 + (lane >> 5);
+    bf16x8_t a[2], b[2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+      a[mi] = *reinterpret_cast<const bf16x8_t*>(ldsA + swz(wm * 64 + mi * 32 + (lane & 31), chunk));
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+      b[ni] = *reinterpret_cast<const bf16x8_t*>(ldsB + swz(wn * 64 + ni * 32 + (lane & 31), chunk));
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[2][2]) {
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+}
+
+// Output coordinates of accumulator element r of fragment (mi, ni) in the
+// workgroup tile: MFMA 32x32 result layout (column = lane % 32, rows in groups
+// of 4 interleaved across the two lane halves).
+__device__ __forceinline__ int acc_row(int wm, int mi, int r) {
+  return wm * 64 + mi * 32 + (r >> 2) * 8 + (lane_id() >> 5) * 4 + (r & 3);
+}
+__device__ __forceinline__ int acc_col(int wn, int ni) { return wn * 64 + ni * 32 + (lane_id() & 31); }
+
+struct TileInfo {
+  int e, row0, rows;
+};
+
+// ---------------------------------------------------------------- forward
+
+// G = xs.W_gate[e], U = xs.W_up[e] (both rounded to bf16), A = silu(G)*U.
+__global__ __launch_bounds__(NT, 1) void k_gate_up(const bf16_t* __restrict__ xs, const bf16_t* __restrict__ wg,
+                                                    const bf16_t* __restrict__ wu, const int32_t* __restrict__ tiles,
+                                                    const int32_t* __restrict__ num_tiles, bf16_t* __restrict__ g_out,
+                                                    bf16_t* __restrict__ u_out, bf16_t* __restrict__ a_out, int H,
+                                                    int F) {
+  __shared__ __attribute__((aligned(16))) char lds[3 * kTileBytes];
+  const int ntn = F / BN;
+  const int tile = blockIdx.x / ntn, nt = blockIdx.x % ntn;
+  if (tile >= *num_tiles) return;
+  const TileInfo ti{tiles[3 * tile], tiles[3 * tile + 1], tiles[3 * tile + 2]};
+  const int w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const bf16_t* a_base = xs + (int64_t)ti.row0 * H;
+  const bf16_t* g_base = wg + (int64_t)ti.e * H * F + nt * BN;
+  const bf16_t* u_base = wu + (int64_t)ti.e * H * F + nt * BN;
+
+  f32x16_t accg[2][2], accu[2][2];
+  zero_acc(accg);
+  zero_acc(accu);
+  LoadKC la;
+  LoadMN lg, lu;
+  const int nk = H / BK;
+  la.load(a_base, H, ti.rows);
+  lg.load(g_base, F, BK);
+  lu.load(u_base, F, BK);
+  for (int kt = 0; kt < nk; ++kt) {
+    la.store(lds);
+    lg.store(lds + kTileBytes);
+    lu.store(lds + 2 * kTileBytes);
+    __syncthreads();
+    if (kt + 1 < nk) {
+      la.load(a_base + (kt + 1) * BK, H, ti.rows);
+      lg.load(g_base + (int64_t)(kt + 1) * BK * F, F, BK);
+      lu.load(u_base + (int64_t)(kt + 1) * BK * F, F, BK);
+    }
+    mma_tile(lds, lds + kTileBytes, accg, wm, wn);
+    mma_tile(lds, lds + 2 * kTileBytes, accu, wm, wn);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = acc_row(wm, mi, r);
+        if (m < ti.rows) {
+          const int64_t o = (int64_t)(ti.row0 + m) * F + nt * BN + acc_col(wn, ni);
+          const bf16_t gb = f32_to_bf16(accg[mi][ni][r]);
+          const bf16_t ub = f32_to_bf16(accu[mi][ni][r]);
+          const float gf = bf16_to_f32(gb), uf = bf16_to_f32(ub);
+          if (g_out) g_out[o] = gb;
+          if (u_out) u_out[o] = ub;
+          a_out[o] = f32_to_bf16(silu_f32(gf) * uf);
+        }
+      }
+}
+
+// ys = A.W_down[e]
+__global__ __launch_bounds__(NT, 2) void k_down(const bf16_t* __restrict__ act, const bf16_t* __restrict__ wd,
+                                                 const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles,
+                                                 bf16_t* __restrict__ ys, int H, int F) {
+  __shared__ __attribute__((aligned(16))) char lds[2 * kTileBytes];
+  const int ntn = H / BN;
+  const int tile = blockIdx.x / ntn, nt = blockIdx.x % ntn;
+  if (tile >= *num_tiles) return;
+  const TileInfo ti{tiles[3 * tile], tiles[3 * tile + 1], tiles[3 * tile + 2]};
+  const int w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const bf16_t* a_base = act + (int64_t)ti.row0 * F;
+  const bf16_t* b_base = wd + (int64_t)ti.e * F * H + nt * BN;
+  f32x16_t acc[2][2];
+  zero_acc(acc);
+  LoadKC la;
+  LoadMN lb;
+  const int nk = F / BK;
+  la.load(a_base, F, ti.rows);
+  lb.load(b_base, H, BK);
+  for (int kt = 0; kt < nk; ++kt) {
+    la.store(lds);
+    lb.store(lds + kTileBytes);
+    __syncthreads();
+    if (kt + 1 < nk) {
+      la.load(a_base + (kt + 1) * BK, F, ti.rows);
+      lb.load(b_base + (int64_t)(kt + 1) * BK * H, H, BK);
+    }
+    mma_tile(lds, lds + kTileBytes, acc, wm, wn);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = acc_row(wm, mi, r);
+        if (m < ti.rows) ys[(int64_t)(ti.row0 + m) * H + nt * BN + acc_col(wn, ni)] = f32_to_bf16(acc[mi][ni][r]);
+      }
+}
+
+// --------------------------------------------------------------- backward
+
+// dA = dys.W_down[e]^T; dG = dA*U*s*(1+G*(1-s)), dU = dA*G*s with s = sigmoid(G).
+__global__ __launch_bounds__(NT, 2) void k_dact(const bf16_t* __restrict__ dys, const bf16_t* __restrict__ wd,
+                                                 const bf16_t* __restrict__ g_in, const bf16_t* __restrict__ u_in,
+                                                 const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles,
+                                                 bf16_t* __restrict__ dg, bf16_t* __restrict__ du, int H, int F) {
+  __shared__ __attribute__((aligned(16))) char lds[2 * kTileBytes];
+  const int ntn = F / BN;
+  const int tile = blockIdx.x / ntn, nt = blockIdx.x % ntn;
+  if (tile >= *num_tiles) return;
+  const TileInfo ti{tiles[3 * tile], tiles[3 * tile + 1], tiles[3 * tile + 2]};
+  const int w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const bf16_t* a_base = dys + (int64_t)ti.row0 * H;
+  // B[k = h][n = f] = W_down[e][f][h]: rows f of W_down[e] are k-contiguous
+  const bf16_t* b_base = wd + (int64_t)ti.e * F * H + (int64_t)nt * BN * H;
+  f32x16_t acc[2][2];
+  zero_acc(acc);
+  LoadKC la, lb;
+  const int nk = H / BK;
+  la.load(a_base, H, ti.rows);
+  lb.load(b_base, H, BN);
+  for (int kt = 0; kt < nk; ++kt) {
+    la.store(lds);
+    lb.store(lds + kTileBytes);
+    __syncthreads();
+    if (kt + 1 < nk) {
+      la.load(a_base + (kt + 1) * BK, H, ti.rows);
+      lb.load(b_base + (kt + 1) * BK, H, BN);
+    }
+    mma_tile(lds, lds + kTileBytes, acc, wm, wn);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = acc_row(wm, mi, r);
+        if (m < ti.rows) {
+          const int64_t o = (int64_t)(ti.row0 + m) * F + nt * BN + acc_col(wn, ni);
+          const float da = acc[mi][ni][r];
+          const float gv = bf16_to_f32(g_in[o]), uv = bf16_to_f32(u_in[o]);
+          const float s = sigmoid_f32(gv);
+          dg[o] = f32_to_bf16(da * uv * s * (1.f + gv * (1.f - s)));
+          du[o] = f32_to_bf16(da * gv * s);
+        }
+      }
+}
+
+// dxs = dG.W_gate[e]^T + dU.W_up[e]^T  (one K loop over 2F)
+__global__ __launch_bounds__(NT, 2) void k_dx(const bf16_t* __restrict__ dg, const bf16_t* __restrict__ du,
+                                               const bf16_t* __restrict__ wg, const bf16_t* __restrict__ wu,
+                                               const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles,
+                                               bf16_t* __restrict__ dxs, int H, int F) {
+  __shared__ __attribute__((aligned(16))) char lds[2 * kTileBytes];
+  const int ntn = H / BN;
+  const int tile = blockIdx.x / ntn, nt = blockIdx.x % ntn;
+  if (tile >= *num_tiles) return;
+  const TileInfo ti{tiles[3 * tile], tiles[3 * tile + 1], tiles[3 * tile + 2]};
+  const int w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  // B[k = f][n = h] = W[e][h][f]: rows h of W[e] are k-contiguous
+  const int64_t woff = (int64_t)ti.e * H * F + (int64_t)nt * BN * F;
+  f32x16_t acc[2][2];
+  zero_acc(acc);
+  LoadKC la, lb;
+  const int nkf = F / BK, nk = 2 * nkf;
+  auto load = [&](int kt) {
+    const bool second = kt >= nkf;
+    const int k0 = (second ? kt - nkf : kt) * BK;
+    la.load((second ? du : dg) + (int64_t)ti.row0 * F + k0, F, ti.rows);
+    lb.load((second ? wu : wg) + woff + k0, F, BN);
+  };
+  load(0);
+  for (int kt = 0; kt < nk; ++kt) {
+    la.store(lds);
+    lb.store(lds + kTileBytes);
+    __syncthreads();
+    if (kt + 1 < nk) load(kt + 1);
+    mma_tile(lds, lds + kTileBytes, acc, wm, wn);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = acc_row(wm, mi, r);
+        if (m < ti.rows) dxs[(int64_t)(ti.row0 + m) * H + nt * BN + acc_col(wn, ni)] = f32_to_bf16(acc[mi][ni][r]);
+      }
+}
+
+// Weight gradients, one workgroup per 128 x 128 output tile of one expert:
+//   problem 0: dW_gate[e] = xs_e^T . dG_e   [H, F]
+//   problem 1: dW_up[e]   = xs_e^T . dU_e   [H, F]
+//   problem 2: dW_down[e] = A_e^T  . dys_e  [F, H]
+// The contraction runs over the expert's rows in ascending 64-row steps.
+__global__ __launch_bounds__(NT, 2) void k_dw(const bf16_t* __restrict__ xs, const bf16_t* __restrict__ act,
+                                               const bf16_t* __restrict__ dys, const bf16_t* __restrict__ dg,
+                                               const bf16_t* __restrict__ du, const int32_t* __restrict__ offsets,
+                                               float* __restrict__ dwg, float* __restrict__ dwu,
+                                               float* __restrict__ dwd, int H, int F, int E) {
+  __shared__ __attribute__((aligned(16))) char lds[2 * kTileBytes];
+  const int tpe = (H / BM) * (F / BN);  // output tiles per expert and problem
+  const int prob = blockIdx.x / (E * tpe);
+  const int rem = blockIdx.x % (E * tpe);
+  const int e = rem / tpe, t = rem % tpe;
+  const bf16_t *L, *R;
+  float* out;
+  int P, Q, mt, nt;
+  if (prob < 2) {
+    P = H; Q = F;
+    L = xs; R = (prob == 0) ? dg : du;
+    out = ((prob == 0) ? dwg : dwu) + (int64_t)e * H * F;
+  } else {
+    P = F; Q = H;
+    L = act; R = dys;
+    out = dwd + (int64_t)e * F * H;
+  }
+  mt = t / (Q / BN);
+  nt = t % (Q / BN);
+  const int w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const int r0 = offsets[e], cnt = offsets[e + 1] - r0;
+  const bf16_t* l_base = L + (int64_t)r0 * P + mt * BM;
+  const bf16_t* r_base = R + (int64_t)r0 * Q + nt * BN;
+  f32x16_t acc[2][2];
+  zero_acc(acc);
+  LoadMN la, lb;
+  const int nk = (cnt + BK - 1) / BK;
+  if (nk > 0) {
+    la.load(l_base, P, cnt);
+    lb.load(r_base, Q, cnt);
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    la.store(lds);
+    lb.store(lds + kTileBytes);
+    __syncthreads();
+    if (kt + 1 < nk) {
+      const int kv = cnt - (kt + 1) * BK;
+      la.load(l_base + (int64_t)(kt + 1) * BK * P, P, kv);
+      lb.load(r_base + (int64_t)(kt + 1) * BK * Q, Q, kv);
+    }
+    mma_tile(lds, lds + kTileBytes, acc, wm, wn);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        out[(int64_t)(mt * BM + acc_row(wm, mi, r)) * Q + nt * BN + acc_col(wn, ni)] = acc[mi][ni][r];
+}
+
+}  // namespace
+
+namespace moe_launch {
+
+hipError_t ffn_gate_up_bf16(const Dims& d, const void* xs, const void* wg, const void* wu, const int32_t* tiles,
+                            const int32_t* num_tiles, void* g, void* u, void* a, hipStream_t s) {
+  unsigned grid = unsigned(max_tiles(d) * (d.F / BN));
+  hipLaunchKernelGGL(k_gate_up, dim3(grid), dim3(NT), 0, s, static_cast<const bf16_t*>(xs),
+                     static_cast<const bf16_t*>(wg), static_cast<const bf16_t*>(wu), tiles, num_tiles,
+                     static_cast<bf16_t*>(g), static_cast<bf16_t*>(u), static_cast<bf16_t*>(a), int(d.H), int(d.F));
+  return hipGetLastError();
+}
+
+hipError_t ffn_down_bf16(const Dims& d, const void* a, const void* wd, const int32_t* tiles, const int32_t* num_tiles,
+                         void* ys, hipStream_t s) {
+  unsigned grid = unsigned(max_tiles(d) * (d.H / BN));
+  hipLaunchKernelGGL(k_down, dim3(grid), dim3(NT), 0, s, static_cast<const bf16_t*>(a),
+                     static_cast<const bf16_t*>(wd), tiles, num_tiles, static_cast<bf16_t*>(ys), int(d.H), int(d.F));
+  return hipGetLastError();
+}
+
+hipError_t ffn_bwd_dact_bf16(const Dims& d, const void* dys, const void* wd, const void* g, const void* u,
+                             const int32_t* tiles, const int32_t* num_tiles, void* dg, void* du, hipStream_t s) {
+  unsigned grid = unsigned(max_tiles(d) * (d.F / BN));
+  hipLaunchKernelGGL(k_dact, dim3(grid), dim3(NT), 0, s, static_cast<const bf16_t*>(dys),
+                     static_cast<const bf16_t*>(wd), static_cast<const bf16_t*>(g), static_cast<const bf16_t*>(u),
+                     tiles, num_tiles, static_cast<bf16_t*>(dg), static_cast<bf16_t*>(du), int(d.H), int(d.F));
+  return hipGetLastError();
+}
+
+hipError_t ffn_bwd_dx_bf16(const Dims& d, const void* dg, const void* du, const void* wg, const void* wu,
+                           const int32_t* tiles, const int32_t* num_tiles, void* dxs, hipStream_t s) {
+  unsigned grid = unsigned(max_tiles(d) * (d.H / BN));
+  hipLaunchKernelGGL(k_dx, dim3(grid), dim3(NT), 0, s, static_cast<const bf16_t*>(dg), static_cast<const bf16_t*>(du),
+                     static_cast<const bf16_t*>(wg), static_cast<const bf16_t*>(wu), tiles, num_tiles,
+                     static_cast<bf16_t*>(dxs), int(d.H), int(d.F));
+  return hipGetLastError();
+}
+
+hipError_t ffn_bwd_dw_bf16(const Dims& d, const void* xs, const void* a, const void* dys, const void* dg,
+                           const void* du, const int32_t* offsets, float* dwg, float* dwu, float* dwd, hipStream_t s) {
+  unsigned grid = unsigned(3 * d.E * (d.H / BM) * (d.F / BN));
+  hipLaunchKernelGGL(k_dw, dim3(grid), dim3(NT), 0, s, static_cast<const bf16_t*>(xs), static_cast<const bf16_t*>(a),
+                     static_cast<const bf16_t*>(dys), static_cast<const bf16_t*>(dg), static_cast<const bf16_t*>(du),
+                     offsets, dwg, dwu, dwd, int(d.H), int(d.F), int(d.E));
+  return hipGetLastError();
+}
+
+}  // namespace moe_launch

@@ -1,0 +1,199 @@
+// float32 grouped GEMMs of the SwiGLU experts (the fp32 storage type), and
+// the dtype dispatch of the expert entry points.
+//
+// Same tile list, same tile-to-workgroup mapping and the same epilogue
+// arithmetic as the bf16 MFMA path, but plain float32 FMA on the vector ALUs
+// with one thread per output element and the contraction in ascending k.
+// This path exists for the fp32 storage type (small correctness-sized
+// problems); the bf16 path carries the performance.
+#include "common.h"
+
+namespace {
+using namespace moe;
+
+constexpr int TN = 128;  // output columns per workgroup
+
+__global__ __launch_bounds__(256) void k_gate_up_f32(const float* __restrict__ xs, const float* __restrict__ wg,
+                                                      const float* __restrict__ wu, const int32_t* __restrict__ tiles,
+                                                      const int32_t* __restrict__ num_tiles, float* __restrict__ g_out,
+                                                      float* __restrict__ u_out, float* __restrict__ a_out, int H,
+                                                      int F) {
+  const int ntn = F / TN;
+  const int tile = blockIdx.x / ntn, nt = blockIdx.x % ntn;
+  if (tile >= *num_tiles) return;
+  const int e = tiles[3 * tile], row0 = tiles[3 * tile + 1], rows = tiles[3 * tile + 2];
+  const float* Wg = wg + (int64_t)e * H * F;
+  const float* Wu = wu + (int64_t)e * H * F;
+  for (int idx = threadIdx.x; idx < rows * TN; idx += 256) {
+    const int m = idx / TN, n = nt * TN + idx % TN;
+    const float* a = xs + (int64_t)(row0 + m) * H;
+    float g = 0.f, u = 0.f;
+    for (int k = 0; k < H; ++k) {
+      g = fmaf(a[k], Wg[(int64_t)k * F + n], g);
+      u = fmaf(a[k], Wu[(int64_t)k * F + n], u);
+    }
+    const int64_t o = (int64_t)(row0 + m) * F + n;
+    if (g_out) g_out[o] = g;
+    if (u_out) u_out[o] = u;
+    a_out[o] = silu_f32(g) * u;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_down_f32(const float* __restrict__ act, const float* __restrict__ wd,
+                                                   const int32_t* __restrict__ tiles,
+                                                   const int32_t* __restrict__ num_tiles, float* __restrict__ ys, int H,
+                                                   int F) {
+  const int ntn = H / TN;
+  const int tile = blockIdx.x / ntn, nt = blockIdx.x % ntn;
+  if (tile >= *num_tiles) return;
+  const int e = tiles[3 * tile], row0 = tiles[3 * tile + 1], rows = tiles[3 * tile + 2];
+  const float* W = wd + (int64_t)e * F * H;
+  for (int idx = threadIdx.x; idx < rows * TN; idx += 256) {
+    const int m = idx / TN, n = nt * TN + idx % TN;
+    const float* a = act + (int64_t)(row0 + m) * F;
+    float s = 0.f;
+    for (int k = 0; k < F; ++k) s = fmaf(a[k], W[(int64_t)k * H + n], s);
+    ys[(int64_t)(row0 + m) * H + n] = s;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_dact_f32(const float* __restrict__ dys, const float* __restrict__ wd,
+                                                   const float* __restrict__ g_in, const float* __restrict__ u_in,
+                                                   const int32_t* __restrict__ tiles,
+                                                   const int32_t* __restrict__ num_tiles, float* __restrict__ dg,
+                                                   float* __restrict__ du, int H, int F) {
+  const int ntn = F / TN;
+  const int tile = blockIdx.x / ntn, nt = blockIdx.x % ntn;
+  if (tile >= *num_tiles) return;
+  const int e = tiles[3 * tile], row0 = tiles[3 * tile + 1], rows = tiles[3 * tile + 2];
+  const float* W = wd + (int64_t)e * F * H;
+  for (int idx = threadIdx.x; idx < rows * TN; idx += 256) {
+    const int m = idx / TN, n = nt * TN + idx % TN;
+    const float* a = dys + (int64_t)(row0 + m) * H;
+    float da = 0.f;
+    for (int k = 0; k < H; ++k) da = fmaf(a[k], W[(int64_t)n * H + k], da);
+    const int64_t o = (int64_t)(row0 + m) * F + n;
+    const float gv = g_in[o], uv = u_in[o];
+    const float s = sigmoid_f32(gv);
+    dg[o] = da * uv * s * (1.f + gv * (1.f - s));
+    du[o] = da * gv * s;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_dx_f32(const float* __restrict__ dg, const float* __restrict__ du,
+                                                 const float* __restrict__ wg, const float* __restrict__ wu,
+                                                 const int32_t* __restrict__ tiles,
+                                                 const int32_t* __restrict__ num_tiles, float* __restrict__ dxs, int H,
+                                                 int F) {
+  const int ntn = H / TN;
+  const int tile = blockIdx.x / ntn, nt = blockIdx.x % ntn;
+  if (tile >= *num_tiles) return;
+  const int e = tiles[3 * tile], row0 = tiles[3 * tile + 1], rows = tiles[3 * tile + 2];
+  const float* Wg = wg + (int64_t)e * H * F;
+  const float* Wu = wu + (int64_t)e * H * F;
+  for (int idx = threadIdx.x; idx < rows * TN; idx += 256) {
+    const int m = idx / TN, n = nt * TN + idx % TN;
+    const float* a = dg + (int64_t)(row0 + m) * F;
+    const float* b = du + (int64_t)(row0 + m) * F;
+    float s = 0.f;
+    for (int k = 0; k < F; ++k) s = fmaf(a[k], Wg[(int64_t)n * F + k], s);
+    for (int k = 0; k < F; ++k) s = fmaf(b[k], Wu[(int64_t)n * F + k], s);
+    dxs[(int64_t)(row0 + m) * H + n] = s;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_dw_f32(const float* __restrict__ xs, const float* __restrict__ act,
+                                                 const float* __restrict__ dys, const float* __restrict__ dg,
+                                                 const float* __restrict__ du, const int32_t* __restrict__ offsets,
+                                                 float* __restrict__ dwg, float* __restrict__ dwu,
+                                                 float* __restrict__ dwd, int H, int F, int E) {
+  const int tpe = (H / TN) * (F / TN);
+  const int prob = blockIdx.x / (E * tpe);
+  const int rem = blockIdx.x % (E * tpe);
+  const int e = rem / tpe, t = rem % tpe;
+  const float *L, *R;
+  float* out;
+  int P, Q;
+  if (prob < 2) {
+    P = H; Q = F;
+    L = xs; R = (prob == 0) ? dg : du;
+    out = ((prob == 0) ? dwg : dwu) + (int64_t)e * H * F;
+  } else {
+    P = F; Q = H;
+    L = act; R = dys;
+    out = dwd + (int64_t)e * F * H;
+  }
+  const int mt = t / (Q / TN), nt = t % (Q / TN);
+  const int r0 = offsets[e], r1 = offsets[e + 1];
+  for (int idx = threadIdx.x; idx < TN * TN; idx += 256) {
+    const int p = mt * TN + idx / TN, q = nt * TN + idx % TN;
+    float s = 0.f;
+    for (int r = r0; r < r1; ++r) s = fmaf(L[(int64_t)r * P + p], R[(int64_t)r * Q + q], s);
+    out[(int64_t)p * Q + q] = s;
+  }
+}
+
+}  // namespace
+
+namespace moe_launch {
+
+hipError_t ffn_gate_up_bf16(const Dims&, const void*, const void*, const void*, const int32_t*, const int32_t*, void*,
+                            void*, void*, hipStream_t);
+hipError_t ffn_down_bf16(const Dims&, const void*, const void*, const int32_t*, const int32_t*, void*, hipStream_t);
+hipError_t ffn_bwd_dact_bf16(const Dims&, const void*, const void*, const void*, const void*, const int32_t*,
+                             const int32_t*, void*, void*, hipStream_t);
+hipError_t ffn_bwd_dx_bf16(const Dims&, const void*, const void*, const void*, const void*, const int32_t*,
+                           const int32_t*, void*, hipStream_t);
+hipError_t ffn_bwd_dw_bf16(const Dims&, const void*, const void*, const void*, const void*, const void*,
+                           const int32_t*, float*, float*, float*, hipStream_t);
+
+hipError_t ffn_gate_up(const Dims& d, const void* xs, const void* wg, const void* wu, const int32_t* tiles,
+                       const int32_t* num_tiles, void* g, void* u, void* a, hipStream_t s) {
+  if (d.dtype == MOE_BF16) return ffn_gate_up_bf16(d, xs, wg, wu, tiles, num_tiles, g, u, a, s);
+  unsigned grid = unsigned(max_tiles(d) * (d.F / TN));
+  hipLaunchKernelGGL(k_gate_up_f32, dim3(grid), dim3(256), 0, s, static_cast<const float*>(xs),
+                     static_cast<const float*>(wg), static_cast<const float*>(wu), tiles, num_tiles,
+                     static_cast<float*>(g), static_cast<float*>(u), static_cast<float*>(a), int(d.H), int(d.F));
+  return hipGetLastError();
+}
+
+hipError_t ffn_down(const Dims& d, const void* a, const void* wd, const int32_t* tiles, const int32_t* num_tiles,
+                    void* ys, hipStream_t s) {
+  if (d.dtype == MOE_BF16) return ffn_down_bf16(d, a, wd, tiles, num_tiles, ys, s);
+  unsigned grid = unsigned(max_tiles(d) * (d.H / TN));
+  hipLaunchKernelGGL(k_down_f32, dim3(grid), dim3(256), 0, s, static_cast<const float*>(a),
+                     static_cast<const float*>(wd), tiles, num_tiles, static_cast<float*>(ys), int(d.H), int(d.F));
+  return hipGetLastError();
+}
+
+hipError_t ffn_bwd_dact(const Dims& d, const void* dys, const void* wd, const void* g, const void* u,
+                        const int32_t* tiles, const int32_t* num_tiles, void* dg, void* du, hipStream_t s) {
+  if (d.dtype == MOE_BF16) return ffn_bwd_dact_bf16(d, dys, wd, g, u, tiles, num_tiles, dg, du, s);
+  unsigned grid = unsigned(max_tiles(d) * (d.F / TN));
+  hipLaunchKernelGGL(k_dact_f32, dim3(grid), dim3(256), 0, s, static_cast<const float*>(dys),
+                     static_cast<const float*>(wd), static_cast<const float*>(g), static_cast<const float*>(u), tiles,
+                     num_tiles, static_cast<float*>(dg), static_cast<float*>(du), int(d.H), int(d.F));
+  return hipGetLastError();
+}
+
+hipError_t ffn_bwd_dx(const Dims& d, const void* dg, const void* du, const void* wg, const void* wu,
+                      const int32_t* tiles, const int32_t* num_tiles, void* dxs, hipStream_t s) {
+  if (d.dtype == MOE_BF16) return ffn_bwd_dx_bf16(d, dg, du, wg, wu, tiles, num_tiles, dxs, s);
+  unsigned grid = unsigned(max_tiles(d) * (d.H / TN));
+  hipLaunchKernelGGL(k_dx_f32, dim3(grid), dim3(256), 0, s, static_cast<const float*>(dg),
+                     static_cast<const float*>(du), static_cast<const float*>(wg), static_cast<const float*>(wu), tiles,
+                     num_tiles, static_cast<float*>(dxs), int(d.H), int(d.F));
+  return hipGetLastError();
+}
+
+hipError_t ffn_bwd_dw(const Dims& d, const void* xs, const void* a, const void* dys, const void* dg, const void* du,
+                      const int32_t* offsets, float* dwg, float* dwu, float* dwd, hipStream_t s) {
+  if (d.dtype == MOE_BF16) return ffn_bwd_dw_bf16(d, xs, a, dys, dg, du, offsets, dwg, dwu, dwd, s);
+  unsigned grid = unsigned(3 * d.E * (d.H / TN) * (d.F / TN));
+  hipLaunchKernelGGL(k_dw_f32, dim3(grid), dim3(256), 0, s, static_cast<const float*>(xs),
+                     static_cast<const float*>(a), static_cast<const float*>(dys), static_cast<const float*>(dg),
+                     static_cast<const float*>(du), offsets, dwg, dwu, dwd, int(d.H), int(d.F), int(d.E));
+  return hipGetLastError();
+}
+
+}  // namespace moe_launch

@@ -1,0 +1,239 @@
+// Row movement of the MoE layer: the permuting gather, the gate-weighted
+// combine, their backward passes, and the router's input-gradient term.
+//
+// "MegaBlocks - architecture and principles", section 2.1: tokens are
+// gathered into expert-grouped order before the expert MLP and scattered back
+// with a multiplication by the routing weight and a sum over the top-k after
+// it; section 4: the backward of the gather is an (unweighted) scatter and
+// vice versa.  Here every output row has exactly one owner: the combine and
+// the gather backward read the K rows of a token through inv[] (a gather-sum
+// in ascending k) instead of scattering with atomics, so results are bitwise
+// reproducible.  All rows move in 16-byte vectors; a row is H elements.
+#include "common.h"
+
+namespace {
+using namespace moe;
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_permute(const T* __restrict__ x, const int32_t* __restrict__ sorted_flat,
+                                                 T* __restrict__ xs, int64_t total_vec, int vpr, int K) {
+  constexpr int V = Vec16<T>::n;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < total_vec; v += stride) {
+    int64_t row = v / vpr;
+    int c = int(v - row * vpr);
+    int64_t tok = sorted_flat[row] / K;
+    const uint4* src = reinterpret_cast<const uint4*>(x + (tok * vpr + c) * V);
+    uint4* dst = reinterpret_cast<uint4*>(xs + v * V);
+    *dst = *src;
+  }
+}
+
+// y[n] = sum_k gates[n,k] * ys[inv[n*K+k]], k ascending, float32 accumulation.
+template <typename T>
+__global__ __launch_bounds__(256) void k_combine(const T* __restrict__ ys, const float* __restrict__ gates,
+                                                 const int32_t* __restrict__ inv, T* __restrict__ y,
+                                                 int64_t total_vec, int vpr, int K) {
+  constexpr int V = Vec16<T>::n;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < total_vec; v += stride) {
+    int64_t n = v / vpr;
+    int c = int(v - n * vpr);
+    float acc[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+    for (int k = 0; k < K; ++k) {
+      int64_t r = inv[n * K + k];
+      float g = gates[n * K + k];
+      float val[V];
+      Vec16<T>::load(ys + (r * vpr + c) * V, val);
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] = fmaf(g, val[i], acc[i]);
+    }
+    Vec16<T>::store(y + v * V, acc);
+  }
+}
+
+// One wave per token: dys[inv[n,k]] = g_k * dy[n]; dgates[n,k] = <dy[n], ys[inv[n,k]]>.
+template <typename T>
+__global__ __launch_bounds__(256) void k_combine_bwd(const T* __restrict__ dy, const T* __restrict__ ys,
+                                                     const float* __restrict__ gates, const int32_t* __restrict__ inv,
+                                                     T* __restrict__ dys, float* __restrict__ dgates, int N, int vpr,
+                                                     int K) {
+  constexpr int V = Vec16<T>::n;
+  const int lane = lane_id();
+  const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= N) return;
+  int64_t r[MOE_MAX_TOPK];
+  float g[MOE_MAX_TOPK], dot[MOE_MAX_TOPK];
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_TOPK; ++k) {
+    r[k] = (k < K) ? inv[n * K + k] : 0;
+    g[k] = (k < K) ? gates[n * K + k] : 0.f;
+    dot[k] = 0.f;
+  }
+  for (int c = lane; c < vpr; c += kWave) {
+    float d[V];
+    Vec16<T>::load(dy + (n * vpr + c) * V, d);
+#pragma unroll
+    for (int k = 0; k < MOE_MAX_TOPK; ++k) {
+      if (k < K) {
+        float yv[V], o[V];
+        Vec16<T>::load(ys + (r[k] * vpr + c) * V, yv);
+        float s = dot[k];
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          s = fmaf(d[i], yv[i], s);
+          o[i] = g[k] * d[i];
+        }
+        dot[k] = s;
+        Vec16<T>::store(dys + (r[k] * vpr + c) * V, o);
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_TOPK; ++k) {
+    if (k < K) {
+      float s = wave_sum(dot[k]);
+      if (lane == 0) dgates[n * K + k] = s;
+    }
+  }
+}
+
+// W_r [H, E] -> W_r^T [E, H] so the router term of dx reads whole rows.
+template <typename T>
+__global__ __launch_bounds__(256) void k_transpose_wr(const T* __restrict__ w_r, T* __restrict__ w_rt, int H, int E) {
+  int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)H * E) return;
+  int e = int(idx / H), h = int(idx % H);
+  w_rt[idx] = w_r[(int64_t)h * E + e];
+}
+
+// dx[n] = sum_k dxs[inv[n*K+k]] + sum_k dlogits[n, e_k] * W_r[:, e_k].
+template <typename T>
+__global__ __launch_bounds__(256) void k_permute_bwd(const T* __restrict__ dxs, const int32_t* __restrict__ inv,
+                                                     const int32_t* __restrict__ topk, const float* __restrict__ dl,
+                                                     const T* __restrict__ w_rt, T* __restrict__ dx, int64_t total_vec,
+                                                     int vpr, int K, int E) {
+  constexpr int V = Vec16<T>::n;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < total_vec; v += stride) {
+    int64_t n = v / vpr;
+    int c = int(v - n * vpr);
+    float acc[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+    for (int k = 0; k < K; ++k) {
+      int64_t r = inv[n * K + k];
+      float val[V];
+      Vec16<T>::load(dxs + (r * vpr + c) * V, val);
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] += val[i];
+    }
+    for (int k = 0; k < K; ++k) {
+      int64_t e = topk[n * K + k];
+      float d = dl[n * E + e];
+      float wv[V];
+      Vec16<T>::load(w_rt + (e * vpr + c) * V, wv);
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] = fmaf(d, wv[i], acc[i]);
+    }
+    Vec16<T>::store(dx + v * V, acc);
+  }
+}
+
+unsigned grid_for(int64_t total, int64_t cap = 8192) {
+  int64_t b = (total + 255) / 256;
+  if (b > cap) b = cap;
+  if (b < 1) b = 1;
+  return unsigned(b);
+}
+
+template <typename T>
+int vpr_of(const moe_launch::Dims& d) {
+  return int(d.H * int64_t(sizeof(T)) / 16);
+}
+
+}  // namespace
+
+namespace moe_launch {
+
+hipError_t permute(const Dims& d, const void* x, const int32_t* sorted_flat, void* xs, hipStream_t s) {
+  if (d.dtype == MOE_BF16) {
+    int vpr = vpr_of<moe::bf16_t>(d);
+    int64_t tot = d.NK() * vpr;
+    hipLaunchKernelGGL(k_permute<moe::bf16_t>, dim3(grid_for(tot)), dim3(256), 0, s,
+                       static_cast<const moe::bf16_t*>(x), sorted_flat, static_cast<moe::bf16_t*>(xs), tot, vpr,
+                       int(d.K));
+  } else {
+    int vpr = vpr_of<float>(d);
+    int64_t tot = d.NK() * vpr;
+    hipLaunchKernelGGL(k_permute<float>, dim3(grid_for(tot)), dim3(256), 0, s, static_cast<const float*>(x),
+                       sorted_flat, static_cast<float*>(xs), tot, vpr, int(d.K));
+  }
+  return hipGetLastError();
+}
+
+hipError_t combine(const Dims& d, const void* ys, const float* gates, const int32_t* inv, void* y, hipStream_t s) {
+  if (d.dtype == MOE_BF16) {
+    int vpr = vpr_of<moe::bf16_t>(d);
+    int64_t tot = d.N * vpr;
+    hipLaunchKernelGGL(k_combine<moe::bf16_t>, dim3(grid_for(tot)), dim3(256), 0, s,
+                       static_cast<const moe::bf16_t*>(ys), gates, inv, static_cast<moe::bf16_t*>(y), tot, vpr,
+                       int(d.K));
+  } else {
+    int vpr = vpr_of<float>(d);
+    int64_t tot = d.N * vpr;
+    hipLaunchKernelGGL(k_combine<float>, dim3(grid_for(tot)), dim3(256), 0, s, static_cast<const float*>(ys), gates,
+                       inv, static_cast<float*>(y), tot, vpr, int(d.K));
+  }
+  return hipGetLastError();
+}
+
+hipError_t combine_bwd(const Dims& d, const void* dy, const void* ys, const float* gates, const int32_t* inv,
+                       void* dys, float* dgates, hipStream_t s) {
+  unsigned grid = unsigned((d.N + 3) / 4);
+  if (d.dtype == MOE_BF16)
+    hipLaunchKernelGGL(k_combine_bwd<moe::bf16_t>, dim3(grid), dim3(256), 0, s,
+                       static_cast<const moe::bf16_t*>(dy), static_cast<const moe::bf16_t*>(ys), gates, inv,
+                       static_cast<moe::bf16_t*>(dys), dgates, int(d.N), vpr_of<moe::bf16_t>(d), int(d.K));
+  else
+    hipLaunchKernelGGL(k_combine_bwd<float>, dim3(grid), dim3(256), 0, s, static_cast<const float*>(dy),
+                       static_cast<const float*>(ys), gates, inv, static_cast<float*>(dys), dgates, int(d.N),
+                       vpr_of<float>(d), int(d.K));
+  return hipGetLastError();
+}
+
+size_t permute_bwd_ws(const Dims& d) {
+  return size_t(d.H) * size_t(d.E) * (d.dtype == MOE_BF16 ? 2 : 4);
+}
+
+hipError_t permute_bwd(const Dims& d, const void* dxs, const int32_t* inv, const int32_t* topk, const float* dlogits,
+                       const void* w_r, void* dx, void* ws, hipStream_t s) {
+  int64_t nw = d.H * d.E;
+  unsigned tg = unsigned((nw + 255) / 256);
+  if (d.dtype == MOE_BF16) {
+    using T = moe::bf16_t;
+    hipLaunchKernelGGL(k_transpose_wr<T>, dim3(tg), dim3(256), 0, s, static_cast<const T*>(w_r), static_cast<T*>(ws),
+                       int(d.H), int(d.E));
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    int vpr = vpr_of<T>(d);
+    int64_t tot = d.N * vpr;
+    hipLaunchKernelGGL(k_permute_bwd<T>, dim3(grid_for(tot)), dim3(256), 0, s, static_cast<const T*>(dxs), inv, topk,
+                       dlogits, static_cast<const T*>(ws), static_cast<T*>(dx), tot, vpr, int(d.K), int(d.E));
+  } else {
+    using T = float;
+    hipLaunchKernelGGL(k_transpose_wr<T>, dim3(tg), dim3(256), 0, s, static_cast<const T*>(w_r), static_cast<T*>(ws),
+                       int(d.H), int(d.E));
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    int vpr = vpr_of<T>(d);
+    int64_t tot = d.N * vpr;
+    hipLaunchKernelGGL(k_permute_bwd<T>, dim3(grid_for(tot)), dim3(256), 0, s, static_cast<const T*>(dxs), inv, topk,
+                       dlogits, static_cast<const T*>(ws), static_cast<T*>(dx), tot, vpr, int(d.K), int(d.E));
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe_launch

@@ -1,0 +1,152 @@
+"""Forward and backward of the dropless top-k MoE SwiGLU layer on the GPU.
+
+``MoELayerRunner`` owns the device buffers of one problem size (allocated
+through PyTorch, which here only supplies memory and streams) and runs the
+layer through the C ABI:
+
+  forward : moe_route -> moe_permute_meta -> moe_permute -> moe_expert_ffn
+            (moe_ffn_gate_up, moe_ffn_down) -> moe_combine
+  backward: moe_combine_bwd -> moe_route_bwd -> moe_expert_ffn_bwd
+            (moe_ffn_bwd_dact, moe_ffn_bwd_dx, moe_ffn_bwd_dw) -> moe_permute_bwd
+
+Nothing is read back to the host between the calls.  ``MoEFunction`` wraps
+one runner call pair as a ``torch.autograd.Function``.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib as L
+
+
+class MoELayerRunner:
+    """Device buffers and C-ABI calls for fixed (N, H, F, E, K, dtype)."""
+
+    def __init__(self, N: int, H: int, F: int, E: int, K: int, dtype: torch.dtype, device="cuda",
+                 backward: bool = True, save_gu: Optional[bool] = None):
+        self.N, self.H, self.F, self.E, self.K = N, H, F, E, K
+        self.dtype = dtype
+        self.device = torch.device(device)
+        self.d = L.dims(N, H, F, E, K, L.dtype_code(dtype))
+        self.with_backward = backward
+        save_gu = backward if save_gu is None else save_gu
+        NK = N * K
+        dev = self.device
+        i32 = torch.int32
+        mt = L.moe_max_tiles(self.d)
+        if mt < 0:
+            raise L.MoEError("moe_max_tiles", L.MOE_EINVAL)
+        self.max_tiles = mt
+        # forward buffers
+        self.topk = torch.empty((N, K), dtype=i32, device=dev)
+        self.gates = torch.empty((N, K), dtype=torch.float32, device=dev)
+        self.sorted_flat = torch.empty((NK,), dtype=i32, device=dev)
+        self.inv = torch.empty((NK,), dtype=i32, device=dev)
+        self.counts = torch.empty((E,), dtype=i32, device=dev)
+        self.offsets = torch.empty((E + 1,), dtype=i32, device=dev)
+        self.tiles = torch.empty((max(1, mt) * 3,), dtype=i32, device=dev)
+        self.num_tiles = torch.empty((1,), dtype=i32, device=dev)
+        self.meta_ws = self._ws(L.MOE_ENTRY_PERMUTE_META)
+        self.xs = torch.empty((NK, H), dtype=dtype, device=dev)
+        self.g = torch.empty((NK, F), dtype=dtype, device=dev) if save_gu else None
+        self.u = torch.empty((NK, F), dtype=dtype, device=dev) if save_gu else None
+        self.act = torch.empty((NK, F), dtype=dtype, device=dev)
+        self.ys = torch.empty((NK, H), dtype=dtype, device=dev)
+        self.y = torch.empty((N, H), dtype=dtype, device=dev)
+        if backward:
+            f32 = torch.float32
+            self.dys = torch.empty((NK, H), dtype=dtype, device=dev)
+            self.dgates = torch.empty((N, K), dtype=f32, device=dev)
+            self.dlogits = torch.empty((N, E), dtype=f32, device=dev)
+            self.dw_r = torch.empty((H, E), dtype=f32, device=dev)
+            self.dg = torch.empty((NK, F), dtype=dtype, device=dev)
+            self.du = torch.empty((NK, F), dtype=dtype, device=dev)
+            self.dxs = torch.empty((NK, H), dtype=dtype, device=dev)
+            self.dw_gate = torch.empty((E, H, F), dtype=f32, device=dev)
+            self.dw_up = torch.empty((E, H, F), dtype=f32, device=dev)
+            self.dw_down = torch.empty((E, F, H), dtype=f32, device=dev)
+            self.dx = torch.empty((N, H), dtype=dtype, device=dev)
+            self.route_ws = self._ws(L.MOE_ENTRY_ROUTE_BWD)
+            self.perm_ws = self._ws(L.MOE_ENTRY_PERMUTE_BWD)
+        self.inputs = None
+
+    def _ws(self, entry: int):
+        n = L.moe_workspace_bytes(self.d, entry)
+        if n == 2 ** 64 - 1:
+            raise L.MoEError("moe_workspace_bytes", L.MOE_EINVAL)
+        return torch.empty((max(16, n),), dtype=torch.uint8, device=self.device)
+
+    # -------------------------------------------------------------- forward
+    def route(self, x, w_r, bias=None, stream=None):
+        L.moe_route(self.d, x, w_r, bias, self.topk, self.gates, stream)
+
+    def meta(self, topk=None, stream=None):
+        L.moe_permute_meta(self.d, self.topk if topk is None else topk, self.sorted_flat, self.inv, self.counts,
+                           self.offsets, self.tiles, self.num_tiles, self.meta_ws, stream)
+
+    def forward(self, x, w_r, w_gate, w_up, w_down, bias=None, topk=None, gates=None, stream=None):
+        """Run the forward; returns y.  ``topk``/``gates`` (optional) replace the
+        router's own assignment (moe_route is then skipped)."""
+        if topk is None:
+            self.route(x, w_r, bias, stream)
+        else:
+            self.topk.copy_(topk)
+            self.gates.copy_(gates)
+        self.meta(stream=stream)
+        L.moe_permute(self.d, x, self.sorted_flat, self.xs, stream)
+        L.moe_ffn_gate_up(self.d, self.xs, w_gate, w_up, self.tiles, self.num_tiles, self.g, self.u, self.act, stream)
+        L.moe_ffn_down(self.d, self.act, w_down, self.tiles, self.num_tiles, self.ys, stream)
+        L.moe_combine(self.d, self.ys, self.gates, self.inv, self.y, stream)
+        self.inputs = (x, w_r, w_gate, w_up, w_down)
+        return self.y
+
+    # ------------------------------------------------------------- backward
+    def backward(self, dy, stream=None):
+        """Run the backward of the last forward; returns a dict of gradients."""
+        if not self.with_backward:
+            raise RuntimeError("runner was built without backward buffers")
+        x, w_r, w_gate, w_up, w_down = self.inputs
+        d = self.d
+        L.moe_combine_bwd(d, dy, self.ys, self.gates, self.inv, self.dys, self.dgates, stream)
+        L.moe_route_bwd(d, x, self.topk, self.gates, self.dgates, self.dlogits, self.dw_r, self.route_ws, stream)
+        L.moe_ffn_bwd_dact(d, self.dys, w_down, self.g, self.u, self.tiles, self.num_tiles, self.dg, self.du, stream)
+        L.moe_ffn_bwd_dx(d, self.dg, self.du, w_gate, w_up, self.tiles, self.num_tiles, self.dxs, stream)
+        L.moe_ffn_bwd_dw(d, self.xs, self.act, self.dys, self.dg, self.du, self.offsets, self.dw_gate, self.dw_up,
+                         self.dw_down, stream)
+        L.moe_permute_bwd(d, self.dxs, self.inv, self.topk, self.dlogits, w_r, self.dx, self.perm_ws, stream)
+        return dict(dx=self.dx, dw_r=self.dw_r, dw_gate=self.dw_gate, dw_up=self.dw_up, dw_down=self.dw_down,
+                    dgates=self.dgates, dlogits=self.dlogits)
+
+
+class MoEFunction(torch.autograd.Function):
+    """y = MoE(x) with gradients for x, W_r, W_gate, W_up, W_down.
+
+    Weight gradients are computed in float32 by the library and returned in
+    the weights' dtype (autograd requires it); use MoELayerRunner directly to
+    keep them in float32.
+    """
+
+    @staticmethod
+    def forward(ctx, x, w_r, w_gate, w_up, w_down, K: int, bias=None):
+        N, H = x.shape
+        E = w_r.shape[1]
+        F = w_gate.shape[2]
+        r = MoELayerRunner(N, H, F, E, K, x.dtype, x.device, backward=True)
+        y = r.forward(x.contiguous(), w_r.contiguous(), w_gate.contiguous(), w_up.contiguous(), w_down.contiguous(),
+                      bias)
+        ctx.runner = r
+        return y.clone()
+
+    @staticmethod
+    def backward(ctx, dy):
+        g = ctx.runner.backward(dy.contiguous())
+        r = ctx.runner
+        return (g["dx"].clone(), g["dw_r"].to(r.dtype), g["dw_gate"].to(r.dtype), g["dw_up"].to(r.dtype),
+                g["dw_down"].to(r.dtype), None, None)
+
+
+def moe_layer(x, w_r, w_gate, w_up, w_down, K: int, bias=None):
+    """Functional form of the layer with autograd support."""
+    return MoEFunction.apply(x, w_r, w_gate, w_up, w_down, K, bias)

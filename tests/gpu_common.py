@@ -1,0 +1,80 @@
+"""Shared helpers of the GPU parity tests (oracle on the CPU, HIP path on the GPU)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from moe_workloads import MoEConfig, make_inputs
+from oracle import moe_oracle as O
+
+# spec tolerances
+TOL_F32_ABS = 1e-4
+TOL_BF16_ABS = 2e-2
+TOL_BF16_RELRMS = 1e-2
+# logit gap below which float32 and float64 may rank two experts differently
+NEAR_TIE = 1e-4
+
+
+def to_np(t) -> np.ndarray:
+    return O.as_f64(t)
+
+
+def rel_rms(got: np.ndarray, ref: np.ndarray) -> float:
+    den = float(np.mean(ref ** 2))
+    num = float(np.mean((got - ref) ** 2))
+    if den == 0.0:
+        return 0.0 if num == 0.0 else float("inf")
+    return float(np.sqrt(num / den))
+
+
+def assert_close(name: str, got, ref: np.ndarray, dtype: str, abs_tol=None, rel_tol=None):
+    g = to_np(got)
+    assert g.shape == ref.shape, (name, g.shape, ref.shape)
+    assert np.all(np.isfinite(g)), f"{name}: non-finite values"
+    err = float(np.max(np.abs(g - ref))) if g.size else 0.0
+    if dtype == "f32":
+        tol = TOL_F32_ABS if abs_tol is None else abs_tol
+        assert err <= tol, f"{name}: max|err| {err:.3e} > {tol:.1e}"
+    else:
+        tol = TOL_BF16_ABS if abs_tol is None else abs_tol
+        rt = TOL_BF16_RELRMS if rel_tol is None else rel_tol
+        rr = rel_rms(g, ref)
+        assert err <= tol and rr <= rt, f"{name}: max|err| {err:.3e} (tol {tol:.1e}), rel-RMS {rr:.3e} (tol {rt:.1e})"
+    return err
+
+
+def store_of(cfg: MoEConfig) -> str:
+    return "f32" if cfg.dtype == "f32" else "bf16"
+
+
+def gpu_inputs(cfg: MoEConfig, seed: int = 0, with_dy=None):
+    cpu = make_inputs(cfg, seed, with_dy=with_dy)
+    dev = {k: (None if v is None else v.to("cuda")) for k, v in cpu.items()}
+    return cpu, dev
+
+
+def oracle_fwd(cfg: MoEConfig, cpu: dict):
+    return O.forward(cpu["x"], cpu["w_r"], cpu["w_gate"], cpu["w_up"], cpu["w_down"], cfg.K, bias=cpu["bias"],
+                     store=store_of(cfg))
+
+
+def assignment_mismatch(topk_gpu: np.ndarray, ofwd: dict, K: int):
+    """Tokens whose GPU top-K differs from the oracle's; asserts each one is a
+    near-tie (several assignments are correct there)."""
+    tg = topk_gpu.astype(np.int64)
+    to = ofwd["topk"].astype(np.int64)
+    bad = np.where(np.any(tg != to, axis=1))[0]
+    l = ofwd["logits"]
+    for n in bad:
+        lv = l[n]
+        # every expert the GPU picked must be within NEAR_TIE of the oracle's
+        # value at the same rank
+        assert len(set(tg[n].tolist())) == K, f"token {n}: repeated expert"
+        ref_sorted = np.sort(lv)[::-1]
+        for k in range(K):
+            assert abs(lv[tg[n, k]] - ref_sorted[k]) <= NEAR_TIE, (n, k, lv[tg[n, k]], ref_sorted[k])
+    return bad
+
+
+def sync():
+    torch.cuda.synchronize()

@@ -1,0 +1,116 @@
+"""The C-ABI library loads, exports every entry point declared in
+include/moe.h, and rejects bad arguments on the host before any launch
+(CPU only: no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_layer_sort_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(moe_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        from mixture_experts_layer_sort_amd.build import build
+        build()
+    return L.lib()
+
+
+def test_header_declares_the_binding(lib):
+    names = header_functions()
+    assert len(names) >= 17
+    assert sorted(L.SIGNATURES) == names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_matches_header(lib):
+    v = int(re.search(r"#define MOE_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert L.moe_abi_version() == v
+
+
+def test_status_strings(lib):
+    for st in (0, -1, -2, -3, -4, 7):
+        assert isinstance(L.moe_status_str(st), str) and L.moe_status_str(st)
+
+
+def D(N=64, H=128, F=256, E=4, K=2, dtype=L.MOE_BF16, reserved=0):
+    d = L.dims(N, H, F, E, K, dtype)
+    d.reserved = reserved
+    return d
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation or has N = 0
+
+
+def route(d, x=FAKE, w=FAKE, b=None, t=FAKE, g=FAKE):
+    return L.lib().moe_route(ctypes.byref(d), x, w, b, t, g, None)
+
+
+@pytest.mark.parametrize("d,status", [
+    (D(H=100), L.MOE_EINVAL), (D(F=200), L.MOE_EINVAL), (D(N=-1), L.MOE_EINVAL), (D(E=0), L.MOE_EINVAL),
+    (D(K=0), L.MOE_EINVAL), (D(K=5, E=4), L.MOE_EUNSUPPORTED), (D(E=300, K=2), L.MOE_EUNSUPPORTED),
+    (D(E=16, K=9), L.MOE_EUNSUPPORTED), (D(dtype=7), L.MOE_EUNSUPPORTED), (D(reserved=1), L.MOE_EINVAL),
+    (D(N=2 ** 30, K=2), L.MOE_EUNSUPPORTED),
+])
+def test_bad_dims_rejected(lib, d, status):
+    assert route(d) == status
+    assert L.moe_max_tiles(d) == -1
+    assert L.moe_workspace_bytes(d, L.MOE_ENTRY_ROUTE_BWD) == 2 ** 64 - 1
+
+
+def test_null_and_misaligned_pointers_rejected(lib):
+    assert route(D(), x=None) == L.MOE_EINVAL
+    assert route(D(), t=FAKE + 4) == L.MOE_EINVAL
+    assert route(D(), b=FAKE + 8) == L.MOE_EINVAL
+    assert L.lib().moe_route(None, FAKE, FAKE, None, FAKE, FAKE, None) == L.MOE_EINVAL
+    d = D()
+    # g_save / u_save must be both set or both NULL
+    assert L.lib().moe_ffn_gate_up(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == L.MOE_EINVAL
+
+
+def test_workspace_checked(lib):
+    d = D()
+    need = L.moe_workspace_bytes(d, L.MOE_ENTRY_ROUTE_BWD)
+    assert need > 0
+    st = L.lib().moe_route_bwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None)
+    assert st == L.MOE_EWORKSPACE
+    st = L.lib().moe_route_bwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, need, None)
+    assert st == L.MOE_EWORKSPACE
+    need = L.moe_workspace_bytes(d, L.MOE_ENTRY_PERMUTE_BWD)
+    st = L.lib().moe_permute_bwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 16, None)
+    assert st == L.MOE_EWORKSPACE
+    assert L.moe_workspace_bytes(d, 99) == 2 ** 64 - 1
+
+
+def test_zero_tokens_returns_ok_without_launch(lib):
+    d = D(N=0)
+    assert route(d) == L.MOE_OK
+    assert L.lib().moe_permute_meta(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == 0
+    assert L.lib().moe_combine(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None) == 0
+
+
+@pytest.mark.parametrize("N,K,E", [(16384, 2, 8), (16384, 6, 64), (8192, 8, 256), (1, 1, 1), (3, 2, 256)])
+def test_max_tiles_bounds_any_routing(lib, N, K, E):
+    d = D(N=N, K=K, E=E)
+    mt = L.moe_max_tiles(d)
+    assert mt == (N * K + E * (L.MOE_TILE_M - 1)) // L.MOE_TILE_M
+    # worst case over routings: sum_e ceil(c_e / T) with sum_e c_e = NK
+    import math
+    NK = N * K
+    worst_spread = sum(math.ceil(c / L.MOE_TILE_M) for c in [NK // E + (1 if i < NK % E else 0) for i in range(E)])
+    assert worst_spread <= mt

@@ -1,0 +1,209 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, element by
+element, on seeded inputs that span several tiles with ragged tails, empty
+experts, K=1, K=E, E=1, the fp32 storage type and the closed-form fixture.
+
+Bars: routing indices and metadata bit-exact (given the same assignment);
+fp32 storage max|err| <= 1e-4; bf16 storage max|err| <= 2e-2 and rel-RMS
+<= 1e-2; repeated runs bitwise identical.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from moe_workloads import CONFIGS, TEST_CONFIGS, MoEConfig
+from oracle import moe_oracle as O
+from tests.gpu_common import (assert_close, assignment_mismatch, gpu_inputs, oracle_fwd, store_of, sync, to_np)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [CONFIGS["c0"]] + list(TEST_CONFIGS.values())
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from mixture_experts_layer_sort_amd import _lib
+    _lib.lib()  # fails loudly when the HIP library is missing
+
+
+def _runner(cfg, backward=True):
+    from mixture_experts_layer_sort_amd.layer import MoELayerRunner
+    return MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, "cuda", backward=backward)
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_route_matches_oracle(cfg):
+    print(f"[route] {cfg.name}", flush=True)
+    cpu, dev = gpu_inputs(cfg)
+    r = _runner(cfg, backward=False)
+    r.route(dev["x"], dev["w_r"], dev["bias"])
+    sync()
+    of = oracle_fwd(cfg, cpu)
+    topk = r.topk.cpu().numpy()
+    bad = assignment_mismatch(topk, of, cfg.K)
+    good = np.setdiff1d(np.arange(cfg.N), bad)
+    assert len(bad) <= max(1, cfg.N // 100)
+    g = r.gates.cpu().numpy().astype(np.float64)
+    assert np.allclose(g.sum(axis=1), 1.0, atol=1e-6)
+    assert np.max(np.abs(g[good] - of["gates"][good])) <= 2e-6
+
+
+@pytest.mark.parametrize("cfg", SMALL + [CONFIGS["c1"], CONFIGS["c2"]], ids=lambda c: c.name)
+def test_permute_meta_bit_exact(cfg):
+    """Given the oracle's assignment, counts, offsets, the stable sort, its
+    inverse and the tile list are bit-exact."""
+    print(f"[meta] {cfg.name}", flush=True)
+    from mixture_experts_layer_sort_amd import _lib as L
+    if cfg.N * cfg.H > 4_000_000:
+        # large shapes: a synthetic skewed assignment of the same size
+        rng = np.random.default_rng(7)
+        p = np.arange(1, cfg.E + 1, dtype=np.float64) ** -1.2
+        p /= p.sum()
+        topk = np.stack([rng.choice(cfg.E, size=cfg.K, replace=False, p=p) for _ in range(cfg.N)]).astype(np.int32)
+    else:
+        cpu, _ = gpu_inputs(cfg)
+        topk = oracle_fwd(cfg, cpu)["topk"]
+    counts, offsets, sorted_flat, inv = O.routing_metadata(topk, cfg.E)
+    tiles = O.tile_list(counts, offsets, L.MOE_TILE_M)
+    r = _runner(cfg, backward=False)
+    r.meta(topk=torch.from_numpy(topk).cuda())
+    sync()
+    assert np.array_equal(r.counts.cpu().numpy(), counts)
+    assert np.array_equal(r.offsets.cpu().numpy(), offsets)
+    assert np.array_equal(r.sorted_flat.cpu().numpy(), sorted_flat)
+    assert np.array_equal(r.inv.cpu().numpy(), inv)
+    nt = int(r.num_tiles.cpu().item())
+    assert nt == len(tiles) and nt <= r.max_tiles
+    assert np.array_equal(r.tiles.cpu().numpy()[:3 * nt].reshape(-1, 3), tiles)
+
+
+def _fwd_bwd(cfg, seed=0):
+    cpu, dev = gpu_inputs(cfg, seed, with_dy=True)
+    of = oracle_fwd(cfg, cpu)
+    r = _runner(cfg)
+    r.route(dev["x"], dev["w_r"], dev["bias"])
+    sync()
+    bad = assignment_mismatch(r.topk.cpu().numpy(), of, cfg.K)
+    if len(bad):
+        # near-ties only: run the rest of the path on the oracle's assignment
+        y = r.forward(dev["x"], dev["w_r"], dev["w_gate"], dev["w_up"], dev["w_down"],
+                      topk=torch.from_numpy(of["topk"]).cuda(),
+                      gates=torch.from_numpy(of["gates"].astype(np.float32)).cuda())
+    else:
+        y = r.forward(dev["x"], dev["w_r"], dev["w_gate"], dev["w_up"], dev["w_down"], dev["bias"])
+    grads = r.backward(dev["dy"])
+    sync()
+    ob = O.backward(of, cpu["dy"])
+    return r, of, ob, y, grads
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_layer_forward_backward_matches_oracle(cfg):
+    print(f"[layer] {cfg.name}", flush=True)
+    r, of, ob, y, g = _fwd_bwd(cfg)
+    dt = store_of(cfg)
+    # intermediates of the forward
+    assert_close("xs", r.xs, of["xs"], dt)
+    assert_close("G", r.g, of["G"], dt)
+    assert_close("U", r.u, of["U"], dt)
+    assert_close("A", r.act, of["A"], dt)
+    assert_close("ys", r.ys, of["ys"], dt)
+    assert_close("y", y, of["y"], dt)
+    # backward
+    assert_close("dys", r.dys, ob["dys"], dt)
+    assert_close("dgates", g["dgates"], ob["dgates"], dt)
+    assert_close("dlogits", g["dlogits"], ob["dlogits"], dt)
+    assert_close("dG", r.dg, ob["dG"], dt)
+    assert_close("dU", r.du, ob["dU"], dt)
+    assert_close("dxs", r.dxs, ob["dxs"], dt)
+    assert_close("dx", g["dx"], ob["dx"], dt)
+    assert_close("dw_r", g["dw_r"], ob["dw_r"], dt)
+    assert_close("dw_gate", g["dw_gate"], ob["dw_gate"], dt)
+    assert_close("dw_up", g["dw_up"], ob["dw_up"], dt)
+    assert_close("dw_down", g["dw_down"], ob["dw_down"], dt)
+    # experts without rows get exact zeros
+    for e in np.where(of["counts"] == 0)[0]:
+        for name in ("dw_gate", "dw_up", "dw_down"):
+            assert torch.count_nonzero(g[name][int(e)]).item() == 0
+
+
+def test_empty_experts_present_in_skewed_case():
+    cfg = TEST_CONFIGS["t_skew"]
+    cpu, _ = gpu_inputs(cfg)
+    assert np.sum(oracle_fwd(cfg, cpu)["counts"] == 0) > 0
+
+
+@pytest.mark.parametrize("cfg", [TEST_CONFIGS["t_ragged"], TEST_CONFIGS["t_skew"], CONFIGS["c0"]],
+                         ids=lambda c: c.name)
+def test_bitwise_reproducible(cfg):
+    """Three runs (one with outputs pre-poisoned) give identical bytes."""
+    print(f"[determinism] {cfg.name}", flush=True)
+    cpu, dev = gpu_inputs(cfg, 3, with_dy=True)
+    outs = []
+    for rep in range(3):
+        r = _runner(cfg)
+        if rep == 1:
+            for name in ("y", "dx", "dw_r", "dw_gate", "dw_up", "dw_down", "dgates", "dlogits", "xs", "ys", "act"):
+                getattr(r, name).view(torch.uint8).fill_(0xFF)
+        y = r.forward(dev["x"], dev["w_r"], dev["w_gate"], dev["w_up"], dev["w_down"], dev["bias"])
+        g = r.backward(dev["dy"])
+        sync()
+        outs.append({k: v.cpu().clone() for k, v in dict(y=y, **g).items()})
+    for rep in (1, 2):
+        for k in outs[0]:
+            assert torch.equal(outs[0][k].view(torch.uint8), outs[rep][k].view(torch.uint8)), (rep, k)
+
+
+def test_closed_form_fixture_on_gpu():
+    """The hand-derived closed-form case, zero-padded to H = F = 128, fp32."""
+    from mixture_experts_layer_sort_amd.layer import MoELayerRunner
+    with open(os.path.join(os.path.dirname(__file__), "golden", "closed_form_e3_k2.json")) as fh:
+        gd = json.load(fh)
+    env = {"log": math.log, "__builtins__": {}}
+
+    def ev(a):
+        return [ev(v) for v in a] if isinstance(a, list) else float(eval(a, env))  # noqa: S307
+
+    H = F = 128
+    N, E, K = gd["N"], gd["E"], gd["K"]
+    inp = {k: np.array(ev(v)) for k, v in gd["inputs"].items()}
+    x = np.zeros((N, H)); x[:, :2] = inp["x"]
+    w_r = np.zeros((H, E)); w_r[:2] = inp["w_r"]
+    wg = np.zeros((E, H, F)); wg[:, :2, :1] = inp["w_gate"]
+    wu = np.zeros((E, H, F)); wu[:, :2, :1] = inp["w_up"]
+    wd = np.zeros((E, F, H)); wd[:, :1, :2] = inp["w_down"]
+    dy = np.zeros((N, H)); dy[:, :2] = inp["dy"]
+    t = lambda a: torch.tensor(a, dtype=torch.float32, device="cuda")  # noqa: E731
+    r = MoELayerRunner(N, H, F, E, K, torch.float32, "cuda")
+    y = r.forward(t(x), t(w_r), t(wg), t(wu), t(wd))
+    g = r.backward(t(dy))
+    sync()
+    ex = gd["expected"]
+    assert r.topk.cpu().tolist() == ex["topk"]
+    assert r.counts.cpu().tolist() == ex["counts"]
+    assert r.sorted_flat.cpu().tolist() == ex["sorted_flat"]
+    assert r.inv.cpu().tolist() == ex["inv"]
+    tol = 2e-6
+    assert np.allclose(r.gates.cpu().numpy(), ev(ex["gates"]), atol=tol)
+    assert np.allclose(y.cpu().numpy()[:, :2], ev(ex["y"]), atol=tol) and not y.cpu()[:, 2:].any()
+    assert np.allclose(g["dgates"].cpu().numpy(), ev(ex["dgates"]), atol=tol)
+    assert np.allclose(g["dlogits"].cpu().numpy(), ev(ex["dlogits"]), atol=tol)
+    assert np.allclose(g["dw_r"].cpu().numpy()[:2], ev(ex["dw_r"]), atol=tol)
+    assert np.allclose(g["dw_down"].cpu().numpy()[:, :1, :2], ev(ex["dw_down"]), atol=tol)
+    assert np.allclose(g["dw_gate"].cpu().numpy()[:, :2, :1], ev(ex["dw_gate"]), atol=tol)
+    assert np.allclose(g["dw_up"].cpu().numpy()[:, :2, :1], ev(ex["dw_up"]), atol=tol)
+    assert np.allclose(g["dx"].cpu().numpy()[:, :2], ev(ex["dx"]), atol=tol)
+
+
+def test_zero_tokens_is_a_noop():
+    from mixture_experts_layer_sort_amd import _lib as L
+    d = L.dims(0, 128, 128, 4, 2, L.MOE_BF16)
+    z = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    L.moe_route(d, z, z, None, z, z)
+    L.moe_combine(d, z, z, z, z)
+    sync()
