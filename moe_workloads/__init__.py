@@ -80,12 +80,12 @@ CONFIGS = {
 # empty experts, K=1, K=E, E=1 and the fp32 path.
 TEST_CONFIGS = {
     "t_ragged": MoEConfig("t_ragged", N=700, H=256, F=384, E=6, K=3, dtype="bf16"),
-    "t_skew": MoEConfig("t_skew", N=600, H=128, F=192, E=16, K=2, dtype="bf16", zipf_s=1.2, zipf_tau=3.0),
-    "t_k1": MoEConfig("t_k1", N=333, H=192, F=128, E=5, K=1, dtype="bf16"),
+    "t_skew": MoEConfig("t_skew", N=600, H=128, F=256, E=16, K=2, dtype="bf16", zipf_s=1.2, zipf_tau=3.0),
+    "t_k1": MoEConfig("t_k1", N=333, H=256, F=128, E=5, K=1, dtype="bf16"),
     "t_keqe": MoEConfig("t_keqe", N=257, H=128, F=256, E=4, K=4, dtype="bf16"),
-    "t_e1": MoEConfig("t_e1", N=300, H=128, F=320, E=1, K=1, dtype="bf16"),
+    "t_e1": MoEConfig("t_e1", N=300, H=128, F=384, E=1, K=1, dtype="bf16"),
     "t_wide_e": MoEConfig("t_wide_e", N=512, H=256, F=128, E=256, K=8, dtype="bf16"),
-    "t_f32": MoEConfig("t_f32", N=203, H=192, F=320, E=7, K=3, dtype="f32"),
+    "t_f32": MoEConfig("t_f32", N=203, H=256, F=384, E=7, K=3, dtype="f32"),
     "t_bigtile": MoEConfig("t_bigtile", N=2048, H=512, F=768, E=4, K=2, dtype="bf16"),
 }
 

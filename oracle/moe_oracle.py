@@ -403,3 +403,159 @@ def token_backward(tf: dict, dyn, w_r, expert_weights: ExpertFn, store: str = "b
     dl[tf["topk"].astype(np.int64)] = dsel
     dx = rho(dxs_sum + w_r @ dl, store)
     return dict(dgates=dg, dlogits=dl, rows=out_rows, dx=dx)
+
+
+# --------------------------------------------------------------------------
+# rounding-decision bands (bf16 storage)
+# --------------------------------------------------------------------------
+#
+# A device implementation accumulates in float32, so the value it rounds to
+# bfloat16 differs from the exact value by a few float32 roundings.  Where the
+# exact value lies that close to a rounding midpoint, either neighbouring
+# bfloat16 value is a correct result, and the choice propagates into later
+# sums.  rounding_bands() returns, per element of each output, a first-order
+# bound of the deviation such choices can cause; it is zero wherever no
+# rounding decision upstream of the element was ambiguous.  Tests compare
+# |device - oracle| <= tolerance + band, which checks every unique result
+# exactly and every ambiguous one for validity.
+
+U32 = 2.0 ** -24  # unit roundoff of float32
+
+
+def gemm_sigma(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Bound of the float32 accumulation error of a @ b (exact products,
+    n-term sums): 4 u sqrt(n) ||row_a * col_b||_2 + 4 u |a @ b|."""
+    n = a.shape[-1]
+    return 4 * U32 * math.sqrt(max(n, 1)) * np.sqrt((a * a) @ (b * b)) + 4 * U32 * np.abs(a @ b)
+
+
+def bf16_flip(pre: np.ndarray, rounded: np.ndarray, sigma: np.ndarray) -> np.ndarray:
+    """Deviation bound of a bfloat16 rounding whose input is known to within
+    +-sigma: sigma + the spacing to the other candidate where the interval
+    reaches a rounding midpoint, else 0 (both ends round alike)."""
+    r32 = np.ascontiguousarray(rounded, dtype=np.float32)
+    bits = r32.view(np.uint32).astype(np.int64)
+    diff = pre - rounded
+    away = (np.sign(diff) == np.sign(rounded)) & (diff != 0)
+    nb_bits = np.where(away, bits + 0x10000, bits - 0x10000) & 0xFFFFFFFF
+    nb = nb_bits.astype(np.uint32).view(np.float32).astype(np.float64)
+    spacing = np.where(rounded == 0, 0.0, np.abs(nb - rounded))
+    dist = spacing / 2 - np.abs(diff)
+    return np.where(dist <= sigma, sigma + spacing, 0.0)
+
+
+def _silu_d1(g):
+    s = sigmoid(g)
+    return s * (1.0 + g * (1.0 - s))
+
+
+def _silu_d2(g):
+    s = sigmoid(g)
+    return s * (1.0 - s) * (2.0 + g * (1.0 - 2.0 * s))
+
+
+def prop(dev: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """Deviation of dev-perturbed rows multiplied by w (dev @ w): the smaller of
+    the worst case |dev| @ |w| and four standard deviations of a sum of
+    independent-sign terms, 4 sqrt(dev^2 @ w^2)."""
+    return np.minimum(dev @ np.abs(w), 4.0 * np.sqrt((dev * dev) @ (w * w)))
+
+
+def rounding_bands(fwd: dict, bwd: Optional[dict] = None, dy=None) -> dict:
+    """Per-element deviation bounds (see above) of every stored tensor and
+    output of a bf16-storage forward (and backward) computed by this module."""
+    assert fwd["store"] == "bf16"
+    K = fwd["K"]
+    x, w_r = fwd["x"], fwd["w_r"]
+    N, H = x.shape
+    E = w_r.shape[1]
+    NK = N * K
+    F = fwd["w_gate"].shape[2]
+    off, sf, inv = fwd["offsets"], fwd["sorted_flat"], fwd["inv"]
+    inv2 = inv.reshape(N, K)
+    tok = sf // K
+    gflat = fwd["gates"].reshape(-1)
+    grow = gflat[sf][:, None]
+    xs, G, U, A, ys = fwd["xs"], fwd["G"], fwd["U"], fwd["A"], fwd["ys"]
+    b = {k: np.zeros((NK, F)) for k in ("G", "U", "A")}
+    b["ys"] = np.zeros((NK, H))
+    for e in range(E):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r1 == r0:
+            continue
+        sl = slice(r0, r1)
+        wg, wu, wd = fwd["w_gate"][e], fwd["w_up"][e], fwd["w_down"][e]
+        b["G"][sl] = bf16_flip(xs[sl] @ wg, G[sl], gemm_sigma(xs[sl], wg))
+        b["U"][sl] = bf16_flip(xs[sl] @ wu, U[sl], gemm_sigma(xs[sl], wu))
+        ap = silu(G[sl]) * U[sl]
+        sa = np.abs(U[sl] * _silu_d1(G[sl])) * b["G"][sl] + np.abs(silu(G[sl])) * b["U"][sl] + 16 * U32 * np.abs(ap)
+        b["A"][sl] = bf16_flip(ap, A[sl], sa)
+        b["ys"][sl] = bf16_flip(A[sl] @ wd, ys[sl], gemm_sigma(A[sl], wd) + prop(b["A"][sl], wd))
+    yp = np.zeros((N, H))
+    sy = np.zeros((N, H))
+    for k in range(K):
+        r = inv2[:, k]
+        g = fwd["gates"][:, k:k + 1]
+        yp += g * ys[r]
+        sy += g * b["ys"][r] + 8 * U32 * np.abs(g * ys[r])
+    b["y"] = bf16_flip(yp, fwd["y"], sy)
+    if bwd is None:
+        return b
+
+    dy = as_f64(dy)
+    # combine backward
+    dysp = grow * dy[tok]
+    b["dys"] = bf16_flip(dysp, bwd["dys"], 8 * U32 * np.abs(dysp))
+    ys_tok = ys[inv2]
+    b_ys_tok = b["ys"][inv2]
+    lin = np.einsum("nh,nkh->nk", np.abs(dy), b_ys_tok)
+    rss = 4.0 * np.sqrt(np.einsum("nh,nkh->nk", dy * dy, b_ys_tok * b_ys_tok))
+    b["dgates"] = (np.minimum(lin, rss)
+                   + 4 * U32 * math.sqrt(H) * np.sqrt(np.einsum("nh,nkh->nk", dy * dy, ys_tok * ys_tok))
+                   + 2 * U32 * np.abs(bwd["dgates"]))
+    # expert backward
+    for k in ("dG", "dU"):
+        b[k] = np.zeros((NK, F))
+    b["dxs"] = np.zeros((NK, H))
+    for k in ("dw_gate", "dw_up", "dw_down"):
+        b[k] = np.zeros_like(fwd[k.replace("dw_", "w_")])
+    for e in range(E):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r1 == r0:
+            continue
+        sl = slice(r0, r1)
+        wg, wu, wd = fwd["w_gate"][e], fwd["w_up"][e], fwd["w_down"][e]
+        d = bwd["dys"][sl]
+        dA = d @ wd.T
+        sdA = gemm_sigma(d, wd.T) + prop(b["dys"][sl], wd.T)
+        g_, u_ = G[sl], U[sl]
+        d1, d2 = _silu_d1(g_), _silu_d2(g_)
+        dgp = dA * u_ * d1
+        sdg = (np.abs(u_ * d1) * sdA + np.abs(dA * d1) * b["U"][sl] + np.abs(dA * u_ * d2) * b["G"][sl]
+               + 16 * U32 * np.abs(dgp))
+        b["dG"][sl] = bf16_flip(dgp, bwd["dG"][sl], sdg)
+        dup = dA * silu(g_)
+        sdu = np.abs(silu(g_)) * sdA + np.abs(dA * d1) * b["G"][sl] + 16 * U32 * np.abs(dup)
+        b["dU"][sl] = bf16_flip(dup, bwd["dU"][sl], sdu)
+        dG, dU = bwd["dG"][sl], bwd["dU"][sl]
+        dxp = dG @ wg.T + dU @ wu.T
+        sdx = gemm_sigma(dG, wg.T) + gemm_sigma(dU, wu.T) + prop(b["dG"][sl], wg.T) + prop(b["dU"][sl], wu.T)
+        b["dxs"][sl] = bf16_flip(dxp, bwd["dxs"][sl], sdx)
+        xt = xs[sl].T
+        b["dw_gate"][e] = prop(b["dG"][sl].T, xt.T).T + gemm_sigma(xt, dG) + 2 * U32 * np.abs(bwd["dw_gate"][e])
+        b["dw_up"][e] = prop(b["dU"][sl].T, xt.T).T + gemm_sigma(xt, dU) + 2 * U32 * np.abs(bwd["dw_up"][e])
+        b["dw_down"][e] = (prop(b["A"][sl].T, d) + prop(b["dys"][sl].T, A[sl]).T + gemm_sigma(A[sl].T, d)
+                           + 2 * U32 * np.abs(bwd["dw_down"][e]))
+    # router backward
+    g = fwd["gates"]
+    sdl = g * (b["dgates"] + np.sum(g * b["dgates"], axis=1, keepdims=True)) + 8 * U32 * (
+        np.abs(g * bwd["dgates"]) + g * np.sum(np.abs(g * bwd["dgates"]), axis=1, keepdims=True))
+    b["dlogits"] = np.zeros((N, E))
+    np.put_along_axis(b["dlogits"], fwd["topk"].astype(np.int64), sdl, axis=1)
+    b["dw_r"] = prop(b["dlogits"].T, x).T + gemm_sigma(x.T, bwd["dlogits"]) + 2 * U32 * np.abs(bwd["dw_r"])
+    # gather backward
+    dxp = bwd["dxs"][inv2].sum(axis=1) + bwd["dlogits"] @ w_r.T
+    sdx = (b["dxs"][inv2].sum(axis=1) + prop(b["dlogits"], w_r.T)
+           + 8 * U32 * (np.abs(bwd["dxs"][inv2]).sum(axis=1) + np.abs(bwd["dlogits"]) @ np.abs(w_r.T)))
+    b["dx"] = bf16_flip(dxp, bwd["dx"], sdx)
+    return b

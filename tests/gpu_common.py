@@ -27,20 +27,40 @@ def rel_rms(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.sqrt(num / den))
 
 
-def assert_close(name: str, got, ref: np.ndarray, dtype: str, abs_tol=None, rel_tol=None):
+BAND_FREE = 1e-3   # elements whose rounding band is below this are held to the plain bound
+
+
+def assert_close(name: str, got, ref: np.ndarray, dtype: str, band=None, abs_tol=None, rel_tol=None):
+    """fp32: max|err| <= 1e-4.  bf16: rel-RMS <= 1e-2 and, per element,
+    |err| <= 2e-2 + band, where band (from oracle.rounding_bands) is nonzero
+    only where an upstream bf16 rounding decision was ambiguous; elements
+    with band < BAND_FREE are held to 2e-2 alone."""
     g = to_np(got)
     assert g.shape == ref.shape, (name, g.shape, ref.shape)
     assert np.all(np.isfinite(g)), f"{name}: non-finite values"
-    err = float(np.max(np.abs(g - ref))) if g.size else 0.0
+    err = np.abs(g - ref)
+    emax = float(err.max()) if g.size else 0.0
     if dtype == "f32":
         tol = TOL_F32_ABS if abs_tol is None else abs_tol
-        assert err <= tol, f"{name}: max|err| {err:.3e} > {tol:.1e}"
-    else:
-        tol = TOL_BF16_ABS if abs_tol is None else abs_tol
-        rt = TOL_BF16_RELRMS if rel_tol is None else rel_tol
-        rr = rel_rms(g, ref)
-        assert err <= tol and rr <= rt, f"{name}: max|err| {err:.3e} (tol {tol:.1e}), rel-RMS {rr:.3e} (tol {rt:.1e})"
-    return err
+        assert emax <= tol, f"{name}: max|err| {emax:.3e} > {tol:.1e}"
+        return emax
+    tol = TOL_BF16_ABS if abs_tol is None else abs_tol
+    rt = TOL_BF16_RELRMS if rel_tol is None else rel_tol
+    rr = rel_rms(g, ref)
+    if band is None:
+        band = np.zeros_like(ref)
+    free = band < BAND_FREE
+    efree = float(err[free].max()) if free.any() else 0.0
+    excess = err - (tol + band)
+    worst = int(np.argmax(excess)) if g.size else 0
+    msg = (f"{name}: max|err| {emax:.3e}, band-free max|err| {efree:.3e} over {free.mean():.1%} of elements, "
+           f"rel-RMS {rr:.3e}; worst excess {excess.reshape(-1)[worst]:.3e} at flat {worst} "
+           f"(err {err.reshape(-1)[worst]:.3e}, band {band.reshape(-1)[worst]:.3e})")
+    print(msg, flush=True)
+    assert rr <= rt, msg
+    assert efree <= tol, msg
+    assert np.all(excess <= 0), msg
+    return emax
 
 
 def store_of(cfg: MoEConfig) -> str:
