@@ -64,6 +64,7 @@ def stage_bytes(cfg):
         "combine": (NK + N) * H * e + NK * 8,
         "combine_bwd": (N + 2 * NK) * H * e + NK * 12,
         "permute_bwd": (NK + N) * H * e + NK * 8 + N * K * 4,
+        "route_bwd": N * H * e + N * K * 12 + N * E * 4 + H * E * 4,
     }
 
 

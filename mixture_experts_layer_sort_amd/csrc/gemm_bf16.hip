@@ -138,71 +138,119 @@ struct TileInfo {
   int e, row0, rows;
 };
 
-// ---------------------------------------------------------------- forward
+// Output tiles leave through LDS: each lane deposits its accumulator elements
+// (MFMA layout) into a [128][kEpiPitch] bf16 tile, then the workgroup writes
+// whole rows with 16-byte stores.  The 8-element row padding puts the two
+// lane halves of a fragment store (rows r and r+4) on different banks.
+constexpr int kEpiPitch = BN + 8;
+constexpr int kEpiBytes = BM * kEpiPitch * 2;
+constexpr int kLds2 = (2 * kTileBytes > kEpiBytes) ? 2 * kTileBytes : kEpiBytes;
 
-// G = xs.W_gate[e], U = xs.W_up[e] (both rounded to bf16), A = silu(G)*U.
-__global__ __launch_bounds__(NT, 1) void k_gate_up(const bf16_t* __restrict__ xs, const bf16_t* __restrict__ wg,
-                                                    const bf16_t* __restrict__ wu, const int32_t* __restrict__ tiles,
-                                                    const int32_t* __restrict__ num_tiles, bf16_t* __restrict__ g_out,
-                                                    bf16_t* __restrict__ u_out, bf16_t* __restrict__ a_out, int H,
-                                                    int F) {
-  __shared__ __attribute__((aligned(16))) char lds[3 * kTileBytes];
-  const int ntn = F / BN;
-  const int tile = blockIdx.x / ntn, nt = blockIdx.x % ntn;
-  if (tile >= *num_tiles) return;
-  const TileInfo ti{tiles[3 * tile], tiles[3 * tile + 1], tiles[3 * tile + 2]};
-  const int w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
-  const bf16_t* a_base = xs + (int64_t)ti.row0 * H;
-  const bf16_t* g_base = wg + (int64_t)ti.e * H * F + nt * BN;
-  const bf16_t* u_base = wu + (int64_t)ti.e * H * F + nt * BN;
+__device__ __forceinline__ int epi_off(int wm, int wn, int mi, int ni, int r) {
+  return acc_row(wm, mi, r) * kEpiPitch + acc_col(wn, ni);
+}
 
-  f32x16_t accg[2][2], accu[2][2];
-  zero_acc(accg);
-  zero_acc(accu);
-  LoadKC la;
-  LoadMN lg, lu;
-  const int nk = H / BK;
-  la.load(a_base, H, ti.rows);
-  lg.load(g_base, F, BK);
-  lu.load(u_base, F, BK);
-  for (int kt = 0; kt < nk; ++kt) {
-    la.store(lds);
-    lg.store(lds + kTileBytes);
-    lu.store(lds + 2 * kTileBytes);
-    __syncthreads();
-    if (kt + 1 < nk) {
-      la.load(a_base + (kt + 1) * BK, H, ti.rows);
-      lg.load(g_base + (int64_t)(kt + 1) * BK * F, F, BK);
-      lu.load(u_base + (int64_t)(kt + 1) * BK * F, F, BK);
-    }
-    mma_tile(lds, lds + kTileBytes, accg, wm, wn);
-    mma_tile(lds, lds + 2 * kTileBytes, accu, wm, wn);
-    __syncthreads();
-  }
+// rows [0, rows) of the staged tile -> out (leading dimension ld)
+__device__ __forceinline__ void epi_store(const bf16_t* tile, bf16_t* out, int64_t ld, int rows) {
+  const int c = threadIdx.x & 15;
+#pragma unroll 4
+  for (int r = threadIdx.x >> 4; r < rows; r += NT / 16)
+    *reinterpret_cast<uint4*>(out + (int64_t)r * ld + c * 8) =
+        *reinterpret_cast<const uint4*>(tile + r * kEpiPitch + c * 8);
+}
+
+// rows [0, rows) of a global bf16 tile (leading dimension ld) -> staged tile
+__device__ __forceinline__ void epi_load(bf16_t* tile, const bf16_t* in, int64_t ld, int rows) {
+  const int c = threadIdx.x & 15;
+#pragma unroll 4
+  for (int r = threadIdx.x >> 4; r < rows; r += NT / 16)
+    *reinterpret_cast<uint4*>(tile + r * kEpiPitch + c * 8) =
+        *reinterpret_cast<const uint4*>(in + (int64_t)r * ld + c * 8);
+}
+
+// staged tile <- bf16(acc)
+__device__ __forceinline__ void epi_put_acc(bf16_t* tile, const f32x16_t (&acc)[2][2], int wm, int wn) {
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = acc_row(wm, mi, r);
-        if (m < ti.rows) {
-          const int64_t o = (int64_t)(ti.row0 + m) * F + nt * BN + acc_col(wn, ni);
-          const bf16_t gb = f32_to_bf16(accg[mi][ni][r]);
-          const bf16_t ub = f32_to_bf16(accu[mi][ni][r]);
-          const float gf = bf16_to_f32(gb), uf = bf16_to_f32(ub);
-          if (g_out) g_out[o] = gb;
-          if (u_out) u_out[o] = ub;
-          a_out[o] = f32_to_bf16(silu_f32(gf) * uf);
-        }
-      }
+      for (int r = 0; r < 16; ++r) tile[epi_off(wm, wn, mi, ni, r)] = f32_to_bf16(acc[mi][ni][r]);
+}
+
+// ---------------------------------------------------------------- forward
+
+// G = xs.W_gate[e], U = xs.W_up[e] (both rounded to bf16), A = silu(G)*U.
+// The B tile interleaves 64 columns of W_gate[e] (tile columns 0..63) with
+// the same 64 columns of W_up[e] (tile columns 64..127), so waves wn = 0
+// hold G and waves wn = 1 hold U; the epilogue pairs them through LDS.
+__global__ __launch_bounds__(NT, 2) void k_gate_up(const bf16_t* __restrict__ xs, const bf16_t* __restrict__ wg,
+                                                    const bf16_t* __restrict__ wu, const int32_t* __restrict__ tiles,
+                                                    const int32_t* __restrict__ num_tiles, bf16_t* __restrict__ g_out,
+                                                    bf16_t* __restrict__ u_out, bf16_t* __restrict__ a_out, int H,
+                                                    int F) {
+  __shared__ __attribute__((aligned(16))) char lds[kLds2];
+  constexpr int HALF = BN / 2;
+  const int ntn = F / HALF;
+  const int tile = blockIdx.x / ntn, nt = blockIdx.x % ntn;
+  if (tile >= *num_tiles) return;
+  const TileInfo ti{tiles[3 * tile], tiles[3 * tile + 1], tiles[3 * tile + 2]};
+  const int w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const bf16_t* a_base = xs + (int64_t)ti.row0 * H;
+  // this thread's 8-column group of the B tile comes from W_gate or W_up
+  const int mc = threadIdx.x & 15;
+  const bf16_t* b_base = ((mc < 8) ? wg : wu) + (int64_t)ti.e * H * F + nt * HALF - (mc < 8 ? 0 : HALF);
+
+  f32x16_t acc[2][2];
+  zero_acc(acc);
+  LoadKC la;
+  LoadMN lb;
+  const int nk = H / BK;
+  la.load(a_base, H, ti.rows);
+  lb.load(b_base, F, BK);
+  for (int kt = 0; kt < nk; ++kt) {
+    la.store(lds);
+    lb.store(lds + kTileBytes);
+    __syncthreads();
+    if (kt + 1 < nk) {
+      la.load(a_base + (kt + 1) * BK, H, ti.rows);
+      lb.load(b_base + (int64_t)(kt + 1) * BK * F, F, BK);
+    }
+    mma_tile(lds, lds + kTileBytes, acc, wm, wn);
+    __syncthreads();
+  }
+  // staged tile: columns 0..63 = G, 64..127 = U (bf16)
+  bf16_t* stg = reinterpret_cast<bf16_t*>(lds);
+  epi_put_acc(stg, acc, wm, wn);
+  __syncthreads();
+  const int64_t obase = (int64_t)ti.row0 * F + nt * HALF;
+  const int c = threadIdx.x & 7;
+#pragma unroll 4
+  for (int r = threadIdx.x >> 3; r < ti.rows; r += NT / 8) {
+    const uint4 gq = *reinterpret_cast<const uint4*>(stg + r * kEpiPitch + c * 8);
+    const uint4 uq = *reinterpret_cast<const uint4*>(stg + r * kEpiPitch + HALF + c * 8);
+    const int64_t o = obase + (int64_t)r * F + c * 8;
+    if (g_out) {
+      *reinterpret_cast<uint4*>(g_out + o) = gq;
+      *reinterpret_cast<uint4*>(u_out + o) = uq;
+    }
+    const uint32_t gw[4] = {gq.x, gq.y, gq.z, gq.w}, uw[4] = {uq.x, uq.y, uq.z, uq.w};
+    uint32_t aw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float g0 = __uint_as_float(gw[i] << 16), g1 = __uint_as_float(gw[i] & 0xffff0000u);
+      const float u0 = __uint_as_float(uw[i] << 16), u1 = __uint_as_float(uw[i] & 0xffff0000u);
+      aw[i] = uint32_t(f32_to_bf16(silu_f32(g0) * u0)) | (uint32_t(f32_to_bf16(silu_f32(g1) * u1)) << 16);
+    }
+    *reinterpret_cast<uint4*>(a_out + o) = make_uint4(aw[0], aw[1], aw[2], aw[3]);
+  }
 }
 
 // ys = A.W_down[e]
 __global__ __launch_bounds__(NT, 2) void k_down(const bf16_t* __restrict__ act, const bf16_t* __restrict__ wd,
                                                  const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles,
                                                  bf16_t* __restrict__ ys, int H, int F) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * kTileBytes];
+  __shared__ __attribute__((aligned(16))) char lds[kLds2];
   const int ntn = H / BN;
   const int tile = blockIdx.x / ntn, nt = blockIdx.x % ntn;
   if (tile >= *num_tiles) return;
@@ -228,15 +276,10 @@ __global__ __launch_bounds__(NT, 2) void k_down(const bf16_t* __restrict__ act, 
     mma_tile(lds, lds + kTileBytes, acc, wm, wn);
     __syncthreads();
   }
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = acc_row(wm, mi, r);
-        if (m < ti.rows) ys[(int64_t)(ti.row0 + m) * H + nt * BN + acc_col(wn, ni)] = f32_to_bf16(acc[mi][ni][r]);
-      }
+  bf16_t* stg = reinterpret_cast<bf16_t*>(lds);
+  epi_put_acc(stg, acc, wm, wn);
+  __syncthreads();
+  epi_store(stg, ys + (int64_t)ti.row0 * H + nt * BN, H, ti.rows);
 }
 
 // --------------------------------------------------------------- backward
@@ -246,7 +289,7 @@ __global__ __launch_bounds__(NT, 2) void k_dact(const bf16_t* __restrict__ dys, 
                                                  const bf16_t* __restrict__ g_in, const bf16_t* __restrict__ u_in,
                                                  const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles,
                                                  bf16_t* __restrict__ dg, bf16_t* __restrict__ du, int H, int F) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * kTileBytes];
+  __shared__ __attribute__((aligned(16))) char lds[kLds2];
   const int ntn = F / BN;
   const int tile = blockIdx.x / ntn, nt = blockIdx.x % ntn;
   if (tile >= *num_tiles) return;
@@ -272,22 +315,43 @@ __global__ __launch_bounds__(NT, 2) void k_dact(const bf16_t* __restrict__ dys, 
     mma_tile(lds, lds + kTileBytes, acc, wm, wn);
     __syncthreads();
   }
+  // G tile -> LDS; acc becomes dA*s*(1+G*(1-s)) and dU = dA*G*s is kept
+  bf16_t* stg = reinterpret_cast<bf16_t*>(lds);
+  const int64_t obase = (int64_t)ti.row0 * F + nt * BN;
+  epi_load(stg, g_in + obase, F, ti.rows);
+  __syncthreads();
+  f32x16_t dup[2][2];
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = acc_row(wm, mi, r);
-        if (m < ti.rows) {
-          const int64_t o = (int64_t)(ti.row0 + m) * F + nt * BN + acc_col(wn, ni);
-          const float da = acc[mi][ni][r];
-          const float gv = bf16_to_f32(g_in[o]), uv = bf16_to_f32(u_in[o]);
-          const float s = sigmoid_f32(gv);
-          dg[o] = f32_to_bf16(da * uv * s * (1.f + gv * (1.f - s)));
-          du[o] = f32_to_bf16(da * gv * s);
-        }
+        const float gv = bf16_to_f32(stg[epi_off(wm, wn, mi, ni, r)]);
+        const float sg = sigmoid_f32(gv);
+        const float da = acc[mi][ni][r];
+        dup[mi][ni][r] = da * gv * sg;
+        acc[mi][ni][r] = da * sg * (1.f + gv * (1.f - sg));
       }
+  __syncthreads();
+  // U tile -> LDS; dG = (dA*s*(1+G*(1-s))) * U written in place
+  epi_load(stg, u_in + obase, F, ti.rows);
+  __syncthreads();
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int o = epi_off(wm, wn, mi, ni, r);
+        stg[o] = f32_to_bf16(acc[mi][ni][r] * bf16_to_f32(stg[o]));
+      }
+  __syncthreads();
+  epi_store(stg, dg + obase, F, ti.rows);
+  __syncthreads();
+  epi_put_acc(stg, dup, wm, wn);
+  __syncthreads();
+  epi_store(stg, du + obase, F, ti.rows);
 }
 
 // dxs = dG.W_gate[e]^T + dU.W_up[e]^T  (one K loop over 2F)
@@ -295,7 +359,7 @@ __global__ __launch_bounds__(NT, 2) void k_dx(const bf16_t* __restrict__ dg, con
                                                const bf16_t* __restrict__ wg, const bf16_t* __restrict__ wu,
                                                const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles,
                                                bf16_t* __restrict__ dxs, int H, int F) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * kTileBytes];
+  __shared__ __attribute__((aligned(16))) char lds[kLds2];
   const int ntn = H / BN;
   const int tile = blockIdx.x / ntn, nt = blockIdx.x % ntn;
   if (tile >= *num_tiles) return;
@@ -322,15 +386,10 @@ __global__ __launch_bounds__(NT, 2) void k_dx(const bf16_t* __restrict__ dg, con
     mma_tile(lds, lds + kTileBytes, acc, wm, wn);
     __syncthreads();
   }
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = acc_row(wm, mi, r);
-        if (m < ti.rows) dxs[(int64_t)(ti.row0 + m) * H + nt * BN + acc_col(wn, ni)] = f32_to_bf16(acc[mi][ni][r]);
-      }
+  bf16_t* stg = reinterpret_cast<bf16_t*>(lds);
+  epi_put_acc(stg, acc, wm, wn);
+  __syncthreads();
+  epi_store(stg, dxs + (int64_t)ti.row0 * H + nt * BN, H, ti.rows);
 }
 
 // Weight gradients, one workgroup per 128 x 128 output tile of one expert:
@@ -343,7 +402,7 @@ __global__ __launch_bounds__(NT, 2) void k_dw(const bf16_t* __restrict__ xs, con
                                                const bf16_t* __restrict__ du, const int32_t* __restrict__ offsets,
                                                float* __restrict__ dwg, float* __restrict__ dwu,
                                                float* __restrict__ dwd, int H, int F, int E) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * kTileBytes];
+  __shared__ __attribute__((aligned(16))) char lds[kLds2];
   const int tpe = (H / BM) * (F / BN);  // output tiles per expert and problem
   const int prob = blockIdx.x / (E * tpe);
   const int rem = blockIdx.x % (E * tpe);
@@ -401,7 +460,7 @@ namespace moe_launch {
 
 hipError_t ffn_gate_up_bf16(const Dims& d, const void* xs, const void* wg, const void* wu, const int32_t* tiles,
                             const int32_t* num_tiles, void* g, void* u, void* a, hipStream_t s) {
-  unsigned grid = unsigned(max_tiles(d) * (d.F / BN));
+  unsigned grid = unsigned(max_tiles(d) * (d.F / (BN / 2)));
   hipLaunchKernelGGL(k_gate_up, dim3(grid), dim3(NT), 0, s, static_cast<const bf16_t*>(xs),
                      static_cast<const bf16_t*>(wg), static_cast<const bf16_t*>(wu), tiles, num_tiles,
                      static_cast<bf16_t*>(g), static_cast<bf16_t*>(u), static_cast<bf16_t*>(a), int(d.H), int(d.F));

@@ -21,48 +21,98 @@ namespace {
 using namespace moe;
 
 constexpr int kRouteTok = 32;  // tokens per workgroup
-constexpr int kRouteHC = 16;   // h per LDS chunk (keeps LDS <= 64 KB at E = 256)
+
+// h per staged chunk: the W_r chunk [HC][EP] float32 stays within 32 KiB and
+// the x chunk [HC][32] within 16 KiB
+template <int EPT>
+constexpr int route_hc() {
+  return (8192 / (8 * EPT)) < 128 ? (8192 / (8 * EPT)) : 128;
+}
 
 template <typename T, int EPT>
 __global__ __launch_bounds__(256) void k_route(const T* __restrict__ x, const T* __restrict__ w_r,
                                                const float* __restrict__ bias, int32_t* __restrict__ topk,
                                                float* __restrict__ gates, int N, int H, int E, int K) {
   constexpr int EP = 8 * EPT;  // padded experts
+  constexpr int HC = route_hc<EPT>();
+  constexpr int V = Vec16<T>::n;
+  constexpr int XV = (kRouteTok * HC / V + 255) / 256;   // x vectors per thread per chunk
+  constexpr int WV = (HC * EP / V + 255) / 256;          // W_r vectors per thread per chunk (upper bound)
   extern __shared__ float smem[];
   float* xs_t = smem;                        // [HC][32]   x chunk, transposed
-  float* w_l = xs_t + kRouteHC * kRouteTok;  // [HC][EP]   W_r chunk
-  float* lg = w_l + kRouteHC * EP;           // [32][EP+1] logits
+  float* w_l = xs_t + HC * kRouteTok;        // [HC][EP]   W_r chunk
+  float* lg = smem;                          // [32][EP+1] logits, reuses the staging space after the h loop
 
   const int tid = threadIdx.x;
   const int t = tid & 31;   // token within the block
   const int j = tid >> 5;   // expert group: experts j*EPT .. j*EPT+EPT-1
   const int n0 = blockIdx.x * kRouteTok;
+  const int wvec = HC * E / V;  // vectors in one W_r chunk (rows h0..h0+HC-1 are contiguous)
 
   float acc[EPT];
 #pragma unroll
   for (int i = 0; i < EPT; ++i) acc[i] = 0.f;
 
-  for (int h0 = 0; h0 < H; h0 += kRouteHC) {
-    // stage x[n0:n0+32, h0:h0+HC] (transposed) and W_r[h0:h0+HC, :]
-    for (int idx = tid; idx < kRouteTok * kRouteHC; idx += 256) {
-      int tt = idx / kRouteHC, hh = idx % kRouteHC;
-      int n = n0 + tt;
-      xs_t[hh * kRouteTok + tt] = (n < N) ? Elt<T>::load(x + (int64_t)n * H + h0 + hh) : 0.f;
+  uint4 xr[XV], wr[WV];
+  auto fetch = [&](int h0) {
+#pragma unroll
+    for (int q = 0; q < XV; ++q) {
+      const int idx = tid + 256 * q;
+      const int tt = idx / (HC / V), hv = idx % (HC / V);
+      xr[q] = (idx < kRouteTok * HC / V && n0 + tt < N)
+                  ? *reinterpret_cast<const uint4*>(x + (int64_t)(n0 + tt) * H + h0 + hv * V)
+                  : make_uint4(0, 0, 0, 0);
     }
-    for (int idx = tid; idx < kRouteHC * EP; idx += 256) {
-      int hh = idx / EP, e = idx % EP;
-      w_l[idx] = (e < E) ? Elt<T>::load(w_r + (int64_t)(h0 + hh) * E + e) : 0.f;
+#pragma unroll
+    for (int q = 0; q < WV; ++q) {
+      const int idx = tid + 256 * q;
+      wr[q] = (idx < wvec) ? *reinterpret_cast<const uint4*>(w_r + (int64_t)h0 * E + idx * V)
+                           : make_uint4(0, 0, 0, 0);
     }
+  };
+  auto deposit = [&]() {
+#pragma unroll
+    for (int q = 0; q < XV; ++q) {
+      const int idx = tid + 256 * q;
+      if (idx < kRouteTok * HC / V) {
+        const int tt = idx / (HC / V), hv = idx % (HC / V);
+        float v[V];
+        Vec16<T>::load(reinterpret_cast<const T*>(&xr[q]), v);
+#pragma unroll
+        for (int i = 0; i < V; ++i) xs_t[(hv * V + i) * kRouteTok + tt] = v[i];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < WV; ++q) {
+      const int idx = tid + 256 * q;
+      if (idx < wvec) {
+        float v[V];
+        Vec16<T>::load(reinterpret_cast<const T*>(&wr[q]), v);
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          const int el = idx * V + i;
+          w_l[(el / E) * EP + el % E] = v[i];
+        }
+      }
+    }
+  };
+  // padded experts of the W_r chunk stay zero
+  for (int idx = tid; idx < HC * EP; idx += 256) w_l[idx] = 0.f;
+  fetch(0);
+  for (int h0 = 0; h0 < H; h0 += HC) {
     __syncthreads();
+    deposit();
+    __syncthreads();
+    if (h0 + HC < H) fetch(h0 + HC);
 #pragma unroll 4
-    for (int hh = 0; hh < kRouteHC; ++hh) {
-      float xv = xs_t[hh * kRouteTok + t];
+    for (int hh = 0; hh < HC; ++hh) {
+      const float xv = xs_t[hh * kRouteTok + t];
       const float* wrow = w_l + hh * EP + j * EPT;
 #pragma unroll
       for (int i = 0; i < EPT; ++i) acc[i] = fmaf(xv, wrow[i], acc[i]);
     }
-    __syncthreads();
   }
+  __syncthreads();
 #pragma unroll
   for (int i = 0; i < EPT; ++i) {
     int e = j * EPT + i;
@@ -154,48 +204,85 @@ __global__ __launch_bounds__(256) void k_route_bwd_dl(const int32_t* __restrict_
   dl[idx] = out;
 }
 
-constexpr int kRbH = 64;  // h per workgroup in the dW_r partial kernel (LDS E*64 floats <= 64 KB)
+constexpr int kRbTok = 128;  // tokens staged in LDS at a time by the dW_r partial kernel
 
-// Partial dW_r of one token chunk: part[c][e][h] = sum_{n in chunk} x[n,h] dl[n,e]
-// (sparse in e: only the K selected experts of each token contribute).
-template <typename T>
-__global__ __launch_bounds__(kRbH) void k_route_bwd_partial(const T* __restrict__ x, const int32_t* __restrict__ topk,
-                                                            const float* __restrict__ dl, float* __restrict__ part,
-                                                            int N, int H, int E, int K, int chunk) {
-  extern __shared__ float acc[];  // [E][kRbH]
+// Partial dW_r of one chunk of tokens and HB hidden units:
+// part[c][e][h] = sum_{n in chunk} x[n,h] dl[n,e], sparse in e (only the K
+// selected experts of a token contribute).  kRbTok tokens at a time, the x
+// slice, expert ids and dlogits values are first staged in LDS with
+// independent loads; then each thread accumulates its h over the tokens in
+// ascending order.
+template <typename T, int HB>
+__global__ __launch_bounds__(HB) void k_route_bwd_partial(const T* __restrict__ x, const int32_t* __restrict__ topk,
+                                                          const float* __restrict__ dl, float* __restrict__ part,
+                                                          int N, int H, int E, int K, int chunk) {
+  extern __shared__ float smem[];
+  float* acc = smem;                                              // [E][HB]
+  float* xs = acc + E * HB;                                       // [kRbTok][HB]
+  int* s_e = reinterpret_cast<int*>(xs + kRbTok * HB);            // [kRbTok*K]
+  float* s_d = reinterpret_cast<float*>(s_e + kRbTok * K);        // [kRbTok*K]
   const int t = threadIdx.x;
-  const int h = blockIdx.x * kRbH + t;
+  const int h0 = blockIdx.x * HB;
   const int c = blockIdx.y;
-  for (int e = 0; e < E; ++e) acc[e * kRbH + t] = 0.f;
   const int nb = c * chunk, ne = min(N, nb + chunk);
-  for (int n = nb; n < ne; ++n) {
-    float xv = Elt<T>::load(x + (int64_t)n * H + h);
-    for (int k = 0; k < K; ++k) {
-      int e = topk[(int64_t)n * K + k];
-      float d = dl[(int64_t)n * E + e];
-      acc[e * kRbH + t] = fmaf(xv, d, acc[e * kRbH + t]);
+  constexpr int V = Vec16<T>::n;
+  constexpr int VPR = HB / V;  // 16-byte vectors per token row of the slice
+  for (int e = 0; e < E; ++e) acc[e * HB + t] = 0.f;
+  for (int s0 = nb; s0 < ne; s0 += kRbTok) {
+    const int nt = min(kRbTok, ne - s0);
+    __syncthreads();
+    for (int i = t; i < nt * VPR; i += HB) {
+      const int tt = i / VPR, v = i % VPR;
+      float val[V];
+      Vec16<T>::load(x + (int64_t)(s0 + tt) * H + h0 + v * V, val);
+#pragma unroll
+      for (int q = 0; q < V; ++q) xs[tt * HB + v * V + q] = val[q];
+    }
+    for (int i = t; i < nt * K; i += HB) {
+      const int64_t f = (int64_t)s0 * K + i;
+      const int e = topk[f];
+      s_e[i] = e;
+      s_d[i] = dl[(f / K) * E + e];
+    }
+    __syncthreads();
+    for (int n = 0; n < nt; ++n) {
+      const float xv = xs[n * HB + t];
+      for (int k = 0; k < K; ++k) {
+        const int e = s_e[n * K + k];
+        acc[e * HB + t] = fmaf(xv, s_d[n * K + k], acc[e * HB + t]);
+      }
     }
   }
   float* out = part + (int64_t)c * E * H;
-  for (int e = 0; e < E; ++e) out[(int64_t)e * H + h] = acc[e * kRbH + t];
+  for (int e = 0; e < E; ++e) out[(int64_t)e * H + h0 + t] = acc[e * HB + t];
 }
 
-// dW_r[h, e] = sum over chunks (ascending) of part[c][e][h].
+// dW_r[h, e] = sum of part[c][e][h] over chunks c: 8 lanes per output each
+// sum a fixed stride-8 subset of the chunks in ascending order, then a fixed
+// butterfly adds the 8 partial sums.
 __global__ __launch_bounds__(256) void k_route_bwd_reduce(const float* __restrict__ part, float* __restrict__ dw_r,
                                                           int H, int E, int nchunks) {
-  int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)E * H) return;
-  int e = int(idx / H), h = int(idx % H);
-  float s = 0.f;
-  for (int c = 0; c < nchunks; ++c) s += part[(int64_t)c * E * H + idx];
-  dw_r[(int64_t)h * E + e] = s;
+  const int64_t o = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 3;
+  const int j = threadIdx.x & 7;
+  float sum = 0.f;
+  if (o < (int64_t)E * H)
+    for (int c = j; c < nchunks; c += 8) sum += part[(int64_t)c * E * H + o];
+  sum += __shfl_xor(sum, 1, kWave);
+  sum += __shfl_xor(sum, 2, kWave);
+  sum += __shfl_xor(sum, 4, kWave);
+  if (j == 0 && o < (int64_t)E * H) {
+    const int e = int(o / H), h = int(o % H);
+    dw_r[(int64_t)h * E + e] = sum;
+  }
 }
 
 template <typename T, int EPT>
 hipError_t launch_route_t(const moe_launch::Dims& d, const void* x, const void* w_r, const float* bias, int32_t* topk,
                           float* gates, hipStream_t s) {
   constexpr int EP = 8 * EPT;
-  size_t lds = sizeof(float) * (kRouteHC * kRouteTok + kRouteHC * EP + kRouteTok * (EP + 1));
+  constexpr int HC = route_hc<EPT>();
+  constexpr size_t stage = HC * kRouteTok + HC * EP, logits = kRouteTok * (EP + 1);
+  size_t lds = sizeof(float) * (stage > logits ? stage : logits);
   int grid = int((d.N + kRouteTok - 1) / kRouteTok);
   hipLaunchKernelGGL((k_route<T, EPT>), dim3(grid), dim3(256), lds, s, static_cast<const T*>(x),
                      static_cast<const T*>(w_r), bias, topk, gates, int(d.N), int(d.H), int(d.E), int(d.K));
@@ -223,10 +310,13 @@ hipError_t route(const Dims& d, const void* x, const void* w_r, const float* bia
   return launch_route<float>(d, x, w_r, bias, topk, gates, s);
 }
 
+// Token chunks of the dW_r partial sums: one per kRbTok tokens, fewer when
+// the partials (chunks * E * H floats) would exceed 16 MiB.
 size_t route_bwd_chunks(const Dims& d) {
-  int64_t c = (d.N + 511) / 512;
+  int64_t c = (d.N + kRbTok - 1) / kRbTok;
+  const int64_t cap = (int64_t(16) << 20) / (4 * d.E * d.H);
+  if (c > cap) c = cap;
   if (c < 1) c = 1;
-  if (c > 64) c = 64;
   return size_t(c);
 }
 
@@ -239,23 +329,37 @@ hipError_t route_bwd(const Dims& d, const void* x, const int32_t* topk, const fl
                      int(d.N), int(d.E), int(d.K));
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  int nch = int(route_bwd_chunks(d));
-  int chunk = int((d.N + nch - 1) / nch);
+  const int nch = int(route_bwd_chunks(d));
+  const int chunk = int((d.N + nch - 1) / nch);
   float* part = static_cast<float*>(ws);
-  size_t lds = sizeof(float) * size_t(d.E) * kRbH;
-  dim3 grid(unsigned(d.H / kRbH), unsigned(nch));
-  if (d.dtype == MOE_BF16)
-    hipLaunchKernelGGL(k_route_bwd_partial<moe::bf16_t>, grid, dim3(kRbH), lds, s,
-                       static_cast<const moe::bf16_t*>(x), topk, dlogits, part, int(d.N), int(d.H), int(d.E), int(d.K),
-                       chunk);
-  else
-    hipLaunchKernelGGL(k_route_bwd_partial<float>, grid, dim3(kRbH), lds, s, static_cast<const float*>(x), topk,
-                       dlogits, part, int(d.N), int(d.H), int(d.E), int(d.K), chunk);
+  if (d.E <= 64) {  // LDS: E*HB + kRbTok*HB + 2*kRbTok*K floats <= 64 KiB
+    constexpr int HB = 64;
+    size_t lds = sizeof(float) * (size_t(d.E) * HB + size_t(kRbTok) * HB + 2 * size_t(kRbTok) * d.K);
+    dim3 grid(unsigned(d.H / HB), unsigned(nch));
+    if (d.dtype == MOE_BF16)
+      hipLaunchKernelGGL((k_route_bwd_partial<moe::bf16_t, HB>), grid, dim3(HB), lds, s,
+                         static_cast<const moe::bf16_t*>(x), topk, dlogits, part, int(d.N), int(d.H), int(d.E),
+                         int(d.K), chunk);
+    else
+      hipLaunchKernelGGL((k_route_bwd_partial<float, HB>), grid, dim3(HB), lds, s, static_cast<const float*>(x),
+                         topk, dlogits, part, int(d.N), int(d.H), int(d.E), int(d.K), chunk);
+  } else {
+    constexpr int HB = 32;
+    size_t lds = sizeof(float) * (size_t(d.E) * HB + size_t(kRbTok) * HB + 2 * size_t(kRbTok) * d.K);
+    dim3 grid(unsigned(d.H / HB), unsigned(nch));
+    if (d.dtype == MOE_BF16)
+      hipLaunchKernelGGL((k_route_bwd_partial<moe::bf16_t, HB>), grid, dim3(HB), lds, s,
+                         static_cast<const moe::bf16_t*>(x), topk, dlogits, part, int(d.N), int(d.H), int(d.E),
+                         int(d.K), chunk);
+    else
+      hipLaunchKernelGGL((k_route_bwd_partial<float, HB>), grid, dim3(HB), lds, s, static_cast<const float*>(x),
+                         topk, dlogits, part, int(d.N), int(d.H), int(d.E), int(d.K), chunk);
+  }
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  int64_t nw = d.E * d.H;
-  hipLaunchKernelGGL(k_route_bwd_reduce, dim3(unsigned((nw + 255) / 256)), dim3(256), 0, s, part, dw_r, int(d.H),
-                     int(d.E), nch);
+  const int64_t nthreads = d.E * d.H * 8;
+  hipLaunchKernelGGL(k_route_bwd_reduce, dim3(unsigned((nthreads + 255) / 256)), dim3(256), 0, s, part, dw_r,
+                     int(d.H), int(d.E), nch);
   return hipGetLastError();
 }
 
