@@ -55,7 +55,7 @@ extern "C" {
 
 #define MOE_ABI_VERSION 1
 /* Rows per tile of the grouped-GEMM tile list built by moe_permute_meta. */
-#define MOE_TILE_M 128
+#define MOE_TILE_M 256
 #define MOE_MAX_EXPERTS 256
 #define MOE_MAX_TOPK 8
 

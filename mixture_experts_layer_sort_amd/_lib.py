@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1
 MOE_ENTRY_PERMUTE_META, MOE_ENTRY_ROUTE_BWD, MOE_ENTRY_PERMUTE_BWD = 1, 2, 3
-MOE_TILE_M = 128
+MOE_TILE_M = 256
 
 # Every exported symbol with (restype, argtypes); the tests check this list
 # against include/moe.h and against the built library.

@@ -10,8 +10,13 @@
 // synchronisation is needed: the grid is sized for the largest possible tile
 // count and workgroups past the real count return at once.
 //
-// Workgroup tile 128 x 128, K step 64, 256 threads = 4 waves in a 2 x 2
-// arrangement, 64 x 64 per wave (2 x 2 MFMA 32x32x16 per 16-deep k step).
+// This file holds the shape for problems too small for the 256 x 256 LDS-DMA
+// kernels (short contractions, few tiles per CU): workgroup tile 128 x 128,
+// K step 64, 256 threads = 4 waves in a 2 x 2 arrangement, 64 x 64 per wave
+// (2 x 2 MFMA 32x32x16 per 16-deep k step).  One LDS buffer plus register
+// prefetch keeps the LDS footprint near 34 KB, so 3 workgroups share a CU
+// and hide each other's latency.  Each workgroup handles half of a 256-row
+// list tile.
 // Operand tiles live in LDS as [128 rows][64 k] bf16 (128 B per row, eight
 // 16-byte chunks) with the chunk index XOR-swizzled by the row, so that both
 // the MFMA fragment reads (8 consecutive rows, same chunk) and the staging
@@ -57,12 +62,25 @@ struct LoadKC {
   }
 };
 
+// Thread -> (8-column group mc, 4-row group kg) of the MN loader.  Each
+// 16-lane phase of a wave covers 8 column groups x 2 row groups, so its
+// 8-byte transposed LDS writes land on 32 distinct banks, while every 8
+// consecutive lanes still read one contiguous 128-byte segment of a row.
+__device__ __forceinline__ int mn_mc() {
+  const int l = threadIdx.x & 63;
+  return (l & 7) | (((l >> 4) & 1) << 3);
+}
+__device__ __forceinline__ int mn_kg() {
+  const int l = threadIdx.x & 63;
+  return (((l >> 3) & 1) | ((l >> 5) << 1)) + 4 * (threadIdx.x >> 6);
+}
+
 // 64 k-rows x 128 mn-columns of a row-major matrix whose mn index is
 // contiguous, stored to LDS transposed as [mn][k].
 struct LoadMN {
   uint4 v[4];
   __device__ __forceinline__ void load(const bf16_t* base, int64_t ld, int k_valid) {
-    const int mc = threadIdx.x & 15, kg = threadIdx.x >> 4;
+    const int mc = mn_mc(), kg = mn_kg();
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       int k = kg * 4 + j;
@@ -73,7 +91,7 @@ struct LoadMN {
     }
   }
   __device__ __forceinline__ void store(char* lds) const {
-    const int mc = threadIdx.x & 15, kg = threadIdx.x >> 4;
+    const int mc = mn_mc(), kg = mn_kg();
     uint32_t w[4][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -138,6 +156,40 @@ struct TileInfo {
   int e, row0, rows;
 };
 
+// The hardware places workgroup b on XCD b % 8 (each XCD has its own L2).
+// Logical block L of `total` gets a contiguous range per XCD, so that the
+// blocks sharing an operand tile (the n-tiles of one row tile, the output
+// tiles of one expert) run on one XCD and share its L2.  The launch grid is
+// a multiple of 8 and at least `total`; returns -1 for blocks with no work.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_block(int total) {
+  const int b = blockIdx.x;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int L = (b % kXcds) * per + b / kXcds;
+  return (b / kXcds < per && L < total) ? L : -1;
+}
+
+// Logical block -> (row tile, n tile) in groups of kGroupM row tiles: inside
+// a group the row tile varies fastest, so the workgroups an XCD runs at once
+// cover a patch of row tiles x n tiles and share operand tiles in its L2.
+constexpr int kGroupM = 8;
+__device__ __forceinline__ void grouped(int L, int nrow, int ncol, int& row, int& col) {
+  const int per_group = kGroupM * ncol;
+  const int g = L / per_group, r = L % per_group;
+  const int first = g * kGroupM;
+  const int gm = min(kGroupM, nrow - first);
+  row = first + r % gm;
+  col = r / gm;
+}
+
+// Half `h` of the 256-row list tiles (two 128-row workgroup tiles per list
+// tile); rows <= 0 when the list tile is shorter.
+constexpr int kSub = MOE_TILE_M / BM;
+__device__ __forceinline__ TileInfo half_tile(const int32_t* tiles, int h) {
+  const int t = h / kSub, part = h % kSub;
+  return TileInfo{tiles[3 * t], tiles[3 * t + 1] + part * BM, min(BM, tiles[3 * t + 2] - part * BM)};
+}
+
 // Output tiles leave through LDS: each lane deposits its accumulator elements
 // (MFMA layout) into a [128][kEpiPitch] bf16 tile, then the workgroup writes
 // whole rows with 16-byte stores.  The 8-element row padding puts the two
@@ -192,13 +244,17 @@ __global__ __launch_bounds__(NT, 2) void k_gate_up(const bf16_t* __restrict__ xs
   __shared__ __attribute__((aligned(16))) char lds[kLds2];
   constexpr int HALF = BN / 2;
   const int ntn = F / HALF;
-  const int tile = blockIdx.x / ntn, nt = blockIdx.x % ntn;
-  if (tile >= *num_tiles) return;
-  const TileInfo ti{tiles[3 * tile], tiles[3 * tile + 1], tiles[3 * tile + 2]};
+  const int nrow = *num_tiles * kSub;
+  const int L = xcd_block(nrow * ntn);
+  if (L < 0) return;
+  int ht, nt;
+  grouped(L, nrow, ntn, ht, nt);
+  const TileInfo ti = half_tile(tiles, ht);
+  if (ti.rows <= 0) return;
   const int w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
   const bf16_t* a_base = xs + (int64_t)ti.row0 * H;
   // this thread's 8-column group of the B tile comes from W_gate or W_up
-  const int mc = threadIdx.x & 15;
+  const int mc = mn_mc();
   const bf16_t* b_base = ((mc < 8) ? wg : wu) + (int64_t)ti.e * H * F + nt * HALF - (mc < 8 ? 0 : HALF);
 
   f32x16_t acc[2][2];
@@ -252,9 +308,13 @@ __global__ __launch_bounds__(NT, 2) void k_down(const bf16_t* __restrict__ act, 
                                                  bf16_t* __restrict__ ys, int H, int F) {
   __shared__ __attribute__((aligned(16))) char lds[kLds2];
   const int ntn = H / BN;
-  const int tile = blockIdx.x / ntn, nt = blockIdx.x % ntn;
-  if (tile >= *num_tiles) return;
-  const TileInfo ti{tiles[3 * tile], tiles[3 * tile + 1], tiles[3 * tile + 2]};
+  const int nrow = *num_tiles * kSub;
+  const int L = xcd_block(nrow * ntn);
+  if (L < 0) return;
+  int ht, nt;
+  grouped(L, nrow, ntn, ht, nt);
+  const TileInfo ti = half_tile(tiles, ht);
+  if (ti.rows <= 0) return;
   const int w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
   const bf16_t* a_base = act + (int64_t)ti.row0 * F;
   const bf16_t* b_base = wd + (int64_t)ti.e * F * H + nt * BN;
@@ -291,9 +351,13 @@ __global__ __launch_bounds__(NT, 2) void k_dact(const bf16_t* __restrict__ dys, 
                                                  bf16_t* __restrict__ dg, bf16_t* __restrict__ du, int H, int F) {
   __shared__ __attribute__((aligned(16))) char lds[kLds2];
   const int ntn = F / BN;
-  const int tile = blockIdx.x / ntn, nt = blockIdx.x % ntn;
-  if (tile >= *num_tiles) return;
-  const TileInfo ti{tiles[3 * tile], tiles[3 * tile + 1], tiles[3 * tile + 2]};
+  const int nrow = *num_tiles * kSub;
+  const int L = xcd_block(nrow * ntn);
+  if (L < 0) return;
+  int ht, nt;
+  grouped(L, nrow, ntn, ht, nt);
+  const TileInfo ti = half_tile(tiles, ht);
+  if (ti.rows <= 0) return;
   const int w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
   const bf16_t* a_base = dys + (int64_t)ti.row0 * H;
   // B[k = h][n = f] = W_down[e][f][h]: rows f of W_down[e] are k-contiguous
@@ -361,9 +425,13 @@ __global__ __launch_bounds__(NT, 2) void k_dx(const bf16_t* __restrict__ dg, con
                                                bf16_t* __restrict__ dxs, int H, int F) {
   __shared__ __attribute__((aligned(16))) char lds[kLds2];
   const int ntn = H / BN;
-  const int tile = blockIdx.x / ntn, nt = blockIdx.x % ntn;
-  if (tile >= *num_tiles) return;
-  const TileInfo ti{tiles[3 * tile], tiles[3 * tile + 1], tiles[3 * tile + 2]};
+  const int nrow = *num_tiles * kSub;
+  const int L = xcd_block(nrow * ntn);
+  if (L < 0) return;
+  int ht, nt;
+  grouped(L, nrow, ntn, ht, nt);
+  const TileInfo ti = half_tile(tiles, ht);
+  if (ti.rows <= 0) return;
   const int w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
   // B[k = f][n = h] = W[e][h][f]: rows h of W[e] are k-contiguous
   const int64_t woff = (int64_t)ti.e * H * F + (int64_t)nt * BN * F;
@@ -404,8 +472,10 @@ __global__ __launch_bounds__(NT, 2) void k_dw(const bf16_t* __restrict__ xs, con
                                                float* __restrict__ dwd, int H, int F, int E) {
   __shared__ __attribute__((aligned(16))) char lds[kLds2];
   const int tpe = (H / BM) * (F / BN);  // output tiles per expert and problem
-  const int prob = blockIdx.x / (E * tpe);
-  const int rem = blockIdx.x % (E * tpe);
+  const int blk = xcd_block(3 * E * tpe);
+  if (blk < 0) return;
+  const int prob = blk / (E * tpe);
+  const int rem = blk % (E * tpe);
   const int e = rem / tpe, t = rem % tpe;
   const bf16_t *L, *R;
   float* out;
@@ -458,44 +528,47 @@ __global__ __launch_bounds__(NT, 2) void k_dw(const bf16_t* __restrict__ xs, con
 
 namespace moe_launch {
 
-hipError_t ffn_gate_up_bf16(const Dims& d, const void* xs, const void* wg, const void* wu, const int32_t* tiles,
+// grid size rounded up to whole XCD rounds
+static unsigned grid8(int64_t n) { return unsigned((n + kXcds - 1) / kXcds * kXcds); }
+
+hipError_t ffn_gate_up_small(const Dims& d, const void* xs, const void* wg, const void* wu, const int32_t* tiles,
                             const int32_t* num_tiles, void* g, void* u, void* a, hipStream_t s) {
-  unsigned grid = unsigned(max_tiles(d) * (d.F / (BN / 2)));
+  unsigned grid = grid8(max_tiles(d) * kSub * (d.F / (BN / 2)));
   hipLaunchKernelGGL(k_gate_up, dim3(grid), dim3(NT), 0, s, static_cast<const bf16_t*>(xs),
                      static_cast<const bf16_t*>(wg), static_cast<const bf16_t*>(wu), tiles, num_tiles,
                      static_cast<bf16_t*>(g), static_cast<bf16_t*>(u), static_cast<bf16_t*>(a), int(d.H), int(d.F));
   return hipGetLastError();
 }
 
-hipError_t ffn_down_bf16(const Dims& d, const void* a, const void* wd, const int32_t* tiles, const int32_t* num_tiles,
+hipError_t ffn_down_small(const Dims& d, const void* a, const void* wd, const int32_t* tiles, const int32_t* num_tiles,
                          void* ys, hipStream_t s) {
-  unsigned grid = unsigned(max_tiles(d) * (d.H / BN));
+  unsigned grid = grid8(max_tiles(d) * kSub * (d.H / BN));
   hipLaunchKernelGGL(k_down, dim3(grid), dim3(NT), 0, s, static_cast<const bf16_t*>(a),
                      static_cast<const bf16_t*>(wd), tiles, num_tiles, static_cast<bf16_t*>(ys), int(d.H), int(d.F));
   return hipGetLastError();
 }
 
-hipError_t ffn_bwd_dact_bf16(const Dims& d, const void* dys, const void* wd, const void* g, const void* u,
+hipError_t ffn_bwd_dact_small(const Dims& d, const void* dys, const void* wd, const void* g, const void* u,
                              const int32_t* tiles, const int32_t* num_tiles, void* dg, void* du, hipStream_t s) {
-  unsigned grid = unsigned(max_tiles(d) * (d.F / BN));
+  unsigned grid = grid8(max_tiles(d) * kSub * (d.F / BN));
   hipLaunchKernelGGL(k_dact, dim3(grid), dim3(NT), 0, s, static_cast<const bf16_t*>(dys),
                      static_cast<const bf16_t*>(wd), static_cast<const bf16_t*>(g), static_cast<const bf16_t*>(u),
                      tiles, num_tiles, static_cast<bf16_t*>(dg), static_cast<bf16_t*>(du), int(d.H), int(d.F));
   return hipGetLastError();
 }
 
-hipError_t ffn_bwd_dx_bf16(const Dims& d, const void* dg, const void* du, const void* wg, const void* wu,
+hipError_t ffn_bwd_dx_small(const Dims& d, const void* dg, const void* du, const void* wg, const void* wu,
                            const int32_t* tiles, const int32_t* num_tiles, void* dxs, hipStream_t s) {
-  unsigned grid = unsigned(max_tiles(d) * (d.H / BN));
+  unsigned grid = grid8(max_tiles(d) * kSub * (d.H / BN));
   hipLaunchKernelGGL(k_dx, dim3(grid), dim3(NT), 0, s, static_cast<const bf16_t*>(dg), static_cast<const bf16_t*>(du),
                      static_cast<const bf16_t*>(wg), static_cast<const bf16_t*>(wu), tiles, num_tiles,
                      static_cast<bf16_t*>(dxs), int(d.H), int(d.F));
   return hipGetLastError();
 }
 
-hipError_t ffn_bwd_dw_bf16(const Dims& d, const void* xs, const void* a, const void* dys, const void* dg,
+hipError_t ffn_bwd_dw_small(const Dims& d, const void* xs, const void* a, const void* dys, const void* dg,
                            const void* du, const int32_t* offsets, float* dwg, float* dwu, float* dwd, hipStream_t s) {
-  unsigned grid = unsigned(3 * d.E * (d.H / BM) * (d.F / BN));
+  unsigned grid = grid8(3 * d.E * (d.H / BM) * (d.F / BN));
   hipLaunchKernelGGL(k_dw, dim3(grid), dim3(NT), 0, s, static_cast<const bf16_t*>(xs), static_cast<const bf16_t*>(a),
                      static_cast<const bf16_t*>(dys), static_cast<const bf16_t*>(dg), static_cast<const bf16_t*>(du),
                      offsets, dwg, dwu, dwd, int(d.H), int(d.F), int(d.E));

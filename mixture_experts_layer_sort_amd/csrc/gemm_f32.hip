@@ -137,19 +137,32 @@ __global__ __launch_bounds__(256) void k_dw_f32(const float* __restrict__ xs, co
 
 namespace moe_launch {
 
-hipError_t ffn_gate_up_bf16(const Dims&, const void*, const void*, const void*, const int32_t*, const int32_t*, void*,
-                            void*, void*, hipStream_t);
-hipError_t ffn_down_bf16(const Dims&, const void*, const void*, const int32_t*, const int32_t*, void*, hipStream_t);
-hipError_t ffn_bwd_dact_bf16(const Dims&, const void*, const void*, const void*, const void*, const int32_t*,
-                             const int32_t*, void*, void*, hipStream_t);
-hipError_t ffn_bwd_dx_bf16(const Dims&, const void*, const void*, const void*, const void*, const int32_t*,
-                           const int32_t*, void*, hipStream_t);
-hipError_t ffn_bwd_dw_bf16(const Dims&, const void*, const void*, const void*, const void*, const void*,
-                           const int32_t*, float*, float*, float*, hipStream_t);
+// bf16 tile shapes: 256 x 256 LDS-DMA kernels (gemm_bf16_big.hip) and
+// 128 x 128 register-staged kernels (gemm_bf16_small.hip).
+#define MOE_BF16_SHAPE(name, ...)                 \
+  hipError_t name##_big(const Dims&, __VA_ARGS__); \
+  hipError_t name##_small(const Dims&, __VA_ARGS__);
+MOE_BF16_SHAPE(ffn_gate_up, const void*, const void*, const void*, const int32_t*, const int32_t*, void*, void*, void*,
+               hipStream_t)
+MOE_BF16_SHAPE(ffn_down, const void*, const void*, const int32_t*, const int32_t*, void*, hipStream_t)
+MOE_BF16_SHAPE(ffn_bwd_dact, const void*, const void*, const void*, const void*, const int32_t*, const int32_t*, void*,
+               void*, hipStream_t)
+MOE_BF16_SHAPE(ffn_bwd_dx, const void*, const void*, const void*, const void*, const int32_t*, const int32_t*, void*,
+               hipStream_t)
+MOE_BF16_SHAPE(ffn_bwd_dw, const void*, const void*, const void*, const void*, const void*, const int32_t*, float*,
+               float*, float*, hipStream_t)
+#undef MOE_BF16_SHAPE
+
+// The 256 x 256 shape pays off once each workgroup's contraction is long
+// enough to amortise its prologue and 132 KiB LDS footprint (one workgroup
+// per CU); measured on MI355X it wins from contraction length 4096 on.
+static bool big_shape(int64_t k_len) { return k_len >= 4096; }
 
 hipError_t ffn_gate_up(const Dims& d, const void* xs, const void* wg, const void* wu, const int32_t* tiles,
                        const int32_t* num_tiles, void* g, void* u, void* a, hipStream_t s) {
-  if (d.dtype == MOE_BF16) return ffn_gate_up_bf16(d, xs, wg, wu, tiles, num_tiles, g, u, a, s);
+  if (d.dtype == MOE_BF16)
+    return big_shape(d.H) ? ffn_gate_up_big(d, xs, wg, wu, tiles, num_tiles, g, u, a, s)
+                          : ffn_gate_up_small(d, xs, wg, wu, tiles, num_tiles, g, u, a, s);
   unsigned grid = unsigned(max_tiles(d) * (d.F / TN));
   hipLaunchKernelGGL(k_gate_up_f32, dim3(grid), dim3(256), 0, s, static_cast<const float*>(xs),
                      static_cast<const float*>(wg), static_cast<const float*>(wu), tiles, num_tiles,
@@ -159,7 +172,9 @@ hipError_t ffn_gate_up(const Dims& d, const void* xs, const void* wg, const void
 
 hipError_t ffn_down(const Dims& d, const void* a, const void* wd, const int32_t* tiles, const int32_t* num_tiles,
                     void* ys, hipStream_t s) {
-  if (d.dtype == MOE_BF16) return ffn_down_bf16(d, a, wd, tiles, num_tiles, ys, s);
+  if (d.dtype == MOE_BF16)
+    return big_shape(d.F) ? ffn_down_big(d, a, wd, tiles, num_tiles, ys, s)
+                          : ffn_down_small(d, a, wd, tiles, num_tiles, ys, s);
   unsigned grid = unsigned(max_tiles(d) * (d.H / TN));
   hipLaunchKernelGGL(k_down_f32, dim3(grid), dim3(256), 0, s, static_cast<const float*>(a),
                      static_cast<const float*>(wd), tiles, num_tiles, static_cast<float*>(ys), int(d.H), int(d.F));
@@ -168,7 +183,9 @@ hipError_t ffn_down(const Dims& d, const void* a, const void* wd, const int32_t*
 
 hipError_t ffn_bwd_dact(const Dims& d, const void* dys, const void* wd, const void* g, const void* u,
                         const int32_t* tiles, const int32_t* num_tiles, void* dg, void* du, hipStream_t s) {
-  if (d.dtype == MOE_BF16) return ffn_bwd_dact_bf16(d, dys, wd, g, u, tiles, num_tiles, dg, du, s);
+  if (d.dtype == MOE_BF16)
+    return big_shape(d.H) ? ffn_bwd_dact_big(d, dys, wd, g, u, tiles, num_tiles, dg, du, s)
+                          : ffn_bwd_dact_small(d, dys, wd, g, u, tiles, num_tiles, dg, du, s);
   unsigned grid = unsigned(max_tiles(d) * (d.F / TN));
   hipLaunchKernelGGL(k_dact_f32, dim3(grid), dim3(256), 0, s, static_cast<const float*>(dys),
                      static_cast<const float*>(wd), static_cast<const float*>(g), static_cast<const float*>(u), tiles,
@@ -178,7 +195,9 @@ hipError_t ffn_bwd_dact(const Dims& d, const void* dys, const void* wd, const vo
 
 hipError_t ffn_bwd_dx(const Dims& d, const void* dg, const void* du, const void* wg, const void* wu,
                       const int32_t* tiles, const int32_t* num_tiles, void* dxs, hipStream_t s) {
-  if (d.dtype == MOE_BF16) return ffn_bwd_dx_bf16(d, dg, du, wg, wu, tiles, num_tiles, dxs, s);
+  if (d.dtype == MOE_BF16)
+    return big_shape(2 * d.F) ? ffn_bwd_dx_big(d, dg, du, wg, wu, tiles, num_tiles, dxs, s)
+                              : ffn_bwd_dx_small(d, dg, du, wg, wu, tiles, num_tiles, dxs, s);
   unsigned grid = unsigned(max_tiles(d) * (d.H / TN));
   hipLaunchKernelGGL(k_dx_f32, dim3(grid), dim3(256), 0, s, static_cast<const float*>(dg),
                      static_cast<const float*>(du), static_cast<const float*>(wg), static_cast<const float*>(wu), tiles,
@@ -188,7 +207,9 @@ hipError_t ffn_bwd_dx(const Dims& d, const void* dg, const void* du, const void*
 
 hipError_t ffn_bwd_dw(const Dims& d, const void* xs, const void* a, const void* dys, const void* dg, const void* du,
                       const int32_t* offsets, float* dwg, float* dwu, float* dwd, hipStream_t s) {
-  if (d.dtype == MOE_BF16) return ffn_bwd_dw_bf16(d, xs, a, dys, dg, du, offsets, dwg, dwu, dwd, s);
+  if (d.dtype == MOE_BF16)
+    return big_shape(d.NK() / d.E) ? ffn_bwd_dw_big(d, xs, a, dys, dg, du, offsets, dwg, dwu, dwd, s)
+                                   : ffn_bwd_dw_small(d, xs, a, dys, dg, du, offsets, dwg, dwu, dwd, s);
   unsigned grid = unsigned(3 * d.E * (d.H / TN) * (d.F / TN));
   hipLaunchKernelGGL(k_dw_f32, dim3(grid), dim3(256), 0, s, static_cast<const float*>(xs),
                      static_cast<const float*>(a), static_cast<const float*>(dys), static_cast<const float*>(dg),
