@@ -1,6 +1,6 @@
 """Benchmark of the dropless top-k MoE layer (forward + backward) on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
 
 A step is one pass of the whole layer over one batch of synthetic input:
 route, routing metadata, gather, gate/up and down grouped GEMMs, combine,
@@ -40,11 +40,11 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC = {
     "sources": "665061b15e16fb2a",
     "bytes": {
-        ("c1", "gate_up"): 340195935,
-        ("c1", "down"): 142611949,
-        ("c1", "dact"): 374894225,
-        ("c1", "dx"): 272249331,
-        ("c1", "dw"): 352595987,
+        ("bf16_n16384_h512_f1024_e8_k2", "gate_up"): 340195935,
+        ("bf16_n16384_h512_f1024_e8_k2", "down"): 142611949,
+        ("bf16_n16384_h512_f1024_e8_k2", "dact"): 374894225,
+        ("bf16_n16384_h512_f1024_e8_k2", "dx"): 272249331,
+        ("bf16_n16384_h512_f1024_e8_k2", "dw"): 352595987,
     },
 }
 
@@ -71,7 +71,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--config", default="c1")
+    p.add_argument("--config", default="bf16_n16384_h512_f1024_e8_k2")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--copy-calibration", action="store_true",

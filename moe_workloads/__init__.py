@@ -26,7 +26,7 @@ from __future__ import annotations
 
 import dataclasses
 import math
-from typing import Optional
+from typing import Dict, Optional
 
 import torch
 
@@ -63,18 +63,31 @@ class MoEConfig:
         return 12 * self.H * self.F * self.NK
 
 
-CONFIGS = {
-    "c0": MoEConfig("c0", N=32, H=128, F=256, E=4, K=2, dtype="f32",
-                    description="tiny fp32 MoE, N=32 H=128 F=256 E=4 K=2"),
-    "c1": MoEConfig("c1", N=16384, H=512, F=1024, E=8, K=2, dtype="bf16",
-                    description="bf16 dropless MoE fwd+bwd, N=16384 (seq 1024 x batch 16) H=512 F=1024 E=8 K=2"),
-    "c2": MoEConfig("c2", N=16384, H=2048, F=1408, E=64, K=6, dtype="bf16", zipf_s=1.2, zipf_tau=1.25,
-                    description="skewed-routing bf16 fwd+bwd, N=16384 H=2048 F=1408 E=64 K=6, Zipf(1.2) logit bias"),
-    "c3": MoEConfig("c3", N=8192, H=7168, F=2048, E=256, K=8, dtype="bf16", backward=False,
-                    description="wide-expert bf16 forward, N=8192 H=7168 F=2048 E=256 K=8 (22.5 GB weights)"),
-    "c4": MoEConfig("c4", N=16384, H=4096, F=14336, E=8, K=2, dtype="bf16",
-                    description="large-FFN bf16 deterministic fwd+bwd, N=16384 H=4096 F=14336 E=8 K=2"),
-}
+def _cfgs(*cfgs: MoEConfig) -> Dict[str, MoEConfig]:
+    return {c.name: c for c in cfgs}
+
+
+# The workloads: named by dtype, routing and sizes.
+CONFIGS = _cfgs(
+    MoEConfig("f32_n32_h128_f256_e4_k2", N=32, H=128, F=256, E=4, K=2, dtype="f32",
+              description="tiny fp32 MoE, N=32 H=128 F=256 E=4 K=2"),
+    MoEConfig("bf16_n16384_h512_f1024_e8_k2", N=16384, H=512, F=1024, E=8, K=2, dtype="bf16",
+              description="bf16 dropless MoE fwd+bwd, N=16384 (seq 1024 x batch 16) H=512 F=1024 E=8 K=2"),
+    MoEConfig("bf16_skewed_n16384_h2048_f1408_e64_k6", N=16384, H=2048, F=1408, E=64, K=6, dtype="bf16",
+              zipf_s=1.2, zipf_tau=1.25,
+              description="skewed-routing bf16 fwd+bwd, N=16384 H=2048 F=1408 E=64 K=6, Zipf(1.2) logit bias"),
+    MoEConfig("bf16_fwd_n8192_h7168_f2048_e256_k8", N=8192, H=7168, F=2048, E=256, K=8, dtype="bf16",
+              backward=False,
+              description="wide-expert bf16 forward, N=8192 H=7168 F=2048 E=256 K=8 (22.5 GB weights)"),
+    MoEConfig("bf16_n16384_h4096_f14336_e8_k2", N=16384, H=4096, F=14336, E=8, K=2, dtype="bf16",
+              description="large-FFN bf16 deterministic fwd+bwd, N=16384 H=4096 F=14336 E=8 K=2"),
+)
+
+TINY = CONFIGS["f32_n32_h128_f256_e4_k2"]
+BASE = CONFIGS["bf16_n16384_h512_f1024_e8_k2"]
+SKEWED = CONFIGS["bf16_skewed_n16384_h2048_f1408_e64_k6"]
+WIDE = CONFIGS["bf16_fwd_n8192_h7168_f2048_e256_k8"]
+LARGE = CONFIGS["bf16_n16384_h4096_f14336_e8_k2"]
 
 # Small shapes for parity tests: several tiles per expert, ragged tails,
 # empty experts, K=1, K=E, E=1 and the fp32 path.

@@ -14,13 +14,13 @@ import numpy as np
 import pytest
 import torch
 
-from moe_workloads import CONFIGS, TEST_CONFIGS, MoEConfig
+from moe_workloads import BASE, CONFIGS, SKEWED, TEST_CONFIGS, TINY, MoEConfig
 from oracle import moe_oracle as O
 from tests.gpu_common import (assert_close, assignment_mismatch, gpu_inputs, oracle_fwd, store_of, sync, to_np)
 
 pytestmark = pytest.mark.gpu
 
-SMALL = [CONFIGS["c0"]] + list(TEST_CONFIGS.values())
+SMALL = [TINY] + list(TEST_CONFIGS.values())
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -53,7 +53,7 @@ def test_route_matches_oracle(cfg):
     assert np.max(np.abs(g[good] - of["gates"][good])) <= 2e-6
 
 
-@pytest.mark.parametrize("cfg", SMALL + [CONFIGS["c1"], CONFIGS["c2"]], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", SMALL + [BASE, SKEWED], ids=lambda c: c.name)
 def test_permute_meta_bit_exact(cfg):
     """Given the oracle's assignment, counts, offsets, the stable sort, its
     inverse and the tile list are bit-exact."""
@@ -128,7 +128,7 @@ def test_empty_experts_present_in_skewed_case():
     assert np.sum(oracle_fwd(cfg, cpu)["counts"] == 0) > 0
 
 
-@pytest.mark.parametrize("cfg", [TEST_CONFIGS["t_ragged"], TEST_CONFIGS["t_skew"], CONFIGS["c0"]],
+@pytest.mark.parametrize("cfg", [TEST_CONFIGS["t_ragged"], TEST_CONFIGS["t_skew"], TINY],
                          ids=lambda c: c.name)
 def test_bitwise_reproducible(cfg):
     """Three runs (one with outputs pre-poisoned) give identical bytes."""

@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 import torch
 
-from moe_workloads import CONFIGS, TEST_CONFIGS, MoEConfig, make_inputs
+from moe_workloads import TEST_CONFIGS, TINY, MoEConfig, make_inputs
 from oracle import moe_oracle as O
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -96,7 +96,7 @@ def _rel(a, b):
     return float(np.max(np.abs(a - b)) / max(1e-30, np.max(np.abs(b))))
 
 
-SMALL = [CONFIGS["c0"], MoEConfig("p_bias", N=24, H=64, F=64, E=6, K=3, dtype="f32", zipf_s=1.2, zipf_tau=1.25),
+SMALL = [TINY, MoEConfig("p_bias", N=24, H=64, F=64, E=6, K=3, dtype="f32", zipf_s=1.2, zipf_tau=1.25),
          MoEConfig("p_k1", N=20, H=64, F=32, E=5, K=1, dtype="f32"),
          MoEConfig("p_keqe", N=16, H=64, F=32, E=3, K=3, dtype="f32")]
 
@@ -273,7 +273,7 @@ def test_forward_e1_is_textbook_swiglu_and_zero_down_gives_zero():
 
 
 def test_forward_token_permutation_equivariance():
-    cfg = CONFIGS["c0"]
+    cfg = TINY
     inp = _inputs(cfg)
     perm = np.random.default_rng(5).permutation(cfg.N)
     a = O.forward(inp["x"], inp["w_r"], inp["w_gate"], inp["w_up"], inp["w_down"], cfg.K, store="f64")
@@ -282,7 +282,7 @@ def test_forward_token_permutation_equivariance():
 
 
 def test_forward_expert_relabelling_invariance():
-    cfg = CONFIGS["c0"]
+    cfg = TINY
     inp = _inputs(cfg)
     perm = np.array([2, 0, 3, 1])
     a = O.forward(inp["x"], inp["w_r"], inp["w_gate"], inp["w_up"], inp["w_down"], cfg.K, store="f64")
@@ -340,7 +340,7 @@ def test_backward_matches_dense_masked_autograd(cfg):
 
 
 def test_backward_finite_differences():
-    cfg = CONFIGS["c0"]
+    cfg = TINY
     inp = _inputs(cfg, 0)
     fwd = O.forward(inp["x"], inp["w_r"], inp["w_gate"], inp["w_up"], inp["w_down"], cfg.K, store="f64")
     gap = min_topk_gap(fwd["logits"], cfg.K)
