@@ -228,12 +228,18 @@ def swiglu_expert(xs: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray
 # whole layer
 # --------------------------------------------------------------------------
 
-def forward(x, w_r, w_gate, w_up, w_down, K: int, bias=None, store: str = "bf16", tile_m: int = 128):
+def forward(x, w_r, w_gate, w_up, w_down, K: int, bias=None, store: str = "bf16", tile_m: int = 128,
+            topk=None):
     """Forward pass of the layer; returns every intermediate in a dict.
 
     Steps in the pages' order: logits, top-K, gates, metadata (histogram,
     cumsum, stable sort), gather, per-expert SwiGLU on the expert's rows,
     gate-weighted index_add combine back to token order.
+
+    ``topk`` [N, K] (optional) replaces the top-K selection with a given
+    assignment of K distinct experts per token, in slot order, for checks
+    made "given the same assignment"; the gates are still the softmax over
+    the logits of the given experts.
     """
     assert store in STORE_TYPES
     x = as_f64(x)
@@ -245,7 +251,12 @@ def forward(x, w_r, w_gate, w_up, w_down, K: int, bias=None, store: str = "bf16"
     F = wg_all.shape[2]
 
     logits = router_logits(x, w_r, bias)
-    topk = topk_experts(logits, K)
+    if topk is None:
+        topk = topk_experts(logits, K)
+    else:
+        topk = np.ascontiguousarray(np.asarray(topk).reshape(N, K)).astype(np.int32)
+        assert all(len(set(r.tolist())) == K for r in topk), "a token's experts must be distinct"
+        assert topk.min() >= 0 and topk.max() < E
     gates = rho32(gates_topk_softmax(logits, topk), store)
     counts, offsets, sorted_flat, inv = routing_metadata(topk, E)
     tiles = tile_list(counts, offsets, tile_m)
@@ -559,3 +570,69 @@ def rounding_bands(fwd: dict, bwd: Optional[dict] = None, dy=None) -> dict:
            + 8 * U32 * (np.abs(bwd["dxs"][inv2]).sum(axis=1) + np.abs(bwd["dlogits"]) @ np.abs(w_r.T)))
     b["dx"] = bf16_flip(dxp, bwd["dx"], sdx)
     return b
+
+
+# --------------------------------------------------------------------------
+# slices of the expert weight gradients (sampled checks at full size)
+# --------------------------------------------------------------------------
+
+def weight_grad_slices(x, dy, topk, gates, e: int, w_gate_e, w_up_e, w_down_e, cols, store: str = "bf16") -> dict:
+    """Columns ``cols`` of dW_gate[e] and dW_up[e] and rows ``cols`` of
+    dW_down[e], with their rounding bands (bf16 storage), from the layer's
+    inputs and a given assignment (topk [N, K], gates [N, K]).
+
+    The f-th column of G, U, A, dG and dU over expert e's rows is all these
+    need, so the cost is a few matrix-vector products per column:
+        rows   = the (n, k) with topk[n, k] == e;   xs = x[n], g = gates[n, k]
+        G[:, f] = xs.Wg[:, f]   U[:, f] = xs.Wu[:, f]   A = silu(G) U
+        dys    = g dy[n]        dA[:, f] = dys.Wd[f, :]
+        dG     = dA U silu'(G)  dU = dA silu(G)
+        dW_gate[:, f] = xs^T dG   dW_up[:, f] = xs^T dU   dW_down[f, :] = A^T dys
+    with the same storage rounding points as ``forward`` / ``backward``; the
+    bands follow ``rounding_bands`` restricted to these columns (every band
+    term of a column depends on that column alone).  Returns dw_gate [H, C],
+    dw_up [H, C], dw_down [C, H] (C = len(cols)) and band_* of the same shapes.
+    """
+    x, dy = as_f64(x), as_f64(dy)
+    topk = np.asarray(topk)
+    N, K = topk.shape
+    gflat = as_f64(gates).reshape(-1)
+    flat = np.nonzero(topk.reshape(-1) == e)[0]
+    tok = flat // K
+    cols = np.asarray(cols, dtype=np.int64)
+    wg = as_f64(w_gate_e)[:, cols]
+    wu = as_f64(w_up_e)[:, cols]
+    wd = as_f64(w_down_e)[cols, :]
+    H = x.shape[1]
+    xs = x[tok]
+    dysp = gflat[flat][:, None] * dy[tok]
+    dys = rho(dysp, store)
+    Gp, Up = xs @ wg, xs @ wu
+    G, U = rho(Gp, store), rho(Up, store)
+    ap = silu(G) * U
+    A = rho(ap, store)
+    dA = dys @ wd.T
+    sg = sigmoid(G)
+    dgp = dA * U * sg * (1.0 + G * (1.0 - sg))
+    dup = dA * (G * sg)
+    dG, dU = rho(dgp, store), rho(dup, store)
+    out = dict(dw_gate=xs.T @ dG, dw_up=xs.T @ dU, dw_down=A.T @ dys)
+    if store != "bf16":
+        for k in ("dw_gate", "dw_up", "dw_down"):
+            out["band_" + k] = np.zeros_like(out[k])
+        return out
+    bG = bf16_flip(Gp, G, gemm_sigma(xs, wg))
+    bU = bf16_flip(Up, U, gemm_sigma(xs, wu))
+    d1, d2 = _silu_d1(G), _silu_d2(G)
+    bA = bf16_flip(ap, A, np.abs(U * d1) * bG + np.abs(silu(G)) * bU + 16 * U32 * np.abs(ap))
+    bdys = bf16_flip(dysp, dys, 8 * U32 * np.abs(dysp))
+    sdA = gemm_sigma(dys, wd.T) + prop(bdys, wd.T)
+    bdG = bf16_flip(dgp, dG, np.abs(U * d1) * sdA + np.abs(dA * d1) * bU + np.abs(dA * U * d2) * bG
+                    + 16 * U32 * np.abs(dgp))
+    bdU = bf16_flip(dup, dU, np.abs(silu(G)) * sdA + np.abs(dA * d1) * bG + 16 * U32 * np.abs(dup))
+    out["band_dw_gate"] = prop(bdG.T, xs).T + gemm_sigma(xs.T, dG) + 2 * U32 * np.abs(out["dw_gate"])
+    out["band_dw_up"] = prop(bdU.T, xs).T + gemm_sigma(xs.T, dU) + 2 * U32 * np.abs(out["dw_up"])
+    out["band_dw_down"] = (prop(bA.T, dys) + prop(bdys.T, A).T + gemm_sigma(A.T, dys)
+                           + 2 * U32 * np.abs(out["dw_down"]))
+    assert out["dw_gate"].shape == (H, cols.size)
+    return out

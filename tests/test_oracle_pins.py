@@ -428,6 +428,66 @@ def test_closed_form_fixture():
 # mutation tests: plant a mistake in the oracle, a pin must fail
 # --------------------------------------------------------------------------
 
+
+# --------------------------------------------------------------------------
+# given assignment, and weight-gradient slices (used by the full-size checks)
+# --------------------------------------------------------------------------
+
+def test_forward_given_assignment_matches_bruteforce():
+    """forward(topk=...) with an arbitrary assignment of distinct experts:
+    per token, y = sum_k softmax(l[sel])_k FFN_{sel_k}(x), brute force."""
+    cfg = MoEConfig("p_given", N=12, H=64, F=32, E=5, K=2, dtype="f32", zipf_s=1.2, zipf_tau=1.25)
+    inp = _inputs(cfg)
+    rng = np.random.default_rng(5)
+    topk = np.stack([rng.permutation(cfg.E)[:cfg.K] for _ in range(cfg.N)])
+    f = O.forward(inp["x"], inp["w_r"], inp["w_gate"], inp["w_up"], inp["w_down"], cfg.K, bias=inp["bias"],
+                  store="f64", topk=topk)
+    assert np.array_equal(f["topk"], topk)
+    for n in range(cfg.N):
+        l = [sum(inp["x"][n, h] * inp["w_r"][h, e] for h in range(cfg.H)) + inp["bias"][e] for e in range(cfg.E)]
+        z = [math.exp(l[e]) for e in topk[n]]
+        ref = np.zeros(cfg.H)
+        for k, e in enumerate(topk[n]):
+            a = inp["x"][n] @ inp["w_gate"][e]
+            ref += z[k] / sum(z) * ((a / (1 + np.exp(-a)) * (inp["x"][n] @ inp["w_up"][e])) @ inp["w_down"][e])
+        assert np.allclose(f["y"][n], ref, rtol=1e-12, atol=1e-12)
+    # the own selection passed back in changes nothing
+    g = O.forward(inp["x"], inp["w_r"], inp["w_gate"], inp["w_up"], inp["w_down"], cfg.K, bias=inp["bias"],
+                  store="f64")
+    h = O.forward(inp["x"], inp["w_r"], inp["w_gate"], inp["w_up"], inp["w_down"], cfg.K, bias=inp["bias"],
+                  store="f64", topk=g["topk"])
+    assert np.array_equal(g["y"], h["y"])
+
+
+@pytest.mark.parametrize("store", ["bf16", "f64"])
+def test_weight_grad_slices_match_whole_layer(store):
+    """Columns of dW_gate / dW_up and rows of dW_down (and their bands) from
+    weight_grad_slices equal the pinned whole-layer backward's, including an
+    expert with no rows (exact zeros)."""
+    cfg = TEST_CONFIGS["t_skew"]
+    inp = _inputs(cfg, seed=2)
+    inp_dy = O.as_f64(make_inputs(cfg, 2, with_dy=True)["dy"])
+    f = O.forward(inp["x"], inp["w_r"], inp["w_gate"], inp["w_up"], inp["w_down"], cfg.K, bias=inp["bias"],
+                  store=store)
+    b = O.backward(f, inp_dy)
+    bands = O.rounding_bands(f, b, inp_dy) if store == "bf16" else None
+    empty = int(np.where(f["counts"] == 0)[0][0])
+    hot = int(np.argmax(f["counts"]))
+    cols = [0, 7, cfg.F - 1]
+    for e in (hot, empty, int(np.argsort(f["counts"])[cfg.E // 2])):
+        s = O.weight_grad_slices(inp["x"], inp_dy, f["topk"], f["gates"], e, inp["w_gate"][e], inp["w_up"][e],
+                                 inp["w_down"][e], cols, store)
+        assert np.allclose(s["dw_gate"], b["dw_gate"][e][:, cols], rtol=1e-12, atol=1e-12)
+        assert np.allclose(s["dw_up"], b["dw_up"][e][:, cols], rtol=1e-12, atol=1e-12)
+        assert np.allclose(s["dw_down"], b["dw_down"][e][cols, :], rtol=1e-12, atol=1e-12)
+        if e == empty:
+            assert not s["dw_gate"].any() and not s["dw_down"].any()
+        if bands is not None:
+            assert np.allclose(s["band_dw_gate"], bands["dw_gate"][e][:, cols], rtol=1e-9, atol=1e-15)
+            assert np.allclose(s["band_dw_up"], bands["dw_up"][e][:, cols], rtol=1e-9, atol=1e-15)
+            assert np.allclose(s["band_dw_down"], bands["dw_down"][e][cols, :], rtol=1e-9, atol=1e-15)
+
+
 def _pins_pass():
     """Run a compact set of pins; True when all hold."""
     try:
