@@ -82,6 +82,33 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
 __device__ __forceinline__ float sigmoid_f32(float g) { return 1.0f / (1.0f + __expf(-g)); }
 
+// The expert of rank p when experts are ordered by row count, largest first
+// (equal counts: lower id first), from offsets [E+1].  The weight-gradient
+// workgroups take their expert in this order, so the longest contractions
+// are dispatched first and spread over every XCD instead of forming a tail.
+// s: 16-byte aligned LDS scratch of at least MOE_MAX_EXPERTS + 1 ints; the
+// call holds two barriers and leaves s free for reuse.
+template <int NT>
+__device__ __forceinline__ int expert_of_rank(const int32_t* __restrict__ offsets, int E, int p, int* s) {
+  const int E4 = (E + 3) & ~3;
+  for (int i = threadIdx.x; i < E4; i += NT) s[i] = i < E ? offsets[i + 1] - offsets[i] : -1;
+  __syncthreads();
+  for (int j = threadIdx.x; j < E; j += NT) {
+    const int c = s[j];
+    int above = 0;
+    for (int i = 0; i < E4; i += 4) {
+      const int4 v = *reinterpret_cast<const int4*>(s + i);
+      above += (v.x > c || (v.x == c && i < j)) + (v.y > c || (v.y == c && i + 1 < j)) +
+               (v.z > c || (v.z == c && i + 2 < j)) + (v.w > c || (v.w == c && i + 3 < j));
+    }
+    if (above == p) s[MOE_MAX_EXPERTS] = j;
+  }
+  __syncthreads();
+  const int e = s[MOE_MAX_EXPERTS];
+  __syncthreads();
+  return e;
+}
+
 }  // namespace moe
 
 // Host-side launch helpers (defined in the kernel sources).

@@ -472,11 +472,12 @@ __global__ __launch_bounds__(NT, 2) void k_dw(const bf16_t* __restrict__ xs, con
                                                float* __restrict__ dwd, int H, int F, int E) {
   __shared__ __attribute__((aligned(16))) char lds[kLds2];
   const int tpe = (H / BM) * (F / BN);  // output tiles per expert and problem
-  const int blk = xcd_block(3 * E * tpe);
-  if (blk < 0) return;
-  const int prob = blk / (E * tpe);
-  const int rem = blk % (E * tpe);
-  const int e = rem / tpe, t = rem % tpe;
+  // experts largest first, each expert's 3 * tpe tiles consecutive: the
+  // hardware deals consecutive workgroups round-robin over the XCDs
+  const int blk = blockIdx.x;
+  if (blk >= 3 * E * tpe) return;  // grid rounded up to a multiple of 8
+  const int e = expert_of_rank<NT>(offsets, E, blk / (3 * tpe), reinterpret_cast<int*>(lds));
+  const int prob = (blk % (3 * tpe)) / tpe, t = blk % tpe;
   const bf16_t *L, *R;
   float* out;
   int P, Q, mt, nt;

@@ -20,7 +20,7 @@
 namespace {
 using namespace moe;
 
-constexpr int kChunk = 4096;           // flat entries per workgroup
+constexpr int kChunk = 1024;           // flat entries per workgroup
 constexpr int kPerWave = kChunk / 4;   // entries per wave (4 waves)
 
 __global__ __launch_bounds__(256) void k_meta_hist(const int32_t* __restrict__ topk, int32_t* __restrict__ blk_hist,
@@ -38,64 +38,105 @@ __global__ __launch_bounds__(256) void k_meta_hist(const int32_t* __restrict__ t
     }
   }
   __syncthreads();
-  if (tid < E) blk_hist[(int64_t)blockIdx.x * E + tid] = hist[tid];
+  if (tid < E) blk_hist[(int64_t)tid * gridDim.x + blockIdx.x] = hist[tid];  // expert-major [E][nblk]
 }
 
-// Inclusive scan of one int per thread over the 256 threads of the block.
-__device__ int block_inclusive_scan(int v, int* buf) {
-  const int tid = threadIdx.x;
-  buf[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    int add = (tid >= off) ? buf[tid - off] : 0;
-    __syncthreads();
-    buf[tid] += add;
-    __syncthreads();
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int t = __shfl_up(v, off, kWave);
+    if (lane >= off) v += t;
   }
-  int r = buf[tid];
-  __syncthreads();
-  return r;
+  return v;
 }
 
-__global__ __launch_bounds__(256) void k_meta_scan(int32_t* __restrict__ blk, int32_t* __restrict__ counts,
-                                                   int32_t* __restrict__ offsets, int32_t* __restrict__ tiles,
-                                                   int32_t* __restrict__ num_tiles, int nblk, int E, int NK,
-                                                   int tile_m) {
-  __shared__ int buf[256];
-  const int e = threadIdx.x;
-  // per-expert total, and each chunk's exclusive prefix within the expert
-  int total = 0;
-  if (e < E) {
-    for (int b = 0; b < nblk; ++b) {
-      int c = blk[(int64_t)b * E + e];
-      blk[(int64_t)b * E + e] = total;
-      total += c;
+// Exclusive prefix sums over the experts of vals[0, E) (E <= 256) by one
+// wave: lane l holds experts 4l .. 4l+3.  Writes the prefix to out[e] and
+// returns the grand total (in every lane).
+__device__ __forceinline__ int wave_excl_scan_experts(const int* vals, int* out, int E) {
+  const int lane = lane_id();
+  int v[4], ls = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 4 * lane + j;
+    v[j] = e < E ? vals[e] : 0;
+    ls += v[j];
+  }
+  const int incl = wave_incl_scan(ls);
+  int run = incl - ls;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 4 * lane + j;
+    if (e < E) out[e] = run;
+    run += v[j];
+  }
+  return __shfl(incl, kWave - 1, kWave);
+}
+
+// One workgroup of 16 waves.  blk [E][nblk] holds the chunk histograms on
+// entry and, on exit, the first sorted position of each (expert, chunk):
+// the expert's offset plus the counts of its earlier chunks.  Also writes
+// counts, offsets and the tile list (ceil(count / tile_m) tiles per expert,
+// experts ascending).
+constexpr int kScanWaves = 16;
+__global__ __launch_bounds__(kScanWaves * 64) void k_meta_scan(int32_t* __restrict__ blk, int32_t* __restrict__ counts,
+                                                              int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ tiles,
+                                                              int32_t* __restrict__ num_tiles, int nblk, int E, int NK,
+                                                              int tile_m) {
+  __shared__ int tot[MOE_MAX_EXPERTS], off[MOE_MAX_EXPERTS], ntl[MOE_MAX_EXPERTS], tfirst[MOE_MAX_EXPERTS];
+  const int w = threadIdx.x >> 6, lane = lane_id();
+  // expert totals (wave per expert; integer sums, order-free)
+  for (int e = w; e < E; e += kScanWaves) {
+    int sum = 0;
+    for (int b = lane; b < nblk; b += kWave) sum += blk[(int64_t)e * nblk + b];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, kWave);
+    if (lane == 0) {
+      tot[e] = sum;
+      ntl[e] = (sum + tile_m - 1) / tile_m;
     }
   }
-  int incl = block_inclusive_scan(e < E ? total : 0, buf);
-  int off = incl - (e < E ? total : 0);
-  if (e < E) {
-    counts[e] = total;
-    offsets[e] = off;
-    for (int b = 0; b < nblk; ++b) blk[(int64_t)b * E + e] += off;
+  __syncthreads();
+  if (w == 0) {
+    wave_excl_scan_experts(tot, off, E);
+    const int nt = wave_excl_scan_experts(ntl, tfirst, E);
+    if (lane == 0) {
+      *num_tiles = nt;
+      offsets[E] = NK;
+    }
   }
-  if (e == 0) offsets[E] = NK;
-  // tile list: ceil(count / tile_m) tiles per expert, experts ascending
-  int nt = (e < E) ? (total + tile_m - 1) / tile_m : 0;
-  int tincl = block_inclusive_scan(nt, buf);
-  int tfirst = tincl - nt;
-  for (int t = 0; t < nt; ++t) {
-    int64_t o = 3 * (int64_t)(tfirst + t);
-    tiles[o + 0] = e;
-    tiles[o + 1] = off + t * tile_m;
-    tiles[o + 2] = min(tile_m, total - t * tile_m);
+  __syncthreads();
+  // per-chunk bases: exclusive prefix over the chunks of each expert
+  for (int e = w; e < E; e += kScanWaves) {
+    int carry = off[e];
+    for (int b0 = 0; b0 < nblk; b0 += kWave) {
+      const int b = b0 + lane;
+      const int c = b < nblk ? blk[(int64_t)e * nblk + b] : 0;
+      const int incl = wave_incl_scan(c);
+      if (b < nblk) blk[(int64_t)e * nblk + b] = carry + incl - c;
+      carry += __shfl(incl, kWave - 1, kWave);
+    }
   }
-  if (e == 255) *num_tiles = tincl;
+  // counts, offsets and the tiles of expert e
+  for (int e = threadIdx.x; e < E; e += kScanWaves * 64) {
+    counts[e] = tot[e];
+    offsets[e] = off[e];
+    for (int t = 0; t < ntl[e]; ++t) {
+      const int64_t o = 3 * (int64_t)(tfirst[e] + t);
+      tiles[o + 0] = e;
+      tiles[o + 1] = off[e] + t * tile_m;
+      tiles[o + 2] = min(tile_m, tot[e] - t * tile_m);
+    }
+  }
 }
 
 __global__ __launch_bounds__(256) void k_meta_rank(const int32_t* __restrict__ topk, const int32_t* __restrict__ blk,
                                                    int32_t* __restrict__ sorted_flat, int32_t* __restrict__ inv, int NK,
                                                    int E, int key_bits) {
+  const int nblk = gridDim.x;
   __shared__ int wcount[4][MOE_MAX_EXPERTS];
   const int tid = threadIdx.x;
   const int w = tid >> 6;
@@ -128,7 +169,7 @@ __global__ __launch_bounds__(256) void k_meta_rank(const int32_t* __restrict__ t
   __syncthreads();
   // per-wave bases: chunk base of the expert + earlier waves of this chunk
   if (tid < E) {
-    int run = blk[(int64_t)blockIdx.x * E + tid];
+    int run = blk[(int64_t)tid * nblk + blockIdx.x];
     for (int q = 0; q < 4; ++q) {
       int c = wcount[q][tid];
       wcount[q][tid] = run;
@@ -175,8 +216,8 @@ hipError_t permute_meta(const Dims& d, const int32_t* topk, int32_t* sorted_flat
   hipLaunchKernelGGL(k_meta_hist, dim3(nblk), dim3(256), 0, s, topk, blk, NK, E);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_meta_scan, dim3(1), dim3(256), 0, s, blk, counts, offsets, tiles, num_tiles, nblk, E, NK,
-                     MOE_TILE_M);
+  hipLaunchKernelGGL(k_meta_scan, dim3(1), dim3(kScanWaves * 64), 0, s, blk, counts, offsets, tiles, num_tiles, nblk, E,
+                     NK, MOE_TILE_M);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   int key_bits = 0;

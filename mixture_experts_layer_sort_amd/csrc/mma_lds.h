@@ -1,0 +1,247 @@
+// MFMA tile machinery for gfx950 shared by the grouped GEMMs and the router:
+// a workgroup tile configuration, operand tiles moved from global memory
+// straight into LDS with the LDS DMA (global_load_lds, 16 bytes per lane),
+// conflict-free XOR-swizzled LDS layouts for K-contiguous and MN-contiguous
+// operands, MFMA fragment reads (16-byte loads, or the transposing
+// ds_read_b64_tr_b16 for MN-contiguous operands), the S-stage K loop on
+// v_mfma_f32_32x32x16_bf16 with float32 accumulation, and the accumulator
+// layout of the 32 x 32 result fragments.
+#pragma once
+#include "common.h"
+
+namespace moe_mma {
+using namespace moe;
+
+template <int BM_, int BN_, int WM_, int WN_, int MINB_, int BK_, int S_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int MINB = MINB_;  // workgroups per CU the registers must allow
+  static constexpr int BK = BK_;      // K depth of one pipeline stage (32 or 64)
+  static constexpr int S = S_;        // pipeline stages in LDS
+  static constexpr int NW = WM * WN, NT = 64 * NW;
+  static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
+  static constexpr int FM = TM / 32, FN = TN / 32;  // 32 x 32 fragments per wave
+  static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int DPT = STAGE / 1024 / NW;              // LDS DMA instructions per stage and wave
+  static constexpr int OP_BYTES = S * STAGE;
+  static constexpr int PITCH = BN + 8;                       // bf16 per staged output row
+  static constexpr int EPI_BYTES = BM * PITCH * 2;
+  static constexpr int DACT_BYTES = 2 * TM * PITCH * 2;      // G and U rows of one wave row
+  static constexpr int LDS_A = OP_BYTES > EPI_BYTES ? OP_BYTES : EPI_BYTES;
+  static constexpr int LDS = LDS_A > DACT_BYTES ? LDS_A : DACT_BYTES;
+  static constexpr int SUB = MOE_TILE_M / BM;  // workgroup row tiles per list tile
+  static_assert(STAGE % (1024 * NW) == 0, "every wave issues the same number of DMA instructions");
+  static_assert(BK == 32 || BK == 64, "stage depth");
+};
+
+#define LDS_AS __attribute__((address_space(3)))
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef short v8s_t __attribute__((ext_vector_type(8)));
+
+// 16 bytes per lane from global memory straight into LDS: the wave's 64
+// lanes fill lds_wave[0 .. 1024) in lane order (gfx950 LDS DMA).
+__device__ __forceinline__ void dma16(const bf16_t* g, char* lds_wave) {
+  __builtin_amdgcn_global_load_lds(g, (LDS_AS void*)lds_wave, 16, 0, 0);
+}
+
+// s_waitcnt with vmcnt(n) and the other counters free (gfx9 encoding:
+// vmcnt[3:0] at bits 3:0 and vmcnt[5:4] at bits 15:14, expcnt bits 6:4,
+// lgkmcnt bits 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// ---- K-contiguous tile: ROWS rows x BK k, 2*BK bytes per row.  16-byte chunk
+// c of row r sits at physical chunk c ^ fk(r), so the MFMA fragment reads (16
+// consecutive rows, one chunk, per 16-lane phase) hit 16 different 16-byte
+// bank slots.
+template <int BK>
+__device__ __forceinline__ int fk(int row) {
+  return BK == 64 ? ((row ^ (row >> 3)) & 7) : ((row >> 2) & 3);
+}
+
+// Issue the DMA of rows [0, ROWS) x k [0, BK) of a row-major matrix (k
+// contiguous, leading dimension ld).  Rows at or past rows_valid read row
+// rows_valid - 1 instead (their results are never stored).
+template <int ROWS, int BK, int NW>
+__device__ __forceinline__ void dma_kc(char* stage, const bf16_t* base, int64_t ld, int rows_valid) {
+  constexpr int CPR = BK / 8, RPI = 1024 / (2 * BK);  // chunks per row, rows per wave instruction
+  const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int i = w; i < ROWS / RPI; i += NW) {
+    const int row = i * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ fk<BK>(row);
+    const int rs = row < rows_valid ? row : rows_valid - 1;
+    dma16(base + (int64_t)rs * ld + c * 8, stage + i * 1024);
+  }
+}
+
+// MFMA operand fragment from a K-contiguous tile: lane l holds row
+// rbase + l%32, k = kk*16 + 8*(l/32) .. +7.
+template <int BK>
+__device__ __forceinline__ bf16x8_t frag_kc(const char* stage, int rbase, int kk) {
+  const int lane = lane_id();
+  const int row = rbase + (lane & 31);
+  const int c = kk * 2 + (lane >> 5);
+  return *reinterpret_cast<const bf16x8_t*>(stage + row * (2 * BK) + ((c ^ fk<BK>(row)) << 4));
+}
+
+// ---- MN-contiguous tile: BK k-rows x COLS columns, COLS*2 bytes per row.
+// 16-byte chunk c of row k sits at physical chunk c ^ fm(k), which makes the
+// transposing fragment reads (4 rows x 64 bytes per 32 lanes) conflict-free.
+__device__ __forceinline__ int fm(int k) { return 4 * (k & 3); }
+
+// Issue the DMA of k [0, BK) x columns [0, COLS) of a row-major matrix
+// (columns contiguous, leading dimension ld).  Columns [0, split) come from
+// base0 and [split, COLS) from base1 (both indexed by the tile column).  k
+// rows at or past k_valid and columns at or past cols_valid read clamped
+// positions (the caller zeroes or discards them).
+template <int COLS, int BK, int NW>
+__device__ __forceinline__ void dma_mn(char* stage, const bf16_t* base0, const bf16_t* base1, int split, int64_t ld,
+                                       int k_valid, int cols_valid) {
+  constexpr int CPR = COLS / 8, RPI = 1024 / (COLS * 2);  // chunks per row, rows per wave instruction
+  const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int i = w; i < BK / RPI; i += NW) {
+    const int k = i * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ fm(k);
+    const int ks = k < k_valid ? k : k_valid - 1;
+    const int cs = c * 8 < cols_valid ? c : (cols_valid >> 3) - 1;
+    const bf16_t* b = cs * 8 < split ? base0 : base1;
+    dma16(b + (int64_t)ks * ld + cs * 8, stage + i * 1024);
+  }
+}
+
+// MFMA operand fragment from an MN-contiguous tile with two transposing LDS
+// reads (ds_read_b64_tr_b16): within each 16-lane group, input lane j points
+// at 4 columns of row k0 + j/4 and output lane i receives the 4 k values of
+// one column.  Lane l ends up with column nbase + l%32, k = kk*16 + 8*(l/32)
+// .. +7, the same k order as frag_kc.
+template <int COLS>
+__device__ __forceinline__ bf16x8_t frag_mn(const char* stage, int nbase, int kk) {
+  constexpr int ROWB = COLS * 2;
+  const int lane = lane_id();
+  const int g = lane >> 4, i = lane & 15;
+  const int col = nbase + 16 * (g & 1) + 4 * (i & 3);
+  const int k0 = kk * 16 + 8 * (g >> 1) + (i >> 2);
+  const char* p0 = stage + k0 * ROWB + (((col >> 3) ^ fm(k0)) << 4) + (col & 7) * 2;
+  const char* p1 = stage + (k0 + 4) * ROWB + (((col >> 3) ^ fm(k0 + 4)) << 4) + (col & 7) * 2;
+  const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s_t*)p0);
+  const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s_t*)p1);
+  const v8s_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+template <class C>
+struct Acc {
+  f32x16_t a[C::FM][C::FN];
+};
+
+template <class C>
+__device__ __forceinline__ void zero_acc(Acc<C>& acc) {
+#pragma unroll
+  for (int mi = 0; mi < C::FM; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < C::FN; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc.a[mi][ni][r] = 0.f;
+}
+
+// One stage (BK deep) of the wave tile: acc[mi][ni] += A . B^T, with each
+// operand read as K-contiguous (ds_read_b128) or MN-contiguous (transposing
+// reads) fragments.  The fragments of k step kk+1 are requested before the
+// MFMAs of step kk are issued, so LDS latency overlaps the matrix cores.
+template <class C, bool A_MN, bool B_MN>
+__device__ __forceinline__ void load_frags(const char* sa, const char* sb, int kk, int wm, int wn,
+                                           bf16x8_t (&a)[C::FM], bf16x8_t (&b)[C::FN]) {
+#pragma unroll
+  for (int mi = 0; mi < C::FM; ++mi)
+    a[mi] = A_MN ? frag_mn<C::BM>(sa, wm * C::TM + mi * 32, kk) : frag_kc<C::BK>(sa, wm * C::TM + mi * 32, kk);
+#pragma unroll
+  for (int ni = 0; ni < C::FN; ++ni)
+    b[ni] = B_MN ? frag_mn<C::BN>(sb, wn * C::TN + ni * 32, kk) : frag_kc<C::BK>(sb, wn * C::TN + ni * 32, kk);
+}
+
+template <class C, bool A_MN, bool B_MN>
+__device__ __forceinline__ void mma_stage(const char* sa, const char* sb, Acc<C>& acc, int wm, int wn) {
+  constexpr int KK = C::BK / 16;
+  bf16x8_t a[2][C::FM], b[2][C::FN];
+  load_frags<C, A_MN, B_MN>(sa, sb, 0, wm, wn, a[0], b[0]);
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    const int cur = kk & 1;
+    if (kk + 1 < KK) load_frags<C, A_MN, B_MN>(sa, sb, kk + 1, wm, wn, a[cur ^ 1], b[cur ^ 1]);
+#pragma unroll
+    for (int mi = 0; mi < C::FM; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < C::FN; ++ni)
+        acc.a[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][mi], b[cur][ni], acc.a[mi][ni], 0, 0, 0);
+  }
+}
+
+// S-stage K loop.  ia(kt, stage) / ib(kt, stage) issue the LDS DMA of K tile
+// kt.  Tiles 0 .. S-2 are issued up front; at step kt every wave waits until
+// its own DMA of tile kt has landed (tiles kt+1 .. kt+S-2 stay in flight),
+// the barrier makes tile kt visible to all waves and retires step kt-1's
+// reads of the stage tile kt+S-1 now reuses, the DMA of tile kt+S-1 starts
+// and the block multiplies tile kt.  When the last tile holds only k_last
+// valid k rows (weight gradients), rows k_last.. of its A stage (an MN tile)
+// are zeroed before it is used.
+template <class C, bool A_MN, bool B_MN, class IA, class IB>
+__device__ __forceinline__ void k_loop(char* lds, Acc<C>& acc, int nk, IA ia, IB ib, int wm, int wn,
+                                       int k_last = C::BK) {
+  zero_acc(acc);
+  if (nk <= 0) return;
+#pragma unroll
+  for (int s = 0; s < C::S - 1; ++s)
+    if (s < nk) {
+      ia(s, lds + s * C::STAGE);
+      ib(s, lds + s * C::STAGE + C::A_BYTES);
+    }
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + C::S - 2 < nk)
+      wait_vm<C::DPT * (C::S - 2)>();
+    else
+      wait_vm<0>();
+    __syncthreads();
+    const int nxt = kt + C::S - 1;
+    if (nxt < nk) {
+      char* st = lds + (nxt % C::S) * C::STAGE;
+      ia(nxt, st);
+      ib(nxt, st + C::A_BYTES);
+    }
+    char* cur = lds + (kt % C::S) * C::STAGE;
+    if (A_MN && kt == nk - 1 && k_last < C::BK) {
+      constexpr int ROWB = C::BM * 2;
+      uint4* z = reinterpret_cast<uint4*>(cur + k_last * ROWB);
+      for (int i = threadIdx.x; i < (C::BK - k_last) * ROWB / 16; i += C::NT) z[i] = make_uint4(0, 0, 0, 0);
+      __syncthreads();
+    }
+    mma_stage<C, A_MN, B_MN>(cur, cur + C::A_BYTES, acc, wm, wn);
+  }
+  __syncthreads();
+}
+
+// Accumulator element r of fragment (mi, ni): MFMA 32x32 result layout
+// (column = lane % 32, rows in groups of 4 interleaved across the two lane
+// halves).  Offsets within the wave tile are compile-time constants added to
+// one per-lane base.
+__device__ __forceinline__ constexpr int frag_row(int mi, int r) { return mi * 32 + (r >> 2) * 8 + (r & 3); }
+template <class C>
+__device__ __forceinline__ int lane_row(int wm) { return wm * C::TM + (lane_id() >> 5) * 4; }
+template <class C>
+__device__ __forceinline__ int lane_col(int wn) { return wn * C::TN + (lane_id() & 31); }
+
+// Dynamic LDS above 64 KiB is enabled once per kernel (one static per
+// kernel, keyed by the kernel itself).
+template <auto Kern>
+hipError_t allow_lds(int bytes) {
+  static const hipError_t st =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(Kern), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  return st;
+}
+
+}  // namespace moe_mma

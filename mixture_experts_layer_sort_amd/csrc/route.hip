@@ -16,6 +16,7 @@
 //   (expert, h) per chunk, tokens ascending), then the chunk partials are
 //   summed in ascending chunk order.
 #include "common.h"
+#include "mma_lds.h"
 
 namespace {
 using namespace moe;
@@ -27,6 +28,74 @@ constexpr int kRouteTok = 32;  // tokens per workgroup
 template <int EPT>
 constexpr int route_hc() {
   return (8192 / (8 * EPT)) < 128 ? (8192 / (8 * EPT)) : 128;
+}
+
+// Top-K of one token's logits lg[0, E) (+ bias[e] if given) under the order
+// (logit desc, expert id asc), and the gates: softmax over the K selected
+// logits.  Called by a whole wave; lane k < K writes slot k of token n.
+// Each lane holds experts lane, lane+64, lane+128, lane+192; NaN logits rank
+// last; K rounds of a wave-wide arg-max pick the winners.
+__device__ __forceinline__ void wave_topk_gates(const float* __restrict__ lg, const float* __restrict__ bias, int E,
+                                                int K, int64_t n, int32_t* __restrict__ topk,
+                                                float* __restrict__ gates) {
+  const int lane = lane_id();
+  float v[4];
+  int id[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int e = lane + 64 * c;
+    float val = -INFINITY;
+    if (e < E) {
+      val = lg[e];
+      if (bias) val += bias[e];
+    }
+    if (val != val) val = -INFINITY;  // NaN logits rank last
+    v[c] = val;
+    id[c] = (e < E) ? e : 0x7fffffff;  // sentinel: never beats a real expert
+  }
+  float sel_v[MOE_MAX_TOPK];
+  int sel_e[MOE_MAX_TOPK];
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_TOPK; ++k) {
+    if (k < K) {
+      // lane-local best
+      float bv = v[0];
+      int be = id[0];
+#pragma unroll
+      for (int c = 1; c < 4; ++c)
+        if (v[c] > bv || (v[c] == bv && id[c] < be)) { bv = v[c]; be = id[c]; }
+      // wave arg-max, (value desc, id asc)
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        float ov = __shfl_xor(bv, off, kWave);
+        int oe = __shfl_xor(be, off, kWave);
+        if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+      }
+      sel_v[k] = bv;
+      sel_e[k] = be;
+      // remove the winner
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (id[c] == be) { v[c] = -INFINITY; id[c] = 0x7fffffff; }
+    }
+  }
+  // gates: softmax over the selected logits (sel_v[0] is the largest)
+  float z[MOE_MAX_TOPK];
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_TOPK; ++k) {
+    z[k] = (k < K) ? expf(sel_v[k] - sel_v[0]) : 0.f;
+    s += z[k];
+  }
+  if (lane < K) {
+    float zk = 0.f;
+    int ek = 0;
+#pragma unroll
+    for (int k = 0; k < MOE_MAX_TOPK; ++k)
+      if (k == lane) { zk = z[k]; ek = sel_e[k]; }
+    topk[n * K + lane] = ek;
+    gates[n * K + lane] = zk / s;
+  }
 }
 
 template <typename T, int EPT>
@@ -123,86 +192,192 @@ __global__ __launch_bounds__(256) void k_route(const T* __restrict__ x, const T*
   __syncthreads();
 
   // top-K: wave w handles tokens w*8 .. w*8+7
-  const int lane = lane_id();
   const int w = tid >> 6;
   for (int q = 0; q < kRouteTok / 4; ++q) {
     const int tt = w * (kRouteTok / 4) + q;
     const int n = n0 + tt;
     if (n >= N) break;  // uniform across the wave
-    // each lane holds experts lane, lane+64, lane+128, lane+192
-    float v[4];
-    int id[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      int e = lane + 64 * c;
-      float val = (e < E) ? lg[tt * (EP + 1) + e] : -INFINITY;
-      if (val != val) val = -INFINITY;  // NaN logits rank last
-      v[c] = val;
-      id[c] = (e < E) ? e : 0x7fffffff;  // sentinel: never beats a real expert
-    }
-    float sel_v[MOE_MAX_TOPK];
-    int sel_e[MOE_MAX_TOPK];
-#pragma unroll
-    for (int k = 0; k < MOE_MAX_TOPK; ++k) {
-      if (k < K) {
-        // lane-local best
-        float bv = v[0];
-        int be = id[0];
-#pragma unroll
-        for (int c = 1; c < 4; ++c)
-          if (v[c] > bv || (v[c] == bv && id[c] < be)) { bv = v[c]; be = id[c]; }
-        // wave arg-max, (value desc, id asc)
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-          float ov = __shfl_xor(bv, off, kWave);
-          int oe = __shfl_xor(be, off, kWave);
-          if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-        }
-        sel_v[k] = bv;
-        sel_e[k] = be;
-        // remove the winner
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          if (id[c] == be) { v[c] = -INFINITY; id[c] = 0x7fffffff; }
-      }
-    }
-    // gates: softmax over the selected logits (sel_v[0] is the largest)
-    float z[MOE_MAX_TOPK];
-    float s = 0.f;
-#pragma unroll
-    for (int k = 0; k < MOE_MAX_TOPK; ++k) {
-      z[k] = (k < K) ? expf(sel_v[k] - sel_v[0]) : 0.f;
-      s += z[k];
-    }
-    if (lane < K) {
-      float zk = 0.f;
-      int ek = 0;
-#pragma unroll
-      for (int k = 0; k < MOE_MAX_TOPK; ++k)
-        if (k == lane) { zk = z[k]; ek = sel_e[k]; }
-      topk[(int64_t)n * K + lane] = ek;
-      gates[(int64_t)n * K + lane] = zk / s;
-    }
+    wave_topk_gates(lg + tt * (EP + 1), nullptr, E, K, n, topk, gates);
   }
 }
 
-// dlogits, dense [N, E]: one thread per element.
-__global__ __launch_bounds__(256) void k_route_bwd_dl(const int32_t* __restrict__ topk, const float* __restrict__ gates,
-                                                      const float* __restrict__ dgates, float* __restrict__ dl, int N,
-                                                      int E, int K) {
-  int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)N * E) return;
-  int n = int(idx / E), e = int(idx % E);
-  const int32_t* tk = topk + (int64_t)n * K;
-  const float* g = gates + (int64_t)n * K;
-  const float* dg = dgates + (int64_t)n * K;
+// Top-K of one token by a single lane: one pass over the logits lg[0, E)
+// (+ bias[e] if given) keeps a sorted list of K (value, id) under the order
+// (logit desc, expert id asc); each new logit is pushed down the list by
+// predicated swaps.  NaN logits rank last; the sentinel id never beats a real
+// expert.  Then the gates (softmax over the K selected logits) and both
+// outputs of token n.
+__device__ __forceinline__ void lane_topk_gates(const float* __restrict__ lg, const float* __restrict__ bias, int E,
+                                                int K, int64_t n, int32_t* __restrict__ topk,
+                                                float* __restrict__ gates) {
+  float tv[MOE_MAX_TOPK];
+  int te[MOE_MAX_TOPK];
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_TOPK; ++k) {
+    tv[k] = -INFINITY;
+    te[k] = 0x7fffffff;
+  }
+  for (int e = 0; e < E; ++e) {
+    float cv = lg[e];
+    if (bias) cv += bias[e];
+    if (cv != cv) cv = -INFINITY;
+    int ce = e;
+#pragma unroll
+    for (int k = 0; k < MOE_MAX_TOPK; ++k) {
+      const bool better = k < K && (cv > tv[k] || (cv == tv[k] && ce < te[k]));
+      const float ov = tv[k];
+      const int oe = te[k];
+      tv[k] = better ? cv : ov;
+      te[k] = better ? ce : oe;
+      cv = better ? ov : cv;
+      ce = better ? oe : ce;
+    }
+  }
+  float z[MOE_MAX_TOPK];
   float s = 0.f;
-  for (int k = 0; k < K; ++k) s = fmaf(g[k], dg[k], s);
-  float out = 0.f;
-  for (int k = 0; k < K; ++k)
-    if (tk[k] == e) out = g[k] * (dg[k] - s);
-  dl[idx] = out;
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_TOPK; ++k) {
+    z[k] = (k < K) ? expf(tv[k] - tv[0]) : 0.f;
+    s += z[k];
+  }
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_TOPK; ++k)
+    if (k < K) {
+      topk[n * K + k] = te[k];
+      gates[n * K + k] = z[k] / s;
+    }
 }
+
+// Router logits on the matrix cores (bf16 storage, E a multiple of 8): one
+// workgroup owns C::BM tokens and every expert, padded to C::BN columns (the
+// padding columns read clamped in-bounds W_r columns and are masked before
+// the top-K).  logits = x.W_r with exact bf16 products accumulated in float32
+// over h ascending, 64 h per pipeline stage; the logits then go through LDS
+// and one lane per token selects its top-K (E <= 64), or one wave per token
+// (more experts: a lane's single pass would be long).
+template <class C>
+__global__ __launch_bounds__(C::NT, C::MINB) void k_route_mma(const bf16_t* __restrict__ x,
+                                                             const bf16_t* __restrict__ w_r,
+                                                             const float* __restrict__ bias,
+                                                             int32_t* __restrict__ topk, float* __restrict__ gates,
+                                                             int N, int H, int E, int K) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int n0 = blockIdx.x * C::BM;
+  const int rows = min(C::BM, N - n0);
+  const int w = threadIdx.x >> 6, wm = w / C::WN, wn = w % C::WN;
+  moe_mma::Acc<C> acc;
+  moe_mma::k_loop<C, false, true>(
+      lds, acc, H / C::BK,
+      [&](int kt, char* st) { moe_mma::dma_kc<C::BM, C::BK, C::NW>(st, x + (int64_t)n0 * H + kt * C::BK, H, rows); },
+      [&](int kt, char* st) {
+        const bf16_t* b = w_r + (int64_t)kt * C::BK * E;
+        moe_mma::dma_mn<C::BN, C::BK, C::NW>(st, b, b, C::BN, E, C::BK, E);
+      },
+      wm, wn);
+  constexpr int LP = C::BN + 1;  // odd pitch: the column writes of a wave spread over the banks
+  float* lg = reinterpret_cast<float*>(lds);
+  float* p = lg + moe_mma::lane_row<C>(wm) * LP + moe_mma::lane_col<C>(wn);
+#pragma unroll
+  for (int mi = 0; mi < C::FM; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < C::FN; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[moe_mma::frag_row(mi, r) * LP + ni * 32] = acc.a[mi][ni][r];
+  __syncthreads();
+  if (E <= 64) {
+    for (int tt = threadIdx.x; tt < rows; tt += C::NT) lane_topk_gates(lg + tt * LP, bias, E, K, n0 + tt, topk, gates);
+  } else {
+    for (int tt = w; tt < rows; tt += C::NW) wave_topk_gates(lg + tt * LP, bias, E, K, n0 + tt, topk, gates);
+  }
+}
+
+// Router tile shapes (tokens x padded experts): the MN-contiguous W_r tile
+// needs at least 128 columns for its swizzle.
+using RouteCfg128 = moe_mma::TileCfg<64, 128, 2, 2, 2, 64, 3>;
+using RouteCfg256 = moe_mma::TileCfg<32, 256, 1, 4, 2, 64, 2>;
+static_assert(RouteCfg128::BM * (RouteCfg128::BN + 1) * 4 <= RouteCfg128::LDS, "logits fit the staging space");
+static_assert(RouteCfg256::BM * (RouteCfg256::BN + 1) * 4 <= RouteCfg256::LDS, "logits fit the staging space");
+
+// dlogits, dense [N, E]: one thread per element.  With planes (bf16 path),
+// also the exact three-way bf16 split dl = hi + mid + lo of every element into
+// planes [3][n_pad][E] (rows N .. n_pad-1 zero), the B operand of the dW_r
+// MFMA kernel: hi = bf16(dl), mid = bf16(dl - hi), lo = bf16(dl - hi - mid);
+// each difference is exact in float32 and 3 x 8 significant bits cover the
+// 24 of a float32.
+__global__ __launch_bounds__(256) void k_route_bwd_dl(const int32_t* __restrict__ topk, const float* __restrict__ gates,
+                                                      const float* __restrict__ dgates, float* __restrict__ dl,
+                                                      bf16_t* __restrict__ planes, int N, int n_pad, int E, int K) {
+  int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)(planes ? n_pad : N) * E;
+  if (idx >= total) return;
+  int n = int(idx / E), e = int(idx % E);
+  float out = 0.f;
+  if (n < N) {
+    const int32_t* tk = topk + (int64_t)n * K;
+    const float* g = gates + (int64_t)n * K;
+    const float* dg = dgates + (int64_t)n * K;
+    float s = 0.f;
+    for (int k = 0; k < K; ++k) s = fmaf(g[k], dg[k], s);
+    for (int k = 0; k < K; ++k)
+      if (tk[k] == e) out = g[k] * (dg[k] - s);
+    dl[idx] = out;
+  }
+  if (planes) {
+    const bf16_t hi = f32_to_bf16(out);
+    const float r1 = out - bf16_to_f32(hi);
+    const bf16_t mid = f32_to_bf16(r1);
+    const bf16_t lo = f32_to_bf16(r1 - bf16_to_f32(mid));
+    const int64_t plane = (int64_t)n_pad * E;
+    planes[idx] = hi;
+    planes[plane + idx] = mid;
+    planes[2 * plane + idx] = lo;
+  }
+}
+
+// Partial dW_r on the matrix cores (bf16 path, E a multiple of 8): workgroup
+// (h tile, expert tile, chunk c) computes part[c][h][e] = sum over the chunk's
+// tokens n of x[n,h] (hi + mid + lo)[n,e], a contraction over 3 x chunk
+// steps: the hi plane over the chunk's tokens in ascending order, then mid,
+// then lo.  Both operands are MN-contiguous tiles; chunks are multiples of
+// 64 tokens and rows past N are zero in the planes (x rows there read a
+// clamped valid row and are multiplied by zero).
+template <class C>
+__global__ __launch_bounds__(C::NT, C::MINB) void k_route_dwr_mma(const bf16_t* __restrict__ x,
+                                                                 const bf16_t* __restrict__ planes,
+                                                                 float* __restrict__ part, int N, int n_pad, int H,
+                                                                 int E, int chunk) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int h0 = blockIdx.x * C::BM, e0 = blockIdx.y * C::BN, c = blockIdx.z;
+  const int nb = c * chunk;
+  const int nks = min(chunk, n_pad - nb) / C::BK;  // steps per plane
+  const int w = threadIdx.x >> 6, wm = w / C::WN, wn = w % C::WN;
+  const int64_t plane = (int64_t)n_pad * E;
+  moe_mma::Acc<C> acc;
+  moe_mma::k_loop<C, true, true>(
+      lds, acc, 3 * nks,
+      [&](int kt, char* st) {
+        const int n = nb + (kt % nks) * C::BK;
+        const bf16_t* a = x + (int64_t)n * H + h0;
+        moe_mma::dma_mn<C::BM, C::BK, C::NW>(st, a, a, C::BM, H, N - n, C::BM);
+      },
+      [&](int kt, char* st) {
+        const int n = nb + (kt % nks) * C::BK;
+        const bf16_t* b = planes + (kt / nks) * plane + (int64_t)n * E + e0;
+        moe_mma::dma_mn<C::BN, C::BK, C::NW>(st, b, b, C::BN, E, C::BK, E - e0);
+      },
+      wm, wn);
+  const int lr = moe_mma::lane_row<C>(wm), lc = moe_mma::lane_col<C>(wn);
+  float* o = part + (int64_t)c * H * E + (int64_t)(h0 + lr) * E + e0 + lc;
+#pragma unroll
+  for (int mi = 0; mi < C::FM; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < C::FN; ++ni)
+      if (e0 + lc + ni * 32 < E)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[(int64_t)moe_mma::frag_row(mi, r) * E + ni * 32] = acc.a[mi][ni][r];
+}
+
+using DwrCfg128 = moe_mma::TileCfg<128, 128, 2, 2, 2, 64, 2>;
 
 constexpr int kRbTok = 128;  // tokens staged in LDS at a time by the dW_r partial kernel
 
@@ -304,8 +479,25 @@ hipError_t launch_route(const moe_launch::Dims& d, const void* x, const void* w_
 
 namespace moe_launch {
 
+template <class C>
+hipError_t route_mma(const Dims& d, const void* x, const void* w_r, const float* bias, int32_t* topk, float* gates,
+                     hipStream_t s) {
+  hipError_t st = moe_mma::allow_lds<k_route_mma<C>>(C::LDS);
+  if (st != hipSuccess) return st;
+  const unsigned grid = unsigned((d.N + C::BM - 1) / C::BM);
+  hipLaunchKernelGGL(k_route_mma<C>, dim3(grid), dim3(C::NT), C::LDS, s, static_cast<const moe::bf16_t*>(x),
+                     static_cast<const moe::bf16_t*>(w_r), bias, topk, gates, int(d.N), int(d.H), int(d.E), int(d.K));
+  return hipGetLastError();
+}
+
+// The matrix-core paths of the router need 16-byte W_r rows (bf16, E % 8 == 0).
+static bool router_mma(const Dims& d) { return d.dtype == MOE_BF16 && d.E % 8 == 0; }
+
 hipError_t route(const Dims& d, const void* x, const void* w_r, const float* bias, int32_t* topk, float* gates,
                  hipStream_t s) {
+  if (router_mma(d))
+    return d.E <= 128 ? route_mma<RouteCfg128>(d, x, w_r, bias, topk, gates, s)
+                      : route_mma<RouteCfg256>(d, x, w_r, bias, topk, gates, s);
   if (d.dtype == MOE_BF16) return launch_route<moe::bf16_t>(d, x, w_r, bias, topk, gates, s);
   return launch_route<float>(d, x, w_r, bias, topk, gates, s);
 }
@@ -320,13 +512,76 @@ size_t route_bwd_chunks(const Dims& d) {
   return size_t(c);
 }
 
-size_t route_bwd_ws(const Dims& d) { return route_bwd_chunks(d) * size_t(d.E) * size_t(d.H) * sizeof(float); }
+// Matrix-core dW_r: chunks of a multiple of 64 tokens over n_pad = N rounded
+// up to 64; the workspace holds the chunk partials, then the bf16 planes.
+struct DwrPlan {
+  int64_t n_pad, chunk, nch;
+  size_t part_bytes, plane_bytes;
+};
+static DwrPlan dwr_plan(const Dims& d) {
+  DwrPlan p;
+  p.n_pad = (d.N + 63) / 64 * 64;
+  const int64_t target = int64_t(route_bwd_chunks(d));
+  p.chunk = ((d.N + target - 1) / target + 63) / 64 * 64;
+  p.nch = (p.n_pad + p.chunk - 1) / p.chunk;
+  p.part_bytes = (size_t(p.nch) * d.H * d.E * sizeof(float) + 255) / 256 * 256;
+  p.plane_bytes = size_t(3) * p.n_pad * d.E * sizeof(moe::bf16_t);
+  return p;
+}
+
+size_t route_bwd_ws(const Dims& d) {
+  const size_t vec = route_bwd_chunks(d) * size_t(d.E) * size_t(d.H) * sizeof(float);
+  if (!router_mma(d)) return vec;
+  const DwrPlan p = dwr_plan(d);
+  return p.part_bytes + p.plane_bytes;
+}
+
+// dW_r[h, e] = sum over chunks c of part[c][h][e] (same index as dW_r):
+// 8 lanes per output each sum a fixed stride-8 subset of the chunks in
+// ascending order, then a fixed butterfly adds the 8 partial sums.
+__global__ __launch_bounds__(256) void k_route_dwr_reduce(const float* __restrict__ part, float* __restrict__ dw_r,
+                                                          int64_t total, int nchunks) {
+  const int64_t o = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 3;
+  const int j = threadIdx.x & 7;
+  float sum = 0.f;
+  if (o < total)
+    for (int c = j; c < nchunks; c += 8) sum += part[(int64_t)c * total + o];
+  sum += __shfl_xor(sum, 1, moe::kWave);
+  sum += __shfl_xor(sum, 2, moe::kWave);
+  sum += __shfl_xor(sum, 4, moe::kWave);
+  if (j == 0 && o < total) dw_r[o] = sum;
+}
+
+hipError_t route_bwd_mma(const Dims& d, const void* x, const int32_t* topk, const float* gates, const float* dgates,
+                         float* dlogits, float* dw_r, void* ws, hipStream_t s) {
+  using C = DwrCfg128;
+  const DwrPlan p = dwr_plan(d);
+  float* part = static_cast<float*>(ws);
+  moe::bf16_t* planes = reinterpret_cast<moe::bf16_t*>(static_cast<char*>(ws) + p.part_bytes);
+  const int64_t ne = p.n_pad * d.E;
+  hipLaunchKernelGGL(k_route_bwd_dl, dim3(unsigned((ne + 255) / 256)), dim3(256), 0, s, topk, gates, dgates, dlogits,
+                     planes, int(d.N), int(p.n_pad), int(d.E), int(d.K));
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  err = moe_mma::allow_lds<k_route_dwr_mma<C>>(C::LDS);
+  if (err != hipSuccess) return err;
+  dim3 grid(unsigned(d.H / C::BM), unsigned((d.E + C::BN - 1) / C::BN), unsigned(p.nch));
+  hipLaunchKernelGGL(k_route_dwr_mma<C>, grid, dim3(C::NT), C::LDS, s, static_cast<const moe::bf16_t*>(x), planes,
+                     part, int(d.N), int(p.n_pad), int(d.H), int(d.E), int(p.chunk));
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t total = d.H * d.E;
+  hipLaunchKernelGGL(k_route_dwr_reduce, dim3(unsigned((total * 8 + 255) / 256)), dim3(256), 0, s, part, dw_r, total,
+                     int(p.nch));
+  return hipGetLastError();
+}
 
 hipError_t route_bwd(const Dims& d, const void* x, const int32_t* topk, const float* gates, const float* dgates,
                      float* dlogits, float* dw_r, void* ws, hipStream_t s) {
+  if (router_mma(d)) return route_bwd_mma(d, x, topk, gates, dgates, dlogits, dw_r, ws, s);
   int64_t ne = d.N * d.E;
   hipLaunchKernelGGL(k_route_bwd_dl, dim3(unsigned((ne + 255) / 256)), dim3(256), 0, s, topk, gates, dgates, dlogits,
-                     int(d.N), int(d.E), int(d.K));
+                     nullptr, int(d.N), int(d.N), int(d.E), int(d.K));
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int nch = int(route_bwd_chunks(d));
