@@ -18,12 +18,19 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t v) { return __uint_as_float(uint32_t(v) << 16); }
 
-// float32 -> bfloat16, round to nearest, ties to even; NaN stays NaN.
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return bf16_t((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return bf16_t(u >> 16);
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// float32 -> bfloat16, round to nearest, ties to even; NaN stays NaN.  gfx950
+// converts in hardware (v_cvt_pk_bf16_f32, two values per instruction); it
+// agrees bit for bit with the integer formulation (add 0x7fff plus the lowest
+// kept bit, keep the upper half; NaN: quiet bit set), denormals included.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f)); }
+
+// Two floats -> two bfloat16 packed in one word (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // Element-type traits: loads return float, stores round to the type.
@@ -65,7 +72,7 @@ template <> struct Vec16<bf16_t> {
   static __device__ __forceinline__ void store(bf16_t* p, const float* in) {
     uint32_t w[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = uint32_t(f32_to_bf16(in[2 * i])) | (uint32_t(f32_to_bf16(in[2 * i + 1])) << 16);
+    for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(in[2 * i], in[2 * i + 1]);
     *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 };
@@ -79,8 +86,10 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
-__device__ __forceinline__ float sigmoid_f32(float g) { return 1.0f / (1.0f + __expf(-g)); }
+// silu and sigmoid with the hardware exponential and reciprocal (a few ulp of
+// float32; the storage rounding to bfloat16 that follows dominates).
+__device__ __forceinline__ float sigmoid_f32(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+__device__ __forceinline__ float silu_f32(float g) { return g * sigmoid_f32(g); }
 
 // The expert of rank p when experts are ordered by row count, largest first
 // (equal counts: lower id first), from offsets [E+1].  The weight-gradient

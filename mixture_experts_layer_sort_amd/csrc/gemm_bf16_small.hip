@@ -296,7 +296,7 @@ __global__ __launch_bounds__(NT, 2) void k_gate_up(const bf16_t* __restrict__ xs
     for (int i = 0; i < 4; ++i) {
       const float g0 = __uint_as_float(gw[i] << 16), g1 = __uint_as_float(gw[i] & 0xffff0000u);
       const float u0 = __uint_as_float(uw[i] << 16), u1 = __uint_as_float(uw[i] & 0xffff0000u);
-      aw[i] = uint32_t(f32_to_bf16(silu_f32(g0) * u0)) | (uint32_t(f32_to_bf16(silu_f32(g1) * u1)) << 16);
+      aw[i] = pack_bf16x2(silu_f32(g0) * u0, silu_f32(g1) * u1);
     }
     *reinterpret_cast<uint4*>(a_out + o) = make_uint4(aw[0], aw[1], aw[2], aw[3]);
   }
