@@ -153,15 +153,29 @@ MOE_BF16_SHAPE(ffn_bwd_dw, const void*, const void*, const void*, const void*, c
                float*, float*, hipStream_t)
 #undef MOE_BF16_SHAPE
 
-// The 256 x 256 shape pays off once each workgroup's contraction is long
-// enough to amortise its prologue and 132 KiB LDS footprint (one workgroup
-// per CU); measured on MI355X it wins from contraction length 4096 on.
-static bool big_shape(int64_t k_len) { return k_len >= 4096; }
+// Which bf16 tile shape each stage uses.  The 256 x 256 tiles (one workgroup
+// per CU, LDS DMA, 132 KiB of LDS) win on long contractions with enough tiles
+// to fill the chip; the 128 x 128 tiles (2-3 workgroups per CU) hide latency
+// better on short contractions, on memory-bound shapes (few rows per
+// expert) and where the big tiles would leave CUs idle.  Measured on MI355X
+// per stage over the shapes (H, F, rows per expert) = (512, 1024, 4096),
+// (2048, 1408, skewed 0..16k), (7168, 2048, 256), (4096, 14336, 4096):
+//   gate/up and down: 256 x 256 only for long contractions (H resp. F >=
+//   4096) over many rows per expert (NK / E >= 2048), else 128 x 128;
+//   dA (contraction H): 256 x 256 from H = 2048 on;
+//   dX (contraction 2F): 256 x 256 from 2F = 2560 on;
+//   dW (contraction over an expert's rows): 256 x 256 when it makes at least
+//   4 tiles per CU (3 E H F / 256^2 >= 1024), else 128 x 128.
+static bool big_gate_up(const Dims& d) { return d.H >= 4096 && d.NK() / d.E >= 2048; }
+static bool big_down(const Dims& d) { return d.F >= 4096 && d.NK() / d.E >= 2048; }
+static bool big_dact(const Dims& d) { return d.H >= 2048; }
+static bool big_dx(const Dims& d) { return 2 * d.F >= 2560; }
+static bool big_dw(const Dims& d) { return 3 * d.E * (d.H / 256) * (d.F / 256) >= 1024; }
 
 hipError_t ffn_gate_up(const Dims& d, const void* xs, const void* wg, const void* wu, const int32_t* tiles,
                        const int32_t* num_tiles, void* g, void* u, void* a, hipStream_t s) {
   if (d.dtype == MOE_BF16)
-    return big_shape(d.H) ? ffn_gate_up_big(d, xs, wg, wu, tiles, num_tiles, g, u, a, s)
+    return big_gate_up(d) ? ffn_gate_up_big(d, xs, wg, wu, tiles, num_tiles, g, u, a, s)
                           : ffn_gate_up_small(d, xs, wg, wu, tiles, num_tiles, g, u, a, s);
   unsigned grid = unsigned(max_tiles(d) * (d.F / TN));
   hipLaunchKernelGGL(k_gate_up_f32, dim3(grid), dim3(256), 0, s, static_cast<const float*>(xs),
@@ -173,8 +187,8 @@ hipError_t ffn_gate_up(const Dims& d, const void* xs, const void* wg, const void
 hipError_t ffn_down(const Dims& d, const void* a, const void* wd, const int32_t* tiles, const int32_t* num_tiles,
                     void* ys, hipStream_t s) {
   if (d.dtype == MOE_BF16)
-    return big_shape(d.F) ? ffn_down_big(d, a, wd, tiles, num_tiles, ys, s)
-                          : ffn_down_small(d, a, wd, tiles, num_tiles, ys, s);
+    return big_down(d) ? ffn_down_big(d, a, wd, tiles, num_tiles, ys, s)
+                       : ffn_down_small(d, a, wd, tiles, num_tiles, ys, s);
   unsigned grid = unsigned(max_tiles(d) * (d.H / TN));
   hipLaunchKernelGGL(k_down_f32, dim3(grid), dim3(256), 0, s, static_cast<const float*>(a),
                      static_cast<const float*>(wd), tiles, num_tiles, static_cast<float*>(ys), int(d.H), int(d.F));
@@ -184,8 +198,8 @@ hipError_t ffn_down(const Dims& d, const void* a, const void* wd, const int32_t*
 hipError_t ffn_bwd_dact(const Dims& d, const void* dys, const void* wd, const void* g, const void* u,
                         const int32_t* tiles, const int32_t* num_tiles, void* dg, void* du, hipStream_t s) {
   if (d.dtype == MOE_BF16)
-    return big_shape(d.H) ? ffn_bwd_dact_big(d, dys, wd, g, u, tiles, num_tiles, dg, du, s)
-                          : ffn_bwd_dact_small(d, dys, wd, g, u, tiles, num_tiles, dg, du, s);
+    return big_dact(d) ? ffn_bwd_dact_big(d, dys, wd, g, u, tiles, num_tiles, dg, du, s)
+                       : ffn_bwd_dact_small(d, dys, wd, g, u, tiles, num_tiles, dg, du, s);
   unsigned grid = unsigned(max_tiles(d) * (d.F / TN));
   hipLaunchKernelGGL(k_dact_f32, dim3(grid), dim3(256), 0, s, static_cast<const float*>(dys),
                      static_cast<const float*>(wd), static_cast<const float*>(g), static_cast<const float*>(u), tiles,
@@ -196,8 +210,8 @@ hipError_t ffn_bwd_dact(const Dims& d, const void* dys, const void* wd, const vo
 hipError_t ffn_bwd_dx(const Dims& d, const void* dg, const void* du, const void* wg, const void* wu,
                       const int32_t* tiles, const int32_t* num_tiles, void* dxs, hipStream_t s) {
   if (d.dtype == MOE_BF16)
-    return big_shape(2 * d.F) ? ffn_bwd_dx_big(d, dg, du, wg, wu, tiles, num_tiles, dxs, s)
-                              : ffn_bwd_dx_small(d, dg, du, wg, wu, tiles, num_tiles, dxs, s);
+    return big_dx(d) ? ffn_bwd_dx_big(d, dg, du, wg, wu, tiles, num_tiles, dxs, s)
+                     : ffn_bwd_dx_small(d, dg, du, wg, wu, tiles, num_tiles, dxs, s);
   unsigned grid = unsigned(max_tiles(d) * (d.H / TN));
   hipLaunchKernelGGL(k_dx_f32, dim3(grid), dim3(256), 0, s, static_cast<const float*>(dg),
                      static_cast<const float*>(du), static_cast<const float*>(wg), static_cast<const float*>(wu), tiles,
@@ -208,8 +222,8 @@ hipError_t ffn_bwd_dx(const Dims& d, const void* dg, const void* du, const void*
 hipError_t ffn_bwd_dw(const Dims& d, const void* xs, const void* a, const void* dys, const void* dg, const void* du,
                       const int32_t* offsets, float* dwg, float* dwu, float* dwd, hipStream_t s) {
   if (d.dtype == MOE_BF16)
-    return big_shape(d.NK() / d.E) ? ffn_bwd_dw_big(d, xs, a, dys, dg, du, offsets, dwg, dwu, dwd, s)
-                                   : ffn_bwd_dw_small(d, xs, a, dys, dg, du, offsets, dwg, dwu, dwd, s);
+    return big_dw(d) ? ffn_bwd_dw_big(d, xs, a, dys, dg, du, offsets, dwg, dwu, dwd, s)
+                     : ffn_bwd_dw_small(d, xs, a, dys, dg, du, offsets, dwg, dwu, dwd, s);
   unsigned grid = unsigned(3 * d.E * (d.H / TN) * (d.F / TN));
   hipLaunchKernelGGL(k_dw_f32, dim3(grid), dim3(256), 0, s, static_cast<const float*>(xs),
                      static_cast<const float*>(a), static_cast<const float*>(dys), static_cast<const float*>(dg),
