@@ -41,7 +41,12 @@ using namespace moe;
 using namespace moe_mma;
 
 using Big = TileCfg<256, 256, 4, 2, 1, 64, 2>;  // 8 waves, 64 x 128 per wave
-static_assert(MOE_TILE_M % Big::BM == 0, "list tiles split into row tiles");
+// 128 x 128 tiles through the same DMA pipeline, 32 k per stage, three stages
+// (48 KiB of LDS, three workgroups per CU): used by the SwiGLU backward on
+// short contractions, where its staged epilogue of G and U overlaps better
+// across workgroups than the register-staged kernels'.
+using Mid = TileCfg<128, 128, 2, 2, 3, 32, 3>;
+static_assert(MOE_TILE_M % Big::BM == 0 && MOE_TILE_M % Mid::BM == 0, "list tiles split into row tiles");
 
 // staged tile <- bf16(acc)
 template <class C>
@@ -152,9 +157,9 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_gate_up(const bf16_t* __rest
   Acc<C> acc;
   k_loop<C, false, true>(
       lds, acc, H / C::BK,
-      [&](int kt, char* st) { dma_kc<C::BM, C::BK, C::NW>(st, a_base + kt * C::BK, H, ti.rows); },
-      [&](int kt, char* st) {
-        dma_mn<C::BN, C::BK, C::NW>(st, b_g + (int64_t)kt * C::BK * F, b_u + (int64_t)kt * C::BK * F, HALF, F, C::BK, C::BN);
+      [&](int kt, char* st, int j) { dma_kc<C::BM, C::BK, C::NW>(st, a_base + kt * C::BK, H, ti.rows, j); },
+      [&](int kt, char* st, int j) {
+        dma_mn<C::BN, C::BK, C::NW>(st, b_g + (int64_t)kt * C::BK * F, b_u + (int64_t)kt * C::BK * F, HALF, F, C::BK, C::BN, j);
       },
       wm, wn);
 
@@ -206,10 +211,10 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_down(const bf16_t* __restric
   const bf16_t* b_base = wd + (int64_t)ti.e * F * H + nt * C::BN;
   Acc<C> acc;
   k_loop<C, false, true>(
-      lds, acc, F / C::BK, [&](int kt, char* st) { dma_kc<C::BM, C::BK, C::NW>(st, a_base + kt * C::BK, F, ti.rows); },
-      [&](int kt, char* st) {
+      lds, acc, F / C::BK, [&](int kt, char* st, int j) { dma_kc<C::BM, C::BK, C::NW>(st, a_base + kt * C::BK, F, ti.rows, j); },
+      [&](int kt, char* st, int j) {
         const bf16_t* b = b_base + (int64_t)kt * C::BK * H;
-        dma_mn<C::BN, C::BK, C::NW>(st, b, b, C::BN, H, C::BK, ncols);
+        dma_mn<C::BN, C::BK, C::NW>(st, b, b, C::BN, H, C::BK, ncols, j);
       },
       wm, wn);
   bf16_t* stg = reinterpret_cast<bf16_t*>(lds);
@@ -242,8 +247,8 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_dact(const bf16_t* __restric
   const bf16_t* b_base = wd + (int64_t)ti.e * F * H + (int64_t)nt * C::BN * H;
   Acc<C> acc;
   k_loop<C, false, false>(
-      lds, acc, H / C::BK, [&](int kt, char* st) { dma_kc<C::BM, C::BK, C::NW>(st, a_base + kt * C::BK, H, ti.rows); },
-      [&](int kt, char* st) { dma_kc<C::BN, C::BK, C::NW>(st, b_base + kt * C::BK, H, ncols); }, wm, wn);
+      lds, acc, H / C::BK, [&](int kt, char* st, int j) { dma_kc<C::BM, C::BK, C::NW>(st, a_base + kt * C::BK, H, ti.rows, j); },
+      [&](int kt, char* st, int j) { dma_kc<C::BN, C::BK, C::NW>(st, b_base + kt * C::BK, H, ncols, j); }, wm, wn);
 
   // Epilogue one wave row (TM rows) at a time: the G and U rows are staged
   // side by side, the waves owning those rows turn them into dG and dU in
@@ -307,14 +312,14 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_dx(const bf16_t* __restrict_
   Acc<C> acc;
   k_loop<C, false, false>(
       lds, acc, 2 * nkf,
-      [&](int kt, char* st) {
+      [&](int kt, char* st, int j) {
         const bool second = kt >= nkf;
         dma_kc<C::BM, C::BK, C::NW>(st, (second ? du : dg) + (int64_t)ti.row0 * F + (second ? kt - nkf : kt) * C::BK, F,
-                             ti.rows);
+                             ti.rows, j);
       },
-      [&](int kt, char* st) {
+      [&](int kt, char* st, int j) {
         const bool second = kt >= nkf;
-        dma_kc<C::BN, C::BK, C::NW>(st, (second ? wu : wg) + woff + (second ? kt - nkf : kt) * C::BK, F, ncols);
+        dma_kc<C::BN, C::BK, C::NW>(st, (second ? wu : wg) + woff + (second ? kt - nkf : kt) * C::BK, F, ncols, j);
       },
       wm, wn);
   bf16_t* stg = reinterpret_cast<bf16_t*>(lds);
@@ -369,13 +374,13 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_dw(const bf16_t* __restrict_
   const int nk = (cnt + C::BK - 1) / C::BK;
   k_loop<C, true, true>(
       lds, acc, nk,
-      [&](int kt, char* st) {
+      [&](int kt, char* st, int j) {
         const bf16_t* b = l_base + (int64_t)kt * C::BK * P;
-        dma_mn<C::BM, C::BK, C::NW>(st, b, b, C::BM, P, cnt - kt * C::BK, prow);
+        dma_mn<C::BM, C::BK, C::NW>(st, b, b, C::BM, P, cnt - kt * C::BK, prow, j);
       },
-      [&](int kt, char* st) {
+      [&](int kt, char* st, int j) {
         const bf16_t* b = r_base + (int64_t)kt * C::BK * Q;
-        dma_mn<C::BN, C::BK, C::NW>(st, b, b, C::BN, Q, cnt - kt * C::BK, qcol);
+        dma_mn<C::BN, C::BK, C::NW>(st, b, b, C::BN, Q, cnt - kt * C::BK, qcol, j);
       },
       wm, wn, cnt - (nk - 1) * C::BK);
   const int lr = lane_row<C>(wm), lc = lane_col<C>(wn);
@@ -448,6 +453,11 @@ static hipError_t dact_t(const Dims& d, const void* dys, const void* wd, const v
 hipError_t ffn_bwd_dact_big(const Dims& d, const void* dys, const void* wd, const void* g, const void* u,
                              const int32_t* tiles, const int32_t* num_tiles, void* dg, void* du, hipStream_t s) {
   return dact_t<Big>(d, dys, wd, g, u, tiles, num_tiles, dg, du, s);
+}
+
+hipError_t ffn_bwd_dact_mid(const Dims& d, const void* dys, const void* wd, const void* g, const void* u,
+                            const int32_t* tiles, const int32_t* num_tiles, void* dg, void* du, hipStream_t s) {
+  return dact_t<Mid>(d, dys, wd, g, u, tiles, num_tiles, dg, du, s);
 }
 
 template <class C>

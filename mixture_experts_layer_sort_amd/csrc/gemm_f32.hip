@@ -147,6 +147,8 @@ MOE_BF16_SHAPE(ffn_gate_up, const void*, const void*, const void*, const int32_t
 MOE_BF16_SHAPE(ffn_down, const void*, const void*, const int32_t*, const int32_t*, void*, hipStream_t)
 MOE_BF16_SHAPE(ffn_bwd_dact, const void*, const void*, const void*, const void*, const int32_t*, const int32_t*, void*,
                void*, hipStream_t)
+hipError_t ffn_bwd_dact_mid(const Dims&, const void*, const void*, const void*, const void*, const int32_t*,
+                            const int32_t*, void*, void*, hipStream_t);
 MOE_BF16_SHAPE(ffn_bwd_dx, const void*, const void*, const void*, const void*, const int32_t*, const int32_t*, void*,
                hipStream_t)
 MOE_BF16_SHAPE(ffn_bwd_dw, const void*, const void*, const void*, const void*, const void*, const int32_t*, float*,
@@ -162,13 +164,15 @@ MOE_BF16_SHAPE(ffn_bwd_dw, const void*, const void*, const void*, const void*, c
 // (2048, 1408, skewed 0..16k), (7168, 2048, 256), (4096, 14336, 4096):
 //   gate/up and down: 256 x 256 only for long contractions (H resp. F >=
 //   4096) over many rows per expert (NK / E >= 2048), else 128 x 128;
-//   dA (contraction H): 256 x 256 from H = 2048 on;
+//   dA (contraction H): 256 x 256 from H = 4096 on, below that 128 x 128
+//   tiles through the LDS DMA pipeline (their staged SwiGLU epilogue beats
+//   the register-staged kernel's);
 //   dX (contraction 2F): 256 x 256 from 2F = 2560 on;
 //   dW (contraction over an expert's rows): 256 x 256 when it makes at least
 //   4 tiles per CU (3 E H F / 256^2 >= 1024), else 128 x 128.
 static bool big_gate_up(const Dims& d) { return d.H >= 4096 && d.NK() / d.E >= 2048; }
 static bool big_down(const Dims& d) { return d.F >= 4096 && d.NK() / d.E >= 2048; }
-static bool big_dact(const Dims& d) { return d.H >= 2048; }
+static bool big_dact(const Dims& d) { return d.H >= 4096; }
 static bool big_dx(const Dims& d) { return 2 * d.F >= 2560; }
 static bool big_dw(const Dims& d) { return 3 * d.E * (d.H / 256) * (d.F / 256) >= 1024; }
 
@@ -199,7 +203,7 @@ hipError_t ffn_bwd_dact(const Dims& d, const void* dys, const void* wd, const vo
                         const int32_t* tiles, const int32_t* num_tiles, void* dg, void* du, hipStream_t s) {
   if (d.dtype == MOE_BF16)
     return big_dact(d) ? ffn_bwd_dact_big(d, dys, wd, g, u, tiles, num_tiles, dg, du, s)
-                       : ffn_bwd_dact_small(d, dys, wd, g, u, tiles, num_tiles, dg, du, s);
+                       : ffn_bwd_dact_mid(d, dys, wd, g, u, tiles, num_tiles, dg, du, s);
   unsigned grid = unsigned(max_tiles(d) * (d.F / TN));
   hipLaunchKernelGGL(k_dact_f32, dim3(grid), dim3(256), 0, s, static_cast<const float*>(dys),
                      static_cast<const float*>(wd), static_cast<const float*>(g), static_cast<const float*>(u), tiles,

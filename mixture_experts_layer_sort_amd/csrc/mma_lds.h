@@ -24,6 +24,7 @@ struct TileCfg {
   static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int DPT = STAGE / 1024 / NW;              // LDS DMA instructions per stage and wave
+  static constexpr int JA = A_BYTES / 1024 / NW, JB = B_BYTES / 1024 / NW;  // ... of which A, B
   static constexpr int OP_BYTES = S * STAGE;
   static constexpr int PITCH = BN + 8;                       // bf16 per staged output row
   static constexpr int EPI_BYTES = BM * PITCH * 2;
@@ -31,7 +32,8 @@ struct TileCfg {
   static constexpr int LDS_A = OP_BYTES > EPI_BYTES ? OP_BYTES : EPI_BYTES;
   static constexpr int LDS = LDS_A > DACT_BYTES ? LDS_A : DACT_BYTES;
   static constexpr int SUB = MOE_TILE_M / BM;  // workgroup row tiles per list tile
-  static_assert(STAGE % (1024 * NW) == 0, "every wave issues the same number of DMA instructions");
+  static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0,
+                "every wave issues the same number of DMA instructions per operand");
   static_assert(BK == 32 || BK == 64, "stage depth");
 };
 
@@ -63,20 +65,21 @@ __device__ __forceinline__ int fk(int row) {
   return BK == 64 ? ((row ^ (row >> 3)) & 7) : ((row >> 2) & 3);
 }
 
-// Issue the DMA of rows [0, ROWS) x k [0, BK) of a row-major matrix (k
-// contiguous, leading dimension ld).  Rows at or past rows_valid read row
-// rows_valid - 1 instead (their results are never stored).
+// The wave's j-th LDS DMA instruction (instruction i = w + j * NW of the
+// ROWS * 2 * BK / 1024 that move the tile) of rows [0, ROWS) x k [0, BK) of a
+// row-major matrix (k contiguous, leading dimension ld).  Rows at or past
+// rows_valid read row rows_valid - 1 instead (their results are never
+// stored).
 template <int ROWS, int BK, int NW>
-__device__ __forceinline__ void dma_kc(char* stage, const bf16_t* base, int64_t ld, int rows_valid) {
+__device__ __forceinline__ void dma_kc(char* stage, const bf16_t* base, int64_t ld, int rows_valid, int j) {
   constexpr int CPR = BK / 8, RPI = 1024 / (2 * BK);  // chunks per row, rows per wave instruction
+  static_assert((ROWS / RPI) % NW == 0, "instructions split evenly over the waves");
   const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-#pragma unroll
-  for (int i = w; i < ROWS / RPI; i += NW) {
-    const int row = i * RPI + lane / CPR;
-    const int c = (lane % CPR) ^ fk<BK>(row);
-    const int rs = row < rows_valid ? row : rows_valid - 1;
-    dma16(base + (int64_t)rs * ld + c * 8, stage + i * 1024);
-  }
+  const int i = w + j * NW;
+  const int row = i * RPI + lane / CPR;
+  const int c = (lane % CPR) ^ fk<BK>(row);
+  const int rs = row < rows_valid ? row : rows_valid - 1;
+  dma16(base + (int64_t)rs * ld + c * 8, stage + i * 1024);
 }
 
 // MFMA operand fragment from a K-contiguous tile: lane l holds row
@@ -94,25 +97,25 @@ __device__ __forceinline__ bf16x8_t frag_kc(const char* stage, int rbase, int kk
 // transposing fragment reads (4 rows x 64 bytes per 32 lanes) conflict-free.
 __device__ __forceinline__ int fm(int k) { return 4 * (k & 3); }
 
-// Issue the DMA of k [0, BK) x columns [0, COLS) of a row-major matrix
-// (columns contiguous, leading dimension ld).  Columns [0, split) come from
-// base0 and [split, COLS) from base1 (both indexed by the tile column).  k
-// rows at or past k_valid and columns at or past cols_valid read clamped
-// positions (the caller zeroes or discards them).
+// The wave's j-th LDS DMA instruction (instruction i = w + j * NW of the
+// BK * COLS * 2 / 1024 that move the tile) of k [0, BK) x columns [0, COLS)
+// of a row-major matrix (columns contiguous, leading dimension ld).  Columns
+// [0, split) come from base0 and [split, COLS) from base1 (both indexed by
+// the tile column).  k rows at or past k_valid and columns at or past
+// cols_valid read clamped positions (the caller zeroes or discards them).
 template <int COLS, int BK, int NW>
 __device__ __forceinline__ void dma_mn(char* stage, const bf16_t* base0, const bf16_t* base1, int split, int64_t ld,
-                                       int k_valid, int cols_valid) {
+                                       int k_valid, int cols_valid, int j) {
   constexpr int CPR = COLS / 8, RPI = 1024 / (COLS * 2);  // chunks per row, rows per wave instruction
+  static_assert((BK / RPI) % NW == 0, "instructions split evenly over the waves");
   const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-#pragma unroll
-  for (int i = w; i < BK / RPI; i += NW) {
-    const int k = i * RPI + lane / CPR;
-    const int c = (lane % CPR) ^ fm(k);
-    const int ks = k < k_valid ? k : k_valid - 1;
-    const int cs = c * 8 < cols_valid ? c : (cols_valid >> 3) - 1;
-    const bf16_t* b = cs * 8 < split ? base0 : base1;
-    dma16(b + (int64_t)ks * ld + cs * 8, stage + i * 1024);
-  }
+  const int i = w + j * NW;
+  const int k = i * RPI + lane / CPR;
+  const int c = (lane % CPR) ^ fm(k);
+  const int ks = k < k_valid ? k : k_valid - 1;
+  const int cs = c * 8 < cols_valid ? c : (cols_valid >> 3) - 1;
+  const bf16_t* b = cs * 8 < split ? base0 : base1;
+  dma16(b + (int64_t)ks * ld + cs * 8, stage + i * 1024);
 }
 
 // MFMA operand fragment from an MN-contiguous tile with two transposing LDS
@@ -182,14 +185,15 @@ __device__ __forceinline__ void mma_stage(const char* sa, const char* sb, Acc<C>
   }
 }
 
-// S-stage K loop.  ia(kt, stage) / ib(kt, stage) issue the LDS DMA of K tile
-// kt.  Tiles 0 .. S-2 are issued up front; at step kt every wave waits until
-// its own DMA of tile kt has landed (tiles kt+1 .. kt+S-2 stay in flight),
-// the barrier makes tile kt visible to all waves and retires step kt-1's
-// reads of the stage tile kt+S-1 now reuses, the DMA of tile kt+S-1 starts
-// and the block multiplies tile kt.  When the last tile holds only k_last
-// valid k rows (weight gradients), rows k_last.. of its A stage (an MN tile)
-// are zeroed before it is used.
+// S-stage K loop.  ia(kt, stage, j) / ib(kt, stage, j) issue the wave's
+// j-th LDS DMA instruction of K tile kt (j < C::JA resp. C::JB).  Tiles
+// 0 .. S-2 are issued up front; at step kt every wave waits until its own DMA
+// of tile kt has landed (tiles kt+1 .. kt+S-2 stay in flight), the barrier
+// makes tile kt visible to all waves and retires step kt-1's reads of the
+// stage tile kt+S-1 now reuses, the DMA of tile kt+S-1 starts and the block
+// multiplies tile kt.  When the last tile holds
+// only k_last valid k rows (weight gradients), rows k_last.. of its A stage
+// (an MN tile) are zeroed before it is used.
 template <class C, bool A_MN, bool B_MN, class IA, class IB>
 __device__ __forceinline__ void k_loop(char* lds, Acc<C>& acc, int nk, IA ia, IB ib, int wm, int wn,
                                        int k_last = C::BK) {
@@ -198,8 +202,11 @@ __device__ __forceinline__ void k_loop(char* lds, Acc<C>& acc, int nk, IA ia, IB
 #pragma unroll
   for (int s = 0; s < C::S - 1; ++s)
     if (s < nk) {
-      ia(s, lds + s * C::STAGE);
-      ib(s, lds + s * C::STAGE + C::A_BYTES);
+      char* st = lds + s * C::STAGE;
+#pragma unroll
+      for (int j = 0; j < C::JA; ++j) ia(s, st, j);
+#pragma unroll
+      for (int j = 0; j < C::JB; ++j) ib(s, st + C::A_BYTES, j);
     }
   for (int kt = 0; kt < nk; ++kt) {
     if (kt + C::S - 2 < nk)
@@ -210,8 +217,10 @@ __device__ __forceinline__ void k_loop(char* lds, Acc<C>& acc, int nk, IA ia, IB
     const int nxt = kt + C::S - 1;
     if (nxt < nk) {
       char* st = lds + (nxt % C::S) * C::STAGE;
-      ia(nxt, st);
-      ib(nxt, st + C::A_BYTES);
+#pragma unroll
+      for (int j = 0; j < C::JA; ++j) ia(nxt, st, j);
+#pragma unroll
+      for (int j = 0; j < C::JB; ++j) ib(nxt, st + C::A_BYTES, j);
     }
     char* cur = lds + (kt % C::S) * C::STAGE;
     if (A_MN && kt == nk - 1 && k_last < C::BK) {

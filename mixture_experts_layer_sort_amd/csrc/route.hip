@@ -268,10 +268,10 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_route_mma(const bf16_t* __re
   moe_mma::Acc<C> acc;
   moe_mma::k_loop<C, false, true>(
       lds, acc, H / C::BK,
-      [&](int kt, char* st) { moe_mma::dma_kc<C::BM, C::BK, C::NW>(st, x + (int64_t)n0 * H + kt * C::BK, H, rows); },
-      [&](int kt, char* st) {
+      [&](int kt, char* st, int j) { moe_mma::dma_kc<C::BM, C::BK, C::NW>(st, x + (int64_t)n0 * H + kt * C::BK, H, rows, j); },
+      [&](int kt, char* st, int j) {
         const bf16_t* b = w_r + (int64_t)kt * C::BK * E;
-        moe_mma::dma_mn<C::BN, C::BK, C::NW>(st, b, b, C::BN, E, C::BK, E);
+        moe_mma::dma_mn<C::BN, C::BK, C::NW>(st, b, b, C::BN, E, C::BK, E, j);
       },
       wm, wn);
   constexpr int LP = C::BN + 1;  // odd pitch: the column writes of a wave spread over the banks
@@ -355,15 +355,15 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_route_dwr_mma(const bf16_t* 
   moe_mma::Acc<C> acc;
   moe_mma::k_loop<C, true, true>(
       lds, acc, 3 * nks,
-      [&](int kt, char* st) {
+      [&](int kt, char* st, int j) {
         const int n = nb + (kt % nks) * C::BK;
         const bf16_t* a = x + (int64_t)n * H + h0;
-        moe_mma::dma_mn<C::BM, C::BK, C::NW>(st, a, a, C::BM, H, N - n, C::BM);
+        moe_mma::dma_mn<C::BM, C::BK, C::NW>(st, a, a, C::BM, H, N - n, C::BM, j);
       },
-      [&](int kt, char* st) {
+      [&](int kt, char* st, int j) {
         const int n = nb + (kt % nks) * C::BK;
         const bf16_t* b = planes + (kt / nks) * plane + (int64_t)n * E + e0;
-        moe_mma::dma_mn<C::BN, C::BK, C::NW>(st, b, b, C::BN, E, C::BK, E - e0);
+        moe_mma::dma_mn<C::BN, C::BK, C::NW>(st, b, b, C::BN, E, C::BK, E - e0, j);
       },
       wm, wn);
   const int lr = moe_mma::lane_row<C>(wm), lc = moe_mma::lane_col<C>(wn);
