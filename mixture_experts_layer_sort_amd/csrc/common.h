@@ -91,6 +91,19 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 __device__ __forceinline__ float sigmoid_f32(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 __device__ __forceinline__ float silu_f32(float g) { return g * sigmoid_f32(g); }
 
+// Windowed XCD mapping: the hardware deals workgroup b to XCD b % 8.  Within
+// each window of 8 * kXcdRun consecutive workgroups, XCD x gets the kXcdRun
+// consecutive logical blocks [x * kXcdRun, (x + 1) * kXcdRun), so blocks that
+// share operand panels run on one XCD and share its L2, while the logical
+// order still advances through all XCDs together.  The launch grid must be a
+// multiple of 8 * kXcdRun; returns -1 for blocks past `total`.
+constexpr int kXcdRun = 8;
+__device__ __forceinline__ int xcd_window_block(int total) {
+  const int b = blockIdx.x;
+  const int L = (b / (8 * kXcdRun)) * (8 * kXcdRun) + (b % 8) * kXcdRun + (b / 8) % kXcdRun;
+  return L < total ? L : -1;
+}
+
 // The expert of rank p when experts are ordered by row count, largest first
 // (equal counts: lower id first), from offsets [E+1].  The weight-gradient
 // workgroups take their expert in this order, so the longest contractions

@@ -344,10 +344,10 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_dw(const bf16_t* __restrict_
   const int th = (H + C::BM - 1) / C::BM, tf = (F + C::BN - 1) / C::BN;
   const int th2 = (H + C::BN - 1) / C::BN, tf2 = (F + C::BM - 1) / C::BM;
   const int tpe = th * tf;  // output tiles per expert, problems 0 and 1 (== tf2 * th2 for square tiles)
-  // experts largest first, each expert's 3 * tpe tiles consecutive: the
-  // hardware deals consecutive workgroups round-robin over the XCDs
-  const int blk = blockIdx.x;
-  if (blk >= 3 * E * tpe) return;  // grid rounded up to a multiple of 8
+  // experts largest first, each expert's 3 * tpe tiles consecutive, dealt to
+  // the XCDs in runs of kXcdRun
+  const int blk = xcd_window_block(3 * E * tpe);
+  if (blk < 0) return;
   const int e = expert_of_rank<C::NT>(offsets, E, blk / (3 * tpe), reinterpret_cast<int*>(lds));
   const int prob = (blk % (3 * tpe)) / tpe, t = blk % tpe;
   const bf16_t *Lm, *Rm;
@@ -483,7 +483,9 @@ static hipError_t dw_t(const Dims& d, const void* xs, const void* a, const void*
   hipError_t st = allow_lds<k_dw<C>>(C::LDS);
   if (st != hipSuccess) return st;
   const int64_t tpe = ((d.H + C::BM - 1) / C::BM) * ((d.F + C::BN - 1) / C::BN);
-  unsigned grid = grid8(3 * d.E * tpe);
+  const int64_t total = 3 * d.E * tpe;
+  const int64_t win = 8 * kXcdRun;
+  unsigned grid = unsigned((total + win - 1) / win * win);
   hipLaunchKernelGGL(k_dw<C>, dim3(grid), dim3(C::NT), C::LDS, s, static_cast<const bf16_t*>(xs),
                      static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(dys), static_cast<const bf16_t*>(dg),
                      static_cast<const bf16_t*>(du), offsets, dwg, dwu, dwd, int(d.H), int(d.F), int(d.E));

@@ -472,10 +472,10 @@ __global__ __launch_bounds__(NT, 2) void k_dw(const bf16_t* __restrict__ xs, con
                                                float* __restrict__ dwd, int H, int F, int E) {
   __shared__ __attribute__((aligned(16))) char lds[kLds2];
   const int tpe = (H / BM) * (F / BN);  // output tiles per expert and problem
-  // experts largest first, each expert's 3 * tpe tiles consecutive: the
-  // hardware deals consecutive workgroups round-robin over the XCDs
-  const int blk = blockIdx.x;
-  if (blk >= 3 * E * tpe) return;  // grid rounded up to a multiple of 8
+  // experts largest first, each expert's 3 * tpe tiles consecutive, dealt to
+  // the XCDs in runs of kXcdRun
+  const int blk = xcd_window_block(3 * E * tpe);
+  if (blk < 0) return;
   const int e = expert_of_rank<NT>(offsets, E, blk / (3 * tpe), reinterpret_cast<int*>(lds));
   const int prob = (blk % (3 * tpe)) / tpe, t = blk % tpe;
   const bf16_t *L, *R;
@@ -569,7 +569,9 @@ hipError_t ffn_bwd_dx_small(const Dims& d, const void* dg, const void* du, const
 
 hipError_t ffn_bwd_dw_small(const Dims& d, const void* xs, const void* a, const void* dys, const void* dg,
                            const void* du, const int32_t* offsets, float* dwg, float* dwu, float* dwd, hipStream_t s) {
-  unsigned grid = grid8(3 * d.E * (d.H / BM) * (d.F / BN));
+  const int64_t total = 3 * d.E * (d.H / BM) * (d.F / BN);
+  const int64_t win = 8 * kXcdRun;
+  unsigned grid = unsigned((total + win - 1) / win * win);
   hipLaunchKernelGGL(k_dw, dim3(grid), dim3(NT), 0, s, static_cast<const bf16_t*>(xs), static_cast<const bf16_t*>(a),
                      static_cast<const bf16_t*>(dys), static_cast<const bf16_t*>(dg), static_cast<const bf16_t*>(du),
                      offsets, dwg, dwu, dwd, int(d.H), int(d.F), int(d.E));
