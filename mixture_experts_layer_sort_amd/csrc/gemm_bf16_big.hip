@@ -41,11 +41,11 @@ using namespace moe;
 using namespace moe_mma;
 
 using Big = TileCfg<256, 256, 4, 2, 1, 64, 2>;  // 8 waves, 64 x 128 per wave
-// 128 x 128 tiles through the same DMA pipeline, 32 k per stage, three stages
-// (48 KiB of LDS, three workgroups per CU): used by the SwiGLU backward on
+// 128 x 256 tiles through the same DMA pipeline, 32 k per stage, three stages
+// (72 KiB of LDS, two workgroups per CU): used by the SwiGLU backward on
 // short contractions, where its staged epilogue of G and U overlaps better
 // across workgroups than the register-staged kernels'.
-using Mid = TileCfg<128, 128, 2, 2, 3, 32, 3>;
+using Mid = TileCfg<128, 256, 2, 4, 2, 32, 3>;
 static_assert(MOE_TILE_M % Big::BM == 0 && MOE_TILE_M % Mid::BM == 0, "list tiles split into row tiles");
 
 // staged tile <- bf16(acc)

@@ -164,7 +164,7 @@ MOE_BF16_SHAPE(ffn_bwd_dw, const void*, const void*, const void*, const void*, c
 // (2048, 1408, skewed 0..16k), (7168, 2048, 256), (4096, 14336, 4096):
 //   gate/up and down: 256 x 256 only for long contractions (H resp. F >=
 //   4096) over many rows per expert (NK / E >= 2048), else 128 x 128;
-//   dA (contraction H): 256 x 256 from H = 4096 on, below that 128 x 128
+//   dA (contraction H): 256 x 256 from H = 4096 on, below that 128 x 256
 //   tiles through the LDS DMA pipeline (their staged SwiGLU epilogue beats
 //   the register-staged kernel's);
 //   dX (contraction 2F): 256 x 256 from 2F = 2560 on;

@@ -54,7 +54,10 @@ __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ ys, const
   }
 }
 
-// One wave per token: dys[inv[n,k]] = g_k * dy[n]; dgates[n,k] = <dy[n], ys[inv[n,k]]>.
+// One wave per token, kTokPerWave tokens per wave in turn:
+// dys[inv[n,k]] = g_k * dy[n]; dgates[n,k] = <dy[n], ys[inv[n,k]]> (fixed
+// lane order and butterfly, so the dot products are reproducible).
+constexpr int kTokPerWave = 2;
 template <typename T>
 __global__ __launch_bounds__(256) void k_combine_bwd(const T* __restrict__ dy, const T* __restrict__ ys,
                                                      const float* __restrict__ gates, const int32_t* __restrict__ inv,
@@ -62,40 +65,54 @@ __global__ __launch_bounds__(256) void k_combine_bwd(const T* __restrict__ dy, c
                                                      int K) {
   constexpr int V = Vec16<T>::n;
   const int lane = lane_id();
-  const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (n >= N) return;
-  int64_t r[MOE_MAX_TOPK];
-  float g[MOE_MAX_TOPK], dot[MOE_MAX_TOPK];
+  const int64_t nbase = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kTokPerWave;
+  int64_t r[kTokPerWave][MOE_MAX_TOPK];
+  float g[kTokPerWave][MOE_MAX_TOPK];
 #pragma unroll
-  for (int k = 0; k < MOE_MAX_TOPK; ++k) {
-    r[k] = (k < K) ? inv[n * K + k] : 0;
-    g[k] = (k < K) ? gates[n * K + k] : 0.f;
-    dot[k] = 0.f;
-  }
-  for (int c = lane; c < vpr; c += kWave) {
-    float d[V];
-    Vec16<T>::load(dy + (n * vpr + c) * V, d);
+  for (int t = 0; t < kTokPerWave; ++t)
+#pragma unroll
+    for (int k = 0; k < MOE_MAX_TOPK; ++k) {
+      const int64_t n = nbase + t;
+      const bool ok = n < N && k < K;
+      r[t][k] = ok ? inv[n * K + k] : 0;
+      g[t][k] = ok ? gates[n * K + k] : 0.f;
+    }
+#pragma unroll
+  for (int t = 0; t < kTokPerWave; ++t) {
+    const int64_t n = nbase + t;
+    if (n >= N) break;  // uniform across the wave
+    float dot[MOE_MAX_TOPK];
+#pragma unroll
+    for (int k = 0; k < MOE_MAX_TOPK; ++k) dot[k] = 0.f;
+    for (int c = lane; c < vpr; c += kWave) {
+      float d[V];
+      Vec16<T>::load(dy + (n * vpr + c) * V, d);
+      uint4 raw[MOE_MAX_TOPK];
+#pragma unroll
+      for (int k = 0; k < MOE_MAX_TOPK; ++k)
+        if (k < K) raw[k] = *reinterpret_cast<const uint4*>(ys + (r[t][k] * vpr + c) * V);
+#pragma unroll
+      for (int k = 0; k < MOE_MAX_TOPK; ++k) {
+        if (k < K) {
+          float yv[V], o[V];
+          Vec16<T>::load(reinterpret_cast<const T*>(&raw[k]), yv);
+          float s = dot[k];
+#pragma unroll
+          for (int i = 0; i < V; ++i) {
+            s = fmaf(d[i], yv[i], s);
+            o[i] = g[t][k] * d[i];
+          }
+          dot[k] = s;
+          Vec16<T>::store(dys + (r[t][k] * vpr + c) * V, o);
+        }
+      }
+    }
 #pragma unroll
     for (int k = 0; k < MOE_MAX_TOPK; ++k) {
       if (k < K) {
-        float yv[V], o[V];
-        Vec16<T>::load(ys + (r[k] * vpr + c) * V, yv);
-        float s = dot[k];
-#pragma unroll
-        for (int i = 0; i < V; ++i) {
-          s = fmaf(d[i], yv[i], s);
-          o[i] = g[k] * d[i];
-        }
-        dot[k] = s;
-        Vec16<T>::store(dys + (r[k] * vpr + c) * V, o);
+        float s = wave_sum(dot[k]);
+        if (lane == 0) dgates[n * K + k] = s;
       }
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < MOE_MAX_TOPK; ++k) {
-    if (k < K) {
-      float s = wave_sum(dot[k]);
-      if (lane == 0) dgates[n * K + k] = s;
     }
   }
 }
@@ -192,7 +209,7 @@ hipError_t combine(const Dims& d, const void* ys, const float* gates, const int3
 
 hipError_t combine_bwd(const Dims& d, const void* dy, const void* ys, const float* gates, const int32_t* inv,
                        void* dys, float* dgates, hipStream_t s) {
-  unsigned grid = unsigned((d.N + 3) / 4);
+  unsigned grid = unsigned((d.N + 4 * kTokPerWave - 1) / (4 * kTokPerWave));
   if (d.dtype == MOE_BF16)
     hipLaunchKernelGGL(k_combine_bwd<moe::bf16_t>, dim3(grid), dim3(256), 0, s,
                        static_cast<const moe::bf16_t*>(dy), static_cast<const moe::bf16_t*>(ys), gates, inv,
