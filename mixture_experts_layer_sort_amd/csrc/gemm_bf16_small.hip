@@ -211,15 +211,6 @@ __device__ __forceinline__ void epi_store(const bf16_t* tile, bf16_t* out, int64
         *reinterpret_cast<const uint4*>(tile + r * kEpiPitch + c * 8);
 }
 
-// rows [0, rows) of a global bf16 tile (leading dimension ld) -> staged tile
-__device__ __forceinline__ void epi_load(bf16_t* tile, const bf16_t* in, int64_t ld, int rows) {
-  const int c = threadIdx.x & 15;
-#pragma unroll 4
-  for (int r = threadIdx.x >> 4; r < rows; r += NT / 16)
-    *reinterpret_cast<uint4*>(tile + r * kEpiPitch + c * 8) =
-        *reinterpret_cast<const uint4*>(in + (int64_t)r * ld + c * 8);
-}
-
 // staged tile <- bf16(acc)
 __device__ __forceinline__ void epi_put_acc(bf16_t* tile, const f32x16_t (&acc)[2][2], int wm, int wn) {
 #pragma unroll
@@ -343,80 +334,6 @@ __global__ __launch_bounds__(NT, 2) void k_down(const bf16_t* __restrict__ act, 
 }
 
 // --------------------------------------------------------------- backward
-
-// dA = dys.W_down[e]^T; dG = dA*U*s*(1+G*(1-s)), dU = dA*G*s with s = sigmoid(G).
-__global__ __launch_bounds__(NT, 2) void k_dact(const bf16_t* __restrict__ dys, const bf16_t* __restrict__ wd,
-                                                 const bf16_t* __restrict__ g_in, const bf16_t* __restrict__ u_in,
-                                                 const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles,
-                                                 bf16_t* __restrict__ dg, bf16_t* __restrict__ du, int H, int F) {
-  __shared__ __attribute__((aligned(16))) char lds[kLds2];
-  const int ntn = F / BN;
-  const int nrow = *num_tiles * kSub;
-  const int L = xcd_block(nrow * ntn);
-  if (L < 0) return;
-  int ht, nt;
-  grouped(L, nrow, ntn, ht, nt);
-  const TileInfo ti = half_tile(tiles, ht);
-  if (ti.rows <= 0) return;
-  const int w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
-  const bf16_t* a_base = dys + (int64_t)ti.row0 * H;
-  // B[k = h][n = f] = W_down[e][f][h]: rows f of W_down[e] are k-contiguous
-  const bf16_t* b_base = wd + (int64_t)ti.e * F * H + (int64_t)nt * BN * H;
-  f32x16_t acc[2][2];
-  zero_acc(acc);
-  LoadKC la, lb;
-  const int nk = H / BK;
-  la.load(a_base, H, ti.rows);
-  lb.load(b_base, H, BN);
-  for (int kt = 0; kt < nk; ++kt) {
-    la.store(lds);
-    lb.store(lds + kTileBytes);
-    __syncthreads();
-    if (kt + 1 < nk) {
-      la.load(a_base + (kt + 1) * BK, H, ti.rows);
-      lb.load(b_base + (kt + 1) * BK, H, BN);
-    }
-    mma_tile(lds, lds + kTileBytes, acc, wm, wn);
-    __syncthreads();
-  }
-  // G tile -> LDS; acc becomes dA*s*(1+G*(1-s)) and dU = dA*G*s is kept
-  bf16_t* stg = reinterpret_cast<bf16_t*>(lds);
-  const int64_t obase = (int64_t)ti.row0 * F + nt * BN;
-  epi_load(stg, g_in + obase, F, ti.rows);
-  __syncthreads();
-  f32x16_t dup[2][2];
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float gv = bf16_to_f32(stg[epi_off(wm, wn, mi, ni, r)]);
-        const float sg = sigmoid_f32(gv);
-        const float da = acc[mi][ni][r];
-        dup[mi][ni][r] = da * gv * sg;
-        acc[mi][ni][r] = da * sg * (1.f + gv * (1.f - sg));
-      }
-  __syncthreads();
-  // U tile -> LDS; dG = (dA*s*(1+G*(1-s))) * U written in place
-  epi_load(stg, u_in + obase, F, ti.rows);
-  __syncthreads();
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int o = epi_off(wm, wn, mi, ni, r);
-        stg[o] = f32_to_bf16(acc[mi][ni][r] * bf16_to_f32(stg[o]));
-      }
-  __syncthreads();
-  epi_store(stg, dg + obase, F, ti.rows);
-  __syncthreads();
-  epi_put_acc(stg, dup, wm, wn);
-  __syncthreads();
-  epi_store(stg, du + obase, F, ti.rows);
-}
 
 // dxs = dG.W_gate[e]^T + dU.W_up[e]^T  (one K loop over 2F)
 __global__ __launch_bounds__(NT, 2) void k_dx(const bf16_t* __restrict__ dg, const bf16_t* __restrict__ du,
@@ -546,15 +463,6 @@ hipError_t ffn_down_small(const Dims& d, const void* a, const void* wd, const in
   unsigned grid = grid8(max_tiles(d) * kSub * (d.H / BN));
   hipLaunchKernelGGL(k_down, dim3(grid), dim3(NT), 0, s, static_cast<const bf16_t*>(a),
                      static_cast<const bf16_t*>(wd), tiles, num_tiles, static_cast<bf16_t*>(ys), int(d.H), int(d.F));
-  return hipGetLastError();
-}
-
-hipError_t ffn_bwd_dact_small(const Dims& d, const void* dys, const void* wd, const void* g, const void* u,
-                             const int32_t* tiles, const int32_t* num_tiles, void* dg, void* du, hipStream_t s) {
-  unsigned grid = grid8(max_tiles(d) * kSub * (d.F / BN));
-  hipLaunchKernelGGL(k_dact, dim3(grid), dim3(NT), 0, s, static_cast<const bf16_t*>(dys),
-                     static_cast<const bf16_t*>(wd), static_cast<const bf16_t*>(g), static_cast<const bf16_t*>(u),
-                     tiles, num_tiles, static_cast<bf16_t*>(dg), static_cast<bf16_t*>(du), int(d.H), int(d.F));
   return hipGetLastError();
 }
 

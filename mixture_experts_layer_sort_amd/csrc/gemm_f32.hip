@@ -137,16 +137,17 @@ __global__ __launch_bounds__(256) void k_dw_f32(const float* __restrict__ xs, co
 
 namespace moe_launch {
 
-// bf16 tile shapes: 256 x 256 LDS-DMA kernels (gemm_bf16_big.hip) and
-// 128 x 128 register-staged kernels (gemm_bf16_small.hip).
+// bf16 tile shapes: 256 x 256 and 128 x 256 (dA only) LDS-DMA kernels
+// (gemm_bf16_big.hip) and 128 x 128 register-staged kernels
+// (gemm_bf16_small.hip).
 #define MOE_BF16_SHAPE(name, ...)                 \
   hipError_t name##_big(const Dims&, __VA_ARGS__); \
   hipError_t name##_small(const Dims&, __VA_ARGS__);
 MOE_BF16_SHAPE(ffn_gate_up, const void*, const void*, const void*, const int32_t*, const int32_t*, void*, void*, void*,
                hipStream_t)
 MOE_BF16_SHAPE(ffn_down, const void*, const void*, const int32_t*, const int32_t*, void*, hipStream_t)
-MOE_BF16_SHAPE(ffn_bwd_dact, const void*, const void*, const void*, const void*, const int32_t*, const int32_t*, void*,
-               void*, hipStream_t)
+hipError_t ffn_bwd_dact_big(const Dims&, const void*, const void*, const void*, const void*, const int32_t*,
+                            const int32_t*, void*, void*, hipStream_t);
 hipError_t ffn_bwd_dact_mid(const Dims&, const void*, const void*, const void*, const void*, const int32_t*,
                             const int32_t*, void*, void*, hipStream_t);
 MOE_BF16_SHAPE(ffn_bwd_dx, const void*, const void*, const void*, const void*, const int32_t*, const int32_t*, void*,

@@ -126,36 +126,56 @@ __global__ __launch_bounds__(256) void k_transpose_wr(const T* __restrict__ w_r,
   w_rt[idx] = w_r[(int64_t)h * E + e];
 }
 
-// dx[n] = sum_k dxs[inv[n*K+k]] + sum_k dlogits[n, e_k] * W_r[:, e_k].
+// dx[n] = sum_k dxs[inv[n*K+k]] + sum_k dlogits[n, e_k] * W_r[:, e_k], both
+// sums in ascending k; one wave per token.
 template <typename T>
 __global__ __launch_bounds__(256) void k_permute_bwd(const T* __restrict__ dxs, const int32_t* __restrict__ inv,
                                                      const int32_t* __restrict__ topk, const float* __restrict__ dl,
-                                                     const T* __restrict__ w_rt, T* __restrict__ dx, int64_t total_vec,
-                                                     int vpr, int K, int E) {
+                                                     const T* __restrict__ w_rt, T* __restrict__ dx, int N, int vpr,
+                                                     int K, int E) {
   constexpr int V = Vec16<T>::n;
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < total_vec; v += stride) {
-    int64_t n = v / vpr;
-    int c = int(v - n * vpr);
+  const int lane = lane_id();
+  const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= N) return;
+  const uint4 *sx[MOE_MAX_TOPK], *sw[MOE_MAX_TOPK];
+  float d[MOE_MAX_TOPK];
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_TOPK; ++k)
+    if (k < K) {
+      const int e = topk[n * K + k];
+      sx[k] = reinterpret_cast<const uint4*>(dxs) + (int64_t)inv[n * K + k] * vpr;
+      sw[k] = reinterpret_cast<const uint4*>(w_rt) + (int64_t)e * vpr;
+      d[k] = dl[n * E + e];
+    }
+  T* dst = dx + n * vpr * V;
+  for (int c = lane; c < vpr; c += kWave) {
+    uint4 rx[MOE_MAX_TOPK], rw[MOE_MAX_TOPK];
+#pragma unroll
+    for (int k = 0; k < MOE_MAX_TOPK; ++k)
+      if (k < K) {
+        rx[k] = sx[k][c];
+        rw[k] = sw[k][c];
+      }
     float acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0.f;
-    for (int k = 0; k < K; ++k) {
-      int64_t r = inv[n * K + k];
-      float val[V];
-      Vec16<T>::load(dxs + (r * vpr + c) * V, val);
 #pragma unroll
-      for (int i = 0; i < V; ++i) acc[i] += val[i];
-    }
-    for (int k = 0; k < K; ++k) {
-      int64_t e = topk[n * K + k];
-      float d = dl[n * E + e];
-      float wv[V];
-      Vec16<T>::load(w_rt + (e * vpr + c) * V, wv);
+    for (int k = 0; k < MOE_MAX_TOPK; ++k)
+      if (k < K) {
+        float val[V];
+        Vec16<T>::load(reinterpret_cast<const T*>(&rx[k]), val);
 #pragma unroll
-      for (int i = 0; i < V; ++i) acc[i] = fmaf(d, wv[i], acc[i]);
-    }
-    Vec16<T>::store(dx + v * V, acc);
+        for (int i = 0; i < V; ++i) acc[i] += val[i];
+      }
+#pragma unroll
+    for (int k = 0; k < MOE_MAX_TOPK; ++k)
+      if (k < K) {
+        float wv[V];
+        Vec16<T>::load(reinterpret_cast<const T*>(&rw[k]), wv);
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[i] = fmaf(d[k], wv[i], acc[i]);
+      }
+    Vec16<T>::store(dst + c * V, acc);
   }
 }
 
@@ -165,6 +185,9 @@ unsigned grid_for(int64_t total, int64_t cap = 8192) {
   if (b < 1) b = 1;
   return unsigned(b);
 }
+
+// Workgroups of 4 waves, one wave per row.
+unsigned waves4(int64_t rows) { return unsigned((rows + 3) / 4); }
 
 template <typename T>
 int vpr_of(const moe_launch::Dims& d) {
@@ -235,20 +258,18 @@ hipError_t permute_bwd(const Dims& d, const void* dxs, const int32_t* inv, const
                        int(d.H), int(d.E));
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    int vpr = vpr_of<T>(d);
-    int64_t tot = d.N * vpr;
-    hipLaunchKernelGGL(k_permute_bwd<T>, dim3(grid_for(tot)), dim3(256), 0, s, static_cast<const T*>(dxs), inv, topk,
-                       dlogits, static_cast<const T*>(ws), static_cast<T*>(dx), tot, vpr, int(d.K), int(d.E));
+    hipLaunchKernelGGL(k_permute_bwd<T>, dim3(waves4(d.N)), dim3(256), 0, s, static_cast<const T*>(dxs), inv, topk,
+                       dlogits, static_cast<const T*>(ws), static_cast<T*>(dx), int(d.N), vpr_of<T>(d), int(d.K),
+                       int(d.E));
   } else {
     using T = float;
     hipLaunchKernelGGL(k_transpose_wr<T>, dim3(tg), dim3(256), 0, s, static_cast<const T*>(w_r), static_cast<T*>(ws),
                        int(d.H), int(d.E));
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    int vpr = vpr_of<T>(d);
-    int64_t tot = d.N * vpr;
-    hipLaunchKernelGGL(k_permute_bwd<T>, dim3(grid_for(tot)), dim3(256), 0, s, static_cast<const T*>(dxs), inv, topk,
-                       dlogits, static_cast<const T*>(ws), static_cast<T*>(dx), tot, vpr, int(d.K), int(d.E));
+    hipLaunchKernelGGL(k_permute_bwd<T>, dim3(waves4(d.N)), dim3(256), 0, s, static_cast<const T*>(dxs), inv, topk,
+                       dlogits, static_cast<const T*>(ws), static_cast<T*>(dx), int(d.N), vpr_of<T>(d), int(d.K),
+                       int(d.E));
   }
   return hipGetLastError();
 }
