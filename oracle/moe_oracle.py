@@ -225,6 +225,41 @@ def swiglu_expert(xs: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray
 
 
 # --------------------------------------------------------------------------
+# Switch load-balancing loss (icman 4.2)
+# --------------------------------------------------------------------------
+#
+# L_aux = alpha * E * sum_i f_i * P_i with f_i the share of the N*K routed
+# assignments that went to expert i (counts_i / (N*K); the token share for
+# K = 1) and P_i the router's softmax probability of expert i averaged over
+# all N tokens, from the same logits that select the experts (bias
+# included).  f is a count and carries no gradient.
+
+def router_probs(logits: np.ndarray) -> np.ndarray:
+    """Softmax over all E experts of every token's logits."""
+    z = np.exp(logits - logits.max(axis=1, keepdims=True))
+    return z / z.sum(axis=1, keepdims=True)
+
+
+def aux_loss(logits: np.ndarray, counts: np.ndarray, K: int, alpha: float) -> float:
+    """alpha * E * sum_i f_i P_i."""
+    N, E = logits.shape
+    P = router_probs(logits).mean(axis=0)
+    f = np.asarray(counts, dtype=np.float64) / (N * K)
+    return float(alpha * E * np.sum(f * P))
+
+
+def aux_loss_grad(logits: np.ndarray, counts: np.ndarray, K: int, scale: float) -> np.ndarray:
+    """d(L_aux)/d logits with alpha * (upstream gradient) = scale:
+    scale * E / N * p[n,j] * (f_j - sum_i f_i p[n,i]) (P_j is the mean of the
+    p[n,j], whose softmax derivative is p[n,j] (delta_ij - p[n,i]))."""
+    N, E = logits.shape
+    p = router_probs(logits)
+    f = np.asarray(counts, dtype=np.float64) / (N * K)
+    s = p @ f
+    return scale * E / N * p * (f[None, :] - s[:, None])
+
+
+# --------------------------------------------------------------------------
 # whole layer
 # --------------------------------------------------------------------------
 
@@ -290,8 +325,12 @@ def forward(x, w_r, w_gate, w_up, w_down, K: int, bias=None, store: str = "bf16"
                 sorted_flat=sorted_flat, inv=inv, tiles=tiles, xs=xs, G=G, U=U, A=A, ys=ys, y=y)
 
 
-def backward(fwd: dict, dy) -> dict:
+def backward(fwd: dict, dy, aux_scale: Optional[float] = None) -> dict:
     """Backward pass given the forward intermediates and dL/dy.
+
+    With aux_scale (alpha times the upstream gradient of the load-balancing
+    loss), the gradient of that loss is added to dlogits before the router's
+    weight and input gradients are formed.
 
     combine backward (gather of dy weighted by the gate, and the gate
     gradient as a dot product), expert backward with the SwiGLU derivative,
@@ -342,9 +381,12 @@ def backward(fwd: dict, dy) -> dict:
 
     # router backward: only the selected logits receive a gradient
     s = np.sum(gates * dgates, axis=1, keepdims=True)
-    dsel = rho32(gates * (dgates - s), store)
+    dsel = gates * (dgates - s)
     dlogits = np.zeros((N, E))
     np.put_along_axis(dlogits, topk.astype(np.int64), dsel, axis=1)
+    if aux_scale is not None:
+        dlogits = dlogits + aux_loss_grad(fwd["logits"], fwd["counts"], K, aux_scale)
+    dlogits = rho32(dlogits, store)
 
     # gather backward (sum over each token's K rows) + router input gradient
     dx = dxs[inv.reshape(N, K)].sum(axis=1) + dlogits @ w_r.T
@@ -472,9 +514,10 @@ def prop(dev: np.ndarray, w: np.ndarray) -> np.ndarray:
     return np.minimum(dev @ np.abs(w), 4.0 * np.sqrt((dev * dev) @ (w * w)))
 
 
-def rounding_bands(fwd: dict, bwd: Optional[dict] = None, dy=None) -> dict:
+def rounding_bands(fwd: dict, bwd: Optional[dict] = None, dy=None, aux_scale: Optional[float] = None) -> dict:
     """Per-element deviation bounds (see above) of every stored tensor and
-    output of a bf16-storage forward (and backward) computed by this module."""
+    output of a bf16-storage forward (and backward, with the load-balancing
+    loss gradient when aux_scale is given) computed by this module."""
     assert fwd["store"] == "bf16"
     K = fwd["K"]
     x, w_r = fwd["x"], fwd["w_r"]
@@ -563,6 +606,16 @@ def rounding_bands(fwd: dict, bwd: Optional[dict] = None, dy=None) -> dict:
         np.abs(g * bwd["dgates"]) + g * np.sum(np.abs(g * bwd["dgates"]), axis=1, keepdims=True))
     b["dlogits"] = np.zeros((N, E))
     np.put_along_axis(b["dlogits"], fwd["topk"].astype(np.int64), sdl, axis=1)
+    if aux_scale is not None:
+        # float32 logits are within gemm_sigma of the exact ones; the aux term
+        # p (f - s) moves by at most 4 max(f) p per unit of logit change, plus
+        # a few float32 roundings of the softmax and the products
+        aux = aux_loss_grad(fwd["logits"], fwd["counts"], K, aux_scale)
+        dl_max = gemm_sigma(x, w_r).max(axis=1, keepdims=True)
+        p = router_probs(fwd["logits"])
+        fmax = float(np.max(fwd["counts"])) / NK
+        b["dlogits"] = b["dlogits"] + 64 * U32 * np.abs(aux) + (
+            abs(aux_scale) * E / N * p * 4 * fmax * dl_max + 8 * U32 * np.abs(bwd["dlogits"]))
     b["dw_r"] = prop(b["dlogits"].T, x).T + gemm_sigma(x.T, bwd["dlogits"]) + 2 * U32 * np.abs(bwd["dw_r"])
     # gather backward
     dxp = bwd["dxs"][inv2].sum(axis=1) + bwd["dlogits"] @ w_r.T
