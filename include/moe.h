@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 /* Rows per tile of the grouped-GEMM tile list built by moe_permute_meta. */
 #define MOE_TILE_M 256
 #define MOE_MAX_EXPERTS 256
@@ -73,7 +73,9 @@ typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 typedef enum moe_entry {
   MOE_ENTRY_PERMUTE_META = 1,
   MOE_ENTRY_ROUTE_BWD = 2,
-  MOE_ENTRY_PERMUTE_BWD = 3
+  MOE_ENTRY_PERMUTE_BWD = 3, /* also moe_permute_bwd_dense */
+  MOE_ENTRY_AUX_LOSS = 4,
+  MOE_ENTRY_ROUTE_BWD_AUX = 5
 } moe_entry;
 
 /* Problem sizes: N tokens, hidden size H, expert FFN size F, E experts,
@@ -218,6 +220,43 @@ int moe_ffn_bwd_dw(const moe_dims* d, const void* xs, const void* act, const voi
  *   dx [N,H] out.  ws: MOE_ENTRY_PERMUTE_BWD (holds W_r transposed). */
 int moe_permute_bwd(const moe_dims* d, const void* dxs, const int32_t* inv, const int32_t* topk_idx,
                     const float* dlogits, const void* w_r, void* dx, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------ load-balancing loss */
+/* Switch load-balancing loss ("MoE computation principle and execution
+ * process", icman.com.cn, section 4.2):
+ *     L_aux = alpha * E * sum_e f_e * P_e
+ * with f_e = counts[e] / (N*K), the share of the N*K routed assignments that
+ * went to expert e (the token share for K = 1), and P_e the softmax over all
+ * E router logits (the same logits, bias included, that select the experts)
+ * averaged over the N tokens.  f is a count and carries no gradient.  */
+
+/* Forward: recomputes the logits x.W_r (+ logit_bias) as moe_route does and
+ * writes probs [N,E] f32 (the full softmax of every token; the backward needs
+ * it) and loss [1] f32 (device memory; never read back by the library).
+ * P_e is summed over token blocks in a fixed order, so the loss is
+ * bitwise reproducible.  counts [E] int32 from moe_permute_meta; alpha finite
+ * (else MOE_EINVAL).  ws: MOE_ENTRY_AUX_LOSS.  N == 0 enqueues nothing and
+ * leaves loss untouched. */
+int moe_aux_loss(const moe_dims* d, const void* x, const void* w_r, const float* logit_bias, const int32_t* counts,
+                 float alpha, float* probs, float* loss, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* moe_route_bwd with the gradient of aux_scale * L_aux / alpha added to every
+ * router logit before dW_r is formed (aux_scale = alpha times the upstream
+ * gradient of L_aux, usually alpha):
+ *     dlogits[n,e] += aux_scale * E / N * probs[n,e] * (f_e - sum_i f_i probs[n,i]).
+ * dlogits is then dense: use moe_permute_bwd_dense for dx.  probs from
+ * moe_aux_loss; counts [E].  ws: MOE_ENTRY_ROUTE_BWD_AUX. */
+int moe_route_bwd_aux(const moe_dims* d, const void* x, const int32_t* topk_idx, const float* gates,
+                      const float* dgates, const float* probs, const int32_t* counts, float aux_scale,
+                      float* dlogits, float* dw_r, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* moe_permute_bwd with the router term over all E experts:
+ *     dx[n] = sum_k dxs[inv[n*K+k]] + sum_e dlogits[n,e] * W_r[:,e],
+ *   k and e ascending, float32 accumulation, one rounding.  Same arguments and
+ *   workspace (MOE_ENTRY_PERMUTE_BWD) as moe_permute_bwd. */
+int moe_permute_bwd_dense(const moe_dims* d, const void* dxs, const int32_t* inv, const int32_t* topk_idx,
+                          const float* dlogits, const void* w_r, void* dx, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1
 MOE_ENTRY_PERMUTE_META, MOE_ENTRY_ROUTE_BWD, MOE_ENTRY_PERMUTE_BWD = 1, 2, 3
+MOE_ENTRY_AUX_LOSS, MOE_ENTRY_ROUTE_BWD_AUX = 4, 5
 MOE_TILE_M = 256
 
 # Every exported symbol with (restype, argtypes); the tests check this list
@@ -28,6 +29,7 @@ _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _I32 = ctypes.c_int32
 _SZ = ctypes.c_size_t
+_F = ctypes.c_float
 
 
 class moe_dims(ctypes.Structure):
@@ -55,6 +57,9 @@ SIGNATURES = {
     "moe_ffn_bwd_dx": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_ffn_bwd_dw": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_permute_bwd": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_permute_bwd_dense": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_aux_loss": (ctypes.c_int, [_DP, _P, _P, _P, _P, _F, _P, _P, _P, _SZ, _P]),
+    "moe_route_bwd_aux": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P, _F, _P, _P, _P, _SZ, _P]),
 }
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -208,3 +213,19 @@ def moe_ffn_bwd_dw(d, xs, act, dys, dg, du, offsets, dw_gate, dw_up, dw_down, st
 def moe_permute_bwd(d, dxs, inv, topk_idx, dlogits, w_r, dx, ws, stream=None):
     _call("moe_permute_bwd", ctypes.byref(d), _ptr(dxs), _ptr(inv), _ptr(topk_idx), _ptr(dlogits), _ptr(w_r),
           _ptr(dx), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+
+
+def moe_permute_bwd_dense(d, dxs, inv, topk_idx, dlogits, w_r, dx, ws, stream=None):
+    _call("moe_permute_bwd_dense", ctypes.byref(d), _ptr(dxs), _ptr(inv), _ptr(topk_idx), _ptr(dlogits), _ptr(w_r),
+          _ptr(dx), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+
+
+def moe_aux_loss(d, x, w_r, logit_bias, counts, alpha, probs, loss, ws, stream=None):
+    _call("moe_aux_loss", ctypes.byref(d), _ptr(x), _ptr(w_r), _ptr(logit_bias), _ptr(counts), float(alpha),
+          _ptr(probs), _ptr(loss), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+
+
+def moe_route_bwd_aux(d, x, topk_idx, gates, dgates, probs, counts, aux_scale, dlogits, dw_r, ws, stream=None):
+    _call("moe_route_bwd_aux", ctypes.byref(d), _ptr(x), _ptr(topk_idx), _ptr(gates), _ptr(dgates), _ptr(probs),
+          _ptr(counts), float(aux_scale), _ptr(dlogits), _ptr(dw_r), _ptr(ws),
+          0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))

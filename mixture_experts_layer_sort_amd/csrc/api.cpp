@@ -6,6 +6,8 @@
 
 #include <cstdint>
 
+#include <cmath>
+
 #include "common.h"
 #include "moe.h"
 
@@ -83,6 +85,8 @@ size_t moe_workspace_bytes(const moe_dims* d, int32_t entry) {
     case MOE_ENTRY_PERMUTE_META: return moe_launch::permute_meta_ws(D);
     case MOE_ENTRY_ROUTE_BWD: return moe_launch::route_bwd_ws(D);
     case MOE_ENTRY_PERMUTE_BWD: return moe_launch::permute_bwd_ws(D);
+    case MOE_ENTRY_AUX_LOSS: return moe_launch::aux_loss_ws(D);
+    case MOE_ENTRY_ROUTE_BWD_AUX: return moe_launch::route_bwd_aux_ws(D);
     default: return size_t(-1);
   }
 }
@@ -220,7 +224,43 @@ int moe_permute_bwd(const moe_dims* d, const void* dxs, const int32_t* inv, cons
   if (D.N == 0) return MOE_OK;
   const size_t need = moe_launch::permute_bwd_ws(D);
   if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return MOE_EWORKSPACE;
-  return from_hip(moe_launch::permute_bwd(D, dxs, inv, topk_idx, dlogits, w_r, dx, ws, stream));
+  return from_hip(moe_launch::permute_bwd(D, dxs, inv, topk_idx, dlogits, w_r, dx, ws, stream, false));
+}
+
+int moe_permute_bwd_dense(const moe_dims* d, const void* dxs, const int32_t* inv, const int32_t* topk_idx,
+                          const float* dlogits, const void* w_r, void* dx, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  MOE_CHECK_DIMS(d, D);
+  if (!ptrs_ok(dxs, inv, topk_idx, dlogits, w_r, dx)) return MOE_EINVAL;
+  if (D.N == 0) return MOE_OK;
+  const size_t need = moe_launch::permute_bwd_ws(D);
+  if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return MOE_EWORKSPACE;
+  return from_hip(moe_launch::permute_bwd(D, dxs, inv, topk_idx, dlogits, w_r, dx, ws, stream, true));
+}
+
+int moe_aux_loss(const moe_dims* d, const void* x, const void* w_r, const float* logit_bias, const int32_t* counts,
+                 float alpha, float* probs, float* loss, void* ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_CHECK_DIMS(d, D);
+  if (!ptrs_ok(x, w_r, counts, probs, loss)) return MOE_EINVAL;
+  if (logit_bias != nullptr && !aligned16(logit_bias)) return MOE_EINVAL;
+  if (!std::isfinite(alpha)) return MOE_EINVAL;
+  if (D.N == 0) return MOE_OK;
+  const size_t need = moe_launch::aux_loss_ws(D);
+  if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return MOE_EWORKSPACE;
+  return from_hip(moe_launch::aux_loss(D, x, w_r, logit_bias, counts, alpha, probs, loss, ws, stream));
+}
+
+int moe_route_bwd_aux(const moe_dims* d, const void* x, const int32_t* topk_idx, const float* gates,
+                      const float* dgates, const float* probs, const int32_t* counts, float aux_scale,
+                      float* dlogits, float* dw_r, void* ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_CHECK_DIMS(d, D);
+  if (!ptrs_ok(x, topk_idx, gates, dgates, probs, counts, dlogits, dw_r)) return MOE_EINVAL;
+  if (!std::isfinite(aux_scale)) return MOE_EINVAL;
+  if (D.N == 0) return MOE_OK;
+  const size_t need = moe_launch::route_bwd_aux_ws(D);
+  if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return MOE_EWORKSPACE;
+  return from_hip(moe_launch::route_bwd_aux(D, x, topk_idx, gates, dgates, probs, counts, aux_scale, dlogits, dw_r,
+                                            ws, stream));
 }
 
 }  // extern "C"

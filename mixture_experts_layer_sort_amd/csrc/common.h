@@ -155,8 +155,15 @@ hipError_t combine_bwd(const Dims& d, const void* dy, const void* ys, const floa
 hipError_t route_bwd(const Dims& d, const void* x, const int32_t* topk, const float* gates, const float* dgates,
                      float* dlogits, float* dw_r, void* ws, hipStream_t s);
 size_t route_bwd_ws(const Dims& d);
+size_t aux_loss_ws(const Dims& d);
+hipError_t aux_loss(const Dims& d, const void* x, const void* w_r, const float* bias, const int32_t* counts,
+                    float alpha, float* probs, float* loss, void* ws, hipStream_t s);
+size_t route_bwd_aux_ws(const Dims& d);
+hipError_t route_bwd_aux(const Dims& d, const void* x, const int32_t* topk, const float* gates, const float* dgates,
+                         const float* probs, const int32_t* counts, float aux_scale, float* dlogits, float* dw_r,
+                         void* ws, hipStream_t s);
 hipError_t permute_bwd(const Dims& d, const void* dxs, const int32_t* inv, const int32_t* topk, const float* dlogits,
-                       const void* w_r, void* dx, void* ws, hipStream_t s);
+                       const void* w_r, void* dx, void* ws, hipStream_t s, bool dense);
 size_t permute_bwd_ws(const Dims& d);
 
 hipError_t ffn_gate_up(const Dims& d, const void* xs, const void* wg, const void* wu, const int32_t* tiles,

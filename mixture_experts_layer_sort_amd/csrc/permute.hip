@@ -127,8 +127,9 @@ __global__ __launch_bounds__(256) void k_transpose_wr(const T* __restrict__ w_r,
 }
 
 // dx[n] = sum_k dxs[inv[n*K+k]] + sum_k dlogits[n, e_k] * W_r[:, e_k], both
-// sums in ascending k; one wave per token.
-template <typename T>
+// sums in ascending k; one wave per token.  DENSE: the router term runs over
+// all E experts (dlogits is dense when the load-balancing loss is on).
+template <typename T, bool DENSE>
 __global__ __launch_bounds__(256) void k_permute_bwd(const T* __restrict__ dxs, const int32_t* __restrict__ inv,
                                                      const int32_t* __restrict__ topk, const float* __restrict__ dl,
                                                      const T* __restrict__ w_rt, T* __restrict__ dx, int N, int vpr,
@@ -167,14 +168,29 @@ __global__ __launch_bounds__(256) void k_permute_bwd(const T* __restrict__ dxs, 
 #pragma unroll
         for (int i = 0; i < V; ++i) acc[i] += val[i];
       }
-#pragma unroll
-    for (int k = 0; k < MOE_MAX_TOPK; ++k)
-      if (k < K) {
+    if (DENSE) {
+      // every router logit has a gradient (load-balancing loss): all E
+      // experts, ascending
+      const float* dln = dl + n * E;
+      const uint4* wr = reinterpret_cast<const uint4*>(w_rt);
+      for (int e = 0; e < E; ++e) {
+        const uint4 raw = wr[(int64_t)e * vpr + c];
         float wv[V];
-        Vec16<T>::load(reinterpret_cast<const T*>(&rw[k]), wv);
+        Vec16<T>::load(reinterpret_cast<const T*>(&raw), wv);
+        const float de = dln[e];
 #pragma unroll
-        for (int i = 0; i < V; ++i) acc[i] = fmaf(d[k], wv[i], acc[i]);
+        for (int i = 0; i < V; ++i) acc[i] = fmaf(de, wv[i], acc[i]);
       }
+    } else {
+#pragma unroll
+      for (int k = 0; k < MOE_MAX_TOPK; ++k)
+        if (k < K) {
+          float wv[V];
+          Vec16<T>::load(reinterpret_cast<const T*>(&rw[k]), wv);
+#pragma unroll
+          for (int i = 0; i < V; ++i) acc[i] = fmaf(d[k], wv[i], acc[i]);
+        }
+    }
     Vec16<T>::store(dst + c * V, acc);
   }
 }
@@ -249,29 +265,27 @@ size_t permute_bwd_ws(const Dims& d) {
 }
 
 hipError_t permute_bwd(const Dims& d, const void* dxs, const int32_t* inv, const int32_t* topk, const float* dlogits,
-                       const void* w_r, void* dx, void* ws, hipStream_t s) {
+                       const void* w_r, void* dx, void* ws, hipStream_t s, bool dense) {
   int64_t nw = d.H * d.E;
   unsigned tg = unsigned((nw + 255) / 256);
-  if (d.dtype == MOE_BF16) {
-    using T = moe::bf16_t;
+  auto run = [&](auto tag) -> hipError_t {
+    using T = decltype(tag);
     hipLaunchKernelGGL(k_transpose_wr<T>, dim3(tg), dim3(256), 0, s, static_cast<const T*>(w_r), static_cast<T*>(ws),
                        int(d.H), int(d.E));
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(k_permute_bwd<T>, dim3(waves4(d.N)), dim3(256), 0, s, static_cast<const T*>(dxs), inv, topk,
-                       dlogits, static_cast<const T*>(ws), static_cast<T*>(dx), int(d.N), vpr_of<T>(d), int(d.K),
-                       int(d.E));
-  } else {
-    using T = float;
-    hipLaunchKernelGGL(k_transpose_wr<T>, dim3(tg), dim3(256), 0, s, static_cast<const T*>(w_r), static_cast<T*>(ws),
-                       int(d.H), int(d.E));
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(k_permute_bwd<T>, dim3(waves4(d.N)), dim3(256), 0, s, static_cast<const T*>(dxs), inv, topk,
-                       dlogits, static_cast<const T*>(ws), static_cast<T*>(dx), int(d.N), vpr_of<T>(d), int(d.K),
-                       int(d.E));
-  }
-  return hipGetLastError();
+    if (dense)
+      hipLaunchKernelGGL((k_permute_bwd<T, true>), dim3(waves4(d.N)), dim3(256), 0, s, static_cast<const T*>(dxs), inv,
+                         topk, dlogits, static_cast<const T*>(ws), static_cast<T*>(dx), int(d.N), vpr_of<T>(d),
+                         int(d.K), int(d.E));
+    else
+      hipLaunchKernelGGL((k_permute_bwd<T, false>), dim3(waves4(d.N)), dim3(256), 0, s, static_cast<const T*>(dxs),
+                         inv, topk, dlogits, static_cast<const T*>(ws), static_cast<T*>(dx), int(d.N), vpr_of<T>(d),
+                         int(d.K), int(d.E));
+    return hipGetLastError();
+  };
+  if (d.dtype == MOE_BF16) return run(moe::bf16_t{});
+  return run(float{});
 }
 
 }  // namespace moe_launch

@@ -15,6 +15,8 @@
 //   reduced over a fixed partition of the tokens (one LDS accumulator per
 //   (expert, h) per chunk, tokens ascending), then the chunk partials are
 //   summed in ascending chunk order.
+#include <type_traits>
+
 #include "common.h"
 #include "mma_lds.h"
 
@@ -98,10 +100,50 @@ __device__ __forceinline__ void wave_topk_gates(const float* __restrict__ lg, co
   }
 }
 
+// Load-balancing loss, forward part ("MoE computation principle and
+// execution process", section 4.2): the full softmax over the E experts of
+// each of the block's `rows` tokens, from the logits lg [rows][LP] in LDS
+// (+ bias[e] if given), stored to probs [N, E]; and the block's column sums of
+// the probabilities (tokens ascending) to part[0, E), summed over the blocks
+// in a fixed order afterwards.
+template <int NT>
+__device__ __forceinline__ void probs_epilogue(float* lg, int LP, int rows, int64_t n0, int E,
+                                               const float* __restrict__ bias, float* __restrict__ probs,
+                                               float* __restrict__ part) {
+  for (int tt = threadIdx.x; tt < rows; tt += NT) {
+    float* l = lg + tt * LP;
+    float m = -INFINITY;
+    for (int e = 0; e < E; ++e) {
+      const float v = l[e] + (bias ? bias[e] : 0.f);
+      l[e] = v;
+      m = fmaxf(m, v);
+    }
+    float sum = 0.f;
+    for (int e = 0; e < E; ++e) {
+      const float z = __expf(l[e] - m);
+      l[e] = z;
+      sum += z;
+    }
+    const float r = 1.0f / sum;
+    for (int e = 0; e < E; ++e) l[e] *= r;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += NT) {
+    float c = 0.f;
+    for (int tt = 0; tt < rows; ++tt) {
+      const float p = lg[tt * LP + e];
+      probs[(n0 + tt) * E + e] = p;
+      c += p;
+    }
+    part[e] = c;
+  }
+}
+
 template <typename T, int EPT>
 __global__ __launch_bounds__(256) void k_route(const T* __restrict__ x, const T* __restrict__ w_r,
                                                const float* __restrict__ bias, int32_t* __restrict__ topk,
-                                               float* __restrict__ gates, int N, int H, int E, int K) {
+                                               float* __restrict__ gates, int N, int H, int E, int K,
+                                               float* __restrict__ probs, float* __restrict__ part) {
   constexpr int EP = 8 * EPT;  // padded experts
   constexpr int HC = route_hc<EPT>();
   constexpr int V = Vec16<T>::n;
@@ -191,6 +233,10 @@ __global__ __launch_bounds__(256) void k_route(const T* __restrict__ x, const T*
   }
   __syncthreads();
 
+  if (probs) {  // load-balancing loss: full softmax instead of the top-K
+    probs_epilogue<256>(lg, EP + 1, min(kRouteTok, N - n0), n0, E, nullptr, probs, part + (int64_t)blockIdx.x * E);
+    return;
+  }
   // top-K: wave w handles tokens w*8 .. w*8+7
   const int w = tid >> 6;
   for (int q = 0; q < kRouteTok / 4; ++q) {
@@ -260,7 +306,8 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_route_mma(const bf16_t* __re
                                                              const bf16_t* __restrict__ w_r,
                                                              const float* __restrict__ bias,
                                                              int32_t* __restrict__ topk, float* __restrict__ gates,
-                                                             int N, int H, int E, int K) {
+                                                             int N, int H, int E, int K, float* __restrict__ probs,
+                                                             float* __restrict__ part) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int n0 = blockIdx.x * C::BM;
   const int rows = min(C::BM, N - n0);
@@ -284,7 +331,9 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_route_mma(const bf16_t* __re
 #pragma unroll
       for (int r = 0; r < 16; ++r) p[moe_mma::frag_row(mi, r) * LP + ni * 32] = acc.a[mi][ni][r];
   __syncthreads();
-  if (E <= 64) {
+  if (probs) {  // load-balancing loss: full softmax instead of the top-K
+    probs_epilogue<C::NT>(lg, LP, rows, n0, E, bias, probs, part + (int64_t)blockIdx.x * E);
+  } else if (E <= 64) {
     for (int tt = threadIdx.x; tt < rows; tt += C::NT) lane_topk_gates(lg + tt * LP, bias, E, K, n0 + tt, topk, gates);
   } else {
     for (int tt = w; tt < rows; tt += C::NW) wave_topk_gates(lg + tt * LP, bias, E, K, n0 + tt, topk, gates);
@@ -298,15 +347,27 @@ using RouteCfg256 = moe_mma::TileCfg<32, 256, 1, 4, 2, 64, 2>;
 static_assert(RouteCfg128::BM * (RouteCfg128::BN + 1) * 4 <= RouteCfg128::LDS, "logits fit the staging space");
 static_assert(RouteCfg256::BM * (RouteCfg256::BN + 1) * 4 <= RouteCfg256::LDS, "logits fit the staging space");
 
-// dlogits, dense [N, E]: one thread per element.  With planes (bf16 path),
+// dlogits, dense [N, E]: one thread per element, plus the load-balancing
+// loss term when aux.probs is set.  With planes (bf16 path),
 // also the exact three-way bf16 split dl = hi + mid + lo of every element into
 // planes [3][n_pad][E] (rows N .. n_pad-1 zero), the B operand of the dW_r
 // MFMA kernel: hi = bf16(dl), mid = bf16(dl - hi), lo = bf16(dl - hi - mid);
 // each difference is exact in float32 and 3 x 8 significant bits cover the
 // 24 of a float32.
+// Load-balancing loss term of the backward (all null / zero: no term):
+// dl[n,e] += coef * p[n,e] * (counts[e] * inv_nk - s[n]) with coef =
+// alpha * (upstream gradient) * E / N and s[n] = sum_i f_i p[n,i].
+struct AuxGrad {
+  const float* probs;
+  const int32_t* counts;
+  const float* s;
+  float coef, inv_nk;
+};
+
 __global__ __launch_bounds__(256) void k_route_bwd_dl(const int32_t* __restrict__ topk, const float* __restrict__ gates,
                                                       const float* __restrict__ dgates, float* __restrict__ dl,
-                                                      bf16_t* __restrict__ planes, int N, int n_pad, int E, int K) {
+                                                      bf16_t* __restrict__ planes, int N, int n_pad, int E, int K,
+                                                      AuxGrad aux) {
   int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t total = (int64_t)(planes ? n_pad : N) * E;
   if (idx >= total) return;
@@ -320,6 +381,7 @@ __global__ __launch_bounds__(256) void k_route_bwd_dl(const int32_t* __restrict_
     for (int k = 0; k < K; ++k) s = fmaf(g[k], dg[k], s);
     for (int k = 0; k < K; ++k)
       if (tk[k] == e) out = g[k] * (dg[k] - s);
+    if (aux.probs) out += aux.coef * aux.probs[idx] * (float(aux.counts[e]) * aux.inv_nk - aux.s[n]);
     dl[idx] = out;
   }
   if (planes) {
@@ -383,11 +445,13 @@ constexpr int kRbTok = 128;  // tokens staged in LDS at a time by the dW_r parti
 
 // Partial dW_r of one chunk of tokens and HB hidden units:
 // part[c][e][h] = sum_{n in chunk} x[n,h] dl[n,e], sparse in e (only the K
-// selected experts of a token contribute).  kRbTok tokens at a time, the x
-// slice, expert ids and dlogits values are first staged in LDS with
-// independent loads; then each thread accumulates its h over the tokens in
-// ascending order.
-template <typename T, int HB>
+// selected experts of a token contribute) unless DENSE (the load-balancing
+// loss gives every logit a gradient: all E experts, ascending, dl read
+// straight from its [N, E] rows).  kRbTok tokens at a time, the x slice,
+// expert ids and dlogits values are first staged in LDS with independent
+// loads; then each thread accumulates its h over the tokens in ascending
+// order.
+template <typename T, int HB, bool DENSE>
 __global__ __launch_bounds__(HB) void k_route_bwd_partial(const T* __restrict__ x, const int32_t* __restrict__ topk,
                                                           const float* __restrict__ dl, float* __restrict__ part,
                                                           int N, int H, int E, int K, int chunk) {
@@ -413,18 +477,24 @@ __global__ __launch_bounds__(HB) void k_route_bwd_partial(const T* __restrict__ 
 #pragma unroll
       for (int q = 0; q < V; ++q) xs[tt * HB + v * V + q] = val[q];
     }
-    for (int i = t; i < nt * K; i += HB) {
-      const int64_t f = (int64_t)s0 * K + i;
-      const int e = topk[f];
-      s_e[i] = e;
-      s_d[i] = dl[(f / K) * E + e];
-    }
+    if (!DENSE)
+      for (int i = t; i < nt * K; i += HB) {
+        const int64_t f = (int64_t)s0 * K + i;
+        const int e = topk[f];
+        s_e[i] = e;
+        s_d[i] = dl[(f / K) * E + e];
+      }
     __syncthreads();
     for (int n = 0; n < nt; ++n) {
       const float xv = xs[n * HB + t];
-      for (int k = 0; k < K; ++k) {
-        const int e = s_e[n * K + k];
-        acc[e * HB + t] = fmaf(xv, s_d[n * K + k], acc[e * HB + t]);
+      if (DENSE) {
+        const float* dn = dl + (int64_t)(s0 + n) * E;
+        for (int e = 0; e < E; ++e) acc[e * HB + t] = fmaf(xv, dn[e], acc[e * HB + t]);
+      } else {
+        for (int k = 0; k < K; ++k) {
+          const int e = s_e[n * K + k];
+          acc[e * HB + t] = fmaf(xv, s_d[n * K + k], acc[e * HB + t]);
+        }
       }
     }
   }
@@ -453,26 +523,60 @@ __global__ __launch_bounds__(256) void k_route_bwd_reduce(const float* __restric
 
 template <typename T, int EPT>
 hipError_t launch_route_t(const moe_launch::Dims& d, const void* x, const void* w_r, const float* bias, int32_t* topk,
-                          float* gates, hipStream_t s) {
+                          float* gates, hipStream_t s, float* probs, float* part) {
   constexpr int EP = 8 * EPT;
   constexpr int HC = route_hc<EPT>();
   constexpr size_t stage = HC * kRouteTok + HC * EP, logits = kRouteTok * (EP + 1);
   size_t lds = sizeof(float) * (stage > logits ? stage : logits);
   int grid = int((d.N + kRouteTok - 1) / kRouteTok);
   hipLaunchKernelGGL((k_route<T, EPT>), dim3(grid), dim3(256), lds, s, static_cast<const T*>(x),
-                     static_cast<const T*>(w_r), bias, topk, gates, int(d.N), int(d.H), int(d.E), int(d.K));
+                     static_cast<const T*>(w_r), bias, topk, gates, int(d.N), int(d.H), int(d.E), int(d.K), probs,
+                     part);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_route(const moe_launch::Dims& d, const void* x, const void* w_r, const float* bias, int32_t* topk,
-                        float* gates, hipStream_t s) {
-  if (d.E <= 8) return launch_route_t<T, 1>(d, x, w_r, bias, topk, gates, s);
-  if (d.E <= 16) return launch_route_t<T, 2>(d, x, w_r, bias, topk, gates, s);
-  if (d.E <= 32) return launch_route_t<T, 4>(d, x, w_r, bias, topk, gates, s);
-  if (d.E <= 64) return launch_route_t<T, 8>(d, x, w_r, bias, topk, gates, s);
-  if (d.E <= 128) return launch_route_t<T, 16>(d, x, w_r, bias, topk, gates, s);
-  return launch_route_t<T, 32>(d, x, w_r, bias, topk, gates, s);
+                        float* gates, hipStream_t s, float* probs = nullptr, float* part = nullptr) {
+  if (d.E <= 8) return launch_route_t<T, 1>(d, x, w_r, bias, topk, gates, s, probs, part);
+  if (d.E <= 16) return launch_route_t<T, 2>(d, x, w_r, bias, topk, gates, s, probs, part);
+  if (d.E <= 32) return launch_route_t<T, 4>(d, x, w_r, bias, topk, gates, s, probs, part);
+  if (d.E <= 64) return launch_route_t<T, 8>(d, x, w_r, bias, topk, gates, s, probs, part);
+  if (d.E <= 128) return launch_route_t<T, 16>(d, x, w_r, bias, topk, gates, s, probs, part);
+  return launch_route_t<T, 32>(d, x, w_r, bias, topk, gates, s, probs, part);
+}
+
+// Load-balancing loss value: P_e = (sum of the block partials, blocks
+// ascending) / N, f_e = counts_e / (N K), loss = alpha * E * sum_e f_e P_e
+// (fixed-order tree over the experts).  One workgroup.
+__global__ __launch_bounds__(256) void k_aux_reduce(const float* __restrict__ part, int nblk,
+                                                    const int32_t* __restrict__ counts, int N, int E, int K,
+                                                    float alpha, float* __restrict__ loss) {
+  __shared__ float t[256];
+  const int e = threadIdx.x;
+  float term = 0.f;
+  if (e < E) {
+    float P = 0.f;
+    for (int b = 0; b < nblk; ++b) P += part[(int64_t)b * E + e];
+    term = (float(counts[e]) / (float(N) * float(K))) * (P / float(N));
+  }
+  t[e] = term;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (e < off) t[e] += t[e + off];
+    __syncthreads();
+  }
+  if (e == 0) *loss = alpha * float(E) * t[0];
+}
+
+// s[n] = sum_i f_i p[n,i] with f_i = counts_i / (N K), experts ascending.
+__global__ __launch_bounds__(256) void k_aux_s(const float* __restrict__ probs, const int32_t* __restrict__ counts,
+                                               float* __restrict__ s, int N, int E, float inv_nk) {
+  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  float acc = 0.f;
+  for (int e = 0; e < E; ++e) acc = fmaf(float(counts[e]) * inv_nk, probs[n * E + e], acc);
+  s[n] = acc;
 }
 
 }  // namespace
@@ -481,12 +585,13 @@ namespace moe_launch {
 
 template <class C>
 hipError_t route_mma(const Dims& d, const void* x, const void* w_r, const float* bias, int32_t* topk, float* gates,
-                     hipStream_t s) {
+                     hipStream_t s, float* probs = nullptr, float* part = nullptr) {
   hipError_t st = moe_mma::allow_lds<k_route_mma<C>>(C::LDS);
   if (st != hipSuccess) return st;
   const unsigned grid = unsigned((d.N + C::BM - 1) / C::BM);
   hipLaunchKernelGGL(k_route_mma<C>, dim3(grid), dim3(C::NT), C::LDS, s, static_cast<const moe::bf16_t*>(x),
-                     static_cast<const moe::bf16_t*>(w_r), bias, topk, gates, int(d.N), int(d.H), int(d.E), int(d.K));
+                     static_cast<const moe::bf16_t*>(w_r), bias, topk, gates, int(d.N), int(d.H), int(d.E), int(d.K),
+                     probs, part);
   return hipGetLastError();
 }
 
@@ -553,14 +658,14 @@ __global__ __launch_bounds__(256) void k_route_dwr_reduce(const float* __restric
 }
 
 hipError_t route_bwd_mma(const Dims& d, const void* x, const int32_t* topk, const float* gates, const float* dgates,
-                         float* dlogits, float* dw_r, void* ws, hipStream_t s) {
+                         float* dlogits, float* dw_r, void* ws, hipStream_t s, AuxGrad aux) {
   using C = DwrCfg128;
   const DwrPlan p = dwr_plan(d);
   float* part = static_cast<float*>(ws);
   moe::bf16_t* planes = reinterpret_cast<moe::bf16_t*>(static_cast<char*>(ws) + p.part_bytes);
   const int64_t ne = p.n_pad * d.E;
   hipLaunchKernelGGL(k_route_bwd_dl, dim3(unsigned((ne + 255) / 256)), dim3(256), 0, s, topk, gates, dgates, dlogits,
-                     planes, int(d.N), int(p.n_pad), int(d.E), int(d.K));
+                     planes, int(d.N), int(p.n_pad), int(d.E), int(d.K), aux);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   err = moe_mma::allow_lds<k_route_dwr_mma<C>>(C::LDS);
@@ -576,39 +681,42 @@ hipError_t route_bwd_mma(const Dims& d, const void* x, const int32_t* topk, cons
   return hipGetLastError();
 }
 
-hipError_t route_bwd(const Dims& d, const void* x, const int32_t* topk, const float* gates, const float* dgates,
-                     float* dlogits, float* dw_r, void* ws, hipStream_t s) {
-  if (router_mma(d)) return route_bwd_mma(d, x, topk, gates, dgates, dlogits, dw_r, ws, s);
+static hipError_t route_bwd_impl(const Dims& d, const void* x, const int32_t* topk, const float* gates,
+                                 const float* dgates, float* dlogits, float* dw_r, void* ws, hipStream_t s,
+                                 AuxGrad aux) {
+  if (router_mma(d)) return route_bwd_mma(d, x, topk, gates, dgates, dlogits, dw_r, ws, s, aux);
   int64_t ne = d.N * d.E;
   hipLaunchKernelGGL(k_route_bwd_dl, dim3(unsigned((ne + 255) / 256)), dim3(256), 0, s, topk, gates, dgates, dlogits,
-                     nullptr, int(d.N), int(d.N), int(d.E), int(d.K));
+                     nullptr, int(d.N), int(d.N), int(d.E), int(d.K), aux);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int nch = int(route_bwd_chunks(d));
   const int chunk = int((d.N + nch - 1) / nch);
   float* part = static_cast<float*>(ws);
-  if (d.E <= 64) {  // LDS: E*HB + kRbTok*HB + 2*kRbTok*K floats <= 64 KiB
-    constexpr int HB = 64;
-    size_t lds = sizeof(float) * (size_t(d.E) * HB + size_t(kRbTok) * HB + 2 * size_t(kRbTok) * d.K);
-    dim3 grid(unsigned(d.H / HB), unsigned(nch));
+  // LDS: E*HB + kRbTok*HB + 2*kRbTok*K floats <= 64 KiB
+  auto partial = [&](auto hb, auto dense) {
+    constexpr int HB = decltype(hb)::value;
+    constexpr bool DENSE = decltype(dense)::value;
+    const size_t lds = sizeof(float) * (size_t(d.E) * HB + size_t(kRbTok) * HB + 2 * size_t(kRbTok) * d.K);
+    const dim3 grid(unsigned(d.H / HB), unsigned(nch));
     if (d.dtype == MOE_BF16)
-      hipLaunchKernelGGL((k_route_bwd_partial<moe::bf16_t, HB>), grid, dim3(HB), lds, s,
+      hipLaunchKernelGGL((k_route_bwd_partial<moe::bf16_t, HB, DENSE>), grid, dim3(HB), lds, s,
                          static_cast<const moe::bf16_t*>(x), topk, dlogits, part, int(d.N), int(d.H), int(d.E),
                          int(d.K), chunk);
     else
-      hipLaunchKernelGGL((k_route_bwd_partial<float, HB>), grid, dim3(HB), lds, s, static_cast<const float*>(x),
-                         topk, dlogits, part, int(d.N), int(d.H), int(d.E), int(d.K), chunk);
+      hipLaunchKernelGGL((k_route_bwd_partial<float, HB, DENSE>), grid, dim3(HB), lds, s,
+                         static_cast<const float*>(x), topk, dlogits, part, int(d.N), int(d.H), int(d.E), int(d.K),
+                         chunk);
+  };
+  using Dense = std::true_type;
+  using Sparse = std::false_type;
+  const bool dense = aux.probs != nullptr;
+  if (d.E <= 64) {
+    using HB = std::integral_constant<int, 64>;
+    dense ? partial(HB{}, Dense{}) : partial(HB{}, Sparse{});
   } else {
-    constexpr int HB = 32;
-    size_t lds = sizeof(float) * (size_t(d.E) * HB + size_t(kRbTok) * HB + 2 * size_t(kRbTok) * d.K);
-    dim3 grid(unsigned(d.H / HB), unsigned(nch));
-    if (d.dtype == MOE_BF16)
-      hipLaunchKernelGGL((k_route_bwd_partial<moe::bf16_t, HB>), grid, dim3(HB), lds, s,
-                         static_cast<const moe::bf16_t*>(x), topk, dlogits, part, int(d.N), int(d.H), int(d.E),
-                         int(d.K), chunk);
-    else
-      hipLaunchKernelGGL((k_route_bwd_partial<float, HB>), grid, dim3(HB), lds, s, static_cast<const float*>(x),
-                         topk, dlogits, part, int(d.N), int(d.H), int(d.E), int(d.K), chunk);
+    using HB = std::integral_constant<int, 32>;
+    dense ? partial(HB{}, Dense{}) : partial(HB{}, Sparse{});
   }
   err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -616,6 +724,55 @@ hipError_t route_bwd(const Dims& d, const void* x, const int32_t* topk, const fl
   hipLaunchKernelGGL(k_route_bwd_reduce, dim3(unsigned((nthreads + 255) / 256)), dim3(256), 0, s, part, dw_r,
                      int(d.H), int(d.E), nch);
   return hipGetLastError();
+}
+
+hipError_t route_bwd(const Dims& d, const void* x, const int32_t* topk, const float* gates, const float* dgates,
+                     float* dlogits, float* dw_r, void* ws, hipStream_t s) {
+  return route_bwd_impl(d, x, topk, gates, dgates, dlogits, dw_r, ws, s, AuxGrad{nullptr, nullptr, nullptr, 0.f, 0.f});
+}
+
+// ---- load-balancing loss
+
+// Token blocks of the probability pass (the router kernel's token tile).
+static int64_t probs_blocks(const Dims& d) {
+  const int64_t bm = router_mma(d) ? (d.E <= 128 ? RouteCfg128::BM : RouteCfg256::BM) : kRouteTok;
+  return (d.N + bm - 1) / bm;
+}
+
+size_t aux_loss_ws(const Dims& d) { return size_t(probs_blocks(d)) * size_t(d.E) * sizeof(float); }
+
+hipError_t aux_loss(const Dims& d, const void* x, const void* w_r, const float* bias, const int32_t* counts,
+                    float alpha, float* probs, float* loss, void* ws, hipStream_t s) {
+  float* part = static_cast<float*>(ws);
+  hipError_t err;
+  if (router_mma(d))
+    err = d.E <= 128 ? route_mma<RouteCfg128>(d, x, w_r, bias, nullptr, nullptr, s, probs, part)
+                     : route_mma<RouteCfg256>(d, x, w_r, bias, nullptr, nullptr, s, probs, part);
+  else if (d.dtype == MOE_BF16)
+    err = launch_route<moe::bf16_t>(d, x, w_r, bias, nullptr, nullptr, s, probs, part);
+  else
+    err = launch_route<float>(d, x, w_r, bias, nullptr, nullptr, s, probs, part);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_aux_reduce, dim3(1), dim3(256), 0, s, part, int(probs_blocks(d)), counts, int(d.N),
+                     int(d.E), int(d.K), alpha, loss);
+  return hipGetLastError();
+}
+
+// route_bwd's workspace, then s[N] of the aux term.
+static size_t route_bwd_ws_aligned(const Dims& d) { return (route_bwd_ws(d) + 255) / 256 * 256; }
+size_t route_bwd_aux_ws(const Dims& d) { return route_bwd_ws_aligned(d) + size_t(d.N) * sizeof(float); }
+
+hipError_t route_bwd_aux(const Dims& d, const void* x, const int32_t* topk, const float* gates, const float* dgates,
+                         const float* probs, const int32_t* counts, float aux_scale, float* dlogits, float* dw_r,
+                         void* ws, hipStream_t s) {
+  float* sn = reinterpret_cast<float*>(static_cast<char*>(ws) + route_bwd_ws_aligned(d));
+  const float inv_nk = 1.0f / (float(d.N) * float(d.K));
+  hipLaunchKernelGGL(k_aux_s, dim3(unsigned((d.N + 255) / 256)), dim3(256), 0, s, probs, counts, sn, int(d.N),
+                     int(d.E), inv_nk);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const AuxGrad aux{probs, counts, sn, aux_scale * float(d.E) / float(d.N), inv_nk};
+  return route_bwd_impl(d, x, topk, gates, dgates, dlogits, dw_r, ws, s, aux);
 }
 
 }  // namespace moe_launch

@@ -25,7 +25,8 @@ class MoELayerRunner:
     """Device buffers and C-ABI calls for fixed (N, H, F, E, K, dtype)."""
 
     def __init__(self, N: int, H: int, F: int, E: int, K: int, dtype: torch.dtype, device="cuda",
-                 backward: bool = True, save_gu: Optional[bool] = None):
+                 backward: bool = True, save_gu: Optional[bool] = None, aux_alpha: Optional[float] = None):
+        """aux_alpha: weight of the Switch load-balancing loss; None turns it off."""
         self.N, self.H, self.F, self.E, self.K = N, H, F, E, K
         self.dtype = dtype
         self.device = torch.device(device)
@@ -55,6 +56,11 @@ class MoELayerRunner:
         self.act = torch.empty((NK, F), dtype=dtype, device=dev)
         self.ys = torch.empty((NK, H), dtype=dtype, device=dev)
         self.y = torch.empty((N, H), dtype=dtype, device=dev)
+        self.aux_alpha = aux_alpha
+        if aux_alpha is not None:
+            self.probs = torch.empty((N, E), dtype=torch.float32, device=dev)
+            self.aux_loss = torch.empty((1,), dtype=torch.float32, device=dev)
+            self.aux_ws = self._ws(L.MOE_ENTRY_AUX_LOSS)
         if backward:
             f32 = torch.float32
             self.dys = torch.empty((NK, H), dtype=dtype, device=dev)
@@ -68,7 +74,7 @@ class MoELayerRunner:
             self.dw_up = torch.empty((E, H, F), dtype=f32, device=dev)
             self.dw_down = torch.empty((E, F, H), dtype=f32, device=dev)
             self.dx = torch.empty((N, H), dtype=dtype, device=dev)
-            self.route_ws = self._ws(L.MOE_ENTRY_ROUTE_BWD)
+            self.route_ws = self._ws(L.MOE_ENTRY_ROUTE_BWD if aux_alpha is None else L.MOE_ENTRY_ROUTE_BWD_AUX)
             self.perm_ws = self._ws(L.MOE_ENTRY_PERMUTE_BWD)
         self.inputs = None
 
@@ -99,23 +105,32 @@ class MoELayerRunner:
         L.moe_ffn_gate_up(self.d, self.xs, w_gate, w_up, self.tiles, self.num_tiles, self.g, self.u, self.act, stream)
         L.moe_ffn_down(self.d, self.act, w_down, self.tiles, self.num_tiles, self.ys, stream)
         L.moe_combine(self.d, self.ys, self.gates, self.inv, self.y, stream)
+        if self.aux_alpha is not None:
+            L.moe_aux_loss(self.d, x, w_r, bias, self.counts, self.aux_alpha, self.probs, self.aux_loss, self.aux_ws,
+                           stream)
         self.inputs = (x, w_r, w_gate, w_up, w_down)
         return self.y
 
     # ------------------------------------------------------------- backward
-    def backward(self, dy, stream=None):
-        """Run the backward of the last forward; returns a dict of gradients."""
+    def backward(self, dy, stream=None, aux_grad: float = 1.0):
+        """Run the backward of the last forward; returns a dict of gradients.
+        aux_grad: upstream gradient of the load-balancing loss (when on)."""
         if not self.with_backward:
             raise RuntimeError("runner was built without backward buffers")
         x, w_r, w_gate, w_up, w_down = self.inputs
         d = self.d
         L.moe_combine_bwd(d, dy, self.ys, self.gates, self.inv, self.dys, self.dgates, stream)
-        L.moe_route_bwd(d, x, self.topk, self.gates, self.dgates, self.dlogits, self.dw_r, self.route_ws, stream)
+        if self.aux_alpha is None:
+            L.moe_route_bwd(d, x, self.topk, self.gates, self.dgates, self.dlogits, self.dw_r, self.route_ws, stream)
+        else:
+            L.moe_route_bwd_aux(d, x, self.topk, self.gates, self.dgates, self.probs, self.counts,
+                                self.aux_alpha * aux_grad, self.dlogits, self.dw_r, self.route_ws, stream)
         L.moe_ffn_bwd_dact(d, self.dys, w_down, self.g, self.u, self.tiles, self.num_tiles, self.dg, self.du, stream)
         L.moe_ffn_bwd_dx(d, self.dg, self.du, w_gate, w_up, self.tiles, self.num_tiles, self.dxs, stream)
         L.moe_ffn_bwd_dw(d, self.xs, self.act, self.dys, self.dg, self.du, self.offsets, self.dw_gate, self.dw_up,
                          self.dw_down, stream)
-        L.moe_permute_bwd(d, self.dxs, self.inv, self.topk, self.dlogits, w_r, self.dx, self.perm_ws, stream)
+        permute_bwd = L.moe_permute_bwd if self.aux_alpha is None else L.moe_permute_bwd_dense
+        permute_bwd(d, self.dxs, self.inv, self.topk, self.dlogits, w_r, self.dx, self.perm_ws, stream)
         return dict(dx=self.dx, dw_r=self.dw_r, dw_gate=self.dw_gate, dw_up=self.dw_up, dw_down=self.dw_down,
                     dgates=self.dgates, dlogits=self.dlogits)
 

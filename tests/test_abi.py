@@ -114,3 +114,27 @@ def test_max_tiles_bounds_any_routing(lib, N, K, E):
     NK = N * K
     worst_spread = sum(math.ceil(c / L.MOE_TILE_M) for c in [NK // E + (1 if i < NK % E else 0) for i in range(E)])
     assert worst_spread <= mt
+
+
+def test_aux_loss_entries_validate_on_the_host(lib):
+    d = D(E=8)
+    lb = L.lib()
+    need = L.moe_workspace_bytes(d, L.MOE_ENTRY_AUX_LOSS)
+    assert need > 0 and need != 2 ** 64 - 1
+    # bad alpha, null pointers, short workspace
+    assert lb.moe_aux_loss(ctypes.byref(d), FAKE, FAKE, None, FAKE, float("nan"), FAKE, FAKE, FAKE, need,
+                           None) == L.MOE_EINVAL
+    assert lb.moe_aux_loss(ctypes.byref(d), FAKE, FAKE, None, None, 0.01, FAKE, FAKE, FAKE, need, None) == L.MOE_EINVAL
+    assert lb.moe_aux_loss(ctypes.byref(d), FAKE, FAKE, None, FAKE, 0.01, FAKE, FAKE, FAKE, need - 4,
+                           None) == L.MOE_EWORKSPACE
+    need_b = L.moe_workspace_bytes(d, L.MOE_ENTRY_ROUTE_BWD_AUX)
+    assert need_b >= L.moe_workspace_bytes(d, L.MOE_ENTRY_ROUTE_BWD) + d.N * 4
+    args = [FAKE] * 6
+    assert lb.moe_route_bwd_aux(ctypes.byref(d), *args, float("inf"), FAKE, FAKE, FAKE, need_b, None) == L.MOE_EINVAL
+    assert lb.moe_route_bwd_aux(ctypes.byref(d), *args, 0.01, FAKE, FAKE, FAKE, need_b - 1,
+                                None) == L.MOE_EWORKSPACE
+    need_p = L.moe_workspace_bytes(d, L.MOE_ENTRY_PERMUTE_BWD)
+    assert lb.moe_permute_bwd_dense(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need_p - 16,
+                                    None) == L.MOE_EWORKSPACE
+    d0 = D(N=0)
+    assert lb.moe_aux_loss(ctypes.byref(d0), FAKE, FAKE, None, FAKE, 0.01, FAKE, FAKE, None, 0, None) == L.MOE_OK
