@@ -10,20 +10,29 @@
 // synchronisation is needed: the grid is sized for the largest possible tile
 // count and workgroups past the real count return at once.
 //
-// Workgroup tile 256 x 256, K step 64, 8 waves in a 4 x 2 arrangement, 64 x
-// 128 per wave.  A 256 x 256 x 64 step moves 64 KB from L2 for 8.4 MFLOP.
-// Used for the long contractions; gemm_bf16_small.hip holds the 128 x 128
-// shape for small problems.
-// Operands go from global memory straight into LDS with the gfx950 LDS DMA
-// (16 bytes per lane, no register staging) into two stages: while the block
-// multiplies one K tile the DMA of the next one is in flight.  A K-contiguous
-// operand (token rows; weight rows in the backward) lands as [rows][64 k] and
-// is read with 16-byte fragment loads; an MN-contiguous operand (the weights
-// in the forward, both operands of the weight gradients) lands as
-// [64 k][columns] and is read with the transposing LDS load
-// (ds_read_b64_tr_b16), so no operand is ever transposed in registers.  Both
-// layouts XOR-swizzle 16-byte chunks by row so the fragment reads are free of
-// bank conflicts.  Output tiles leave through LDS with 16-byte row stores.
+// Workgroup tile 256 x 256, K step 64.  A 256 x 256 x 64 step moves 64 KB
+// from L2 for 8.4 MFLOP.  Used for the long contractions;
+// gemm_bf16_small.hip holds the 128 x 128 shape for short ones.
+//
+// Main configuration (Big): 4 waves in a 2 x 2 arrangement, 128 x 128 per
+// wave (256 accumulator registers each, one workgroup per CU).  Each thread
+// requests its 16-byte chunks of the next K tile into registers, one request
+// per two MFMAs over the first half of the step, and stores them into the
+// other LDS stage between the last k step's MFMAs; one barrier per step.
+// Spreading the requests keeps each wave's in-order issue from parking its
+// MFMAs behind a burst of loads, which is what held the LDS DMA version of
+// this loop near 0.8 PFLOP/s.  The SwiGLU backward keeps an 8-wave
+// configuration through the LDS DMA pipeline (BigDma): its G/U epilogue
+// wants more waves to issue loads.
+//
+// A K-contiguous operand (token rows; weight rows in the backward) sits in
+// LDS as [rows][64 k] and is read with 16-byte fragment loads; an
+// MN-contiguous operand (the weights in the forward, both operands of the
+// weight gradients) sits as [64 k][columns] and is read with the transposing
+// LDS load (ds_read_b64_tr_b16), so no operand is ever transposed in
+// registers.  Both layouts XOR-swizzle 16-byte chunks by row so the fragment
+// reads are free of bank conflicts.  Output tiles leave through LDS with
+// 16-byte row stores.
 //
 // Tails: N (and, for the weight gradients, M) may end on a 128 boundary
 // inside a tile; loads past the end read clamped in-bounds positions whose
@@ -40,13 +49,18 @@ using namespace moe;
 
 using namespace moe_mma;
 
-using Big = TileCfg<256, 256, 4, 2, 1, 64, 2>;  // 8 waves, 64 x 128 per wave
+using Big = TileCfg<256, 256, 2, 2, 1, 64, 2, true>;  // 4 waves, 128 x 128 per wave, register-staged
+// 8 waves of 64 x 128 through the LDS DMA pipeline: kept for the SwiGLU
+// backward, whose G/U epilogue runs with twice as many waves to issue its
+// loads.
+using BigDma = TileCfg<256, 256, 4, 2, 1, 64, 2>;
 // 128 x 256 tiles through the same DMA pipeline, 32 k per stage, three stages
 // (72 KiB of LDS, two workgroups per CU): used by the SwiGLU backward on
 // short contractions, where its staged epilogue of G and U overlaps better
 // across workgroups than the register-staged kernels'.
 using Mid = TileCfg<128, 256, 2, 4, 2, 32, 3>;
-static_assert(MOE_TILE_M % Big::BM == 0 && MOE_TILE_M % Mid::BM == 0, "list tiles split into row tiles");
+static_assert(MOE_TILE_M % Big::BM == 0 && MOE_TILE_M % BigDma::BM == 0 && MOE_TILE_M % Mid::BM == 0,
+              "list tiles split into row tiles");
 
 // staged tile <- bf16(acc)
 template <class C>
@@ -83,6 +97,8 @@ __device__ __forceinline__ void epi_load(bf16_t* stg, const bf16_t* in, int64_t 
     *reinterpret_cast<uint4*>(stg + r * C::PITCH + c * 8) =
         *reinterpret_cast<const uint4*>(in + (int64_t)r * ld + c * 8);
 }
+
+constexpr int kNoSplit = 1 << 30;  // single-source K-contiguous operand
 
 struct TileInfo {
   int e, row0, rows;
@@ -155,13 +171,19 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_gate_up(const bf16_t* __rest
   const bf16_t* b_u = wu + eoff - HALF;
 
   Acc<C> acc;
-  k_loop<C, false, true>(
-      lds, acc, H / C::BK,
-      [&](int kt, char* st, int j) { dma_kc<C::BM, C::BK, C::NW>(st, a_base + kt * C::BK, H, ti.rows, j); },
-      [&](int kt, char* st, int j) {
-        dma_mn<C::BN, C::BK, C::NW>(st, b_g + (int64_t)kt * C::BK * F, b_u + (int64_t)kt * C::BK * F, HALF, F, C::BK, C::BN, j);
-      },
-      wm, wn);
+  if constexpr (C::REG) {
+    k_loop_reg<C, false, true>(lds, acc, H / C::BK, KcOp<C::BM, C::BK, C::NT>(a_base, a_base, kNoSplit, H, ti.rows),
+                               MnOp<C::BN, C::BK, C::NT>(b_g, b_u, HALF, F, C::BN, H), wm, wn);
+  } else {
+    k_loop<C, false, true>(
+        lds, acc, H / C::BK,
+        [&](int kt, char* st, int j) { dma_kc<C::BM, C::BK, C::NW>(st, a_base + kt * C::BK, H, ti.rows, j); },
+        [&](int kt, char* st, int j) {
+          dma_mn<C::BN, C::BK, C::NW>(st, b_g + (int64_t)kt * C::BK * F, b_u + (int64_t)kt * C::BK * F, HALF, F,
+                                      C::BK, C::BN, j);
+        },
+        wm, wn);
+  }
 
   // staged tile: columns 0..HALF-1 = G, HALF..BN-1 = U (bf16)
   bf16_t* stg = reinterpret_cast<bf16_t*>(lds);
@@ -210,13 +232,19 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_down(const bf16_t* __restric
   const bf16_t* a_base = act + (int64_t)ti.row0 * F;
   const bf16_t* b_base = wd + (int64_t)ti.e * F * H + nt * C::BN;
   Acc<C> acc;
-  k_loop<C, false, true>(
-      lds, acc, F / C::BK, [&](int kt, char* st, int j) { dma_kc<C::BM, C::BK, C::NW>(st, a_base + kt * C::BK, F, ti.rows, j); },
-      [&](int kt, char* st, int j) {
-        const bf16_t* b = b_base + (int64_t)kt * C::BK * H;
-        dma_mn<C::BN, C::BK, C::NW>(st, b, b, C::BN, H, C::BK, ncols, j);
-      },
-      wm, wn);
+  if constexpr (C::REG) {
+    k_loop_reg<C, false, true>(lds, acc, F / C::BK, KcOp<C::BM, C::BK, C::NT>(a_base, a_base, kNoSplit, F, ti.rows),
+                               MnOp<C::BN, C::BK, C::NT>(b_base, b_base, C::BN, H, ncols, F), wm, wn);
+  } else {
+    k_loop<C, false, true>(
+        lds, acc, F / C::BK,
+        [&](int kt, char* st, int j) { dma_kc<C::BM, C::BK, C::NW>(st, a_base + kt * C::BK, F, ti.rows, j); },
+        [&](int kt, char* st, int j) {
+          const bf16_t* b = b_base + (int64_t)kt * C::BK * H;
+          dma_mn<C::BN, C::BK, C::NW>(st, b, b, C::BN, H, C::BK, ncols, j);
+        },
+        wm, wn);
+  }
   bf16_t* stg = reinterpret_cast<bf16_t*>(lds);
   epi_put<C>(stg, acc, wm, wn);
   __syncthreads();
@@ -246,9 +274,15 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_dact(const bf16_t* __restric
   // B[k = h][n = f] = W_down[e][f][h]: rows f of W_down[e] are k-contiguous
   const bf16_t* b_base = wd + (int64_t)ti.e * F * H + (int64_t)nt * C::BN * H;
   Acc<C> acc;
-  k_loop<C, false, false>(
-      lds, acc, H / C::BK, [&](int kt, char* st, int j) { dma_kc<C::BM, C::BK, C::NW>(st, a_base + kt * C::BK, H, ti.rows, j); },
-      [&](int kt, char* st, int j) { dma_kc<C::BN, C::BK, C::NW>(st, b_base + kt * C::BK, H, ncols, j); }, wm, wn);
+  if constexpr (C::REG) {
+    k_loop_reg<C, false, false>(lds, acc, H / C::BK, KcOp<C::BM, C::BK, C::NT>(a_base, a_base, kNoSplit, H, ti.rows),
+                                KcOp<C::BN, C::BK, C::NT>(b_base, b_base, kNoSplit, H, ncols), wm, wn);
+  } else {
+    k_loop<C, false, false>(
+        lds, acc, H / C::BK,
+        [&](int kt, char* st, int j) { dma_kc<C::BM, C::BK, C::NW>(st, a_base + kt * C::BK, H, ti.rows, j); },
+        [&](int kt, char* st, int j) { dma_kc<C::BN, C::BK, C::NW>(st, b_base + kt * C::BK, H, ncols, j); }, wm, wn);
+  }
 
   // Epilogue one wave row (TM rows) at a time: the G and U rows are staged
   // side by side, the waves owning those rows turn them into dG and dU in
@@ -310,6 +344,12 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_dx(const bf16_t* __restrict_
   const int64_t woff = (int64_t)ti.e * H * F + (int64_t)nt * C::BN * F;
   const int nkf = F / C::BK;
   Acc<C> acc;
+  if constexpr (C::REG) {
+    const int64_t aoff = (int64_t)ti.row0 * F;
+    k_loop_reg<C, false, false>(lds, acc, 2 * nkf,
+                                KcOp<C::BM, C::BK, C::NT>(dg + aoff, du + aoff, nkf, F, ti.rows),
+                                KcOp<C::BN, C::BK, C::NT>(wg + woff, wu + woff, nkf, F, ncols), wm, wn);
+  } else {
   k_loop<C, false, false>(
       lds, acc, 2 * nkf,
       [&](int kt, char* st, int j) {
@@ -322,6 +362,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_dx(const bf16_t* __restrict_
         dma_kc<C::BN, C::BK, C::NW>(st, (second ? wu : wg) + woff + (second ? kt - nkf : kt) * C::BK, F, ncols, j);
       },
       wm, wn);
+  }
   bf16_t* stg = reinterpret_cast<bf16_t*>(lds);
   epi_put<C>(stg, acc, wm, wn);
   __syncthreads();
@@ -372,6 +413,11 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_dw(const bf16_t* __restrict_
   const bf16_t* r_base = Rm + (int64_t)r0 * Q + nt * C::BN;
   Acc<C> acc;
   const int nk = (cnt + C::BK - 1) / C::BK;
+  if constexpr (C::REG) {
+    k_loop_reg<C, true, true>(lds, acc, nk, MnOp<C::BM, C::BK, C::NT>(l_base, l_base, C::BM, P, prow, cnt),
+                              MnOp<C::BN, C::BK, C::NT>(r_base, r_base, C::BN, Q, qcol, cnt), wm, wn,
+                              cnt - (nk - 1) * C::BK);
+  } else {
   k_loop<C, true, true>(
       lds, acc, nk,
       [&](int kt, char* st, int j) {
@@ -383,6 +429,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_dw(const bf16_t* __restrict_
         dma_mn<C::BN, C::BK, C::NW>(st, b, b, C::BN, Q, cnt - kt * C::BK, qcol, j);
       },
       wm, wn, cnt - (nk - 1) * C::BK);
+  }
   const int lr = lane_row<C>(wm), lc = lane_col<C>(wn);
   float* o = out + (int64_t)(mt * C::BM + lr) * Q + nt * C::BN + lc;
 #pragma unroll
@@ -452,7 +499,7 @@ static hipError_t dact_t(const Dims& d, const void* dys, const void* wd, const v
 
 hipError_t ffn_bwd_dact_big(const Dims& d, const void* dys, const void* wd, const void* g, const void* u,
                              const int32_t* tiles, const int32_t* num_tiles, void* dg, void* du, hipStream_t s) {
-  return dact_t<Big>(d, dys, wd, g, u, tiles, num_tiles, dg, du, s);
+  return dact_t<BigDma>(d, dys, wd, g, u, tiles, num_tiles, dg, du, s);
 }
 
 hipError_t ffn_bwd_dact_mid(const Dims& d, const void* dys, const void* wd, const void* g, const void* u,

@@ -6,6 +6,9 @@
 // with one thread per output element and the contraction in ascending k.
 // This path exists for the fp32 storage type (small correctness-sized
 // problems); the bf16 path carries the performance.
+#include <cstdlib>
+#include <cstring>
+
 #include "common.h"
 
 namespace {
@@ -157,25 +160,39 @@ MOE_BF16_SHAPE(ffn_bwd_dw, const void*, const void*, const void*, const void*, c
 #undef MOE_BF16_SHAPE
 
 // Which bf16 tile shape each stage uses.  The 256 x 256 tiles (one workgroup
-// per CU, LDS DMA, 132 KiB of LDS) win on long contractions with enough tiles
-// to fill the chip; the 128 x 128 tiles (2-3 workgroups per CU) hide latency
-// better on short contractions, on memory-bound shapes (few rows per
-// expert) and where the big tiles would leave CUs idle.  Measured on MI355X
-// per stage over the shapes (H, F, rows per expert) = (512, 1024, 4096),
-// (2048, 1408, skewed 0..16k), (7168, 2048, 256), (4096, 14336, 4096):
-//   gate/up and down: 256 x 256 only for long contractions (H resp. F >=
-//   4096) over many rows per expert (NK / E >= 2048), else 128 x 128;
-//   dA (contraction H): 256 x 256 from H = 4096 on, below that 128 x 256
-//   tiles through the LDS DMA pipeline (their staged SwiGLU epilogue beats
-//   the register-staged kernel's);
+// per CU: 4 waves of 128 x 128 with register-staged loads, or, for dA, 8
+// waves of 64 x 128 through the LDS DMA) win on long contractions; the
+// 128 x 128 tiles (2-3 workgroups per CU) hide latency better on short ones,
+// where a 256 x 256 tile spends a large share of its time in its prologue and
+// epilogue.  Measured on MI355X per stage over the shapes (H, F, rows per
+// expert) = (512, 1024, 4096), (2048, 1408, skewed 0..16k), (7168, 2048,
+// 256), (4096, 14336, 4096):
+//   gate/up (contraction H): 256 x 256 from H = 2048 on, else 128 x 128;
+//   down (contraction F): 256 x 256 from F = 1280 on, else 128 x 128;
+//   dA (contraction H): 256 x 256 (8 waves, LDS DMA) from H = 4096 on, below
+//   that 128 x 256 tiles through the LDS DMA pipeline (their staged SwiGLU
+//   epilogue overlaps across two workgroups per CU);
 //   dX (contraction 2F): 256 x 256 from 2F = 2560 on;
-//   dW (contraction over an expert's rows): 256 x 256 when it makes at least
-//   4 tiles per CU (3 E H F / 256^2 >= 1024), else 128 x 128.
-static bool big_gate_up(const Dims& d) { return d.H >= 4096 && d.NK() / d.E >= 2048; }
-static bool big_down(const Dims& d) { return d.F >= 4096 && d.NK() / d.E >= 2048; }
-static bool big_dact(const Dims& d) { return d.H >= 4096; }
-static bool big_dx(const Dims& d) { return 2 * d.F >= 2560; }
-static bool big_dw(const Dims& d) { return 3 * d.E * (d.H / 256) * (d.F / 256) >= 1024; }
+//   dW (contraction over an expert's rows): 256 x 256 throughout.
+// MOE_GEMM_TILES=256 or =128 in the environment (read at every launch)
+// overrides the choice for every stage (128 selects the 128 x 256 dA tiles);
+// any other value, or none, keeps the measured choice.
+static int tile_override() {
+  const char* v = std::getenv("MOE_GEMM_TILES");
+  if (v == nullptr) return -1;
+  if (std::strcmp(v, "256") == 0) return 1;
+  if (std::strcmp(v, "128") == 0) return 0;
+  return -1;
+}
+static bool pick(bool measured) {
+  const int o = tile_override();
+  return o < 0 ? measured : o == 1;
+}
+static bool big_gate_up(const Dims& d) { return pick(d.H >= 2048); }
+static bool big_down(const Dims& d) { return pick(d.F >= 1280); }
+static bool big_dact(const Dims& d) { return pick(d.H >= 4096); }
+static bool big_dx(const Dims& d) { return pick(2 * d.F >= 2560); }
+static bool big_dw(const Dims&) { return pick(true); }
 
 hipError_t ffn_gate_up(const Dims& d, const void* xs, const void* wg, const void* wu, const int32_t* tiles,
                        const int32_t* num_tiles, void* g, void* u, void* a, hipStream_t s) {

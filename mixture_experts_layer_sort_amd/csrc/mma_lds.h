@@ -12,9 +12,10 @@
 namespace moe_mma {
 using namespace moe;
 
-template <int BM_, int BN_, int WM_, int WN_, int MINB_, int BK_, int S_>
+template <int BM_, int BN_, int WM_, int WN_, int MINB_, int BK_, int S_, bool REG_ = false>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr bool REG = REG_;   // register-staged K loop (k_loop_reg) instead of the LDS DMA (k_loop)
   static constexpr int MINB = MINB_;  // workgroups per CU the registers must allow
   static constexpr int BK = BK_;      // K depth of one pipeline stage (32 or 64)
   static constexpr int S = S_;        // pipeline stages in LDS
@@ -38,6 +39,7 @@ struct TileCfg {
 };
 
 #define LDS_AS __attribute__((address_space(3)))
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef short v4s_t __attribute__((ext_vector_type(4)));
 typedef short v8s_t __attribute__((ext_vector_type(8)));
 
@@ -232,6 +234,162 @@ __device__ __forceinline__ void k_loop(char* lds, Acc<C>& acc, int nk, IA ia, IB
     mma_stage<C, A_MN, B_MN>(cur, cur + C::A_BYTES, acc, wm, wn);
   }
   __syncthreads();
+}
+
+// ---- register-staged operand tiles (same LDS layouts as the DMA tiles)
+//
+// Thread t of the workgroup moves the 16-byte chunks q = t + i * NT of a
+// tile: global memory -> registers (issued early, spread between MFMAs) ->
+// LDS (after the MFMAs that read the other stage).
+
+// K-contiguous operand: ROWS rows x BK k of a row-major matrix (leading
+// dimension ld).  K tile kt starts at k = kt * BK of base0, or, from tile
+// nk0 on, at k = (kt - nk0) * BK of base1 (two stacked contractions).  Rows
+// at or past rows_valid read row rows_valid - 1 (results never stored).
+template <int ROWS, int BK, int NT>
+struct KcOp {
+  static constexpr int CPR = BK / 8, RP = NT / CPR, N = ROWS / RP;
+  static_assert(NT % CPR == 0 && ROWS % RP == 0, "chunks split evenly over the threads");
+  const bf16_t *base0, *base1;
+  int nk0;
+  int off[N];  // element offset of chunk i within a K tile
+  __device__ __forceinline__ KcOp(const bf16_t* b0, const bf16_t* b1, int nk0_, int64_t ld, int rows_valid)
+      : base0(b0), base1(b1), nk0(nk0_) {
+    const int r0 = threadIdx.x / CPR, c = threadIdx.x % CPR;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int r = r0 + i * RP;
+      off[i] = int((r < rows_valid ? r : rows_valid - 1) * ld) + c * 8;
+    }
+  }
+  __device__ __forceinline__ void load(u32x4_t (&v)[N], int kt) const {
+    const bf16_t* p = kt < nk0 ? base0 + kt * BK : base1 + (kt - nk0) * BK;
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = *reinterpret_cast<const u32x4_t*>(p + off[i]);
+  }
+  __device__ __forceinline__ void store(const u32x4_t (&v)[N], char* st, int) const {
+    const int r0 = threadIdx.x / CPR, c = threadIdx.x % CPR;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int r = r0 + i * RP;
+      *reinterpret_cast<u32x4_t*>(st + r * (2 * BK) + ((c ^ fk<BK>(r)) << 4)) = v[i];
+    }
+  }
+};
+
+// MN-contiguous operand: BK k rows x COLS columns of a row-major matrix
+// (leading dimension ld); K tile kt covers k rows [kt * BK, kt * BK + BK).
+// Columns [0, split) come from base0 and [split, COLS) from base1 (both
+// indexed by the tile column); columns at or past cols_valid read a clamped
+// column (results discarded); k rows at or past k_total read the last valid
+// row (k_loop_reg zeroes them in the A operand).
+template <int COLS, int BK, int NT>
+struct MnOp {
+  static constexpr int CPR = COLS / 8, KP = NT / CPR, N = BK / KP;
+  static_assert(NT % CPR == 0 && BK % KP == 0, "chunks split evenly over the threads");
+  const bf16_t* base;  // this thread's column, k row 0
+  int64_t ld;
+  int k_total;
+  __device__ __forceinline__ MnOp(const bf16_t* b0, const bf16_t* b1, int split, int64_t ld_, int cols_valid,
+                                  int k_total_)
+      : ld(ld_), k_total(k_total_) {
+    const int c = threadIdx.x % CPR;
+    const int cs = c * 8 < cols_valid ? c : (cols_valid >> 3) - 1;
+    base = (cs * 8 < split ? b0 : b1) + (int64_t)(threadIdx.x / CPR) * ld_ + cs * 8;
+  }
+  // rows past the valid ones (at least one valid row per loaded tile) read the
+  // tile's last valid row
+  __device__ __forceinline__ void load(u32x4_t (&v)[N], int kt) const {
+    const int k0 = threadIdx.x / CPR;
+    const int kv = k_total - kt * BK;  // valid k rows of the tile
+    const bf16_t* p = base + (int64_t)kt * BK * ld;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int k = k0 + i * KP < kv ? i * KP : kv - 1 - k0;  // relative to this thread's first row
+      v[i] = *reinterpret_cast<const u32x4_t*>(p + (int64_t)k * ld);
+    }
+  }
+  __device__ __forceinline__ void store(const u32x4_t (&v)[N], char* st, int) const {
+    const int k0 = threadIdx.x / CPR, c = threadIdx.x % CPR;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int k = k0 + i * KP;
+      *reinterpret_cast<u32x4_t*>(st + k * (COLS * 2) + ((c ^ fm(k)) << 4)) = v[i];
+    }
+  }
+};
+
+// Register-staged K loop over two LDS stages, for 64-deep stages (four MFMA
+// k steps).  Each step: the k-step-0 fragments of the current stage are read,
+// the next K tile's chunks are requested into registers one per two MFMAs
+// over k steps 0 and 1, k steps 1..3's fragments are read one per MFMA while
+// the previous k step multiplies, the chunks go to the other stage between
+// k step 3's MFMAs, and one barrier ends the step.  The last step reloads its
+// own tile (in bounds, never read).  Spreading the requests keeps the wave's
+// in-order issue from stalling its MFMAs behind a burst of loads.  When the
+// last tile holds only k_last valid k rows (weight gradients), rows k_last..
+// of its A stage (an MN tile) are zeroed before it is used.
+template <class C, bool A_MN, bool B_MN, class OA, class OB>
+__device__ __forceinline__ void k_loop_reg(char* lds, Acc<C>& acc, int nk, const OA& oa, const OB& ob, int wm,
+                                           int wn, int k_last = C::BK) {
+  constexpr int KK = C::BK / 16;
+  constexpr int FR = C::FM * (A_MN ? 2 : 1) + C::FN * (B_MN ? 2 : 1);  // LDS reads per k step
+  constexpr int MK = C::FM * C::FN;                                    // MFMAs per k step
+  constexpr int GL = OA::N + OB::N;                                    // chunks per thread and tile
+  static_assert(KK == 4 && C::S == 2, "four k steps per stage, two stages");
+  static_assert(GL % 2 == 0 && GL <= MK && FR <= MK, "schedule fits the MFMAs of a k step");
+  zero_acc(acc);
+  if (nk <= 0) return;
+  u32x4_t va[OA::N], vb[OB::N];
+  oa.load(va, 0);
+  ob.load(vb, 0);
+  oa.store(va, lds, 0);
+  ob.store(vb, lds + C::A_BYTES, 0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    char* cur = lds + (kt & 1) * C::STAGE;
+    char* nxt = lds + ((kt + 1) & 1) * C::STAGE;
+    const int kn = kt + 1 < nk ? kt + 1 : kt;
+    if (A_MN && kt == nk - 1 && k_last < C::BK) {
+      constexpr int ROWB = C::BM * 2;
+      u32x4_t* z = reinterpret_cast<u32x4_t*>(cur + k_last * ROWB);
+      for (int i = threadIdx.x; i < (C::BK - k_last) * ROWB / 16; i += C::NT) z[i] = u32x4_t{0u, 0u, 0u, 0u};
+      __syncthreads();
+    }
+    bf16x8_t fa[2][C::FM], fb[2][C::FN];
+    load_frags<C, A_MN, B_MN>(cur, cur + C::A_BYTES, 0, wm, wn, fa[0], fb[0]);
+    oa.load(va, kn);
+    ob.load(vb, kn);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int cb = kk & 1;
+      if (kk + 1 < KK) load_frags<C, A_MN, B_MN>(cur, cur + C::A_BYTES, kk + 1, wm, wn, fa[cb ^ 1], fb[cb ^ 1]);
+#pragma unroll
+      for (int mi = 0; mi < C::FM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < C::FN; ++ni)
+          acc.a[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cb][mi], fb[cb][ni], acc.a[mi][ni], 0, 0, 0);
+    }
+    oa.store(va, nxt, kn);
+    ob.store(vb, nxt + C::A_BYTES, kn);
+    // instruction order of the step (masks: 0x008 MFMA, 0x020 VMEM read,
+    // 0x100 LDS read, 0x200 LDS write)
+    __builtin_amdgcn_sched_group_barrier(0x100, FR, 0);
+#pragma unroll
+    for (int kk = 0; kk + 1 < KK; ++kk)
+#pragma unroll
+      for (int i = 0; i < MK; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < FR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (kk < 2 && i % 2 == 0 && i / 2 < GL / 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+#pragma unroll
+    for (int i = 0; i < MK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < GL) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    }
+    __syncthreads();
+  }
 }
 
 // Accumulator element r of fragment (mi, ni): MFMA 32x32 result layout
