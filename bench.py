@@ -38,13 +38,13 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # kernel sources whose hash is stored with them; once any source under csrc/
 # changes, the figure is reported as null until the counters are taken again.
 TRAFFIC = {
-    "sources": "ee08f8f5b711be9e",
+    "sources": "aa8cfd277f7cf79b",
     "bytes": {
-        ("bf16_n16384_h512_f1024_e8_k2", "gate_up"): 336450432,
-        ("bf16_n16384_h512_f1024_e8_k2", "down"): 144055445,
-        ("bf16_n16384_h512_f1024_e8_k2", "dact"): 339665280,
-        ("bf16_n16384_h512_f1024_e8_k2", "dx"): 272201165,
-        ("bf16_n16384_h512_f1024_e8_k2", "dw"): 862152466,
+        ("bf16_n16384_h512_f1024_e8_k2", "gate_up"): 336237477,
+        ("bf16_n16384_h512_f1024_e8_k2", "down"): 144180094,
+        ("bf16_n16384_h512_f1024_e8_k2", "dact"): 339640637,
+        ("bf16_n16384_h512_f1024_e8_k2", "dx"): 272830856,
+        ("bf16_n16384_h512_f1024_e8_k2", "dw"): 352732447,
     },
 }
 
@@ -73,6 +73,8 @@ def parse():
     p.add_argument("--config", default="bf16_n16384_h512_f1024_e8_k2")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--aux-alpha", type=float, default=None,
+                   help="also compute the Switch load-balancing loss with this weight (forward and its gradient)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain 1 GiB streaming copy (for scaling HBM byte counters) and exit")
     return p.parse_args()
@@ -102,11 +104,11 @@ def stage_flops(cfg):
     return {"gate_up": 4 * hf, "down": 2 * hf, "dact": 2 * hf, "dx": 4 * hf, "dw": 6 * hf}
 
 
-def stage_bytes(cfg):
+def stage_bytes(cfg, aux=False):
     """Algorithmic HBM bytes of the row-movement and metadata stages."""
     e = 2 if cfg.dtype == "bf16" else 4
     N, NK, H, E, K = cfg.N, cfg.NK, cfg.H, cfg.E, cfg.K
-    return {
+    out = {
         "route": N * H * e + H * E * e + N * K * 8,
         "meta": NK * 4 * 3 + NK * 8 + (2 * E + 1) * 4,
         "permute": (N + NK) * H * e + NK * 4,           # read each token once (cached), write NK rows
@@ -115,6 +117,13 @@ def stage_bytes(cfg):
         "permute_bwd": (NK + N) * H * e + NK * 8 + N * K * 4,
         "route_bwd": N * H * e + N * K * 12 + N * E * 4 + H * E * 4,
     }
+    if aux:
+        # load-balancing loss: x and W_r read, probabilities [N, E] written;
+        # its gradient reads them back (dense dlogits) and dx reads all E
+        out["aux_loss"] = N * H * e + H * E * e + N * E * 4 + E * 4
+        out["route_bwd"] += 2 * N * E * 4
+        out["permute_bwd"] += N * E * 4
+    return out
 
 
 def main():
@@ -145,7 +154,9 @@ def main():
         cpu = make_inputs(cfg, args.seed, with_dy=cfg.backward)
         inp = {k: (None if v is None else v.to(dev)) for k, v in cpu.items()}
     torch.cuda.synchronize()
-    r = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, dev, backward=cfg.backward)
+    aux = args.aux_alpha
+    r = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, dev, backward=cfg.backward,
+                       aux_alpha=aux)
     d = r.d
     x, w_r, wg, wu, wd, bias, dy = (inp[k] for k in ("x", "w_r", "w_gate", "w_up", "w_down", "bias", "dy"))
     stream = torch.cuda.current_stream()
@@ -158,16 +169,23 @@ def main():
         yield "gate_up", lambda: L.moe_ffn_gate_up(d, r.xs, wg, wu, r.tiles, r.num_tiles, r.g, r.u, r.act, stream)
         yield "down", lambda: L.moe_ffn_down(d, r.act, wd, r.tiles, r.num_tiles, r.ys, stream)
         yield "combine", lambda: L.moe_combine(d, r.ys, r.gates, r.inv, r.y, stream)
+        if aux is not None:
+            yield "aux_loss", lambda: L.moe_aux_loss(d, x, w_r, bias, r.counts, aux, r.probs, r.aux_loss, r.aux_ws,
+                                                     stream)
         if cfg.backward:
             yield "combine_bwd", lambda: L.moe_combine_bwd(d, dy, r.ys, r.gates, r.inv, r.dys, r.dgates, stream)
-            yield "route_bwd", lambda: L.moe_route_bwd(d, x, r.topk, r.gates, r.dgates, r.dlogits, r.dw_r,
-                                                       r.route_ws, stream)
+            if aux is None:
+                yield "route_bwd", lambda: L.moe_route_bwd(d, x, r.topk, r.gates, r.dgates, r.dlogits, r.dw_r,
+                                                           r.route_ws, stream)
+            else:
+                yield "route_bwd", lambda: L.moe_route_bwd_aux(d, x, r.topk, r.gates, r.dgates, r.probs, r.counts,
+                                                               aux, r.dlogits, r.dw_r, r.route_ws, stream)
             yield "dact", lambda: L.moe_ffn_bwd_dact(d, r.dys, wd, r.g, r.u, r.tiles, r.num_tiles, r.dg, r.du, stream)
             yield "dx", lambda: L.moe_ffn_bwd_dx(d, r.dg, r.du, wg, wu, r.tiles, r.num_tiles, r.dxs, stream)
             yield "dw", lambda: L.moe_ffn_bwd_dw(d, r.xs, r.act, r.dys, r.dg, r.du, r.offsets, r.dw_gate, r.dw_up,
                                                  r.dw_down, stream)
-            yield "permute_bwd", lambda: L.moe_permute_bwd(d, r.dxs, r.inv, r.topk, r.dlogits, w_r, r.dx, r.perm_ws,
-                                                           stream)
+            permute_bwd = L.moe_permute_bwd if aux is None else L.moe_permute_bwd_dense
+            yield "permute_bwd", lambda: permute_bwd(d, r.dxs, r.inv, r.topk, r.dlogits, w_r, r.dx, r.perm_ws, stream)
 
     def step(ev=None, only=None):
         for name, fn in stages():
@@ -214,25 +232,25 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "algorithmic_flops_per_launch": fl[dominant], "launch_ms": round(dom_ms, 5)}
     else:
-        byt = stage_bytes(cfg)[dominant]
+        byt = stage_bytes(cfg, aux is not None)[dominant]
         achieved = byt / (dom_ms * 1e-3) / 1e9
         roof = {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                 "algorithmic_bytes_per_launch": byt, "launch_ms": round(dom_ms, 5)}
-    roof["traffic"] = measured_traffic(cfg.name, dominant)
+    roof["traffic"] = measured_traffic(cfg.name, dominant) if aux is None else None
 
     counts = r.counts.cpu().numpy().astype(np.float64)
     tbar = cfg.NK / cfg.E
     maxvio = float(counts.max() / tbar - 1.0)
 
     hbm = {}
-    for k, b in stage_bytes(cfg).items():
+    for k, b in stage_bytes(cfg, aux is not None).items():
         if k in stage_ms and stage_ms[k] > 0:
             hbm[k] = round(b / (stage_ms[k] * 1e-3) / 1e9, 1)
 
     cpu_base = None
     if not args.no_cpu_baseline and not big:
-        cpu_base = cpu_baseline(cfg, cpu)
+        cpu_base = cpu_baseline(cfg, cpu, aux)
 
     out = {
         "metric": "MoE layer tokens/sec fwd+bwd; grouped-GEMM % of bf16 MFMA peak",
@@ -249,6 +267,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.description, "N": cfg.N, "H": cfg.H, "F": cfg.F, "E": cfg.E, "K": cfg.K,
                    "backward": cfg.backward, "parallelism": "single GPU", "maxvio": round(maxvio, 4),
+                   "load_balancing_loss_alpha": aux,
                    "empty_experts": int((counts == 0).sum())},
         "grouped_gemm": {"tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 2),
                          "frac_of_bf16_peak": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
@@ -262,7 +281,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(cfg, cpu):
+def cpu_baseline(cfg, cpu, aux=None):
     """The oracle (as it stands) on the host: whole-layer passes over the
     workload's first S tokens, repeated until about 12 s have passed."""
     import torch
@@ -277,8 +296,10 @@ def cpu_baseline(cfg, cpu):
     passes = 0
     while True:
         f = O.forward(x, cpu["w_r"], cpu["w_gate"], cpu["w_up"], cpu["w_down"], cfg.K, bias=cpu["bias"], store=store)
+        if aux is not None:
+            O.aux_loss(f["logits"], f["counts"], cfg.K, aux)
         if dy is not None:
-            O.backward(f, dy)
+            O.backward(f, dy, aux_scale=aux)
         passes += 1
         if time.perf_counter() - t0 > 12.0 or passes >= 20:
             break

@@ -59,7 +59,12 @@ using BigDma = TileCfg<256, 256, 4, 2, 1, 64, 2>;
 // short contractions, where its staged epilogue of G and U overlaps better
 // across workgroups than the register-staged kernels'.
 using Mid = TileCfg<128, 256, 2, 4, 2, 32, 3>;
-static_assert(MOE_TILE_M % Big::BM == 0 && MOE_TILE_M % BigDma::BM == 0 && MOE_TILE_M % Mid::BM == 0,
+// 128 x 256 tiles on the register-staged loop: 4 waves of 64 x 128, 32 k per
+// stage, two stages (48 KiB of operands, 67 KiB with the staged epilogue),
+// two workgroups per CU so one's epilogue overlaps the other's main loop.
+using MidR = TileCfg<128, 256, 2, 2, 2, 32, 2, true>;
+static_assert(MOE_TILE_M % Big::BM == 0 && MOE_TILE_M % BigDma::BM == 0 && MOE_TILE_M % Mid::BM == 0 &&
+                  MOE_TILE_M % MidR::BM == 0,
               "list tiles split into row tiles");
 
 // staged tile <- bf16(acc)
@@ -382,15 +387,18 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_dw(const bf16_t* __restrict_
                                               float* __restrict__ dwg, float* __restrict__ dwu,
                                               float* __restrict__ dwd, int H, int F, int E) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  const int th = (H + C::BM - 1) / C::BM, tf = (F + C::BN - 1) / C::BN;
-  const int th2 = (H + C::BN - 1) / C::BN, tf2 = (F + C::BM - 1) / C::BM;
-  const int tpe = th * tf;  // output tiles per expert, problems 0 and 1 (== tf2 * th2 for square tiles)
-  // experts largest first, each expert's 3 * tpe tiles consecutive, dealt to
-  // the XCDs in runs of kXcdRun
-  const int blk = xcd_window_block(3 * E * tpe);
+  const int tf = (F + C::BN - 1) / C::BN, th2 = (H + C::BN - 1) / C::BN;
+  const int tpe = ((H + C::BM - 1) / C::BM) * tf;    // output tiles of problems 0 and 1 per expert
+  const int tpe2 = ((F + C::BM - 1) / C::BM) * th2;  // ... of problem 2
+  const int per = 2 * tpe + tpe2;
+  // experts largest first, each expert's tiles consecutive, dealt to the XCDs
+  // in runs of kXcdRun
+  const int blk = xcd_window_block(E * per);
   if (blk < 0) return;
-  const int e = expert_of_rank<C::NT>(offsets, E, blk / (3 * tpe), reinterpret_cast<int*>(lds));
-  const int prob = (blk % (3 * tpe)) / tpe, t = blk % tpe;
+  const int e = expert_of_rank<C::NT>(offsets, E, blk / per, reinterpret_cast<int*>(lds));
+  const int within = blk % per;
+  const int prob = within < 2 * tpe ? within / tpe : 2;
+  const int t = within - prob * tpe;
   const bf16_t *Lm, *Rm;
   float* out;
   int P, Q, mt, nt;
@@ -404,7 +412,6 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_dw(const bf16_t* __restrict_
     Lm = act; Rm = dys;
     out = dwd + (int64_t)e * F * H;
     mt = t / th2; nt = t % th2;
-    (void)tf2;
   }
   const int prow = min(C::BM, P - mt * C::BM), qcol = min(C::BN, Q - nt * C::BN);
   const int w = threadIdx.x >> 6, wm = w / C::WN, wn = w % C::WN;
@@ -530,7 +537,8 @@ static hipError_t dw_t(const Dims& d, const void* xs, const void* a, const void*
   hipError_t st = allow_lds<k_dw<C>>(C::LDS);
   if (st != hipSuccess) return st;
   const int64_t tpe = ((d.H + C::BM - 1) / C::BM) * ((d.F + C::BN - 1) / C::BN);
-  const int64_t total = 3 * d.E * tpe;
+  const int64_t tpe2 = ((d.F + C::BM - 1) / C::BM) * ((d.H + C::BN - 1) / C::BN);
+  const int64_t total = d.E * (2 * tpe + tpe2);
   const int64_t win = 8 * kXcdRun;
   unsigned grid = unsigned((total + win - 1) / win * win);
   hipLaunchKernelGGL(k_dw<C>, dim3(grid), dim3(C::NT), C::LDS, s, static_cast<const bf16_t*>(xs),
@@ -542,6 +550,28 @@ static hipError_t dw_t(const Dims& d, const void* xs, const void* a, const void*
 hipError_t ffn_bwd_dw_big(const Dims& d, const void* xs, const void* a, const void* dys, const void* dg,
                            const void* du, const int32_t* offsets, float* dwg, float* dwu, float* dwd, hipStream_t s) {
   return dw_t<Big>(d, xs, a, dys, dg, du, offsets, dwg, dwu, dwd, s);
+}
+
+// 128 x 256 register-staged tiles
+hipError_t ffn_gate_up_midr(const Dims& d, const void* xs, const void* wg, const void* wu, const int32_t* tiles,
+                            const int32_t* num_tiles, void* g, void* u, void* a, hipStream_t s) {
+  return gate_up_t<MidR>(d, xs, wg, wu, tiles, num_tiles, g, u, a, s);
+}
+hipError_t ffn_down_midr(const Dims& d, const void* a, const void* wd, const int32_t* tiles, const int32_t* num_tiles,
+                         void* ys, hipStream_t s) {
+  return down_t<MidR>(d, a, wd, tiles, num_tiles, ys, s);
+}
+hipError_t ffn_bwd_dact_midr(const Dims& d, const void* dys, const void* wd, const void* g, const void* u,
+                             const int32_t* tiles, const int32_t* num_tiles, void* dg, void* du, hipStream_t s) {
+  return dact_t<MidR>(d, dys, wd, g, u, tiles, num_tiles, dg, du, s);
+}
+hipError_t ffn_bwd_dx_midr(const Dims& d, const void* dg, const void* du, const void* wg, const void* wu,
+                           const int32_t* tiles, const int32_t* num_tiles, void* dxs, hipStream_t s) {
+  return dx_t<MidR>(d, dg, du, wg, wu, tiles, num_tiles, dxs, s);
+}
+hipError_t ffn_bwd_dw_midr(const Dims& d, const void* xs, const void* a, const void* dys, const void* dg,
+                           const void* du, const int32_t* offsets, float* dwg, float* dwu, float* dwd, hipStream_t s) {
+  return dw_t<MidR>(d, xs, a, dys, dg, du, offsets, dwg, dwu, dwd, s);
 }
 
 }  // namespace moe_launch

@@ -153,6 +153,15 @@ hipError_t ffn_bwd_dact_big(const Dims&, const void*, const void*, const void*, 
                             const int32_t*, void*, void*, hipStream_t);
 hipError_t ffn_bwd_dact_mid(const Dims&, const void*, const void*, const void*, const void*, const int32_t*,
                             const int32_t*, void*, void*, hipStream_t);
+hipError_t ffn_gate_up_midr(const Dims&, const void*, const void*, const void*, const int32_t*, const int32_t*, void*,
+                            void*, void*, hipStream_t);
+hipError_t ffn_down_midr(const Dims&, const void*, const void*, const int32_t*, const int32_t*, void*, hipStream_t);
+hipError_t ffn_bwd_dact_midr(const Dims&, const void*, const void*, const void*, const void*, const int32_t*,
+                             const int32_t*, void*, void*, hipStream_t);
+hipError_t ffn_bwd_dx_midr(const Dims&, const void*, const void*, const void*, const void*, const int32_t*,
+                           const int32_t*, void*, hipStream_t);
+hipError_t ffn_bwd_dw_midr(const Dims&, const void*, const void*, const void*, const void*, const void*,
+                           const int32_t*, float*, float*, float*, hipStream_t);
 MOE_BF16_SHAPE(ffn_bwd_dx, const void*, const void*, const void*, const void*, const int32_t*, const int32_t*, void*,
                hipStream_t)
 MOE_BF16_SHAPE(ffn_bwd_dw, const void*, const void*, const void*, const void*, const void*, const int32_t*, float*,
@@ -174,31 +183,32 @@ MOE_BF16_SHAPE(ffn_bwd_dw, const void*, const void*, const void*, const void*, c
 //   epilogue overlaps across two workgroups per CU);
 //   dX (contraction 2F): 256 x 256 from 2F = 2560 on;
 //   dW (contraction over an expert's rows): 256 x 256 throughout.
-// MOE_GEMM_TILES=256 or =128 in the environment (read at every launch)
-// overrides the choice for every stage (128 selects the 128 x 256 dA tiles);
-// any other value, or none, keeps the measured choice.
-static int tile_override() {
+// MOE_GEMM_TILES=256, =128x256 or =128 in the environment (read at every
+// launch) overrides the choice for every stage (128 selects the 128 x 256 DMA
+// dA tiles); any other value, or none, keeps the measured choice.
+enum class Tiles { Small, MidR, Big };
+static Tiles pick(Tiles measured) {
   const char* v = std::getenv("MOE_GEMM_TILES");
-  if (v == nullptr) return -1;
-  if (std::strcmp(v, "256") == 0) return 1;
-  if (std::strcmp(v, "128") == 0) return 0;
-  return -1;
+  if (v == nullptr) return measured;
+  if (std::strcmp(v, "256") == 0) return Tiles::Big;
+  if (std::strcmp(v, "128x256") == 0) return Tiles::MidR;
+  if (std::strcmp(v, "128") == 0) return Tiles::Small;
+  return measured;
 }
-static bool pick(bool measured) {
-  const int o = tile_override();
-  return o < 0 ? measured : o == 1;
-}
-static bool big_gate_up(const Dims& d) { return pick(d.H >= 2048); }
-static bool big_down(const Dims& d) { return pick(d.F >= 1280); }
-static bool big_dact(const Dims& d) { return pick(d.H >= 4096); }
-static bool big_dx(const Dims& d) { return pick(2 * d.F >= 2560); }
-static bool big_dw(const Dims&) { return pick(true); }
+static Tiles tiles_gate_up(const Dims& d) { return pick(d.H >= 2048 ? Tiles::Big : Tiles::Small); }
+static Tiles tiles_down(const Dims& d) { return pick(d.F >= 1280 ? Tiles::Big : Tiles::Small); }
+static Tiles tiles_dact(const Dims& d) { return pick(d.H >= 4096 ? Tiles::Big : Tiles::Small); }
+static Tiles tiles_dx(const Dims& d) { return pick(2 * d.F >= 2560 ? Tiles::Big : Tiles::Small); }
+static Tiles tiles_dw(const Dims&) { return pick(Tiles::Big); }
 
 hipError_t ffn_gate_up(const Dims& d, const void* xs, const void* wg, const void* wu, const int32_t* tiles,
                        const int32_t* num_tiles, void* g, void* u, void* a, hipStream_t s) {
   if (d.dtype == MOE_BF16)
-    return big_gate_up(d) ? ffn_gate_up_big(d, xs, wg, wu, tiles, num_tiles, g, u, a, s)
-                          : ffn_gate_up_small(d, xs, wg, wu, tiles, num_tiles, g, u, a, s);
+    switch (tiles_gate_up(d)) {
+      case Tiles::Big: return ffn_gate_up_big(d, xs, wg, wu, tiles, num_tiles, g, u, a, s);
+      case Tiles::MidR: return ffn_gate_up_midr(d, xs, wg, wu, tiles, num_tiles, g, u, a, s);
+      default: return ffn_gate_up_small(d, xs, wg, wu, tiles, num_tiles, g, u, a, s);
+    }
   unsigned grid = unsigned(max_tiles(d) * (d.F / TN));
   hipLaunchKernelGGL(k_gate_up_f32, dim3(grid), dim3(256), 0, s, static_cast<const float*>(xs),
                      static_cast<const float*>(wg), static_cast<const float*>(wu), tiles, num_tiles,
@@ -209,8 +219,11 @@ hipError_t ffn_gate_up(const Dims& d, const void* xs, const void* wg, const void
 hipError_t ffn_down(const Dims& d, const void* a, const void* wd, const int32_t* tiles, const int32_t* num_tiles,
                     void* ys, hipStream_t s) {
   if (d.dtype == MOE_BF16)
-    return big_down(d) ? ffn_down_big(d, a, wd, tiles, num_tiles, ys, s)
-                       : ffn_down_small(d, a, wd, tiles, num_tiles, ys, s);
+    switch (tiles_down(d)) {
+      case Tiles::Big: return ffn_down_big(d, a, wd, tiles, num_tiles, ys, s);
+      case Tiles::MidR: return ffn_down_midr(d, a, wd, tiles, num_tiles, ys, s);
+      default: return ffn_down_small(d, a, wd, tiles, num_tiles, ys, s);
+    }
   unsigned grid = unsigned(max_tiles(d) * (d.H / TN));
   hipLaunchKernelGGL(k_down_f32, dim3(grid), dim3(256), 0, s, static_cast<const float*>(a),
                      static_cast<const float*>(wd), tiles, num_tiles, static_cast<float*>(ys), int(d.H), int(d.F));
@@ -220,8 +233,11 @@ hipError_t ffn_down(const Dims& d, const void* a, const void* wd, const int32_t*
 hipError_t ffn_bwd_dact(const Dims& d, const void* dys, const void* wd, const void* g, const void* u,
                         const int32_t* tiles, const int32_t* num_tiles, void* dg, void* du, hipStream_t s) {
   if (d.dtype == MOE_BF16)
-    return big_dact(d) ? ffn_bwd_dact_big(d, dys, wd, g, u, tiles, num_tiles, dg, du, s)
-                       : ffn_bwd_dact_mid(d, dys, wd, g, u, tiles, num_tiles, dg, du, s);
+    switch (tiles_dact(d)) {
+      case Tiles::Big: return ffn_bwd_dact_big(d, dys, wd, g, u, tiles, num_tiles, dg, du, s);
+      case Tiles::MidR: return ffn_bwd_dact_midr(d, dys, wd, g, u, tiles, num_tiles, dg, du, s);
+      default: return ffn_bwd_dact_mid(d, dys, wd, g, u, tiles, num_tiles, dg, du, s);
+    }
   unsigned grid = unsigned(max_tiles(d) * (d.F / TN));
   hipLaunchKernelGGL(k_dact_f32, dim3(grid), dim3(256), 0, s, static_cast<const float*>(dys),
                      static_cast<const float*>(wd), static_cast<const float*>(g), static_cast<const float*>(u), tiles,
@@ -232,8 +248,11 @@ hipError_t ffn_bwd_dact(const Dims& d, const void* dys, const void* wd, const vo
 hipError_t ffn_bwd_dx(const Dims& d, const void* dg, const void* du, const void* wg, const void* wu,
                       const int32_t* tiles, const int32_t* num_tiles, void* dxs, hipStream_t s) {
   if (d.dtype == MOE_BF16)
-    return big_dx(d) ? ffn_bwd_dx_big(d, dg, du, wg, wu, tiles, num_tiles, dxs, s)
-                     : ffn_bwd_dx_small(d, dg, du, wg, wu, tiles, num_tiles, dxs, s);
+    switch (tiles_dx(d)) {
+      case Tiles::Big: return ffn_bwd_dx_big(d, dg, du, wg, wu, tiles, num_tiles, dxs, s);
+      case Tiles::MidR: return ffn_bwd_dx_midr(d, dg, du, wg, wu, tiles, num_tiles, dxs, s);
+      default: return ffn_bwd_dx_small(d, dg, du, wg, wu, tiles, num_tiles, dxs, s);
+    }
   unsigned grid = unsigned(max_tiles(d) * (d.H / TN));
   hipLaunchKernelGGL(k_dx_f32, dim3(grid), dim3(256), 0, s, static_cast<const float*>(dg),
                      static_cast<const float*>(du), static_cast<const float*>(wg), static_cast<const float*>(wu), tiles,
@@ -244,8 +263,11 @@ hipError_t ffn_bwd_dx(const Dims& d, const void* dg, const void* du, const void*
 hipError_t ffn_bwd_dw(const Dims& d, const void* xs, const void* a, const void* dys, const void* dg, const void* du,
                       const int32_t* offsets, float* dwg, float* dwu, float* dwd, hipStream_t s) {
   if (d.dtype == MOE_BF16)
-    return big_dw(d) ? ffn_bwd_dw_big(d, xs, a, dys, dg, du, offsets, dwg, dwu, dwd, s)
-                     : ffn_bwd_dw_small(d, xs, a, dys, dg, du, offsets, dwg, dwu, dwd, s);
+    switch (tiles_dw(d)) {
+      case Tiles::Big: return ffn_bwd_dw_big(d, xs, a, dys, dg, du, offsets, dwg, dwu, dwd, s);
+      case Tiles::MidR: return ffn_bwd_dw_midr(d, xs, a, dys, dg, du, offsets, dwg, dwu, dwd, s);
+      default: return ffn_bwd_dw_small(d, xs, a, dys, dg, du, offsets, dwg, dwu, dwd, s);
+    }
   unsigned grid = unsigned(3 * d.E * (d.H / TN) * (d.F / TN));
   hipLaunchKernelGGL(k_dw_f32, dim3(grid), dim3(256), 0, s, static_cast<const float*>(xs),
                      static_cast<const float*>(a), static_cast<const float*>(dys), static_cast<const float*>(dg),

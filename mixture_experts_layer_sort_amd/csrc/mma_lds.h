@@ -319,16 +319,42 @@ struct MnOp {
   }
 };
 
-// Register-staged K loop over two LDS stages, for 64-deep stages (four MFMA
-// k steps).  Each step: the k-step-0 fragments of the current stage are read,
-// the next K tile's chunks are requested into registers one per two MFMAs
-// over k steps 0 and 1, k steps 1..3's fragments are read one per MFMA while
-// the previous k step multiplies, the chunks go to the other stage between
-// k step 3's MFMAs, and one barrier ends the step.  The last step reloads its
-// own tile (in bounds, never read).  Spreading the requests keeps the wave's
-// in-order issue from stalling its MFMAs behind a burst of loads.  When the
-// last tile holds only k_last valid k rows (weight gradients), rows k_last..
-// of its A stage (an MN tile) are zeroed before it is used.
+// Instruction order of one step of k_loop_reg (sched_group_barrier masks:
+// 0x008 MFMA, 0x020 VMEM read, 0x100 LDS read, 0x200 LDS write).  The
+// step's KK * MK MFMAs are the slots; after slot j come its share of
+//   - the next k step's fragment reads (FR per k step, k steps 0..KK-2),
+//   - the next K tile's global loads (GL, over the first max(1, KK/2) k steps),
+//   - the LDS stores of those loads (GL, over the last k step),
+// each spread evenly over the slots it covers.  The first k step's fragment
+// reads open the step.
+template <int KK, int MK, int FR, int GL, int J = 0>
+__device__ __forceinline__ void reg_step_schedule() {
+  if constexpr (J == 0) __builtin_amdgcn_sched_group_barrier(0x100, FR, 0);
+  if constexpr (J < KK * MK) {
+    constexpr int kk = J / MK, i = J % MK;
+    constexpr int LK = KK / 2 > 0 ? KK / 2 : 1;
+    constexpr int r = kk + 1 < KK ? (i + 1) * FR / MK - i * FR / MK : 0;
+    constexpr int g = kk < LK ? (J + 1) * GL / (LK * MK) - J * GL / (LK * MK) : 0;
+    constexpr int w = kk == KK - 1 ? (i + 1) * GL / MK - i * GL / MK : 0;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
+    if constexpr (g > 0) __builtin_amdgcn_sched_group_barrier(0x020, g, 0);
+    if constexpr (w > 0) __builtin_amdgcn_sched_group_barrier(0x200, w, 0);
+    reg_step_schedule<KK, MK, FR, GL, J + 1>();
+  }
+}
+
+// Register-staged K loop over two LDS stages (KK = BK / 16 MFMA k steps per
+// stage).  Each step: the k-step-0 fragments of the current stage are read,
+// the next K tile's chunks are requested into registers, spread between the
+// MFMAs of the first half of the step, each later k step's fragments are
+// read while the previous k step multiplies, the chunks go to the other
+// stage between the last k step's MFMAs, and one barrier ends the step.  The
+// last step reloads its own tile (in bounds, never read).  Spreading the
+// requests keeps the wave's in-order issue from stalling its MFMAs behind a
+// burst of loads.  When the last tile holds only k_last valid k rows (weight
+// gradients), rows k_last.. of its A stage (an MN tile) are zeroed before it
+// is used.
 template <class C, bool A_MN, bool B_MN, class OA, class OB>
 __device__ __forceinline__ void k_loop_reg(char* lds, Acc<C>& acc, int nk, const OA& oa, const OB& ob, int wm,
                                            int wn, int k_last = C::BK) {
@@ -336,8 +362,7 @@ __device__ __forceinline__ void k_loop_reg(char* lds, Acc<C>& acc, int nk, const
   constexpr int FR = C::FM * (A_MN ? 2 : 1) + C::FN * (B_MN ? 2 : 1);  // LDS reads per k step
   constexpr int MK = C::FM * C::FN;                                    // MFMAs per k step
   constexpr int GL = OA::N + OB::N;                                    // chunks per thread and tile
-  static_assert(KK == 4 && C::S == 2, "four k steps per stage, two stages");
-  static_assert(GL % 2 == 0 && GL <= MK && FR <= MK, "schedule fits the MFMAs of a k step");
+  static_assert(C::S == 2 && KK >= 2 && KK % 2 == 0, "two stages, an even number of k steps per stage");
   zero_acc(acc);
   if (nk <= 0) return;
   u32x4_t va[OA::N], vb[OB::N];
@@ -372,22 +397,7 @@ __device__ __forceinline__ void k_loop_reg(char* lds, Acc<C>& acc, int nk, const
     }
     oa.store(va, nxt, kn);
     ob.store(vb, nxt + C::A_BYTES, kn);
-    // instruction order of the step (masks: 0x008 MFMA, 0x020 VMEM read,
-    // 0x100 LDS read, 0x200 LDS write)
-    __builtin_amdgcn_sched_group_barrier(0x100, FR, 0);
-#pragma unroll
-    for (int kk = 0; kk + 1 < KK; ++kk)
-#pragma unroll
-      for (int i = 0; i < MK; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (i < FR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        if (kk < 2 && i % 2 == 0 && i / 2 < GL / 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      }
-#pragma unroll
-    for (int i = 0; i < MK; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < GL) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-    }
+    reg_step_schedule<KK, MK, FR, GL>();
     __syncthreads();
   }
 }

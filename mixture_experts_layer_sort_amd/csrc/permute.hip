@@ -195,6 +195,84 @@ __global__ __launch_bounds__(256) void k_permute_bwd(const T* __restrict__ dxs, 
   }
 }
 
+// Dense router term (load-balancing loss on) for many experts: one wave per
+// kTokTile tokens, so each W_r^T vector read serves all of them; the tile's
+// dlogits rows are staged in LDS (the wave's own slice, read back as
+// broadcasts).  Per output element the same order as k_permute_bwd<T, true>:
+// dxs rows in ascending k, then dl * W_r^T over ascending e.
+constexpr int kTokTile = 8;
+template <typename T>
+__global__ __launch_bounds__(256) void k_permute_bwd_dense_tiled(const T* __restrict__ dxs,
+                                                                 const int32_t* __restrict__ inv,
+                                                                 const float* __restrict__ dl,
+                                                                 const T* __restrict__ w_rt, T* __restrict__ dx,
+                                                                 int N, int vpr, int K, int E) {
+  constexpr int V = Vec16<T>::n;
+  __shared__ float sdl[4][kTokTile * MOE_MAX_EXPERTS];
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  const int64_t n0 = ((int64_t)blockIdx.x * 4 + w) * kTokTile;
+  if (n0 >= N) return;
+  const int nt = int(min<int64_t>(kTokTile, N - n0));
+  float* sd = sdl[w];
+  for (int i = lane; i < nt * E; i += kWave) sd[i] = dl[n0 * E + i];  // rows n0.. are contiguous
+  __builtin_amdgcn_wave_barrier();
+  const uint4* wr = reinterpret_cast<const uint4*>(w_rt);
+  const uint4* xs4 = reinterpret_cast<const uint4*>(dxs);
+  for (int c = lane; c < vpr; c += kWave) {
+    float acc[kTokTile][V];
+#pragma unroll
+    for (int t = 0; t < kTokTile; ++t) {
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[t][i] = 0.f;
+      if (t < nt) {
+        uint4 rx[MOE_MAX_TOPK];
+#pragma unroll
+        for (int k = 0; k < MOE_MAX_TOPK; ++k)
+          if (k < K) rx[k] = xs4[(int64_t)inv[(n0 + t) * K + k] * vpr + c];
+#pragma unroll
+        for (int k = 0; k < MOE_MAX_TOPK; ++k)
+          if (k < K) {
+            float val[V];
+            Vec16<T>::load(reinterpret_cast<const T*>(&rx[k]), val);
+#pragma unroll
+            for (int i = 0; i < V; ++i) acc[t][i] += val[i];
+          }
+      }
+    }
+    int e = 0;
+    for (; e + 4 <= E; e += 4) {
+      uint4 raw[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) raw[q] = wr[(int64_t)(e + q) * vpr + c];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float wv[V];
+        Vec16<T>::load(reinterpret_cast<const T*>(&raw[q]), wv);
+#pragma unroll
+        for (int t = 0; t < kTokTile; ++t) {
+          const float de = sd[t * E + e + q];
+#pragma unroll
+          for (int i = 0; i < V; ++i) acc[t][i] = fmaf(de, wv[i], acc[t][i]);
+        }
+      }
+    }
+    for (; e < E; ++e) {
+      const uint4 raw = wr[(int64_t)e * vpr + c];
+      float wv[V];
+      Vec16<T>::load(reinterpret_cast<const T*>(&raw), wv);
+#pragma unroll
+      for (int t = 0; t < kTokTile; ++t) {
+        const float de = sd[t * E + e];
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[t][i] = fmaf(de, wv[i], acc[t][i]);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kTokTile; ++t)
+      if (t < nt) Vec16<T>::store(dx + ((n0 + t) * vpr + c) * V, acc[t]);
+  }
+}
+
 unsigned grid_for(int64_t total, int64_t cap = 8192) {
   int64_t b = (total + 255) / 256;
   if (b > cap) b = cap;
@@ -274,7 +352,11 @@ hipError_t permute_bwd(const Dims& d, const void* dxs, const int32_t* inv, const
                        int(d.H), int(d.E));
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    if (dense)
+    if (dense && d.E > 8)
+      hipLaunchKernelGGL((k_permute_bwd_dense_tiled<T>), dim3(waves4((d.N + kTokTile - 1) / kTokTile)), dim3(256), 0,
+                         s, static_cast<const T*>(dxs), inv, dlogits, static_cast<const T*>(ws), static_cast<T*>(dx),
+                         int(d.N), vpr_of<T>(d), int(d.K), int(d.E));
+    else if (dense)
       hipLaunchKernelGGL((k_permute_bwd<T, true>), dim3(waves4(d.N)), dim3(256), 0, s, static_cast<const T*>(dxs), inv,
                          topk, dlogits, static_cast<const T*>(ws), static_cast<T*>(dx), int(d.N), vpr_of<T>(d),
                          int(d.K), int(d.E));

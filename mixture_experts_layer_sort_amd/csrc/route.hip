@@ -546,27 +546,47 @@ hipError_t launch_route(const moe_launch::Dims& d, const void* x, const void* w_
   return launch_route_t<T, 32>(d, x, w_r, bias, topk, gates, s, probs, part);
 }
 
-// Load-balancing loss value: P_e = (sum of the block partials, blocks
-// ascending) / N, f_e = counts_e / (N K), loss = alpha * E * sum_e f_e P_e
-// (fixed-order tree over the experts).  One workgroup.
+// Load-balancing loss value: P_e = (sum of the block partials) / N, f_e =
+// counts_e / (N K), loss = alpha * E * sum_e f_e P_e.  One workgroup: thread
+// t sums the partials of expert t % E over blocks j, j + J, j + 2J, ... (j =
+// t / E, J = 256 / E groups; eight independent loads in flight, added in a
+// fixed order), the J group sums of each expert are added in ascending j,
+// and the E terms by a fixed tree.  The result does not depend on timing.
 __global__ __launch_bounds__(256) void k_aux_reduce(const float* __restrict__ part, int nblk,
                                                     const int32_t* __restrict__ counts, int N, int E, int K,
                                                     float alpha, float* __restrict__ loss) {
+  __shared__ float g[256];
   __shared__ float t[256];
-  const int e = threadIdx.x;
-  float term = 0.f;
-  if (e < E) {
-    float P = 0.f;
-    for (int b = 0; b < nblk; ++b) P += part[(int64_t)b * E + e];
-    term = (float(counts[e]) / (float(N) * float(K))) * (P / float(N));
+  const int tid = threadIdx.x;
+  const int J = 256 / E;  // groups per expert (E <= 256)
+  const int e = tid % E, j = tid / E;
+  float acc = 0.f;
+  if (j < J) {
+    int b = j;
+    for (; b + 7 * J < nblk; b += 8 * J) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = part[(int64_t)(b + i * J) * E + e];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc += v[i];
+    }
+    for (; b < nblk; b += J) acc += part[(int64_t)b * E + e];
   }
-  t[e] = term;
+  g[tid] = acc;
+  __syncthreads();
+  float term = 0.f;
+  if (tid < E) {
+    float P = 0.f;
+    for (int q = 0; q < J; ++q) P += g[q * E + tid];
+    term = (float(counts[tid]) / (float(N) * float(K))) * (P / float(N));
+  }
+  t[tid] = term;
   __syncthreads();
   for (int off = 128; off > 0; off >>= 1) {
-    if (e < off) t[e] += t[e + off];
+    if (tid < off) t[tid] += t[tid + off];
     __syncthreads();
   }
-  if (e == 0) *loss = alpha * float(E) * t[0];
+  if (tid == 0) *loss = alpha * float(E) * t[0];
 }
 
 // s[n] = sum_i f_i p[n,i] with f_i = counts_i / (N K), experts ascending.

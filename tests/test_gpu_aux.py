@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 import torch
 
-from moe_workloads import BASE, TEST_CONFIGS, TINY
+from moe_workloads import BASE, TEST_CONFIGS, TINY, MoEConfig
 from oracle import moe_oracle as O
 from tests.gpu_common import assert_close, gpu_inputs, oracle_fwd, store_of, sync, to_np
 
@@ -60,7 +60,9 @@ def _check_dw_r_and_dx(x, w_r, dl, dw_r, dx, dxs, inv, K, dtype):
         assert np.all(np.abs(dx - rounded) <= O.bf16_flip(pre, rounded, sig)), "dx = sum_k dxs[inv] + dlogits W_r^T"
 
 
-CASES = [TEST_CONFIGS["t_skew"], TEST_CONFIGS["t_wide_e"], TEST_CONFIGS["t_ragged"], TEST_CONFIGS["t_f32"], TINY, BASE]
+CASES = [TEST_CONFIGS["t_skew"], TEST_CONFIGS["t_wide_e"], TEST_CONFIGS["t_ragged"], TEST_CONFIGS["t_f32"], TINY, BASE,
+         # fp32 storage with more than 8 experts (token-tiled dense gather backward)
+         MoEConfig("t_aux_f32_e12", N=150, H=128, F=256, E=12, K=2, dtype="f32")]
 
 
 @pytest.mark.parametrize("cfg", CASES, ids=lambda c: c.name)

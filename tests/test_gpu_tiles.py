@@ -3,8 +3,9 @@
 The dispatcher picks the GEMM tile shape per stage from the problem size, so
 at small sizes only the 128-wide kernels run.  MOE_GEMM_TILES forces one
 family for every stage (256: the register-staged 256 x 256 kernels and the
-8-wave LDS DMA 256 x 256 dA kernel; 128: the 128 x 128 kernels and the
-128 x 256 dA tiles); each is run here on inputs
+8-wave LDS DMA 256 x 256 dA kernel; 128x256: the register-staged 128 x 256
+kernels; 128: the 128 x 128 kernels and the 128 x 256 LDS DMA dA tiles);
+each is run here on inputs
 with ragged row tiles, partial column tiles, empty experts, K = E and a single
 expert, with the oracle's assignment, and every stored intermediate and
 gradient is compared with the oracle under the usual bf16 bars and rounding
@@ -47,7 +48,7 @@ def _run(cfg, cpu, dev, of):
     return {k: v.clone() for k, v in got.items()}
 
 
-@pytest.mark.parametrize("tiles", ["256", "128"])
+@pytest.mark.parametrize("tiles", ["256", "128x256", "128"])
 @pytest.mark.parametrize("cfg", CASES, ids=lambda c: c.name)
 def test_gemm_tiles_match_oracle(cfg, tiles, monkeypatch):
     monkeypatch.setenv("MOE_GEMM_TILES", tiles)
