@@ -160,48 +160,78 @@ def main():
     d = r.d
     x, w_r, wg, wu, wd, bias, dy = (inp[k] for k in ("x", "w_r", "w_gate", "w_up", "w_down", "bias", "dy"))
     stream = torch.cuda.current_stream()
+    # the backward runs the router backward beside dA on a second stream
+    # (default priority), and the weight gradients beside dX when they cannot
+    # fill the CUs alone, as MoELayerRunner does
+    side = torch.cuda.Stream() if cfg.backward else None
+    permute_bwd = L.moe_permute_bwd if aux is None else L.moe_permute_bwd_dense
+    fns = {
+        "route": lambda st: L.moe_route(d, x, w_r, bias, r.topk, r.gates, st),
+        "meta": lambda st: L.moe_permute_meta(d, r.topk, r.sorted_flat, r.inv, r.counts, r.offsets, r.tiles,
+                                              r.num_tiles, r.meta_ws, st),
+        "permute": lambda st: L.moe_permute(d, x, r.sorted_flat, r.xs, st),
+        "gate_up": lambda st: L.moe_ffn_gate_up(d, r.xs, wg, wu, r.tiles, r.num_tiles, r.g, r.u, r.act, st),
+        "down": lambda st: L.moe_ffn_down(d, r.act, wd, r.tiles, r.num_tiles, r.ys, st),
+        "combine": lambda st: L.moe_combine(d, r.ys, r.gates, r.inv, r.y, st),
+        "aux_loss": lambda st: L.moe_aux_loss(d, x, w_r, bias, r.counts, aux, r.probs, r.aux_loss, r.aux_ws, st),
+        "combine_bwd": lambda st: L.moe_combine_bwd(d, dy, r.ys, r.gates, r.inv, r.dys, r.dgates, st),
+        "route_bwd": ((lambda st: L.moe_route_bwd(d, x, r.topk, r.gates, r.dgates, r.dlogits, r.dw_r, r.route_ws,
+                                                  st)) if aux is None else
+                      (lambda st: L.moe_route_bwd_aux(d, x, r.topk, r.gates, r.dgates, r.probs, r.counts, aux,
+                                                      r.dlogits, r.dw_r, r.route_ws, st))),
+        "dact": lambda st: L.moe_ffn_bwd_dact(d, r.dys, wd, r.g, r.u, r.tiles, r.num_tiles, r.dg, r.du, st),
+        "dx": lambda st: L.moe_ffn_bwd_dx(d, r.dg, r.du, wg, wu, r.tiles, r.num_tiles, r.dxs, st),
+        "dw": lambda st: L.moe_ffn_bwd_dw(d, r.xs, r.act, r.dys, r.dg, r.du, r.offsets, r.dw_gate, r.dw_up,
+                                          r.dw_down, st),
+        "permute_bwd": lambda st: permute_bwd(d, r.dxs, r.inv, r.topk, r.dlogits, w_r, r.dx, r.perm_ws, st),
+    }
+    fwd_names = ["route", "meta", "permute", "gate_up", "down", "combine"] + (["aux_loss"] if aux is not None else [])
+    bwd_names = ["combine_bwd", "route_bwd", "dact", "dx", "dw", "permute_bwd"] if cfg.backward else []
 
-    def stages():
-        yield "route", lambda: L.moe_route(d, x, w_r, bias, r.topk, r.gates, stream)
-        yield "meta", lambda: L.moe_permute_meta(d, r.topk, r.sorted_flat, r.inv, r.counts, r.offsets, r.tiles,
-                                                 r.num_tiles, r.meta_ws, stream)
-        yield "permute", lambda: L.moe_permute(d, x, r.sorted_flat, r.xs, stream)
-        yield "gate_up", lambda: L.moe_ffn_gate_up(d, r.xs, wg, wu, r.tiles, r.num_tiles, r.g, r.u, r.act, stream)
-        yield "down", lambda: L.moe_ffn_down(d, r.act, wd, r.tiles, r.num_tiles, r.ys, stream)
-        yield "combine", lambda: L.moe_combine(d, r.ys, r.gates, r.inv, r.y, stream)
-        if aux is not None:
-            yield "aux_loss", lambda: L.moe_aux_loss(d, x, w_r, bias, r.counts, aux, r.probs, r.aux_loss, r.aux_ws,
-                                                     stream)
-        if cfg.backward:
-            yield "combine_bwd", lambda: L.moe_combine_bwd(d, dy, r.ys, r.gates, r.inv, r.dys, r.dgates, stream)
-            if aux is None:
-                yield "route_bwd", lambda: L.moe_route_bwd(d, x, r.topk, r.gates, r.dgates, r.dlogits, r.dw_r,
-                                                           r.route_ws, stream)
-            else:
-                yield "route_bwd", lambda: L.moe_route_bwd_aux(d, x, r.topk, r.gates, r.dgates, r.probs, r.counts,
-                                                               aux, r.dlogits, r.dw_r, r.route_ws, stream)
-            yield "dact", lambda: L.moe_ffn_bwd_dact(d, r.dys, wd, r.g, r.u, r.tiles, r.num_tiles, r.dg, r.du, stream)
-            yield "dx", lambda: L.moe_ffn_bwd_dx(d, r.dg, r.du, wg, wu, r.tiles, r.num_tiles, r.dxs, stream)
-            yield "dw", lambda: L.moe_ffn_bwd_dw(d, r.xs, r.act, r.dys, r.dg, r.du, r.offsets, r.dw_gate, r.dw_up,
-                                                 r.dw_down, stream)
-            permute_bwd = L.moe_permute_bwd if aux is None else L.moe_permute_bwd_dense
-            yield "permute_bwd", lambda: permute_bwd(d, r.dxs, r.inv, r.topk, r.dlogits, w_r, r.dx, r.perm_ws, stream)
-
-    def step(ev=None, only=None):
-        for name, fn in stages():
+    def step(ev=None, only=None, overlap=False):
+        def run(name, st):
             if ev is not None and (only is None or name == only):
                 a = torch.cuda.Event(enable_timing=True)
                 b = torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                fn()
-                b.record(stream)
+                a.record(st)
+                fns[name](st)
+                b.record(st)
                 ev.setdefault(name, []).append((a, b))
             else:
-                fn()
+                fns[name](st)
+
+        def hand_over(frm, to):
+            e = torch.cuda.Event()
+            e.record(frm)
+            to.wait_event(e)
+
+        for name in fwd_names:
+            run(name, stream)
+        if not cfg.backward:
+            return
+        if not overlap:
+            for name in bwd_names:
+                run(name, stream)
+            return
+        run("combine_bwd", stream)
+        hand_over(stream, side)
+        run("route_bwd", side)
+        route_done = torch.cuda.Event()
+        route_done.record(side)
+        run("dact", stream)
+        if r.dw_beside_dx:
+            hand_over(stream, side)
+            run("dw", side)
+        else:
+            run("dw", stream)
+        run("dx", stream)
+        stream.wait_event(route_done)
+        run("permute_bwd", stream)
+        hand_over(side, stream)
 
     # warm-up (untimed)
     for _ in range(args.warmup):
-        step()
+        step(overlap=True)
     torch.cuda.synchronize()
     # untimed per-stage breakdown
     ev = {}
@@ -219,7 +249,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(ev_dom, only=dominant)
+        step(ev_dom, only=dominant, overlap=True)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
@@ -268,6 +298,8 @@ def main():
         "config": {"workload": cfg.description, "N": cfg.N, "H": cfg.H, "F": cfg.F, "E": cfg.E, "K": cfg.K,
                    "backward": cfg.backward, "parallelism": "single GPU", "maxvio": round(maxvio, 4),
                    "load_balancing_loss_alpha": aux,
+                   "streams": "router backward beside dA" + (", dW beside dX" if cfg.backward and r.dw_beside_dx
+                                                             else "") if cfg.backward else "one",
                    "empty_experts": int((counts == 0).sum())},
         "grouped_gemm": {"tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 2),
                          "frac_of_bf16_peak": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
