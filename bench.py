@@ -170,7 +170,9 @@ def main():
         "meta": lambda st: L.moe_permute_meta(d, r.topk, r.sorted_flat, r.inv, r.counts, r.offsets, r.tiles,
                                               r.num_tiles, r.meta_ws, st),
         "permute": lambda st: L.moe_permute(d, x, r.sorted_flat, r.xs, st),
-        "gate_up": lambda st: L.moe_ffn_gate_up(d, r.xs, wg, wu, r.tiles, r.num_tiles, r.g, r.u, r.act, st),
+        "gate_up": ((lambda st: L.moe_ffn_gate_up_gather(d, x, r.sorted_flat, wg, wu, r.tiles, r.num_tiles, r.g, r.u,
+                                                         r.act, st)) if r.gather_fused else
+                    (lambda st: L.moe_ffn_gate_up(d, r.xs, wg, wu, r.tiles, r.num_tiles, r.g, r.u, r.act, st))),
         "down": lambda st: L.moe_ffn_down(d, r.act, wd, r.tiles, r.num_tiles, r.ys, st),
         "combine": lambda st: L.moe_combine(d, r.ys, r.gates, r.inv, r.y, st),
         "aux_loss": lambda st: L.moe_aux_loss(d, x, w_r, bias, r.counts, aux, r.probs, r.aux_loss, r.aux_ws, st),
@@ -185,7 +187,8 @@ def main():
                                           r.dw_down, st),
         "permute_bwd": lambda st: permute_bwd(d, r.dxs, r.inv, r.topk, r.dlogits, w_r, r.dx, r.perm_ws, st),
     }
-    fwd_names = ["route", "meta", "permute", "gate_up", "down", "combine"] + (["aux_loss"] if aux is not None else [])
+    fwd_names = (["route", "meta"] + ([] if r.gather_fused else ["permute"]) + ["gate_up", "down", "combine"] +
+                 (["aux_loss"] if aux is not None else []))
     bwd_names = ["combine_bwd", "route_bwd", "dact", "dx", "dw", "permute_bwd"] if cfg.backward else []
 
     def step(ev=None, only=None, overlap=False):
@@ -298,6 +301,7 @@ def main():
         "config": {"workload": cfg.description, "N": cfg.N, "H": cfg.H, "F": cfg.F, "E": cfg.E, "K": cfg.K,
                    "backward": cfg.backward, "parallelism": "single GPU", "maxvio": round(maxvio, 4),
                    "load_balancing_loss_alpha": aux,
+                   "gather_fused_into_gate_up": r.gather_fused,
                    "streams": "router backward beside dA" + (", dW beside dX" if cfg.backward and r.dw_beside_dx
                                                              else "") if cfg.backward else "one",
                    "empty_experts": int((counts == 0).sum())},

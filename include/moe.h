@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 /* Rows per tile of the grouped-GEMM tile list built by moe_permute_meta. */
 #define MOE_TILE_M 256
 #define MOE_MAX_EXPERTS 256
@@ -149,6 +149,19 @@ int moe_expert_ffn(const moe_dims* d, const void* xs, const void* w_gate, const 
 /* First grouped GEMM of moe_expert_ffn: G, U and A = silu(G)*U. */
 int moe_ffn_gate_up(const moe_dims* d, const void* xs, const void* w_gate, const void* w_up, const int32_t* tiles,
                     const int32_t* num_tiles, void* g_save, void* u_save, void* act, hipStream_t stream);
+
+/* moe_ffn_gate_up with the permuting gather fused into its row loads
+ * (MegaBlocks section 2.1 gather, folded into the grouped GEMM as the
+ * "MoE computation principle..." page's section 3.4 merges tokens per expert):
+ * row i of the grouped order is read as x[sorted_flat[i] / K], so no xs
+ * buffer is written or read.  Results are bit-identical to moe_permute
+ * followed by moe_ffn_gate_up.  For callers that need no backward (the
+ * weight gradients read xs).
+ *   x [N,H] act in; sorted_flat [NK] from moe_permute_meta; the rest as
+ *   moe_ffn_gate_up.  Requires N*H < 2^31 (MOE_EUNSUPPORTED otherwise). */
+int moe_ffn_gate_up_gather(const moe_dims* d, const void* x, const int32_t* sorted_flat, const void* w_gate,
+                           const void* w_up, const int32_t* tiles, const int32_t* num_tiles, void* g_save,
+                           void* u_save, void* act, hipStream_t stream);
 
 /* Second grouped GEMM of moe_expert_ffn: ys = A.W_down[e]. */
 int moe_ffn_down(const moe_dims* d, const void* act, const void* w_down, const int32_t* tiles,

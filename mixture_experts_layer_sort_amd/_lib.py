@@ -48,6 +48,7 @@ SIGNATURES = {
     "moe_permute": (ctypes.c_int, [_DP, _P, _P, _P, _P]),
     "moe_expert_ffn": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_ffn_gate_up": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_ffn_gate_up_gather": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_ffn_down": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P]),
     "moe_combine": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P]),
     "moe_combine_bwd": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P, _P]),
@@ -167,6 +168,10 @@ def moe_expert_ffn(d, xs, w_gate, w_up, w_down, tiles, num_tiles, g_save, u_save
 def moe_ffn_gate_up(d, xs, w_gate, w_up, tiles, num_tiles, g_save, u_save, act, stream=None):
     _call("moe_ffn_gate_up", ctypes.byref(d), _ptr(xs), _ptr(w_gate), _ptr(w_up), _ptr(tiles), _ptr(num_tiles),
           _ptr(g_save), _ptr(u_save), _ptr(act), _stream(stream))
+
+def moe_ffn_gate_up_gather(d, x, sorted_flat, w_gate, w_up, tiles, num_tiles, g_save, u_save, act, stream=None):
+    _call("moe_ffn_gate_up_gather", ctypes.byref(d), _ptr(x), _ptr(sorted_flat), _ptr(w_gate), _ptr(w_up),
+          _ptr(tiles), _ptr(num_tiles), _ptr(g_save), _ptr(u_save), _ptr(act), _stream(stream))
 
 
 def moe_ffn_down(d, act, w_down, tiles, num_tiles, ys, stream=None):

@@ -126,7 +126,20 @@ int moe_ffn_gate_up(const moe_dims* d, const void* xs, const void* w_gate, const
   if ((g_save == nullptr) != (u_save == nullptr)) return MOE_EINVAL;
   if (g_save != nullptr && !ptrs_ok(g_save, u_save)) return MOE_EINVAL;
   if (D.N == 0) return MOE_OK;
-  return from_hip(moe_launch::ffn_gate_up(D, xs, w_gate, w_up, tiles, num_tiles, g_save, u_save, act, stream));
+  return from_hip(moe_launch::ffn_gate_up(D, xs, nullptr, w_gate, w_up, tiles, num_tiles, g_save, u_save, act, stream));
+}
+
+int moe_ffn_gate_up_gather(const moe_dims* d, const void* x, const int32_t* sorted_flat, const void* w_gate,
+                           const void* w_up, const int32_t* tiles, const int32_t* num_tiles, void* g_save,
+                           void* u_save, void* act, hipStream_t stream) {
+  MOE_CHECK_DIMS(d, D);
+  if (!ptrs_ok(x, sorted_flat, w_gate, w_up, tiles, num_tiles, act)) return MOE_EINVAL;
+  if ((g_save == nullptr) != (u_save == nullptr)) return MOE_EINVAL;
+  if (g_save != nullptr && !ptrs_ok(g_save, u_save)) return MOE_EINVAL;
+  if (D.N * D.H >= (int64_t(1) << 31)) return MOE_EUNSUPPORTED;  // 32-bit row offsets into x
+  if (D.N == 0) return MOE_OK;
+  return from_hip(
+      moe_launch::ffn_gate_up(D, x, sorted_flat, w_gate, w_up, tiles, num_tiles, g_save, u_save, act, stream));
 }
 
 int moe_ffn_down(const moe_dims* d, const void* act, const void* w_down, const int32_t* tiles,
@@ -145,7 +158,7 @@ int moe_expert_ffn(const moe_dims* d, const void* xs, const void* w_gate, const 
   if ((g_save == nullptr) != (u_save == nullptr)) return MOE_EINVAL;
   if (g_save != nullptr && !ptrs_ok(g_save, u_save)) return MOE_EINVAL;
   if (D.N == 0) return MOE_OK;
-  int st = from_hip(moe_launch::ffn_gate_up(D, xs, w_gate, w_up, tiles, num_tiles, g_save, u_save, act, stream));
+  int st = from_hip(moe_launch::ffn_gate_up(D, xs, nullptr, w_gate, w_up, tiles, num_tiles, g_save, u_save, act, stream));
   if (st != MOE_OK) return st;
   return from_hip(moe_launch::ffn_down(D, act, w_down, tiles, num_tiles, ys, stream));
 }

@@ -166,8 +166,10 @@ hipError_t permute_bwd(const Dims& d, const void* dxs, const int32_t* inv, const
                        const void* w_r, void* dx, void* ws, hipStream_t s, bool dense);
 size_t permute_bwd_ws(const Dims& d);
 
-hipError_t ffn_gate_up(const Dims& d, const void* xs, const void* wg, const void* wu, const int32_t* tiles,
-                       const int32_t* num_tiles, void* g, void* u, void* a, hipStream_t s);
+// sorted_flat non-null: xs is the token matrix x and the rows are gathered
+// on load (row i = x[sorted_flat[i] / K]); null: xs is the grouped matrix.
+hipError_t ffn_gate_up(const Dims& d, const void* xs, const int32_t* sorted_flat, const void* wg, const void* wu,
+                       const int32_t* tiles, const int32_t* num_tiles, void* g, void* u, void* a, hipStream_t s);
 hipError_t ffn_down(const Dims& d, const void* a, const void* wd, const int32_t* tiles, const int32_t* num_tiles,
                     void* ys, hipStream_t s);
 hipError_t ffn_bwd_dact(const Dims& d, const void* dys, const void* wd, const void* g, const void* u,

@@ -151,8 +151,12 @@ __device__ __forceinline__ TileInfo row_tile(const int32_t* tiles, int sub) {
 // The B tile interleaves BN/2 columns of W_gate[e] (tile columns 0..BN/2-1)
 // with the same columns of W_up[e] (tile columns BN/2..BN-1): waves wn = 0
 // hold G and waves wn = 1 hold U; the epilogue pairs them through LDS.
-template <class C>
-__global__ __launch_bounds__(C::NT, C::MINB) void k_gate_up(const bf16_t* __restrict__ xs, const bf16_t* __restrict__ wg,
+// GATHER: `xs` is the token matrix x and row i of the grouped order is read
+// as x[sorted_flat[i] / K] (the permute fused into the A-tile loads).
+template <class C, bool GATHER = false>
+__global__ __launch_bounds__(C::NT, C::MINB) void k_gate_up(const bf16_t* __restrict__ xs,
+                                                   const int32_t* __restrict__ sorted_flat, int K,
+                                                   const bf16_t* __restrict__ wg,
                                                    const bf16_t* __restrict__ wu, const int32_t* __restrict__ tiles,
                                                    const int32_t* __restrict__ num_tiles, bf16_t* __restrict__ g_out,
                                                    bf16_t* __restrict__ u_out, bf16_t* __restrict__ a_out, int H,
@@ -176,7 +180,12 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_gate_up(const bf16_t* __rest
   const bf16_t* b_u = wu + eoff - HALF;
 
   Acc<C> acc;
-  if constexpr (C::REG) {
+  if constexpr (GATHER) {
+    static_assert(C::REG, "the gathered A tile uses the register-staged loop");
+    k_loop_reg<C, false, true>(lds, acc, H / C::BK,
+                               KcGather<C::BM, C::BK, C::NT>(xs, sorted_flat + ti.row0, K, H, ti.rows),
+                               MnOp<C::BN, C::BK, C::NT>(b_g, b_u, HALF, F, C::BN, H), wm, wn);
+  } else if constexpr (C::REG) {
     k_loop_reg<C, false, true>(lds, acc, H / C::BK, KcOp<C::BM, C::BK, C::NT>(a_base, a_base, kNoSplit, H, ti.rows),
                                MnOp<C::BN, C::BK, C::NT>(b_g, b_u, HALF, F, C::BN, H), wm, wn);
   } else {
@@ -459,21 +468,24 @@ namespace moe_launch {
 // grid size rounded up to whole XCD rounds
 static unsigned grid8(int64_t n) { return unsigned((n + kXcds - 1) / kXcds * kXcds); }
 
-template <class C>
-static hipError_t gate_up_t(const Dims& d, const void* xs, const void* wg, const void* wu, const int32_t* tiles,
-                            const int32_t* num_tiles, void* g, void* u, void* a, hipStream_t s) {
-  hipError_t st = allow_lds<k_gate_up<C>>(C::LDS);
+template <class C, bool GATHER = false>
+static hipError_t gate_up_t(const Dims& d, const void* xs, const int32_t* sorted_flat, const void* wg, const void* wu,
+                            const int32_t* tiles, const int32_t* num_tiles, void* g, void* u, void* a, hipStream_t s) {
+  hipError_t st = allow_lds<k_gate_up<C, GATHER>>(C::LDS);
   if (st != hipSuccess) return st;
   unsigned grid = grid8(max_tiles(d) * C::SUB * (d.F / (C::BN / 2)));
-  hipLaunchKernelGGL(k_gate_up<C>, dim3(grid), dim3(C::NT), C::LDS, s, static_cast<const bf16_t*>(xs),
-                     static_cast<const bf16_t*>(wg), static_cast<const bf16_t*>(wu), tiles, num_tiles,
-                     static_cast<bf16_t*>(g), static_cast<bf16_t*>(u), static_cast<bf16_t*>(a), int(d.H), int(d.F));
+  hipLaunchKernelGGL((k_gate_up<C, GATHER>), dim3(grid), dim3(C::NT), C::LDS, s, static_cast<const bf16_t*>(xs),
+                     sorted_flat, int(d.K), static_cast<const bf16_t*>(wg), static_cast<const bf16_t*>(wu), tiles,
+                     num_tiles, static_cast<bf16_t*>(g), static_cast<bf16_t*>(u), static_cast<bf16_t*>(a), int(d.H),
+                     int(d.F));
   return hipGetLastError();
 }
 
-hipError_t ffn_gate_up_big(const Dims& d, const void* xs, const void* wg, const void* wu, const int32_t* tiles,
-                            const int32_t* num_tiles, void* g, void* u, void* a, hipStream_t s) {
-  return gate_up_t<Big>(d, xs, wg, wu, tiles, num_tiles, g, u, a, s);
+// sorted_flat non-null: xs is x and the rows are gathered on load
+hipError_t ffn_gate_up_big(const Dims& d, const void* xs, const int32_t* sorted_flat, const void* wg, const void* wu,
+                           const int32_t* tiles, const int32_t* num_tiles, void* g, void* u, void* a, hipStream_t s) {
+  return sorted_flat ? gate_up_t<Big, true>(d, xs, sorted_flat, wg, wu, tiles, num_tiles, g, u, a, s)
+                     : gate_up_t<Big>(d, xs, nullptr, wg, wu, tiles, num_tiles, g, u, a, s);
 }
 
 template <class C>
@@ -553,9 +565,11 @@ hipError_t ffn_bwd_dw_big(const Dims& d, const void* xs, const void* a, const vo
 }
 
 // 128 x 256 register-staged tiles
-hipError_t ffn_gate_up_midr(const Dims& d, const void* xs, const void* wg, const void* wu, const int32_t* tiles,
-                            const int32_t* num_tiles, void* g, void* u, void* a, hipStream_t s) {
-  return gate_up_t<MidR>(d, xs, wg, wu, tiles, num_tiles, g, u, a, s);
+hipError_t ffn_gate_up_midr(const Dims& d, const void* xs, const int32_t* sorted_flat, const void* wg,
+                            const void* wu, const int32_t* tiles, const int32_t* num_tiles, void* g, void* u, void* a,
+                            hipStream_t s) {
+  return sorted_flat ? gate_up_t<MidR, true>(d, xs, sorted_flat, wg, wu, tiles, num_tiles, g, u, a, s)
+                     : gate_up_t<MidR>(d, xs, nullptr, wg, wu, tiles, num_tiles, g, u, a, s);
 }
 hipError_t ffn_down_midr(const Dims& d, const void* a, const void* wd, const int32_t* tiles, const int32_t* num_tiles,
                          void* ys, hipStream_t s) {

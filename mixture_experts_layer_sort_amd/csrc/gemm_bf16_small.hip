@@ -62,6 +62,32 @@ struct LoadKC {
   }
 };
 
+// 128 rows x 64 k gathered from the token matrix: tile row r is row
+// rows_src[r] / K of x (the permute fused into the loads).  Offsets are
+// computed once per tile; rows past the tile load zeros.
+struct LoadKCg {
+  uint4 v[4];
+  int off[4];
+  __device__ __forceinline__ void init(const int32_t* rows_src, int K, int64_t ld, int rows_valid) {
+    const int c = threadIdx.x & 7, r0 = threadIdx.x >> 3;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = r0 + 32 * i;
+      off[i] = r < rows_valid ? int((rows_src[r] / K) * ld) + c * 8 : -1;
+    }
+  }
+  __device__ __forceinline__ void load(const bf16_t* x, int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      v[i] = off[i] >= 0 ? *reinterpret_cast<const uint4*>(x + off[i] + k0) : make_uint4(0, 0, 0, 0);
+  }
+  __device__ __forceinline__ void store(char* lds) const {
+    const int c = threadIdx.x & 7, r0 = threadIdx.x >> 3;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(lds + swz(r0 + 32 * i, c)) = v[i];
+  }
+};
+
 // Thread -> (8-column group mc, 4-row group kg) of the MN loader.  Each
 // 16-lane phase of a wave covers 8 column groups x 2 row groups, so its
 // 8-byte transposed LDS writes land on 32 distinct banks, while every 8
@@ -227,7 +253,12 @@ __device__ __forceinline__ void epi_put_acc(bf16_t* tile, const f32x16_t (&acc)[
 // The B tile interleaves 64 columns of W_gate[e] (tile columns 0..63) with
 // the same 64 columns of W_up[e] (tile columns 64..127), so waves wn = 0
 // hold G and waves wn = 1 hold U; the epilogue pairs them through LDS.
-__global__ __launch_bounds__(NT, 2) void k_gate_up(const bf16_t* __restrict__ xs, const bf16_t* __restrict__ wg,
+// GATHER: `xs` is the token matrix x and row i of the grouped order is read
+// as x[sorted_flat[i] / K].
+template <bool GATHER>
+__global__ __launch_bounds__(NT, 2) void k_gate_up(const bf16_t* __restrict__ xs,
+                                                    const int32_t* __restrict__ sorted_flat, int K,
+                                                    const bf16_t* __restrict__ wg,
                                                     const bf16_t* __restrict__ wu, const int32_t* __restrict__ tiles,
                                                     const int32_t* __restrict__ num_tiles, bf16_t* __restrict__ g_out,
                                                     bf16_t* __restrict__ u_out, bf16_t* __restrict__ a_out, int H,
@@ -251,16 +282,28 @@ __global__ __launch_bounds__(NT, 2) void k_gate_up(const bf16_t* __restrict__ xs
   f32x16_t acc[2][2];
   zero_acc(acc);
   LoadKC la;
+  LoadKCg lg;
   LoadMN lb;
   const int nk = H / BK;
-  la.load(a_base, H, ti.rows);
+  if (GATHER) {
+    lg.init(sorted_flat + ti.row0, K, H, ti.rows);
+    lg.load(xs, 0);
+  } else {
+    la.load(a_base, H, ti.rows);
+  }
   lb.load(b_base, F, BK);
   for (int kt = 0; kt < nk; ++kt) {
-    la.store(lds);
+    if (GATHER)
+      lg.store(lds);
+    else
+      la.store(lds);
     lb.store(lds + kTileBytes);
     __syncthreads();
     if (kt + 1 < nk) {
-      la.load(a_base + (kt + 1) * BK, H, ti.rows);
+      if (GATHER)
+        lg.load(xs, (kt + 1) * BK);
+      else
+        la.load(a_base + (kt + 1) * BK, H, ti.rows);
       lb.load(b_base + (int64_t)(kt + 1) * BK * F, F, BK);
     }
     mma_tile(lds, lds + kTileBytes, acc, wm, wn);
@@ -449,12 +492,19 @@ namespace moe_launch {
 // grid size rounded up to whole XCD rounds
 static unsigned grid8(int64_t n) { return unsigned((n + kXcds - 1) / kXcds * kXcds); }
 
-hipError_t ffn_gate_up_small(const Dims& d, const void* xs, const void* wg, const void* wu, const int32_t* tiles,
-                            const int32_t* num_tiles, void* g, void* u, void* a, hipStream_t s) {
+// sorted_flat non-null: xs is x and the rows are gathered on load
+hipError_t ffn_gate_up_small(const Dims& d, const void* xs, const int32_t* sorted_flat, const void* wg,
+                             const void* wu, const int32_t* tiles, const int32_t* num_tiles, void* g, void* u,
+                             void* a, hipStream_t s) {
   unsigned grid = grid8(max_tiles(d) * kSub * (d.F / (BN / 2)));
-  hipLaunchKernelGGL(k_gate_up, dim3(grid), dim3(NT), 0, s, static_cast<const bf16_t*>(xs),
-                     static_cast<const bf16_t*>(wg), static_cast<const bf16_t*>(wu), tiles, num_tiles,
-                     static_cast<bf16_t*>(g), static_cast<bf16_t*>(u), static_cast<bf16_t*>(a), int(d.H), int(d.F));
+  if (sorted_flat)
+    hipLaunchKernelGGL(k_gate_up<true>, dim3(grid), dim3(NT), 0, s, static_cast<const bf16_t*>(xs), sorted_flat,
+                       int(d.K), static_cast<const bf16_t*>(wg), static_cast<const bf16_t*>(wu), tiles, num_tiles,
+                       static_cast<bf16_t*>(g), static_cast<bf16_t*>(u), static_cast<bf16_t*>(a), int(d.H), int(d.F));
+  else
+    hipLaunchKernelGGL(k_gate_up<false>, dim3(grid), dim3(NT), 0, s, static_cast<const bf16_t*>(xs), nullptr,
+                       int(d.K), static_cast<const bf16_t*>(wg), static_cast<const bf16_t*>(wu), tiles, num_tiles,
+                       static_cast<bf16_t*>(g), static_cast<bf16_t*>(u), static_cast<bf16_t*>(a), int(d.H), int(d.F));
   return hipGetLastError();
 }
 

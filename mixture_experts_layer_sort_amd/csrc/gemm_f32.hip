@@ -16,7 +16,11 @@ using namespace moe;
 
 constexpr int TN = 128;  // output columns per workgroup
 
-__global__ __launch_bounds__(256) void k_gate_up_f32(const float* __restrict__ xs, const float* __restrict__ wg,
+// sorted_flat non-null: xs is the token matrix x and row i of the grouped
+// order is x[sorted_flat[i] / K] (the permute fused into the loads).
+__global__ __launch_bounds__(256) void k_gate_up_f32(const float* __restrict__ xs,
+                                                      const int32_t* __restrict__ sorted_flat, int K,
+                                                      const float* __restrict__ wg,
                                                       const float* __restrict__ wu, const int32_t* __restrict__ tiles,
                                                       const int32_t* __restrict__ num_tiles, float* __restrict__ g_out,
                                                       float* __restrict__ u_out, float* __restrict__ a_out, int H,
@@ -29,7 +33,8 @@ __global__ __launch_bounds__(256) void k_gate_up_f32(const float* __restrict__ x
   const float* Wu = wu + (int64_t)e * H * F;
   for (int idx = threadIdx.x; idx < rows * TN; idx += 256) {
     const int m = idx / TN, n = nt * TN + idx % TN;
-    const float* a = xs + (int64_t)(row0 + m) * H;
+    const int64_t src = sorted_flat ? sorted_flat[row0 + m] / K : row0 + m;
+    const float* a = xs + src * H;
     float g = 0.f, u = 0.f;
     for (int k = 0; k < H; ++k) {
       g = fmaf(a[k], Wg[(int64_t)k * F + n], g);
@@ -146,15 +151,15 @@ namespace moe_launch {
 #define MOE_BF16_SHAPE(name, ...)                 \
   hipError_t name##_big(const Dims&, __VA_ARGS__); \
   hipError_t name##_small(const Dims&, __VA_ARGS__);
-MOE_BF16_SHAPE(ffn_gate_up, const void*, const void*, const void*, const int32_t*, const int32_t*, void*, void*, void*,
-               hipStream_t)
+MOE_BF16_SHAPE(ffn_gate_up, const void*, const int32_t*, const void*, const void*, const int32_t*, const int32_t*, void*,
+               void*, void*, hipStream_t)
 MOE_BF16_SHAPE(ffn_down, const void*, const void*, const int32_t*, const int32_t*, void*, hipStream_t)
 hipError_t ffn_bwd_dact_big(const Dims&, const void*, const void*, const void*, const void*, const int32_t*,
                             const int32_t*, void*, void*, hipStream_t);
 hipError_t ffn_bwd_dact_mid(const Dims&, const void*, const void*, const void*, const void*, const int32_t*,
                             const int32_t*, void*, void*, hipStream_t);
-hipError_t ffn_gate_up_midr(const Dims&, const void*, const void*, const void*, const int32_t*, const int32_t*, void*,
-                            void*, void*, hipStream_t);
+hipError_t ffn_gate_up_midr(const Dims&, const void*, const int32_t*, const void*, const void*, const int32_t*,
+                            const int32_t*, void*, void*, void*, hipStream_t);
 hipError_t ffn_down_midr(const Dims&, const void*, const void*, const int32_t*, const int32_t*, void*, hipStream_t);
 hipError_t ffn_bwd_dact_midr(const Dims&, const void*, const void*, const void*, const void*, const int32_t*,
                              const int32_t*, void*, void*, hipStream_t);
@@ -201,17 +206,17 @@ static Tiles tiles_dact(const Dims& d) { return pick(d.H >= 4096 ? Tiles::Big : 
 static Tiles tiles_dx(const Dims& d) { return pick(2 * d.F >= 2560 ? Tiles::Big : Tiles::Small); }
 static Tiles tiles_dw(const Dims&) { return pick(Tiles::Big); }
 
-hipError_t ffn_gate_up(const Dims& d, const void* xs, const void* wg, const void* wu, const int32_t* tiles,
-                       const int32_t* num_tiles, void* g, void* u, void* a, hipStream_t s) {
+hipError_t ffn_gate_up(const Dims& d, const void* xs, const int32_t* sorted_flat, const void* wg, const void* wu,
+                       const int32_t* tiles, const int32_t* num_tiles, void* g, void* u, void* a, hipStream_t s) {
   if (d.dtype == MOE_BF16)
     switch (tiles_gate_up(d)) {
-      case Tiles::Big: return ffn_gate_up_big(d, xs, wg, wu, tiles, num_tiles, g, u, a, s);
-      case Tiles::MidR: return ffn_gate_up_midr(d, xs, wg, wu, tiles, num_tiles, g, u, a, s);
-      default: return ffn_gate_up_small(d, xs, wg, wu, tiles, num_tiles, g, u, a, s);
+      case Tiles::Big: return ffn_gate_up_big(d, xs, sorted_flat, wg, wu, tiles, num_tiles, g, u, a, s);
+      case Tiles::MidR: return ffn_gate_up_midr(d, xs, sorted_flat, wg, wu, tiles, num_tiles, g, u, a, s);
+      default: return ffn_gate_up_small(d, xs, sorted_flat, wg, wu, tiles, num_tiles, g, u, a, s);
     }
   unsigned grid = unsigned(max_tiles(d) * (d.F / TN));
-  hipLaunchKernelGGL(k_gate_up_f32, dim3(grid), dim3(256), 0, s, static_cast<const float*>(xs),
-                     static_cast<const float*>(wg), static_cast<const float*>(wu), tiles, num_tiles,
+  hipLaunchKernelGGL(k_gate_up_f32, dim3(grid), dim3(256), 0, s, static_cast<const float*>(xs), sorted_flat,
+                     int(d.K), static_cast<const float*>(wg), static_cast<const float*>(wu), tiles, num_tiles,
                      static_cast<float*>(g), static_cast<float*>(u), static_cast<float*>(a), int(d.H), int(d.F));
   return hipGetLastError();
 }

@@ -277,6 +277,42 @@ struct KcOp {
   }
 };
 
+// K-contiguous operand whose rows are gathered: tile row r is row
+// rows_src[r] / K of x (leading dimension ld), so the expert-grouped rows
+// are read straight from the token rows (rows_src = the sorted flat indices
+// of the tile's first row on).  Rows at or past rows_valid read the last
+// valid row.  Element offsets are 32-bit (callers keep N * ld < 2^31).
+template <int ROWS, int BK, int NT>
+struct KcGather {
+  static constexpr int CPR = BK / 8, RP = NT / CPR, N = ROWS / RP;
+  static_assert(NT % CPR == 0 && ROWS % RP == 0, "chunks split evenly over the threads");
+  const bf16_t* base;
+  int off[N];
+  __device__ __forceinline__ KcGather(const bf16_t* x, const int32_t* rows_src, int K, int64_t ld, int rows_valid)
+      : base(x) {
+    const int r0 = threadIdx.x / CPR, c = threadIdx.x % CPR;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int r = r0 + i * RP;
+      const int tok = rows_src[r < rows_valid ? r : rows_valid - 1] / K;
+      off[i] = int(tok * ld) + c * 8;
+    }
+  }
+  __device__ __forceinline__ void load(u32x4_t (&v)[N], int kt) const {
+    const bf16_t* p = base + kt * BK;
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = *reinterpret_cast<const u32x4_t*>(p + off[i]);
+  }
+  __device__ __forceinline__ void store(const u32x4_t (&v)[N], char* st, int) const {
+    const int r0 = threadIdx.x / CPR, c = threadIdx.x % CPR;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int r = r0 + i * RP;
+      *reinterpret_cast<u32x4_t*>(st + r * (2 * BK) + ((c ^ fk<BK>(r)) << 4)) = v[i];
+    }
+  }
+};
+
 // MN-contiguous operand: BK k rows x COLS columns of a row-major matrix
 // (leading dimension ld); K tile kt covers k rows [kt * BK, kt * BK + BK).
 // Columns [0, split) come from base0 and [split, COLS) from base1 (both

@@ -5,7 +5,8 @@ through PyTorch, which here only supplies memory and streams) and runs the
 layer through the C ABI:
 
   forward : moe_route -> moe_permute_meta -> moe_permute -> moe_expert_ffn
-            (moe_ffn_gate_up, moe_ffn_down) -> moe_combine
+            (moe_ffn_gate_up, moe_ffn_down) -> moe_combine; without a backward,
+            moe_ffn_gate_up_gather replaces moe_permute + moe_ffn_gate_up
   backward: moe_combine_bwd -> moe_route_bwd -> moe_expert_ffn_bwd
             (moe_ffn_bwd_dact, moe_ffn_bwd_dx, moe_ffn_bwd_dw) -> moe_permute_bwd
 
@@ -50,7 +51,10 @@ class MoELayerRunner:
         self.tiles = torch.empty((max(1, mt) * 3,), dtype=i32, device=dev)
         self.num_tiles = torch.empty((1,), dtype=i32, device=dev)
         self.meta_ws = self._ws(L.MOE_ENTRY_PERMUTE_META)
-        self.xs = torch.empty((NK, H), dtype=dtype, device=dev)
+        # without a backward nothing reads xs after gate/up: the gather is
+        # fused into gate/up's row loads and xs is never materialised
+        self.gather_fused = (not backward) and N * H < 2 ** 31
+        self.xs = None if self.gather_fused else torch.empty((NK, H), dtype=dtype, device=dev)
         self.g = torch.empty((NK, F), dtype=dtype, device=dev) if save_gu else None
         self.u = torch.empty((NK, F), dtype=dtype, device=dev) if save_gu else None
         self.act = torch.empty((NK, F), dtype=dtype, device=dev)
@@ -106,8 +110,13 @@ class MoELayerRunner:
             self.topk.copy_(topk)
             self.gates.copy_(gates)
         self.meta(stream=stream)
-        L.moe_permute(self.d, x, self.sorted_flat, self.xs, stream)
-        L.moe_ffn_gate_up(self.d, self.xs, w_gate, w_up, self.tiles, self.num_tiles, self.g, self.u, self.act, stream)
+        if self.gather_fused:
+            L.moe_ffn_gate_up_gather(self.d, x, self.sorted_flat, w_gate, w_up, self.tiles, self.num_tiles, self.g,
+                                     self.u, self.act, stream)
+        else:
+            L.moe_permute(self.d, x, self.sorted_flat, self.xs, stream)
+            L.moe_ffn_gate_up(self.d, self.xs, w_gate, w_up, self.tiles, self.num_tiles, self.g, self.u, self.act,
+                              stream)
         L.moe_ffn_down(self.d, self.act, w_down, self.tiles, self.num_tiles, self.ys, stream)
         L.moe_combine(self.d, self.ys, self.gates, self.inv, self.y, stream)
         if self.aux_alpha is not None:

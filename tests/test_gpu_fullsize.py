@@ -180,7 +180,9 @@ def _sampled_token_checks(cfg, dev, r, x, topk, gates, tokens, y, grads):
     inv_gpu = r.inv.cpu().numpy().astype(np.int64)
     gpu_rows = inv_gpu.reshape(cfg.N, K)[tsel].reshape(-1)      # token-major (i, k)
     ora_rows = of["inv"].reshape(len(tokens), K).reshape(-1)
-    names = ["xs", "G", "U", "A", "ys"] + (["dys", "dG", "dU", "dxs"] if cfg.backward else [])
+    # a forward-only runner gathers the rows inside gate/up and holds no xs
+    names = (["xs"] if r.xs is not None else []) + ["G", "U", "A", "ys"] + (
+        ["dys", "dG", "dU", "dxs"] if cfg.backward else [])
     bufs = {"xs": r.xs, "G": r.g, "U": r.u, "A": r.act, "ys": r.ys}
     if cfg.backward:
         bufs.update({"dys": r.dys, "dG": r.dg, "dU": r.du, "dxs": r.dxs})

@@ -69,3 +69,36 @@ def test_gemm_tiles_match_oracle(cfg, tiles, monkeypatch):
     for name, t in got.items():
         assert torch.equal(t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32),
                            again[name].view(torch.int16) if t.dtype == torch.bfloat16 else again[name].view(torch.int32)), name
+
+
+@pytest.mark.parametrize("tiles", ["256", "128x256", "128"])
+@pytest.mark.parametrize("cfg", [TEST_CONFIGS["t_bigtile"], TEST_CONFIGS["t_ragged"], TEST_CONFIGS["t_skew"],
+                                 TEST_CONFIGS["t_f32"], TEST_CONFIGS["t_wide_e"]], ids=lambda c: c.name)
+def test_gate_up_gather_equals_permute_then_gate_up(cfg, tiles, monkeypatch):
+    """moe_ffn_gate_up_gather (rows read as x[sorted_flat / K]) gives the same
+    bytes as moe_permute followed by moe_ffn_gate_up, for every tile family."""
+    from mixture_experts_layer_sort_amd import _lib as L
+    from mixture_experts_layer_sort_amd.layer import MoELayerRunner
+    monkeypatch.setenv("MOE_GEMM_TILES", tiles)
+    print(f"[gather {tiles}] {cfg.name}", flush=True)
+    cpu, dev = gpu_inputs(cfg, 2)
+    r = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, "cuda")
+    r.route(dev["x"], dev["w_r"], dev["bias"])
+    r.meta()
+    L.moe_permute(r.d, dev["x"], r.sorted_flat, r.xs)
+    L.moe_ffn_gate_up(r.d, r.xs, dev["w_gate"], dev["w_up"], r.tiles, r.num_tiles, r.g, r.u, r.act)
+    ref = {k: getattr(r, k).clone() for k in ("g", "u", "act")}
+    for k in ref:
+        getattr(r, k).view(torch.uint8).fill_(0xFF)
+    L.moe_ffn_gate_up_gather(r.d, dev["x"], r.sorted_flat, dev["w_gate"], dev["w_up"], r.tiles, r.num_tiles, r.g,
+                             r.u, r.act)
+    sync()
+    for k, v in ref.items():
+        assert torch.equal(getattr(r, k).view(torch.uint8), v.view(torch.uint8)), k
+    # the forward-only runner takes this path and holds no xs
+    f = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, "cuda", backward=False)
+    assert f.gather_fused and f.xs is None
+    y = f.forward(dev["x"], dev["w_r"], dev["w_gate"], dev["w_up"], dev["w_down"], dev["bias"])
+    r.forward(dev["x"], dev["w_r"], dev["w_gate"], dev["w_up"], dev["w_down"], dev["bias"])
+    sync()
+    assert torch.equal(y.view(torch.uint8), r.y.view(torch.uint8))
