@@ -162,22 +162,44 @@ def gates_renormalised_softmax(logits: np.ndarray, topk: np.ndarray) -> np.ndarr
 # dropless routing metadata (MegaBlocks 2.1 / 2.3, section 4)
 # --------------------------------------------------------------------------
 
-def routing_metadata(topk: np.ndarray, E: int):
+def routing_metadata(topk: np.ndarray, E: int, capacity: Optional[int] = None):
     """Histogram, cumsum bins and the stable sort of the flat assignment.
 
     Returns (counts [E], offsets [E+1], sorted_flat [NK], inv [NK]) where
     offsets is the exclusive cumsum of counts (offsets[1:] are the inclusive
     bins), sorted_flat[i] is the flat index f = n*K + k of the i-th row of
     the expert-grouped order (stable in f), and inv[f] is the row of f.
+
+    With a capacity C ("MoE computation principle and execution process",
+    section 3.4: each expert takes at most C rows, the overflow is dropped),
+    expert e keeps the first min(counts[e], C) of its rows in that stable
+    order (the lowest flat indices).  counts stays the full histogram of the
+    assignment; offsets bins the kept rows only; sorted_flat holds the kept
+    rows, expert-grouped, followed by -1 for every dropped row; inv[f] is -1
+    for a dropped f.
     """
     flat = topk.reshape(-1).astype(np.int64)
     counts = np.bincount(flat, minlength=E).astype(np.int64)
+    order = np.argsort(flat, kind="stable").astype(np.int64)
+    start = np.zeros(E + 1, dtype=np.int64)
+    start[1:] = np.cumsum(counts)
+    rank = np.arange(order.size, dtype=np.int64) - start[flat[order]]   # position within the expert
+    keep = np.ones(order.size, dtype=bool) if capacity is None else rank < capacity
+    kept_counts = counts if capacity is None else np.minimum(counts, capacity)
     offsets = np.zeros(E + 1, dtype=np.int64)
-    offsets[1:] = np.cumsum(counts)
-    sorted_flat = np.argsort(flat, kind="stable").astype(np.int64)
-    inv = np.empty_like(sorted_flat)
-    inv[sorted_flat] = np.arange(sorted_flat.size, dtype=np.int64)
+    offsets[1:] = np.cumsum(kept_counts)
+    sorted_flat = np.full(order.size, -1, dtype=np.int64)
+    sorted_flat[:int(offsets[E])] = order[keep]
+    inv = np.full(order.size, -1, dtype=np.int64)
+    inv[order[keep]] = np.arange(int(offsets[E]), dtype=np.int64)
     return counts, offsets, sorted_flat, inv
+
+
+def capacity_of(N: int, K: int, E: int, capacity_factor: float) -> int:
+    """Expert capacity ceil(capacity_factor * N * K / E): the page's
+    ceil(N / E * capacity_factor) with N read as the N * K routed slots
+    ("MoE computation principle and execution process", section 3.4)."""
+    return int(math.ceil(capacity_factor * N * K / E))
 
 
 def tile_list(counts: np.ndarray, offsets: np.ndarray, tile_m: int) -> np.ndarray:
@@ -264,7 +286,7 @@ def aux_loss_grad(logits: np.ndarray, counts: np.ndarray, K: int, scale: float) 
 # --------------------------------------------------------------------------
 
 def forward(x, w_r, w_gate, w_up, w_down, K: int, bias=None, store: str = "bf16", tile_m: int = 128,
-            topk=None):
+            topk=None, capacity: Optional[int] = None):
     """Forward pass of the layer; returns every intermediate in a dict.
 
     Steps in the pages' order: logits, top-K, gates, metadata (histogram,
@@ -275,6 +297,10 @@ def forward(x, w_r, w_gate, w_up, w_down, K: int, bias=None, store: str = "bf16"
     assignment of K distinct experts per token, in slot order, for checks
     made "given the same assignment"; the gates are still the softmax over
     the logits of the given experts.
+
+    ``capacity`` (optional) caps the rows each expert takes (see
+    routing_metadata); a dropped slot contributes nothing to y and its gate
+    is not renormalised away.  Rows past the kept ones stay zero.
     """
     assert store in STORE_TYPES
     x = as_f64(x)
@@ -293,12 +319,14 @@ def forward(x, w_r, w_gate, w_up, w_down, K: int, bias=None, store: str = "bf16"
         assert all(len(set(r.tolist())) == K for r in topk), "a token's experts must be distinct"
         assert topk.min() >= 0 and topk.max() < E
     gates = rho32(gates_topk_softmax(logits, topk), store)
-    counts, offsets, sorted_flat, inv = routing_metadata(topk, E)
-    tiles = tile_list(counts, offsets, tile_m)
+    counts, offsets, sorted_flat, inv = routing_metadata(topk, E, capacity)
+    tiles = tile_list(np.diff(offsets), offsets, tile_m)
 
-    tok = sorted_flat // K
-    xs = x[tok]
     NK = N * K
+    nkept = int(offsets[E])
+    tok = np.maximum(sorted_flat, 0) // K
+    xs = np.zeros((NK, H))
+    xs[:nkept] = x[tok[:nkept]]
     G = np.zeros((NK, F))
     U = np.zeros((NK, F))
     A = np.zeros((NK, F))
@@ -322,7 +350,8 @@ def forward(x, w_r, w_gate, w_up, w_down, K: int, bias=None, store: str = "bf16"
     y = rho(y, store)
     return dict(x=x, w_r=w_r, bias=bias, w_gate=wg_all, w_up=wu_all, w_down=wd_all, K=K, store=store,
                 logits=logits, topk=topk, gates=gates, counts=counts, offsets=offsets,
-                sorted_flat=sorted_flat, inv=inv, tiles=tiles, xs=xs, G=G, U=U, A=A, ys=ys, y=y)
+                sorted_flat=sorted_flat, inv=inv, tiles=tiles, xs=xs, G=G, U=U, A=A, ys=ys, y=y,
+                capacity=capacity)
 
 
 def backward(fwd: dict, dy, aux_scale: Optional[float] = None) -> dict:
@@ -349,11 +378,14 @@ def backward(fwd: dict, dy, aux_scale: Optional[float] = None) -> dict:
     sorted_flat, inv, offsets = fwd["sorted_flat"], fwd["inv"], fwd["offsets"]
     gates, topk = fwd["gates"], fwd["topk"]
     gflat = gates.reshape(-1)
-    tok = sorted_flat // K
+    kept_row = sorted_flat >= 0                            # rows past the kept ones: dropped slots
+    sf = np.maximum(sorted_flat, 0)
+    tok = sf // K
+    kept_slot = (inv >= 0).reshape(N, K)
 
-    # combine backward
-    dys = rho(gflat[sorted_flat][:, None] * dy[tok], store)
-    ys_tok = fwd["ys"][inv.reshape(N, K)]                 # [N, K, H]
+    # combine backward (a dropped slot has no row and a zero gate gradient)
+    dys = rho(np.where(kept_row[:, None], gflat[sf][:, None] * dy[tok], 0.0), store)
+    ys_tok = fwd["ys"][np.maximum(inv, 0).reshape(N, K)] * kept_slot[:, :, None]   # [N, K, H]
     dgates = rho32(np.einsum("nh,nkh->nk", dy, ys_tok), store)
 
     # expert backward
@@ -388,8 +420,8 @@ def backward(fwd: dict, dy, aux_scale: Optional[float] = None) -> dict:
         dlogits = dlogits + aux_loss_grad(fwd["logits"], fwd["counts"], K, aux_scale)
     dlogits = rho32(dlogits, store)
 
-    # gather backward (sum over each token's K rows) + router input gradient
-    dx = dxs[inv.reshape(N, K)].sum(axis=1) + dlogits @ w_r.T
+    # gather backward (sum over each token's kept rows) + router input gradient
+    dx = (dxs[np.maximum(inv, 0).reshape(N, K)] * kept_slot[:, :, None]).sum(axis=1) + dlogits @ w_r.T
     dx = rho(dx, store)
     dw_r = x.T @ dlogits
     return dict(dys=dys, dgates=dgates, dG=dG, dU=dU, dxs=dxs, dlogits=dlogits, dx=dx, dw_r=dw_r,

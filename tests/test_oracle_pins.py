@@ -516,8 +516,8 @@ MUTATIONS = {
         top.astype(np.int64), axis=1)),
     "tiebreak_id_descending": ("topk_experts", lambda l, K: np.ascontiguousarray(
         (l.shape[1] - 1 - np.argsort(-l[:, ::-1], axis=1, kind="stable"))[:, :K]).astype(np.int32)),
-    "unstable_sort": ("routing_metadata", lambda topk, E: (lambda c, o, s, i: (c, o, s[::-1].copy(), i))(
-        *_orig_meta(topk, E))),
+    "unstable_sort": ("routing_metadata", lambda topk, E, capacity=None: (lambda c, o, s, i: (c, o, s[::-1].copy(), i))(
+        *_orig_meta(topk, E, capacity))),
     "sigmoid_wrong_sign": ("sigmoid", lambda z: 1.0 / (1.0 + np.exp(z))),
     "silu_wrong": ("silu", lambda z: z / (1.0 + np.exp(z))),
     "bias_dropped": ("router_logits", lambda x, w_r, bias=None: x @ w_r),
