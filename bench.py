@@ -18,6 +18,7 @@ steps), and the CPU oracle timed on the host as a reported baseline.
 from __future__ import annotations
 
 import argparse
+import math
 import json
 import os
 import platform
@@ -75,6 +76,8 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--aux-alpha", type=float, default=None,
                    help="also compute the Switch load-balancing loss with this weight (forward and its gradient)")
+    p.add_argument("--capacity-factor", type=float, default=None,
+                   help="token-dropping variant: expert capacity ceil(cf * N * K / E), overflow dropped")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain 1 GiB streaming copy (for scaling HBM byte counters) and exit")
     return p.parse_args()
@@ -99,8 +102,10 @@ def copy_calibration():
           flush=True)
 
 
-def stage_flops(cfg):
-    hf = cfg.H * cfg.F * cfg.NK
+def stage_flops(cfg, rows=None):
+    """Algorithmic flops of the grouped GEMMs over `rows` routed rows (all
+    N*K by default; the kept rows of the token-dropping variant)."""
+    hf = cfg.H * cfg.F * (cfg.NK if rows is None else rows)
     return {"gate_up": 4 * hf, "down": 2 * hf, "dact": 2 * hf, "dx": 4 * hf, "dw": 6 * hf}
 
 
@@ -155,8 +160,11 @@ def main():
         inp = {k: (None if v is None else v.to(dev)) for k, v in cpu.items()}
     torch.cuda.synchronize()
     aux = args.aux_alpha
+    capacity = None
+    if args.capacity_factor is not None:
+        capacity = int(math.ceil(args.capacity_factor * cfg.N * cfg.K / cfg.E))
     r = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, dev, backward=cfg.backward,
-                       aux_alpha=aux)
+                       aux_alpha=aux, capacity=capacity)
     d = r.d
     x, w_r, wg, wu, wd, bias, dy = (inp[k] for k in ("x", "w_r", "w_gate", "w_up", "w_down", "bias", "dy"))
     stream = torch.cuda.current_stream()
@@ -167,8 +175,7 @@ def main():
     permute_bwd = L.moe_permute_bwd if aux is None else L.moe_permute_bwd_dense
     fns = {
         "route": lambda st: L.moe_route(d, x, w_r, bias, r.topk, r.gates, st),
-        "meta": lambda st: L.moe_permute_meta(d, r.topk, r.sorted_flat, r.inv, r.counts, r.offsets, r.tiles,
-                                              r.num_tiles, r.meta_ws, st),
+        "meta": lambda st: r.meta(stream=st),
         "permute": lambda st: L.moe_permute(d, x, r.sorted_flat, r.xs, st),
         "gate_up": ((lambda st: L.moe_ffn_gate_up_gather(d, x, r.sorted_flat, wg, wu, r.tiles, r.num_tiles, r.g, r.u,
                                                          r.act, st)) if r.gather_fused else
@@ -242,7 +249,8 @@ def main():
         step(ev)
     torch.cuda.synchronize()
     stage_ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
-    fl = stage_flops(cfg)
+    kept_rows = int(r.offsets[cfg.E].item())
+    fl = stage_flops(cfg, kept_rows)
     gemm_ms = sum(stage_ms[k] for k in fl if k in stage_ms)
     gemm_flops = sum(v for k, v in fl.items() if k in stage_ms)
     dominant = max(stage_ms, key=stage_ms.get)
@@ -302,6 +310,8 @@ def main():
                    "backward": cfg.backward, "parallelism": "single GPU", "maxvio": round(maxvio, 4),
                    "load_balancing_loss_alpha": aux,
                    "gather_fused_into_gate_up": r.gather_fused,
+                   "capacity": capacity,
+                   "dropped_rows": cfg.NK - kept_rows,
                    "streams": "router backward beside dA" + (", dW beside dX" if cfg.backward and r.dw_beside_dx
                                                              else "") if cfg.backward else "one",
                    "empty_experts": int((counts == 0).sum())},

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 /* Rows per tile of the grouped-GEMM tile list built by moe_permute_meta. */
 #define MOE_TILE_M 256
 #define MOE_MAX_EXPERTS 256
@@ -128,6 +128,27 @@ int moe_route(const moe_dims* d, const void* x, const void* w_r, const float* lo
 int moe_permute_meta(const moe_dims* d, const int32_t* topk_idx, int32_t* sorted_flat, int32_t* inv, int32_t* counts,
                      int32_t* offsets, int32_t* tiles, int32_t* num_tiles, void* ws, size_t ws_bytes,
                      hipStream_t stream);
+
+/* Token-dropping variant of moe_permute_meta with an expert capacity C >= 0
+ * ("MoE computation principle and execution process" section 3.4: each
+ * expert takes at most C rows, the overflow is dropped).  Expert e keeps the
+ * first min(counts[e], C) of its rows in the stable grouped order (lowest
+ * flat index first); every other row is dropped.
+ *   counts [E]      full histogram of the assignment (before dropping);
+ *   offsets [E+1]   exclusive cumsum of the kept counts, offsets[E] = kept
+ *                   rows in total;
+ *   sorted_flat [NK] the kept rows grouped by expert, then -1 for each
+ *                   dropped row;
+ *   inv [NK]        row of f, or -1 when f is dropped;
+ *   tiles, num_tiles over the kept rows.
+ * Downstream, moe_permute skips -1 rows, moe_combine / moe_combine_bwd /
+ * moe_permute_bwd(_dense) treat inv < 0 as a slot that adds nothing (zero
+ * gate gradient, no dxs row); the GEMMs see only the kept rows through the
+ * tile list and offsets.  C >= max(counts) reproduces moe_permute_meta.
+ * capacity < 0 -> MOE_EINVAL.  ws: MOE_ENTRY_PERMUTE_META. */
+int moe_permute_meta_capacity(const moe_dims* d, const int32_t* topk_idx, int32_t capacity, int32_t* sorted_flat,
+                              int32_t* inv, int32_t* counts, int32_t* offsets, int32_t* tiles, int32_t* num_tiles,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Permuting gather: xs[i] = x[sorted_flat[i] / K]  (MegaBlocks section 2.1).
  *   x [N,H] act in; sorted_flat [NK] in; xs [NK,H] act out. */

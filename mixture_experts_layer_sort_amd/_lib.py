@@ -45,6 +45,7 @@ SIGNATURES = {
     "moe_workspace_bytes": (_SZ, [_DP, _I32]),
     "moe_route": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P]),
     "moe_permute_meta": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_permute_meta_capacity": (ctypes.c_int, [_DP, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_permute": (ctypes.c_int, [_DP, _P, _P, _P, _P]),
     "moe_expert_ffn": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_ffn_gate_up": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
@@ -154,6 +155,13 @@ def moe_permute_meta(d, topk_idx, sorted_flat, inv, counts, offsets, tiles, num_
     _call("moe_permute_meta", ctypes.byref(d), _ptr(topk_idx), _ptr(sorted_flat), _ptr(inv), _ptr(counts),
           _ptr(offsets), _ptr(tiles), _ptr(num_tiles), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
           _stream(stream))
+
+
+def moe_permute_meta_capacity(d, topk_idx, capacity, sorted_flat, inv, counts, offsets, tiles, num_tiles, ws,
+                              stream=None):
+    _call("moe_permute_meta_capacity", ctypes.byref(d), _ptr(topk_idx), int(capacity), _ptr(sorted_flat), _ptr(inv),
+          _ptr(counts), _ptr(offsets), _ptr(tiles), _ptr(num_tiles), _ptr(ws),
+          0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
 
 
 def moe_permute(d, x, sorted_flat, xs, stream=None):

@@ -100,16 +100,24 @@ int moe_route(const moe_dims* d, const void* x, const void* w_r, const float* lo
   return from_hip(moe_launch::route(D, x, w_r, logit_bias, topk_idx, gates, stream));
 }
 
-int moe_permute_meta(const moe_dims* d, const int32_t* topk_idx, int32_t* sorted_flat, int32_t* inv, int32_t* counts,
-                     int32_t* offsets, int32_t* tiles, int32_t* num_tiles, void* ws, size_t ws_bytes,
-                     hipStream_t stream) {
+int moe_permute_meta_capacity(const moe_dims* d, const int32_t* topk_idx, int32_t capacity, int32_t* sorted_flat,
+                              int32_t* inv, int32_t* counts, int32_t* offsets, int32_t* tiles, int32_t* num_tiles,
+                              void* ws, size_t ws_bytes, hipStream_t stream) {
   MOE_CHECK_DIMS(d, D);
   if (!ptrs_ok(topk_idx, sorted_flat, inv, counts, offsets, tiles, num_tiles)) return MOE_EINVAL;
+  if (capacity < 0) return MOE_EINVAL;
   if (D.N == 0) return MOE_OK;
   const size_t need = moe_launch::permute_meta_ws(D);
   if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned16(ws))) return MOE_EWORKSPACE;
-  return from_hip(moe_launch::permute_meta(D, topk_idx, sorted_flat, inv, counts, offsets, tiles, num_tiles, ws,
-                                           stream));
+  return from_hip(moe_launch::permute_meta(D, topk_idx, capacity, sorted_flat, inv, counts, offsets, tiles, num_tiles,
+                                           ws, stream));
+}
+
+int moe_permute_meta(const moe_dims* d, const int32_t* topk_idx, int32_t* sorted_flat, int32_t* inv, int32_t* counts,
+                     int32_t* offsets, int32_t* tiles, int32_t* num_tiles, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  return moe_permute_meta_capacity(d, topk_idx, INT32_MAX, sorted_flat, inv, counts, offsets, tiles, num_tiles, ws,
+                                   ws_bytes, stream);
 }
 
 int moe_permute(const moe_dims* d, const void* x, const int32_t* sorted_flat, void* xs, hipStream_t stream) {

@@ -145,8 +145,9 @@ size_t route_bwd_chunks(const Dims& d);
 
 hipError_t route(const Dims& d, const void* x, const void* w_r, const float* bias, int32_t* topk, float* gates,
                  hipStream_t s);
-hipError_t permute_meta(const Dims& d, const int32_t* topk, int32_t* sorted_flat, int32_t* inv, int32_t* counts,
-                        int32_t* offsets, int32_t* tiles, int32_t* num_tiles, void* ws, hipStream_t s);
+hipError_t permute_meta(const Dims& d, const int32_t* topk, int32_t capacity, int32_t* sorted_flat, int32_t* inv,
+                        int32_t* counts, int32_t* offsets, int32_t* tiles, int32_t* num_tiles, void* ws,
+                        hipStream_t s);
 size_t permute_meta_ws(const Dims& d);
 hipError_t permute(const Dims& d, const void* x, const int32_t* sorted_flat, void* xs, hipStream_t s);
 hipError_t combine(const Dims& d, const void* ys, const float* gates, const int32_t* inv, void* y, hipStream_t s);

@@ -13,8 +13,15 @@
 //                experts, per-chunk bases, and the tile list;
 //   k_meta_rank  stable ranks: each wave walks its sub-chunk in order, 64
 //                entries at a time, and ranks equal keys with ballots, so the
-//                position of entry f is its expert's base plus the number of
-//                earlier entries with the same expert.
+//                rank of entry f within its expert is the number of earlier
+//                entries with the same expert.
+//
+// Expert capacity C ("MoE computation principle and execution process",
+// section 3.4): an entry whose rank within its expert is C or more is dropped
+// (inv = -1); expert e keeps min(count_e, C) rows, the bins (offsets) and the
+// tile list cover the kept rows only, and sorted_flat lists the kept rows
+// followed by -1 for each dropped one.  counts stays the full histogram.
+// With C >= every count nothing is dropped and the result is the dropless one.
 #include "common.h"
 
 namespace {
@@ -76,17 +83,22 @@ __device__ __forceinline__ int wave_excl_scan_experts(const int* vals, int* out,
 }
 
 // One workgroup of 16 waves.  blk [E][nblk] holds the chunk histograms on
-// entry and, on exit, the first sorted position of each (expert, chunk):
-// the expert's offset plus the counts of its earlier chunks.  Also writes
-// counts, offsets and the tile list (ceil(count / tile_m) tiles per expert,
+// entry and, on exit, the rank within its expert of the first entry of each
+// (expert, chunk): the counts of the expert's earlier chunks.  pos [2][E]
+// receives, per expert, the first position of its kept rows and of its
+// dropped rows (after all kept rows).  Also writes counts (full), offsets
+// (kept rows) and the tile list (ceil(kept / tile_m) tiles per expert,
 // experts ascending).
 constexpr int kScanWaves = 16;
-__global__ __launch_bounds__(kScanWaves * 64) void k_meta_scan(int32_t* __restrict__ blk, int32_t* __restrict__ counts,
+__global__ __launch_bounds__(kScanWaves * 64) void k_meta_scan(int32_t* __restrict__ blk, int32_t* __restrict__ pos,
+                                                              int32_t* __restrict__ counts,
                                                               int32_t* __restrict__ offsets,
                                                               int32_t* __restrict__ tiles,
-                                                              int32_t* __restrict__ num_tiles, int nblk, int E, int NK,
-                                                              int tile_m) {
-  __shared__ int tot[MOE_MAX_EXPERTS], off[MOE_MAX_EXPERTS], ntl[MOE_MAX_EXPERTS], tfirst[MOE_MAX_EXPERTS];
+                                                              int32_t* __restrict__ num_tiles, int nblk, int E,
+                                                              int tile_m, int capacity) {
+  __shared__ int tot[MOE_MAX_EXPERTS], kept[MOE_MAX_EXPERTS], drop[MOE_MAX_EXPERTS], off[MOE_MAX_EXPERTS],
+      doff[MOE_MAX_EXPERTS], ntl[MOE_MAX_EXPERTS], tfirst[MOE_MAX_EXPERTS];
+  __shared__ int nkept;
   const int w = threadIdx.x >> 6, lane = lane_id();
   // expert totals (wave per expert; integer sums, order-free)
   for (int e = w; e < E; e += kScanWaves) {
@@ -95,23 +107,28 @@ __global__ __launch_bounds__(kScanWaves * 64) void k_meta_scan(int32_t* __restri
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, kWave);
     if (lane == 0) {
+      const int k = min(sum, capacity);
       tot[e] = sum;
-      ntl[e] = (sum + tile_m - 1) / tile_m;
+      kept[e] = k;
+      drop[e] = sum - k;
+      ntl[e] = (k + tile_m - 1) / tile_m;
     }
   }
   __syncthreads();
   if (w == 0) {
-    wave_excl_scan_experts(tot, off, E);
+    const int nk = wave_excl_scan_experts(kept, off, E);
+    wave_excl_scan_experts(drop, doff, E);
     const int nt = wave_excl_scan_experts(ntl, tfirst, E);
     if (lane == 0) {
       *num_tiles = nt;
-      offsets[E] = NK;
+      offsets[E] = nk;
+      nkept = nk;
     }
   }
   __syncthreads();
   // per-chunk bases: exclusive prefix over the chunks of each expert
   for (int e = w; e < E; e += kScanWaves) {
-    int carry = off[e];
+    int carry = 0;
     for (int b0 = 0; b0 < nblk; b0 += kWave) {
       const int b = b0 + lane;
       const int c = b < nblk ? blk[(int64_t)e * nblk + b] : 0;
@@ -120,22 +137,25 @@ __global__ __launch_bounds__(kScanWaves * 64) void k_meta_scan(int32_t* __restri
       carry += __shfl(incl, kWave - 1, kWave);
     }
   }
-  // counts, offsets and the tiles of expert e
+  // counts, offsets, first kept / dropped positions and the tiles of expert e
   for (int e = threadIdx.x; e < E; e += kScanWaves * 64) {
     counts[e] = tot[e];
     offsets[e] = off[e];
+    pos[e] = off[e];
+    pos[E + e] = nkept + doff[e];
     for (int t = 0; t < ntl[e]; ++t) {
       const int64_t o = 3 * (int64_t)(tfirst[e] + t);
       tiles[o + 0] = e;
       tiles[o + 1] = off[e] + t * tile_m;
-      tiles[o + 2] = min(tile_m, tot[e] - t * tile_m);
+      tiles[o + 2] = min(tile_m, kept[e] - t * tile_m);
     }
   }
 }
 
 __global__ __launch_bounds__(256) void k_meta_rank(const int32_t* __restrict__ topk, const int32_t* __restrict__ blk,
-                                                   int32_t* __restrict__ sorted_flat, int32_t* __restrict__ inv, int NK,
-                                                   int E, int key_bits) {
+                                                   const int32_t* __restrict__ pos0, int32_t* __restrict__ sorted_flat,
+                                                   int32_t* __restrict__ inv, int NK, int E, int key_bits,
+                                                   int capacity) {
   const int nblk = gridDim.x;
   __shared__ int wcount[4][MOE_MAX_EXPERTS];
   const int tid = threadIdx.x;
@@ -177,18 +197,24 @@ __global__ __launch_bounds__(256) void k_meta_rank(const int32_t* __restrict__ t
     }
   }
   __syncthreads();
-  // pass 2: stable positions, 64 entries at a time in flat order
+  // pass 2: stable ranks, 64 entries at a time in flat order; a kept entry
+  // goes to its expert's kept rows, a dropped one marks a dropped row
   for (int p = 0; p < kPerWave; p += kWave) {
     int f = base + p + lane;
     int key = (f < NK) ? topk[f] : -1;
     bool valid = unsigned(key) < unsigned(E);
     if (!valid) key = 0;
     uint64_t m = match(key, valid);
-    int pos = 0;
     if (valid) {
-      pos = wcount[w][key] + __popcll(m & lt_mask);
-      sorted_flat[pos] = f;
-      inv[f] = pos;
+      const int g = wcount[w][key] + __popcll(m & lt_mask);
+      if (g < capacity) {
+        const int pos = pos0[key] + g;
+        sorted_flat[pos] = f;
+        inv[f] = pos;
+      } else {
+        sorted_flat[pos0[E + key] + (g - capacity)] = -1;
+        inv[f] = -1;
+      }
     }
     __builtin_amdgcn_wave_barrier();
     if (valid && (m & lt_mask) == 0) wcount[w][key] += __popcll(m);
@@ -202,27 +228,31 @@ namespace moe_launch {
 
 int64_t max_tiles(const Dims& d) { return (d.NK() + d.E * (MOE_TILE_M - 1)) / MOE_TILE_M; }
 
+// [E][nblk] chunk histograms / bases, then [2][E] first kept / dropped positions
 size_t permute_meta_ws(const Dims& d) {
   int64_t nblk = (d.NK() + kChunk - 1) / kChunk;
-  return size_t(nblk) * size_t(d.E) * sizeof(int32_t);
+  return (size_t(nblk) * size_t(d.E) + 2 * size_t(d.E)) * sizeof(int32_t);
 }
 
-hipError_t permute_meta(const Dims& d, const int32_t* topk, int32_t* sorted_flat, int32_t* inv, int32_t* counts,
-                        int32_t* offsets, int32_t* tiles, int32_t* num_tiles, void* ws, hipStream_t s) {
+hipError_t permute_meta(const Dims& d, const int32_t* topk, int32_t capacity, int32_t* sorted_flat, int32_t* inv,
+                        int32_t* counts, int32_t* offsets, int32_t* tiles, int32_t* num_tiles, void* ws,
+                        hipStream_t s) {
   int NK = int(d.NK());
   int E = int(d.E);
   int nblk = (NK + kChunk - 1) / kChunk;
   int32_t* blk = static_cast<int32_t*>(ws);
+  int32_t* pos = blk + (int64_t)nblk * E;
   hipLaunchKernelGGL(k_meta_hist, dim3(nblk), dim3(256), 0, s, topk, blk, NK, E);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_meta_scan, dim3(1), dim3(kScanWaves * 64), 0, s, blk, counts, offsets, tiles, num_tiles, nblk, E,
-                     NK, MOE_TILE_M);
+  hipLaunchKernelGGL(k_meta_scan, dim3(1), dim3(kScanWaves * 64), 0, s, blk, pos, counts, offsets, tiles, num_tiles, nblk,
+                     E, MOE_TILE_M, int(capacity));
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   int key_bits = 0;
   while ((1 << key_bits) < E) ++key_bits;
-  hipLaunchKernelGGL(k_meta_rank, dim3(nblk), dim3(256), 0, s, topk, blk, sorted_flat, inv, NK, E, key_bits);
+  hipLaunchKernelGGL(k_meta_rank, dim3(nblk), dim3(256), 0, s, topk, blk, pos, sorted_flat, inv, NK, E, key_bits,
+                     int(capacity));
   return hipGetLastError();
 }
 

@@ -22,14 +22,17 @@ __global__ __launch_bounds__(256) void k_permute(const T* __restrict__ x, const 
   for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < total_vec; v += stride) {
     int64_t row = v / vpr;
     int c = int(v - row * vpr);
-    int64_t tok = sorted_flat[row] / K;
+    const int32_t f = sorted_flat[row];
+    if (f < 0) continue;  // dropped row (capacity): never read
+    int64_t tok = f / K;
     const uint4* src = reinterpret_cast<const uint4*>(x + (tok * vpr + c) * V);
     uint4* dst = reinterpret_cast<uint4*>(xs + v * V);
     *dst = *src;
   }
 }
 
-// y[n] = sum_k gates[n,k] * ys[inv[n*K+k]], k ascending, float32 accumulation.
+// y[n] = sum_k gates[n,k] * ys[inv[n*K+k]], k ascending, float32 accumulation;
+// dropped slots (inv < 0) add nothing.
 template <typename T>
 __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ ys, const float* __restrict__ gates,
                                                  const int32_t* __restrict__ inv, T* __restrict__ y,
@@ -44,6 +47,7 @@ __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ ys, const
     for (int i = 0; i < V; ++i) acc[i] = 0.f;
     for (int k = 0; k < K; ++k) {
       int64_t r = inv[n * K + k];
+      if (r < 0) continue;
       float g = gates[n * K + k];
       float val[V];
       Vec16<T>::load(ys + (r * vpr + c) * V, val);
@@ -56,7 +60,8 @@ __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ ys, const
 
 // One wave per token, kTokPerWave tokens per wave in turn:
 // dys[inv[n,k]] = g_k * dy[n]; dgates[n,k] = <dy[n], ys[inv[n,k]]> (fixed
-// lane order and butterfly, so the dot products are reproducible).
+// lane order and butterfly, so the dot products are reproducible).  A
+// dropped slot (inv < 0) has no row and a zero gate gradient.
 constexpr int kTokPerWave = 2;
 template <typename T>
 __global__ __launch_bounds__(256) void k_combine_bwd(const T* __restrict__ dy, const T* __restrict__ ys,
@@ -90,10 +95,10 @@ __global__ __launch_bounds__(256) void k_combine_bwd(const T* __restrict__ dy, c
       uint4 raw[MOE_MAX_TOPK];
 #pragma unroll
       for (int k = 0; k < MOE_MAX_TOPK; ++k)
-        if (k < K) raw[k] = *reinterpret_cast<const uint4*>(ys + (r[t][k] * vpr + c) * V);
+        if (k < K && r[t][k] >= 0) raw[k] = *reinterpret_cast<const uint4*>(ys + (r[t][k] * vpr + c) * V);
 #pragma unroll
       for (int k = 0; k < MOE_MAX_TOPK; ++k) {
-        if (k < K) {
+        if (k < K && r[t][k] >= 0) {
           float yv[V], o[V];
           Vec16<T>::load(reinterpret_cast<const T*>(&raw[k]), yv);
           float s = dot[k];
@@ -127,8 +132,9 @@ __global__ __launch_bounds__(256) void k_transpose_wr(const T* __restrict__ w_r,
 }
 
 // dx[n] = sum_k dxs[inv[n*K+k]] + sum_k dlogits[n, e_k] * W_r[:, e_k], both
-// sums in ascending k; one wave per token.  DENSE: the router term runs over
-// all E experts (dlogits is dense when the load-balancing loss is on).
+// sums in ascending k (dropped slots, inv < 0, have no dxs row); one wave per
+// token.  DENSE: the router term runs over all E experts (dlogits is dense
+// when the load-balancing loss is on).
 template <typename T, bool DENSE>
 __global__ __launch_bounds__(256) void k_permute_bwd(const T* __restrict__ dxs, const int32_t* __restrict__ inv,
                                                      const int32_t* __restrict__ topk, const float* __restrict__ dl,
@@ -140,11 +146,14 @@ __global__ __launch_bounds__(256) void k_permute_bwd(const T* __restrict__ dxs, 
   if (n >= N) return;
   const uint4 *sx[MOE_MAX_TOPK], *sw[MOE_MAX_TOPK];
   float d[MOE_MAX_TOPK];
+  bool kept[MOE_MAX_TOPK];
 #pragma unroll
   for (int k = 0; k < MOE_MAX_TOPK; ++k)
     if (k < K) {
       const int e = topk[n * K + k];
-      sx[k] = reinterpret_cast<const uint4*>(dxs) + (int64_t)inv[n * K + k] * vpr;
+      const int32_t r = inv[n * K + k];
+      kept[k] = r >= 0;
+      sx[k] = reinterpret_cast<const uint4*>(dxs) + (int64_t)(kept[k] ? r : 0) * vpr;
       sw[k] = reinterpret_cast<const uint4*>(w_rt) + (int64_t)e * vpr;
       d[k] = dl[n * E + e];
     }
@@ -154,7 +163,7 @@ __global__ __launch_bounds__(256) void k_permute_bwd(const T* __restrict__ dxs, 
 #pragma unroll
     for (int k = 0; k < MOE_MAX_TOPK; ++k)
       if (k < K) {
-        rx[k] = sx[k][c];
+        if (kept[k]) rx[k] = sx[k][c];
         rw[k] = sw[k][c];
       }
     float acc[V];
@@ -162,7 +171,7 @@ __global__ __launch_bounds__(256) void k_permute_bwd(const T* __restrict__ dxs, 
     for (int i = 0; i < V; ++i) acc[i] = 0.f;
 #pragma unroll
     for (int k = 0; k < MOE_MAX_TOPK; ++k)
-      if (k < K) {
+      if (k < K && kept[k]) {
         float val[V];
         Vec16<T>::load(reinterpret_cast<const T*>(&rx[k]), val);
 #pragma unroll
@@ -226,12 +235,15 @@ __global__ __launch_bounds__(256) void k_permute_bwd_dense_tiled(const T* __rest
       for (int i = 0; i < V; ++i) acc[t][i] = 0.f;
       if (t < nt) {
         uint4 rx[MOE_MAX_TOPK];
+        int32_t rr[MOE_MAX_TOPK];
+#pragma unroll
+        for (int k = 0; k < MOE_MAX_TOPK; ++k) {
+          rr[k] = k < K ? inv[(n0 + t) * K + k] : -1;
+          if (rr[k] >= 0) rx[k] = xs4[(int64_t)rr[k] * vpr + c];
+        }
 #pragma unroll
         for (int k = 0; k < MOE_MAX_TOPK; ++k)
-          if (k < K) rx[k] = xs4[(int64_t)inv[(n0 + t) * K + k] * vpr + c];
-#pragma unroll
-        for (int k = 0; k < MOE_MAX_TOPK; ++k)
-          if (k < K) {
+          if (rr[k] >= 0) {
             float val[V];
             Vec16<T>::load(reinterpret_cast<const T*>(&rx[k]), val);
 #pragma unroll

@@ -26,12 +26,16 @@ class MoELayerRunner:
     """Device buffers and C-ABI calls for fixed (N, H, F, E, K, dtype)."""
 
     def __init__(self, N: int, H: int, F: int, E: int, K: int, dtype: torch.dtype, device="cuda",
-                 backward: bool = True, save_gu: Optional[bool] = None, aux_alpha: Optional[float] = None):
-        """aux_alpha: weight of the Switch load-balancing loss; None turns it off."""
+                 backward: bool = True, save_gu: Optional[bool] = None, aux_alpha: Optional[float] = None,
+                 capacity: Optional[int] = None):
+        """aux_alpha: weight of the Switch load-balancing loss; None turns it off.
+        capacity: expert capacity (rows per expert, the overflow dropped);
+        None is the dropless layer."""
         self.N, self.H, self.F, self.E, self.K = N, H, F, E, K
         self.dtype = dtype
         self.device = torch.device(device)
         self.d = L.dims(N, H, F, E, K, L.dtype_code(dtype))
+        self.capacity = capacity
         self.with_backward = backward
         save_gu = backward if save_gu is None else save_gu
         NK = N * K
@@ -98,8 +102,13 @@ class MoELayerRunner:
         L.moe_route(self.d, x, w_r, bias, self.topk, self.gates, stream)
 
     def meta(self, topk=None, stream=None):
-        L.moe_permute_meta(self.d, self.topk if topk is None else topk, self.sorted_flat, self.inv, self.counts,
-                           self.offsets, self.tiles, self.num_tiles, self.meta_ws, stream)
+        tk = self.topk if topk is None else topk
+        if self.capacity is None:
+            L.moe_permute_meta(self.d, tk, self.sorted_flat, self.inv, self.counts, self.offsets, self.tiles,
+                               self.num_tiles, self.meta_ws, stream)
+        else:
+            L.moe_permute_meta_capacity(self.d, tk, self.capacity, self.sorted_flat, self.inv, self.counts,
+                                        self.offsets, self.tiles, self.num_tiles, self.meta_ws, stream)
 
     def forward(self, x, w_r, w_gate, w_up, w_down, bias=None, topk=None, gates=None, stream=None):
         """Run the forward; returns y.  ``topk``/``gates`` (optional) replace the

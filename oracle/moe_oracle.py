@@ -558,10 +558,13 @@ def rounding_bands(fwd: dict, bwd: Optional[dict] = None, dy=None, aux_scale: Op
     NK = N * K
     F = fwd["w_gate"].shape[2]
     off, sf, inv = fwd["offsets"], fwd["sorted_flat"], fwd["inv"]
-    inv2 = inv.reshape(N, K)
-    tok = sf // K
+    # dropped slots (capacity) have no row: masked out of every sum below
+    kept2 = (inv >= 0).reshape(N, K)
+    kept_row = (sf >= 0)[:, None]
+    inv2 = np.maximum(inv, 0).reshape(N, K)
+    tok = np.maximum(sf, 0) // K
     gflat = fwd["gates"].reshape(-1)
-    grow = gflat[sf][:, None]
+    grow = gflat[np.maximum(sf, 0)][:, None] * kept_row
     xs, G, U, A, ys = fwd["xs"], fwd["G"], fwd["U"], fwd["A"], fwd["ys"]
     b = {k: np.zeros((NK, F)) for k in ("G", "U", "A")}
     b["ys"] = np.zeros((NK, H))
@@ -581,7 +584,7 @@ def rounding_bands(fwd: dict, bwd: Optional[dict] = None, dy=None, aux_scale: Op
     sy = np.zeros((N, H))
     for k in range(K):
         r = inv2[:, k]
-        g = fwd["gates"][:, k:k + 1]
+        g = fwd["gates"][:, k:k + 1] * kept2[:, k:k + 1]
         yp += g * ys[r]
         sy += g * b["ys"][r] + 8 * U32 * np.abs(g * ys[r])
     b["y"] = bf16_flip(yp, fwd["y"], sy)
@@ -592,8 +595,8 @@ def rounding_bands(fwd: dict, bwd: Optional[dict] = None, dy=None, aux_scale: Op
     # combine backward
     dysp = grow * dy[tok]
     b["dys"] = bf16_flip(dysp, bwd["dys"], 8 * U32 * np.abs(dysp))
-    ys_tok = ys[inv2]
-    b_ys_tok = b["ys"][inv2]
+    ys_tok = ys[inv2] * kept2[:, :, None]
+    b_ys_tok = b["ys"][inv2] * kept2[:, :, None]
     lin = np.einsum("nh,nkh->nk", np.abs(dy), b_ys_tok)
     rss = 4.0 * np.sqrt(np.einsum("nh,nkh->nk", dy * dy, b_ys_tok * b_ys_tok))
     b["dgates"] = (np.minimum(lin, rss)
@@ -650,9 +653,10 @@ def rounding_bands(fwd: dict, bwd: Optional[dict] = None, dy=None, aux_scale: Op
             abs(aux_scale) * E / N * p * 4 * fmax * dl_max + 8 * U32 * np.abs(bwd["dlogits"]))
     b["dw_r"] = prop(b["dlogits"].T, x).T + gemm_sigma(x.T, bwd["dlogits"]) + 2 * U32 * np.abs(bwd["dw_r"])
     # gather backward
-    dxp = bwd["dxs"][inv2].sum(axis=1) + bwd["dlogits"] @ w_r.T
-    sdx = (b["dxs"][inv2].sum(axis=1) + prop(b["dlogits"], w_r.T)
-           + 8 * U32 * (np.abs(bwd["dxs"][inv2]).sum(axis=1) + np.abs(bwd["dlogits"]) @ np.abs(w_r.T)))
+    dxs_tok = bwd["dxs"][inv2] * kept2[:, :, None]
+    dxp = dxs_tok.sum(axis=1) + bwd["dlogits"] @ w_r.T
+    sdx = ((b["dxs"][inv2] * kept2[:, :, None]).sum(axis=1) + prop(b["dlogits"], w_r.T)
+           + 8 * U32 * (np.abs(dxs_tok).sum(axis=1) + np.abs(bwd["dlogits"]) @ np.abs(w_r.T)))
     b["dx"] = bf16_flip(dxp, bwd["dx"], sdx)
     return b
 

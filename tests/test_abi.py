@@ -138,3 +138,22 @@ def test_aux_loss_entries_validate_on_the_host(lib):
                                     None) == L.MOE_EWORKSPACE
     d0 = D(N=0)
     assert lb.moe_aux_loss(ctypes.byref(d0), FAKE, FAKE, None, FAKE, 0.01, FAKE, FAKE, None, 0, None) == L.MOE_OK
+
+
+def test_capacity_and_gather_entries_validate_on_the_host(lib):
+    d = D(E=8)
+    lb = L.lib()
+    need = L.moe_workspace_bytes(d, L.MOE_ENTRY_PERMUTE_META)
+    args = [FAKE] * 7
+    assert lb.moe_permute_meta_capacity(ctypes.byref(d), FAKE, -1, *args, need, None) == L.MOE_EINVAL
+    assert lb.moe_permute_meta_capacity(ctypes.byref(d), FAKE, 5, *args, need - 4, None) == L.MOE_EWORKSPACE
+    assert lb.moe_permute_meta_capacity(ctypes.byref(d), None, 5, *args, need, None) == L.MOE_EINVAL
+    d0 = D(N=0)
+    assert lb.moe_permute_meta_capacity(ctypes.byref(d0), FAKE, 0, *([FAKE] * 6), None, 0, None) == L.MOE_OK
+    # gathered gate/up: null source rows, one of g/u missing, 32-bit row offsets
+    gu = [FAKE] * 4
+    assert lb.moe_ffn_gate_up_gather(ctypes.byref(d), FAKE, None, *gu, FAKE, FAKE, FAKE, None) == L.MOE_EINVAL
+    assert lb.moe_ffn_gate_up_gather(ctypes.byref(d), FAKE, FAKE, *gu, FAKE, None, FAKE, None) == L.MOE_EINVAL
+    big = D(N=2 ** 21, H=1024)
+    assert lb.moe_ffn_gate_up_gather(ctypes.byref(big), FAKE, FAKE, *gu, FAKE, FAKE, FAKE,
+                                     None) == L.MOE_EUNSUPPORTED

@@ -1,0 +1,153 @@
+"""Parity of the token-dropping capacity variant on the GPU (through the C
+ABI) with the CPU oracle.
+
+Expert capacity C: each expert keeps its first C rows in the stable grouped
+order and drops the rest ("MoE computation principle and execution process",
+section 3.4).  Checked: the metadata bit-exact (counts, kept bins, sorted
+rows with the -1 tail, inv with -1 for dropped slots, tile list), the whole
+forward and backward against the oracle with the oracle's assignment, the
+case C >= max count against the dropless path byte for byte, C = 0, the
+forward-only gathered gate/up with dropping, and the metadata at the skewed
+workload's full size.
+"""
+import numpy as np
+import pytest
+import torch
+
+from moe_workloads import BASE, SKEWED, TEST_CONFIGS, make_inputs
+from oracle import moe_oracle as O
+from tests.gpu_common import assert_close, gpu_inputs, store_of, sync, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from mixture_experts_layer_sort_amd import _lib
+    _lib.lib()
+
+
+def _runner(cfg, C, backward=True):
+    from mixture_experts_layer_sort_amd.layer import MoELayerRunner
+    return MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, "cuda", backward=backward, capacity=C)
+
+
+def _oracle(cfg, cpu, C):
+    return O.forward(cpu["x"], cpu["w_r"], cpu["w_gate"], cpu["w_up"], cpu["w_down"], cfg.K, bias=cpu["bias"],
+                     store=store_of(cfg), tile_m=256, capacity=C)
+
+
+def _check_meta(r, of, label):
+    nt = int(r.num_tiles.cpu().item())
+    got = dict(counts=r.counts, offsets=r.offsets, sorted_flat=r.sorted_flat, inv=r.inv)
+    for k, v in got.items():
+        assert np.array_equal(v.cpu().numpy().astype(np.int64), of[k].astype(np.int64)), (label, k)
+    assert nt == len(of["tiles"]) and nt <= r.max_tiles, label
+    assert np.array_equal(r.tiles.cpu().numpy()[:3 * nt].reshape(-1, 3), of["tiles"]), label
+
+
+CASES = [(TEST_CONFIGS["t_skew"], 1.0), (TEST_CONFIGS["t_ragged"], 0.75), (TEST_CONFIGS["t_f32"], 0.8),
+         (TEST_CONFIGS["t_wide_e"], 1.0), (BASE, 0.95)]
+
+
+@pytest.mark.parametrize("cfg,cf", CASES, ids=lambda v: getattr(v, "name", str(v)))
+def test_capacity_layer_matches_oracle(cfg, cf):
+    C = O.capacity_of(cfg.N, cfg.K, cfg.E, cf)
+    print(f"[capacity] {cfg.name} C={C}", flush=True)
+    cpu, dev = gpu_inputs(cfg, 8, with_dy=True)
+    of = _oracle(cfg, cpu, C)
+    nk = int(of["offsets"][-1])
+    assert nk < cfg.N * cfg.K, "the case must drop rows"
+    r = _runner(cfg, C)
+    y = r.forward(dev["x"], dev["w_r"], dev["w_gate"], dev["w_up"], dev["w_down"], dev["bias"],
+                  topk=torch.from_numpy(of["topk"]).cuda(),
+                  gates=torch.from_numpy(of["gates"].astype(np.float32)).cuda())
+    g = r.backward(dev["dy"])
+    sync()
+    _check_meta(r, of, cfg.name)
+    dt = store_of(cfg)
+    ob = O.backward(of, cpu["dy"])
+    bd = O.rounding_bands(of, ob, cpu["dy"]) if dt == "bf16" else {}
+    ref = dict(of)
+    ref.update(ob)
+    rows = {"xs": r.xs, "G": r.g, "U": r.u, "A": r.act, "ys": r.ys, "dys": r.dys, "dG": r.dg, "dU": r.du,
+            "dxs": r.dxs}
+    for name, t in rows.items():          # kept rows only: the rows past them are never written
+        band = bd.get(name)
+        assert_close(name, t[:nk], ref[name][:nk], dt, band=None if band is None else band[:nk])
+    for name, t in {"y": y, "dgates": g["dgates"], "dlogits": g["dlogits"], "dx": g["dx"], "dw_r": g["dw_r"],
+                    "dw_gate": g["dw_gate"], "dw_up": g["dw_up"], "dw_down": g["dw_down"]}.items():
+        assert_close(name, t, ref[name], dt, band=bd.get(name))
+    dropped = of["inv"].reshape(cfg.N, cfg.K) < 0
+    assert np.all(to_np(g["dgates"])[dropped] == 0)
+
+
+@pytest.mark.parametrize("cfg", [TEST_CONFIGS["t_skew"], TEST_CONFIGS["t_ragged"]], ids=lambda c: c.name)
+def test_capacity_at_max_count_equals_dropless_bitwise(cfg):
+    cpu, dev = gpu_inputs(cfg, 9, with_dy=True)
+    outs = []
+    for C in (None, "max"):
+        r = _runner(cfg, None)
+        if C == "max":
+            r.route(dev["x"], dev["w_r"], dev["bias"])
+            r.meta()
+            sync()
+            r = _runner(cfg, int(r.counts.max().item()))
+        y = r.forward(dev["x"], dev["w_r"], dev["w_gate"], dev["w_up"], dev["w_down"], dev["bias"])
+        g = r.backward(dev["dy"])
+        sync()
+        outs.append({k: v.clone() for k, v in dict(y=y, **g).items()})
+    for k, v in outs[0].items():
+        assert torch.equal(v.view(torch.uint8), outs[1][k].view(torch.uint8)), k
+
+
+def test_zero_capacity_gives_zero_output_and_gradients():
+    cfg = TEST_CONFIGS["t_skew"]
+    cpu, dev = gpu_inputs(cfg, 10, with_dy=True)
+    r = _runner(cfg, 0)
+    for name in ("y", "dx", "dgates", "dlogits", "dw_r", "dw_gate", "dw_up", "dw_down"):
+        getattr(r, name).view(torch.uint8).fill_(0xFF)
+    y = r.forward(dev["x"], dev["w_r"], dev["w_gate"], dev["w_up"], dev["w_down"], dev["bias"])
+    g = r.backward(dev["dy"])
+    sync()
+    assert int(r.num_tiles.item()) == 0 and int(r.offsets[-1].item()) == 0
+    assert torch.all(r.inv == -1) and torch.all(r.sorted_flat == -1)
+    for name, t in dict(y=y, **g).items():
+        assert torch.count_nonzero(t).item() == 0, name
+
+
+@pytest.mark.parametrize("cfg,cf", [(TEST_CONFIGS["t_skew"], 1.0), (TEST_CONFIGS["t_wide_e"], 1.0)],
+                         ids=lambda v: getattr(v, "name", str(v)))
+def test_capacity_forward_only_gather_equals_training_forward(cfg, cf):
+    C = O.capacity_of(cfg.N, cfg.K, cfg.E, cf)
+    cpu, dev = gpu_inputs(cfg, 11)
+    f = _runner(cfg, C, backward=False)
+    t = _runner(cfg, C)
+    assert f.gather_fused
+    yf = f.forward(dev["x"], dev["w_r"], dev["w_gate"], dev["w_up"], dev["w_down"], dev["bias"])
+    yt = t.forward(dev["x"], dev["w_r"], dev["w_gate"], dev["w_up"], dev["w_down"], dev["bias"])
+    sync()
+    assert torch.equal(yf.view(torch.uint8), yt.view(torch.uint8))
+
+
+def test_capacity_metadata_at_full_size_skewed():
+    """Skewed workload (N=16384, E=64, K=6, Zipf bias), capacity factor 1.25:
+    the hottest experts overflow; the metadata of the oracle's assignment is
+    bit-exact."""
+    cfg = SKEWED
+    C = O.capacity_of(cfg.N, cfg.K, cfg.E, 1.25)
+    cpu = make_inputs(cfg, 0)
+    x, w_r, b = (O.as_f64(cpu[k]) for k in ("x", "w_r", "bias"))
+    topk = O.topk_experts(O.router_logits(x, w_r, b), cfg.K)
+    counts, offsets, sf, inv = O.routing_metadata(topk, cfg.E, C)
+    of = dict(counts=counts, offsets=offsets, sorted_flat=sf, inv=inv,
+              tiles=O.tile_list(np.diff(offsets), offsets, 256))
+    assert (counts > C).sum() > 0
+    r = _runner(cfg, C, backward=False)
+    r.meta(topk=torch.from_numpy(topk.astype(np.int32)).cuda())
+    sync()
+    _check_meta(r, of, cfg.name)
+    print(f"skewed: C={C}, {int((counts > C).sum())} experts overflow, "
+          f"{cfg.N * cfg.K - int(offsets[-1])} of {cfg.N * cfg.K} rows dropped", flush=True)

@@ -171,3 +171,34 @@ def test_planted_mistake_keeping_the_last_rows_is_caught(monkeypatch):
         test_output_matches_bruteforce_keep_rule(CFGS[0], 0.5)
     monkeypatch.setattr(O, "routing_metadata", good)
     test_output_matches_bruteforce_keep_rule(CFGS[0], 0.5)
+
+
+@pytest.mark.parametrize("cfg", CFGS, ids=lambda c: c.name)
+def test_bands_with_capacity(cfg):
+    """Rounding bands: with C >= max count they are the dropless bands; with
+    a binding C the dropped slots carry no band and the float32 evaluation of
+    the kept rows' combine lands inside the y band."""
+    inp = _inputs(cfg, 6)
+    cfg16 = dict(store="bf16")
+    ref = _fwd(inp, cfg.K, None, **cfg16)
+    rb = O.backward(ref, inp["dy"])
+    band_ref = O.rounding_bands(ref, rb, inp["dy"])
+    big = _fwd(inp, cfg.K, int(ref["counts"].max()), **cfg16)
+    band_big = O.rounding_bands(big, O.backward(big, inp["dy"]), inp["dy"])
+    for k, v in band_ref.items():
+        assert np.array_equal(band_big[k], v), k
+    C = O.capacity_of(cfg.N, cfg.K, cfg.E, 0.75)
+    f = _fwd(inp, cfg.K, C, **cfg16)
+    b = O.backward(f, inp["dy"])
+    band = O.rounding_bands(f, b, inp["dy"])
+    dropped = f["inv"].reshape(cfg.N, cfg.K) < 0
+    assert dropped.any() and np.all(band["dgates"][dropped] == 0) and np.all(b["dgates"][dropped] == 0)
+    for k, v in band.items():
+        assert np.all(np.isfinite(v)) and np.all(v >= 0), k
+    # float32 combine of the kept rows (k ascending) stays inside the y band
+    inv = np.maximum(f["inv"], 0).reshape(cfg.N, cfg.K)
+    y32 = np.zeros((cfg.N, cfg.H), dtype=np.float32)
+    for k in range(cfg.K):
+        y32 += (f["gates"][:, k:k + 1] * ~dropped[:, k:k + 1]).astype(np.float32) * f["ys"][inv[:, k]].astype(np.float32)
+    y32 = O.round_bf16(y32.astype(np.float64))
+    assert np.all(np.abs(y32 - f["y"]) <= band["y"] + 1e-30)
