@@ -39,13 +39,13 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # kernel sources whose hash is stored with them; once any source under csrc/
 # changes, the figure is reported as null until the counters are taken again.
 TRAFFIC = {
-    "sources": "aa8cfd277f7cf79b",
+    "sources": "8bf9ccd18e985276",
     "bytes": {
-        ("bf16_n16384_h512_f1024_e8_k2", "gate_up"): 336237477,
-        ("bf16_n16384_h512_f1024_e8_k2", "down"): 144180094,
-        ("bf16_n16384_h512_f1024_e8_k2", "dact"): 339640637,
-        ("bf16_n16384_h512_f1024_e8_k2", "dx"): 272830856,
-        ("bf16_n16384_h512_f1024_e8_k2", "dw"): 352732447,
+        ("bf16_n16384_h512_f1024_e8_k2", "gate_up"): 336261941,
+        ("bf16_n16384_h512_f1024_e8_k2", "down"): 144317487,
+        ("bf16_n16384_h512_f1024_e8_k2", "dact"): 339593548,
+        ("bf16_n16384_h512_f1024_e8_k2", "dx"): 273149465,
+        ("bf16_n16384_h512_f1024_e8_k2", "dw"): 352734088,
     },
 }
 
@@ -169,8 +169,7 @@ def main():
     x, w_r, wg, wu, wd, bias, dy = (inp[k] for k in ("x", "w_r", "w_gate", "w_up", "w_down", "bias", "dy"))
     stream = torch.cuda.current_stream()
     # the backward runs the router backward beside dA on a second stream
-    # (default priority), and the weight gradients beside dX when they cannot
-    # fill the CUs alone, as MoELayerRunner does
+    # (default priority), as MoELayerRunner does; the GEMMs keep the GPU
     side = torch.cuda.Stream() if cfg.backward else None
     permute_bwd = L.moe_permute_bwd if aux is None else L.moe_permute_bwd_dense
     fns = {
@@ -229,12 +228,8 @@ def main():
         route_done = torch.cuda.Event()
         route_done.record(side)
         run("dact", stream)
-        if r.dw_beside_dx:
-            hand_over(stream, side)
-            run("dw", side)
-        else:
-            run("dw", stream)
         run("dx", stream)
+        run("dw", stream)
         stream.wait_event(route_done)
         run("permute_bwd", stream)
         hand_over(side, stream)
@@ -312,8 +307,7 @@ def main():
                    "gather_fused_into_gate_up": r.gather_fused,
                    "capacity": capacity,
                    "dropped_rows": cfg.NK - kept_rows,
-                   "streams": "router backward beside dA" + (", dW beside dX" if cfg.backward and r.dw_beside_dx
-                                                             else "") if cfg.backward else "one",
+                   "streams": "router backward beside dA" if cfg.backward else "one",
                    "empty_experts": int((counts == 0).sum())},
         "grouped_gemm": {"tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 2),
                          "frac_of_bf16_peak": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),

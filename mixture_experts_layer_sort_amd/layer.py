@@ -85,11 +85,6 @@ class MoELayerRunner:
             self.route_ws = self._ws(L.MOE_ENTRY_ROUTE_BWD if aux_alpha is None else L.MOE_ENTRY_ROUTE_BWD_AUX)
             self.perm_ws = self._ws(L.MOE_ENTRY_PERMUTE_BWD)
         self.inputs = None
-        # with a side stream the weight gradients run beside dX when their
-        # 256 x 256 output tiles (three problems per expert) cannot fill the
-        # CUs by themselves; otherwise beside dX they only slow each other
-        cus = torch.cuda.get_device_properties(self.device).multi_processor_count if self.device.type == "cuda" else 0
-        self.dw_beside_dx = 3 * E * (-(-H // 256)) * (-(-F // 256)) < cus
 
     def _ws(self, entry: int):
         n = L.moe_workspace_bytes(self.d, entry)
@@ -139,10 +134,10 @@ class MoELayerRunner:
         """Run the backward of the last forward; returns a dict of gradients.
         aux_grad: upstream gradient of the load-balancing loss (when on).
         side_stream: optional second stream (default priority).  The router
-        backward then runs beside dA, and, when they cannot fill the CUs by
-        themselves (``dw_beside_dx``), the weight gradients beside dX.  Every
-        launch is deterministic by itself, so the results are the same bits
-        either way.  ``stream`` waits for the side stream before returning."""
+        backward then runs beside dA (it needs only dgates); every launch is
+        deterministic by itself, so the results are the same bits either way.
+        The grouped GEMMs keep the whole GPU.  ``stream`` waits for the side
+        stream before returning."""
         if not self.with_backward:
             raise RuntimeError("runner was built without backward buffers")
         x, w_r, w_gate, w_up, w_down = self.inputs
@@ -172,12 +167,9 @@ class MoELayerRunner:
         route_done = torch.cuda.Event()
         route_done.record(side)
         L.moe_ffn_bwd_dact(d, self.dys, w_down, self.g, self.u, self.tiles, self.num_tiles, self.dg, self.du, main)
-        dw_stream = side if self.dw_beside_dx else main
-        if dw_stream is side:
-            fork()
-        L.moe_ffn_bwd_dw(d, self.xs, self.act, self.dys, self.dg, self.du, self.offsets, self.dw_gate, self.dw_up,
-                         self.dw_down, dw_stream)
         L.moe_ffn_bwd_dx(d, self.dg, self.du, w_gate, w_up, self.tiles, self.num_tiles, self.dxs, main)
+        L.moe_ffn_bwd_dw(d, self.xs, self.act, self.dys, self.dg, self.du, self.offsets, self.dw_gate, self.dw_up,
+                         self.dw_down, main)
         if side is not main:
             main.wait_event(route_done)
         permute_bwd = L.moe_permute_bwd if self.aux_alpha is None else L.moe_permute_bwd_dense

@@ -149,19 +149,15 @@ def test_bitwise_reproducible(cfg):
             assert torch.equal(outs[0][k].view(torch.uint8), outs[rep][k].view(torch.uint8)), (rep, k)
 
 
-@pytest.mark.parametrize("cfg", [TEST_CONFIGS["t_skew"], BASE,
-                                 # weight gradients fill the CUs: only the router backward moves
-                                 MoEConfig("t_streams_e32", N=1024, H=1024, F=1024, E=32, K=2, dtype="bf16")],
-                         ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [TEST_CONFIGS["t_skew"], BASE], ids=lambda c: c.name)
 def test_two_stream_backward_is_bitwise_identical(cfg):
-    """The backward with the router backward and the weight gradients on a
-    second stream gives the same bytes as the one-stream backward, repeated
+    """The backward with the router backward on a second stream gives the
+    same bytes as the one-stream backward, repeated
     three times with the forward in between (the side stream's reads of the
     previous step must be finished before the next forward writes)."""
     print(f"[two streams] {cfg.name}", flush=True)
     cpu, dev = gpu_inputs(cfg, 4, with_dy=True)
     r = _runner(cfg)
-    assert r.dw_beside_dx == (cfg.name != "t_streams_e32")
     y = r.forward(dev["x"], dev["w_r"], dev["w_gate"], dev["w_up"], dev["w_down"], dev["bias"])
     g = r.backward(dev["dy"])
     sync()
