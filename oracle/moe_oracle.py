@@ -286,7 +286,7 @@ def aux_loss_grad(logits: np.ndarray, counts: np.ndarray, K: int, scale: float) 
 # --------------------------------------------------------------------------
 
 def forward(x, w_r, w_gate, w_up, w_down, K: int, bias=None, store: str = "bf16", tile_m: int = 128,
-            topk=None, capacity: Optional[int] = None):
+            topk=None, capacity: Optional[int] = None, shared=None):
     """Forward pass of the layer; returns every intermediate in a dict.
 
     Steps in the pages' order: logits, top-K, gates, metadata (histogram,
@@ -301,6 +301,12 @@ def forward(x, w_r, w_gate, w_up, w_down, K: int, bias=None, store: str = "bf16"
     ``capacity`` (optional) caps the rows each expert takes (see
     routing_metadata); a dropped slot contributes nothing to y and its gate
     is not renormalised away.  Rows past the kept ones stay zero.
+
+    ``shared`` (optional) = (W_gate_s [H,Fs], W_up_s [H,Fs], W_down_s [Fs,H]):
+    a dense SwiGLU expert every token passes through with weight 1, added to
+    the routed output ("MegaBlocks - architecture and principles", section
+    2.1: the layer's output plus an optional shared-expert MLP over all
+    tokens): y = round(sum_k g_k ys[inv] + ys_s), ys_s stored rounded.
     """
     assert store in STORE_TYPES
     x = as_f64(x)
@@ -337,6 +343,13 @@ def forward(x, w_r, w_gate, w_up, w_down, K: int, bias=None, store: str = "bf16"
             continue
         G[r0:r1], U[r0:r1], A[r0:r1], ys[r0:r1] = swiglu_expert(xs[r0:r1], wg_all[e], wu_all[e], wd_all[e], store)
 
+    # shared expert: every token, token order, weight 1
+    sh = None
+    if shared is not None:
+        wgs, wus, wds = (as_f64(w) for w in shared)
+        Gs, Us, As, yss = swiglu_expert(x, wgs, wus, wds, store)
+        sh = dict(w_gate=wgs, w_up=wus, w_down=wds, G=Gs, U=Us, A=As, ys=yss)
+
     # index_add-style combine: each expert adds its gate-weighted rows into
     # the tokens they came from
     y = np.zeros((N, H))
@@ -347,11 +360,13 @@ def forward(x, w_r, w_gate, w_up, w_down, K: int, bias=None, store: str = "bf16"
             continue
         f = sorted_flat[r0:r1]
         np.add.at(y, f // K, gflat[f][:, None] * ys[r0:r1])
+    if sh is not None:
+        y = y + sh["ys"]
     y = rho(y, store)
     return dict(x=x, w_r=w_r, bias=bias, w_gate=wg_all, w_up=wu_all, w_down=wd_all, K=K, store=store,
                 logits=logits, topk=topk, gates=gates, counts=counts, offsets=offsets,
                 sorted_flat=sorted_flat, inv=inv, tiles=tiles, xs=xs, G=G, U=U, A=A, ys=ys, y=y,
-                capacity=capacity)
+                capacity=capacity, shared=sh)
 
 
 def backward(fwd: dict, dy, aux_scale: Optional[float] = None) -> dict:
@@ -420,12 +435,27 @@ def backward(fwd: dict, dy, aux_scale: Optional[float] = None) -> dict:
         dlogits = dlogits + aux_loss_grad(fwd["logits"], fwd["counts"], K, aux_scale)
     dlogits = rho32(dlogits, store)
 
-    # gather backward (sum over each token's kept rows) + router input gradient
+    # shared expert backward: its upstream gradient is dy itself
+    out_sh = {}
+    sh = fwd.get("shared")
+    if sh is not None:
+        dA = dy @ sh["w_down"].T
+        sg = sigmoid(sh["G"])
+        dGs = rho(dA * sh["U"] * sg * (1.0 + sh["G"] * (1.0 - sg)), store)
+        dUs = rho(dA * (sh["G"] * sg), store)
+        dxs_s = rho(dGs @ sh["w_gate"].T + dUs @ sh["w_up"].T, store)
+        out_sh = dict(dG_s=dGs, dU_s=dUs, dxs_s=dxs_s, dw_gate_s=x.T @ dGs, dw_up_s=x.T @ dUs,
+                      dw_down_s=sh["A"].T @ dy)
+
+    # gather backward (sum over each token's kept rows) + router input
+    # gradient (+ the shared expert's input gradient)
     dx = (dxs[np.maximum(inv, 0).reshape(N, K)] * kept_slot[:, :, None]).sum(axis=1) + dlogits @ w_r.T
+    if sh is not None:
+        dx = dx + out_sh["dxs_s"]
     dx = rho(dx, store)
     dw_r = x.T @ dlogits
     return dict(dys=dys, dgates=dgates, dG=dG, dU=dU, dxs=dxs, dlogits=dlogits, dx=dx, dw_r=dw_r,
-                dw_gate=dw_gate, dw_up=dw_up, dw_down=dw_down)
+                dw_gate=dw_gate, dw_up=dw_up, dw_down=dw_down, **out_sh)
 
 
 # --------------------------------------------------------------------------
@@ -582,6 +612,18 @@ def rounding_bands(fwd: dict, bwd: Optional[dict] = None, dy=None, aux_scale: Op
         b["ys"][sl] = bf16_flip(A[sl] @ wd, ys[sl], gemm_sigma(A[sl], wd) + prop(b["A"][sl], wd))
     yp = np.zeros((N, H))
     sy = np.zeros((N, H))
+    sh = fwd.get("shared")
+    if sh is not None:
+        # shared expert: one more expert over all tokens (rows = x), weight 1
+        Gs, Us, As, yss = sh["G"], sh["U"], sh["A"], sh["ys"]
+        b["G_s"] = bf16_flip(x @ sh["w_gate"], Gs, gemm_sigma(x, sh["w_gate"]))
+        b["U_s"] = bf16_flip(x @ sh["w_up"], Us, gemm_sigma(x, sh["w_up"]))
+        ap = silu(Gs) * Us
+        sa = np.abs(Us * _silu_d1(Gs)) * b["G_s"] + np.abs(silu(Gs)) * b["U_s"] + 16 * U32 * np.abs(ap)
+        b["A_s"] = bf16_flip(ap, As, sa)
+        b["ys_s"] = bf16_flip(As @ sh["w_down"], yss, gemm_sigma(As, sh["w_down"]) + prop(b["A_s"], sh["w_down"]))
+        yp += yss
+        sy += b["ys_s"] + 8 * U32 * np.abs(yss)
     for k in range(K):
         r = inv2[:, k]
         g = fwd["gates"][:, k:k + 1] * kept2[:, k:k + 1]
@@ -657,6 +699,27 @@ def rounding_bands(fwd: dict, bwd: Optional[dict] = None, dy=None, aux_scale: Op
     dxp = dxs_tok.sum(axis=1) + bwd["dlogits"] @ w_r.T
     sdx = ((b["dxs"][inv2] * kept2[:, :, None]).sum(axis=1) + prop(b["dlogits"], w_r.T)
            + 8 * U32 * (np.abs(dxs_tok).sum(axis=1) + np.abs(bwd["dlogits"]) @ np.abs(w_r.T)))
+    if sh is not None:
+        # shared expert backward (its dys is dy itself, exact)
+        Gs, Us, As = sh["G"], sh["U"], sh["A"]
+        dA = dy @ sh["w_down"].T
+        sdA = gemm_sigma(dy, sh["w_down"].T)
+        d1, d2 = _silu_d1(Gs), _silu_d2(Gs)
+        dgp = dA * Us * d1
+        b["dG_s"] = bf16_flip(dgp, bwd["dG_s"], np.abs(Us * d1) * sdA + np.abs(dA * d1) * b["U_s"]
+                              + np.abs(dA * Us * d2) * b["G_s"] + 16 * U32 * np.abs(dgp))
+        dup = dA * silu(Gs)
+        b["dU_s"] = bf16_flip(dup, bwd["dU_s"], np.abs(silu(Gs)) * sdA + np.abs(dA * d1) * b["G_s"]
+                              + 16 * U32 * np.abs(dup))
+        dGs, dUs = bwd["dG_s"], bwd["dU_s"]
+        dxsp = dGs @ sh["w_gate"].T + dUs @ sh["w_up"].T
+        b["dxs_s"] = bf16_flip(dxsp, bwd["dxs_s"], gemm_sigma(dGs, sh["w_gate"].T) + gemm_sigma(dUs, sh["w_up"].T)
+                               + prop(b["dG_s"], sh["w_gate"].T) + prop(b["dU_s"], sh["w_up"].T))
+        b["dw_gate_s"] = prop(b["dG_s"].T, x).T + gemm_sigma(x.T, dGs) + 2 * U32 * np.abs(bwd["dw_gate_s"])
+        b["dw_up_s"] = prop(b["dU_s"].T, x).T + gemm_sigma(x.T, dUs) + 2 * U32 * np.abs(bwd["dw_up_s"])
+        b["dw_down_s"] = (prop(b["A_s"].T, dy) + gemm_sigma(As.T, dy) + 2 * U32 * np.abs(bwd["dw_down_s"]))
+        dxp = dxp + bwd["dxs_s"]
+        sdx = sdx + b["dxs_s"] + 8 * U32 * np.abs(bwd["dxs_s"])
     b["dx"] = bf16_flip(dxp, bwd["dx"], sdx)
     return b
 
