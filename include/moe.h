@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 /* Rows per tile of the grouped-GEMM tile list built by moe_permute_meta. */
 #define MOE_TILE_M 256
 #define MOE_MAX_EXPERTS 256
@@ -75,7 +75,9 @@ typedef enum moe_entry {
   MOE_ENTRY_ROUTE_BWD = 2,
   MOE_ENTRY_PERMUTE_BWD = 3, /* also moe_permute_bwd_dense */
   MOE_ENTRY_AUX_LOSS = 4,
-  MOE_ENTRY_ROUTE_BWD_AUX = 5
+  MOE_ENTRY_ROUTE_BWD_AUX = 5,
+  MOE_ENTRY_SHARED_FFN = 6,    /* shared-expert dims only (E = K = 1) */
+  MOE_ENTRY_SHARED_FFN_BWD = 7 /* shared-expert dims only (E = K = 1) */
 } moe_entry;
 
 /* Problem sizes: N tokens, hidden size H, expert FFN size F, E experts,
@@ -291,6 +293,60 @@ int moe_route_bwd_aux(const moe_dims* d, const void* x, const int32_t* topk_idx,
 int moe_permute_bwd_dense(const moe_dims* d, const void* dxs, const int32_t* inv, const int32_t* topk_idx,
                           const float* dlogits, const void* w_r, void* dx, void* ws, size_t ws_bytes,
                           hipStream_t stream);
+
+/* ------------------------------------------------------- shared expert */
+/* A shared expert ("MegaBlocks - architecture and principles",
+ * ai-reference-codex, section 2.1: the layer's output plus an optional
+ * shared-expert MLP that every token passes through): one dense SwiGLU
+ * expert of intermediate size Fs over all N tokens, weight 1,
+ *     y[n] = sum_k g_n,k FFN_{e_n,k}(x_n) + FFN_s(x_n).
+ * Its calls take the shared expert's own dims ds = {N, H, Fs, E = 1, K = 1,
+ * dtype} (any other E or K: MOE_EINVAL; moe_workspace_bytes returns
+ * (size_t)-1).  Its weights: w_gate, w_up [H,Fs]; w_down [Fs,H]; its rows
+ * are x itself, in token order. */
+
+/* Forward of the shared expert:
+ *   G = x.W_gate_s, U = x.W_up_s, A = silu(G)*U, ys_shared = A.W_down_s
+ *   (each stored rounded, float32 accumulation).
+ *   x [N,H]; g_save, u_save [N,Fs] out or both NULL (forward only);
+ *   act [N,Fs] out; ys_shared [N,H] out.  ws: MOE_ENTRY_SHARED_FFN (its tile
+ *   list, rebuilt on every call). */
+int moe_shared_ffn(const moe_dims* ds, const void* x, const void* w_gate, const void* w_up, const void* w_down,
+                   void* g_save, void* u_save, void* act, void* ys_shared, void* ws, size_t ws_bytes,
+                   hipStream_t stream);
+
+/* moe_combine with the shared expert's output added after the K routed
+ * terms: y[n] = sum_k gates[n,k]*ys[inv[n*K+k]] + ys_shared[n], float32,
+ * one rounding.  d: the layer's dims; ys_shared [N,H] act. */
+int moe_combine_shared(const moe_dims* d, const void* ys, const float* gates, const int32_t* inv,
+                       const void* ys_shared, void* y, hipStream_t stream);
+
+/* Backward of the shared expert (its upstream gradient is dy itself):
+ *   dA = dy.W_down_s^T; s = sigmoid(G);
+ *   dG = dA*U*s*(1 + G*(1-s)), dU = dA*G*s (stored rounded);
+ *   dx_shared = dG.W_gate_s^T + dU.W_up_s^T (stored rounded);
+ *   dW_gate_s = x^T.dG, dW_up_s = x^T.dU, dW_down_s = A^T.dy (float32).
+ * The weight gradients contract over all N tokens: the tokens are cut into
+ * fixed row chunks whose float32 partial products are summed in chunk
+ * order, so results are bitwise reproducible for a given N, H, Fs.
+ *   dy [N,H]; g_save, u_save, act [N,Fs] from moe_shared_ffn; dg, du [N,Fs]
+ *   out; dx_shared [N,H] out (add it with moe_permute_bwd_add);
+ *   dw_gate, dw_up [H,Fs] f32 out; dw_down [Fs,H] f32 out.
+ *   ws: MOE_ENTRY_SHARED_FFN_BWD (tile list, chunk bounds and, when the
+ *   contraction is split, 3*S*H*Fs float32 partials). */
+int moe_shared_ffn_bwd(const moe_dims* ds, const void* x, const void* dy, const void* w_gate, const void* w_up,
+                       const void* w_down, const void* g_save, const void* u_save, const void* act, void* dg, void* du,
+                       void* dx_shared, float* dw_gate, float* dw_up, float* dw_down, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/* moe_permute_bwd (dense = 0) or moe_permute_bwd_dense (dense = 1; other
+ * values MOE_EINVAL) with one more row added last:
+ *   dx[n] = sum_k dxs[inv[n*K+k]] + (router term) + dx_add[n],
+ *   float32, one rounding.  dx_add [N,H] act (the shared expert's
+ *   dx_shared).  d: the layer's dims.  ws: MOE_ENTRY_PERMUTE_BWD. */
+int moe_permute_bwd_add(const moe_dims* d, const void* dxs, const int32_t* inv, const int32_t* topk_idx,
+                        const float* dlogits, const void* w_r, int32_t dense, const void* dx_add, void* dx, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

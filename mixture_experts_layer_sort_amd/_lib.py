@@ -21,6 +21,7 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, 
 MOE_F32, MOE_BF16 = 0, 1
 MOE_ENTRY_PERMUTE_META, MOE_ENTRY_ROUTE_BWD, MOE_ENTRY_PERMUTE_BWD = 1, 2, 3
 MOE_ENTRY_AUX_LOSS, MOE_ENTRY_ROUTE_BWD_AUX = 4, 5
+MOE_ENTRY_SHARED_FFN, MOE_ENTRY_SHARED_FFN_BWD = 6, 7
 MOE_TILE_M = 256
 
 # Every exported symbol with (restype, argtypes); the tests check this list
@@ -62,6 +63,10 @@ SIGNATURES = {
     "moe_permute_bwd_dense": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_aux_loss": (ctypes.c_int, [_DP, _P, _P, _P, _P, _F, _P, _P, _P, _SZ, _P]),
     "moe_route_bwd_aux": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P, _F, _P, _P, _P, _SZ, _P]),
+    "moe_shared_ffn": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_combine_shared": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P]),
+    "moe_shared_ffn_bwd": (ctypes.c_int, [_DP] + [_P] * 15 + [_SZ, _P]),
+    "moe_permute_bwd_add": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
 }
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -242,3 +247,29 @@ def moe_route_bwd_aux(d, x, topk_idx, gates, dgates, probs, counts, aux_scale, d
     _call("moe_route_bwd_aux", ctypes.byref(d), _ptr(x), _ptr(topk_idx), _ptr(gates), _ptr(dgates), _ptr(probs),
           _ptr(counts), float(aux_scale), _ptr(dlogits), _ptr(dw_r), _ptr(ws),
           0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+
+
+def _nbytes(ws) -> int:
+    return 0 if ws is None else ws.numel() * ws.element_size()
+
+
+def moe_shared_ffn(ds, x, w_gate, w_up, w_down, g_save, u_save, act, ys_shared, ws, stream=None):
+    _call("moe_shared_ffn", ctypes.byref(ds), _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(g_save),
+          _ptr(u_save), _ptr(act), _ptr(ys_shared), _ptr(ws), _nbytes(ws), _stream(stream))
+
+
+def moe_combine_shared(d, ys, gates, inv, ys_shared, y, stream=None):
+    _call("moe_combine_shared", ctypes.byref(d), _ptr(ys), _ptr(gates), _ptr(inv), _ptr(ys_shared), _ptr(y),
+          _stream(stream))
+
+
+def moe_shared_ffn_bwd(ds, x, dy, w_gate, w_up, w_down, g_save, u_save, act, dg, du, dx_shared, dw_gate, dw_up,
+                       dw_down, ws, stream=None):
+    _call("moe_shared_ffn_bwd", ctypes.byref(ds), _ptr(x), _ptr(dy), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+          _ptr(g_save), _ptr(u_save), _ptr(act), _ptr(dg), _ptr(du), _ptr(dx_shared), _ptr(dw_gate), _ptr(dw_up),
+          _ptr(dw_down), _ptr(ws), _nbytes(ws), _stream(stream))
+
+
+def moe_permute_bwd_add(d, dxs, inv, topk_idx, dlogits, w_r, dense, dx_add, dx, ws, stream=None):
+    _call("moe_permute_bwd_add", ctypes.byref(d), _ptr(dxs), _ptr(inv), _ptr(topk_idx), _ptr(dlogits), _ptr(w_r),
+          int(dense), _ptr(dx_add), _ptr(dx), _ptr(ws), _nbytes(ws), _stream(stream))

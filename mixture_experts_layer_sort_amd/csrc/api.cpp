@@ -48,6 +48,9 @@ bool ptrs_ok(P... p) {
 
 int from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
+// The shared expert's dims: one expert, every token routed to it once.
+bool is_shared(const Dims& D) { return D.E == 1 && D.K == 1; }
+
 #define MOE_CHECK_DIMS(d, D)            \
   Dims D;                               \
   {                                     \
@@ -87,6 +90,8 @@ size_t moe_workspace_bytes(const moe_dims* d, int32_t entry) {
     case MOE_ENTRY_PERMUTE_BWD: return moe_launch::permute_bwd_ws(D);
     case MOE_ENTRY_AUX_LOSS: return moe_launch::aux_loss_ws(D);
     case MOE_ENTRY_ROUTE_BWD_AUX: return moe_launch::route_bwd_aux_ws(D);
+    case MOE_ENTRY_SHARED_FFN: return is_shared(D) ? moe_launch::shared_ffn_ws(D) : size_t(-1);
+    case MOE_ENTRY_SHARED_FFN_BWD: return is_shared(D) ? moe_launch::shared_ffn_bwd_ws(D) : size_t(-1);
     default: return size_t(-1);
   }
 }
@@ -176,7 +181,7 @@ int moe_combine(const moe_dims* d, const void* ys, const float* gates, const int
   MOE_CHECK_DIMS(d, D);
   if (!ptrs_ok(ys, gates, inv, y)) return MOE_EINVAL;
   if (D.N == 0) return MOE_OK;
-  return from_hip(moe_launch::combine(D, ys, gates, inv, y, stream));
+  return from_hip(moe_launch::combine(D, ys, gates, inv, nullptr, y, stream));
 }
 
 int moe_combine_bwd(const moe_dims* d, const void* dy, const void* ys, const float* gates, const int32_t* inv,
@@ -245,7 +250,7 @@ int moe_permute_bwd(const moe_dims* d, const void* dxs, const int32_t* inv, cons
   if (D.N == 0) return MOE_OK;
   const size_t need = moe_launch::permute_bwd_ws(D);
   if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return MOE_EWORKSPACE;
-  return from_hip(moe_launch::permute_bwd(D, dxs, inv, topk_idx, dlogits, w_r, dx, ws, stream, false));
+  return from_hip(moe_launch::permute_bwd(D, dxs, inv, topk_idx, dlogits, w_r, nullptr, dx, ws, stream, false));
 }
 
 int moe_permute_bwd_dense(const moe_dims* d, const void* dxs, const int32_t* inv, const int32_t* topk_idx,
@@ -256,7 +261,55 @@ int moe_permute_bwd_dense(const moe_dims* d, const void* dxs, const int32_t* inv
   if (D.N == 0) return MOE_OK;
   const size_t need = moe_launch::permute_bwd_ws(D);
   if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return MOE_EWORKSPACE;
-  return from_hip(moe_launch::permute_bwd(D, dxs, inv, topk_idx, dlogits, w_r, dx, ws, stream, true));
+  return from_hip(moe_launch::permute_bwd(D, dxs, inv, topk_idx, dlogits, w_r, nullptr, dx, ws, stream, true));
+}
+
+int moe_combine_shared(const moe_dims* d, const void* ys, const float* gates, const int32_t* inv,
+                       const void* ys_shared, void* y, hipStream_t stream) {
+  MOE_CHECK_DIMS(d, D);
+  if (!ptrs_ok(ys, gates, inv, ys_shared, y)) return MOE_EINVAL;
+  if (D.N == 0) return MOE_OK;
+  return from_hip(moe_launch::combine(D, ys, gates, inv, ys_shared, y, stream));
+}
+
+int moe_permute_bwd_add(const moe_dims* d, const void* dxs, const int32_t* inv, const int32_t* topk_idx,
+                        const float* dlogits, const void* w_r, int32_t dense, const void* dx_add, void* dx, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+  MOE_CHECK_DIMS(d, D);
+  if (!ptrs_ok(dxs, inv, topk_idx, dlogits, w_r, dx_add, dx)) return MOE_EINVAL;
+  if (dense != 0 && dense != 1) return MOE_EINVAL;
+  if (D.N == 0) return MOE_OK;
+  const size_t need = moe_launch::permute_bwd_ws(D);
+  if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return MOE_EWORKSPACE;
+  return from_hip(moe_launch::permute_bwd(D, dxs, inv, topk_idx, dlogits, w_r, dx_add, dx, ws, stream, dense == 1));
+}
+
+int moe_shared_ffn(const moe_dims* ds, const void* x, const void* w_gate, const void* w_up, const void* w_down,
+                   void* g_save, void* u_save, void* act, void* ys, void* ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_CHECK_DIMS(ds, D);
+  if (!is_shared(D)) return MOE_EINVAL;
+  if (!ptrs_ok(x, w_gate, w_up, w_down, act, ys)) return MOE_EINVAL;
+  if ((g_save == nullptr) != (u_save == nullptr)) return MOE_EINVAL;
+  if (g_save != nullptr && !ptrs_ok(g_save, u_save)) return MOE_EINVAL;
+  if (D.N == 0) return MOE_OK;
+  const size_t need = moe_launch::shared_ffn_ws(D);
+  if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return MOE_EWORKSPACE;
+  return from_hip(moe_launch::shared_ffn(D, x, w_gate, w_up, w_down, g_save, u_save, act, ys, ws, stream));
+}
+
+int moe_shared_ffn_bwd(const moe_dims* ds, const void* x, const void* dy, const void* w_gate, const void* w_up,
+                       const void* w_down, const void* g_save, const void* u_save, const void* act, void* dg, void* du,
+                       void* dx_shared, float* dw_gate, float* dw_up, float* dw_down, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  MOE_CHECK_DIMS(ds, D);
+  if (!is_shared(D)) return MOE_EINVAL;
+  if (!ptrs_ok(x, dy, w_gate, w_up, w_down, g_save, u_save, act, dg, du, dx_shared, dw_gate, dw_up, dw_down))
+    return MOE_EINVAL;
+  if (D.N == 0) return MOE_OK;
+  const size_t need = moe_launch::shared_ffn_bwd_ws(D);
+  if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return MOE_EWORKSPACE;
+  return from_hip(moe_launch::shared_ffn_bwd(D, x, dy, w_gate, w_up, w_down, g_save, u_save, act, dg, du, dx_shared,
+                                             dw_gate, dw_up, dw_down, ws, stream));
 }
 
 int moe_aux_loss(const moe_dims* d, const void* x, const void* w_r, const float* logit_bias, const int32_t* counts,

@@ -150,7 +150,10 @@ hipError_t permute_meta(const Dims& d, const int32_t* topk, int32_t capacity, in
                         hipStream_t s);
 size_t permute_meta_ws(const Dims& d);
 hipError_t permute(const Dims& d, const void* x, const int32_t* sorted_flat, void* xs, hipStream_t s);
-hipError_t combine(const Dims& d, const void* ys, const float* gates, const int32_t* inv, void* y, hipStream_t s);
+// add (optional, [N,H], may be null): a row added with weight 1 to each
+// token's result (the shared expert's output / input gradient).
+hipError_t combine(const Dims& d, const void* ys, const float* gates, const int32_t* inv, const void* add, void* y,
+                   hipStream_t s);
 hipError_t combine_bwd(const Dims& d, const void* dy, const void* ys, const float* gates, const int32_t* inv,
                        void* dys, float* dgates, hipStream_t s);
 hipError_t route_bwd(const Dims& d, const void* x, const int32_t* topk, const float* gates, const float* dgates,
@@ -164,7 +167,7 @@ hipError_t route_bwd_aux(const Dims& d, const void* x, const int32_t* topk, cons
                          const float* probs, const int32_t* counts, float aux_scale, float* dlogits, float* dw_r,
                          void* ws, hipStream_t s);
 hipError_t permute_bwd(const Dims& d, const void* dxs, const int32_t* inv, const int32_t* topk, const float* dlogits,
-                       const void* w_r, void* dx, void* ws, hipStream_t s, bool dense);
+                       const void* w_r, const void* add, void* dx, void* ws, hipStream_t s, bool dense);
 size_t permute_bwd_ws(const Dims& d);
 
 // sorted_flat non-null: xs is the token matrix x and the rows are gathered
@@ -179,4 +182,15 @@ hipError_t ffn_bwd_dx(const Dims& d, const void* dg, const void* du, const void*
                       const int32_t* tiles, const int32_t* num_tiles, void* dxs, hipStream_t s);
 hipError_t ffn_bwd_dw(const Dims& d, const void* xs, const void* a, const void* dys, const void* dg, const void* du,
                       const int32_t* offsets, float* dwg, float* dwu, float* dwd, hipStream_t s);
+
+// Shared expert: a dense SwiGLU expert over all N tokens (dims E = K = 1,
+// F = its intermediate size).  The workspace holds its tile list, the row
+// chunks of its split weight gradient and their float32 partial sums.
+size_t shared_ffn_ws(const Dims& ds);
+size_t shared_ffn_bwd_ws(const Dims& ds);
+hipError_t shared_ffn(const Dims& ds, const void* x, const void* wg, const void* wu, const void* wd, void* g, void* u,
+                      void* a, void* ys, void* ws, hipStream_t s);
+hipError_t shared_ffn_bwd(const Dims& ds, const void* x, const void* dy, const void* wg, const void* wu,
+                          const void* wd, const void* g, const void* u, const void* a, void* dg, void* du, void* dxs,
+                          float* dwg, float* dwu, float* dwd, void* ws, hipStream_t s);
 }  // namespace moe_launch

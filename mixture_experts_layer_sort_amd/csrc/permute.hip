@@ -32,11 +32,12 @@ __global__ __launch_bounds__(256) void k_permute(const T* __restrict__ x, const 
 }
 
 // y[n] = sum_k gates[n,k] * ys[inv[n*K+k]], k ascending, float32 accumulation;
-// dropped slots (inv < 0) add nothing.
+// dropped slots (inv < 0) add nothing.  add (optional, [N,H]): a row added
+// with weight 1 after the K terms (the shared expert's output).
 template <typename T>
 __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ ys, const float* __restrict__ gates,
-                                                 const int32_t* __restrict__ inv, T* __restrict__ y,
-                                                 int64_t total_vec, int vpr, int K) {
+                                                 const int32_t* __restrict__ inv, const T* __restrict__ add,
+                                                 T* __restrict__ y, int64_t total_vec, int vpr, int K) {
   constexpr int V = Vec16<T>::n;
   const int64_t stride = (int64_t)gridDim.x * 256;
   for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < total_vec; v += stride) {
@@ -53,6 +54,12 @@ __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ ys, const
       Vec16<T>::load(ys + (r * vpr + c) * V, val);
 #pragma unroll
       for (int i = 0; i < V; ++i) acc[i] = fmaf(g, val[i], acc[i]);
+    }
+    if (add != nullptr) {
+      float val[V];
+      Vec16<T>::load(add + v * V, val);
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] += val[i];
     }
     Vec16<T>::store(y + v * V, acc);
   }
@@ -138,8 +145,8 @@ __global__ __launch_bounds__(256) void k_transpose_wr(const T* __restrict__ w_r,
 template <typename T, bool DENSE>
 __global__ __launch_bounds__(256) void k_permute_bwd(const T* __restrict__ dxs, const int32_t* __restrict__ inv,
                                                      const int32_t* __restrict__ topk, const float* __restrict__ dl,
-                                                     const T* __restrict__ w_rt, T* __restrict__ dx, int N, int vpr,
-                                                     int K, int E) {
+                                                     const T* __restrict__ w_rt, const T* __restrict__ add,
+                                                     T* __restrict__ dx, int N, int vpr, int K, int E) {
   constexpr int V = Vec16<T>::n;
   const int lane = lane_id();
   const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -200,6 +207,12 @@ __global__ __launch_bounds__(256) void k_permute_bwd(const T* __restrict__ dxs, 
           for (int i = 0; i < V; ++i) acc[i] = fmaf(d[k], wv[i], acc[i]);
         }
     }
+    if (add != nullptr) {
+      float val[V];
+      Vec16<T>::load(add + (n * vpr + c) * V, val);
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] += val[i];
+    }
     Vec16<T>::store(dst + c * V, acc);
   }
 }
@@ -214,7 +227,8 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_permute_bwd_dense_tiled(const T* __restrict__ dxs,
                                                                  const int32_t* __restrict__ inv,
                                                                  const float* __restrict__ dl,
-                                                                 const T* __restrict__ w_rt, T* __restrict__ dx,
+                                                                 const T* __restrict__ w_rt,
+                                                                 const T* __restrict__ add, T* __restrict__ dx,
                                                                  int N, int vpr, int K, int E) {
   constexpr int V = Vec16<T>::n;
   __shared__ float sdl[4][kTokTile * MOE_MAX_EXPERTS];
@@ -281,7 +295,15 @@ __global__ __launch_bounds__(256) void k_permute_bwd_dense_tiled(const T* __rest
     }
 #pragma unroll
     for (int t = 0; t < kTokTile; ++t)
-      if (t < nt) Vec16<T>::store(dx + ((n0 + t) * vpr + c) * V, acc[t]);
+      if (t < nt) {
+        if (add != nullptr) {
+          float val[V];
+          Vec16<T>::load(add + ((n0 + t) * vpr + c) * V, val);
+#pragma unroll
+          for (int i = 0; i < V; ++i) acc[t][i] += val[i];
+        }
+        Vec16<T>::store(dx + ((n0 + t) * vpr + c) * V, acc[t]);
+      }
   }
 }
 
@@ -320,19 +342,19 @@ hipError_t permute(const Dims& d, const void* x, const int32_t* sorted_flat, voi
   return hipGetLastError();
 }
 
-hipError_t combine(const Dims& d, const void* ys, const float* gates, const int32_t* inv, void* y, hipStream_t s) {
-  if (d.dtype == MOE_BF16) {
-    int vpr = vpr_of<moe::bf16_t>(d);
-    int64_t tot = d.N * vpr;
-    hipLaunchKernelGGL(k_combine<moe::bf16_t>, dim3(grid_for(tot)), dim3(256), 0, s,
-                       static_cast<const moe::bf16_t*>(ys), gates, inv, static_cast<moe::bf16_t*>(y), tot, vpr,
-                       int(d.K));
-  } else {
-    int vpr = vpr_of<float>(d);
-    int64_t tot = d.N * vpr;
-    hipLaunchKernelGGL(k_combine<float>, dim3(grid_for(tot)), dim3(256), 0, s, static_cast<const float*>(ys), gates,
-                       inv, static_cast<float*>(y), tot, vpr, int(d.K));
-  }
+hipError_t combine(const Dims& d, const void* ys, const float* gates, const int32_t* inv, const void* add, void* y,
+                   hipStream_t s) {
+  auto run = [&](auto tag) {
+    using T = decltype(tag);
+    const int vpr = vpr_of<T>(d);
+    const int64_t tot = d.N * vpr;
+    hipLaunchKernelGGL(k_combine<T>, dim3(grid_for(tot)), dim3(256), 0, s, static_cast<const T*>(ys), gates, inv,
+                       static_cast<const T*>(add), static_cast<T*>(y), tot, vpr, int(d.K));
+  };
+  if (d.dtype == MOE_BF16)
+    run(moe::bf16_t{});
+  else
+    run(float{});
   return hipGetLastError();
 }
 
@@ -355,7 +377,7 @@ size_t permute_bwd_ws(const Dims& d) {
 }
 
 hipError_t permute_bwd(const Dims& d, const void* dxs, const int32_t* inv, const int32_t* topk, const float* dlogits,
-                       const void* w_r, void* dx, void* ws, hipStream_t s, bool dense) {
+                       const void* w_r, const void* add, void* dx, void* ws, hipStream_t s, bool dense) {
   int64_t nw = d.H * d.E;
   unsigned tg = unsigned((nw + 255) / 256);
   auto run = [&](auto tag) -> hipError_t {
@@ -366,16 +388,16 @@ hipError_t permute_bwd(const Dims& d, const void* dxs, const int32_t* inv, const
     if (err != hipSuccess) return err;
     if (dense && d.E > 8)
       hipLaunchKernelGGL((k_permute_bwd_dense_tiled<T>), dim3(waves4((d.N + kTokTile - 1) / kTokTile)), dim3(256), 0,
-                         s, static_cast<const T*>(dxs), inv, dlogits, static_cast<const T*>(ws), static_cast<T*>(dx),
-                         int(d.N), vpr_of<T>(d), int(d.K), int(d.E));
+                         s, static_cast<const T*>(dxs), inv, dlogits, static_cast<const T*>(ws), static_cast<const T*>(add),
+                         static_cast<T*>(dx), int(d.N), vpr_of<T>(d), int(d.K), int(d.E));
     else if (dense)
       hipLaunchKernelGGL((k_permute_bwd<T, true>), dim3(waves4(d.N)), dim3(256), 0, s, static_cast<const T*>(dxs), inv,
-                         topk, dlogits, static_cast<const T*>(ws), static_cast<T*>(dx), int(d.N), vpr_of<T>(d),
-                         int(d.K), int(d.E));
+                         topk, dlogits, static_cast<const T*>(ws), static_cast<const T*>(add), static_cast<T*>(dx),
+                         int(d.N), vpr_of<T>(d), int(d.K), int(d.E));
     else
       hipLaunchKernelGGL((k_permute_bwd<T, false>), dim3(waves4(d.N)), dim3(256), 0, s, static_cast<const T*>(dxs),
-                         inv, topk, dlogits, static_cast<const T*>(ws), static_cast<T*>(dx), int(d.N), vpr_of<T>(d),
-                         int(d.K), int(d.E));
+                         inv, topk, dlogits, static_cast<const T*>(ws), static_cast<const T*>(add), static_cast<T*>(dx),
+                         int(d.N), vpr_of<T>(d), int(d.K), int(d.E));
     return hipGetLastError();
   };
   if (d.dtype == MOE_BF16) return run(moe::bf16_t{});

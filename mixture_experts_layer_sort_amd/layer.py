@@ -10,6 +10,10 @@ layer through the C ABI:
   backward: moe_combine_bwd -> moe_route_bwd -> moe_expert_ffn_bwd
             (moe_ffn_bwd_dact, moe_ffn_bwd_dx, moe_ffn_bwd_dw) -> moe_permute_bwd
 
+With a shared expert, moe_shared_ffn runs beside the routed path and
+moe_combine_shared adds its output; in the backward moe_shared_ffn_bwd gives
+its gradients and moe_permute_bwd_add adds its input gradient to dx.
+
 Nothing is read back to the host between the calls.  ``MoEFunction`` wraps
 one runner call pair as a ``torch.autograd.Function``.
 """
@@ -27,10 +31,12 @@ class MoELayerRunner:
 
     def __init__(self, N: int, H: int, F: int, E: int, K: int, dtype: torch.dtype, device="cuda",
                  backward: bool = True, save_gu: Optional[bool] = None, aux_alpha: Optional[float] = None,
-                 capacity: Optional[int] = None):
+                 capacity: Optional[int] = None, shared_ffn: Optional[int] = None):
         """aux_alpha: weight of the Switch load-balancing loss; None turns it off.
         capacity: expert capacity (rows per expert, the overflow dropped);
-        None is the dropless layer."""
+        None is the dropless layer.  shared_ffn: intermediate size Fs of a
+        shared expert every token passes through (weights passed to forward
+        as ``shared``); None: no shared expert."""
         self.N, self.H, self.F, self.E, self.K = N, H, F, E, K
         self.dtype = dtype
         self.device = torch.device(device)
@@ -84,10 +90,29 @@ class MoELayerRunner:
             self.dx = torch.empty((N, H), dtype=dtype, device=dev)
             self.route_ws = self._ws(L.MOE_ENTRY_ROUTE_BWD if aux_alpha is None else L.MOE_ENTRY_ROUTE_BWD_AUX)
             self.perm_ws = self._ws(L.MOE_ENTRY_PERMUTE_BWD)
+        self.shared_ffn = shared_ffn
+        if shared_ffn is not None:
+            Fs = shared_ffn
+            self.ds = L.dims(N, H, Fs, 1, 1, L.dtype_code(dtype))
+            self.g_s = torch.empty((N, Fs), dtype=dtype, device=dev) if save_gu else None
+            self.u_s = torch.empty((N, Fs), dtype=dtype, device=dev) if save_gu else None
+            self.act_s = torch.empty((N, Fs), dtype=dtype, device=dev)
+            self.ys_s = torch.empty((N, H), dtype=dtype, device=dev)
+            # the backward layout starts with the forward one
+            self.shared_ws = self._ws(L.MOE_ENTRY_SHARED_FFN_BWD if backward else L.MOE_ENTRY_SHARED_FFN, self.ds)
+            if backward:
+                f32 = torch.float32
+                self.dg_s = torch.empty((N, Fs), dtype=dtype, device=dev)
+                self.du_s = torch.empty((N, Fs), dtype=dtype, device=dev)
+                self.dx_s = torch.empty((N, H), dtype=dtype, device=dev)
+                self.dw_gate_s = torch.empty((H, Fs), dtype=f32, device=dev)
+                self.dw_up_s = torch.empty((H, Fs), dtype=f32, device=dev)
+                self.dw_down_s = torch.empty((Fs, H), dtype=f32, device=dev)
         self.inputs = None
+        self.shared_w = None
 
-    def _ws(self, entry: int):
-        n = L.moe_workspace_bytes(self.d, entry)
+    def _ws(self, entry: int, d=None):
+        n = L.moe_workspace_bytes(self.d if d is None else d, entry)
         if n == 2 ** 64 - 1:
             raise L.MoEError("moe_workspace_bytes", L.MOE_EINVAL)
         return torch.empty((max(16, n),), dtype=torch.uint8, device=self.device)
@@ -105,9 +130,29 @@ class MoELayerRunner:
             L.moe_permute_meta_capacity(self.d, tk, self.capacity, self.sorted_flat, self.inv, self.counts,
                                         self.offsets, self.tiles, self.num_tiles, self.meta_ws, stream)
 
-    def forward(self, x, w_r, w_gate, w_up, w_down, bias=None, topk=None, gates=None, stream=None):
+    def forward(self, x, w_r, w_gate, w_up, w_down, bias=None, topk=None, gates=None, stream=None, shared=None,
+                side_stream=None):
         """Run the forward; returns y.  ``topk``/``gates`` (optional) replace the
-        router's own assignment (moe_route is then skipped)."""
+        router's own assignment (moe_route is then skipped).  ``shared`` =
+        (W_gate_s [H,Fs], W_up_s [H,Fs], W_down_s [Fs,H]) when the runner has a
+        shared expert; with ``side_stream`` it runs there, beside the routed
+        path, and the combine waits for it."""
+        if (shared is None) != (self.shared_ffn is None):
+            raise ValueError("shared weights must be given exactly when the runner has a shared expert")
+        main = torch.cuda.current_stream(self.device) if stream is None else stream
+        shared_done = None
+        if shared is not None:
+            side = main if side_stream is None else side_stream
+            if side is not main:
+                ev = torch.cuda.Event()
+                ev.record(main)
+                side.wait_event(ev)
+            L.moe_shared_ffn(self.ds, x, shared[0], shared[1], shared[2], self.g_s, self.u_s, self.act_s, self.ys_s,
+                             self.shared_ws, side)
+            if side is not main:
+                shared_done = torch.cuda.Event()
+                shared_done.record(side)
+        stream = main
         if topk is None:
             self.route(x, w_r, bias, stream)
         else:
@@ -122,11 +167,17 @@ class MoELayerRunner:
             L.moe_ffn_gate_up(self.d, self.xs, w_gate, w_up, self.tiles, self.num_tiles, self.g, self.u, self.act,
                               stream)
         L.moe_ffn_down(self.d, self.act, w_down, self.tiles, self.num_tiles, self.ys, stream)
-        L.moe_combine(self.d, self.ys, self.gates, self.inv, self.y, stream)
+        if shared is None:
+            L.moe_combine(self.d, self.ys, self.gates, self.inv, self.y, stream)
+        else:
+            if shared_done is not None:
+                stream.wait_event(shared_done)
+            L.moe_combine_shared(self.d, self.ys, self.gates, self.inv, self.ys_s, self.y, stream)
         if self.aux_alpha is not None:
             L.moe_aux_loss(self.d, x, w_r, bias, self.counts, self.aux_alpha, self.probs, self.aux_loss, self.aux_ws,
                            stream)
         self.inputs = (x, w_r, w_gate, w_up, w_down)
+        self.shared_w = shared
         return self.y
 
     # ------------------------------------------------------------- backward
@@ -134,7 +185,8 @@ class MoELayerRunner:
         """Run the backward of the last forward; returns a dict of gradients.
         aux_grad: upstream gradient of the load-balancing loss (when on).
         side_stream: optional second stream (default priority).  The router
-        backward then runs beside dA (it needs only dgates); every launch is
+        backward (and the shared expert's backward) then runs beside dA (they
+        need only dgates and dy); every launch is
         deterministic by itself, so the results are the same bits either way.
         The grouped GEMMs keep the whole GPU.  ``stream`` waits for the side
         stream before returning."""
@@ -164,6 +216,11 @@ class MoELayerRunner:
         else:
             L.moe_route_bwd_aux(d, x, self.topk, self.gates, self.dgates, self.probs, self.counts,
                                 self.aux_alpha * aux_grad, self.dlogits, self.dw_r, self.route_ws, side)
+        if self.shared_w is not None:
+            # the shared expert's backward needs only dy and its own saved rows
+            L.moe_shared_ffn_bwd(self.ds, x, dy, self.shared_w[0], self.shared_w[1], self.shared_w[2], self.g_s,
+                                 self.u_s, self.act_s, self.dg_s, self.du_s, self.dx_s, self.dw_gate_s, self.dw_up_s,
+                                 self.dw_down_s, self.shared_ws, side)
         route_done = torch.cuda.Event()
         route_done.record(side)
         L.moe_ffn_bwd_dact(d, self.dys, w_down, self.g, self.u, self.tiles, self.num_tiles, self.dg, self.du, main)
@@ -172,11 +229,18 @@ class MoELayerRunner:
                          self.dw_down, main)
         if side is not main:
             main.wait_event(route_done)
-        permute_bwd = L.moe_permute_bwd if self.aux_alpha is None else L.moe_permute_bwd_dense
-        permute_bwd(d, self.dxs, self.inv, self.topk, self.dlogits, w_r, self.dx, self.perm_ws, main)
+        if self.shared_w is None:
+            permute_bwd = L.moe_permute_bwd if self.aux_alpha is None else L.moe_permute_bwd_dense
+            permute_bwd(d, self.dxs, self.inv, self.topk, self.dlogits, w_r, self.dx, self.perm_ws, main)
+        else:
+            L.moe_permute_bwd_add(d, self.dxs, self.inv, self.topk, self.dlogits, w_r, self.aux_alpha is not None,
+                                  self.dx_s, self.dx, self.perm_ws, main)
         join(main, side)
-        return dict(dx=self.dx, dw_r=self.dw_r, dw_gate=self.dw_gate, dw_up=self.dw_up, dw_down=self.dw_down,
-                    dgates=self.dgates, dlogits=self.dlogits)
+        out = dict(dx=self.dx, dw_r=self.dw_r, dw_gate=self.dw_gate, dw_up=self.dw_up, dw_down=self.dw_down,
+                   dgates=self.dgates, dlogits=self.dlogits)
+        if self.shared_w is not None:
+            out.update(dw_gate_s=self.dw_gate_s, dw_up_s=self.dw_up_s, dw_down_s=self.dw_down_s)
+        return out
 
 
 class MoEFunction(torch.autograd.Function):

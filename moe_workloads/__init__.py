@@ -30,8 +30,8 @@ from typing import Dict, Optional
 
 import torch
 
-__all__ = ["MoEConfig", "CONFIGS", "TEST_CONFIGS", "make_inputs", "make_expert_weights", "zipf_bias",
-           "tensor_seed"]
+__all__ = ["MoEConfig", "CONFIGS", "TEST_CONFIGS", "make_inputs", "make_expert_weights", "make_shared_weights",
+           "zipf_bias", "tensor_seed"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -102,7 +102,8 @@ TEST_CONFIGS = {
     "t_bigtile": MoEConfig("t_bigtile", N=2048, H=512, F=768, E=4, K=2, dtype="bf16"),
 }
 
-_TENSOR_IDS = {"x": 1, "w_r": 2, "w_gate": 3, "w_up": 4, "w_down": 5, "dy": 6}
+_TENSOR_IDS = {"x": 1, "w_r": 2, "w_gate": 3, "w_up": 4, "w_down": 5, "dy": 6, "w_gate_s": 7, "w_up_s": 8,
+               "w_down_s": 9}
 
 
 def tensor_seed(base_seed: int, name: str, expert: int = 0) -> int:
@@ -161,6 +162,17 @@ def make_inputs(cfg: MoEConfig, seed: int = 0, device="cpu", with_dy: Optional[b
     else:
         out["dy"] = None
     return out
+
+
+def make_shared_weights(cfg: MoEConfig, seed: int, F_s: int, device="cpu"):
+    """(W_gate_s [H,Fs], W_up_s [H,Fs], W_down_s [Fs,H]) of a shared expert of
+    intermediate size F_s, drawn like a routed expert's (std 1/sqrt(fan_in)),
+    in cfg's dtype."""
+    dt = cfg.torch_dtype
+    wg = (_randn((cfg.H, F_s), tensor_seed(seed, "w_gate_s"), device) / math.sqrt(cfg.H)).to(dt)
+    wu = (_randn((cfg.H, F_s), tensor_seed(seed, "w_up_s"), device) / math.sqrt(cfg.H)).to(dt)
+    wd = (_randn((F_s, cfg.H), tensor_seed(seed, "w_down_s"), device) / math.sqrt(F_s)).to(dt)
+    return wg, wu, wd
 
 
 def get_config(name: str) -> MoEConfig:

@@ -157,3 +157,49 @@ def test_capacity_and_gather_entries_validate_on_the_host(lib):
     big = D(N=2 ** 21, H=1024)
     assert lb.moe_ffn_gate_up_gather(ctypes.byref(big), FAKE, FAKE, *gu, FAKE, FAKE, FAKE,
                                      None) == L.MOE_EUNSUPPORTED
+
+
+def test_shared_expert_entries_validate_on_the_host(lib):
+    lb = L.lib()
+    d = D(E=8)
+    ds = D(N=64, H=128, F=384, E=1, K=1)
+    for e in (L.MOE_ENTRY_SHARED_FFN, L.MOE_ENTRY_SHARED_FFN_BWD):
+        assert L.moe_workspace_bytes(d, e) == 2 ** 64 - 1          # only the one-expert dims
+    nf = L.moe_workspace_bytes(ds, L.MOE_ENTRY_SHARED_FFN)
+    nb = L.moe_workspace_bytes(ds, L.MOE_ENTRY_SHARED_FFN_BWD)
+    assert 0 < nf <= nb
+    f8 = [FAKE] * 8
+    assert lb.moe_shared_ffn(ctypes.byref(d), *f8, FAKE, nf, None) == L.MOE_EINVAL           # E, K != 1
+    assert lb.moe_shared_ffn(ctypes.byref(ds), *f8, FAKE, nf - 4, None) == L.MOE_EWORKSPACE
+    assert lb.moe_shared_ffn(ctypes.byref(ds), *([FAKE] * 4), None, FAKE, FAKE, FAKE, FAKE, nf,
+                             None) == L.MOE_EINVAL                                              # g without u
+    assert lb.moe_shared_ffn(ctypes.byref(ds), *([FAKE] * 4), None, None, FAKE, FAKE, FAKE, nf - 4,
+                             None) == L.MOE_EWORKSPACE                                          # forward only
+    f14 = [FAKE] * 14
+    assert lb.moe_shared_ffn_bwd(ctypes.byref(ds), *f14, FAKE, nb - 4, None) == L.MOE_EWORKSPACE
+    assert lb.moe_shared_ffn_bwd(ctypes.byref(d), *f14, FAKE, nb, None) == L.MOE_EINVAL
+    assert lb.moe_shared_ffn_bwd(ctypes.byref(ds), None, *f14[1:], FAKE, nb, None) == L.MOE_EINVAL
+    need_p = L.moe_workspace_bytes(d, L.MOE_ENTRY_PERMUTE_BWD)
+    f5 = [FAKE] * 5
+    assert lb.moe_permute_bwd_add(ctypes.byref(d), *f5, 2, FAKE, FAKE, FAKE, need_p, None) == L.MOE_EINVAL
+    assert lb.moe_permute_bwd_add(ctypes.byref(d), *f5, 0, None, FAKE, FAKE, need_p, None) == L.MOE_EINVAL
+    assert lb.moe_permute_bwd_add(ctypes.byref(d), *f5, 1, FAKE, FAKE, FAKE, need_p - 16, None) == L.MOE_EWORKSPACE
+    assert lb.moe_combine_shared(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, None) == L.MOE_EINVAL
+    d0, ds0 = D(N=0), D(N=0, E=1, K=1)
+    assert lb.moe_combine_shared(ctypes.byref(d0), *([FAKE] * 5), None) == L.MOE_OK
+    assert lb.moe_shared_ffn(ctypes.byref(ds0), *f8, None, 0, None) == L.MOE_OK
+
+
+@pytest.mark.parametrize("N,H,Fs,S", [(16384, 512, 1024, 10), (700, 256, 512, 2), (64, 128, 384, 1),
+                                      (16384, 4096, 14336, 1), (1500, 256, 768, 3)])
+def test_shared_weight_gradient_split(lib, N, H, Fs, S):
+    """The shared expert's weight-gradient contraction is cut into S row
+    chunks: as many as fill 256 CUs once with 3*ceil(H/256)*ceil(Fs/256)
+    output tiles per chunk, each of at least 512 rows (rounded to 64-row
+    steps).  The backward workspace holds S+1 chunk bounds and, for S > 1,
+    the 3*S*H*Fs float32 partial sums."""
+    ds = D(N=N, H=H, F=Fs, E=1, K=1)
+    nf = L.moe_workspace_bytes(ds, L.MOE_ENTRY_SHARED_FFN)
+    nb = L.moe_workspace_bytes(ds, L.MOE_ENTRY_SHARED_FFN_BWD)
+    part = 3 * S * H * Fs * 4 if S > 1 else 0
+    assert nb - nf == (S + 1) * 4 + (-(S + 1) * 4) % 16 + part
