@@ -39,13 +39,13 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # kernel sources whose hash is stored with them; once any source under csrc/
 # changes, the figure is reported as null until the counters are taken again.
 TRAFFIC = {
-    "sources": "8bf9ccd18e985276",
+    "sources": "d104cde7f5d6cd70",
     "bytes": {
-        ("bf16_n16384_h512_f1024_e8_k2", "gate_up"): 336261941,
-        ("bf16_n16384_h512_f1024_e8_k2", "down"): 144317487,
-        ("bf16_n16384_h512_f1024_e8_k2", "dact"): 339593548,
-        ("bf16_n16384_h512_f1024_e8_k2", "dx"): 273149465,
-        ("bf16_n16384_h512_f1024_e8_k2", "dw"): 352734088,
+        ("bf16_n16384_h512_f1024_e8_k2", "gate_up"): 336395932,
+        ("bf16_n16384_h512_f1024_e8_k2", "down"): 144512335,
+        ("bf16_n16384_h512_f1024_e8_k2", "dact"): 339658739,
+        ("bf16_n16384_h512_f1024_e8_k2", "dx"): 272945477,
+        ("bf16_n16384_h512_f1024_e8_k2", "dw"): 352734984,
     },
 }
 
@@ -78,6 +78,8 @@ def parse():
                    help="also compute the Switch load-balancing loss with this weight (forward and its gradient)")
     p.add_argument("--capacity-factor", type=float, default=None,
                    help="token-dropping variant: expert capacity ceil(cf * N * K / E), overflow dropped")
+    p.add_argument("--shared-ffn", type=int, default=None,
+                   help="add a shared expert of this intermediate size that every token passes through")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain 1 GiB streaming copy (for scaling HBM byte counters) and exit")
     return p.parse_args()
@@ -102,14 +104,25 @@ def copy_calibration():
           flush=True)
 
 
-def stage_flops(cfg, rows=None):
+def stage_flops(cfg, rows=None, shared_ffn=None):
     """Algorithmic flops of the grouped GEMMs over `rows` routed rows (all
-    N*K by default; the kept rows of the token-dropping variant)."""
+    N*K by default; the kept rows of the token-dropping variant), and of the
+    shared expert's GEMMs over all N tokens when it is on."""
     hf = cfg.H * cfg.F * (cfg.NK if rows is None else rows)
-    return {"gate_up": 4 * hf, "down": 2 * hf, "dact": 2 * hf, "dx": 4 * hf, "dw": 6 * hf}
+    out = {"gate_up": 4 * hf, "down": 2 * hf, "dact": 2 * hf, "dx": 4 * hf, "dw": 6 * hf}
+    if shared_ffn is not None:
+        hs = cfg.H * shared_ffn * cfg.N
+        out["shared_ffn"] = 6 * hs
+        if cfg.backward:
+            out["shared_bwd"] = 12 * hs
+    return out
 
 
-def stage_bytes(cfg, aux=False):
+# stages that are one call of several launches (not a single kernel)
+COMPOSITE = {"meta", "route_bwd", "permute_bwd", "shared_ffn", "shared_bwd"}
+
+
+def stage_bytes(cfg, aux=False, shared=False):
     """Algorithmic HBM bytes of the row-movement and metadata stages."""
     e = 2 if cfg.dtype == "bf16" else 4
     N, NK, H, E, K = cfg.N, cfg.NK, cfg.H, cfg.E, cfg.K
@@ -128,6 +141,10 @@ def stage_bytes(cfg, aux=False):
         out["aux_loss"] = N * H * e + H * E * e + N * E * 4 + E * 4
         out["route_bwd"] += 2 * N * E * 4
         out["permute_bwd"] += N * E * 4
+    if shared:
+        # the shared expert's output / input gradient: one more [N, H] read
+        out["combine"] += N * H * e
+        out["permute_bwd"] += N * H * e
     return out
 
 
@@ -145,7 +162,7 @@ def main():
 
     from mixture_experts_layer_sort_amd import _lib as L
     from mixture_experts_layer_sort_amd.layer import MoELayerRunner
-    from moe_workloads import get_config, make_inputs
+    from moe_workloads import get_config, make_inputs, make_shared_weights
 
     cfg = get_config(args.config)
     torch.cuda.set_device(0)
@@ -163,14 +180,19 @@ def main():
     capacity = None
     if args.capacity_factor is not None:
         capacity = int(math.ceil(args.capacity_factor * cfg.N * cfg.K / cfg.E))
+    Fs = args.shared_ffn
+    shared = None
+    if Fs is not None:
+        shared_cpu = make_shared_weights(cfg, args.seed, Fs)
+        shared = tuple(w.to(dev) for w in shared_cpu)
     r = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, dev, backward=cfg.backward,
-                       aux_alpha=aux, capacity=capacity)
+                       aux_alpha=aux, capacity=capacity, shared_ffn=Fs)
     d = r.d
     x, w_r, wg, wu, wd, bias, dy = (inp[k] for k in ("x", "w_r", "w_gate", "w_up", "w_down", "bias", "dy"))
     stream = torch.cuda.current_stream()
     # the backward runs the router backward beside dA on a second stream
     # (default priority), as MoELayerRunner does; the GEMMs keep the GPU
-    side = torch.cuda.Stream() if cfg.backward else None
+    side = torch.cuda.Stream() if (cfg.backward or shared is not None) else None
     permute_bwd = L.moe_permute_bwd if aux is None else L.moe_permute_bwd_dense
     fns = {
         "route": lambda st: L.moe_route(d, x, w_r, bias, r.topk, r.gates, st),
@@ -180,7 +202,13 @@ def main():
                                                          r.act, st)) if r.gather_fused else
                     (lambda st: L.moe_ffn_gate_up(d, r.xs, wg, wu, r.tiles, r.num_tiles, r.g, r.u, r.act, st))),
         "down": lambda st: L.moe_ffn_down(d, r.act, wd, r.tiles, r.num_tiles, r.ys, st),
-        "combine": lambda st: L.moe_combine(d, r.ys, r.gates, r.inv, r.y, st),
+        "combine": ((lambda st: L.moe_combine(d, r.ys, r.gates, r.inv, r.y, st)) if shared is None else
+                    (lambda st: L.moe_combine_shared(d, r.ys, r.gates, r.inv, r.ys_s, r.y, st))),
+        "shared_ffn": lambda st: L.moe_shared_ffn(r.ds, x, shared[0], shared[1], shared[2], r.g_s, r.u_s, r.act_s,
+                                                  r.ys_s, r.shared_ws, st),
+        "shared_bwd": lambda st: L.moe_shared_ffn_bwd(r.ds, x, dy, shared[0], shared[1], shared[2], r.g_s, r.u_s,
+                                                      r.act_s, r.dg_s, r.du_s, r.dx_s, r.dw_gate_s, r.dw_up_s,
+                                                      r.dw_down_s, r.shared_ws, st),
         "aux_loss": lambda st: L.moe_aux_loss(d, x, w_r, bias, r.counts, aux, r.probs, r.aux_loss, r.aux_ws, st),
         "combine_bwd": lambda st: L.moe_combine_bwd(d, dy, r.ys, r.gates, r.inv, r.dys, r.dgates, st),
         "route_bwd": ((lambda st: L.moe_route_bwd(d, x, r.topk, r.gates, r.dgates, r.dlogits, r.dw_r, r.route_ws,
@@ -191,11 +219,16 @@ def main():
         "dx": lambda st: L.moe_ffn_bwd_dx(d, r.dg, r.du, wg, wu, r.tiles, r.num_tiles, r.dxs, st),
         "dw": lambda st: L.moe_ffn_bwd_dw(d, r.xs, r.act, r.dys, r.dg, r.du, r.offsets, r.dw_gate, r.dw_up,
                                           r.dw_down, st),
-        "permute_bwd": lambda st: permute_bwd(d, r.dxs, r.inv, r.topk, r.dlogits, w_r, r.dx, r.perm_ws, st),
+        "permute_bwd": ((lambda st: permute_bwd(d, r.dxs, r.inv, r.topk, r.dlogits, w_r, r.dx, r.perm_ws, st))
+                        if shared is None else
+                        (lambda st: L.moe_permute_bwd_add(d, r.dxs, r.inv, r.topk, r.dlogits, w_r, aux is not None,
+                                                          r.dx_s, r.dx, r.perm_ws, st))),
     }
-    fwd_names = (["route", "meta"] + ([] if r.gather_fused else ["permute"]) + ["gate_up", "down", "combine"] +
+    fwd_names = ((["shared_ffn"] if shared is not None else []) + ["route", "meta"] +
+                 ([] if r.gather_fused else ["permute"]) + ["gate_up", "down", "combine"] +
                  (["aux_loss"] if aux is not None else []))
-    bwd_names = ["combine_bwd", "route_bwd", "dact", "dx", "dw", "permute_bwd"] if cfg.backward else []
+    bwd_names = ((["combine_bwd", "route_bwd"] + (["shared_bwd"] if shared is not None else []) +
+                  ["dact", "dx", "dw", "permute_bwd"]) if cfg.backward else [])
 
     def step(ev=None, only=None, overlap=False):
         def run(name, st):
@@ -214,17 +247,29 @@ def main():
             e.record(frm)
             to.wait_event(e)
 
+        if not overlap:
+            for name in fwd_names + bwd_names:
+                run(name, stream)
+            return
+        # the shared expert's forward runs beside the routed forward and
+        # joins before the combine
         for name in fwd_names:
+            if name == "shared_ffn":
+                hand_over(stream, side)
+                run(name, side)
+                shared_done = torch.cuda.Event()
+                shared_done.record(side)
+                continue
+            if name == "combine" and shared is not None:
+                stream.wait_event(shared_done)
             run(name, stream)
         if not cfg.backward:
-            return
-        if not overlap:
-            for name in bwd_names:
-                run(name, stream)
             return
         run("combine_bwd", stream)
         hand_over(stream, side)
         run("route_bwd", side)
+        if shared is not None:
+            run("shared_bwd", side)
         route_done = torch.cuda.Event()
         route_done.record(side)
         run("dact", stream)
@@ -245,10 +290,12 @@ def main():
     torch.cuda.synchronize()
     stage_ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
     kept_rows = int(r.offsets[cfg.E].item())
-    fl = stage_flops(cfg, kept_rows)
+    fl = stage_flops(cfg, kept_rows, Fs)
     gemm_ms = sum(stage_ms[k] for k in fl if k in stage_ms)
     gemm_flops = sum(v for k, v in fl.items() if k in stage_ms)
-    dominant = max(stage_ms, key=stage_ms.get)
+    # the roofline entry is for one kernel: stages of several launches are
+    # reported in the breakdown only
+    dominant = max((k for k in stage_ms if k not in COMPOSITE), key=stage_ms.get)
 
     # timed region: exactly K steps; events only around the dominant kernel
     ev_dom = {}
@@ -268,25 +315,25 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "algorithmic_flops_per_launch": fl[dominant], "launch_ms": round(dom_ms, 5)}
     else:
-        byt = stage_bytes(cfg, aux is not None)[dominant]
+        byt = stage_bytes(cfg, aux is not None, shared is not None)[dominant]
         achieved = byt / (dom_ms * 1e-3) / 1e9
         roof = {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                 "algorithmic_bytes_per_launch": byt, "launch_ms": round(dom_ms, 5)}
-    roof["traffic"] = measured_traffic(cfg.name, dominant) if aux is None else None
+    roof["traffic"] = measured_traffic(cfg.name, dominant) if (aux is None and shared is None) else None
 
     counts = r.counts.cpu().numpy().astype(np.float64)
     tbar = cfg.NK / cfg.E
     maxvio = float(counts.max() / tbar - 1.0)
 
     hbm = {}
-    for k, b in stage_bytes(cfg, aux is not None).items():
+    for k, b in stage_bytes(cfg, aux is not None, shared is not None).items():
         if k in stage_ms and stage_ms[k] > 0:
             hbm[k] = round(b / (stage_ms[k] * 1e-3) / 1e9, 1)
 
     cpu_base = None
     if not args.no_cpu_baseline and not big:
-        cpu_base = cpu_baseline(cfg, cpu, aux)
+        cpu_base = cpu_baseline(cfg, cpu, aux, shared_cpu if shared is not None else None)
 
     out = {
         "metric": "MoE layer tokens/sec fwd+bwd; grouped-GEMM % of bf16 MFMA peak",
@@ -307,7 +354,9 @@ def main():
                    "gather_fused_into_gate_up": r.gather_fused,
                    "capacity": capacity,
                    "dropped_rows": cfg.NK - kept_rows,
-                   "streams": "router backward beside dA" if cfg.backward else "one",
+                   "shared_expert_ffn": Fs,
+                   "streams": ("router backward beside dA" if cfg.backward else "one") +
+                              ("; shared expert beside the routed path" if shared is not None else ""),
                    "empty_experts": int((counts == 0).sum())},
         "grouped_gemm": {"tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 2),
                          "frac_of_bf16_peak": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
@@ -321,7 +370,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(cfg, cpu, aux=None):
+def cpu_baseline(cfg, cpu, aux=None, shared=None):
     """The oracle (as it stands) on the host: whole-layer passes over the
     workload's first S tokens, repeated until about 12 s have passed."""
     import torch
@@ -335,7 +384,8 @@ def cpu_baseline(cfg, cpu, aux=None):
     t0 = time.perf_counter()
     passes = 0
     while True:
-        f = O.forward(x, cpu["w_r"], cpu["w_gate"], cpu["w_up"], cpu["w_down"], cfg.K, bias=cpu["bias"], store=store)
+        f = O.forward(x, cpu["w_r"], cpu["w_gate"], cpu["w_up"], cpu["w_down"], cfg.K, bias=cpu["bias"], store=store,
+                      shared=shared)
         if aux is not None:
             O.aux_loss(f["logits"], f["counts"], cfg.K, aux)
         if dy is not None:
