@@ -109,7 +109,8 @@ def stage_flops(cfg, rows=None, shared_ffn=None):
     N*K by default; the kept rows of the token-dropping variant), and of the
     shared expert's GEMMs over all N tokens when it is on."""
     hf = cfg.H * cfg.F * (cfg.NK if rows is None else rows)
-    out = {"gate_up": 4 * hf, "down": 2 * hf, "dact": 2 * hf, "dx": 4 * hf, "dw": 6 * hf}
+    # dx_dw: dX (4 H F per row) and the three weight gradients (6 H F) in one launch
+    out = {"gate_up": 4 * hf, "down": 2 * hf, "dact": 2 * hf, "dx_dw": 10 * hf}
     if shared_ffn is not None:
         hs = cfg.H * shared_ffn * cfg.N
         out["shared_ffn"] = 6 * hs
@@ -216,9 +217,8 @@ def main():
                       (lambda st: L.moe_route_bwd_aux(d, x, r.topk, r.gates, r.dgates, r.probs, r.counts, aux,
                                                       r.dlogits, r.dw_r, r.route_ws, st))),
         "dact": lambda st: L.moe_ffn_bwd_dact(d, r.dys, wd, r.g, r.u, r.tiles, r.num_tiles, r.dg, r.du, st),
-        "dx": lambda st: L.moe_ffn_bwd_dx(d, r.dg, r.du, wg, wu, r.tiles, r.num_tiles, r.dxs, st),
-        "dw": lambda st: L.moe_ffn_bwd_dw(d, r.xs, r.act, r.dys, r.dg, r.du, r.offsets, r.dw_gate, r.dw_up,
-                                          r.dw_down, st),
+        "dx_dw": lambda st: L.moe_ffn_bwd_dx_dw(d, r.dg, r.du, wg, wu, r.tiles, r.num_tiles, r.dxs, r.xs, r.act,
+                                                r.dys, r.offsets, r.dw_gate, r.dw_up, r.dw_down, st),
         "permute_bwd": ((lambda st: permute_bwd(d, r.dxs, r.inv, r.topk, r.dlogits, w_r, r.dx, r.perm_ws, st))
                         if shared is None else
                         (lambda st: L.moe_permute_bwd_add(d, r.dxs, r.inv, r.topk, r.dlogits, w_r, aux is not None,
@@ -228,7 +228,7 @@ def main():
                  ([] if r.gather_fused else ["permute"]) + ["gate_up", "down", "combine"] +
                  (["aux_loss"] if aux is not None else []))
     bwd_names = ((["combine_bwd", "route_bwd"] + (["shared_bwd"] if shared is not None else []) +
-                  ["dact", "dx", "dw", "permute_bwd"]) if cfg.backward else [])
+                  ["dact", "dx_dw", "permute_bwd"]) if cfg.backward else [])
 
     def step(ev=None, only=None, overlap=False):
         def run(name, st):
@@ -273,8 +273,7 @@ def main():
         route_done = torch.cuda.Event()
         route_done.record(side)
         run("dact", stream)
-        run("dx", stream)
-        run("dw", stream)
+        run("dx_dw", stream)
         stream.wait_event(route_done)
         run("permute_bwd", stream)
         hand_over(side, stream)

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 /* Rows per tile of the grouped-GEMM tile list built by moe_permute_meta. */
 #define MOE_TILE_M 256
 #define MOE_MAX_EXPERTS 256
@@ -230,7 +230,7 @@ int moe_route_bwd(const moe_dims* d, const void* x, const int32_t* topk_idx, con
  *   act [NK,F] from moe_expert_ffn; offsets, tiles, num_tiles from
  *   moe_permute_meta; dg, du [NK,F] out; dxs [NK,H] out; dw_gate, dw_up
  *   [E,H,F] f32 out; dw_down [E,F,H] f32 out.
- * Calls moe_ffn_bwd_dact, moe_ffn_bwd_dx and moe_ffn_bwd_dw. */
+ * Calls moe_ffn_bwd_dact, then moe_ffn_bwd_dx_dw. */
 int moe_expert_ffn_bwd(const moe_dims* d, const void* dys, const void* xs, const void* w_gate, const void* w_up,
                        const void* w_down, const void* g_save, const void* u_save, const void* act,
                        const int32_t* offsets, const int32_t* tiles, const int32_t* num_tiles, void* dg, void* du,
@@ -248,6 +248,19 @@ int moe_ffn_bwd_dx(const moe_dims* d, const void* dg, const void* du, const void
 int moe_ffn_bwd_dw(const moe_dims* d, const void* xs, const void* act, const void* dys, const void* dg,
                    const void* du, const int32_t* offsets, float* dw_gate, float* dw_up, float* dw_down,
                    hipStream_t stream);
+
+/* moe_ffn_bwd_dx and moe_ffn_bwd_dw in one call.  For bf16 it is one launch
+ * of 256 x 256 tiles: the weight-gradient tiles are dispatched first and the
+ * dX tiles fill the CUs they leave idle (the weight gradients alone have
+ * 3*E*ceil(H/256)*ceil(F/256) tiles, 192 at H = 512, F = 1024, E = 8).  Every
+ * output element has one owner and the same ascending contraction order as
+ * in the separate calls.  With MOE_GEMM_TILES set in the environment, and
+ * for float32, it makes the two separate launches.  Arguments as in those
+ * two calls. */
+int moe_ffn_bwd_dx_dw(const moe_dims* d, const void* dg, const void* du, const void* w_gate, const void* w_up,
+                      const int32_t* tiles, const int32_t* num_tiles, void* dxs, const void* xs, const void* act,
+                      const void* dys, const int32_t* offsets, float* dw_gate, float* dw_up, float* dw_down,
+                      hipStream_t stream);
 
 /* Backward of the gather plus the router's input gradient:
  *   dx[n] = sum_k dxs[inv[n*K+k]] + sum_k dlogits[n,e_k] * W_r[:,e_k],

@@ -67,6 +67,7 @@ SIGNATURES = {
     "moe_combine_shared": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P]),
     "moe_shared_ffn_bwd": (ctypes.c_int, [_DP] + [_P] * 15 + [_SZ, _P]),
     "moe_permute_bwd_add": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
+    "moe_ffn_bwd_dx_dw": (ctypes.c_int, [_DP] + [_P] * 14 + [_P]),
 }
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -273,3 +274,10 @@ def moe_shared_ffn_bwd(ds, x, dy, w_gate, w_up, w_down, g_save, u_save, act, dg,
 def moe_permute_bwd_add(d, dxs, inv, topk_idx, dlogits, w_r, dense, dx_add, dx, ws, stream=None):
     _call("moe_permute_bwd_add", ctypes.byref(d), _ptr(dxs), _ptr(inv), _ptr(topk_idx), _ptr(dlogits), _ptr(w_r),
           int(dense), _ptr(dx_add), _ptr(dx), _ptr(ws), _nbytes(ws), _stream(stream))
+
+
+def moe_ffn_bwd_dx_dw(d, dg, du, w_gate, w_up, tiles, num_tiles, dxs, xs, act, dys, offsets, dw_gate, dw_up, dw_down,
+                      stream=None):
+    _call("moe_ffn_bwd_dx_dw", ctypes.byref(d), _ptr(dg), _ptr(du), _ptr(w_gate), _ptr(w_up), _ptr(tiles),
+          _ptr(num_tiles), _ptr(dxs), _ptr(xs), _ptr(act), _ptr(dys), _ptr(offsets), _ptr(dw_gate), _ptr(dw_up),
+          _ptr(dw_down), _stream(stream))

@@ -227,6 +227,18 @@ int moe_ffn_bwd_dw(const moe_dims* d, const void* xs, const void* act, const voi
   return from_hip(moe_launch::ffn_bwd_dw(D, xs, act, dys, dg, du, offsets, dw_gate, dw_up, dw_down, stream));
 }
 
+int moe_ffn_bwd_dx_dw(const moe_dims* d, const void* dg, const void* du, const void* w_gate, const void* w_up,
+                      const int32_t* tiles, const int32_t* num_tiles, void* dxs, const void* xs, const void* act,
+                      const void* dys, const int32_t* offsets, float* dw_gate, float* dw_up, float* dw_down,
+                      hipStream_t stream) {
+  MOE_CHECK_DIMS(d, D);
+  if (!ptrs_ok(dg, du, w_gate, w_up, tiles, num_tiles, dxs, xs, act, dys, offsets, dw_gate, dw_up, dw_down))
+    return MOE_EINVAL;
+  if (D.N == 0) return MOE_OK;
+  return from_hip(moe_launch::ffn_bwd_dx_dw(D, dg, du, w_gate, w_up, tiles, num_tiles, dxs, xs, act, dys, offsets,
+                                            dw_gate, dw_up, dw_down, stream));
+}
+
 int moe_expert_ffn_bwd(const moe_dims* d, const void* dys, const void* xs, const void* w_gate, const void* w_up,
                        const void* w_down, const void* g_save, const void* u_save, const void* act,
                        const int32_t* offsets, const int32_t* tiles, const int32_t* num_tiles, void* dg, void* du,
@@ -238,9 +250,8 @@ int moe_expert_ffn_bwd(const moe_dims* d, const void* dys, const void* xs, const
   if (D.N == 0) return MOE_OK;
   int st = from_hip(moe_launch::ffn_bwd_dact(D, dys, w_down, g_save, u_save, tiles, num_tiles, dg, du, stream));
   if (st != MOE_OK) return st;
-  st = from_hip(moe_launch::ffn_bwd_dx(D, dg, du, w_gate, w_up, tiles, num_tiles, dxs, stream));
-  if (st != MOE_OK) return st;
-  return from_hip(moe_launch::ffn_bwd_dw(D, xs, act, dys, dg, du, offsets, dw_gate, dw_up, dw_down, stream));
+  return from_hip(moe_launch::ffn_bwd_dx_dw(D, dg, du, w_gate, w_up, tiles, num_tiles, dxs, xs, act, dys, offsets,
+                                            dw_gate, dw_up, dw_down, stream));
 }
 
 int moe_permute_bwd(const moe_dims* d, const void* dxs, const int32_t* inv, const int32_t* topk_idx,

@@ -98,11 +98,11 @@ __device__ __forceinline__ float silu_f32(float g) { return g * sigmoid_f32(g); 
 // order still advances through all XCDs together.  The launch grid must be a
 // multiple of 8 * kXcdRun; returns -1 for blocks past `total`.
 constexpr int kXcdRun = 8;
-__device__ __forceinline__ int xcd_window_block(int total) {
-  const int b = blockIdx.x;
+__device__ __forceinline__ int xcd_window_block(int b, int total) {
   const int L = (b / (8 * kXcdRun)) * (8 * kXcdRun) + (b % 8) * kXcdRun + (b / 8) % kXcdRun;
   return L < total ? L : -1;
 }
+__device__ __forceinline__ int xcd_window_block(int total) { return xcd_window_block(blockIdx.x, total); }
 
 // The expert of rank p when experts are ordered by row count, largest first
 // (equal counts: lower id first), from offsets [E+1].  The weight-gradient
@@ -182,6 +182,10 @@ hipError_t ffn_bwd_dx(const Dims& d, const void* dg, const void* du, const void*
                       const int32_t* tiles, const int32_t* num_tiles, void* dxs, hipStream_t s);
 hipError_t ffn_bwd_dw(const Dims& d, const void* xs, const void* a, const void* dys, const void* dg, const void* du,
                       const int32_t* offsets, float* dwg, float* dwu, float* dwd, hipStream_t s);
+// ffn_bwd_dx and ffn_bwd_dw together (one launch for bf16).
+hipError_t ffn_bwd_dx_dw(const Dims& d, const void* dg, const void* du, const void* wg, const void* wu,
+                         const int32_t* tiles, const int32_t* num_tiles, void* dxs, const void* xs, const void* a,
+                         const void* dys, const int32_t* offsets, float* dwg, float* dwu, float* dwd, hipStream_t s);
 
 // Shared expert: a dense SwiGLU expert over all N tokens (dims E = K = 1,
 // F = its intermediate size).  The workspace holds its tile list, the row

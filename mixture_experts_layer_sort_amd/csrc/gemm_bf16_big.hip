@@ -115,12 +115,12 @@ struct TileInfo {
 // tiles of one expert) run on one XCD and share its L2.  The launch grid is
 // a multiple of 8 and at least `total`; returns -1 for blocks with no work.
 constexpr int kXcds = 8;
-__device__ __forceinline__ int xcd_block(int total) {
-  const int b = blockIdx.x;
+__device__ __forceinline__ int xcd_block(int b, int total) {
   const int per = (total + kXcds - 1) / kXcds;
   const int L = (b % kXcds) * per + b / kXcds;
   return (b / kXcds < per && L < total) ? L : -1;
 }
+__device__ __forceinline__ int xcd_block(int total) { return xcd_block(blockIdx.x, total); }
 
 // Logical block -> (row tile, n tile) in groups of kGroupM row tiles: inside
 // a group the row tile varies fastest, so the ~32 workgroups an XCD runs at
@@ -337,16 +337,17 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_dact(const bf16_t* __restric
   }
 }
 
-// dxs = dG.W_gate[e]^T + dU.W_up[e]^T  (one K loop over 2F)
+// dxs = dG.W_gate[e]^T + dU.W_up[e]^T  (one K loop over 2F); b: this
+// workgroup's block index within the dX part of the launch.
 template <class C>
-__global__ __launch_bounds__(C::NT, C::MINB) void k_dx(const bf16_t* __restrict__ dg, const bf16_t* __restrict__ du,
-                                              const bf16_t* __restrict__ wg, const bf16_t* __restrict__ wu,
-                                              const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles,
-                                              bf16_t* __restrict__ dxs, int H, int F) {
-  extern __shared__ __attribute__((aligned(16))) char lds[];
+__device__ __forceinline__ void dx_tile(char* lds, int b, const bf16_t* __restrict__ dg,
+                                        const bf16_t* __restrict__ du, const bf16_t* __restrict__ wg,
+                                        const bf16_t* __restrict__ wu, const int32_t* __restrict__ tiles,
+                                        const int32_t* __restrict__ num_tiles, bf16_t* __restrict__ dxs, int H,
+                                        int F) {
   const int ntn = (H + C::BN - 1) / C::BN;
   const int nrow = *num_tiles * C::SUB;
-  const int L = xcd_block(nrow * ntn);
+  const int L = xcd_block(b, nrow * ntn);
   if (L < 0) return;
   int rt, nt;
   grouped(L, nrow, ntn, rt, nt);
@@ -383,26 +384,35 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_dx(const bf16_t* __restrict_
   epi_store<C>(stg, dxs + (int64_t)ti.row0 * H + nt * C::BN, H, ti.rows, ncols);
 }
 
+template <class C>
+__global__ __launch_bounds__(C::NT, C::MINB) void k_dx(const bf16_t* __restrict__ dg, const bf16_t* __restrict__ du,
+                                              const bf16_t* __restrict__ wg, const bf16_t* __restrict__ wu,
+                                              const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles,
+                                              bf16_t* __restrict__ dxs, int H, int F) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  dx_tile<C>(lds, blockIdx.x, dg, du, wg, wu, tiles, num_tiles, dxs, H, F);
+}
+
 // Weight gradients, one workgroup per BM x BN output tile of one expert:
 //   problem 0: dW_gate[e] = xs_e^T . dG_e   [H, F]
 //   problem 1: dW_up[e]   = xs_e^T . dU_e   [H, F]
 //   problem 2: dW_down[e] = A_e^T  . dys_e  [F, H]
 // The contraction runs over the expert's rows in ascending 64-row steps;
 // experts without rows write exact zeros.
+// b: this workgroup's block index within the dW part of the launch.
 template <class C>
-__global__ __launch_bounds__(C::NT, C::MINB) void k_dw(const bf16_t* __restrict__ xs, const bf16_t* __restrict__ act,
-                                              const bf16_t* __restrict__ dys, const bf16_t* __restrict__ dg,
-                                              const bf16_t* __restrict__ du, const int32_t* __restrict__ offsets,
-                                              float* __restrict__ dwg, float* __restrict__ dwu,
-                                              float* __restrict__ dwd, int H, int F, int E) {
-  extern __shared__ __attribute__((aligned(16))) char lds[];
+__device__ __forceinline__ void dw_tile(char* lds, int b, const bf16_t* __restrict__ xs,
+                                        const bf16_t* __restrict__ act, const bf16_t* __restrict__ dys,
+                                        const bf16_t* __restrict__ dg, const bf16_t* __restrict__ du,
+                                        const int32_t* __restrict__ offsets, float* __restrict__ dwg,
+                                        float* __restrict__ dwu, float* __restrict__ dwd, int H, int F, int E) {
   const int tf = (F + C::BN - 1) / C::BN, th2 = (H + C::BN - 1) / C::BN;
   const int tpe = ((H + C::BM - 1) / C::BM) * tf;    // output tiles of problems 0 and 1 per expert
   const int tpe2 = ((F + C::BM - 1) / C::BM) * th2;  // ... of problem 2
   const int per = 2 * tpe + tpe2;
   // experts largest first, each expert's tiles consecutive, dealt to the XCDs
   // in runs of kXcdRun
-  const int blk = xcd_window_block(E * per);
+  const int blk = xcd_window_block(b, E * per);
   if (blk < 0) return;
   const int e = expert_of_rank<C::NT>(offsets, E, blk / per, reinterpret_cast<int*>(lds));
   const int within = blk % per;
@@ -460,6 +470,35 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_dw(const bf16_t* __restrict_
     }
 }
 
+template <class C>
+__global__ __launch_bounds__(C::NT, C::MINB) void k_dw(const bf16_t* __restrict__ xs, const bf16_t* __restrict__ act,
+                                              const bf16_t* __restrict__ dys, const bf16_t* __restrict__ dg,
+                                              const bf16_t* __restrict__ du, const int32_t* __restrict__ offsets,
+                                              float* __restrict__ dwg, float* __restrict__ dwu,
+                                              float* __restrict__ dwd, int H, int F, int E) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  dw_tile<C>(lds, blockIdx.x, xs, act, dys, dg, du, offsets, dwg, dwu, dwd, H, F, E);
+}
+
+// dX and dW in one launch.  Both read only dG and dU (plus xs, A, dys and the
+// weights), so their tiles are independent: the first dw_grid workgroups take
+// the weight-gradient tiles (longest contractions first), the rest the dX
+// tiles, which fill the CUs the weight gradients leave idle and their tail.
+// dw_grid is a multiple of 8 * kXcdRun, so both parts keep their XCD mapping.
+template <class C>
+__global__ __launch_bounds__(C::NT, C::MINB) void k_dx_dw(
+    const bf16_t* __restrict__ dg, const bf16_t* __restrict__ du, const bf16_t* __restrict__ wg,
+    const bf16_t* __restrict__ wu, const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles,
+    bf16_t* __restrict__ dxs, const bf16_t* __restrict__ xs, const bf16_t* __restrict__ act,
+    const bf16_t* __restrict__ dys, const int32_t* __restrict__ offsets, float* __restrict__ dwg,
+    float* __restrict__ dwu, float* __restrict__ dwd, int H, int F, int E, int dw_grid) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int b = blockIdx.x;
+  if (b < dw_grid)
+    dw_tile<C>(lds, b, xs, act, dys, dg, du, offsets, dwg, dwu, dwd, H, F, E);
+  else
+    dx_tile<C>(lds, b - dw_grid, dg, du, wg, wu, tiles, num_tiles, dxs, H, F);
+}
 
 }  // namespace
 
@@ -543,16 +582,23 @@ hipError_t ffn_bwd_dx_big(const Dims& d, const void* dg, const void* du, const v
   return dx_t<Big>(d, dg, du, wg, wu, tiles, num_tiles, dxs, s);
 }
 
+// workgroups of a weight-gradient launch: E experts x (two H x F problems +
+// one F x H), rounded up to whole XCD windows
+template <class C>
+static unsigned dw_grid(const Dims& d) {
+  const int64_t tpe = ((d.H + C::BM - 1) / C::BM) * ((d.F + C::BN - 1) / C::BN);
+  const int64_t tpe2 = ((d.F + C::BM - 1) / C::BM) * ((d.H + C::BN - 1) / C::BN);
+  const int64_t total = d.E * (2 * tpe + tpe2);
+  const int64_t win = 8 * kXcdRun;
+  return unsigned((total + win - 1) / win * win);
+}
+
 template <class C>
 static hipError_t dw_t(const Dims& d, const void* xs, const void* a, const void* dys, const void* dg, const void* du,
                        const int32_t* offsets, float* dwg, float* dwu, float* dwd, hipStream_t s) {
   hipError_t st = allow_lds<k_dw<C>>(C::LDS);
   if (st != hipSuccess) return st;
-  const int64_t tpe = ((d.H + C::BM - 1) / C::BM) * ((d.F + C::BN - 1) / C::BN);
-  const int64_t tpe2 = ((d.F + C::BM - 1) / C::BM) * ((d.H + C::BN - 1) / C::BN);
-  const int64_t total = d.E * (2 * tpe + tpe2);
-  const int64_t win = 8 * kXcdRun;
-  unsigned grid = unsigned((total + win - 1) / win * win);
+  const unsigned grid = dw_grid<C>(d);
   hipLaunchKernelGGL(k_dw<C>, dim3(grid), dim3(C::NT), C::LDS, s, static_cast<const bf16_t*>(xs),
                      static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(dys), static_cast<const bf16_t*>(dg),
                      static_cast<const bf16_t*>(du), offsets, dwg, dwu, dwd, int(d.H), int(d.F), int(d.E));
@@ -562,6 +608,23 @@ static hipError_t dw_t(const Dims& d, const void* xs, const void* a, const void*
 hipError_t ffn_bwd_dw_big(const Dims& d, const void* xs, const void* a, const void* dys, const void* dg,
                            const void* du, const int32_t* offsets, float* dwg, float* dwu, float* dwd, hipStream_t s) {
   return dw_t<Big>(d, xs, a, dys, dg, du, offsets, dwg, dwu, dwd, s);
+}
+
+hipError_t ffn_bwd_dx_dw_big(const Dims& d, const void* dg, const void* du, const void* wg, const void* wu,
+                             const int32_t* tiles, const int32_t* num_tiles, void* dxs, const void* xs, const void* a,
+                             const void* dys, const int32_t* offsets, float* dwg, float* dwu, float* dwd,
+                             hipStream_t s) {
+  using C = Big;
+  hipError_t st = allow_lds<k_dx_dw<C>>(C::LDS);
+  if (st != hipSuccess) return st;
+  const unsigned gw = dw_grid<C>(d);
+  const unsigned gx = grid8(max_tiles(d) * C::SUB * ((d.H + C::BN - 1) / C::BN));
+  hipLaunchKernelGGL(k_dx_dw<C>, dim3(gw + gx), dim3(C::NT), C::LDS, s, static_cast<const bf16_t*>(dg),
+                     static_cast<const bf16_t*>(du), static_cast<const bf16_t*>(wg), static_cast<const bf16_t*>(wu),
+                     tiles, num_tiles, static_cast<bf16_t*>(dxs), static_cast<const bf16_t*>(xs),
+                     static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(dys), offsets, dwg, dwu, dwd,
+                     int(d.H), int(d.F), int(d.E), int(gw));
+  return hipGetLastError();
 }
 
 // 128 x 256 register-staged tiles

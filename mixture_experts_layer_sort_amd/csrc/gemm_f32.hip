@@ -172,6 +172,9 @@ MOE_BF16_SHAPE(ffn_bwd_dx, const void*, const void*, const void*, const void*, c
 MOE_BF16_SHAPE(ffn_bwd_dw, const void*, const void*, const void*, const void*, const void*, const int32_t*, float*,
                float*, float*, hipStream_t)
 #undef MOE_BF16_SHAPE
+hipError_t ffn_bwd_dx_dw_big(const Dims&, const void*, const void*, const void*, const void*, const int32_t*,
+                             const int32_t*, void*, const void*, const void*, const void*, const int32_t*, float*,
+                             float*, float*, hipStream_t);
 
 // Which bf16 tile shape each stage uses.  The 256 x 256 tiles (one workgroup
 // per CU: 4 waves of 128 x 128 with register-staged loads, or, for dA, 8
@@ -278,6 +281,21 @@ hipError_t ffn_bwd_dw(const Dims& d, const void* xs, const void* a, const void* 
                      static_cast<const float*>(a), static_cast<const float*>(dys), static_cast<const float*>(dg),
                      static_cast<const float*>(du), offsets, dwg, dwu, dwd, int(d.H), int(d.F), int(d.E));
   return hipGetLastError();
+}
+
+// dX and the weight gradients.  bf16: one launch of 256 x 256 tiles, the
+// weight-gradient tiles first and the dX tiles filling the CUs they leave
+// idle (at (H, F, E) = (512, 1024, 8) the weight gradients alone have 192
+// workgroups for 256 CUs); with MOE_GEMM_TILES set, the two stages run as
+// separate launches of the forced family.  float32: two launches.
+hipError_t ffn_bwd_dx_dw(const Dims& d, const void* dg, const void* du, const void* wg, const void* wu,
+                         const int32_t* tiles, const int32_t* num_tiles, void* dxs, const void* xs, const void* a,
+                         const void* dys, const int32_t* offsets, float* dwg, float* dwu, float* dwd, hipStream_t s) {
+  if (d.dtype == MOE_BF16 && std::getenv("MOE_GEMM_TILES") == nullptr)
+    return ffn_bwd_dx_dw_big(d, dg, du, wg, wu, tiles, num_tiles, dxs, xs, a, dys, offsets, dwg, dwu, dwd, s);
+  hipError_t st = ffn_bwd_dx(d, dg, du, wg, wu, tiles, num_tiles, dxs, s);
+  if (st != hipSuccess) return st;
+  return ffn_bwd_dw(d, xs, a, dys, dg, du, offsets, dwg, dwu, dwd, s);
 }
 
 }  // namespace moe_launch

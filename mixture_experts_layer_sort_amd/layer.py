@@ -8,7 +8,7 @@ layer through the C ABI:
             (moe_ffn_gate_up, moe_ffn_down) -> moe_combine; without a backward,
             moe_ffn_gate_up_gather replaces moe_permute + moe_ffn_gate_up
   backward: moe_combine_bwd -> moe_route_bwd -> moe_expert_ffn_bwd
-            (moe_ffn_bwd_dact, moe_ffn_bwd_dx, moe_ffn_bwd_dw) -> moe_permute_bwd
+            (moe_ffn_bwd_dact, moe_ffn_bwd_dx_dw) -> moe_permute_bwd
 
 With a shared expert, moe_shared_ffn runs beside the routed path and
 moe_combine_shared adds its output; in the backward moe_shared_ffn_bwd gives
@@ -224,9 +224,8 @@ class MoELayerRunner:
         route_done = torch.cuda.Event()
         route_done.record(side)
         L.moe_ffn_bwd_dact(d, self.dys, w_down, self.g, self.u, self.tiles, self.num_tiles, self.dg, self.du, main)
-        L.moe_ffn_bwd_dx(d, self.dg, self.du, w_gate, w_up, self.tiles, self.num_tiles, self.dxs, main)
-        L.moe_ffn_bwd_dw(d, self.xs, self.act, self.dys, self.dg, self.du, self.offsets, self.dw_gate, self.dw_up,
-                         self.dw_down, main)
+        L.moe_ffn_bwd_dx_dw(d, self.dg, self.du, w_gate, w_up, self.tiles, self.num_tiles, self.dxs, self.xs,
+                            self.act, self.dys, self.offsets, self.dw_gate, self.dw_up, self.dw_down, main)
         if side is not main:
             main.wait_event(route_done)
         if self.shared_w is None:

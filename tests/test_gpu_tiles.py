@@ -102,3 +102,39 @@ def test_gate_up_gather_equals_permute_then_gate_up(cfg, tiles, monkeypatch):
     r.forward(dev["x"], dev["w_r"], dev["w_gate"], dev["w_up"], dev["w_down"], dev["bias"])
     sync()
     assert torch.equal(y.view(torch.uint8), r.y.view(torch.uint8))
+
+
+@pytest.mark.parametrize("cfg", [TEST_CONFIGS["t_skew"], TEST_CONFIGS["t_ragged"], TEST_CONFIGS["t_e1"],
+                                 MoEConfig("t_tiles_f640", N=1500, H=384, F=640, E=3, K=2, dtype="bf16"),
+                                 MoEConfig("t_dxdw_base_shape", N=4096, H=512, F=1024, E=8, K=2, dtype="bf16")],
+                         ids=lambda c: c.name)
+def test_merged_dx_dw_launch_equals_separate_launches(cfg, monkeypatch):
+    """moe_ffn_bwd_dx_dw (one launch: weight-gradient tiles first, dX tiles
+    after) gives the same bytes as the separate 256 x 256 dX and dW launches,
+    on poisoned outputs, with empty experts and ragged tails."""
+    from mixture_experts_layer_sort_amd import _lib as L
+    from mixture_experts_layer_sort_amd.layer import MoELayerRunner
+    monkeypatch.delenv("MOE_GEMM_TILES", raising=False)
+    print(f"[dx_dw] {cfg.name}", flush=True)
+    cpu, dev = gpu_inputs(cfg, 21, with_dy=True)
+    r = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, "cuda")
+    r.forward(dev["x"], dev["w_r"], dev["w_gate"], dev["w_up"], dev["w_down"], dev["bias"])
+    r.backward(dev["dy"])
+    sync()
+    outs = []
+    for forced in (None, "256"):
+        if forced is not None:
+            monkeypatch.setenv("MOE_GEMM_TILES", forced)
+        dxs = torch.full_like(r.dxs, float("nan"))
+        dwg, dwu, dwd = (torch.full_like(t, float("nan")) for t in (r.dw_gate, r.dw_up, r.dw_down))
+        L.moe_ffn_bwd_dx_dw(r.d, r.dg, r.du, dev["w_gate"], dev["w_up"], r.tiles, r.num_tiles, dxs, r.xs, r.act,
+                            r.dys, r.offsets, dwg, dwu, dwd)
+        sync()
+        outs.append((dxs, dwg, dwu, dwd))
+    nk = int(r.offsets[-1].item())
+    for name, a, b in zip(("dxs", "dw_gate", "dw_up", "dw_down"), outs[0], outs[1]):
+        if name == "dxs":
+            a, b = a[:nk], b[:nk]
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), name
+    # and the runner's own backward (merged launch) wrote the same dW
+    assert torch.equal(outs[0][1].view(torch.uint8), r.dw_gate.view(torch.uint8))
