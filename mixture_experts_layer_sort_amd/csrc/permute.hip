@@ -9,6 +9,8 @@
 // the gather backward read the K rows of a token through inv[] (a gather-sum
 // in ascending k) instead of scattering with atomics, so results are bitwise
 // reproducible.  All rows move in 16-byte vectors; a row is H elements.
+#include <type_traits>
+
 #include "common.h"
 
 namespace {
@@ -33,31 +35,43 @@ __global__ __launch_bounds__(256) void k_permute(const T* __restrict__ x, const 
 
 // y[n] = sum_k gates[n,k] * ys[inv[n*K+k]], k ascending, float32 accumulation;
 // dropped slots (inv < 0) add nothing.  add (optional, [N,H]): a row added
-// with weight 1 after the K terms (the shared expert's output).
-template <typename T>
+// with weight 1 after the K terms (the shared expert's output).  KT = K: all
+// K row loads of a vector are issued before the first multiply.
+template <typename T, int KT>
 __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ ys, const float* __restrict__ gates,
                                                  const int32_t* __restrict__ inv, const T* __restrict__ add,
-                                                 T* __restrict__ y, int64_t total_vec, int vpr, int K) {
+                                                 T* __restrict__ y, int64_t total_vec, int vpr) {
   constexpr int V = Vec16<T>::n;
   const int64_t stride = (int64_t)gridDim.x * 256;
   for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < total_vec; v += stride) {
-    int64_t n = v / vpr;
-    int c = int(v - n * vpr);
+    const int64_t n = v / vpr;
+    const int c = int(v - n * vpr);
+    int32_t r[KT];
+    float g[KT];
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+      r[k] = inv[n * KT + k];
+      g[k] = gates[n * KT + k];
+    }
+    uint4 raw[KT], ra;
+#pragma unroll
+    for (int k = 0; k < KT; ++k)
+      if (r[k] >= 0) raw[k] = *reinterpret_cast<const uint4*>(ys + ((int64_t)r[k] * vpr + c) * V);
+    if (add != nullptr) ra = *reinterpret_cast<const uint4*>(add + v * V);
     float acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0.f;
-    for (int k = 0; k < K; ++k) {
-      int64_t r = inv[n * K + k];
-      if (r < 0) continue;
-      float g = gates[n * K + k];
-      float val[V];
-      Vec16<T>::load(ys + (r * vpr + c) * V, val);
 #pragma unroll
-      for (int i = 0; i < V; ++i) acc[i] = fmaf(g, val[i], acc[i]);
-    }
+    for (int k = 0; k < KT; ++k)
+      if (r[k] >= 0) {
+        float val[V];
+        Vec16<T>::load(reinterpret_cast<const T*>(&raw[k]), val);
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[i] = fmaf(g[k], val[i], acc[i]);
+      }
     if (add != nullptr) {
       float val[V];
-      Vec16<T>::load(add + v * V, val);
+      Vec16<T>::load(reinterpret_cast<const T*>(&ra), val);
 #pragma unroll
       for (int i = 0; i < V; ++i) acc[i] += val[i];
     }
@@ -65,66 +79,77 @@ __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ ys, const
   }
 }
 
-// One wave per token, kTokPerWave tokens per wave in turn:
-// dys[inv[n,k]] = g_k * dy[n]; dgates[n,k] = <dy[n], ys[inv[n,k]]> (fixed
-// lane order and butterfly, so the dot products are reproducible).  A
-// dropped slot (inv < 0) has no row and a zero gate gradient.
-constexpr int kTokPerWave = 2;
-template <typename T>
+// One wave per tok_per_wave(K) tokens, their loads issued together:
+// dys[inv[n,k]] = g_k * dy[n]; dgates[n,k] = <dy[n], ys[inv[n,k]]> (each
+// lane sums its vectors in ascending order, then a fixed butterfly, so the
+// dot products are reproducible).  A dropped slot (inv < 0) has no row and a
+// zero gate gradient.  KT = K.
+// Tokens per wave: two while the row registers of both fit (K <= 4), else one.
+__host__ __device__ constexpr int tok_per_wave(int K) { return K <= 4 ? 2 : 1; }
+template <typename T, int KT>
 __global__ __launch_bounds__(256) void k_combine_bwd(const T* __restrict__ dy, const T* __restrict__ ys,
                                                      const float* __restrict__ gates, const int32_t* __restrict__ inv,
-                                                     T* __restrict__ dys, float* __restrict__ dgates, int N, int vpr,
-                                                     int K) {
+                                                     T* __restrict__ dys, float* __restrict__ dgates, int N, int vpr) {
   constexpr int V = Vec16<T>::n;
+  constexpr int TW = tok_per_wave(KT);
   const int lane = lane_id();
-  const int64_t nbase = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kTokPerWave;
-  int64_t r[kTokPerWave][MOE_MAX_TOPK];
-  float g[kTokPerWave][MOE_MAX_TOPK];
+  const int64_t nbase = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * TW;
+  if (nbase >= N) return;  // uniform across the wave
+  int32_t r[TW][KT];
+  float g[TW][KT];
+  bool valid[TW];
 #pragma unroll
-  for (int t = 0; t < kTokPerWave; ++t)
-#pragma unroll
-    for (int k = 0; k < MOE_MAX_TOPK; ++k) {
-      const int64_t n = nbase + t;
-      const bool ok = n < N && k < K;
-      r[t][k] = ok ? inv[n * K + k] : 0;
-      g[t][k] = ok ? gates[n * K + k] : 0.f;
-    }
-#pragma unroll
-  for (int t = 0; t < kTokPerWave; ++t) {
+  for (int t = 0; t < TW; ++t) {
     const int64_t n = nbase + t;
-    if (n >= N) break;  // uniform across the wave
-    float dot[MOE_MAX_TOPK];
+    valid[t] = n < N;
 #pragma unroll
-    for (int k = 0; k < MOE_MAX_TOPK; ++k) dot[k] = 0.f;
-    for (int c = lane; c < vpr; c += kWave) {
-      float d[V];
-      Vec16<T>::load(dy + (n * vpr + c) * V, d);
-      uint4 raw[MOE_MAX_TOPK];
+    for (int k = 0; k < KT; ++k) {
+      r[t][k] = valid[t] ? inv[n * KT + k] : -1;
+      g[t][k] = valid[t] ? gates[n * KT + k] : 0.f;
+    }
+  }
+  float dot[TW][KT];
 #pragma unroll
-      for (int k = 0; k < MOE_MAX_TOPK; ++k)
-        if (k < K && r[t][k] >= 0) raw[k] = *reinterpret_cast<const uint4*>(ys + (r[t][k] * vpr + c) * V);
+  for (int t = 0; t < TW; ++t)
 #pragma unroll
-      for (int k = 0; k < MOE_MAX_TOPK; ++k) {
-        if (k < K && r[t][k] >= 0) {
-          float yv[V], o[V];
-          Vec16<T>::load(reinterpret_cast<const T*>(&raw[k]), yv);
-          float s = dot[k];
+    for (int k = 0; k < KT; ++k) dot[t][k] = 0.f;
+  for (int c = lane; c < vpr; c += kWave) {
+    uint4 rd[TW], raw[TW][KT];
 #pragma unroll
-          for (int i = 0; i < V; ++i) {
-            s = fmaf(d[i], yv[i], s);
-            o[i] = g[t][k] * d[i];
-          }
-          dot[k] = s;
-          Vec16<T>::store(dys + (r[t][k] * vpr + c) * V, o);
-        }
-      }
+    for (int t = 0; t < TW; ++t) {
+      if (valid[t]) rd[t] = *reinterpret_cast<const uint4*>(dy + ((nbase + t) * vpr + c) * V);
+#pragma unroll
+      for (int k = 0; k < KT; ++k)
+        if (r[t][k] >= 0) raw[t][k] = *reinterpret_cast<const uint4*>(ys + ((int64_t)r[t][k] * vpr + c) * V);
     }
 #pragma unroll
-    for (int k = 0; k < MOE_MAX_TOPK; ++k) {
-      if (k < K) {
-        float s = wave_sum(dot[k]);
-        if (lane == 0) dgates[n * K + k] = s;
+    for (int t = 0; t < TW; ++t) {
+      if (!valid[t]) continue;
+      float d[V];
+      Vec16<T>::load(reinterpret_cast<const T*>(&rd[t]), d);
+#pragma unroll
+      for (int k = 0; k < KT; ++k) {
+        if (r[t][k] < 0) continue;
+        float yv[V], o[V];
+        Vec16<T>::load(reinterpret_cast<const T*>(&raw[t][k]), yv);
+        float s = dot[t][k];
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          s = fmaf(d[i], yv[i], s);
+          o[i] = g[t][k] * d[i];
+        }
+        dot[t][k] = s;
+        Vec16<T>::store(dys + ((int64_t)r[t][k] * vpr + c) * V, o);
       }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < TW; ++t) {
+    if (!valid[t]) continue;  // uniform across the wave
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+      const float s = wave_sum(dot[t][k]);
+      if (lane == 0) dgates[(nbase + t) * KT + k] = s;
     }
   }
 }
@@ -138,82 +163,100 @@ __global__ __launch_bounds__(256) void k_transpose_wr(const T* __restrict__ w_r,
   w_rt[idx] = w_r[(int64_t)h * E + e];
 }
 
-// dx[n] = sum_k dxs[inv[n*K+k]] + sum_k dlogits[n, e_k] * W_r[:, e_k], both
-// sums in ascending k (dropped slots, inv < 0, have no dxs row); one wave per
-// token.  DENSE: the router term runs over all E experts (dlogits is dense
-// when the load-balancing loss is on).
-template <typename T, bool DENSE>
+// dx[n] = sum_k dxs[inv[n*K+k]] (kept slots, k ascending) + the router
+// term sum_k dlogits[n,e_k] * W_r^T[e_k] (k ascending; dlogits of a dropped
+// slot is not zero: its gate still takes part in the softmax), float32, one
+// rounding.  DENSE: the router term runs over all E experts in ascending
+// order (dlogits is dense when the load-balancing loss is on; used for
+// E <= 8).  add (optional): one more row added last.  One wave per
+// tok_per_wave(K) tokens with every row load of a vector issued together;
+// KT = K.
+template <typename T, bool DENSE, int KT>
 __global__ __launch_bounds__(256) void k_permute_bwd(const T* __restrict__ dxs, const int32_t* __restrict__ inv,
                                                      const int32_t* __restrict__ topk, const float* __restrict__ dl,
                                                      const T* __restrict__ w_rt, const T* __restrict__ add,
-                                                     T* __restrict__ dx, int N, int vpr, int K, int E) {
+                                                     T* __restrict__ dx, int N, int vpr, int E) {
   constexpr int V = Vec16<T>::n;
+  constexpr int TW = tok_per_wave(KT);
   const int lane = lane_id();
-  const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (n >= N) return;
-  const uint4 *sx[MOE_MAX_TOPK], *sw[MOE_MAX_TOPK];
-  float d[MOE_MAX_TOPK];
-  bool kept[MOE_MAX_TOPK];
+  const int64_t nbase = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * TW;
+  if (nbase >= N) return;  // uniform across the wave
+  int32_t r[TW][KT], ex[TW][KT];
+  float dk[TW][KT];
+  bool valid[TW];
 #pragma unroll
-  for (int k = 0; k < MOE_MAX_TOPK; ++k)
-    if (k < K) {
-      const int e = topk[n * K + k];
-      const int32_t r = inv[n * K + k];
-      kept[k] = r >= 0;
-      sx[k] = reinterpret_cast<const uint4*>(dxs) + (int64_t)(kept[k] ? r : 0) * vpr;
-      sw[k] = reinterpret_cast<const uint4*>(w_rt) + (int64_t)e * vpr;
-      d[k] = dl[n * E + e];
+  for (int t = 0; t < TW; ++t) {
+    const int64_t n = nbase + t;
+    valid[t] = n < N;
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+      r[t][k] = valid[t] ? inv[n * KT + k] : -1;
+      ex[t][k] = valid[t] ? topk[n * KT + k] : 0;
+      dk[t][k] = (!DENSE && valid[t]) ? dl[n * E + ex[t][k]] : 0.f;
     }
-  T* dst = dx + n * vpr * V;
+  }
+  const uint4* xs4 = reinterpret_cast<const uint4*>(dxs);
+  const uint4* wr4 = reinterpret_cast<const uint4*>(w_rt);
   for (int c = lane; c < vpr; c += kWave) {
-    uint4 rx[MOE_MAX_TOPK], rw[MOE_MAX_TOPK];
+    uint4 rx[TW][KT], rw[TW][KT], ra[TW];
 #pragma unroll
-    for (int k = 0; k < MOE_MAX_TOPK; ++k)
-      if (k < K) {
-        if (kept[k]) rx[k] = sx[k][c];
-        rw[k] = sw[k][c];
+    for (int t = 0; t < TW; ++t) {
+#pragma unroll
+      for (int k = 0; k < KT; ++k) {
+        if (r[t][k] >= 0) rx[t][k] = xs4[(int64_t)r[t][k] * vpr + c];
+        if (!DENSE && valid[t]) rw[t][k] = wr4[(int64_t)ex[t][k] * vpr + c];
       }
-    float acc[V];
+      if (add != nullptr && valid[t]) ra[t] = reinterpret_cast<const uint4*>(add)[(nbase + t) * vpr + c];
+    }
+    float acc[TW][V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+    for (int t = 0; t < TW; ++t) {
 #pragma unroll
-    for (int k = 0; k < MOE_MAX_TOPK; ++k)
-      if (k < K && kept[k]) {
-        float val[V];
-        Vec16<T>::load(reinterpret_cast<const T*>(&rx[k]), val);
+      for (int i = 0; i < V; ++i) acc[t][i] = 0.f;
 #pragma unroll
-        for (int i = 0; i < V; ++i) acc[i] += val[i];
+      for (int k = 0; k < KT; ++k)
+        if (r[t][k] >= 0) {
+          float val[V];
+          Vec16<T>::load(reinterpret_cast<const T*>(&rx[t][k]), val);
+#pragma unroll
+          for (int i = 0; i < V; ++i) acc[t][i] += val[i];
+        }
+      if (!DENSE) {
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+          float wv[V];
+          Vec16<T>::load(reinterpret_cast<const T*>(&rw[t][k]), wv);
+#pragma unroll
+          for (int i = 0; i < V; ++i) acc[t][i] = fmaf(dk[t][k], wv[i], acc[t][i]);
+        }
       }
+    }
     if (DENSE) {
-      // every router logit has a gradient (load-balancing loss): all E
-      // experts, ascending
-      const float* dln = dl + n * E;
-      const uint4* wr = reinterpret_cast<const uint4*>(w_rt);
+      // every router logit has a gradient: all E experts, ascending; each
+      // W_r^T vector serves the wave's tokens
       for (int e = 0; e < E; ++e) {
-        const uint4 raw = wr[(int64_t)e * vpr + c];
+        const uint4 raw = wr4[(int64_t)e * vpr + c];
         float wv[V];
         Vec16<T>::load(reinterpret_cast<const T*>(&raw), wv);
-        const float de = dln[e];
 #pragma unroll
-        for (int i = 0; i < V; ++i) acc[i] = fmaf(de, wv[i], acc[i]);
-      }
-    } else {
+        for (int t = 0; t < TW; ++t) {
+          const float de = valid[t] ? dl[(nbase + t) * E + e] : 0.f;
 #pragma unroll
-      for (int k = 0; k < MOE_MAX_TOPK; ++k)
-        if (k < K) {
-          float wv[V];
-          Vec16<T>::load(reinterpret_cast<const T*>(&rw[k]), wv);
-#pragma unroll
-          for (int i = 0; i < V; ++i) acc[i] = fmaf(d[k], wv[i], acc[i]);
+          for (int i = 0; i < V; ++i) acc[t][i] = fmaf(de, wv[i], acc[t][i]);
         }
+      }
     }
-    if (add != nullptr) {
-      float val[V];
-      Vec16<T>::load(add + (n * vpr + c) * V, val);
 #pragma unroll
-      for (int i = 0; i < V; ++i) acc[i] += val[i];
+    for (int t = 0; t < TW; ++t) {
+      if (!valid[t]) continue;
+      if (add != nullptr) {
+        float val[V];
+        Vec16<T>::load(reinterpret_cast<const T*>(&ra[t]), val);
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[t][i] += val[i];
+      }
+      Vec16<T>::store(dx + ((nbase + t) * vpr + c) * V, acc[t]);
     }
-    Vec16<T>::store(dst + c * V, acc);
   }
 }
 
@@ -307,6 +350,23 @@ __global__ __launch_bounds__(256) void k_permute_bwd_dense_tiled(const T* __rest
   }
 }
 
+// Calls f(std::integral_constant<int, K>) for K in 1..MOE_MAX_TOPK.
+template <typename Fn>
+hipError_t with_k(int K, Fn&& f) {
+  static_assert(MOE_MAX_TOPK == 8, "one case per K");
+  switch (K) {
+    case 1: return f(std::integral_constant<int, 1>{});
+    case 2: return f(std::integral_constant<int, 2>{});
+    case 3: return f(std::integral_constant<int, 3>{});
+    case 4: return f(std::integral_constant<int, 4>{});
+    case 5: return f(std::integral_constant<int, 5>{});
+    case 6: return f(std::integral_constant<int, 6>{});
+    case 7: return f(std::integral_constant<int, 7>{});
+    case 8: return f(std::integral_constant<int, 8>{});
+    default: return hipErrorInvalidValue;
+  }
+}
+
 unsigned grid_for(int64_t total, int64_t cap = 8192) {
   int64_t b = (total + 255) / 256;
   if (b > cap) b = cap;
@@ -348,28 +408,30 @@ hipError_t combine(const Dims& d, const void* ys, const float* gates, const int3
     using T = decltype(tag);
     const int vpr = vpr_of<T>(d);
     const int64_t tot = d.N * vpr;
-    hipLaunchKernelGGL(k_combine<T>, dim3(grid_for(tot)), dim3(256), 0, s, static_cast<const T*>(ys), gates, inv,
-                       static_cast<const T*>(add), static_cast<T*>(y), tot, vpr, int(d.K));
+    return with_k(int(d.K), [&](auto kt) {
+      hipLaunchKernelGGL((k_combine<T, decltype(kt)::value>), dim3(grid_for(tot)), dim3(256), 0, s,
+                         static_cast<const T*>(ys), gates, inv, static_cast<const T*>(add), static_cast<T*>(y), tot,
+                         vpr);
+      return hipGetLastError();
+    });
   };
-  if (d.dtype == MOE_BF16)
-    run(moe::bf16_t{});
-  else
-    run(float{});
-  return hipGetLastError();
+  return d.dtype == MOE_BF16 ? run(moe::bf16_t{}) : run(float{});
 }
 
 hipError_t combine_bwd(const Dims& d, const void* dy, const void* ys, const float* gates, const int32_t* inv,
                        void* dys, float* dgates, hipStream_t s) {
-  unsigned grid = unsigned((d.N + 4 * kTokPerWave - 1) / (4 * kTokPerWave));
-  if (d.dtype == MOE_BF16)
-    hipLaunchKernelGGL(k_combine_bwd<moe::bf16_t>, dim3(grid), dim3(256), 0, s,
-                       static_cast<const moe::bf16_t*>(dy), static_cast<const moe::bf16_t*>(ys), gates, inv,
-                       static_cast<moe::bf16_t*>(dys), dgates, int(d.N), vpr_of<moe::bf16_t>(d), int(d.K));
-  else
-    hipLaunchKernelGGL(k_combine_bwd<float>, dim3(grid), dim3(256), 0, s, static_cast<const float*>(dy),
-                       static_cast<const float*>(ys), gates, inv, static_cast<float*>(dys), dgates, int(d.N),
-                       vpr_of<float>(d), int(d.K));
-  return hipGetLastError();
+  const int tpb = 4 * tok_per_wave(int(d.K));
+  const unsigned grid = unsigned((d.N + tpb - 1) / tpb);
+  auto run = [&](auto tag) {
+    using T = decltype(tag);
+    return with_k(int(d.K), [&](auto kt) {
+      hipLaunchKernelGGL((k_combine_bwd<T, decltype(kt)::value>), dim3(grid), dim3(256), 0, s,
+                         static_cast<const T*>(dy), static_cast<const T*>(ys), gates, inv, static_cast<T*>(dys),
+                         dgates, int(d.N), vpr_of<T>(d));
+      return hipGetLastError();
+    });
+  };
+  return d.dtype == MOE_BF16 ? run(moe::bf16_t{}) : run(float{});
 }
 
 size_t permute_bwd_ws(const Dims& d) {
@@ -380,25 +442,32 @@ hipError_t permute_bwd(const Dims& d, const void* dxs, const int32_t* inv, const
                        const void* w_r, const void* add, void* dx, void* ws, hipStream_t s, bool dense) {
   int64_t nw = d.H * d.E;
   unsigned tg = unsigned((nw + 255) / 256);
+  const int tpb = 4 * tok_per_wave(int(d.K));
+  const unsigned grid = unsigned((d.N + tpb - 1) / tpb);
   auto run = [&](auto tag) -> hipError_t {
     using T = decltype(tag);
     hipLaunchKernelGGL(k_transpose_wr<T>, dim3(tg), dim3(256), 0, s, static_cast<const T*>(w_r), static_cast<T*>(ws),
                        int(d.H), int(d.E));
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    if (dense && d.E > 8)
+    if (dense && d.E > 8) {
       hipLaunchKernelGGL((k_permute_bwd_dense_tiled<T>), dim3(waves4((d.N + kTokTile - 1) / kTokTile)), dim3(256), 0,
                          s, static_cast<const T*>(dxs), inv, dlogits, static_cast<const T*>(ws), static_cast<const T*>(add),
                          static_cast<T*>(dx), int(d.N), vpr_of<T>(d), int(d.K), int(d.E));
-    else if (dense)
-      hipLaunchKernelGGL((k_permute_bwd<T, true>), dim3(waves4(d.N)), dim3(256), 0, s, static_cast<const T*>(dxs), inv,
-                         topk, dlogits, static_cast<const T*>(ws), static_cast<const T*>(add), static_cast<T*>(dx),
-                         int(d.N), vpr_of<T>(d), int(d.K), int(d.E));
-    else
-      hipLaunchKernelGGL((k_permute_bwd<T, false>), dim3(waves4(d.N)), dim3(256), 0, s, static_cast<const T*>(dxs),
-                         inv, topk, dlogits, static_cast<const T*>(ws), static_cast<const T*>(add), static_cast<T*>(dx),
-                         int(d.N), vpr_of<T>(d), int(d.K), int(d.E));
-    return hipGetLastError();
+      return hipGetLastError();
+    }
+    return with_k(int(d.K), [&](auto kt) {
+      constexpr int KT = decltype(kt)::value;
+      if (dense)
+        hipLaunchKernelGGL((k_permute_bwd<T, true, KT>), dim3(grid), dim3(256), 0, s, static_cast<const T*>(dxs), inv,
+                           topk, dlogits, static_cast<const T*>(ws), static_cast<const T*>(add), static_cast<T*>(dx),
+                           int(d.N), vpr_of<T>(d), int(d.E));
+      else
+        hipLaunchKernelGGL((k_permute_bwd<T, false, KT>), dim3(grid), dim3(256), 0, s, static_cast<const T*>(dxs),
+                           inv, topk, dlogits, static_cast<const T*>(ws), static_cast<const T*>(add),
+                           static_cast<T*>(dx), int(d.N), vpr_of<T>(d), int(d.E));
+      return hipGetLastError();
+    });
   };
   if (d.dtype == MOE_BF16) return run(moe::bf16_t{});
   return run(float{});
