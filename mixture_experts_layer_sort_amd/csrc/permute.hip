@@ -16,6 +16,8 @@
 namespace {
 using namespace moe;
 
+// xs[i] = x[sorted_flat[i] / K], one 16-byte vector per thread, grid-stride;
+// dropped rows (sorted_flat < 0, capacity) are skipped.
 template <typename T>
 __global__ __launch_bounds__(256) void k_permute(const T* __restrict__ x, const int32_t* __restrict__ sorted_flat,
                                                  T* __restrict__ xs, int64_t total_vec, int vpr, int K) {
@@ -33,59 +35,71 @@ __global__ __launch_bounds__(256) void k_permute(const T* __restrict__ x, const 
   }
 }
 
+// Tokens per wave: two while the row registers of both fit (K <= 4), else one.
+__host__ __device__ constexpr int tok_per_wave(int K) { return K <= 4 ? 2 : 1; }
+
 // y[n] = sum_k gates[n,k] * ys[inv[n*K+k]], k ascending, float32 accumulation;
 // dropped slots (inv < 0) add nothing.  add (optional, [N,H]): a row added
-// with weight 1 after the K terms (the shared expert's output).  KT = K: all
-// K row loads of a vector are issued before the first multiply.
+// with weight 1 after the K terms (the shared expert's output).  One wave per
+// tok_per_wave(K) tokens, all row loads of a vector issued before the first
+// multiply; KT = K.
 template <typename T, int KT>
 __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ ys, const float* __restrict__ gates,
                                                  const int32_t* __restrict__ inv, const T* __restrict__ add,
-                                                 T* __restrict__ y, int64_t total_vec, int vpr) {
+                                                 T* __restrict__ y, int N, int vpr) {
   constexpr int V = Vec16<T>::n;
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < total_vec; v += stride) {
-    const int64_t n = v / vpr;
-    const int c = int(v - n * vpr);
-    int32_t r[KT];
-    float g[KT];
+  constexpr int TW = tok_per_wave(KT);
+  const int lane = lane_id();
+  const int64_t nbase = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * TW;
+  if (nbase >= N) return;  // uniform across the wave
+  int32_t r[TW][KT];
+  float g[TW][KT];
+  bool valid[TW];
+#pragma unroll
+  for (int t = 0; t < TW; ++t) {
+    const int64_t n = nbase + t;
+    valid[t] = n < N;
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
-      r[k] = inv[n * KT + k];
-      g[k] = gates[n * KT + k];
+      r[t][k] = valid[t] ? inv[n * KT + k] : -1;
+      g[t][k] = valid[t] ? gates[n * KT + k] : 0.f;
     }
-    uint4 raw[KT], ra;
+  }
+  const uint4* ys4 = reinterpret_cast<const uint4*>(ys);
+  for (int c = lane; c < vpr; c += kWave) {
+    uint4 raw[TW][KT], ra[TW];
 #pragma unroll
-    for (int k = 0; k < KT; ++k)
-      if (r[k] >= 0) raw[k] = *reinterpret_cast<const uint4*>(ys + ((int64_t)r[k] * vpr + c) * V);
-    if (add != nullptr) ra = *reinterpret_cast<const uint4*>(add + v * V);
-    float acc[V];
+    for (int t = 0; t < TW; ++t) {
 #pragma unroll
-    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+      for (int k = 0; k < KT; ++k)
+        if (r[t][k] >= 0) raw[t][k] = ys4[(int64_t)r[t][k] * vpr + c];
+      if (add != nullptr && valid[t]) ra[t] = reinterpret_cast<const uint4*>(add)[(nbase + t) * vpr + c];
+    }
 #pragma unroll
-    for (int k = 0; k < KT; ++k)
-      if (r[k] >= 0) {
+    for (int t = 0; t < TW; ++t) {
+      if (!valid[t]) continue;
+      float acc[V];
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int k = 0; k < KT; ++k)
+        if (r[t][k] >= 0) {
+          float val[V];
+          Vec16<T>::load(reinterpret_cast<const T*>(&raw[t][k]), val);
+#pragma unroll
+          for (int i = 0; i < V; ++i) acc[i] = fmaf(g[t][k], val[i], acc[i]);
+        }
+      if (add != nullptr) {
         float val[V];
-        Vec16<T>::load(reinterpret_cast<const T*>(&raw[k]), val);
+        Vec16<T>::load(reinterpret_cast<const T*>(&ra[t]), val);
 #pragma unroll
-        for (int i = 0; i < V; ++i) acc[i] = fmaf(g[k], val[i], acc[i]);
+        for (int i = 0; i < V; ++i) acc[i] += val[i];
       }
-    if (add != nullptr) {
-      float val[V];
-      Vec16<T>::load(reinterpret_cast<const T*>(&ra), val);
-#pragma unroll
-      for (int i = 0; i < V; ++i) acc[i] += val[i];
+      Vec16<T>::store(y + ((nbase + t) * vpr + c) * V, acc);
     }
-    Vec16<T>::store(y + v * V, acc);
   }
 }
 
-// One wave per tok_per_wave(K) tokens, their loads issued together:
-// dys[inv[n,k]] = g_k * dy[n]; dgates[n,k] = <dy[n], ys[inv[n,k]]> (each
-// lane sums its vectors in ascending order, then a fixed butterfly, so the
-// dot products are reproducible).  A dropped slot (inv < 0) has no row and a
-// zero gate gradient.  KT = K.
-// Tokens per wave: two while the row registers of both fit (K <= 4), else one.
-__host__ __device__ constexpr int tok_per_wave(int K) { return K <= 4 ? 2 : 1; }
 template <typename T, int KT>
 __global__ __launch_bounds__(256) void k_combine_bwd(const T* __restrict__ dy, const T* __restrict__ ys,
                                                      const float* __restrict__ gates, const int32_t* __restrict__ inv,
@@ -404,14 +418,13 @@ hipError_t permute(const Dims& d, const void* x, const int32_t* sorted_flat, voi
 
 hipError_t combine(const Dims& d, const void* ys, const float* gates, const int32_t* inv, const void* add, void* y,
                    hipStream_t s) {
+  const int tpb = 4 * tok_per_wave(int(d.K));
+  const unsigned grid = unsigned((d.N + tpb - 1) / tpb);
   auto run = [&](auto tag) {
     using T = decltype(tag);
-    const int vpr = vpr_of<T>(d);
-    const int64_t tot = d.N * vpr;
     return with_k(int(d.K), [&](auto kt) {
-      hipLaunchKernelGGL((k_combine<T, decltype(kt)::value>), dim3(grid_for(tot)), dim3(256), 0, s,
-                         static_cast<const T*>(ys), gates, inv, static_cast<const T*>(add), static_cast<T*>(y), tot,
-                         vpr);
+      hipLaunchKernelGGL((k_combine<T, decltype(kt)::value>), dim3(grid), dim3(256), 0, s, static_cast<const T*>(ys),
+                         gates, inv, static_cast<const T*>(add), static_cast<T*>(y), int(d.N), vpr_of<T>(d));
       return hipGetLastError();
     });
   };
