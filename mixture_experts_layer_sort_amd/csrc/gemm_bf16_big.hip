@@ -63,6 +63,12 @@ using Mid = TileCfg<128, 256, 2, 4, 2, 32, 3>;
 // stage, two stages (48 KiB of operands, 67 KiB with the staged epilogue),
 // two workgroups per CU so one's epilogue overlaps the other's main loop.
 using MidR = TileCfg<128, 256, 2, 2, 2, 32, 2, true>;
+// dX tiles inside the merged dX / weight-gradient launch.  128 x 256 tiles
+// would balance that launch better (at H = 512, F = 1024, E = 8 its 192
+// weight-gradient tiles take 64 k steps and the dX tiles 32), but measured
+// slower on every workload (221 -> 238 us there with 64 k per stage, 260 with
+// 32): the smaller tile's operand traffic per flop outweighs the balance.
+using DxInMerged = Big;
 static_assert(MOE_TILE_M % Big::BM == 0 && MOE_TILE_M % BigDma::BM == 0 && MOE_TILE_M % Mid::BM == 0 &&
                   MOE_TILE_M % MidR::BM == 0,
               "list tiles split into row tiles");
@@ -485,19 +491,22 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_dw(const bf16_t* __restrict_
 // the weight-gradient tiles (longest contractions first), the rest the dX
 // tiles, which fill the CUs the weight gradients leave idle and their tail.
 // dw_grid is a multiple of 8 * kXcdRun, so both parts keep their XCD mapping.
-template <class C>
-__global__ __launch_bounds__(C::NT, C::MINB) void k_dx_dw(
+// CW: the weight-gradient tiles' shape; CX: the dX tiles' shape (same block
+// size; the launch gets the larger LDS of the two).
+template <class CW, class CX>
+__global__ __launch_bounds__(CW::NT, CW::MINB) void k_dx_dw(
     const bf16_t* __restrict__ dg, const bf16_t* __restrict__ du, const bf16_t* __restrict__ wg,
     const bf16_t* __restrict__ wu, const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles,
     bf16_t* __restrict__ dxs, const bf16_t* __restrict__ xs, const bf16_t* __restrict__ act,
     const bf16_t* __restrict__ dys, const int32_t* __restrict__ offsets, float* __restrict__ dwg,
     float* __restrict__ dwu, float* __restrict__ dwd, int H, int F, int E, int dw_grid) {
+  static_assert(CW::NT == CX::NT, "one block size");
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int b = blockIdx.x;
   if (b < dw_grid)
-    dw_tile<C>(lds, b, xs, act, dys, dg, du, offsets, dwg, dwu, dwd, H, F, E);
+    dw_tile<CW>(lds, b, xs, act, dys, dg, du, offsets, dwg, dwu, dwd, H, F, E);
   else
-    dx_tile<C>(lds, b - dw_grid, dg, du, wg, wu, tiles, num_tiles, dxs, H, F);
+    dx_tile<CX>(lds, b - dw_grid, dg, du, wg, wu, tiles, num_tiles, dxs, H, F);
 }
 
 }  // namespace
@@ -614,12 +623,14 @@ hipError_t ffn_bwd_dx_dw_big(const Dims& d, const void* dg, const void* du, cons
                              const int32_t* tiles, const int32_t* num_tiles, void* dxs, const void* xs, const void* a,
                              const void* dys, const int32_t* offsets, float* dwg, float* dwu, float* dwd,
                              hipStream_t s) {
-  using C = Big;
-  hipError_t st = allow_lds<k_dx_dw<C>>(C::LDS);
+  using CW = Big;
+  using CX = DxInMerged;
+  constexpr int lds_bytes = CW::LDS > CX::LDS ? CW::LDS : CX::LDS;
+  hipError_t st = allow_lds<k_dx_dw<CW, CX>>(lds_bytes);
   if (st != hipSuccess) return st;
-  const unsigned gw = dw_grid<C>(d);
-  const unsigned gx = grid8(max_tiles(d) * C::SUB * ((d.H + C::BN - 1) / C::BN));
-  hipLaunchKernelGGL(k_dx_dw<C>, dim3(gw + gx), dim3(C::NT), C::LDS, s, static_cast<const bf16_t*>(dg),
+  const unsigned gw = dw_grid<CW>(d);
+  const unsigned gx = grid8(max_tiles(d) * CX::SUB * ((d.H + CX::BN - 1) / CX::BN));
+  hipLaunchKernelGGL((k_dx_dw<CW, CX>), dim3(gw + gx), dim3(CW::NT), lds_bytes, s, static_cast<const bf16_t*>(dg),
                      static_cast<const bf16_t*>(du), static_cast<const bf16_t*>(wg), static_cast<const bf16_t*>(wu),
                      tiles, num_tiles, static_cast<bf16_t*>(dxs), static_cast<const bf16_t*>(xs),
                      static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(dys), offsets, dwg, dwu, dwd,
