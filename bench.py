@@ -30,6 +30,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 # HBM bytes per launch of each GEMM stage, from two rocprofv3 --pmc runs of
@@ -116,6 +117,23 @@ def stage_flops(cfg, rows=None, shared_ffn=None):
         if cfg.backward:
             out["shared_bwd"] = 12 * hs
     return out
+
+
+def gemm_bytes(cfg, rows, experts_used, save_gu):
+    """Algorithmic HBM bytes of the grouped-GEMM stages over `rows` routed
+    rows: each operand row and each used expert's weights read once, each
+    output written once (dG and dU counted once in the merged dX/dW launch;
+    the fp32 weight gradients of all E experts are written, empty ones as
+    zeros)."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    H, F = cfg.H, cfg.F
+    w = experts_used * H * F * e
+    return {
+        "gate_up": rows * H * e + 2 * w + (3 if save_gu else 1) * rows * F * e,
+        "down": rows * F * e + w + rows * H * e,
+        "dact": rows * H * e + w + 4 * rows * F * e,
+        "dx_dw": 2 * rows * F * e + 2 * w + rows * H * e + 2 * rows * H * e + rows * F * e + 3 * cfg.E * H * F * 4,
+    }
 
 
 # stages that are one call of several launches (not a single kernel)
@@ -307,11 +325,25 @@ def main():
     dom_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_dom[dominant]]))
     tokens_per_s = cfg.N * args.steps / (t1 - t0)
 
-    if dominant in fl:
+    peak_flops = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    used = int((np.diff(r.offsets.cpu().numpy()) > 0).sum())
+    gb = gemm_bytes(cfg, kept_rows, used, r.g is not None)
+    if dominant in fl and fl[dominant] / (peak_flops * 1e12) < gb[dominant] / (PEAK_HBM_GBS * 1e9):
+        # a grouped GEMM whose bytes at HBM peak take longer than its flops at
+        # the matrix-core peak (the wide-expert forward streams every expert's
+        # weights for about 256 rows each): HBM-bound
+        achieved = gb[dominant] / (dom_ms * 1e-3) / 1e9
+        roof = {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "algorithmic_bytes_per_launch": gb[dominant], "algorithmic_flops_per_launch": fl[dominant],
+                "launch_ms": round(dom_ms, 5)}
+    elif dominant in fl:
         achieved = fl[dominant] / (dom_ms * 1e-3) / 1e12
-        roof = {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "algorithmic_flops_per_launch": fl[dominant], "launch_ms": round(dom_ms, 5)}
+        roof = {"kernel": dominant, "bound": "mfma" if cfg.dtype == "bf16" else "alu", "achieved": round(achieved, 2),
+                "peak": peak_flops,
+                "unit": "TFLOP/s", "frac": round(achieved / peak_flops, 4),
+                "algorithmic_flops_per_launch": fl[dominant], "algorithmic_bytes_per_launch": gb.get(dominant),
+                "launch_ms": round(dom_ms, 5)}
     else:
         byt = stage_bytes(cfg, aux is not None, shared is not None)[dominant]
         achieved = byt / (dom_ms * 1e-3) / 1e9
@@ -323,6 +355,17 @@ def main():
     counts = r.counts.cpu().numpy().astype(np.float64)
     tbar = cfg.NK / cfg.E
     maxvio = float(counts.max() / tbar - 1.0)
+
+    # every grouped-GEMM stage against its own bound (from the event-timed breakdown)
+    gemm_roof = {}
+    for k in gb:
+        if k in stage_ms and stage_ms[k] > 0:
+            t = stage_ms[k] * 1e-3
+            if fl[k] / (peak_flops * 1e12) < gb[k] / (PEAK_HBM_GBS * 1e9):
+                gemm_roof[k] = {"bound": "hbm", "frac": round(gb[k] / t / 1e9 / PEAK_HBM_GBS, 4)}
+            else:
+                gemm_roof[k] = {"bound": "mfma" if cfg.dtype == "bf16" else "alu",
+                                "frac": round(fl[k] / t / 1e12 / peak_flops, 4)}
 
     hbm = {}
     for k, b in stage_bytes(cfg, aux is not None, shared is not None).items():
@@ -361,6 +404,7 @@ def main():
                          "ms": round(gemm_ms, 4), "algorithmic_flops": gemm_flops},
         "stages_ms": {k: round(v, 5) for k, v in stage_ms.items()},
         "stages_hbm_gbs": hbm,
+        "gemm_stages_roofline": gemm_roof,
         "roofline": roof,
         "cpu_baseline": cpu_base,
         "host": {"cpu": platform.processor() or platform.machine(), "cores": os.cpu_count()},
