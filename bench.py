@@ -137,7 +137,7 @@ def gemm_bytes(cfg, rows, experts_used, save_gu):
 
 
 # stages that are one call of several launches (not a single kernel)
-COMPOSITE = {"meta", "route_bwd", "permute_bwd", "shared_ffn", "shared_bwd"}
+COMPOSITE = {"route_meta", "route_bwd", "permute_bwd", "shared_ffn", "shared_bwd"}
 
 
 def stage_bytes(cfg, aux=False, shared=False):
@@ -145,8 +145,9 @@ def stage_bytes(cfg, aux=False, shared=False):
     e = 2 if cfg.dtype == "bf16" else 4
     N, NK, H, E, K = cfg.N, cfg.NK, cfg.H, cfg.E, cfg.K
     out = {
-        "route": N * H * e + H * E * e + N * K * 8,
-        "meta": NK * 4 * 3 + NK * 8 + (2 * E + 1) * 4,
+        # router (x and W_r read, top-K and gates written) + metadata (topk read,
+        # sorted_flat and inv written, counts and offsets)
+        "route_meta": N * H * e + H * E * e + N * K * 8 + NK * 4 + NK * 8 + (2 * E + 1) * 4,
         "permute": (N + NK) * H * e + NK * 4,           # read each token once (cached), write NK rows
         "combine": (NK + N) * H * e + NK * 8,
         "combine_bwd": (N + 2 * NK) * H * e + NK * 12,
@@ -213,8 +214,9 @@ def main():
     side = torch.cuda.Stream() if (cfg.backward or shared is not None) else None
     permute_bwd = L.moe_permute_bwd if aux is None else L.moe_permute_bwd_dense
     fns = {
-        "route": lambda st: L.moe_route(d, x, w_r, bias, r.topk, r.gates, st),
-        "meta": lambda st: r.meta(stream=st),
+        "route_meta": lambda st: L.moe_route_meta(d, x, w_r, bias, 2 ** 31 - 1 if capacity is None else capacity,
+                                                  r.topk, r.gates, r.sorted_flat, r.inv, r.counts, r.offsets,
+                                                  r.tiles, r.num_tiles, r.route_meta_ws, st),
         "permute": lambda st: L.moe_permute(d, x, r.sorted_flat, r.xs, st),
         "gate_up": ((lambda st: L.moe_ffn_gate_up_gather(d, x, r.sorted_flat, wg, wu, r.tiles, r.num_tiles, r.g, r.u,
                                                          r.act, st)) if r.gather_fused else
@@ -241,7 +243,7 @@ def main():
                         (lambda st: L.moe_permute_bwd_add(d, r.dxs, r.inv, r.topk, r.dlogits, w_r, aux is not None,
                                                           r.dx_s, r.dx, r.perm_ws, st))),
     }
-    fwd_names = ((["shared_ffn"] if shared is not None else []) + ["route", "meta"] +
+    fwd_names = ((["shared_ffn"] if shared is not None else []) + ["route_meta"] +
                  ([] if r.gather_fused else ["permute"]) + ["gate_up", "down", "combine"] +
                  (["aux_loss"] if aux is not None else []))
     bwd_names = ((["combine_bwd", "route_bwd"] + (["shared_bwd"] if shared is not None else []) +

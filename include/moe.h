@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 6
+#define MOE_ABI_VERSION 7
 /* Rows per tile of the grouped-GEMM tile list built by moe_permute_meta. */
 #define MOE_TILE_M 256
 #define MOE_MAX_EXPERTS 256
@@ -77,7 +77,8 @@ typedef enum moe_entry {
   MOE_ENTRY_AUX_LOSS = 4,
   MOE_ENTRY_ROUTE_BWD_AUX = 5,
   MOE_ENTRY_SHARED_FFN = 6,    /* shared-expert dims only (E = K = 1) */
-  MOE_ENTRY_SHARED_FFN_BWD = 7 /* shared-expert dims only (E = K = 1) */
+  MOE_ENTRY_SHARED_FFN_BWD = 7, /* shared-expert dims only (E = K = 1) */
+  MOE_ENTRY_ROUTE_META = 8
 } moe_entry;
 
 /* Problem sizes: N tokens, hidden size H, expert FFN size F, E experts,
@@ -115,6 +116,22 @@ size_t moe_workspace_bytes(const moe_dims* d, int32_t entry);
  *   topk_idx [N,K] int32 out (slot k = rank k); gates [N,K] f32 out. */
 int moe_route(const moe_dims* d, const void* x, const void* w_r, const float* logit_bias, int32_t* topk_idx,
               float* gates, hipStream_t stream);
+
+/* moe_route followed by moe_permute_meta_capacity (capacity INT32_MAX: the
+ * dropless metadata), with the same outputs, fused into two launches: the
+ * router also leaves each 32-token block's histogram of the chosen experts
+ * in the workspace, and one metadata kernel turns those histograms into the
+ * bins, the stable ranks and the tile list without a separate histogram or
+ * scan launch (MegaBlocks sections 2.1 and 2.3: histogram, cumsum into bins,
+ * sort; routing and sort fused as in "MoK: high-performance Megakernel for
+ * deterministic training of large MoE models" (jsqmd.com), section 1.3).
+ * Every workgroup of that kernel re-reads all block histograms, so the
+ * fusion is used while ceil(N/32)*E <= 32768; above that the call runs the
+ * unfused kernels.  capacity < 0: MOE_EINVAL.  ws: MOE_ENTRY_ROUTE_META. */
+int moe_route_meta(const moe_dims* d, const void* x, const void* w_r, const float* logit_bias, int32_t capacity,
+                   int32_t* topk_idx, float* gates, int32_t* sorted_flat, int32_t* inv, int32_t* counts,
+                   int32_t* offsets, int32_t* tiles, int32_t* num_tiles, void* ws, size_t ws_bytes,
+                   hipStream_t stream);
 
 /* Dropless routing metadata from the flat assignment f = n*K + k (MegaBlocks
  * sections 2.1, 2.3 and 4: sort by expert id, histogram, cumsum into bins):

@@ -21,7 +21,7 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, 
 MOE_F32, MOE_BF16 = 0, 1
 MOE_ENTRY_PERMUTE_META, MOE_ENTRY_ROUTE_BWD, MOE_ENTRY_PERMUTE_BWD = 1, 2, 3
 MOE_ENTRY_AUX_LOSS, MOE_ENTRY_ROUTE_BWD_AUX = 4, 5
-MOE_ENTRY_SHARED_FFN, MOE_ENTRY_SHARED_FFN_BWD = 6, 7
+MOE_ENTRY_SHARED_FFN, MOE_ENTRY_SHARED_FFN_BWD, MOE_ENTRY_ROUTE_META = 6, 7, 8
 MOE_TILE_M = 256
 
 # Every exported symbol with (restype, argtypes); the tests check this list
@@ -68,6 +68,7 @@ SIGNATURES = {
     "moe_shared_ffn_bwd": (ctypes.c_int, [_DP] + [_P] * 15 + [_SZ, _P]),
     "moe_permute_bwd_add": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
     "moe_ffn_bwd_dx_dw": (ctypes.c_int, [_DP] + [_P] * 14 + [_P]),
+    "moe_route_meta": (ctypes.c_int, [_DP, _P, _P, _P, _I32] + [_P] * 9 + [_SZ, _P]),
 }
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -281,3 +282,10 @@ def moe_ffn_bwd_dx_dw(d, dg, du, w_gate, w_up, tiles, num_tiles, dxs, xs, act, d
     _call("moe_ffn_bwd_dx_dw", ctypes.byref(d), _ptr(dg), _ptr(du), _ptr(w_gate), _ptr(w_up), _ptr(tiles),
           _ptr(num_tiles), _ptr(dxs), _ptr(xs), _ptr(act), _ptr(dys), _ptr(offsets), _ptr(dw_gate), _ptr(dw_up),
           _ptr(dw_down), _stream(stream))
+
+
+def moe_route_meta(d, x, w_r, logit_bias, capacity, topk_idx, gates, sorted_flat, inv, counts, offsets, tiles,
+                   num_tiles, ws, stream=None):
+    _call("moe_route_meta", ctypes.byref(d), _ptr(x), _ptr(w_r), _ptr(logit_bias), int(capacity), _ptr(topk_idx),
+          _ptr(gates), _ptr(sorted_flat), _ptr(inv), _ptr(counts), _ptr(offsets), _ptr(tiles), _ptr(num_tiles),
+          _ptr(ws), _nbytes(ws), _stream(stream))

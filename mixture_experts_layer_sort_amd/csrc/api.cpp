@@ -92,6 +92,7 @@ size_t moe_workspace_bytes(const moe_dims* d, int32_t entry) {
     case MOE_ENTRY_ROUTE_BWD_AUX: return moe_launch::route_bwd_aux_ws(D);
     case MOE_ENTRY_SHARED_FFN: return is_shared(D) ? moe_launch::shared_ffn_ws(D) : size_t(-1);
     case MOE_ENTRY_SHARED_FFN_BWD: return is_shared(D) ? moe_launch::shared_ffn_bwd_ws(D) : size_t(-1);
+    case MOE_ENTRY_ROUTE_META: return moe_launch::route_meta_ws(D);
     default: return size_t(-1);
   }
 }
@@ -103,6 +104,21 @@ int moe_route(const moe_dims* d, const void* x, const void* w_r, const float* lo
   if (logit_bias != nullptr && !aligned16(logit_bias)) return MOE_EINVAL;
   if (D.N == 0) return MOE_OK;
   return from_hip(moe_launch::route(D, x, w_r, logit_bias, topk_idx, gates, stream));
+}
+
+int moe_route_meta(const moe_dims* d, const void* x, const void* w_r, const float* logit_bias, int32_t capacity,
+                   int32_t* topk_idx, float* gates, int32_t* sorted_flat, int32_t* inv, int32_t* counts,
+                   int32_t* offsets, int32_t* tiles, int32_t* num_tiles, void* ws, size_t ws_bytes,
+                   hipStream_t stream) {
+  MOE_CHECK_DIMS(d, D);
+  if (!ptrs_ok(x, w_r, topk_idx, gates, sorted_flat, inv, counts, offsets, tiles, num_tiles)) return MOE_EINVAL;
+  if (logit_bias != nullptr && !aligned16(logit_bias)) return MOE_EINVAL;
+  if (capacity < 0) return MOE_EINVAL;
+  if (D.N == 0) return MOE_OK;
+  const size_t need = moe_launch::route_meta_ws(D);
+  if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return MOE_EWORKSPACE;
+  return from_hip(moe_launch::route_meta(D, x, w_r, logit_bias, capacity, topk_idx, gates, sorted_flat, inv, counts,
+                                         offsets, tiles, num_tiles, ws, stream));
 }
 
 int moe_permute_meta_capacity(const moe_dims* d, const int32_t* topk_idx, int32_t capacity, int32_t* sorted_flat,

@@ -143,8 +143,16 @@ struct Dims {
 int64_t max_tiles(const Dims& d);
 size_t route_bwd_chunks(const Dims& d);
 
+// hist (optional, [ceil(N / 32)][E]): each 32-token block's histogram of
+// the chosen experts.
 hipError_t route(const Dims& d, const void* x, const void* w_r, const float* bias, int32_t* topk, float* gates,
-                 hipStream_t s);
+                 hipStream_t s, int32_t* hist = nullptr);
+// route + permute_meta (with a capacity; INT32_MAX: dropless), fused into
+// two launches when the block histograms are small enough.
+size_t route_meta_ws(const Dims& d);
+hipError_t route_meta(const Dims& d, const void* x, const void* w_r, const float* bias, int32_t capacity,
+                      int32_t* topk, float* gates, int32_t* sorted_flat, int32_t* inv, int32_t* counts,
+                      int32_t* offsets, int32_t* tiles, int32_t* num_tiles, void* ws, hipStream_t s);
 hipError_t permute_meta(const Dims& d, const int32_t* topk, int32_t capacity, int32_t* sorted_flat, int32_t* inv,
                         int32_t* counts, int32_t* offsets, int32_t* tiles, int32_t* num_tiles, void* ws,
                         hipStream_t s);

@@ -37,9 +37,10 @@ constexpr int route_hc() {
 // logits.  Called by a whole wave; lane k < K writes slot k of token n.
 // Each lane holds experts lane, lane+64, lane+128, lane+192; NaN logits rank
 // last; K rounds of a wave-wide arg-max pick the winners.
+// lhist (LDS, optional): the chosen experts are counted into lhist[e].
 __device__ __forceinline__ void wave_topk_gates(const float* __restrict__ lg, const float* __restrict__ bias, int E,
                                                 int K, int64_t n, int32_t* __restrict__ topk,
-                                                float* __restrict__ gates) {
+                                                float* __restrict__ gates, int* lhist = nullptr) {
   const int lane = lane_id();
   float v[4];
   int id[4];
@@ -97,6 +98,7 @@ __device__ __forceinline__ void wave_topk_gates(const float* __restrict__ lg, co
       if (k == lane) { zk = z[k]; ek = sel_e[k]; }
     topk[n * K + lane] = ek;
     gates[n * K + lane] = zk / s;
+    if (lhist) atomicAdd(&lhist[ek], 1);
   }
 }
 
@@ -139,11 +141,14 @@ __device__ __forceinline__ void probs_epilogue(float* lg, int LP, int rows, int6
   }
 }
 
+// hist (optional, [gridDim.x][E]): this block's histogram of the chosen
+// experts (integer LDS atomics: the counts do not depend on their order).
 template <typename T, int EPT>
 __global__ __launch_bounds__(256) void k_route(const T* __restrict__ x, const T* __restrict__ w_r,
                                                const float* __restrict__ bias, int32_t* __restrict__ topk,
                                                float* __restrict__ gates, int N, int H, int E, int K,
-                                               float* __restrict__ probs, float* __restrict__ part) {
+                                               float* __restrict__ probs, float* __restrict__ part,
+                                               int32_t* __restrict__ hist) {
   constexpr int EP = 8 * EPT;  // padded experts
   constexpr int HC = route_hc<EPT>();
   constexpr int V = Vec16<T>::n;
@@ -153,6 +158,10 @@ __global__ __launch_bounds__(256) void k_route(const T* __restrict__ x, const T*
   float* xs_t = smem;                        // [HC][32]   x chunk, transposed
   float* w_l = xs_t + HC * kRouteTok;        // [HC][EP]   W_r chunk
   float* lg = smem;                          // [32][EP+1] logits, reuses the staging space after the h loop
+  constexpr int HC_ = HC;
+  constexpr int LG_FLOATS = (HC_ * kRouteTok + HC_ * EP) > kRouteTok * (EP + 1) ? (HC_ * kRouteTok + HC_ * EP)
+                                                                                 : kRouteTok * (EP + 1);
+  int* lhist = reinterpret_cast<int*>(smem + LG_FLOATS);  // [E] past the staging space
 
   const int tid = threadIdx.x;
   const int t = tid & 31;   // token within the block
@@ -237,13 +246,21 @@ __global__ __launch_bounds__(256) void k_route(const T* __restrict__ x, const T*
     probs_epilogue<256>(lg, EP + 1, min(kRouteTok, N - n0), n0, E, nullptr, probs, part + (int64_t)blockIdx.x * E);
     return;
   }
+  if (hist) {
+    for (int e = tid; e < E; e += 256) lhist[e] = 0;
+    __syncthreads();
+  }
   // top-K: wave w handles tokens w*8 .. w*8+7
   const int w = tid >> 6;
   for (int q = 0; q < kRouteTok / 4; ++q) {
     const int tt = w * (kRouteTok / 4) + q;
     const int n = n0 + tt;
     if (n >= N) break;  // uniform across the wave
-    wave_topk_gates(lg + tt * (EP + 1), nullptr, E, K, n, topk, gates);
+    wave_topk_gates(lg + tt * (EP + 1), nullptr, E, K, n, topk, gates, hist ? lhist : nullptr);
+  }
+  if (hist) {
+    __syncthreads();
+    for (int e = tid; e < E; e += 256) hist[(int64_t)blockIdx.x * E + e] = lhist[e];
   }
 }
 
@@ -255,7 +272,7 @@ __global__ __launch_bounds__(256) void k_route(const T* __restrict__ x, const T*
 // outputs of token n.
 __device__ __forceinline__ void lane_topk_gates(const float* __restrict__ lg, const float* __restrict__ bias, int E,
                                                 int K, int64_t n, int32_t* __restrict__ topk,
-                                                float* __restrict__ gates) {
+                                                float* __restrict__ gates, int* lhist = nullptr) {
   float tv[MOE_MAX_TOPK];
   int te[MOE_MAX_TOPK];
 #pragma unroll
@@ -291,6 +308,7 @@ __device__ __forceinline__ void lane_topk_gates(const float* __restrict__ lg, co
     if (k < K) {
       topk[n * K + k] = te[k];
       gates[n * K + k] = z[k] / s;
+      if (lhist) atomicAdd(&lhist[te[k]], 1);
     }
 }
 
@@ -307,7 +325,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_route_mma(const bf16_t* __re
                                                              const float* __restrict__ bias,
                                                              int32_t* __restrict__ topk, float* __restrict__ gates,
                                                              int N, int H, int E, int K, float* __restrict__ probs,
-                                                             float* __restrict__ part) {
+                                                             float* __restrict__ part, int32_t* __restrict__ hist) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int n0 = blockIdx.x * C::BM;
   const int rows = min(C::BM, N - n0);
@@ -333,10 +351,23 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_route_mma(const bf16_t* __re
   __syncthreads();
   if (probs) {  // load-balancing loss: full softmax instead of the top-K
     probs_epilogue<C::NT>(lg, LP, rows, n0, E, bias, probs, part + (int64_t)blockIdx.x * E);
-  } else if (E <= 64) {
-    for (int tt = threadIdx.x; tt < rows; tt += C::NT) lane_topk_gates(lg + tt * LP, bias, E, K, n0 + tt, topk, gates);
+    return;
+  }
+  // block histogram of the chosen experts, past the logits in LDS
+  int* lhist = reinterpret_cast<int*>(lds + C::LDS) - MOE_MAX_EXPERTS;
+  if (hist) {
+    for (int e = threadIdx.x; e < E; e += C::NT) lhist[e] = 0;
+    __syncthreads();
+  }
+  int* lh = hist ? lhist : nullptr;
+  if (E <= 64) {
+    for (int tt = threadIdx.x; tt < rows; tt += C::NT) lane_topk_gates(lg + tt * LP, bias, E, K, n0 + tt, topk, gates, lh);
   } else {
-    for (int tt = w; tt < rows; tt += C::NW) wave_topk_gates(lg + tt * LP, bias, E, K, n0 + tt, topk, gates);
+    for (int tt = w; tt < rows; tt += C::NW) wave_topk_gates(lg + tt * LP, bias, E, K, n0 + tt, topk, gates, lh);
+  }
+  if (hist) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += C::NT) hist[(int64_t)blockIdx.x * E + e] = lhist[e];
   }
 }
 
@@ -347,8 +378,12 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_route_mma(const bf16_t* __re
 // 9.1 vs 10.7 us (H = 512, E = 8) and 53.6 vs 56.6 us (H = 2048, E = 64).
 using RouteCfg128 = moe_mma::TileCfg<32, 128, 1, 4, 4, 64, 2>;
 using RouteCfg256 = moe_mma::TileCfg<32, 256, 1, 4, 2, 64, 2>;
-static_assert(RouteCfg128::BM * (RouteCfg128::BN + 1) * 4 <= RouteCfg128::LDS, "logits fit the staging space");
-static_assert(RouteCfg256::BM * (RouteCfg256::BN + 1) * 4 <= RouteCfg256::LDS, "logits fit the staging space");
+static_assert(RouteCfg128::BM * (RouteCfg128::BN + 1) * 4 + MOE_MAX_EXPERTS * 4 <= RouteCfg128::LDS,
+              "logits and the block histogram fit the staging space");
+static_assert(RouteCfg256::BM * (RouteCfg256::BN + 1) * 4 + MOE_MAX_EXPERTS * 4 <= RouteCfg256::LDS,
+              "logits and the block histogram fit the staging space");
+static_assert(RouteCfg128::BM == 32 && RouteCfg256::BM == 32 && kRouteTok == 32,
+              "every router path has 32-token blocks (the routing metadata reads their histograms)");
 
 // dlogits, dense [N, E]: one thread per element, plus the load-balancing
 // loss term when aux.probs is set.  With planes (bf16 path),
@@ -526,27 +561,28 @@ __global__ __launch_bounds__(256) void k_route_bwd_reduce(const float* __restric
 
 template <typename T, int EPT>
 hipError_t launch_route_t(const moe_launch::Dims& d, const void* x, const void* w_r, const float* bias, int32_t* topk,
-                          float* gates, hipStream_t s, float* probs, float* part) {
+                          float* gates, hipStream_t s, float* probs, float* part, int32_t* hist) {
   constexpr int EP = 8 * EPT;
   constexpr int HC = route_hc<EPT>();
   constexpr size_t stage = HC * kRouteTok + HC * EP, logits = kRouteTok * (EP + 1);
-  size_t lds = sizeof(float) * (stage > logits ? stage : logits);
+  size_t lds = sizeof(float) * (stage > logits ? stage : logits) + sizeof(int) * MOE_MAX_EXPERTS;
   int grid = int((d.N + kRouteTok - 1) / kRouteTok);
   hipLaunchKernelGGL((k_route<T, EPT>), dim3(grid), dim3(256), lds, s, static_cast<const T*>(x),
                      static_cast<const T*>(w_r), bias, topk, gates, int(d.N), int(d.H), int(d.E), int(d.K), probs,
-                     part);
+                     part, hist);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_route(const moe_launch::Dims& d, const void* x, const void* w_r, const float* bias, int32_t* topk,
-                        float* gates, hipStream_t s, float* probs = nullptr, float* part = nullptr) {
-  if (d.E <= 8) return launch_route_t<T, 1>(d, x, w_r, bias, topk, gates, s, probs, part);
-  if (d.E <= 16) return launch_route_t<T, 2>(d, x, w_r, bias, topk, gates, s, probs, part);
-  if (d.E <= 32) return launch_route_t<T, 4>(d, x, w_r, bias, topk, gates, s, probs, part);
-  if (d.E <= 64) return launch_route_t<T, 8>(d, x, w_r, bias, topk, gates, s, probs, part);
-  if (d.E <= 128) return launch_route_t<T, 16>(d, x, w_r, bias, topk, gates, s, probs, part);
-  return launch_route_t<T, 32>(d, x, w_r, bias, topk, gates, s, probs, part);
+                        float* gates, hipStream_t s, float* probs = nullptr, float* part = nullptr,
+                        int32_t* hist = nullptr) {
+  if (d.E <= 8) return launch_route_t<T, 1>(d, x, w_r, bias, topk, gates, s, probs, part, hist);
+  if (d.E <= 16) return launch_route_t<T, 2>(d, x, w_r, bias, topk, gates, s, probs, part, hist);
+  if (d.E <= 32) return launch_route_t<T, 4>(d, x, w_r, bias, topk, gates, s, probs, part, hist);
+  if (d.E <= 64) return launch_route_t<T, 8>(d, x, w_r, bias, topk, gates, s, probs, part, hist);
+  if (d.E <= 128) return launch_route_t<T, 16>(d, x, w_r, bias, topk, gates, s, probs, part, hist);
+  return launch_route_t<T, 32>(d, x, w_r, bias, topk, gates, s, probs, part, hist);
 }
 
 // Load-balancing loss value: P_e = (sum of the block partials) / N, f_e =
@@ -608,13 +644,13 @@ namespace moe_launch {
 
 template <class C>
 hipError_t route_mma(const Dims& d, const void* x, const void* w_r, const float* bias, int32_t* topk, float* gates,
-                     hipStream_t s, float* probs = nullptr, float* part = nullptr) {
+                     hipStream_t s, float* probs = nullptr, float* part = nullptr, int32_t* hist = nullptr) {
   hipError_t st = moe_mma::allow_lds<k_route_mma<C>>(C::LDS);
   if (st != hipSuccess) return st;
   const unsigned grid = unsigned((d.N + C::BM - 1) / C::BM);
   hipLaunchKernelGGL(k_route_mma<C>, dim3(grid), dim3(C::NT), C::LDS, s, static_cast<const moe::bf16_t*>(x),
                      static_cast<const moe::bf16_t*>(w_r), bias, topk, gates, int(d.N), int(d.H), int(d.E), int(d.K),
-                     probs, part);
+                     probs, part, hist);
   return hipGetLastError();
 }
 
@@ -622,12 +658,12 @@ hipError_t route_mma(const Dims& d, const void* x, const void* w_r, const float*
 static bool router_mma(const Dims& d) { return d.dtype == MOE_BF16 && d.E % 8 == 0; }
 
 hipError_t route(const Dims& d, const void* x, const void* w_r, const float* bias, int32_t* topk, float* gates,
-                 hipStream_t s) {
+                 hipStream_t s, int32_t* hist) {
   if (router_mma(d))
-    return d.E <= 128 ? route_mma<RouteCfg128>(d, x, w_r, bias, topk, gates, s)
-                      : route_mma<RouteCfg256>(d, x, w_r, bias, topk, gates, s);
-  if (d.dtype == MOE_BF16) return launch_route<moe::bf16_t>(d, x, w_r, bias, topk, gates, s);
-  return launch_route<float>(d, x, w_r, bias, topk, gates, s);
+    return d.E <= 128 ? route_mma<RouteCfg128>(d, x, w_r, bias, topk, gates, s, nullptr, nullptr, hist)
+                      : route_mma<RouteCfg256>(d, x, w_r, bias, topk, gates, s, nullptr, nullptr, hist);
+  if (d.dtype == MOE_BF16) return launch_route<moe::bf16_t>(d, x, w_r, bias, topk, gates, s, nullptr, nullptr, hist);
+  return launch_route<float>(d, x, w_r, bias, topk, gates, s, nullptr, nullptr, hist);
 }
 
 // Token chunks of the dW_r partial sums: one per kRbTok tokens, fewer when

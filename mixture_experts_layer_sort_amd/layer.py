@@ -4,7 +4,7 @@
 through PyTorch, which here only supplies memory and streams) and runs the
 layer through the C ABI:
 
-  forward : moe_route -> moe_permute_meta -> moe_permute -> moe_expert_ffn
+  forward : moe_route_meta (moe_route + moe_permute_meta) -> moe_permute -> moe_expert_ffn
             (moe_ffn_gate_up, moe_ffn_down) -> moe_combine; without a backward,
             moe_ffn_gate_up_gather replaces moe_permute + moe_ffn_gate_up
   backward: moe_combine_bwd -> moe_route_bwd -> moe_expert_ffn_bwd
@@ -61,6 +61,7 @@ class MoELayerRunner:
         self.tiles = torch.empty((max(1, mt) * 3,), dtype=i32, device=dev)
         self.num_tiles = torch.empty((1,), dtype=i32, device=dev)
         self.meta_ws = self._ws(L.MOE_ENTRY_PERMUTE_META)
+        self.route_meta_ws = self._ws(L.MOE_ENTRY_ROUTE_META)
         # without a backward nothing reads xs after gate/up: the gather is
         # fused into gate/up's row loads and xs is never materialised
         self.gather_fused = (not backward) and N * H < 2 ** 31
@@ -154,11 +155,14 @@ class MoELayerRunner:
                 shared_done.record(side)
         stream = main
         if topk is None:
-            self.route(x, w_r, bias, stream)
+            # router and routing metadata in two launches
+            L.moe_route_meta(self.d, x, w_r, bias, 2 ** 31 - 1 if self.capacity is None else self.capacity,
+                             self.topk, self.gates, self.sorted_flat, self.inv, self.counts, self.offsets, self.tiles,
+                             self.num_tiles, self.route_meta_ws, stream)
         else:
             self.topk.copy_(topk)
             self.gates.copy_(gates)
-        self.meta(stream=stream)
+            self.meta(stream=stream)
         if self.gather_fused:
             L.moe_ffn_gate_up_gather(self.d, x, self.sorted_flat, w_gate, w_up, self.tiles, self.num_tiles, self.g,
                                      self.u, self.act, stream)

@@ -203,3 +203,32 @@ def test_shared_weight_gradient_split(lib, N, H, Fs, S):
     nb = L.moe_workspace_bytes(ds, L.MOE_ENTRY_SHARED_FFN_BWD)
     part = 3 * S * H * Fs * 4 if S > 1 else 0
     assert nb - nf == (S + 1) * 4 + (-(S + 1) * 4) % 16 + part
+
+
+def test_route_meta_entry_validates_on_the_host(lib):
+    lb = L.lib()
+    d = D(N=64, E=8)
+    need = L.moe_workspace_bytes(d, L.MOE_ENTRY_ROUTE_META)
+    assert need == 2 * 8 * 4                      # two 32-token blocks x 8 experts
+    f9 = [FAKE] * 8
+    assert lb.moe_route_meta(ctypes.byref(d), FAKE, FAKE, None, -1, *f9, FAKE, need, None) == L.MOE_EINVAL
+    assert lb.moe_route_meta(ctypes.byref(d), FAKE, FAKE, None, 5, *f9, FAKE, need - 4, None) == L.MOE_EWORKSPACE
+    assert lb.moe_route_meta(ctypes.byref(d), FAKE, None, None, 5, *f9, FAKE, need, None) == L.MOE_EINVAL
+    assert lb.moe_route_meta(ctypes.byref(d), FAKE, FAKE, FAKE + 4, 5, *f9, FAKE, need, None) == L.MOE_EINVAL
+    d0 = D(N=0)
+    assert lb.moe_route_meta(ctypes.byref(d0), FAKE, FAKE, None, 0, *f9, None, 0, None) == L.MOE_OK
+
+
+@pytest.mark.parametrize("N,E,K,fused", [(16384, 8, 2, True), (16384, 64, 6, True), (8192, 256, 8, False),
+                                         (16384, 128, 2, False), (32, 1, 1, True)])
+def test_route_meta_workspace_follows_the_fusion_rule(lib, N, E, K, fused):
+    """Fused while ceil(N/32) * E <= 32768 (the block histograms); else the
+    unfused metadata's workspace."""
+    d = D(N=N, E=E, K=K)
+    got = L.moe_workspace_bytes(d, L.MOE_ENTRY_ROUTE_META)
+    blocks = -(-N // 32)
+    assert (blocks * E <= 32768) == fused
+    if fused:
+        assert got == blocks * E * 4
+    else:
+        assert got == L.moe_workspace_bytes(d, L.MOE_ENTRY_PERMUTE_META)
