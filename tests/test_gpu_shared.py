@@ -169,3 +169,18 @@ def test_shared_expert_with_binding_capacity():
     ref.update(ob)
     for name, t in dict(y=y, **g).items():
         assert_close(name, t, ref[name], "bf16", band=bd.get(name))
+
+
+def test_forward_only_runner_with_shared_expert_equals_training_forward():
+    """Without a backward the shared expert keeps no G/U (g_save = u_save =
+    NULL) and the routed gather is fused into gate/up; y is the same bytes."""
+    cfg, Fs = TEST_CONFIGS["t_ragged"], 512
+    cpu, dev = gpu_inputs(cfg, 17)
+    ws = tuple(w.cuda() for w in make_shared_weights(cfg, 17, Fs))
+    f = _runner(cfg, Fs, backward=False)
+    t = _runner(cfg, Fs)
+    assert f.g_s is None and f.gather_fused
+    yf = f.forward(dev["x"], dev["w_r"], dev["w_gate"], dev["w_up"], dev["w_down"], dev["bias"], shared=ws)
+    yt = t.forward(dev["x"], dev["w_r"], dev["w_gate"], dev["w_up"], dev["w_down"], dev["bias"], shared=ws)
+    sync()
+    assert torch.equal(yf.view(torch.uint8), yt.view(torch.uint8))

@@ -138,3 +138,33 @@ def test_merged_dx_dw_launch_equals_separate_launches(cfg, monkeypatch):
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), name
     # and the runner's own backward (merged launch) wrote the same dW
     assert torch.equal(outs[0][1].view(torch.uint8), r.dw_gate.view(torch.uint8))
+
+
+@pytest.mark.parametrize("cfg", [TEST_CONFIGS["t_skew"], TEST_CONFIGS["t_ragged"], TEST_CONFIGS["t_f32"]],
+                         ids=lambda c: c.name)
+def test_grouped_entry_points_equal_the_single_gemm_calls(cfg, monkeypatch):
+    """moe_expert_ffn (gate/up + down) and moe_expert_ffn_bwd (dA, then dX
+    and dW) give the same bytes as the per-GEMM calls the layer runner
+    makes, on poisoned outputs."""
+    from mixture_experts_layer_sort_amd import _lib as L
+    from mixture_experts_layer_sort_amd.layer import MoELayerRunner
+    monkeypatch.delenv("MOE_GEMM_TILES", raising=False)
+    cpu, dev = gpu_inputs(cfg, 22, with_dy=True)
+    r = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, "cuda")
+    r.forward(dev["x"], dev["w_r"], dev["w_gate"], dev["w_up"], dev["w_down"], dev["bias"])
+    r.backward(dev["dy"])
+    sync()
+    nk = int(r.offsets[-1].item())
+    poison = lambda t: torch.full_like(t, float("nan"))
+    g, u, a, ys = (poison(t) for t in (r.g, r.u, r.act, r.ys))
+    L.moe_expert_ffn(r.d, r.xs, dev["w_gate"], dev["w_up"], dev["w_down"], r.tiles, r.num_tiles, g, u, a, ys)
+    dg, du, dxs = (poison(t) for t in (r.dg, r.du, r.dxs))
+    dwg, dwu, dwd = (poison(t) for t in (r.dw_gate, r.dw_up, r.dw_down))
+    L.moe_expert_ffn_bwd(r.d, r.dys, r.xs, dev["w_gate"], dev["w_up"], dev["w_down"], r.g, r.u, r.act, r.offsets,
+                         r.tiles, r.num_tiles, dg, du, dxs, dwg, dwu, dwd)
+    sync()
+    for name, got, ref in (("G", g, r.g), ("U", u, r.u), ("A", a, r.act), ("ys", ys, r.ys), ("dG", dg, r.dg),
+                           ("dU", du, r.du), ("dxs", dxs, r.dxs)):
+        assert torch.equal(got[:nk].view(torch.uint8), ref[:nk].view(torch.uint8)), name
+    for name, got, ref in (("dw_gate", dwg, r.dw_gate), ("dw_up", dwu, r.dw_up), ("dw_down", dwd, r.dw_down)):
+        assert torch.equal(got.view(torch.uint8), ref.view(torch.uint8)), name
