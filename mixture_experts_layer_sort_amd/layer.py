@@ -247,32 +247,57 @@ class MoELayerRunner:
 
 
 class MoEFunction(torch.autograd.Function):
-    """y = MoE(x) with gradients for x, W_r, W_gate, W_up, W_down.
+    """y = MoE(x) with gradients for x, W_r, W_gate, W_up, W_down and, with a
+    shared expert, W_gate_s, W_up_s, W_down_s.
 
     Weight gradients are computed in float32 by the library and returned in
     the weights' dtype (autograd requires it); use MoELayerRunner directly to
-    keep them in float32.
+    keep them in float32.  With aux_alpha set, the Switch load-balancing loss
+    is returned as a second output that carries no autograd edge: its
+    gradient is added to the router's in the backward as if aux_grad * loss
+    were part of the training loss (aux_grad is a constant, so no device
+    value is read back to the host).
     """
 
     @staticmethod
-    def forward(ctx, x, w_r, w_gate, w_up, w_down, K: int, bias=None):
+    def forward(ctx, x, w_r, w_gate, w_up, w_down, w_gate_s, w_up_s, w_down_s, K: int, bias, capacity, aux_alpha,
+                aux_grad):
         N, H = x.shape
         E = w_r.shape[1]
         F = w_gate.shape[2]
-        r = MoELayerRunner(N, H, F, E, K, x.dtype, x.device, backward=True)
+        shared = None if w_gate_s is None else (w_gate_s.contiguous(), w_up_s.contiguous(), w_down_s.contiguous())
+        r = MoELayerRunner(N, H, F, E, K, x.dtype, x.device, backward=True, aux_alpha=aux_alpha, capacity=capacity,
+                           shared_ffn=None if shared is None else shared[0].shape[1])
         y = r.forward(x.contiguous(), w_r.contiguous(), w_gate.contiguous(), w_up.contiguous(), w_down.contiguous(),
-                      bias)
+                      bias, shared=shared)
         ctx.runner = r
-        return y.clone()
+        ctx.aux_grad = aux_grad
+        aux = r.aux_loss.clone() if aux_alpha is not None else torch.zeros((1,), dtype=torch.float32,
+                                                                             device=x.device)
+        ctx.mark_non_differentiable(aux)
+        return y.clone(), aux
 
     @staticmethod
-    def backward(ctx, dy):
-        g = ctx.runner.backward(dy.contiguous())
+    def backward(ctx, dy, _daux):
         r = ctx.runner
-        return (g["dx"].clone(), g["dw_r"].to(r.dtype), g["dw_gate"].to(r.dtype), g["dw_up"].to(r.dtype),
-                g["dw_down"].to(r.dtype), None, None)
+        g = r.backward(dy.contiguous(), aux_grad=ctx.aux_grad)
+        cast = lambda t: t.to(r.dtype)
+        shared = ((cast(g["dw_gate_s"]), cast(g["dw_up_s"]), cast(g["dw_down_s"])) if r.shared_ffn is not None
+                  else (None, None, None))
+        return ((g["dx"].clone(), cast(g["dw_r"]), cast(g["dw_gate"]), cast(g["dw_up"]), cast(g["dw_down"])) + shared
+                + (None,) * 5)
 
 
-def moe_layer(x, w_r, w_gate, w_up, w_down, K: int, bias=None):
-    """Functional form of the layer with autograd support."""
-    return MoEFunction.apply(x, w_r, w_gate, w_up, w_down, K, bias)
+def moe_layer(x, w_r, w_gate, w_up, w_down, K: int, bias=None, *, capacity: Optional[int] = None,
+              shared=None, aux_alpha: Optional[float] = None, aux_grad: float = 1.0):
+    """Functional form of the layer with autograd support.
+
+    shared = (W_gate_s [H,Fs], W_up_s [H,Fs], W_down_s [Fs,H]) adds a shared
+    expert; capacity caps the rows per expert (token dropping); aux_alpha
+    turns on the Switch load-balancing loss.  Returns y, or (y, aux_loss)
+    when aux_alpha is set.
+    """
+    ws = (None, None, None) if shared is None else tuple(shared)
+    y, aux = MoEFunction.apply(x, w_r, w_gate, w_up, w_down, ws[0], ws[1], ws[2], K, bias, capacity, aux_alpha,
+                               aux_grad)
+    return (y, aux) if aux_alpha is not None else y
