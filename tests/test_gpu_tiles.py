@@ -168,3 +168,42 @@ def test_grouped_entry_points_equal_the_single_gemm_calls(cfg, monkeypatch):
         assert torch.equal(got[:nk].view(torch.uint8), ref[:nk].view(torch.uint8)), name
     for name, got, ref in (("dw_gate", dwg, r.dw_gate), ("dw_up", dwu, r.dw_up), ("dw_down", dwd, r.dw_down)):
         assert torch.equal(got.view(torch.uint8), ref.view(torch.uint8)), name
+
+
+@pytest.mark.parametrize("cfg", [TEST_CONFIGS["t_skew"], TEST_CONFIGS["t_bigtile"], TEST_CONFIGS["t_f32"]],
+                         ids=lambda c: c.name)
+def test_separate_dx_and_dw_entries(cfg, monkeypatch):
+    """moe_ffn_bwd_dx and moe_ffn_bwd_dw called on their own: dW is the same
+    bytes as the merged launch (same 256 x 256 kernel); dX, whose tile shape
+    follows the per-stage choice, is checked against the oracle's dxs for
+    the same dG, dU."""
+    from mixture_experts_layer_sort_amd import _lib as L
+    from mixture_experts_layer_sort_amd.layer import MoELayerRunner
+    monkeypatch.delenv("MOE_GEMM_TILES", raising=False)
+    cpu, dev = gpu_inputs(cfg, 23, with_dy=True)
+    r = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, "cuda")
+    r.forward(dev["x"], dev["w_r"], dev["w_gate"], dev["w_up"], dev["w_down"], dev["bias"])
+    r.backward(dev["dy"])
+    sync()
+    nk = int(r.offsets[-1].item())
+    dxs = torch.full_like(r.dxs, float("nan"))
+    dwg, dwu, dwd = (torch.full_like(t, float("nan")) for t in (r.dw_gate, r.dw_up, r.dw_down))
+    L.moe_ffn_bwd_dx(r.d, r.dg, r.du, dev["w_gate"], dev["w_up"], r.tiles, r.num_tiles, dxs)
+    L.moe_ffn_bwd_dw(r.d, r.xs, r.act, r.dys, r.dg, r.du, r.offsets, dwg, dwu, dwd)
+    sync()
+    for name, got, ref in (("dw_gate", dwg, r.dw_gate), ("dw_up", dwu, r.dw_up), ("dw_down", dwd, r.dw_down)):
+        assert torch.equal(got.view(torch.uint8), ref.view(torch.uint8)), name
+    # dxs = dG W_gate^T + dU W_up^T per expert, from the device's own dG, dU
+    dg, du = O.as_f64(r.dg[:nk]), O.as_f64(r.du[:nk])
+    wg, wu = O.as_f64(cpu["w_gate"]), O.as_f64(cpu["w_up"])
+    offs = r.offsets.cpu().numpy()
+    ref = np.zeros((nk, cfg.H))
+    for e in range(cfg.E):
+        a, b = offs[e], offs[e + 1]
+        ref[a:b] = dg[a:b] @ wg[e].T + du[a:b] @ wu[e].T
+    got = O.as_f64(dxs[:nk])
+    if cfg.dtype == "f32":
+        assert np.max(np.abs(got - ref)) <= 1e-4
+    else:
+        # one bf16 rounding (half a unit: 2^-9 relative) plus the fp32 summation order
+        assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-3), "dxs"
