@@ -80,6 +80,8 @@ def parse():
                    help="token-dropping variant: expert capacity ceil(cf * N * K / E), overflow dropped")
     p.add_argument("--shared-ffn", type=int, default=None,
                    help="add a shared expert of this intermediate size that every token passes through")
+    p.add_argument("--dw-gather", action="store_true",
+                   help="weight gradients read the x rows through sorted_flat: no grouped copy xs (less memory)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain 1 GiB streaming copy (for scaling HBM byte counters) and exit")
     return p.parse_args()
@@ -205,7 +207,7 @@ def main():
         shared_cpu = make_shared_weights(cfg, args.seed, Fs)
         shared = tuple(w.to(dev) for w in shared_cpu)
     r = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, dev, backward=cfg.backward,
-                       aux_alpha=aux, capacity=capacity, shared_ffn=Fs)
+                       aux_alpha=aux, capacity=capacity, shared_ffn=Fs, dw_gather=args.dw_gather)
     d = r.d
     x, w_r, wg, wu, wd, bias, dy = (inp[k] for k in ("x", "w_r", "w_gate", "w_up", "w_down", "bias", "dy"))
     stream = torch.cuda.current_stream()
@@ -236,15 +238,19 @@ def main():
                       (lambda st: L.moe_route_bwd_aux(d, x, r.topk, r.gates, r.dgates, r.probs, r.counts, aux,
                                                       r.dlogits, r.dw_r, r.route_ws, st))),
         "dact": lambda st: L.moe_ffn_bwd_dact(d, r.dys, wd, r.g, r.u, r.tiles, r.num_tiles, r.dg, r.du, st),
-        "dx_dw": lambda st: L.moe_ffn_bwd_dx_dw(d, r.dg, r.du, wg, wu, r.tiles, r.num_tiles, r.dxs, r.xs, r.act,
-                                                r.dys, r.offsets, r.dw_gate, r.dw_up, r.dw_down, st),
+        "dx_dw": ((lambda st: L.moe_ffn_bwd_dx_dw_gather(d, r.dg, r.du, wg, wu, r.tiles, r.num_tiles, r.dxs, x,
+                                                         r.sorted_flat, r.act, r.dys, r.offsets, r.dw_gate, r.dw_up,
+                                                         r.dw_down, st)) if r.dw_gather else
+                  (lambda st: L.moe_ffn_bwd_dx_dw(d, r.dg, r.du, wg, wu, r.tiles, r.num_tiles, r.dxs, r.xs, r.act,
+                                                  r.dys, r.offsets, r.dw_gate, r.dw_up, r.dw_down, st))),
         "permute_bwd": ((lambda st: permute_bwd(d, r.dxs, r.inv, r.topk, r.dlogits, w_r, r.dx, r.perm_ws, st))
                         if shared is None else
                         (lambda st: L.moe_permute_bwd_add(d, r.dxs, r.inv, r.topk, r.dlogits, w_r, aux is not None,
                                                           r.dx_s, r.dx, r.perm_ws, st))),
     }
     fwd_names = ((["shared_ffn"] if shared is not None else []) + ["route_meta"] +
-                 ([] if r.gather_fused else ["permute"]) + ["gate_up", "down", "combine"] +
+                 (["permute", "gate_up"] if not r.gather_fused else
+                  ["gate_up"] + (["permute"] if r.xs is not None else [])) + ["down", "combine"] +
                  (["aux_loss"] if aux is not None else []))
     bwd_names = ((["combine_bwd", "route_bwd"] + (["shared_bwd"] if shared is not None else []) +
                   ["dact", "dx_dw", "permute_bwd"]) if cfg.backward else [])
@@ -395,6 +401,7 @@ def main():
                    "backward": cfg.backward, "parallelism": "single GPU", "maxvio": round(maxvio, 4),
                    "load_balancing_loss_alpha": aux,
                    "gather_fused_into_gate_up": r.gather_fused,
+                   "gather_fused_into_dw": r.dw_gather,
                    "capacity": capacity,
                    "dropped_rows": cfg.NK - kept_rows,
                    "shared_expert_ffn": Fs,

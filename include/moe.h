@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 7
+#define MOE_ABI_VERSION 8
 /* Rows per tile of the grouped-GEMM tile list built by moe_permute_meta. */
 #define MOE_TILE_M 256
 #define MOE_MAX_EXPERTS 256
@@ -278,6 +278,19 @@ int moe_ffn_bwd_dx_dw(const moe_dims* d, const void* dg, const void* du, const v
                       const int32_t* tiles, const int32_t* num_tiles, void* dxs, const void* xs, const void* act,
                       const void* dys, const int32_t* offsets, float* dw_gate, float* dw_up, float* dw_down,
                       hipStream_t stream);
+
+/* moe_ffn_bwd_dx_dw with the grouped rows read from the token rows: x [N,H]
+ * replaces xs and row i of the grouped order is x[sorted_flat[i] / K] in
+ * dW_gate = xs_e^T.dG_e and dW_up = xs_e^T.dU_e (the gather of moe_permute
+ * done inside the weight-gradient loads, MegaBlocks section 2.1, so a
+ * training step needs no xs).  Same bytes as moe_permute + moe_ffn_bwd_dx_dw.
+ *   sorted_flat [NK] from moe_permute_meta; other arguments as
+ *   moe_ffn_bwd_dx_dw. */
+int moe_ffn_bwd_dx_dw_gather(const moe_dims* d, const void* dg, const void* du, const void* w_gate,
+                             const void* w_up, const int32_t* tiles, const int32_t* num_tiles, void* dxs,
+                             const void* x, const int32_t* sorted_flat, const void* act, const void* dys,
+                             const int32_t* offsets, float* dw_gate, float* dw_up, float* dw_down,
+                             hipStream_t stream);
 
 /* Backward of the gather plus the router's input gradient:
  *   dx[n] = sum_k dxs[inv[n*K+k]] + sum_k dlogits[n,e_k] * W_r[:,e_k],

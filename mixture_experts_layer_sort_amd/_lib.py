@@ -69,6 +69,7 @@ SIGNATURES = {
     "moe_permute_bwd_add": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
     "moe_ffn_bwd_dx_dw": (ctypes.c_int, [_DP] + [_P] * 14 + [_P]),
     "moe_route_meta": (ctypes.c_int, [_DP, _P, _P, _P, _I32] + [_P] * 9 + [_SZ, _P]),
+    "moe_ffn_bwd_dx_dw_gather": (ctypes.c_int, [_DP] + [_P] * 15 + [_P]),
 }
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -289,3 +290,10 @@ def moe_route_meta(d, x, w_r, logit_bias, capacity, topk_idx, gates, sorted_flat
     _call("moe_route_meta", ctypes.byref(d), _ptr(x), _ptr(w_r), _ptr(logit_bias), int(capacity), _ptr(topk_idx),
           _ptr(gates), _ptr(sorted_flat), _ptr(inv), _ptr(counts), _ptr(offsets), _ptr(tiles), _ptr(num_tiles),
           _ptr(ws), _nbytes(ws), _stream(stream))
+
+
+def moe_ffn_bwd_dx_dw_gather(d, dg, du, w_gate, w_up, tiles, num_tiles, dxs, x, sorted_flat, act, dys, offsets,
+                             dw_gate, dw_up, dw_down, stream=None):
+    _call("moe_ffn_bwd_dx_dw_gather", ctypes.byref(d), _ptr(dg), _ptr(du), _ptr(w_gate), _ptr(w_up), _ptr(tiles),
+          _ptr(num_tiles), _ptr(dxs), _ptr(x), _ptr(sorted_flat), _ptr(act), _ptr(dys), _ptr(offsets),
+          _ptr(dw_gate), _ptr(dw_up), _ptr(dw_down), _stream(stream))

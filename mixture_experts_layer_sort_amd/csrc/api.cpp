@@ -240,7 +240,8 @@ int moe_ffn_bwd_dw(const moe_dims* d, const void* xs, const void* act, const voi
   MOE_CHECK_DIMS(d, D);
   if (!ptrs_ok(xs, act, dys, dg, du, offsets, dw_gate, dw_up, dw_down)) return MOE_EINVAL;
   if (D.N == 0) return MOE_OK;
-  return from_hip(moe_launch::ffn_bwd_dw(D, xs, act, dys, dg, du, offsets, dw_gate, dw_up, dw_down, stream));
+  return from_hip(
+      moe_launch::ffn_bwd_dw(D, xs, nullptr, act, dys, dg, du, offsets, dw_gate, dw_up, dw_down, stream));
 }
 
 int moe_ffn_bwd_dx_dw(const moe_dims* d, const void* dg, const void* du, const void* w_gate, const void* w_up,
@@ -251,8 +252,22 @@ int moe_ffn_bwd_dx_dw(const moe_dims* d, const void* dg, const void* du, const v
   if (!ptrs_ok(dg, du, w_gate, w_up, tiles, num_tiles, dxs, xs, act, dys, offsets, dw_gate, dw_up, dw_down))
     return MOE_EINVAL;
   if (D.N == 0) return MOE_OK;
-  return from_hip(moe_launch::ffn_bwd_dx_dw(D, dg, du, w_gate, w_up, tiles, num_tiles, dxs, xs, act, dys, offsets,
+  return from_hip(moe_launch::ffn_bwd_dx_dw(D, dg, du, w_gate, w_up, tiles, num_tiles, dxs, xs, nullptr, act, dys, offsets,
                                             dw_gate, dw_up, dw_down, stream));
+}
+
+int moe_ffn_bwd_dx_dw_gather(const moe_dims* d, const void* dg, const void* du, const void* w_gate,
+                             const void* w_up, const int32_t* tiles, const int32_t* num_tiles, void* dxs,
+                             const void* x, const int32_t* sorted_flat, const void* act, const void* dys,
+                             const int32_t* offsets, float* dw_gate, float* dw_up, float* dw_down,
+                             hipStream_t stream) {
+  MOE_CHECK_DIMS(d, D);
+  if (!ptrs_ok(dg, du, w_gate, w_up, tiles, num_tiles, dxs, x, sorted_flat, act, dys, offsets, dw_gate, dw_up,
+               dw_down))
+    return MOE_EINVAL;
+  if (D.N == 0) return MOE_OK;
+  return from_hip(moe_launch::ffn_bwd_dx_dw(D, dg, du, w_gate, w_up, tiles, num_tiles, dxs, x, sorted_flat, act, dys,
+                                            offsets, dw_gate, dw_up, dw_down, stream));
 }
 
 int moe_expert_ffn_bwd(const moe_dims* d, const void* dys, const void* xs, const void* w_gate, const void* w_up,
@@ -266,7 +281,7 @@ int moe_expert_ffn_bwd(const moe_dims* d, const void* dys, const void* xs, const
   if (D.N == 0) return MOE_OK;
   int st = from_hip(moe_launch::ffn_bwd_dact(D, dys, w_down, g_save, u_save, tiles, num_tiles, dg, du, stream));
   if (st != MOE_OK) return st;
-  return from_hip(moe_launch::ffn_bwd_dx_dw(D, dg, du, w_gate, w_up, tiles, num_tiles, dxs, xs, act, dys, offsets,
+  return from_hip(moe_launch::ffn_bwd_dx_dw(D, dg, du, w_gate, w_up, tiles, num_tiles, dxs, xs, nullptr, act, dys, offsets,
                                             dw_gate, dw_up, dw_down, stream));
 }
 

@@ -188,12 +188,17 @@ hipError_t ffn_bwd_dact(const Dims& d, const void* dys, const void* wd, const vo
                         const int32_t* tiles, const int32_t* num_tiles, void* dg, void* du, hipStream_t s);
 hipError_t ffn_bwd_dx(const Dims& d, const void* dg, const void* du, const void* wg, const void* wu,
                       const int32_t* tiles, const int32_t* num_tiles, void* dxs, hipStream_t s);
-hipError_t ffn_bwd_dw(const Dims& d, const void* xs, const void* a, const void* dys, const void* dg, const void* du,
-                      const int32_t* offsets, float* dwg, float* dwu, float* dwd, hipStream_t s);
+// sorted_flat non-null: xs is the token matrix x and dW_gate / dW_up read
+// row i of the grouped order as x[sorted_flat[i] / K]; null: xs is the
+// grouped matrix.
+hipError_t ffn_bwd_dw(const Dims& d, const void* xs, const int32_t* sorted_flat, const void* a, const void* dys,
+                      const void* dg, const void* du, const int32_t* offsets, float* dwg, float* dwu, float* dwd,
+                      hipStream_t s);
 // ffn_bwd_dx and ffn_bwd_dw together (one launch for bf16).
 hipError_t ffn_bwd_dx_dw(const Dims& d, const void* dg, const void* du, const void* wg, const void* wu,
-                         const int32_t* tiles, const int32_t* num_tiles, void* dxs, const void* xs, const void* a,
-                         const void* dys, const int32_t* offsets, float* dwg, float* dwu, float* dwd, hipStream_t s);
+                         const int32_t* tiles, const int32_t* num_tiles, void* dxs, const void* xs,
+                         const int32_t* sorted_flat, const void* a, const void* dys, const int32_t* offsets,
+                         float* dwg, float* dwu, float* dwd, hipStream_t s);
 
 // Shared expert: a dense SwiGLU expert over all N tokens (dims E = K = 1,
 // F = its intermediate size).  The workspace holds its tile list, the row

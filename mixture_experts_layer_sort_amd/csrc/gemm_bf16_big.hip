@@ -41,7 +41,10 @@
 //
 // Determinism: every output element has exactly one owning workgroup and its
 // K loop runs in ascending order.
+#include <type_traits>
+
 #include "common.h"
+
 #include "mma_lds.h"
 
 namespace {
@@ -406,12 +409,15 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_dx(const bf16_t* __restrict_
 // The contraction runs over the expert's rows in ascending 64-row steps;
 // experts without rows write exact zeros.
 // b: this workgroup's block index within the dW part of the launch.
-template <class C>
+// GATHER: xs is the token matrix x and row i of the grouped order is read as
+// x[sorted_flat[i] / K] (dW_gate and dW_up gather their rows on load).
+template <class C, bool GATHER = false>
 __device__ __forceinline__ void dw_tile(char* lds, int b, const bf16_t* __restrict__ xs,
                                         const bf16_t* __restrict__ act, const bf16_t* __restrict__ dys,
                                         const bf16_t* __restrict__ dg, const bf16_t* __restrict__ du,
                                         const int32_t* __restrict__ offsets, float* __restrict__ dwg,
-                                        float* __restrict__ dwu, float* __restrict__ dwd, int H, int F, int E) {
+                                        float* __restrict__ dwu, float* __restrict__ dwd, int H, int F, int E,
+                                        const int32_t* __restrict__ sorted_flat = nullptr, int K = 1) {
   const int tf = (F + C::BN - 1) / C::BN, th2 = (H + C::BN - 1) / C::BN;
   const int tpe = ((H + C::BM - 1) / C::BM) * tf;    // output tiles of problems 0 and 1 per expert
   const int tpe2 = ((F + C::BM - 1) / C::BM) * th2;  // ... of problem 2
@@ -445,7 +451,18 @@ __device__ __forceinline__ void dw_tile(char* lds, int b, const bf16_t* __restri
   const bf16_t* r_base = Rm + (int64_t)r0 * Q + nt * C::BN;
   Acc<C> acc;
   const int nk = (cnt + C::BK - 1) / C::BK;
-  if constexpr (C::REG) {
+  if constexpr (GATHER) {
+    static_assert(C::REG, "the gathered rows use the register-staged loop");
+    if (prob < 2)
+      k_loop_reg<C, true, true>(lds, acc, nk,
+                                MnGather<C::BM, C::BK, C::NT>(xs + mt * C::BM, sorted_flat + r0, K, P, prow, cnt),
+                                MnOp<C::BN, C::BK, C::NT>(r_base, r_base, C::BN, Q, qcol, cnt), wm, wn,
+                                cnt - (nk - 1) * C::BK);
+    else
+      k_loop_reg<C, true, true>(lds, acc, nk, MnOp<C::BM, C::BK, C::NT>(l_base, l_base, C::BM, P, prow, cnt),
+                                MnOp<C::BN, C::BK, C::NT>(r_base, r_base, C::BN, Q, qcol, cnt), wm, wn,
+                                cnt - (nk - 1) * C::BK);
+  } else if constexpr (C::REG) {
     k_loop_reg<C, true, true>(lds, acc, nk, MnOp<C::BM, C::BK, C::NT>(l_base, l_base, C::BM, P, prow, cnt),
                               MnOp<C::BN, C::BK, C::NT>(r_base, r_base, C::BN, Q, qcol, cnt), wm, wn,
                               cnt - (nk - 1) * C::BK);
@@ -476,14 +493,15 @@ __device__ __forceinline__ void dw_tile(char* lds, int b, const bf16_t* __restri
     }
 }
 
-template <class C>
+template <class C, bool GATHER = false>
 __global__ __launch_bounds__(C::NT, C::MINB) void k_dw(const bf16_t* __restrict__ xs, const bf16_t* __restrict__ act,
                                               const bf16_t* __restrict__ dys, const bf16_t* __restrict__ dg,
                                               const bf16_t* __restrict__ du, const int32_t* __restrict__ offsets,
                                               float* __restrict__ dwg, float* __restrict__ dwu,
-                                              float* __restrict__ dwd, int H, int F, int E) {
+                                              float* __restrict__ dwd, int H, int F, int E,
+                                              const int32_t* __restrict__ sorted_flat, int K) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  dw_tile<C>(lds, blockIdx.x, xs, act, dys, dg, du, offsets, dwg, dwu, dwd, H, F, E);
+  dw_tile<C, GATHER>(lds, blockIdx.x, xs, act, dys, dg, du, offsets, dwg, dwu, dwd, H, F, E, sorted_flat, K);
 }
 
 // dX and dW in one launch.  Both read only dG and dU (plus xs, A, dys and the
@@ -493,18 +511,19 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_dw(const bf16_t* __restrict_
 // dw_grid is a multiple of 8 * kXcdRun, so both parts keep their XCD mapping.
 // CW: the weight-gradient tiles' shape; CX: the dX tiles' shape (same block
 // size; the launch gets the larger LDS of the two).
-template <class CW, class CX>
+template <class CW, class CX, bool GATHER = false>
 __global__ __launch_bounds__(CW::NT, CW::MINB) void k_dx_dw(
     const bf16_t* __restrict__ dg, const bf16_t* __restrict__ du, const bf16_t* __restrict__ wg,
     const bf16_t* __restrict__ wu, const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles,
     bf16_t* __restrict__ dxs, const bf16_t* __restrict__ xs, const bf16_t* __restrict__ act,
     const bf16_t* __restrict__ dys, const int32_t* __restrict__ offsets, float* __restrict__ dwg,
-    float* __restrict__ dwu, float* __restrict__ dwd, int H, int F, int E, int dw_grid) {
+    float* __restrict__ dwu, float* __restrict__ dwd, int H, int F, int E, int dw_grid,
+    const int32_t* __restrict__ sorted_flat, int K) {
   static_assert(CW::NT == CX::NT, "one block size");
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int b = blockIdx.x;
   if (b < dw_grid)
-    dw_tile<CW>(lds, b, xs, act, dys, dg, du, offsets, dwg, dwu, dwd, H, F, E);
+    dw_tile<CW, GATHER>(lds, b, xs, act, dys, dg, du, offsets, dwg, dwu, dwd, H, F, E, sorted_flat, K);
   else
     dx_tile<CX>(lds, b - dw_grid, dg, du, wg, wu, tiles, num_tiles, dxs, H, F);
 }
@@ -602,40 +621,52 @@ static unsigned dw_grid(const Dims& d) {
   return unsigned((total + win - 1) / win * win);
 }
 
+// sorted_flat non-null: xs is x and dW_gate / dW_up gather their rows
 template <class C>
-static hipError_t dw_t(const Dims& d, const void* xs, const void* a, const void* dys, const void* dg, const void* du,
-                       const int32_t* offsets, float* dwg, float* dwu, float* dwd, hipStream_t s) {
-  hipError_t st = allow_lds<k_dw<C>>(C::LDS);
-  if (st != hipSuccess) return st;
-  const unsigned grid = dw_grid<C>(d);
-  hipLaunchKernelGGL(k_dw<C>, dim3(grid), dim3(C::NT), C::LDS, s, static_cast<const bf16_t*>(xs),
-                     static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(dys), static_cast<const bf16_t*>(dg),
-                     static_cast<const bf16_t*>(du), offsets, dwg, dwu, dwd, int(d.H), int(d.F), int(d.E));
-  return hipGetLastError();
+static hipError_t dw_t(const Dims& d, const void* xs, const int32_t* sorted_flat, const void* a, const void* dys,
+                       const void* dg, const void* du, const int32_t* offsets, float* dwg, float* dwu, float* dwd,
+                       hipStream_t s) {
+  auto run = [&](auto gather) -> hipError_t {
+    constexpr bool G = decltype(gather)::value;
+    hipError_t st = allow_lds<k_dw<C, G>>(C::LDS);
+    if (st != hipSuccess) return st;
+    const unsigned grid = dw_grid<C>(d);
+    hipLaunchKernelGGL((k_dw<C, G>), dim3(grid), dim3(C::NT), C::LDS, s, static_cast<const bf16_t*>(xs),
+                       static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(dys),
+                       static_cast<const bf16_t*>(dg), static_cast<const bf16_t*>(du), offsets, dwg, dwu, dwd,
+                       int(d.H), int(d.F), int(d.E), sorted_flat, int(d.K));
+    return hipGetLastError();
+  };
+  return sorted_flat ? run(std::true_type{}) : run(std::false_type{});
 }
 
-hipError_t ffn_bwd_dw_big(const Dims& d, const void* xs, const void* a, const void* dys, const void* dg,
-                           const void* du, const int32_t* offsets, float* dwg, float* dwu, float* dwd, hipStream_t s) {
-  return dw_t<Big>(d, xs, a, dys, dg, du, offsets, dwg, dwu, dwd, s);
+hipError_t ffn_bwd_dw_big(const Dims& d, const void* xs, const int32_t* sorted_flat, const void* a, const void* dys,
+                          const void* dg, const void* du, const int32_t* offsets, float* dwg, float* dwu, float* dwd,
+                          hipStream_t s) {
+  return dw_t<Big>(d, xs, sorted_flat, a, dys, dg, du, offsets, dwg, dwu, dwd, s);
 }
 
 hipError_t ffn_bwd_dx_dw_big(const Dims& d, const void* dg, const void* du, const void* wg, const void* wu,
-                             const int32_t* tiles, const int32_t* num_tiles, void* dxs, const void* xs, const void* a,
-                             const void* dys, const int32_t* offsets, float* dwg, float* dwu, float* dwd,
-                             hipStream_t s) {
+                             const int32_t* tiles, const int32_t* num_tiles, void* dxs, const void* xs,
+                             const int32_t* sorted_flat, const void* a, const void* dys, const int32_t* offsets,
+                             float* dwg, float* dwu, float* dwd, hipStream_t s) {
   using CW = Big;
   using CX = DxInMerged;
   constexpr int lds_bytes = CW::LDS > CX::LDS ? CW::LDS : CX::LDS;
-  hipError_t st = allow_lds<k_dx_dw<CW, CX>>(lds_bytes);
-  if (st != hipSuccess) return st;
-  const unsigned gw = dw_grid<CW>(d);
-  const unsigned gx = grid8(max_tiles(d) * CX::SUB * ((d.H + CX::BN - 1) / CX::BN));
-  hipLaunchKernelGGL((k_dx_dw<CW, CX>), dim3(gw + gx), dim3(CW::NT), lds_bytes, s, static_cast<const bf16_t*>(dg),
-                     static_cast<const bf16_t*>(du), static_cast<const bf16_t*>(wg), static_cast<const bf16_t*>(wu),
-                     tiles, num_tiles, static_cast<bf16_t*>(dxs), static_cast<const bf16_t*>(xs),
-                     static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(dys), offsets, dwg, dwu, dwd,
-                     int(d.H), int(d.F), int(d.E), int(gw));
-  return hipGetLastError();
+  auto run = [&](auto gather) -> hipError_t {
+    constexpr bool G = decltype(gather)::value;
+    hipError_t st = allow_lds<k_dx_dw<CW, CX, G>>(lds_bytes);
+    if (st != hipSuccess) return st;
+    const unsigned gw = dw_grid<CW>(d);
+    const unsigned gx = grid8(max_tiles(d) * CX::SUB * ((d.H + CX::BN - 1) / CX::BN));
+    hipLaunchKernelGGL((k_dx_dw<CW, CX, G>), dim3(gw + gx), dim3(CW::NT), lds_bytes, s,
+                       static_cast<const bf16_t*>(dg), static_cast<const bf16_t*>(du), static_cast<const bf16_t*>(wg),
+                       static_cast<const bf16_t*>(wu), tiles, num_tiles, static_cast<bf16_t*>(dxs),
+                       static_cast<const bf16_t*>(xs), static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(dys),
+                       offsets, dwg, dwu, dwd, int(d.H), int(d.F), int(d.E), int(gw), sorted_flat, int(d.K));
+    return hipGetLastError();
+  };
+  return sorted_flat ? run(std::true_type{}) : run(std::false_type{});
 }
 
 // 128 x 256 register-staged tiles
@@ -657,9 +688,10 @@ hipError_t ffn_bwd_dx_midr(const Dims& d, const void* dg, const void* du, const 
                            const int32_t* tiles, const int32_t* num_tiles, void* dxs, hipStream_t s) {
   return dx_t<MidR>(d, dg, du, wg, wu, tiles, num_tiles, dxs, s);
 }
-hipError_t ffn_bwd_dw_midr(const Dims& d, const void* xs, const void* a, const void* dys, const void* dg,
-                           const void* du, const int32_t* offsets, float* dwg, float* dwu, float* dwd, hipStream_t s) {
-  return dw_t<MidR>(d, xs, a, dys, dg, du, offsets, dwg, dwu, dwd, s);
+hipError_t ffn_bwd_dw_midr(const Dims& d, const void* xs, const int32_t* sorted_flat, const void* a, const void* dys,
+                           const void* dg, const void* du, const int32_t* offsets, float* dwg, float* dwu, float* dwd,
+                           hipStream_t s) {
+  return dw_t<MidR>(d, xs, sorted_flat, a, dys, dg, du, offsets, dwg, dwu, dwd, s);
 }
 
 }  // namespace moe_launch

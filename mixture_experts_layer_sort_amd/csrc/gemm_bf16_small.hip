@@ -116,6 +116,19 @@ struct LoadMN {
         v[j] = make_uint4(0, 0, 0, 0);
     }
   }
+  // k row k is token row rows_src[k] / K of x (base = x + the tile's column)
+  __device__ __forceinline__ void load_gather(const bf16_t* base, const int32_t* rows_src, int K, int64_t ld,
+                                              int k_valid) {
+    const int mc = mn_mc(), kg = mn_kg();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int k = kg * 4 + j;
+      if (k < k_valid)
+        v[j] = *reinterpret_cast<const uint4*>(base + (int64_t)(rows_src[k] / K) * ld + mc * 8);
+      else
+        v[j] = make_uint4(0, 0, 0, 0);
+    }
+  }
   __device__ __forceinline__ void store(char* lds) const {
     const int mc = mn_mc(), kg = mn_kg();
     uint32_t w[4][4];
@@ -425,11 +438,13 @@ __global__ __launch_bounds__(NT, 2) void k_dx(const bf16_t* __restrict__ dg, con
 //   problem 1: dW_up[e]   = xs_e^T . dU_e   [H, F]
 //   problem 2: dW_down[e] = A_e^T  . dys_e  [F, H]
 // The contraction runs over the expert's rows in ascending 64-row steps.
+// gsrc non-null: xs is x and the rows of dW_gate / dW_up are x[gsrc[i] / K]
 __global__ __launch_bounds__(NT, 2) void k_dw(const bf16_t* __restrict__ xs, const bf16_t* __restrict__ act,
                                                const bf16_t* __restrict__ dys, const bf16_t* __restrict__ dg,
                                                const bf16_t* __restrict__ du, const int32_t* __restrict__ offsets,
                                                float* __restrict__ dwg, float* __restrict__ dwu,
-                                               float* __restrict__ dwd, int H, int F, int E) {
+                                               float* __restrict__ dwd, int H, int F, int E,
+                                               const int32_t* __restrict__ gsrc, int K) {
   __shared__ __attribute__((aligned(16))) char lds[kLds2];
   const int tpe = (H / BM) * (F / BN);  // output tiles per expert and problem
   // experts largest first, each expert's 3 * tpe tiles consecutive, dealt to
@@ -459,9 +474,17 @@ __global__ __launch_bounds__(NT, 2) void k_dw(const bf16_t* __restrict__ xs, con
   f32x16_t acc[2][2];
   zero_acc(acc);
   LoadMN la, lb;
+  const bool gather = gsrc != nullptr && prob < 2;
+  const bf16_t* x_cols = xs + mt * BM;
+  auto load_l = [&](int kt, int kv) {
+    if (gather)
+      la.load_gather(x_cols, gsrc + r0 + kt * BK, K, P, kv);
+    else
+      la.load(l_base + (int64_t)kt * BK * P, P, kv);
+  };
   const int nk = (cnt + BK - 1) / BK;
   if (nk > 0) {
-    la.load(l_base, P, cnt);
+    load_l(0, cnt);
     lb.load(r_base, Q, cnt);
   }
   for (int kt = 0; kt < nk; ++kt) {
@@ -470,7 +493,7 @@ __global__ __launch_bounds__(NT, 2) void k_dw(const bf16_t* __restrict__ xs, con
     __syncthreads();
     if (kt + 1 < nk) {
       const int kv = cnt - (kt + 1) * BK;
-      la.load(l_base + (int64_t)(kt + 1) * BK * P, P, kv);
+      load_l(kt + 1, kv);
       lb.load(r_base + (int64_t)(kt + 1) * BK * Q, Q, kv);
     }
     mma_tile(lds, lds + kTileBytes, acc, wm, wn);
@@ -525,14 +548,16 @@ hipError_t ffn_bwd_dx_small(const Dims& d, const void* dg, const void* du, const
   return hipGetLastError();
 }
 
-hipError_t ffn_bwd_dw_small(const Dims& d, const void* xs, const void* a, const void* dys, const void* dg,
-                           const void* du, const int32_t* offsets, float* dwg, float* dwu, float* dwd, hipStream_t s) {
+// sorted_flat non-null: xs is x and dW_gate / dW_up gather their rows
+hipError_t ffn_bwd_dw_small(const Dims& d, const void* xs, const int32_t* sorted_flat, const void* a, const void* dys,
+                            const void* dg, const void* du, const int32_t* offsets, float* dwg, float* dwu,
+                            float* dwd, hipStream_t s) {
   const int64_t total = 3 * d.E * (d.H / BM) * (d.F / BN);
   const int64_t win = 8 * kXcdRun;
   unsigned grid = unsigned((total + win - 1) / win * win);
   hipLaunchKernelGGL(k_dw, dim3(grid), dim3(NT), 0, s, static_cast<const bf16_t*>(xs), static_cast<const bf16_t*>(a),
                      static_cast<const bf16_t*>(dys), static_cast<const bf16_t*>(dg), static_cast<const bf16_t*>(du),
-                     offsets, dwg, dwu, dwd, int(d.H), int(d.F), int(d.E));
+                     offsets, dwg, dwu, dwd, int(d.H), int(d.F), int(d.E), sorted_flat, int(d.K));
   return hipGetLastError();
 }
 

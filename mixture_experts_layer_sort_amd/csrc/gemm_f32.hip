@@ -110,11 +110,13 @@ __global__ __launch_bounds__(256) void k_dx_f32(const float* __restrict__ dg, co
   }
 }
 
+// gsrc non-null: xs is x and row r of dW_gate / dW_up's rows is x[gsrc[r] / K]
 __global__ __launch_bounds__(256) void k_dw_f32(const float* __restrict__ xs, const float* __restrict__ act,
                                                  const float* __restrict__ dys, const float* __restrict__ dg,
                                                  const float* __restrict__ du, const int32_t* __restrict__ offsets,
                                                  float* __restrict__ dwg, float* __restrict__ dwu,
-                                                 float* __restrict__ dwd, int H, int F, int E) {
+                                                 float* __restrict__ dwd, int H, int F, int E,
+                                                 const int32_t* __restrict__ gsrc, int K) {
   const int tpe = (H / TN) * (F / TN);
   const int prob = blockIdx.x / (E * tpe);
   const int rem = blockIdx.x % (E * tpe);
@@ -136,7 +138,11 @@ __global__ __launch_bounds__(256) void k_dw_f32(const float* __restrict__ xs, co
   for (int idx = threadIdx.x; idx < TN * TN; idx += 256) {
     const int p = mt * TN + idx / TN, q = nt * TN + idx % TN;
     float s = 0.f;
-    for (int r = r0; r < r1; ++r) s = fmaf(L[(int64_t)r * P + p], R[(int64_t)r * Q + q], s);
+    const bool gather = gsrc != nullptr && prob < 2;
+    for (int r = r0; r < r1; ++r) {
+      const int64_t lr = gather ? (int64_t)(gsrc[r] / K) : r;
+      s = fmaf(L[lr * P + p], R[(int64_t)r * Q + q], s);
+    }
     out[(int64_t)p * Q + q] = s;
   }
 }
@@ -165,16 +171,16 @@ hipError_t ffn_bwd_dact_midr(const Dims&, const void*, const void*, const void*,
                              const int32_t*, void*, void*, hipStream_t);
 hipError_t ffn_bwd_dx_midr(const Dims&, const void*, const void*, const void*, const void*, const int32_t*,
                            const int32_t*, void*, hipStream_t);
-hipError_t ffn_bwd_dw_midr(const Dims&, const void*, const void*, const void*, const void*, const void*,
-                           const int32_t*, float*, float*, float*, hipStream_t);
+hipError_t ffn_bwd_dw_midr(const Dims&, const void*, const int32_t*, const void*, const void*, const void*,
+                           const void*, const int32_t*, float*, float*, float*, hipStream_t);
 MOE_BF16_SHAPE(ffn_bwd_dx, const void*, const void*, const void*, const void*, const int32_t*, const int32_t*, void*,
                hipStream_t)
-MOE_BF16_SHAPE(ffn_bwd_dw, const void*, const void*, const void*, const void*, const void*, const int32_t*, float*,
-               float*, float*, hipStream_t)
+MOE_BF16_SHAPE(ffn_bwd_dw, const void*, const int32_t*, const void*, const void*, const void*, const void*,
+               const int32_t*, float*, float*, float*, hipStream_t)
 #undef MOE_BF16_SHAPE
 hipError_t ffn_bwd_dx_dw_big(const Dims&, const void*, const void*, const void*, const void*, const int32_t*,
-                             const int32_t*, void*, const void*, const void*, const void*, const int32_t*, float*,
-                             float*, float*, hipStream_t);
+                             const int32_t*, void*, const void*, const int32_t*, const void*, const void*,
+                             const int32_t*, float*, float*, float*, hipStream_t);
 
 // Which bf16 tile shape each stage uses.  The 256 x 256 tiles (one workgroup
 // per CU: 4 waves of 128 x 128 with register-staged loads, or, for dA, 8
@@ -268,18 +274,20 @@ hipError_t ffn_bwd_dx(const Dims& d, const void* dg, const void* du, const void*
   return hipGetLastError();
 }
 
-hipError_t ffn_bwd_dw(const Dims& d, const void* xs, const void* a, const void* dys, const void* dg, const void* du,
-                      const int32_t* offsets, float* dwg, float* dwu, float* dwd, hipStream_t s) {
+hipError_t ffn_bwd_dw(const Dims& d, const void* xs, const int32_t* sorted_flat, const void* a, const void* dys,
+                      const void* dg, const void* du, const int32_t* offsets, float* dwg, float* dwu, float* dwd,
+                      hipStream_t s) {
   if (d.dtype == MOE_BF16)
     switch (tiles_dw(d)) {
-      case Tiles::Big: return ffn_bwd_dw_big(d, xs, a, dys, dg, du, offsets, dwg, dwu, dwd, s);
-      case Tiles::MidR: return ffn_bwd_dw_midr(d, xs, a, dys, dg, du, offsets, dwg, dwu, dwd, s);
-      default: return ffn_bwd_dw_small(d, xs, a, dys, dg, du, offsets, dwg, dwu, dwd, s);
+      case Tiles::Big: return ffn_bwd_dw_big(d, xs, sorted_flat, a, dys, dg, du, offsets, dwg, dwu, dwd, s);
+      case Tiles::MidR: return ffn_bwd_dw_midr(d, xs, sorted_flat, a, dys, dg, du, offsets, dwg, dwu, dwd, s);
+      default: return ffn_bwd_dw_small(d, xs, sorted_flat, a, dys, dg, du, offsets, dwg, dwu, dwd, s);
     }
   unsigned grid = unsigned(3 * d.E * (d.H / TN) * (d.F / TN));
   hipLaunchKernelGGL(k_dw_f32, dim3(grid), dim3(256), 0, s, static_cast<const float*>(xs),
                      static_cast<const float*>(a), static_cast<const float*>(dys), static_cast<const float*>(dg),
-                     static_cast<const float*>(du), offsets, dwg, dwu, dwd, int(d.H), int(d.F), int(d.E));
+                     static_cast<const float*>(du), offsets, dwg, dwu, dwd, int(d.H), int(d.F), int(d.E), sorted_flat,
+                     int(d.K));
   return hipGetLastError();
 }
 
@@ -289,13 +297,15 @@ hipError_t ffn_bwd_dw(const Dims& d, const void* xs, const void* a, const void* 
 // workgroups for 256 CUs); with MOE_GEMM_TILES set, the two stages run as
 // separate launches of the forced family.  float32: two launches.
 hipError_t ffn_bwd_dx_dw(const Dims& d, const void* dg, const void* du, const void* wg, const void* wu,
-                         const int32_t* tiles, const int32_t* num_tiles, void* dxs, const void* xs, const void* a,
-                         const void* dys, const int32_t* offsets, float* dwg, float* dwu, float* dwd, hipStream_t s) {
+                         const int32_t* tiles, const int32_t* num_tiles, void* dxs, const void* xs,
+                         const int32_t* sorted_flat, const void* a, const void* dys, const int32_t* offsets,
+                         float* dwg, float* dwu, float* dwd, hipStream_t s) {
   if (d.dtype == MOE_BF16 && std::getenv("MOE_GEMM_TILES") == nullptr)
-    return ffn_bwd_dx_dw_big(d, dg, du, wg, wu, tiles, num_tiles, dxs, xs, a, dys, offsets, dwg, dwu, dwd, s);
+    return ffn_bwd_dx_dw_big(d, dg, du, wg, wu, tiles, num_tiles, dxs, xs, sorted_flat, a, dys, offsets, dwg, dwu,
+                             dwd, s);
   hipError_t st = ffn_bwd_dx(d, dg, du, wg, wu, tiles, num_tiles, dxs, s);
   if (st != hipSuccess) return st;
-  return ffn_bwd_dw(d, xs, a, dys, dg, du, offsets, dwg, dwu, dwd, s);
+  return ffn_bwd_dw(d, xs, sorted_flat, a, dys, dg, du, offsets, dwg, dwu, dwd, s);
 }
 
 }  // namespace moe_launch

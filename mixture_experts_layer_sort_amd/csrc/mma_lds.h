@@ -355,6 +355,49 @@ struct MnOp {
   }
 };
 
+// MN-contiguous operand whose k rows are gathered: k row r of the
+// contraction (r from 0 over the expert's rows) is token row rows_src[r] / K
+// of x (leading dimension ld), so the weight gradients read x instead of the
+// grouped copy of its rows.  Columns as in MnOp; k rows at or past k_total
+// read the last valid row (k_loop_reg zeroes them in the A operand).
+template <int COLS, int BK, int NT>
+struct MnGather {
+  static constexpr int CPR = COLS / 8, KP = NT / CPR, N = BK / KP;
+  static_assert(NT % CPR == 0 && BK % KP == 0, "chunks split evenly over the threads");
+  const bf16_t* base;  // x + this thread's column
+  const int32_t* rows_src;
+  int K;
+  int64_t ld;
+  int k_total;
+  __device__ __forceinline__ MnGather(const bf16_t* x_cols, const int32_t* rows_src_, int K_, int64_t ld_,
+                                      int cols_valid, int k_total_)
+      : rows_src(rows_src_), K(K_), ld(ld_), k_total(k_total_) {
+    const int c = threadIdx.x % CPR;
+    const int cs = c * 8 < cols_valid ? c : (cols_valid >> 3) - 1;
+    base = x_cols + cs * 8;
+  }
+  __device__ __forceinline__ void load(u32x4_t (&v)[N], int kt) const {
+    const int k0 = threadIdx.x / CPR;
+    const int kv = k_total - kt * BK;  // valid k rows of the tile
+    int src[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int k = k0 + i * KP < kv ? k0 + i * KP : kv - 1;
+      src[i] = rows_src[kt * BK + k] / K;
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = *reinterpret_cast<const u32x4_t*>(base + (int64_t)src[i] * ld);
+  }
+  __device__ __forceinline__ void store(const u32x4_t (&v)[N], char* st, int) const {
+    const int k0 = threadIdx.x / CPR, c = threadIdx.x % CPR;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int k = k0 + i * KP;
+      *reinterpret_cast<u32x4_t*>(st + k * (COLS * 2) + ((c ^ fm(k)) << 4)) = v[i];
+    }
+  }
+};
+
 // Instruction order of one step of k_loop_reg (sched_group_barrier masks:
 // 0x008 MFMA, 0x020 VMEM read, 0x100 LDS read, 0x200 LDS write).  The
 // step's KK * MK MFMAs are the slots; after slot j come its share of

@@ -143,12 +143,12 @@ hipError_t shared_ffn_bwd(const Dims& ds, const void* x, const void* dy, const v
   if (err != hipSuccess) return err;
   Dims dc = ds;
   dc.E = sp.S;
-  if (sp.S == 1) return ffn_bwd_dw(dc, x, a, dy, dg, du, offs, dwg, dwu, dwd, s);
+  if (sp.S == 1) return ffn_bwd_dw(dc, x, nullptr, a, dy, dg, du, offs, dwg, dwu, dwd, s);
   const int64_t hf = ds.H * ds.F;
   float* p0 = reinterpret_cast<float*>(w + l.part);
   float* p1 = p0 + sp.S * hf;
   float* p2 = p1 + sp.S * hf;
-  err = ffn_bwd_dw(dc, x, a, dy, dg, du, offs, p0, p1, p2, s);
+  err = ffn_bwd_dw(dc, x, nullptr, a, dy, dg, du, offs, p0, p1, p2, s);
   if (err != hipSuccess) return err;
   const int64_t blocks = std::min<int64_t>((hf / 4 + 255) / 256, 2048);
   hipLaunchKernelGGL(k_sum_partials, dim3(unsigned(blocks), 3), dim3(256), 0, s, p0, p1, p2, dwg, dwu, dwd, hf,

@@ -4,11 +4,16 @@
 through PyTorch, which here only supplies memory and streams) and runs the
 layer through the C ABI:
 
-  forward : moe_route_meta (moe_route + moe_permute_meta) -> moe_permute -> moe_expert_ffn
-            (moe_ffn_gate_up, moe_ffn_down) -> moe_combine; without a backward,
-            moe_ffn_gate_up_gather replaces moe_permute + moe_ffn_gate_up
-  backward: moe_combine_bwd -> moe_route_bwd -> moe_expert_ffn_bwd
-            (moe_ffn_bwd_dact, moe_ffn_bwd_dx_dw) -> moe_permute_bwd
+  forward : moe_route_meta (moe_route + moe_permute_meta) -> moe_ffn_gate_up_gather
+            (the permute fused into gate/up's row loads) -> moe_permute (the
+            grouped copy xs, for the weight gradients) -> moe_ffn_down -> moe_combine
+  backward: moe_combine_bwd -> moe_route_bwd -> moe_ffn_bwd_dact ->
+            moe_ffn_bwd_dx_dw (dX and the weight gradients) -> moe_permute_bwd
+With gather=False gate/up reads xs too (moe_ffn_gate_up).  With
+dw_gather=True the weight gradients read the x rows through sorted_flat
+(moe_ffn_bwd_dx_dw_gather) and xs is never materialised: NK*H elements less
+memory, for a slower weight-gradient launch.  A forward-only runner holds no
+xs.
 
 With a shared expert, moe_shared_ffn runs beside the routed path and
 moe_combine_shared adds its output; in the backward moe_shared_ffn_bwd gives
@@ -31,12 +36,16 @@ class MoELayerRunner:
 
     def __init__(self, N: int, H: int, F: int, E: int, K: int, dtype: torch.dtype, device="cuda",
                  backward: bool = True, save_gu: Optional[bool] = None, aux_alpha: Optional[float] = None,
-                 capacity: Optional[int] = None, shared_ffn: Optional[int] = None):
+                 capacity: Optional[int] = None, shared_ffn: Optional[int] = None, gather: Optional[bool] = None,
+                 dw_gather: bool = False):
         """aux_alpha: weight of the Switch load-balancing loss; None turns it off.
         capacity: expert capacity (rows per expert, the overflow dropped);
         None is the dropless layer.  shared_ffn: intermediate size Fs of a
         shared expert every token passes through (weights passed to forward
-        as ``shared``); None: no shared expert."""
+        as ``shared``); None: no shared expert.  gather: gate/up reads the
+        grouped rows straight from x; None: whenever N*H < 2^31.  dw_gather:
+        the weight gradients read them from x as well, so xs is never
+        materialised (needs the gathered gate/up)."""
         self.N, self.H, self.F, self.E, self.K = N, H, F, E, K
         self.dtype = dtype
         self.device = torch.device(device)
@@ -62,10 +71,17 @@ class MoELayerRunner:
         self.num_tiles = torch.empty((1,), dtype=i32, device=dev)
         self.meta_ws = self._ws(L.MOE_ENTRY_PERMUTE_META)
         self.route_meta_ws = self._ws(L.MOE_ENTRY_ROUTE_META)
-        # without a backward nothing reads xs after gate/up: the gather is
-        # fused into gate/up's row loads and xs is never materialised
-        self.gather_fused = (not backward) and N * H < 2 ** 31
-        self.xs = None if self.gather_fused else torch.empty((NK, H), dtype=dtype, device=dev)
+        # the gather is fused into gate/up's row loads; the weight gradients
+        # read the grouped copy xs unless dw_gather (then xs never exists)
+        fits = N * H < 2 ** 31
+        if gather and not fits:
+            raise ValueError("gathered row loads need N*H < 2^31")
+        self.gather_fused = fits if gather is None else bool(gather)
+        if dw_gather and not self.gather_fused:
+            raise ValueError("dw_gather needs the gathered gate/up (gather and N*H < 2^31)")
+        self.dw_gather = bool(dw_gather) and backward
+        need_xs = not self.gather_fused or (backward and not self.dw_gather)
+        self.xs = torch.empty((NK, H), dtype=dtype, device=dev) if need_xs else None
         self.g = torch.empty((NK, F), dtype=dtype, device=dev) if save_gu else None
         self.u = torch.empty((NK, F), dtype=dtype, device=dev) if save_gu else None
         self.act = torch.empty((NK, F), dtype=dtype, device=dev)
@@ -166,6 +182,8 @@ class MoELayerRunner:
         if self.gather_fused:
             L.moe_ffn_gate_up_gather(self.d, x, self.sorted_flat, w_gate, w_up, self.tiles, self.num_tiles, self.g,
                                      self.u, self.act, stream)
+            if self.xs is not None:
+                L.moe_permute(self.d, x, self.sorted_flat, self.xs, stream)
         else:
             L.moe_permute(self.d, x, self.sorted_flat, self.xs, stream)
             L.moe_ffn_gate_up(self.d, self.xs, w_gate, w_up, self.tiles, self.num_tiles, self.g, self.u, self.act,
@@ -228,8 +246,13 @@ class MoELayerRunner:
         route_done = torch.cuda.Event()
         route_done.record(side)
         L.moe_ffn_bwd_dact(d, self.dys, w_down, self.g, self.u, self.tiles, self.num_tiles, self.dg, self.du, main)
-        L.moe_ffn_bwd_dx_dw(d, self.dg, self.du, w_gate, w_up, self.tiles, self.num_tiles, self.dxs, self.xs,
-                            self.act, self.dys, self.offsets, self.dw_gate, self.dw_up, self.dw_down, main)
+        if self.dw_gather:
+            L.moe_ffn_bwd_dx_dw_gather(d, self.dg, self.du, w_gate, w_up, self.tiles, self.num_tiles, self.dxs, x,
+                                       self.sorted_flat, self.act, self.dys, self.offsets, self.dw_gate, self.dw_up,
+                                       self.dw_down, main)
+        else:
+            L.moe_ffn_bwd_dx_dw(d, self.dg, self.du, w_gate, w_up, self.tiles, self.num_tiles, self.dxs, self.xs,
+                                self.act, self.dys, self.offsets, self.dw_gate, self.dw_up, self.dw_down, main)
         if side is not main:
             main.wait_event(route_done)
         if self.shared_w is None:

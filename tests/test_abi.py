@@ -157,6 +157,14 @@ def test_capacity_and_gather_entries_validate_on_the_host(lib):
     big = D(N=2 ** 21, H=1024)
     assert lb.moe_ffn_gate_up_gather(ctypes.byref(big), FAKE, FAKE, *gu, FAKE, FAKE, FAKE,
                                      None) == L.MOE_EUNSUPPORTED
+    # gathered weight gradients: null or misaligned x, null sorted_flat; N = 0 launches nothing
+    lf = lb.moe_ffn_bwd_dx_dw_gather
+    pre = [FAKE] * 7                      # dg, du, w_gate, w_up, tiles, num_tiles, dxs
+    post = [FAKE] * 6                     # act, dys, offsets, dw_gate, dw_up, dw_down
+    assert lf(ctypes.byref(d), *pre, None, FAKE, *post, None) == L.MOE_EINVAL
+    assert lf(ctypes.byref(d), *pre, FAKE, None, *post, None) == L.MOE_EINVAL
+    assert lf(ctypes.byref(d), *pre, FAKE + 2, FAKE, *post, None) == L.MOE_EINVAL
+    assert lf(ctypes.byref(d0), *pre, FAKE, FAKE, *post, None) == L.MOE_OK
 
 
 def test_shared_expert_entries_validate_on_the_host(lib):

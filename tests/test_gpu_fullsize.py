@@ -81,7 +81,8 @@ def test_default_workload_every_element():
            "dx": grads["dx"], "dw_r": grads["dw_r"], "dw_gate": grads["dw_gate"], "dw_up": grads["dw_up"],
            "dw_down": grads["dw_down"]}
     for name, t in got.items():
-        assert_close(name, t, ref[name], "bf16", band=bd.get(name))
+        if t is not None:                 # xs: gathered from x, never materialised
+            assert_close(name, t, ref[name], "bf16", band=bd.get(name))
     nt = int(r.num_tiles.item())
     from mixture_experts_layer_sort_amd import _lib as L
     assert np.array_equal(r.tiles.cpu().numpy()[:3 * nt].reshape(-1, 3),
@@ -270,7 +271,9 @@ def _property_checks(cfg, dev, r, x, grads, y):
     e = int(np.argmax(counts))
     sl = slice(int(off[e]), int(off[e + 1]))
     cols = slice(cfg.F - 128, cfg.F)
-    xs_e = to_np(r.xs[sl].cpu())
+    # the expert's rows of the grouped order, x[sorted_flat / K]
+    src = r.sorted_flat[sl].long() // cfg.K
+    xs_e = to_np(dev["x"][src].cpu())
     dG_e = to_np(r.dg[sl, cols].cpu())
     ref = xs_e.T @ dG_e
     _within(f"dW_gate[{e}] = xs_e^T dG_e (last 128 columns)", grads["dw_gate"][e][:, cols].cpu(), ref,
@@ -308,7 +311,8 @@ def test_large_ffn_bitwise_identical_across_three_runs():
     for rep in range(3):
         if rep == 1:
             for t in (r.y, r.dx, r.dw_gate, r.dw_up, r.dw_down, r.dw_r, r.xs, r.act, r.ys, r.dg, r.du):
-                t.fill_(float("nan"))
+                if t is not None:
+                    t.fill_(float("nan"))
         y = r.forward(dev["x"], dev["w_r"], dev["w_gate"], dev["w_up"], dev["w_down"], dev["bias"])
         grads = r.backward(dev["dy"])
         sync()

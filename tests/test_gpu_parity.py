@@ -31,9 +31,10 @@ def _gpu():
     _lib.lib()  # fails loudly when the HIP library is missing
 
 
-def _runner(cfg, backward=True):
+def _runner(cfg, backward=True, gather=None, dw_gather=False):
     from mixture_experts_layer_sort_amd.layer import MoELayerRunner
-    return MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, "cuda", backward=backward)
+    return MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, "cuda", backward=backward,
+                          gather=gather, dw_gather=dw_gather)
 
 
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
@@ -82,10 +83,10 @@ def test_permute_meta_bit_exact(cfg):
     assert np.array_equal(r.tiles.cpu().numpy()[:3 * nt].reshape(-1, 3), tiles)
 
 
-def _fwd_bwd(cfg, seed=0):
+def _fwd_bwd(cfg, seed=0, gather=None, dw_gather=False):
     cpu, dev = gpu_inputs(cfg, seed, with_dy=True)
     of = oracle_fwd(cfg, cpu)
-    r = _runner(cfg)
+    r = _runner(cfg, gather=gather, dw_gather=dw_gather)
     r.route(dev["x"], dev["w_r"], dev["bias"])
     sync()
     bad = assignment_mismatch(r.topk.cpu().numpy(), of, cfg.K)
@@ -102,10 +103,14 @@ def _fwd_bwd(cfg, seed=0):
     return r, of, ob, y, grads
 
 
+@pytest.mark.parametrize("mode", ["xs", "gather", "dw_gather"])
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
-def test_layer_forward_backward_matches_oracle(cfg):
-    print(f"[layer] {cfg.name}", flush=True)
-    r, of, ob, y, g = _fwd_bwd(cfg)
+def test_layer_forward_backward_matches_oracle(cfg, mode):
+    """xs: the permute writes xs and gate/up and the weight gradients read it;
+    gather: gate/up reads the rows from x, the weight gradients read xs;
+    dw_gather: both read x and xs is never materialised."""
+    print(f"[layer] {cfg.name} mode={mode}", flush=True)
+    r, of, ob, y, g = _fwd_bwd(cfg, gather=mode != "xs", dw_gather=mode == "dw_gather")
     dt = store_of(cfg)
     cpu_dy = gpu_inputs(cfg, 0, with_dy=True)[0]["dy"]
     bd = O.rounding_bands(of, ob, cpu_dy) if dt == "bf16" else {}
@@ -114,8 +119,10 @@ def test_layer_forward_backward_matches_oracle(cfg):
     got = {"xs": r.xs, "G": r.g, "U": r.u, "A": r.act, "ys": r.ys, "y": y, "dys": r.dys, "dgates": g["dgates"],
            "dlogits": g["dlogits"], "dG": r.dg, "dU": r.du, "dxs": r.dxs, "dx": g["dx"], "dw_r": g["dw_r"],
            "dw_gate": g["dw_gate"], "dw_up": g["dw_up"], "dw_down": g["dw_down"]}
+    assert (r.xs is None) == (mode == "dw_gather") and r.gather_fused == (mode != "xs")
     for name, t in got.items():
-        assert_close(name, t, ref[name], dt, band=bd.get(name))
+        if t is not None:
+            assert_close(name, t, ref[name], dt, band=bd.get(name))
     # experts without rows get exact zeros
     for e in np.where(of["counts"] == 0)[0]:
         for name in ("dw_gate", "dw_up", "dw_down"):
@@ -139,7 +146,8 @@ def test_bitwise_reproducible(cfg):
         r = _runner(cfg)
         if rep == 1:
             for name in ("y", "dx", "dw_r", "dw_gate", "dw_up", "dw_down", "dgates", "dlogits", "xs", "ys", "act"):
-                getattr(r, name).view(torch.uint8).fill_(0xFF)
+                if getattr(r, name) is not None:
+                    getattr(r, name).view(torch.uint8).fill_(0xFF)
         y = r.forward(dev["x"], dev["w_r"], dev["w_gate"], dev["w_up"], dev["w_down"], dev["bias"])
         g = r.backward(dev["dy"])
         sync()

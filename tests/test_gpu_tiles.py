@@ -82,7 +82,7 @@ def test_gate_up_gather_equals_permute_then_gate_up(cfg, tiles, monkeypatch):
     monkeypatch.setenv("MOE_GEMM_TILES", tiles)
     print(f"[gather {tiles}] {cfg.name}", flush=True)
     cpu, dev = gpu_inputs(cfg, 2)
-    r = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, "cuda")
+    r = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, "cuda", gather=False)
     r.route(dev["x"], dev["w_r"], dev["bias"])
     r.meta()
     L.moe_permute(r.d, dev["x"], r.sorted_flat, r.xs)
@@ -117,7 +117,7 @@ def test_merged_dx_dw_launch_equals_separate_launches(cfg, monkeypatch):
     monkeypatch.delenv("MOE_GEMM_TILES", raising=False)
     print(f"[dx_dw] {cfg.name}", flush=True)
     cpu, dev = gpu_inputs(cfg, 21, with_dy=True)
-    r = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, "cuda")
+    r = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, "cuda", gather=False)
     r.forward(dev["x"], dev["w_r"], dev["w_gate"], dev["w_up"], dev["w_down"], dev["bias"])
     r.backward(dev["dy"])
     sync()
@@ -150,7 +150,7 @@ def test_grouped_entry_points_equal_the_single_gemm_calls(cfg, monkeypatch):
     from mixture_experts_layer_sort_amd.layer import MoELayerRunner
     monkeypatch.delenv("MOE_GEMM_TILES", raising=False)
     cpu, dev = gpu_inputs(cfg, 22, with_dy=True)
-    r = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, "cuda")
+    r = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, "cuda", gather=False)
     r.forward(dev["x"], dev["w_r"], dev["w_gate"], dev["w_up"], dev["w_down"], dev["bias"])
     r.backward(dev["dy"])
     sync()
@@ -181,7 +181,7 @@ def test_separate_dx_and_dw_entries(cfg, monkeypatch):
     from mixture_experts_layer_sort_amd.layer import MoELayerRunner
     monkeypatch.delenv("MOE_GEMM_TILES", raising=False)
     cpu, dev = gpu_inputs(cfg, 23, with_dy=True)
-    r = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, "cuda")
+    r = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, "cuda", gather=False)
     r.forward(dev["x"], dev["w_r"], dev["w_gate"], dev["w_up"], dev["w_down"], dev["bias"])
     r.backward(dev["dy"])
     sync()
@@ -207,3 +207,33 @@ def test_separate_dx_and_dw_entries(cfg, monkeypatch):
     else:
         # one bf16 rounding (half a unit: 2^-9 relative) plus the fp32 summation order
         assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-3), "dxs"
+
+
+@pytest.mark.parametrize("tiles", [None, "256", "128x256", "128"], ids=lambda t: t or "default")
+@pytest.mark.parametrize("cfg", [TEST_CONFIGS["t_skew"], TEST_CONFIGS["t_ragged"], TEST_CONFIGS["t_f32"],
+                                 MoEConfig("t_tiles_f640", N=1500, H=384, F=640, E=3, K=2, dtype="bf16")],
+                         ids=lambda c: c.name)
+def test_gathered_weight_gradients_equal_the_xs_path(cfg, tiles, monkeypatch):
+    """moe_ffn_bwd_dx_dw_gather (dW_gate and dW_up read x[sorted_flat / K])
+    gives the same bytes as moe_permute + moe_ffn_bwd_dx_dw, for every tile
+    family and the fp32 path, on poisoned outputs."""
+    from mixture_experts_layer_sort_amd import _lib as L
+    from mixture_experts_layer_sort_amd.layer import MoELayerRunner
+    if tiles is None:
+        monkeypatch.delenv("MOE_GEMM_TILES", raising=False)
+    else:
+        monkeypatch.setenv("MOE_GEMM_TILES", tiles)
+    cpu, dev = gpu_inputs(cfg, 24, with_dy=True)
+    r = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, "cuda", gather=False)
+    r.forward(dev["x"], dev["w_r"], dev["w_gate"], dev["w_up"], dev["w_down"], dev["bias"])
+    r.backward(dev["dy"])
+    sync()
+    nk = int(r.offsets[-1].item())
+    dxs = torch.full_like(r.dxs, float("nan"))
+    dwg, dwu, dwd = (torch.full_like(t, float("nan")) for t in (r.dw_gate, r.dw_up, r.dw_down))
+    L.moe_ffn_bwd_dx_dw_gather(r.d, r.dg, r.du, dev["w_gate"], dev["w_up"], r.tiles, r.num_tiles, dxs, dev["x"],
+                               r.sorted_flat, r.act, r.dys, r.offsets, dwg, dwu, dwd)
+    sync()
+    assert torch.equal(dxs[:nk].view(torch.uint8), r.dxs[:nk].view(torch.uint8))
+    for name, got, ref in (("dw_gate", dwg, r.dw_gate), ("dw_up", dwu, r.dw_up), ("dw_down", dwd, r.dw_down)):
+        assert torch.equal(got.view(torch.uint8), ref.view(torch.uint8)), name
