@@ -327,3 +327,29 @@ def test_large_ffn_bitwise_identical_across_three_runs():
         _log(f"[determinism] run {rep} done")
     del r, dev, first
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("cfg", [BASE, SKEWED, LARGE], ids=lambda c: c.name)
+def test_gathered_weight_gradients_at_full_size(cfg):
+    """The weight gradients reading x through sorted_flat (no xs, as
+    bench.py --dw-gather runs them) give the same bytes as the default
+    launch configuration, whose results the tests above check against the
+    oracle."""
+    from mixture_experts_layer_sort_amd.layer import MoELayerRunner
+    _log(f"[dw_gather] {cfg.name}")
+    dev = make_inputs(cfg, 2, device=DEV, with_dy=True)
+    outs = []
+    for dwg in (False, True):
+        r = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, DEV, dw_gather=dwg)
+        assert (r.xs is None) == dwg
+        y = r.forward(dev["x"], dev["w_r"], dev["w_gate"], dev["w_up"], dev["w_down"], dev["bias"])
+        g = r.backward(dev["dy"])
+        sync()
+        outs.append([y.clone()] + [g[k].clone() for k in ("dx", "dw_gate", "dw_up", "dw_down", "dw_r")])
+        del r, y, g
+        torch.cuda.empty_cache()
+    for name, a, b in zip(("y", "dx", "dw_gate", "dw_up", "dw_down", "dw_r"), outs[0], outs[1]):
+        bits = torch.int32 if a.dtype == torch.float32 else torch.int16
+        assert torch.equal(a.view(bits), b.view(bits)), name
+    del dev, outs
+    torch.cuda.empty_cache()
