@@ -284,13 +284,13 @@ class MoEFunction(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, x, w_r, w_gate, w_up, w_down, w_gate_s, w_up_s, w_down_s, K: int, bias, capacity, aux_alpha,
-                aux_grad):
+                aux_grad, dw_gather):
         N, H = x.shape
         E = w_r.shape[1]
         F = w_gate.shape[2]
         shared = None if w_gate_s is None else (w_gate_s.contiguous(), w_up_s.contiguous(), w_down_s.contiguous())
         r = MoELayerRunner(N, H, F, E, K, x.dtype, x.device, backward=True, aux_alpha=aux_alpha, capacity=capacity,
-                           shared_ffn=None if shared is None else shared[0].shape[1])
+                           shared_ffn=None if shared is None else shared[0].shape[1], dw_gather=dw_gather)
         y = r.forward(x.contiguous(), w_r.contiguous(), w_gate.contiguous(), w_up.contiguous(), w_down.contiguous(),
                       bias, shared=shared)
         ctx.runner = r
@@ -308,19 +308,20 @@ class MoEFunction(torch.autograd.Function):
         shared = ((cast(g["dw_gate_s"]), cast(g["dw_up_s"]), cast(g["dw_down_s"])) if r.shared_ffn is not None
                   else (None, None, None))
         return ((g["dx"].clone(), cast(g["dw_r"]), cast(g["dw_gate"]), cast(g["dw_up"]), cast(g["dw_down"])) + shared
-                + (None,) * 5)
+                + (None,) * 6)
 
 
 def moe_layer(x, w_r, w_gate, w_up, w_down, K: int, bias=None, *, capacity: Optional[int] = None,
-              shared=None, aux_alpha: Optional[float] = None, aux_grad: float = 1.0):
+              shared=None, aux_alpha: Optional[float] = None, aux_grad: float = 1.0, dw_gather: bool = False):
     """Functional form of the layer with autograd support.
 
     shared = (W_gate_s [H,Fs], W_up_s [H,Fs], W_down_s [Fs,H]) adds a shared
     expert; capacity caps the rows per expert (token dropping); aux_alpha
-    turns on the Switch load-balancing loss.  Returns y, or (y, aux_loss)
-    when aux_alpha is set.
+    turns on the Switch load-balancing loss; dw_gather keeps no grouped copy
+    of x for the weight gradients (less memory, slower).  Returns y, or
+    (y, aux_loss) when aux_alpha is set.
     """
     ws = (None, None, None) if shared is None else tuple(shared)
     y, aux = MoEFunction.apply(x, w_r, w_gate, w_up, w_down, ws[0], ws[1], ws[2], K, bias, capacity, aux_alpha,
-                               aux_grad)
+                               aux_grad, dw_gather)
     return (y, aux) if aux_alpha is not None else y

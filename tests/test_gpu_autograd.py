@@ -1,7 +1,8 @@
 """The torch.autograd wrapper (moe_layer / MoEFunction) on the GPU: the same
 bytes as the layer runner it drives, with and without the optional parts
-(shared expert, expert capacity, load-balancing loss), and end to end
-against the CPU oracle on the tiny fp32 workload.
+(shared expert, expert capacity, load-balancing loss, weight gradients
+gathered from x), and end to end against the CPU oracle on the tiny fp32
+workload.
 """
 import numpy as np
 import pytest
@@ -43,8 +44,8 @@ def test_moe_layer_equals_the_runner(cfg, opts):
     if opts == "all":
         shared = tuple(w.cuda() for w in make_shared_weights(cfg, 41, Fs))
         C = O.capacity_of(cfg.N, cfg.K, cfg.E, 1.0)
-        kw = dict(capacity=C, shared=tuple(_leaf(w) for w in shared), aux_alpha=0.5, aux_grad=1.0)
-        rkw = dict(capacity=C, shared_ffn=Fs, aux_alpha=0.5)
+        kw = dict(capacity=C, shared=tuple(_leaf(w) for w in shared), aux_alpha=0.5, aux_grad=1.0, dw_gather=True)
+        rkw = dict(capacity=C, shared_ffn=Fs, aux_alpha=0.5, dw_gather=True)
     leaves = {k: _leaf(dev[k]) for k in ("x", "w_r", "w_gate", "w_up", "w_down")}
     out = moe_layer(leaves["x"], leaves["w_r"], leaves["w_gate"], leaves["w_up"], leaves["w_down"], cfg.K,
                     dev["bias"], **kw)

@@ -153,3 +153,26 @@ def test_capacity_metadata_at_full_size_skewed():
     _check_meta(r, of, cfg.name)
     print(f"skewed: C={C}, {int((counts > C).sum())} experts overflow, "
           f"{cfg.N * cfg.K - int(offsets[-1])} of {cfg.N * cfg.K} rows dropped", flush=True)
+
+
+@pytest.mark.parametrize("cfg,cf", [(TEST_CONFIGS["t_skew"], 1.0), (TEST_CONFIGS["t_f32"], 0.8), (BASE, 0.95)],
+                         ids=lambda v: getattr(v, "name", str(v)))
+def test_capacity_gathered_weight_gradients_equal_the_xs_path(cfg, cf):
+    """With rows dropped, the weight gradients reading x through sorted_flat
+    (only kept rows lie inside the expert ranges) give the same bytes as the
+    layer that keeps xs."""
+    from mixture_experts_layer_sort_amd.layer import MoELayerRunner
+    C = O.capacity_of(cfg.N, cfg.K, cfg.E, cf)
+    cpu, dev = gpu_inputs(cfg, 12, with_dy=True)
+    outs = []
+    for dwg in (False, True):
+        r = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, "cuda", capacity=C, dw_gather=dwg)
+        for t in (r.dw_gate, r.dw_up, r.dw_down):
+            t.fill_(float("nan"))
+        y = r.forward(dev["x"], dev["w_r"], dev["w_gate"], dev["w_up"], dev["w_down"], dev["bias"])
+        g = r.backward(dev["dy"])
+        sync()
+        assert int(r.offsets[-1].item()) < cfg.N * cfg.K, "the case must drop rows"
+        outs.append({k: v.clone() for k, v in dict(y=y, **g).items()})
+    for k, v in outs[0].items():
+        assert torch.equal(v.view(torch.uint8), outs[1][k].view(torch.uint8)), k
