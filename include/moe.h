@@ -284,8 +284,13 @@ int moe_ffn_bwd_dx_dw(const moe_dims* d, const void* dg, const void* du, const v
  * dW_gate = xs_e^T.dG_e and dW_up = xs_e^T.dU_e (the gather of moe_permute
  * done inside the weight-gradient loads, MegaBlocks section 2.1, so a
  * training step needs no xs).  Same bytes as moe_permute + moe_ffn_bwd_dx_dw.
- *   sorted_flat [NK] from moe_permute_meta; other arguments as
- *   moe_ffn_bwd_dx_dw. */
+ * It saves the NK x H xs buffer and the permute, but the launch itself is
+ * slower than the xs form (scattered row loads), so it is meant for callers
+ * short of memory.
+ *   sorted_flat [NK] from moe_permute_meta (or moe_route_meta), read only in
+ *   the expert ranges offsets[e] .. offsets[e+1], which hold no dropped row;
+ *   other arguments as moe_ffn_bwd_dx_dw.  Errors: as moe_ffn_bwd_dx_dw, plus
+ *   MOE_EINVAL for a null or misaligned x or sorted_flat. */
 int moe_ffn_bwd_dx_dw_gather(const moe_dims* d, const void* dg, const void* du, const void* w_gate,
                              const void* w_up, const int32_t* tiles, const int32_t* num_tiles, void* dxs,
                              const void* x, const int32_t* sorted_flat, const void* act, const void* dys,
