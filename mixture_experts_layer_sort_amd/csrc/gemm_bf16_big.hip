@@ -257,7 +257,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_down(const bf16_t* __restric
   Acc<C> acc;
   if constexpr (C::REG) {
     k_loop_reg<C, false, true>(lds, acc, F / C::BK, KcOp<C::BM, C::BK, C::NT>(a_base, a_base, kNoSplit, F, ti.rows),
-                               MnOp<C::BN, C::BK, C::NT>(b_base, b_base, C::BN, H, ncols, F), wm, wn);
+                               MnBuf<C::BN, C::BK, C::NT>(b_base, H, ncols, F), wm, wn);
   } else {
     k_loop<C, false, true>(
         lds, acc, F / C::BK,
@@ -456,16 +456,13 @@ __device__ __forceinline__ void dw_tile(char* lds, int b, const bf16_t* __restri
     if (prob < 2)
       k_loop_reg<C, true, true>(lds, acc, nk,
                                 MnGather<C::BM, C::BK, C::NT>(xs + mt * C::BM, sorted_flat + r0, K, P, prow, cnt),
-                                MnOp<C::BN, C::BK, C::NT>(r_base, r_base, C::BN, Q, qcol, cnt), wm, wn,
-                                cnt - (nk - 1) * C::BK);
+                                MnBuf<C::BN, C::BK, C::NT>(r_base, Q, qcol, cnt), wm, wn, cnt - (nk - 1) * C::BK);
     else
-      k_loop_reg<C, true, true>(lds, acc, nk, MnOp<C::BM, C::BK, C::NT>(l_base, l_base, C::BM, P, prow, cnt),
-                                MnOp<C::BN, C::BK, C::NT>(r_base, r_base, C::BN, Q, qcol, cnt), wm, wn,
-                                cnt - (nk - 1) * C::BK);
+      k_loop_reg<C, true, true>(lds, acc, nk, MnBuf<C::BM, C::BK, C::NT>(l_base, P, prow, cnt),
+                                MnBuf<C::BN, C::BK, C::NT>(r_base, Q, qcol, cnt), wm, wn, cnt - (nk - 1) * C::BK);
   } else if constexpr (C::REG) {
-    k_loop_reg<C, true, true>(lds, acc, nk, MnOp<C::BM, C::BK, C::NT>(l_base, l_base, C::BM, P, prow, cnt),
-                              MnOp<C::BN, C::BK, C::NT>(r_base, r_base, C::BN, Q, qcol, cnt), wm, wn,
-                              cnt - (nk - 1) * C::BK);
+    k_loop_reg<C, true, true>(lds, acc, nk, MnBuf<C::BM, C::BK, C::NT>(l_base, P, prow, cnt),
+                              MnBuf<C::BN, C::BK, C::NT>(r_base, Q, qcol, cnt), wm, wn, cnt - (nk - 1) * C::BK);
   } else {
   k_loop<C, true, true>(
       lds, acc, nk,

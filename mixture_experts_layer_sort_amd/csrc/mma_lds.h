@@ -250,22 +250,27 @@ template <int ROWS, int BK, int NT>
 struct KcOp {
   static constexpr int CPR = BK / 8, RP = NT / CPR, N = ROWS / RP;
   static_assert(NT % CPR == 0 && ROWS % RP == 0, "chunks split evenly over the threads");
-  const bf16_t *base0, *base1;
+  const bf16_t *base0, *base1;  // the same address in every lane
   int nk0;
-  int off[N];  // element offset of chunk i within a K tile
+  int off[N];  // byte offset of chunk i within a K tile (ROWS * ld * 2 < 2^31)
   __device__ __forceinline__ KcOp(const bf16_t* b0, const bf16_t* b1, int nk0_, int64_t ld, int rows_valid)
       : base0(b0), base1(b1), nk0(nk0_) {
     const int r0 = threadIdx.x / CPR, c = threadIdx.x % CPR;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int r = r0 + i * RP;
-      off[i] = int((r < rows_valid ? r : rows_valid - 1) * ld) + c * 8;
+      off[i] = int(((r < rows_valid ? r : rows_valid - 1) * ld + c * 8) * 2);
     }
   }
+  // Through a buffer resource at the K tile's base: each chunk's address is
+  // its 32-bit lane offset, with no per-row 64-bit add.  Every offset is in
+  // bounds (rows clamped above), so the range check never applies.
   __device__ __forceinline__ void load(u32x4_t (&v)[N], int kt) const {
     const bf16_t* p = kt < nk0 ? base0 + kt * BK : base1 + (kt - nk0) * BK;
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(p), (short)0, 0x7fffffff, 0x00020000);
 #pragma unroll
-    for (int i = 0; i < N; ++i) v[i] = *reinterpret_cast<const u32x4_t*>(p + off[i]);
+    for (int i = 0; i < N; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, off[i], 0, 0);
   }
   __device__ __forceinline__ void store(const u32x4_t (&v)[N], char* st, int) const {
     const int r0 = threadIdx.x / CPR, c = threadIdx.x % CPR;
@@ -344,6 +349,47 @@ struct MnOp {
       const int k = k0 + i * KP < kv ? i * KP : kv - 1 - k0;  // relative to this thread's first row
       v[i] = *reinterpret_cast<const u32x4_t*>(p + (int64_t)k * ld);
     }
+  }
+  __device__ __forceinline__ void store(const u32x4_t (&v)[N], char* st, int) const {
+    const int k0 = threadIdx.x / CPR, c = threadIdx.x % CPR;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int k = k0 + i * KP;
+      *reinterpret_cast<u32x4_t*>(st + k * (COLS * 2) + ((c ^ fm(k)) << 4)) = v[i];
+    }
+  }
+};
+
+// MN-contiguous operand of one source read through a buffer resource: BK k
+// rows x COLS columns of a row-major slab (leading dimension ld) whose row 0,
+// column 0 is `tile` (the same address in every lane).  The resource of K
+// tile kt ends after its last valid k row, so rows past k_total read zeros
+// from the hardware's range check and each row's address is one 32-bit add
+// (no clamp, no 64-bit multiply per row).  Columns at or past cols_valid read
+// a clamped column (results discarded).  Needs BK * ld * 2 < 2^31.
+template <int COLS, int BK, int NT>
+struct MnBuf {
+  static constexpr int CPR = COLS / 8, KP = NT / CPR, N = BK / KP;
+  static_assert(NT % CPR == 0 && BK % KP == 0, "chunks split evenly over the threads");
+  const char* tile;
+  int64_t ld;
+  int k_total;
+  int voff;      // this thread's byte offset in a K tile: first k row, column chunk
+  int row_step;  // bytes between the k rows of one thread (KP rows)
+  __device__ __forceinline__ MnBuf(const bf16_t* tile_, int64_t ld_, int cols_valid, int k_total_)
+      : tile(reinterpret_cast<const char*>(tile_)), ld(ld_), k_total(k_total_) {
+    const int c = threadIdx.x % CPR;
+    const int cs = c * 8 < cols_valid ? c : (cols_valid >> 3) - 1;
+    voff = int((threadIdx.x / CPR) * ld_ * 2) + cs * 16;
+    row_step = int(KP * ld_ * 2);
+  }
+  __device__ __forceinline__ void load(u32x4_t (&v)[N], int kt) const {
+    const int kv = k_total - kt * BK;  // valid k rows of the tile (at least one)
+    const int rows = kv < BK ? kv : BK;
+    __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(tile + (int64_t)kt * BK * ld * 2), (short)0, int(rows * ld * 2), 0x00020000);
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, voff + i * row_step, 0, 0);
   }
   __device__ __forceinline__ void store(const u32x4_t (&v)[N], char* st, int) const {
     const int k0 = threadIdx.x / CPR, c = threadIdx.x % CPR;
