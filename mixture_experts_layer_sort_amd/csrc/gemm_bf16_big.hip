@@ -66,6 +66,14 @@ using Mid = TileCfg<128, 256, 2, 4, 2, 32, 3>;
 // stage, two stages (48 KiB of operands, 67 KiB with the staged epilogue),
 // two workgroups per CU so one's epilogue overlaps the other's main loop.
 using MidR = TileCfg<128, 256, 2, 2, 2, 32, 2, true>;
+// 128 x 128 tiles on the register-staged loop for the short-contraction
+// forward GEMMs (H or F below the 256 x 256 thresholds): 4 waves of 64 x 64.
+// gate/up takes 32 k per stage (32 KiB of operands, four workgroups per CU);
+// down takes 64 k per stage (64 KiB, two per CU).  At H = 512, F = 1024
+// they measured 121-123 against 125-129 us (gate/up) and 61 against 68 us
+// (down) for the 128 x 128 kernels of gemm_bf16_small.hip.
+using SmallR32 = TileCfg<128, 128, 2, 2, 4, 32, 2, true>;
+using SmallR64 = TileCfg<128, 128, 2, 2, 2, 64, 2, true>;
 // dX tiles inside the merged dX / weight-gradient launch.  128 x 256 tiles
 // would balance that launch better (at H = 512, F = 1024, E = 8 its 192
 // weight-gradient tiles take 64 k steps and the dX tiles 32), but measured
@@ -73,7 +81,7 @@ using MidR = TileCfg<128, 256, 2, 2, 2, 32, 2, true>;
 // 32): the smaller tile's operand traffic per flop outweighs the balance.
 using DxInMerged = Big;
 static_assert(MOE_TILE_M % Big::BM == 0 && MOE_TILE_M % BigDma::BM == 0 && MOE_TILE_M % Mid::BM == 0 &&
-                  MOE_TILE_M % MidR::BM == 0,
+                  MOE_TILE_M % MidR::BM == 0 && MOE_TILE_M % SmallR32::BM == 0 && MOE_TILE_M % SmallR64::BM == 0,
               "list tiles split into row tiles");
 
 // staged tile <- bf16(acc)
@@ -676,6 +684,16 @@ hipError_t ffn_gate_up_midr(const Dims& d, const void* xs, const int32_t* sorted
 hipError_t ffn_down_midr(const Dims& d, const void* a, const void* wd, const int32_t* tiles, const int32_t* num_tiles,
                          void* ys, hipStream_t s) {
   return down_t<MidR>(d, a, wd, tiles, num_tiles, ys, s);
+}
+hipError_t ffn_gate_up_smallr(const Dims& d, const void* xs, const int32_t* sorted_flat, const void* wg,
+                              const void* wu, const int32_t* tiles, const int32_t* num_tiles, void* g, void* u,
+                              void* a, hipStream_t s) {
+  return sorted_flat ? gate_up_t<SmallR32, true>(d, xs, sorted_flat, wg, wu, tiles, num_tiles, g, u, a, s)
+                     : gate_up_t<SmallR32>(d, xs, nullptr, wg, wu, tiles, num_tiles, g, u, a, s);
+}
+hipError_t ffn_down_smallr(const Dims& d, const void* a, const void* wd, const int32_t* tiles,
+                           const int32_t* num_tiles, void* ys, hipStream_t s) {
+  return down_t<SmallR64>(d, a, wd, tiles, num_tiles, ys, s);
 }
 hipError_t ffn_bwd_dact_midr(const Dims& d, const void* dys, const void* wd, const void* g, const void* u,
                              const int32_t* tiles, const int32_t* num_tiles, void* dg, void* du, hipStream_t s) {

@@ -167,6 +167,9 @@ hipError_t ffn_bwd_dact_mid(const Dims&, const void*, const void*, const void*, 
 hipError_t ffn_gate_up_midr(const Dims&, const void*, const int32_t*, const void*, const void*, const int32_t*,
                             const int32_t*, void*, void*, void*, hipStream_t);
 hipError_t ffn_down_midr(const Dims&, const void*, const void*, const int32_t*, const int32_t*, void*, hipStream_t);
+hipError_t ffn_gate_up_smallr(const Dims&, const void*, const int32_t*, const void*, const void*, const int32_t*,
+                              const int32_t*, void*, void*, void*, hipStream_t);
+hipError_t ffn_down_smallr(const Dims&, const void*, const void*, const int32_t*, const int32_t*, void*, hipStream_t);
 hipError_t ffn_bwd_dact_midr(const Dims&, const void*, const void*, const void*, const void*, const int32_t*,
                              const int32_t*, void*, void*, hipStream_t);
 hipError_t ffn_bwd_dx_midr(const Dims&, const void*, const void*, const void*, const void*, const int32_t*,
@@ -190,8 +193,10 @@ hipError_t ffn_bwd_dx_dw_big(const Dims&, const void*, const void*, const void*,
 // epilogue.  Measured on MI355X per stage over the shapes (H, F, rows per
 // expert) = (512, 1024, 4096), (2048, 1408, skewed 0..16k), (7168, 2048,
 // 256), (4096, 14336, 4096):
-//   gate/up (contraction H): 256 x 256 from H = 2048 on, else 128 x 128;
-//   down (contraction F): 256 x 256 from F = 1280 on, else 128 x 128;
+//   gate/up (contraction H): 256 x 256 from H = 2048 on, else 128 x 128 on
+//   the register-staged loop (SmallR);
+//   down (contraction F): 256 x 256 from F = 1280 on, else 128 x 128 on the
+//   register-staged loop (SmallR);
 //   dA (contraction H): 256 x 256 (8 waves, LDS DMA) from H = 4096 on, below
 //   that 128 x 256 tiles through the LDS DMA pipeline (their staged SwiGLU
 //   epilogue overlaps across two workgroups per CU);
@@ -199,8 +204,9 @@ hipError_t ffn_bwd_dx_dw_big(const Dims&, const void*, const void*, const void*,
 //   dW (contraction over an expert's rows): 256 x 256 throughout.
 // MOE_GEMM_TILES=256, =128x256 or =128 in the environment (read at every
 // launch) overrides the choice for every stage (128 selects the 128 x 256 DMA
-// dA tiles); any other value, or none, keeps the measured choice.
-enum class Tiles { Small, MidR, Big };
+// dA tiles); any other value, or none, keeps the measured choice.  SmallR is
+// only ever the measured choice.
+enum class Tiles { Small, SmallR, MidR, Big };
 static Tiles pick(Tiles measured) {
   const char* v = std::getenv("MOE_GEMM_TILES");
   if (v == nullptr) return measured;
@@ -209,8 +215,8 @@ static Tiles pick(Tiles measured) {
   if (std::strcmp(v, "128") == 0) return Tiles::Small;
   return measured;
 }
-static Tiles tiles_gate_up(const Dims& d) { return pick(d.H >= 2048 ? Tiles::Big : Tiles::Small); }
-static Tiles tiles_down(const Dims& d) { return pick(d.F >= 1280 ? Tiles::Big : Tiles::Small); }
+static Tiles tiles_gate_up(const Dims& d) { return pick(d.H >= 2048 ? Tiles::Big : Tiles::SmallR); }
+static Tiles tiles_down(const Dims& d) { return pick(d.F >= 1280 ? Tiles::Big : Tiles::SmallR); }
 static Tiles tiles_dact(const Dims& d) { return pick(d.H >= 4096 ? Tiles::Big : Tiles::Small); }
 static Tiles tiles_dx(const Dims& d) { return pick(2 * d.F >= 2560 ? Tiles::Big : Tiles::Small); }
 static Tiles tiles_dw(const Dims&) { return pick(Tiles::Big); }
@@ -221,6 +227,7 @@ hipError_t ffn_gate_up(const Dims& d, const void* xs, const int32_t* sorted_flat
     switch (tiles_gate_up(d)) {
       case Tiles::Big: return ffn_gate_up_big(d, xs, sorted_flat, wg, wu, tiles, num_tiles, g, u, a, s);
       case Tiles::MidR: return ffn_gate_up_midr(d, xs, sorted_flat, wg, wu, tiles, num_tiles, g, u, a, s);
+      case Tiles::SmallR: return ffn_gate_up_smallr(d, xs, sorted_flat, wg, wu, tiles, num_tiles, g, u, a, s);
       default: return ffn_gate_up_small(d, xs, sorted_flat, wg, wu, tiles, num_tiles, g, u, a, s);
     }
   unsigned grid = unsigned(max_tiles(d) * (d.F / TN));
@@ -236,6 +243,7 @@ hipError_t ffn_down(const Dims& d, const void* a, const void* wd, const int32_t*
     switch (tiles_down(d)) {
       case Tiles::Big: return ffn_down_big(d, a, wd, tiles, num_tiles, ys, s);
       case Tiles::MidR: return ffn_down_midr(d, a, wd, tiles, num_tiles, ys, s);
+      case Tiles::SmallR: return ffn_down_smallr(d, a, wd, tiles, num_tiles, ys, s);
       default: return ffn_down_small(d, a, wd, tiles, num_tiles, ys, s);
     }
   unsigned grid = unsigned(max_tiles(d) * (d.H / TN));
