@@ -201,10 +201,10 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_gate_up(const bf16_t* __rest
     static_assert(C::REG, "the gathered A tile uses the register-staged loop");
     k_loop_reg<C, false, true>(lds, acc, H / C::BK,
                                KcGather<C::BM, C::BK, C::NT>(xs, sorted_flat + ti.row0, K, H, ti.rows),
-                               MnOp<C::BN, C::BK, C::NT>(b_g, b_u, HALF, F, C::BN, H), wm, wn);
+                               MnOp<C::BN, C::BK, C::NT>(b_g, b_u, HALF, F, C::BN), wm, wn);
   } else if constexpr (C::REG) {
     k_loop_reg<C, false, true>(lds, acc, H / C::BK, KcOp<C::BM, C::BK, C::NT>(a_base, a_base, kNoSplit, H, ti.rows),
-                               MnOp<C::BN, C::BK, C::NT>(b_g, b_u, HALF, F, C::BN, H), wm, wn);
+                               MnOp<C::BN, C::BK, C::NT>(b_g, b_u, HALF, F, C::BN), wm, wn);
   } else {
     k_loop<C, false, true>(
         lds, acc, H / C::BK,

@@ -319,36 +319,28 @@ struct KcGather {
 };
 
 // MN-contiguous operand: BK k rows x COLS columns of a row-major matrix
-// (leading dimension ld); K tile kt covers k rows [kt * BK, kt * BK + BK).
-// Columns [0, split) come from base0 and [split, COLS) from base1 (both
-// indexed by the tile column); columns at or past cols_valid read a clamped
-// column (results discarded); k rows at or past k_total read the last valid
-// row (k_loop_reg zeroes them in the A operand).
+// (leading dimension ld); K tile kt covers k rows [kt * BK, kt * BK + BK),
+// all of them valid (the contraction length is a multiple of BK).  Columns
+// [0, split) come from base0 and [split, COLS) from base1 (both indexed by
+// the tile column); columns at or past cols_valid read a clamped column
+// (results discarded).  Each row's address is this thread's pointer plus a
+// multiple of the (uniform) row stride.
 template <int COLS, int BK, int NT>
 struct MnOp {
   static constexpr int CPR = COLS / 8, KP = NT / CPR, N = BK / KP;
   static_assert(NT % CPR == 0 && BK % KP == 0, "chunks split evenly over the threads");
   const bf16_t* base;  // this thread's column, k row 0
   int64_t ld;
-  int k_total;
-  __device__ __forceinline__ MnOp(const bf16_t* b0, const bf16_t* b1, int split, int64_t ld_, int cols_valid,
-                                  int k_total_)
-      : ld(ld_), k_total(k_total_) {
+  __device__ __forceinline__ MnOp(const bf16_t* b0, const bf16_t* b1, int split, int64_t ld_, int cols_valid)
+      : ld(ld_) {
     const int c = threadIdx.x % CPR;
     const int cs = c * 8 < cols_valid ? c : (cols_valid >> 3) - 1;
     base = (cs * 8 < split ? b0 : b1) + (int64_t)(threadIdx.x / CPR) * ld_ + cs * 8;
   }
-  // rows past the valid ones (at least one valid row per loaded tile) read the
-  // tile's last valid row
   __device__ __forceinline__ void load(u32x4_t (&v)[N], int kt) const {
-    const int k0 = threadIdx.x / CPR;
-    const int kv = k_total - kt * BK;  // valid k rows of the tile
     const bf16_t* p = base + (int64_t)kt * BK * ld;
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int k = k0 + i * KP < kv ? i * KP : kv - 1 - k0;  // relative to this thread's first row
-      v[i] = *reinterpret_cast<const u32x4_t*>(p + (int64_t)k * ld);
-    }
+    for (int i = 0; i < N; ++i) v[i] = *reinterpret_cast<const u32x4_t*>(p + (int64_t)(i * KP) * ld);
   }
   __device__ __forceinline__ void store(const u32x4_t (&v)[N], char* st, int) const {
     const int k0 = threadIdx.x / CPR, c = threadIdx.x % CPR;
