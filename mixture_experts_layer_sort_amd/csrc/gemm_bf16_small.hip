@@ -10,8 +10,10 @@
 // synchronisation is needed: the grid is sized for the largest possible tile
 // count and workgroups past the real count return at once.
 //
-// This file holds the shape for problems too small for the 256 x 256 LDS-DMA
-// kernels (short contractions, few tiles per CU): workgroup tile 128 x 128,
+// This file holds an older 128 x 128 shape.  The short-contraction forward
+// GEMMs now run on the register-staged 128 x 128 tiles of gemm_bf16_big.hip;
+// this one serves dX launched on its own below 2F = 2560, and every stage
+// when the 128 family is forced.  Workgroup tile 128 x 128,
 // K step 64, 256 threads = 4 waves in a 2 x 2 arrangement, 64 x 64 per wave
 // (2 x 2 MFMA 32x32x16 per 16-deep k step).  One LDS buffer plus register
 // prefetch keeps the LDS footprint near 34 KB, so 3 workgroups share a CU
