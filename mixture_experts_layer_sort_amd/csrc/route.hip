@@ -371,6 +371,110 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_route_mma(const bf16_t* __re
   }
 }
 
+// Router for few experts and short rows (bf16, E <= 32, H <= 1024).  The
+// workgroup's 32 token rows and the whole of W_r, transposed to [expert][h]
+// (experts E..31 zero), come into LDS with all of a thread's loads issued
+// before its first store; one wave then multiplies them on the matrix cores
+// (one 32 x 32 tile, H / 16 k steps, float32 accumulation) and the epilogue
+// is k_route_mma's.  The ring-pipelined router above pads W_r to 128
+// columns and waits on each 64-deep stage, which leaves it latency-bound
+// when E is small.
+constexpr int kSmallRouteE = 32, kSmallRouteH = 1024;
+constexpr int kSmallRouteLoads = kRouteTok * kSmallRouteH / 8 / 256;  // 16-byte loads per thread, at most
+
+__host__ __device__ constexpr int small_route_pitch(int H) { return H + 8; }  // bf16 per staged row
+__host__ __device__ constexpr size_t small_route_lds(int H) {
+  return size_t(2) * 32 * small_route_pitch(H) * 2 + size_t(kRouteTok) * (kSmallRouteE + 1) * 4 +
+         size_t(MOE_MAX_EXPERTS) * 4;
+}
+
+__global__ __launch_bounds__(256) void k_route_small(const bf16_t* __restrict__ x, const bf16_t* __restrict__ w_r,
+                                                     const float* __restrict__ bias, int32_t* __restrict__ topk,
+                                                     float* __restrict__ gates, int N, int H, int E, int K,
+                                                     float* __restrict__ probs, float* __restrict__ part,
+                                                     int32_t* __restrict__ hist) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  using moe_mma::u32x4_t;
+  const int P = small_route_pitch(H);
+  bf16_t* xl = reinterpret_cast<bf16_t*>(lds);                        // [32][P] token rows
+  bf16_t* wl = xl + kRouteTok * P;                                    // [32][P] W_r^T
+  constexpr int LP = kSmallRouteE + 1;
+  float* lg = reinterpret_cast<float*>(wl + kSmallRouteE * P);        // [32][LP] logits
+  int* lhist = reinterpret_cast<int*>(lg + kRouteTok * LP);           // [E]
+  const int n0 = blockIdx.x * kRouteTok;
+  const int rows = min(kRouteTok, N - n0);
+  const int tid = threadIdx.x;
+  const int cpr = H / 8;  // 16-byte chunks per token row
+  {
+    u32x4_t v[kSmallRouteLoads];
+#pragma unroll
+    for (int i = 0; i < kSmallRouteLoads; ++i) {
+      const int q = tid + 256 * i, r = q / cpr;
+      v[i] = u32x4_t{0u, 0u, 0u, 0u};
+      if (q < kRouteTok * cpr && r < rows)
+        v[i] = *reinterpret_cast<const u32x4_t*>(x + (int64_t)(n0 + r) * H + (q % cpr) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < kSmallRouteLoads; ++i) {
+      const int q = tid + 256 * i;
+      if (q < kRouteTok * cpr) *reinterpret_cast<u32x4_t*>(xl + (q / cpr) * P + (q % cpr) * 8) = v[i];
+    }
+  }
+  {
+    // W_r [H][E]: chunk q holds experts 8 (q % cpe) .. +7 of row h = q / cpe
+    const int cpe = E / 8;
+    u32x4_t v[kSmallRouteLoads];
+#pragma unroll
+    for (int i = 0; i < kSmallRouteLoads; ++i) {
+      const int q = tid + 256 * i;
+      v[i] = u32x4_t{0u, 0u, 0u, 0u};
+      if (q < H * cpe) v[i] = *reinterpret_cast<const u32x4_t*>(w_r + (int64_t)q * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < kSmallRouteLoads; ++i) {
+      const int q = tid + 256 * i;
+      if (q < H * cpe) {
+        const int h = q / cpe, e0 = (q % cpe) * 8;
+        const bf16_t* b = reinterpret_cast<const bf16_t*>(&v[i]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) wl[(e0 + j) * P + h] = b[j];
+      }
+    }
+    for (int q = tid; q < (kSmallRouteE - E) * cpr; q += 256)
+      *reinterpret_cast<u32x4_t*>(wl + (E + q / cpr) * P + (q % cpr) * 8) = u32x4_t{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+  if (tid < 64) {
+    // A = the token rows (lane: row l % 32, k 8 (l / 32) ..), B = W_r^T rows
+    // (lane: expert l % 32, same k); C[token][expert] in the 32 x 32 layout
+    const bf16_t* ap = xl + (tid & 31) * P + 8 * (tid >> 5);
+    const bf16_t* bp = wl + (tid & 31) * P + 8 * (tid >> 5);
+    f32x16_t acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    for (int k = 0; k < H; k += 16)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(ap + k),
+                                                    *reinterpret_cast<const bf16x8_t*>(bp + k), acc, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) lg[((r >> 2) * 8 + (tid >> 5) * 4 + (r & 3)) * LP + (tid & 31)] = acc[r];
+  }
+  __syncthreads();
+  if (probs) {  // load-balancing loss: full softmax instead of the top-K
+    probs_epilogue<256>(lg, LP, rows, n0, E, bias, probs, part + (int64_t)blockIdx.x * E);
+    return;
+  }
+  if (hist) {
+    for (int e = tid; e < E; e += 256) lhist[e] = 0;
+    __syncthreads();
+  }
+  int* lh = hist ? lhist : nullptr;
+  for (int tt = tid; tt < rows; tt += 256) lane_topk_gates(lg + tt * LP, bias, E, K, n0 + tt, topk, gates, lh);
+  if (hist) {
+    __syncthreads();
+    for (int e = tid; e < E; e += 256) hist[(int64_t)blockIdx.x * E + e] = lhist[e];
+  }
+}
+
 // Router tile shapes (tokens x padded experts): the MN-contiguous W_r tile
 // needs at least 128 columns for its swizzle.  Up to 128 experts: 32 tokens
 // per workgroup and four workgroups per CU (their two-stage rings fill the
@@ -656,9 +760,27 @@ hipError_t route_mma(const Dims& d, const void* x, const void* w_r, const float*
 
 // The matrix-core paths of the router need 16-byte W_r rows (bf16, E % 8 == 0).
 static bool router_mma(const Dims& d) { return d.dtype == MOE_BF16 && d.E % 8 == 0; }
+// ... and the LDS-resident form takes few experts and short rows.
+static bool router_small(const Dims& d) {
+  return router_mma(d) && d.E <= kSmallRouteE && d.H <= kSmallRouteH;
+}
+
+static hipError_t route_small(const Dims& d, const void* x, const void* w_r, const float* bias, int32_t* topk,
+                              float* gates, hipStream_t s, float* probs = nullptr, float* part = nullptr,
+                              int32_t* hist = nullptr) {
+  const size_t lds = small_route_lds(int(d.H));
+  hipError_t st = moe_mma::allow_lds<k_route_small>(int(small_route_lds(kSmallRouteH)));
+  if (st != hipSuccess) return st;
+  const unsigned grid = unsigned((d.N + kRouteTok - 1) / kRouteTok);
+  hipLaunchKernelGGL(k_route_small, dim3(grid), dim3(256), lds, s, static_cast<const moe::bf16_t*>(x),
+                     static_cast<const moe::bf16_t*>(w_r), bias, topk, gates, int(d.N), int(d.H), int(d.E), int(d.K),
+                     probs, part, hist);
+  return hipGetLastError();
+}
 
 hipError_t route(const Dims& d, const void* x, const void* w_r, const float* bias, int32_t* topk, float* gates,
                  hipStream_t s, int32_t* hist) {
+  if (router_small(d)) return route_small(d, x, w_r, bias, topk, gates, s, nullptr, nullptr, hist);
   if (router_mma(d))
     return d.E <= 128 ? route_mma<RouteCfg128>(d, x, w_r, bias, topk, gates, s, nullptr, nullptr, hist)
                       : route_mma<RouteCfg256>(d, x, w_r, bias, topk, gates, s, nullptr, nullptr, hist);
@@ -804,7 +926,9 @@ hipError_t aux_loss(const Dims& d, const void* x, const void* w_r, const float* 
                     float alpha, float* probs, float* loss, void* ws, hipStream_t s) {
   float* part = static_cast<float*>(ws);
   hipError_t err;
-  if (router_mma(d))
+  if (router_small(d))
+    err = route_small(d, x, w_r, bias, nullptr, nullptr, s, probs, part);
+  else if (router_mma(d))
     err = d.E <= 128 ? route_mma<RouteCfg128>(d, x, w_r, bias, nullptr, nullptr, s, probs, part)
                      : route_mma<RouteCfg256>(d, x, w_r, bias, nullptr, nullptr, s, probs, part);
   else if (d.dtype == MOE_BF16)
