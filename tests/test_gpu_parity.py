@@ -37,7 +37,16 @@ def _runner(cfg, backward=True, gather=None, dw_gather=False):
                           gather=gather, dw_gather=dw_gather)
 
 
-@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+# one case per router kernel the small configs do not reach: the
+# ring-pipelined matrix-core router at E = 64 (128 padded columns) and at a
+# row longer than the LDS-resident router takes (H = 1152), and the
+# LDS-resident router at its largest shape (E = 32, H = 1024)
+ROUTER_PATHS = [MoEConfig("t_route_e64", N=300, H=256, F=128, E=64, K=4, dtype="bf16"),
+                MoEConfig("t_route_h1152", N=300, H=1152, F=128, E=8, K=2, dtype="bf16"),
+                MoEConfig("t_route_e32_h1024", N=300, H=1024, F=128, E=32, K=6, dtype="bf16")]
+
+
+@pytest.mark.parametrize("cfg", SMALL + ROUTER_PATHS, ids=lambda c: c.name)
 def test_route_matches_oracle(cfg):
     print(f"[route] {cfg.name}", flush=True)
     cpu, dev = gpu_inputs(cfg)
