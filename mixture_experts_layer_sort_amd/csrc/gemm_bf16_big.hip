@@ -53,6 +53,12 @@ using namespace moe;
 using namespace moe_mma;
 
 using Big = TileCfg<256, 256, 2, 2, 1, 64, 2, true>;  // 4 waves, 128 x 128 per wave, register-staged
+// The same tile with 8 waves of 64 x 128 (two per SIMD, each covering the
+// other's issue stalls): used for dX, the weight gradients and down, where it
+// measured faster (merged dX/dW 866-870 -> 891-896 TFLOP/s at H = 512,
+// F = 1024, E = 8; 846-851 -> 881 at the skewed H = 2048, E = 64 workload);
+// gate/up keeps 4 waves (1.29 -> 1.31 ms and 5.49 -> 5.61 ms with 8).
+using Big8 = TileCfg<256, 256, 4, 2, 1, 64, 2, true>;
 // 8 waves of 64 x 128 through the LDS DMA pipeline: kept for the SwiGLU
 // backward, whose G/U epilogue runs with twice as many waves to issue its
 // loads.
@@ -79,8 +85,8 @@ using SmallR64 = TileCfg<128, 128, 2, 2, 2, 64, 2, true>;
 // weight-gradient tiles take 64 k steps and the dX tiles 32), but measured
 // slower on every workload (221 -> 238 us there with 64 k per stage, 260 with
 // 32): the smaller tile's operand traffic per flop outweighs the balance.
-using DxInMerged = Big;
-static_assert(MOE_TILE_M % Big::BM == 0 && MOE_TILE_M % BigDma::BM == 0 && MOE_TILE_M % Mid::BM == 0 &&
+using DxInMerged = Big8;
+static_assert(MOE_TILE_M % Big::BM == 0 && MOE_TILE_M % Big8::BM == 0 && MOE_TILE_M % BigDma::BM == 0 && MOE_TILE_M % Mid::BM == 0 &&
                   MOE_TILE_M % MidR::BM == 0 && MOE_TILE_M % SmallR32::BM == 0 && MOE_TILE_M % SmallR64::BM == 0,
               "list tiles split into row tiles");
 
@@ -573,7 +579,7 @@ static hipError_t down_t(const Dims& d, const void* a, const void* wd, const int
 
 hipError_t ffn_down_big(const Dims& d, const void* a, const void* wd, const int32_t* tiles, const int32_t* num_tiles,
                          void* ys, hipStream_t s) {
-  return down_t<Big>(d, a, wd, tiles, num_tiles, ys, s);
+  return down_t<Big8>(d, a, wd, tiles, num_tiles, ys, s);
 }
 
 template <class C>
@@ -612,7 +618,7 @@ static hipError_t dx_t(const Dims& d, const void* dg, const void* du, const void
 
 hipError_t ffn_bwd_dx_big(const Dims& d, const void* dg, const void* du, const void* wg, const void* wu,
                            const int32_t* tiles, const int32_t* num_tiles, void* dxs, hipStream_t s) {
-  return dx_t<Big>(d, dg, du, wg, wu, tiles, num_tiles, dxs, s);
+  return dx_t<Big8>(d, dg, du, wg, wu, tiles, num_tiles, dxs, s);
 }
 
 // workgroups of a weight-gradient launch: E experts x (two H x F problems +
@@ -648,14 +654,14 @@ static hipError_t dw_t(const Dims& d, const void* xs, const int32_t* sorted_flat
 hipError_t ffn_bwd_dw_big(const Dims& d, const void* xs, const int32_t* sorted_flat, const void* a, const void* dys,
                           const void* dg, const void* du, const int32_t* offsets, float* dwg, float* dwu, float* dwd,
                           hipStream_t s) {
-  return dw_t<Big>(d, xs, sorted_flat, a, dys, dg, du, offsets, dwg, dwu, dwd, s);
+  return dw_t<Big8>(d, xs, sorted_flat, a, dys, dg, du, offsets, dwg, dwu, dwd, s);
 }
 
 hipError_t ffn_bwd_dx_dw_big(const Dims& d, const void* dg, const void* du, const void* wg, const void* wu,
                              const int32_t* tiles, const int32_t* num_tiles, void* dxs, const void* xs,
                              const int32_t* sorted_flat, const void* a, const void* dys, const int32_t* offsets,
                              float* dwg, float* dwu, float* dwd, hipStream_t s) {
-  using CW = Big;
+  using CW = Big8;
   using CX = DxInMerged;
   constexpr int lds_bytes = CW::LDS > CX::LDS ? CW::LDS : CX::LDS;
   auto run = [&](auto gather) -> hipError_t {
