@@ -71,7 +71,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--config", default="bf16_n16384_h512_f1024_e8_k2")
+    # the largest fwd+bwd workload that fits one GPU: the large-FFN deterministic one
+    p.add_argument("--config", default="bf16_n16384_h4096_f14336_e8_k2")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--aux-alpha", type=float, default=None,
@@ -416,19 +417,48 @@ def main():
         "gemm_stages_roofline": gemm_roof,
         "roofline": roof,
         "cpu_baseline": cpu_base,
-        "host": {"cpu": platform.processor() or platform.machine(), "cores": os.cpu_count()},
+        "host": {"cpu": host_cpu_model(), "cores": os.cpu_count(), "blas_threads": blas_threads()},
     }
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(cfg, cpu, aux=None, shared=None):
-    """The oracle (as it stands) on the host: whole-layer passes over the
-    workload's first S tokens, repeated until about 12 s have passed."""
-    import torch
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
+
+def blas_threads():
+    """Threads of the BLAS that NumPy's matmuls (the oracle's) run on."""
+    try:
+        from threadpoolctl import threadpool_info
+        n = [d.get("num_threads") for d in threadpool_info() if d.get("user_api") == "blas"]
+        if n and n[0]:
+            return int(n[0])
+    except Exception:  # noqa: BLE001 - reporting only
+        pass
+    return os.cpu_count()
+
+
+# float64 multiply-adds per second the host is assumed to sustain in the
+# oracle's matmuls; only sizes the sample so that it takes 10-30 s
+CPU_SAMPLE_FLOPS = 40e9
+CPU_SAMPLE_SECONDS = 12.0
+
+
+def cpu_baseline(cfg, cpu, aux=None, shared=None):
+    """The oracle (as it stands) on the host, on a bounded sample of the
+    workload: whole-layer passes over its first S tokens, with S sized by the
+    layer's flops per token for about CPU_SAMPLE_SECONDS of work, repeated
+    until that much time has passed (at most 20 passes)."""
     from oracle import moe_oracle as O
-    threads = torch.get_num_threads()
-    S = min(cfg.N, 16384)
+    per_token = (18 if cpu["dy"] is not None else 6) * cfg.H * cfg.F * cfg.K
+    S = int(min(cfg.N, max(16, CPU_SAMPLE_FLOPS * CPU_SAMPLE_SECONDS / per_token)))
     x = cpu["x"][:S]
     dy = cpu["dy"][:S] if cpu["dy"] is not None else None
     store = "bf16" if cfg.dtype == "bf16" else "f32"
@@ -441,13 +471,16 @@ def cpu_baseline(cfg, cpu, aux=None, shared=None):
             O.aux_loss(f["logits"], f["counts"], cfg.K, aux)
         if dy is not None:
             O.backward(f, dy, aux_scale=aux)
+        del f
         passes += 1
-        if time.perf_counter() - t0 > 12.0 or passes >= 20:
+        if time.perf_counter() - t0 > CPU_SAMPLE_SECONDS or passes >= 20:
             break
     dt = time.perf_counter() - t0
-    return {"value": round(S * passes / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {S} tokens of the workload, {passes} whole-layer pass(es) "
-                      f"({'fwd+bwd' if dy is not None else 'fwd'}), float64 NumPy, {dt:.1f} s"}
+    return {"value": round(S * passes / dt, 1), "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+            "cpu": host_cpu_model(),
+            "sample": f"first {S} of {cfg.N} tokens of the workload (all {cfg.E} experts' weights), {passes} "
+                      f"whole-layer pass(es) ({'fwd+bwd' if dy is not None else 'fwd'}), float64 NumPy on "
+                      f"{blas_threads()} BLAS threads, {dt:.1f} s"}
 
 
 if __name__ == "__main__":

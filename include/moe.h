@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 8
+#define MOE_ABI_VERSION 9
 /* Rows per tile of the grouped-GEMM tile list built by moe_permute_meta. */
 #define MOE_TILE_M 256
 #define MOE_MAX_EXPERTS 256
@@ -81,12 +81,26 @@ typedef enum moe_entry {
   MOE_ENTRY_ROUTE_META = 8
 } moe_entry;
 
+/* bf16 grouped-GEMM tile family (moe_dims.gemm_tiles).  AUTO lets the
+ * library choose per stage from the problem size (what the layer runs); the
+ * others force one family on every GEMM stage of the call, so that tests can
+ * reach each kernel family at small sizes.  Every family computes the same
+ * values up to float32 summation order.  Ignored for MOE_F32. */
+typedef enum moe_gemm_tiles {
+  MOE_TILES_AUTO = 0,
+  MOE_TILES_256 = 1,     /* 256 x 256 tiles */
+  MOE_TILES_128X256 = 2, /* 128 x 256 register-staged tiles */
+  MOE_TILES_128 = 3      /* 128 x 128 tiles (dA: 128 x 256 through the LDS DMA) */
+} moe_gemm_tiles;
+
 /* Problem sizes: N tokens, hidden size H, expert FFN size F, E experts,
- * K experts per token, dtype a moe_dtype.  NK = N*K routed rows. */
+ * K experts per token, dtype a moe_dtype.  NK = N*K routed rows.
+ * gemm_tiles is a moe_gemm_tiles value (0 = AUTO); with a forced family the
+ * merged dX/dW call makes two launches of that family. */
 typedef struct moe_dims {
   int64_t N, H, F, E, K;
   int32_t dtype;
-  int32_t reserved; /* must be 0 */
+  int32_t gemm_tiles;
 } moe_dims;
 
 /* ABI version of the loaded library (MOE_ABI_VERSION it was built with). */
@@ -186,7 +200,18 @@ int moe_expert_ffn(const moe_dims* d, const void* xs, const void* w_gate, const 
                    const int32_t* tiles, const int32_t* num_tiles, void* g_save, void* u_save, void* act, void* ys,
                    hipStream_t stream);
 
-/* First grouped GEMM of moe_expert_ffn: G, U and A = silu(G)*U. */
+/* First grouped GEMM of moe_expert_ffn: the gate and up projections of the
+ * SwiGLU expert and its activation (icman section 2.3: silu on the gate
+ * branch times the linear up branch; intelliparadigm section 2.1: the
+ * expert FeedForward without biases), over the variable-size expert groups
+ * of the tile list (MegaBlocks section 2.3, grouped GEMM), row i of expert e:
+ *   G[i] = xs[i].W_gate[e], U[i] = xs[i].W_up[e]  (float32 sums, stored
+ *   rounded); A[i] = silu(G[i]) * U[i] from the rounded G, U.
+ *   xs [NK,H] act; w_gate, w_up [E,H,F]; tiles, num_tiles from
+ *   moe_permute_meta; g_save, u_save [NK,F] out or both NULL (no backward);
+ *   act [NK,F] out.  Rows past offsets[E] are not written.
+ * Errors: MOE_EINVAL for a bad shape or a null/misaligned xs, weight, tile
+ * or act pointer (or exactly one of g_save, u_save NULL). */
 int moe_ffn_gate_up(const moe_dims* d, const void* xs, const void* w_gate, const void* w_up, const int32_t* tiles,
                     const int32_t* num_tiles, void* g_save, void* u_save, void* act, hipStream_t stream);
 
@@ -203,7 +228,13 @@ int moe_ffn_gate_up_gather(const moe_dims* d, const void* x, const int32_t* sort
                            const void* w_up, const int32_t* tiles, const int32_t* num_tiles, void* g_save,
                            void* u_save, void* act, hipStream_t stream);
 
-/* Second grouped GEMM of moe_expert_ffn: ys = A.W_down[e]. */
+/* Second grouped GEMM of moe_expert_ffn: the SwiGLU expert's down
+ * projection (icman section 2.3; MegaBlocks section 2.3, grouped GEMM over
+ * the variable-size groups), row i of expert e:
+ *   ys[i] = A[i].W_down[e]  (float32 sums, stored rounded).
+ *   act [NK,F] from moe_ffn_gate_up; w_down [E,F,H]; tiles, num_tiles from
+ *   moe_permute_meta; ys [NK,H] out.  Errors: MOE_EINVAL for a bad shape or a
+ *   null/misaligned pointer. */
 int moe_ffn_down(const moe_dims* d, const void* act, const void* w_down, const int32_t* tiles,
                  const int32_t* num_tiles, void* ys, hipStream_t stream);
 
@@ -236,7 +267,10 @@ int moe_combine_bwd(const moe_dims* d, const void* dy, const void* ys, const flo
 int moe_route_bwd(const moe_dims* d, const void* x, const int32_t* topk_idx, const float* gates,
                   const float* dgates, float* dlogits, float* dw_r, void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Backward of the grouped SwiGLU experts, for every row i of expert e:
+/* Backward of the grouped SwiGLU experts (the expert of icman section 2.3,
+ * differentiated; the activation is recomputed from the stored G and U as
+ * MegaBlocks section 4 recomputes it in the backward), for every row i of
+ * expert e:
  *   dA = dys[i].W_down[e]^T; s = sigmoid(G[i]);
  *   dG[i] = dA*U[i]*s*(1 + G[i]*(1-s)), dU[i] = dA*G[i]*s   (stored rounded);
  *   dxs[i] = dG[i].W_gate[e]^T + dU[i].W_up[e]^T;
@@ -253,15 +287,37 @@ int moe_expert_ffn_bwd(const moe_dims* d, const void* dys, const void* xs, const
                        const int32_t* offsets, const int32_t* tiles, const int32_t* num_tiles, void* dg, void* du,
                        void* dxs, float* dw_gate, float* dw_up, float* dw_down, hipStream_t stream);
 
-/* dA = dys.W_down[e]^T with the SwiGLU derivative applied: writes dG, dU. */
+/* First step of moe_expert_ffn_bwd: the down projection's input gradient
+ * and the SwiGLU derivative (icman section 2.3, differentiated), row i of
+ * expert e:
+ *   dA = dys[i].W_down[e]^T (float32, not stored); s = sigmoid(G[i]);
+ *   dG[i] = dA*U[i]*s*(1 + G[i]*(1-s)), dU[i] = dA*G[i]*s (stored rounded).
+ *   dys [NK,H] act from moe_combine_bwd; w_down [E,F,H]; g_save, u_save
+ *   [NK,F] from moe_ffn_gate_up; tiles, num_tiles from moe_permute_meta;
+ *   dg, du [NK,F] out.  Errors: MOE_EINVAL for a bad shape or a
+ *   null/misaligned pointer. */
 int moe_ffn_bwd_dact(const moe_dims* d, const void* dys, const void* w_down, const void* g_save, const void* u_save,
                      const int32_t* tiles, const int32_t* num_tiles, void* dg, void* du, hipStream_t stream);
 
-/* dxs = dG.W_gate[e]^T + dU.W_up[e]^T. */
+/* Input gradient of the expert rows (icman section 2.3, differentiated),
+ * row i of expert e:
+ *   dxs[i] = dG[i].W_gate[e]^T + dU[i].W_up[e]^T (one float32 sum over both
+ *   contractions, stored rounded).
+ *   dg, du [NK,F] from moe_ffn_bwd_dact; w_gate, w_up [E,H,F]; tiles,
+ *   num_tiles from moe_permute_meta; dxs [NK,H] out.  Errors: MOE_EINVAL for
+ *   a bad shape or a null/misaligned pointer. */
 int moe_ffn_bwd_dx(const moe_dims* d, const void* dg, const void* du, const void* w_gate, const void* w_up,
                    const int32_t* tiles, const int32_t* num_tiles, void* dxs, hipStream_t stream);
 
-/* The three weight gradients, one owner per output tile. */
+/* Weight gradients of the experts (icman section 2.3, differentiated; fp32
+ * gradient buffers as the MoonEP page's section 04 keeps them):
+ *   dW_gate[e] = xs_e^T.dG_e, dW_up[e] = xs_e^T.dU_e, dW_down[e] = A_e^T.dys_e
+ * with xs_e, A_e, ... the rows offsets[e] .. offsets[e+1]-1.  One workgroup
+ * owns each output tile and sums the expert's rows in ascending order, so
+ * results are bitwise reproducible; experts with no rows get exact zeros.
+ *   xs [NK,H]; act [NK,F]; dys [NK,H]; dg, du [NK,F]; offsets [E+1];
+ *   dw_gate, dw_up [E,H,F] f32 out; dw_down [E,F,H] f32 out.  Errors:
+ *   MOE_EINVAL for a bad shape or a null/misaligned pointer. */
 int moe_ffn_bwd_dw(const moe_dims* d, const void* xs, const void* act, const void* dys, const void* dg,
                    const void* du, const int32_t* offsets, float* dw_gate, float* dw_up, float* dw_down,
                    hipStream_t stream);
@@ -271,9 +327,9 @@ int moe_ffn_bwd_dw(const moe_dims* d, const void* xs, const void* act, const voi
  * dX tiles fill the CUs they leave idle (the weight gradients alone have
  * 3*E*ceil(H/256)*ceil(F/256) tiles, 192 at H = 512, F = 1024, E = 8).  Every
  * output element has one owner and the same ascending contraction order as
- * in the separate calls.  With MOE_GEMM_TILES set in the environment, and
- * for float32, it makes the two separate launches.  Arguments as in those
- * two calls. */
+ * in the separate calls.  With a forced tile family (moe_dims.gemm_tiles),
+ * and for float32, it makes the two separate launches.  Arguments as in
+ * those two calls. */
 int moe_ffn_bwd_dx_dw(const moe_dims* d, const void* dg, const void* du, const void* w_gate, const void* w_up,
                       const int32_t* tiles, const int32_t* num_tiles, void* dxs, const void* xs, const void* act,
                       const void* dys, const int32_t* offsets, float* dw_gate, float* dw_up, float* dw_down,
@@ -297,7 +353,10 @@ int moe_ffn_bwd_dx_dw_gather(const moe_dims* d, const void* dg, const void* du, 
                              const int32_t* offsets, float* dw_gate, float* dw_up, float* dw_down,
                              hipStream_t stream);
 
-/* Backward of the gather plus the router's input gradient:
+/* Backward of the gather plus the router's input gradient (MegaBlocks
+ * section 4: the backward of a gather is a scatter, here a gather-sum over
+ * each token's K rows so that no atomics are needed; the router term is the
+ * logits' input gradient, icman section 2.2):
  *   dx[n] = sum_k dxs[inv[n*K+k]] + sum_k dlogits[n,e_k] * W_r[:,e_k],
  *   k ascending, float32 accumulation, one rounding.
  *   dxs [NK,H]; inv [NK]; topk_idx [N,K]; dlogits [N,E] f32; w_r [H,E];

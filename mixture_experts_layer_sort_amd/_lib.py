@@ -23,6 +23,8 @@ MOE_ENTRY_PERMUTE_META, MOE_ENTRY_ROUTE_BWD, MOE_ENTRY_PERMUTE_BWD = 1, 2, 3
 MOE_ENTRY_AUX_LOSS, MOE_ENTRY_ROUTE_BWD_AUX = 4, 5
 MOE_ENTRY_SHARED_FFN, MOE_ENTRY_SHARED_FFN_BWD, MOE_ENTRY_ROUTE_META = 6, 7, 8
 MOE_TILE_M = 256
+# moe_gemm_tiles (moe_dims.gemm_tiles): AUTO, or one bf16 tile family forced on every GEMM stage
+MOE_TILES_AUTO, MOE_TILES_256, MOE_TILES_128X256, MOE_TILES_128 = 0, 1, 2, 3
 
 # Every exported symbol with (restype, argtypes); the tests check this list
 # against include/moe.h and against the built library.
@@ -34,7 +36,7 @@ _F = ctypes.c_float
 
 
 class moe_dims(ctypes.Structure):
-    _fields_ = [("N", _I64), ("H", _I64), ("F", _I64), ("E", _I64), ("K", _I64), ("dtype", _I32), ("reserved", _I32)]
+    _fields_ = [("N", _I64), ("H", _I64), ("F", _I64), ("E", _I64), ("K", _I64), ("dtype", _I32), ("gemm_tiles", _I32)]
 
 
 _DP = ctypes.POINTER(moe_dims)
@@ -100,8 +102,8 @@ def lib(path: Optional[str] = None) -> ctypes.CDLL:
     return h
 
 
-def dims(N: int, H: int, F: int, E: int, K: int, dtype: int) -> moe_dims:
-    return moe_dims(N, H, F, E, K, dtype, 0)
+def dims(N: int, H: int, F: int, E: int, K: int, dtype: int, gemm_tiles: int = MOE_TILES_AUTO) -> moe_dims:
+    return moe_dims(N, H, F, E, K, dtype, gemm_tiles)
 
 
 def dtype_code(t: torch.dtype) -> int:

@@ -20,7 +20,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Shape and limit checks shared by every entry point.
 int check_dims(const moe_dims* d, Dims* out) {
   if (d == nullptr) return MOE_EINVAL;
-  if (d->reserved != 0) return MOE_EINVAL;
+  if (d->gemm_tiles < MOE_TILES_AUTO || d->gemm_tiles > MOE_TILES_128) return MOE_EINVAL;
   if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_EUNSUPPORTED;
   if (d->N < 0 || d->H <= 0 || d->F <= 0 || d->E <= 0 || d->K <= 0) return MOE_EINVAL;
   if (d->H % 128 != 0 || d->F % 128 != 0) return MOE_EINVAL;
@@ -34,6 +34,7 @@ int check_dims(const moe_dims* d, Dims* out) {
   out->E = d->E;
   out->K = d->K;
   out->dtype = d->dtype;
+  out->tiles = d->gemm_tiles;
   return MOE_OK;
 }
 

@@ -138,6 +138,7 @@ namespace moe_launch {
 struct Dims {
   int64_t N, H, F, E, K;
   int dtype;
+  int tiles = 0;  // moe_gemm_tiles: 0 = chosen per stage
   int64_t NK() const { return N * K; }
 };
 int64_t max_tiles(const Dims& d);

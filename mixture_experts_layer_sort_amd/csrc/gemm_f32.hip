@@ -6,8 +6,6 @@
 // with one thread per output element and the contraction in ascending k.
 // This path exists for the fp32 storage type (small correctness-sized
 // problems); the bf16 path carries the performance.
-#include <cstdlib>
-#include <cstring>
 
 #include "common.h"
 
@@ -202,24 +200,24 @@ hipError_t ffn_bwd_dx_dw_big(const Dims&, const void*, const void*, const void*,
 //   epilogue overlaps across two workgroups per CU);
 //   dX (contraction 2F): 256 x 256 from 2F = 2560 on;
 //   dW (contraction over an expert's rows): 256 x 256 throughout.
-// MOE_GEMM_TILES=256, =128x256 or =128 in the environment (read at every
-// launch) overrides the choice for every stage (128 selects the 128 x 256 DMA
-// dA tiles); any other value, or none, keeps the measured choice.  SmallR is
+// A forced family in Dims::tiles (moe_dims.gemm_tiles: 256, 128 x 256 or
+// 128, the last selecting the 128 x 256 DMA dA tiles) overrides the choice
+// for every stage of the call; AUTO keeps the measured choice.  SmallR is
 // only ever the measured choice.
 enum class Tiles { Small, SmallR, MidR, Big };
-static Tiles pick(Tiles measured) {
-  const char* v = std::getenv("MOE_GEMM_TILES");
-  if (v == nullptr) return measured;
-  if (std::strcmp(v, "256") == 0) return Tiles::Big;
-  if (std::strcmp(v, "128x256") == 0) return Tiles::MidR;
-  if (std::strcmp(v, "128") == 0) return Tiles::Small;
-  return measured;
+static Tiles pick(const Dims& d, Tiles measured) {
+  switch (d.tiles) {
+    case MOE_TILES_256: return Tiles::Big;
+    case MOE_TILES_128X256: return Tiles::MidR;
+    case MOE_TILES_128: return Tiles::Small;
+    default: return measured;
+  }
 }
-static Tiles tiles_gate_up(const Dims& d) { return pick(d.H >= 2048 ? Tiles::Big : Tiles::SmallR); }
-static Tiles tiles_down(const Dims& d) { return pick(d.F >= 1280 ? Tiles::Big : Tiles::SmallR); }
-static Tiles tiles_dact(const Dims& d) { return pick(d.H >= 4096 ? Tiles::Big : Tiles::Small); }
-static Tiles tiles_dx(const Dims& d) { return pick(2 * d.F >= 2560 ? Tiles::Big : Tiles::Small); }
-static Tiles tiles_dw(const Dims&) { return pick(Tiles::Big); }
+static Tiles tiles_gate_up(const Dims& d) { return pick(d, d.H >= 2048 ? Tiles::Big : Tiles::SmallR); }
+static Tiles tiles_down(const Dims& d) { return pick(d, d.F >= 1280 ? Tiles::Big : Tiles::SmallR); }
+static Tiles tiles_dact(const Dims& d) { return pick(d, d.H >= 4096 ? Tiles::Big : Tiles::Small); }
+static Tiles tiles_dx(const Dims& d) { return pick(d, 2 * d.F >= 2560 ? Tiles::Big : Tiles::Small); }
+static Tiles tiles_dw(const Dims& d) { return pick(d, Tiles::Big); }
 
 hipError_t ffn_gate_up(const Dims& d, const void* xs, const int32_t* sorted_flat, const void* wg, const void* wu,
                        const int32_t* tiles, const int32_t* num_tiles, void* g, void* u, void* a, hipStream_t s) {
@@ -302,13 +300,13 @@ hipError_t ffn_bwd_dw(const Dims& d, const void* xs, const int32_t* sorted_flat,
 // dX and the weight gradients.  bf16: one launch of 256 x 256 tiles, the
 // weight-gradient tiles first and the dX tiles filling the CUs they leave
 // idle (at (H, F, E) = (512, 1024, 8) the weight gradients alone have 192
-// workgroups for 256 CUs); with MOE_GEMM_TILES set, the two stages run as
-// separate launches of the forced family.  float32: two launches.
+// workgroups for 256 CUs); with a forced tile family the two stages run as
+// separate launches of that family.  float32: two launches.
 hipError_t ffn_bwd_dx_dw(const Dims& d, const void* dg, const void* du, const void* wg, const void* wu,
                          const int32_t* tiles, const int32_t* num_tiles, void* dxs, const void* xs,
                          const int32_t* sorted_flat, const void* a, const void* dys, const int32_t* offsets,
                          float* dwg, float* dwu, float* dwd, hipStream_t s) {
-  if (d.dtype == MOE_BF16 && std::getenv("MOE_GEMM_TILES") == nullptr)
+  if (d.dtype == MOE_BF16 && d.tiles == MOE_TILES_AUTO)
     return ffn_bwd_dx_dw_big(d, dg, du, wg, wu, tiles, num_tiles, dxs, xs, sorted_flat, a, dys, offsets, dwg, dwu,
                              dwd, s);
   hipError_t st = ffn_bwd_dx(d, dg, du, wg, wu, tiles, num_tiles, dxs, s);

@@ -37,7 +37,7 @@ class MoELayerRunner:
     def __init__(self, N: int, H: int, F: int, E: int, K: int, dtype: torch.dtype, device="cuda",
                  backward: bool = True, save_gu: Optional[bool] = None, aux_alpha: Optional[float] = None,
                  capacity: Optional[int] = None, shared_ffn: Optional[int] = None, gather: Optional[bool] = None,
-                 dw_gather: bool = False):
+                 dw_gather: bool = False, gemm_tiles: int = L.MOE_TILES_AUTO):
         """aux_alpha: weight of the Switch load-balancing loss; None turns it off.
         capacity: expert capacity (rows per expert, the overflow dropped);
         None is the dropless layer.  shared_ffn: intermediate size Fs of a
@@ -45,11 +45,13 @@ class MoELayerRunner:
         as ``shared``); None: no shared expert.  gather: gate/up reads the
         grouped rows straight from x; None: whenever N*H < 2^31.  dw_gather:
         the weight gradients read them from x as well, so xs is never
-        materialised (needs the gathered gate/up)."""
+        materialised (needs the gathered gate/up).  gemm_tiles: a
+        moe_gemm_tiles value forcing one bf16 GEMM tile family on every
+        stage (tests); AUTO lets the library choose per stage."""
         self.N, self.H, self.F, self.E, self.K = N, H, F, E, K
         self.dtype = dtype
         self.device = torch.device(device)
-        self.d = L.dims(N, H, F, E, K, L.dtype_code(dtype))
+        self.d = L.dims(N, H, F, E, K, L.dtype_code(dtype), gemm_tiles)
         self.capacity = capacity
         self.with_backward = backward
         save_gu = backward if save_gu is None else save_gu

@@ -528,11 +528,26 @@ def token_backward(tf: dict, dyn, w_r, expert_weights: ExpertFn, store: str = "b
 # bfloat16 differs from the exact value by a few float32 roundings.  Where the
 # exact value lies that close to a rounding midpoint, either neighbouring
 # bfloat16 value is a correct result, and the choice propagates into later
-# sums.  rounding_bands() returns, per element of each output, a first-order
-# bound of the deviation such choices can cause; it is zero wherever no
-# rounding decision upstream of the element was ambiguous.  Tests compare
-# |device - oracle| <= tolerance + band, which checks every unique result
-# exactly and every ambiguous one for validity.
+# sums.  rounding_bands() returns, per element of each bf16-stored tensor, a
+# first-order bound of the deviation such choices can cause, capped at two
+# bf16 spacings of the element (of the element and the K rows summed into it,
+# for y and dx); it is zero wherever no rounding decision upstream of the
+# element was ambiguous.  Tests compare |device - oracle| <= tolerance + band,
+# which checks every unique result exactly and every ambiguous one for
+# validity.  The float32 outputs (dgates, dlogits, the weight gradients) get
+# no band: they sum bf16-stored values over H or over thousands of tokens, so
+# the flips of two correct runs add up there, and they are checked step by
+# step from the run's own stored inputs instead.
+
+BAND_CAP_SPACINGS = 2.0
+
+
+def bf16_spacing(v: np.ndarray) -> np.ndarray:
+    """Distance from the bfloat16 value v to the next one away from zero
+    (2^(e - 7) for |v| in [2^e, 2^(e+1))); 0 at v = 0."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, np.exp2(e - 7), 0.0)
 
 U32 = 2.0 ** -24  # unit roundoff of float32
 
@@ -576,10 +591,12 @@ def prop(dev: np.ndarray, w: np.ndarray) -> np.ndarray:
     return np.minimum(dev @ np.abs(w), 4.0 * np.sqrt((dev * dev) @ (w * w)))
 
 
-def rounding_bands(fwd: dict, bwd: Optional[dict] = None, dy=None, aux_scale: Optional[float] = None) -> dict:
-    """Per-element deviation bounds (see above) of every stored tensor and
-    output of a bf16-storage forward (and backward, with the load-balancing
-    loss gradient when aux_scale is given) computed by this module."""
+def rounding_bands(fwd: dict, bwd: Optional[dict] = None, dy=None, aux_scale: Optional[float] = None,
+                   cap: bool = True) -> dict:
+    """Per-element deviation bounds (see above) of every bf16-stored tensor
+    of a bf16-storage forward (and backward, with the load-balancing loss
+    gradient when aux_scale is given) computed by this module, each capped
+    at BAND_CAP_SPACINGS bf16 spacings."""
     assert fwd["store"] == "bf16"
     K = fwd["K"]
     x, w_r = fwd["x"], fwd["w_r"]
@@ -631,7 +648,7 @@ def rounding_bands(fwd: dict, bwd: Optional[dict] = None, dy=None, aux_scale: Op
         sy += g * b["ys"][r] + 8 * U32 * np.abs(g * ys[r])
     b["y"] = bf16_flip(yp, fwd["y"], sy)
     if bwd is None:
-        return b
+        return _capped(b, fwd, None, cap)
 
     dy = as_f64(dy)
     # combine backward
@@ -648,8 +665,6 @@ def rounding_bands(fwd: dict, bwd: Optional[dict] = None, dy=None, aux_scale: Op
     for k in ("dG", "dU"):
         b[k] = np.zeros((NK, F))
     b["dxs"] = np.zeros((NK, H))
-    for k in ("dw_gate", "dw_up", "dw_down"):
-        b[k] = np.zeros_like(fwd[k.replace("dw_", "w_")])
     for e in range(E):
         r0, r1 = int(off[e]), int(off[e + 1])
         if r1 == r0:
@@ -672,11 +687,6 @@ def rounding_bands(fwd: dict, bwd: Optional[dict] = None, dy=None, aux_scale: Op
         dxp = dG @ wg.T + dU @ wu.T
         sdx = gemm_sigma(dG, wg.T) + gemm_sigma(dU, wu.T) + prop(b["dG"][sl], wg.T) + prop(b["dU"][sl], wu.T)
         b["dxs"][sl] = bf16_flip(dxp, bwd["dxs"][sl], sdx)
-        xt = xs[sl].T
-        b["dw_gate"][e] = prop(b["dG"][sl].T, xt.T).T + gemm_sigma(xt, dG) + 2 * U32 * np.abs(bwd["dw_gate"][e])
-        b["dw_up"][e] = prop(b["dU"][sl].T, xt.T).T + gemm_sigma(xt, dU) + 2 * U32 * np.abs(bwd["dw_up"][e])
-        b["dw_down"][e] = (prop(b["A"][sl].T, d) + prop(b["dys"][sl].T, A[sl]).T + gemm_sigma(A[sl].T, d)
-                           + 2 * U32 * np.abs(bwd["dw_down"][e]))
     # router backward
     g = fwd["gates"]
     sdl = g * (b["dgates"] + np.sum(g * b["dgates"], axis=1, keepdims=True)) + 8 * U32 * (
@@ -693,7 +703,6 @@ def rounding_bands(fwd: dict, bwd: Optional[dict] = None, dy=None, aux_scale: Op
         fmax = float(np.max(fwd["counts"])) / NK
         b["dlogits"] = b["dlogits"] + 64 * U32 * np.abs(aux) + (
             abs(aux_scale) * E / N * p * 4 * fmax * dl_max + 8 * U32 * np.abs(bwd["dlogits"]))
-    b["dw_r"] = prop(b["dlogits"].T, x).T + gemm_sigma(x.T, bwd["dlogits"]) + 2 * U32 * np.abs(bwd["dw_r"])
     # gather backward
     dxs_tok = bwd["dxs"][inv2] * kept2[:, :, None]
     dxp = dxs_tok.sum(axis=1) + bwd["dlogits"] @ w_r.T
@@ -715,13 +724,73 @@ def rounding_bands(fwd: dict, bwd: Optional[dict] = None, dy=None, aux_scale: Op
         dxsp = dGs @ sh["w_gate"].T + dUs @ sh["w_up"].T
         b["dxs_s"] = bf16_flip(dxsp, bwd["dxs_s"], gemm_sigma(dGs, sh["w_gate"].T) + gemm_sigma(dUs, sh["w_up"].T)
                                + prop(b["dG_s"], sh["w_gate"].T) + prop(b["dU_s"], sh["w_up"].T))
-        b["dw_gate_s"] = prop(b["dG_s"].T, x).T + gemm_sigma(x.T, dGs) + 2 * U32 * np.abs(bwd["dw_gate_s"])
-        b["dw_up_s"] = prop(b["dU_s"].T, x).T + gemm_sigma(x.T, dUs) + 2 * U32 * np.abs(bwd["dw_up_s"])
-        b["dw_down_s"] = (prop(b["A_s"].T, dy) + gemm_sigma(As.T, dy) + 2 * U32 * np.abs(bwd["dw_down_s"]))
         dxp = dxp + bwd["dxs_s"]
         sdx = sdx + b["dxs_s"] + 8 * U32 * np.abs(bwd["dxs_s"])
     b["dx"] = bf16_flip(dxp, bwd["dx"], sdx)
-    return b
+    return _capped(b, fwd, bwd, cap)
+
+
+def _capped(b: dict, fwd: dict, bwd: Optional[dict], cap: bool = True) -> dict:
+    """The bands of the bf16-stored tensors, each at most BAND_CAP_SPACINGS
+    spacings of the element; for y and dx the spacings of the K rows (and
+    the shared expert's row) summed into the element count as well."""
+    c = BAND_CAP_SPACINGS if cap else np.inf
+    vals = dict(fwd)
+    if bwd is not None:
+        vals.update(bwd)
+    sh = fwd.get("shared")
+    if sh is not None:
+        vals.update({k + "_s": sh[k] for k in ("G", "U", "A", "ys")})
+    N, K = fwd["gates"].shape
+    inv = fwd["inv"].reshape(N, K)
+    kept = (inv >= 0)[:, :, None]
+    rows = np.maximum(inv, 0)
+    out = {}
+    for name in ("G", "U", "A", "ys", "dys", "dG", "dU", "dxs", "G_s", "U_s", "A_s", "ys_s", "dG_s", "dU_s", "dxs_s"):
+        if name in b and name in vals:
+            out[name] = np.minimum(b[name], c * bf16_spacing(vals[name]))
+    cap_y = bf16_spacing(fwd["y"]) + (fwd["gates"][:, :, None] * bf16_spacing(fwd["ys"])[rows] * kept).sum(axis=1)
+    if sh is not None:
+        cap_y = cap_y + bf16_spacing(sh["ys"])
+    out["y"] = np.minimum(b["y"], c * cap_y)
+    if bwd is not None:
+        cap_dx = bf16_spacing(bwd["dx"]) + (bf16_spacing(bwd["dxs"])[rows] * kept).sum(axis=1)
+        if "dxs_s" in bwd:
+            cap_dx = cap_dx + bf16_spacing(bwd["dxs_s"])
+        out["dx"] = np.minimum(b["dx"], c * cap_dx)
+    return out
+
+
+# --------------------------------------------------------------------------
+# some rows of one expert (sampled checks at full size)
+# --------------------------------------------------------------------------
+
+def expert_rows(xs, g, dy_rows, w_gate_e, w_up_e, w_down_e, store: str = "bf16") -> dict:
+    """Every per-row quantity of some routed rows of one expert, from the
+    layer's inputs: xs [R, H] the rows' tokens, g [R] their gates, dy_rows
+    [R, H] (or None) the upstream gradients of their tokens.  The same steps
+    and storage rounding points as ``forward`` and ``backward`` (SwiGLU
+    expert of "MoE computation principle and execution process" section 2.3,
+    its derivative, the combine backward's gate-weighted gather):
+        G = xs.Wg, U = xs.Wu, A = silu(G) U, ys = A.Wd;
+        dys = g dy, dA = dys.Wd^T, dG = dA U silu'(G), dU = dA silu(G),
+        dxs = dG.Wg^T + dU.Wu^T.
+    A row depends on its token and its expert alone, so any subset of a
+    layer's rows gives the layer's values for those rows."""
+    xs = as_f64(xs)
+    wg, wu, wd = as_f64(w_gate_e), as_f64(w_up_e), as_f64(w_down_e)
+    G, U, A, ys = swiglu_expert(xs, wg, wu, wd, store)
+    out = dict(xs=xs, G=G, U=U, A=A, ys=ys)
+    if dy_rows is None:
+        return out
+    dys = rho(as_f64(g).reshape(-1, 1) * as_f64(dy_rows), store)
+    dA = dys @ wd.T
+    sg = sigmoid(G)
+    dG = rho(dA * U * sg * (1.0 + G * (1.0 - sg)), store)
+    dU = rho(dA * (G * sg), store)
+    dxs = rho(dG @ wg.T + dU @ wu.T, store)
+    out.update(dys=dys, dG=dG, dU=dU, dxs=dxs)
+    return out
 
 
 # --------------------------------------------------------------------------
@@ -730,8 +799,8 @@ def rounding_bands(fwd: dict, bwd: Optional[dict] = None, dy=None, aux_scale: Op
 
 def weight_grad_slices(x, dy, topk, gates, e: int, w_gate_e, w_up_e, w_down_e, cols, store: str = "bf16") -> dict:
     """Columns ``cols`` of dW_gate[e] and dW_up[e] and rows ``cols`` of
-    dW_down[e], with their rounding bands (bf16 storage), from the layer's
-    inputs and a given assignment (topk [N, K], gates [N, K]).
+    dW_down[e] from the layer's inputs and a given assignment (topk [N, K],
+    gates [N, K]).
 
     The f-th column of G, U, A, dG and dU over expert e's rows is all these
     need, so the cost is a few matrix-vector products per column:
@@ -740,10 +809,8 @@ def weight_grad_slices(x, dy, topk, gates, e: int, w_gate_e, w_up_e, w_down_e, c
         dys    = g dy[n]        dA[:, f] = dys.Wd[f, :]
         dG     = dA U silu'(G)  dU = dA silu(G)
         dW_gate[:, f] = xs^T dG   dW_up[:, f] = xs^T dU   dW_down[f, :] = A^T dys
-    with the same storage rounding points as ``forward`` / ``backward``; the
-    bands follow ``rounding_bands`` restricted to these columns (every band
-    term of a column depends on that column alone).  Returns dw_gate [H, C],
-    dw_up [H, C], dw_down [C, H] (C = len(cols)) and band_* of the same shapes.
+    with the same storage rounding points as ``forward`` / ``backward``.
+    Returns dw_gate [H, C], dw_up [H, C], dw_down [C, H] (C = len(cols)).
     """
     x, dy = as_f64(x), as_f64(dy)
     topk = np.asarray(topk)
@@ -757,34 +824,13 @@ def weight_grad_slices(x, dy, topk, gates, e: int, w_gate_e, w_up_e, w_down_e, c
     wd = as_f64(w_down_e)[cols, :]
     H = x.shape[1]
     xs = x[tok]
-    dysp = gflat[flat][:, None] * dy[tok]
-    dys = rho(dysp, store)
-    Gp, Up = xs @ wg, xs @ wu
-    G, U = rho(Gp, store), rho(Up, store)
-    ap = silu(G) * U
-    A = rho(ap, store)
+    dys = rho(gflat[flat][:, None] * dy[tok], store)
+    G, U = rho(xs @ wg, store), rho(xs @ wu, store)
+    A = rho(silu(G) * U, store)
     dA = dys @ wd.T
     sg = sigmoid(G)
-    dgp = dA * U * sg * (1.0 + G * (1.0 - sg))
-    dup = dA * (G * sg)
-    dG, dU = rho(dgp, store), rho(dup, store)
+    dG = rho(dA * U * sg * (1.0 + G * (1.0 - sg)), store)
+    dU = rho(dA * (G * sg), store)
     out = dict(dw_gate=xs.T @ dG, dw_up=xs.T @ dU, dw_down=A.T @ dys)
-    if store != "bf16":
-        for k in ("dw_gate", "dw_up", "dw_down"):
-            out["band_" + k] = np.zeros_like(out[k])
-        return out
-    bG = bf16_flip(Gp, G, gemm_sigma(xs, wg))
-    bU = bf16_flip(Up, U, gemm_sigma(xs, wu))
-    d1, d2 = _silu_d1(G), _silu_d2(G)
-    bA = bf16_flip(ap, A, np.abs(U * d1) * bG + np.abs(silu(G)) * bU + 16 * U32 * np.abs(ap))
-    bdys = bf16_flip(dysp, dys, 8 * U32 * np.abs(dysp))
-    sdA = gemm_sigma(dys, wd.T) + prop(bdys, wd.T)
-    bdG = bf16_flip(dgp, dG, np.abs(U * d1) * sdA + np.abs(dA * d1) * bU + np.abs(dA * U * d2) * bG
-                    + 16 * U32 * np.abs(dgp))
-    bdU = bf16_flip(dup, dU, np.abs(silu(G)) * sdA + np.abs(dA * d1) * bG + 16 * U32 * np.abs(dup))
-    out["band_dw_gate"] = prop(bdG.T, xs).T + gemm_sigma(xs.T, dG) + 2 * U32 * np.abs(out["dw_gate"])
-    out["band_dw_up"] = prop(bdU.T, xs).T + gemm_sigma(xs.T, dU) + 2 * U32 * np.abs(out["dw_up"])
-    out["band_dw_down"] = (prop(bA.T, dys) + prop(bdys.T, A).T + gemm_sigma(A.T, dys)
-                           + 2 * U32 * np.abs(out["dw_down"]))
     assert out["dw_gate"].shape == (H, cols.size)
     return out

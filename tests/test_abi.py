@@ -48,10 +48,8 @@ def test_status_strings(lib):
         assert isinstance(L.moe_status_str(st), str) and L.moe_status_str(st)
 
 
-def D(N=64, H=128, F=256, E=4, K=2, dtype=L.MOE_BF16, reserved=0):
-    d = L.dims(N, H, F, E, K, dtype)
-    d.reserved = reserved
-    return d
+def D(N=64, H=128, F=256, E=4, K=2, dtype=L.MOE_BF16, gemm_tiles=L.MOE_TILES_AUTO):
+    return L.dims(N, H, F, E, K, dtype, gemm_tiles)
 
 
 FAKE = 0x10000  # never dereferenced: every call below fails validation or has N = 0
@@ -64,7 +62,8 @@ def route(d, x=FAKE, w=FAKE, b=None, t=FAKE, g=FAKE):
 @pytest.mark.parametrize("d,status", [
     (D(H=100), L.MOE_EINVAL), (D(F=200), L.MOE_EINVAL), (D(N=-1), L.MOE_EINVAL), (D(E=0), L.MOE_EINVAL),
     (D(K=0), L.MOE_EINVAL), (D(K=5, E=4), L.MOE_EUNSUPPORTED), (D(E=300, K=2), L.MOE_EUNSUPPORTED),
-    (D(E=16, K=9), L.MOE_EUNSUPPORTED), (D(dtype=7), L.MOE_EUNSUPPORTED), (D(reserved=1), L.MOE_EINVAL),
+    (D(E=16, K=9), L.MOE_EUNSUPPORTED), (D(dtype=7), L.MOE_EUNSUPPORTED), (D(gemm_tiles=4), L.MOE_EINVAL),
+    (D(gemm_tiles=-1), L.MOE_EINVAL),
     (D(N=2 ** 30, K=2), L.MOE_EUNSUPPORTED),
 ])
 def test_bad_dims_rejected(lib, d, status):

@@ -10,7 +10,7 @@ import torch
 
 from moe_workloads import BASE, TEST_CONFIGS, TINY, MoEConfig
 from oracle import moe_oracle as O
-from tests.gpu_common import assert_close, gpu_inputs, oracle_fwd, store_of, sync, to_np
+from tests.gpu_common import assert_close, check_runner_steps, gpu_inputs, oracle_fwd, store_of, sync, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -106,6 +106,9 @@ def test_aux_loss_forward_and_backward(cfg):
     bd = O.rounding_bands(of, ob, cpu["dy"], aux_scale=ALPHA) if dt == "bf16" else {}
     for name in ("dlogits", "dw_r", "dx", "dgates", "dw_gate", "dw_up", "dw_down"):
         assert_close(name, grads[name], ob[name], dt, band=bd.get(name))
+    # every step from its own stored inputs, the loss term from the stored probabilities
+    check_runner_steps(cfg, cpu, r, None, grads,
+                       aux=dict(probs=to_np(r.probs), counts=r.counts.cpu().numpy(), scale=ALPHA))
 
 
 def test_aux_loss_bitwise_reproducible():

@@ -16,7 +16,7 @@ import torch
 
 from moe_workloads import BASE, SKEWED, TEST_CONFIGS, make_inputs
 from oracle import moe_oracle as O
-from tests.gpu_common import assert_close, gpu_inputs, store_of, sync, to_np
+from tests.gpu_common import assert_close, check_runner_steps, gpu_inputs, store_of, sync, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -84,6 +84,7 @@ def test_capacity_layer_matches_oracle(cfg, cf):
         assert_close(name, t, ref[name], dt, band=bd.get(name))
     dropped = of["inv"].reshape(cfg.N, cfg.K) < 0
     assert np.all(to_np(g["dgates"])[dropped] == 0)
+    check_runner_steps(cfg, cpu, r, y, g, capacity=C)
 
 
 @pytest.mark.parametrize("cfg", [TEST_CONFIGS["t_skew"], TEST_CONFIGS["t_ragged"]], ids=lambda c: c.name)

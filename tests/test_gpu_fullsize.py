@@ -2,21 +2,27 @@
 benchmark times (MoELayerRunner: the same entry points, dims and stream).
 
 The default workload (N=16384, H=512, F=1024, E=8, K=2) is compared element
-by element with the whole-layer oracle.  The larger workloads are compared on
-what the oracle can compute one by one:
+by element with the whole-layer oracle, and every step of it from its own
+stored inputs (tests/parity.py, both levels).  The larger workloads are
+compared on what the oracle can compute one by one, so that every tile of
+every grouped GEMM is in some oracle comparison:
   * the routing of every token: top-K bit-exact away from near-ties, gates;
   * the routing metadata and tile list of every row, bit-exact;
+  * one row of every 256-row list tile of every expert (the last row of each
+    expert's last, ragged tile): xs, G, U, A, ys (and dys, dG, dU, dxs)
+    against the oracle's values of that row (oracle.expert_rows), within
+    2e-2 plus two bf16 spacings, and each of those steps from the row's own
+    stored inputs (tight);
   * sampled tokens (the first and last row of the hottest expert, the last
-    row of a ragged tile, random ones): every stored intermediate of their K
-    rows, y, dgates, dlogits and dx, against the oracle run on those tokens
-    alone with the same assignment (experts restricted to the ones they
-    use), with rounding bands;
-  * sampled columns of dW_gate / dW_up and rows of dW_down of the hottest, a
-    middle and the coldest non-empty expert, with bands; exact zeros for
-    experts without rows;
-  * properties that hold at any size, over every element: y = sum_k g ys[inv],
-    dx = sum_k dxs[inv] + dlogits W_r^T, dW_r = x^T dlogits, and
-    dW_gate[e] = xs_e^T dG_e on a column slice of the hottest expert.
+    row of a ragged tile, random ones): y, dgates, dlogits and dx against the
+    oracle run on those tokens alone with the same assignment;
+  * the weight gradients of every expert at one column of F in every
+    256-wide block, over all H (so every 256 x 256 output tile): against the
+    oracle (oracle.weight_grad_slices, rel-RMS) and from the run's own stored
+    rows (tight); exact zeros for experts without rows;
+  * the steps that are cheap at any size over every element: y = sum_k g
+    ys[inv], dgates = <dy, ys[inv]>, dlogits, dW_r = x^T dlogits and
+    dx = sum_k dxs[inv] + dlogits W_r^T.
 """
 import numpy as np
 import pytest
@@ -24,7 +30,9 @@ import torch
 
 from moe_workloads import BASE, LARGE, SKEWED, WIDE, make_inputs
 from oracle import moe_oracle as O
-from tests.gpu_common import assert_close, assignment_mismatch, gpu_inputs, oracle_fwd, sync, to_np
+from tests import parity as P
+from tests.gpu_common import (assert_close, assignment_mismatch, check_runner_steps, gpu_inputs, oracle_fwd,
+                              runner_run, sync, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -87,6 +95,8 @@ def test_default_workload_every_element():
     from mixture_experts_layer_sort_amd import _lib as L
     assert np.array_equal(r.tiles.cpu().numpy()[:3 * nt].reshape(-1, 3),
                           O.tile_list(of["counts"], of["offsets"], L.MOE_TILE_M))
+    _log("[full] every step from its stored inputs")
+    check_runner_steps(cfg, cpu, r, y, grads)
 
 
 # --------------------------------------------------------------------------
@@ -148,13 +158,67 @@ def _sample_tokens(cfg, counts, offsets, sorted_flat, n_random, seed=11):
     return sorted(set(picks))
 
 
+def _tile_rows(tiles, seed=5):
+    """One grouped row per list tile: a random row of each full tile, the
+    last row of each expert's last tile."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for i, (e, r0, n) in enumerate(tiles):
+        last = i + 1 == len(tiles) or tiles[i + 1][0] != e
+        rows.append(int(r0 + n - 1) if last else int(r0 + rng.integers(n)))
+    return np.asarray(rows, dtype=np.int64)
+
+
 def _rows(t, idx):
     return to_np(t[torch.as_tensor(idx, dtype=torch.int64, device=t.device)].cpu())
 
 
+def _expert_w(dev, e):
+    return tuple(to_np(dev[k][e].cpu()) for k in ("w_gate", "w_up", "w_down"))
+
+
+def _tile_row_checks(cfg, dev, r, x, gates, rows):
+    """Both levels on one row of every list tile: the oracle's values of the
+    rows (from x and the weights alone) and each step from the rows' stored
+    inputs."""
+    K = cfg.K
+    off = r.offsets.cpu().numpy().astype(np.int64)
+    sf = r.sorted_flat.cpu().numpy().astype(np.int64)
+    exp = P.expert_of_rows(off, rows)
+    bufs = {"xs": r.xs, "G": r.g, "U": r.u, "A": r.act, "ys": r.ys}
+    run = runner_run(r)
+    dy = None
+    if cfg.backward:
+        bufs.update({"dys": r.dys, "dG": r.dg, "dU": r.du, "dxs": r.dxs})
+        run.t.update(dys=r.dys, dG=r.dg, dU=r.du, dxs=r.dxs)
+        dy = _host(dev["dy"])
+    quiet = lambda msg: None  # noqa: E731
+    worst = {}
+    for e in np.unique(exp):
+        rr = rows[exp == e]
+        tok = sf[rr] // K
+        w = _expert_w(dev, int(e))
+        ref = O.expert_rows(x[tok], gates.reshape(-1)[sf[rr]], None if dy is None else dy[tok], *w, "bf16")
+        for name, buf in bufs.items():
+            if buf is None:
+                continue
+            band = O.BAND_CAP_SPACINGS * O.bf16_spacing(ref[name])
+            m = P.compare_with_oracle(f"{name}[expert {e}, {rr.size} tile rows]", _rows(buf, rr), ref[name], "bf16",
+                                      band=band, log=quiet)
+            worst[name] = max(worst.get(name, 0.0), m["max_err"])
+        # each step of those rows from its own stored inputs
+        P.check_rows_forward(x, lambda _e: w, K, run, rr, "bf16", log=quiet)
+        if dy is not None:
+            P.check_rows_backward(lambda _e: w, K, run, dy, rr, "bf16", log=quiet)
+    for name, v in worst.items():
+        _log(f"[tile rows] {name}: {rows.size} rows (one per list tile) vs the oracle, max|err| {v:.3e}")
+    _log(f"[tile rows] every step of the {rows.size} rows from its stored inputs")
+
+
 def _sampled_token_checks(cfg, dev, r, x, topk, gates, tokens, y, grads):
     """The oracle on the sampled tokens alone, same assignment, experts
-    restricted to the ones they use."""
+    restricted to the ones they use: the token-level outputs y, dgates,
+    dlogits and dx."""
     K = cfg.K
     tsel = np.asarray(tokens)
     top_s = topk[tsel]
@@ -171,113 +235,58 @@ def _sampled_token_checks(cfg, dev, r, x, topk, gates, tokens, y, grads):
     of = O.forward(x[tsel], w_r[:, used], wg, wu, wd, K, bias=None if bias is None else bias[used], store="bf16",
                    topk=remap[top_s])
     assert np.max(np.abs(of["gates"] - gates[tsel])) <= 1e-7
-    ob = None
     if cfg.backward:
         dy_s = _rows(dev["dy"], tsel)
         ob = O.backward(of, dy_s)
         bd = O.rounding_bands(of, ob, dy_s)
     else:
         bd = O.rounding_bands(of)
-    inv_gpu = r.inv.cpu().numpy().astype(np.int64)
-    gpu_rows = inv_gpu.reshape(cfg.N, K)[tsel].reshape(-1)      # token-major (i, k)
-    ora_rows = of["inv"].reshape(len(tokens), K).reshape(-1)
-    # a forward-only runner gathers the rows inside gate/up and holds no xs
-    names = (["xs"] if r.xs is not None else []) + ["G", "U", "A", "ys"] + (
-        ["dys", "dG", "dU", "dxs"] if cfg.backward else [])
-    bufs = {"xs": r.xs, "G": r.g, "U": r.u, "A": r.act, "ys": r.ys}
-    if cfg.backward:
-        bufs.update({"dys": r.dys, "dG": r.dg, "dU": r.du, "dxs": r.dxs})
-    ref = dict(of)
-    if ob is not None:
-        ref.update(ob)
-    for name in names:
-        if bufs[name] is None:
-            continue
-        band = bd.get(name)
-        assert_close(f"{name}[sampled rows]", _rows(bufs[name], gpu_rows), ref[name][ora_rows], "bf16",
-                     band=None if band is None else band[ora_rows])
     assert_close("y[sampled]", _rows(y, tsel), of["y"], "bf16", band=bd["y"])
     if cfg.backward:
-        assert_close("dgates[sampled]", _rows(grads["dgates"], tsel), ob["dgates"], "bf16", band=bd["dgates"])
+        assert_close("dgates[sampled]", _rows(grads["dgates"], tsel), ob["dgates"], "bf16")
         dl = _rows(grads["dlogits"], tsel)
-        assert_close("dlogits[sampled]", dl[:, used], ob["dlogits"], "bf16", band=bd["dlogits"])
+        assert_close("dlogits[sampled]", dl[:, used], ob["dlogits"], "bf16")
         others = np.setdiff1d(np.arange(cfg.E), used)
         assert not dl[:, others].any(), "unselected logits must get exactly zero gradient"
         assert_close("dx[sampled]", _rows(grads["dx"], tsel), ob["dx"], "bf16", band=bd["dx"])
 
 
 def _weight_grad_checks(cfg, dev, r, x, topk, gates, counts, grads):
+    """Every expert's weight gradients at one column of F per 256-wide block
+    (all H): against the oracle's slices, and from the run's stored rows."""
     dy = _host(dev["dy"])
-    nonempty = np.where(counts > 0)[0]
-    order = nonempty[np.argsort(counts[nonempty], kind="stable")]
-    experts = sorted({int(order[-1]), int(order[len(order) // 2]), int(order[0])})
     rng = np.random.default_rng(3)
-    cols = sorted({0, int(rng.integers(1, cfg.F - 1)), cfg.F - 1})
-    for e in experts:
-        s = O.weight_grad_slices(x, dy, topk, gates, e, to_np(dev["w_gate"][e].cpu()), to_np(dev["w_up"][e].cpu()),
-                                 to_np(dev["w_down"][e].cpu()), cols, "bf16")
-        c = torch.as_tensor(cols, dtype=torch.int64, device=DEV)
-        assert_close(f"dw_gate[{e}][:, {cols}]", to_np(grads["dw_gate"][e].index_select(1, c).cpu()), s["dw_gate"],
-                     "bf16", band=s["band_dw_gate"])
-        assert_close(f"dw_up[{e}][:, {cols}]", to_np(grads["dw_up"][e].index_select(1, c).cpu()), s["dw_up"],
-                     "bf16", band=s["band_dw_up"])
-        assert_close(f"dw_down[{e}][{cols}, :]", to_np(grads["dw_down"][e].index_select(0, c).cpu()),
-                     s["dw_down"], "bf16", band=s["band_dw_down"])
-    for e in np.where(counts == 0)[0]:
-        for name in ("dw_gate", "dw_up", "dw_down"):
-            assert torch.count_nonzero(grads[name][int(e)]).item() == 0, f"{name}[{e}] of an empty expert"
+    cols = np.asarray([b + int(rng.integers(min(256, cfg.F - b))) for b in range(0, cfg.F, 256)], dtype=np.int64)
+    c = torch.as_tensor(cols, dtype=torch.int64, device=DEV)
+    worst = {}
+    for e in np.where(counts > 0)[0]:
+        e = int(e)
+        wg, wu, wd = _expert_w(dev, e)
+        s = O.weight_grad_slices(x, dy, topk, gates, e, wg, wu, wd, cols, "bf16")
+        for name, got in (("dw_gate", grads["dw_gate"][e].index_select(1, c)),
+                          ("dw_up", grads["dw_up"][e].index_select(1, c)),
+                          ("dw_down", grads["dw_down"][e].index_select(0, c))):
+            m = P.compare_with_oracle(f"{name}[{e}][{cols.size} columns]", to_np(got.cpu()), s[name], "bf16",
+                                      log=lambda msg: None)
+            worst[name] = max(worst.get(name, 0.0), m["max_err"])
+    for name, v in worst.items():
+        _log(f"[dW] {name}: {int((counts > 0).sum())} experts x {cols.size} columns (one per 256-block) vs the "
+             f"oracle, max|err| {v:.3e}")
+    run = runner_run(r, None, grads)
+    P.check_weight_grads(x, cfg.K, run, "bf16", experts=range(cfg.E), cols=cols, log=lambda msg: None)
+    _log(f"[dW] every expert's weight gradients at {cols.size} columns per matrix: every element from the stored "
+         f"rows; experts without rows exactly zero")
 
 
-def _within(name, got, pre, sigma):
-    """|got - pre| <= sigma element by element (got float32 results)."""
-    dev = np.abs(to_np(got) - pre)
-    worst = float((dev - sigma).max())
-    _log(f"{name}: max|dev| {float(dev.max()):.3e}, worst dev - bound {worst:.3e}")
-    assert worst <= 0, name
-
-
-def _rounded_within(name, got, pre, sigma):
-    """A bf16 result of a float32 sum whose exact value is pre (to within
-    sigma): equal to round(pre) unless the interval reaches a midpoint."""
-    rounded = O.round_bf16(pre)
-    band = O.bf16_flip(pre, rounded, sigma)
-    dev = np.abs(to_np(got) - rounded)
-    assert np.all(dev <= band), f"{name}: {int(np.sum(dev > band))} elements off"
-    _log(f"{name}: {int(np.sum(dev > 0))} of {dev.size} elements on the other side of a midpoint, all within band")
-
-
-def _property_checks(cfg, dev, r, x, grads, y):
-    K = cfg.K
-    inv = r.inv.cpu().numpy().astype(np.int64).reshape(cfg.N, K)
-    g = r.gates.cpu().numpy().astype(np.float64)
-    ys = to_np(r.ys.cpu())
-    terms = g[:, :, None] * ys[inv]
-    _rounded_within("y = sum_k g ys[inv]", y.cpu(), terms.sum(axis=1), 8 * U32 * np.abs(terms).sum(axis=1))
-    del ys, terms
+def _whole_tensor_steps(cfg, dev, r, x, grads, y):
+    """The steps that are cheap at any size, over every element."""
+    run = runner_run(r, y, grads)
+    P.check_combine(cfg.K, run, "bf16")
     if not cfg.backward:
         return
-    dxs = to_np(r.dxs.cpu())
-    dl = to_np(grads["dlogits"].cpu())
-    w_r = _host(dev["w_r"])
-    rows = dxs[inv].sum(axis=1)
-    pre = rows + dl @ w_r.T
-    sig = 8 * U32 * (np.abs(dxs[inv]).sum(axis=1) + np.abs(dl) @ np.abs(w_r.T)) + O.gemm_sigma(dl, w_r.T)
-    _rounded_within("dx = sum_k dxs[inv] + dlogits W_r^T", grads["dx"].cpu(), pre, sig)
-    del dxs, rows, pre, sig
-    ref = x.T @ dl
-    _within("dW_r = x^T dlogits", grads["dw_r"].cpu(), ref, O.gemm_sigma(x.T, dl) + 2 * U32 * np.abs(ref))
-    counts = r.counts.cpu().numpy()
-    off = r.offsets.cpu().numpy()
-    e = int(np.argmax(counts))
-    sl = slice(int(off[e]), int(off[e + 1]))
-    cols = slice(cfg.F - 128, cfg.F)
-    # the expert's rows of the grouped order, x[sorted_flat / K]
-    src = r.sorted_flat[sl].long() // cfg.K
-    xs_e = to_np(dev["x"][src].cpu())
-    dG_e = to_np(r.dg[sl, cols].cpu())
-    ref = xs_e.T @ dG_e
-    _within(f"dW_gate[{e}] = xs_e^T dG_e (last 128 columns)", grads["dw_gate"][e][:, cols].cpu(), ref,
-            O.gemm_sigma(xs_e.T, dG_e) + 2 * U32 * np.abs(ref))
+    P.check_combine_bwd_gates(cfg.K, run, _host(dev["dy"]))
+    P.check_route_bwd(x, cfg.K, run, "bf16")
+    P.check_permute_bwd(_host(dev["w_r"]), cfg.K, run, "bf16")
 
 
 @pytest.mark.parametrize("cfg,n_random", [(SKEWED, 2), (LARGE, 1), (WIDE, 0)], ids=lambda v: getattr(v, "name", ""))
@@ -291,11 +300,14 @@ def test_large_workload_sampled(cfg, n_random):
     grads = r.backward(dev["dy"]) if cfg.backward else None
     sync()
     counts, offsets, sorted_flat, inv = _metadata_exact(cfg, r, topk)
+    from mixture_experts_layer_sort_amd import _lib as L
+    rows = _tile_rows(O.tile_list(counts, offsets, L.MOE_TILE_M))
+    _tile_row_checks(cfg, dev, r, x, gates, rows)
     tokens = _sample_tokens(cfg, counts, offsets, sorted_flat, n_random)
     _sampled_token_checks(cfg, dev, r, x, topk, gates, tokens, y, grads)
     if cfg.backward:
         _weight_grad_checks(cfg, dev, r, x, topk, gates, counts, grads)
-    _property_checks(cfg, dev, r, x, grads, y)
+    _whole_tensor_steps(cfg, dev, r, x, grads, y)
     del r, dev
     torch.cuda.empty_cache()
 

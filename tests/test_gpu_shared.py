@@ -18,7 +18,7 @@ import torch
 
 from moe_workloads import BASE, TEST_CONFIGS, MoEConfig, make_shared_weights
 from oracle import moe_oracle as O
-from tests.gpu_common import assert_close, gpu_inputs, store_of, sync, to_np
+from tests.gpu_common import assert_close, check_runner_steps, gpu_inputs, store_of, sync, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -75,6 +75,7 @@ def test_shared_layer_matches_oracle(cfg, Fs):
            "dw_up_s": g["dw_up_s"], "dw_down_s": g["dw_down_s"]}
     for name, t in got.items():
         assert_close(name, t, ref[name], dt, band=bd.get(name))
+    check_runner_steps(cfg, cpu, r, y, g, shared=ws_cpu)
 
 
 def test_zero_down_projection_leaves_routed_results_unchanged():
@@ -169,6 +170,7 @@ def test_shared_expert_with_binding_capacity():
     ref.update(ob)
     for name, t in dict(y=y, **g).items():
         assert_close(name, t, ref[name], "bf16", band=bd.get(name))
+    check_runner_steps(cfg, cpu, r, y, g, capacity=C, shared=ws_cpu)
 
 
 def test_forward_only_runner_with_shared_expert_equals_training_forward():

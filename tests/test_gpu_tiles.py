@@ -1,7 +1,7 @@
 """Every bf16 GEMM tile shape against the oracle, element by element.
 
 The dispatcher picks the GEMM tile shape per stage from the problem size, so
-at small sizes only the 128-wide kernels run.  MOE_GEMM_TILES forces one
+at small sizes only the 128-wide kernels run.  moe_dims.gemm_tiles forces one
 family for every stage (256: the register-staged 256 x 256 kernels and the
 8-wave LDS DMA 256 x 256 dA kernel; 128x256: the register-staged 128 x 256
 kernels; 128: the 128 x 128 kernels and the 128 x 256 LDS DMA dA tiles);
@@ -17,7 +17,7 @@ import torch
 
 from moe_workloads import TEST_CONFIGS, MoEConfig
 from oracle import moe_oracle as O
-from tests.gpu_common import assert_close, gpu_inputs, oracle_fwd, sync
+from tests.gpu_common import assert_close, check_runner_steps, gpu_inputs, oracle_fwd, sync
 
 pytestmark = pytest.mark.gpu
 
@@ -35,9 +35,16 @@ def _gpu():
     _lib.lib()
 
 
-def _run(cfg, cpu, dev, of):
+def _family(tiles):
+    """moe_gemm_tiles value of a family name (None: the library's choice)."""
+    from mixture_experts_layer_sort_amd import _lib as L
+    return {None: L.MOE_TILES_AUTO, "256": L.MOE_TILES_256, "128x256": L.MOE_TILES_128X256,
+            "128": L.MOE_TILES_128}[tiles]
+
+
+def _run(cfg, cpu, dev, of, tiles):
     from mixture_experts_layer_sort_amd.layer import MoELayerRunner
-    r = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, "cuda")
+    r = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, "cuda", gemm_tiles=_family(tiles))
     y = r.forward(dev["x"], dev["w_r"], dev["w_gate"], dev["w_up"], dev["w_down"], dev["bias"],
                   topk=torch.from_numpy(of["topk"]).cuda(),
                   gates=torch.from_numpy(of["gates"].astype(np.float32)).cuda())
@@ -45,17 +52,18 @@ def _run(cfg, cpu, dev, of):
     sync()
     got = {"G": r.g, "U": r.u, "A": r.act, "ys": r.ys, "y": y, "dys": r.dys, "dG": r.dg, "dU": r.du, "dxs": r.dxs,
            "dx": g["dx"], "dw_gate": g["dw_gate"], "dw_up": g["dw_up"], "dw_down": g["dw_down"]}
-    return {k: v.clone() for k, v in got.items()}
+    return {k: v.clone() for k, v in got.items()}, (r, y, g)
 
 
 @pytest.mark.parametrize("tiles", ["256", "128x256", "128"])
 @pytest.mark.parametrize("cfg", CASES, ids=lambda c: c.name)
-def test_gemm_tiles_match_oracle(cfg, tiles, monkeypatch):
-    monkeypatch.setenv("MOE_GEMM_TILES", tiles)
+def test_gemm_tiles_match_oracle(cfg, tiles):
     print(f"[tiles {tiles}] {cfg.name}", flush=True)
     cpu, dev = gpu_inputs(cfg, 11, with_dy=True)
     of = oracle_fwd(cfg, cpu)
-    got = _run(cfg, cpu, dev, of)
+    got, (r, y, g) = _run(cfg, cpu, dev, of, tiles)
+    check_runner_steps(cfg, cpu, r, y, g)
+    del r, y, g
     ob = O.backward(of, cpu["dy"])
     bd = O.rounding_bands(of, ob, cpu["dy"])
     ref = dict(of)
@@ -65,7 +73,7 @@ def test_gemm_tiles_match_oracle(cfg, tiles, monkeypatch):
     for e in np.where(of["counts"] == 0)[0]:
         for name in ("dw_gate", "dw_up", "dw_down"):
             assert torch.count_nonzero(got[name][int(e)]).item() == 0
-    again = _run(cfg, cpu, dev, of)
+    again, _ = _run(cfg, cpu, dev, of, tiles)
     for name, t in got.items():
         assert torch.equal(t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32),
                            again[name].view(torch.int16) if t.dtype == torch.bfloat16 else again[name].view(torch.int32)), name
@@ -74,15 +82,15 @@ def test_gemm_tiles_match_oracle(cfg, tiles, monkeypatch):
 @pytest.mark.parametrize("tiles", ["256", "128x256", "128"])
 @pytest.mark.parametrize("cfg", [TEST_CONFIGS["t_bigtile"], TEST_CONFIGS["t_ragged"], TEST_CONFIGS["t_skew"],
                                  TEST_CONFIGS["t_f32"], TEST_CONFIGS["t_wide_e"]], ids=lambda c: c.name)
-def test_gate_up_gather_equals_permute_then_gate_up(cfg, tiles, monkeypatch):
+def test_gate_up_gather_equals_permute_then_gate_up(cfg, tiles):
     """moe_ffn_gate_up_gather (rows read as x[sorted_flat / K]) gives the same
     bytes as moe_permute followed by moe_ffn_gate_up, for every tile family."""
     from mixture_experts_layer_sort_amd import _lib as L
     from mixture_experts_layer_sort_amd.layer import MoELayerRunner
-    monkeypatch.setenv("MOE_GEMM_TILES", tiles)
     print(f"[gather {tiles}] {cfg.name}", flush=True)
     cpu, dev = gpu_inputs(cfg, 2)
-    r = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, "cuda", gather=False)
+    r = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, "cuda", gather=False,
+                       gemm_tiles=_family(tiles))
     r.route(dev["x"], dev["w_r"], dev["bias"])
     r.meta()
     L.moe_permute(r.d, dev["x"], r.sorted_flat, r.xs)
@@ -96,7 +104,8 @@ def test_gate_up_gather_equals_permute_then_gate_up(cfg, tiles, monkeypatch):
     for k, v in ref.items():
         assert torch.equal(getattr(r, k).view(torch.uint8), v.view(torch.uint8)), k
     # the forward-only runner takes this path and holds no xs
-    f = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, "cuda", backward=False)
+    f = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, "cuda", backward=False,
+                       gemm_tiles=_family(tiles))
     assert f.gather_fused and f.xs is None
     y = f.forward(dev["x"], dev["w_r"], dev["w_gate"], dev["w_up"], dev["w_down"], dev["bias"])
     r.forward(dev["x"], dev["w_r"], dev["w_gate"], dev["w_up"], dev["w_down"], dev["bias"])
@@ -108,13 +117,12 @@ def test_gate_up_gather_equals_permute_then_gate_up(cfg, tiles, monkeypatch):
                                  MoEConfig("t_tiles_f640", N=1500, H=384, F=640, E=3, K=2, dtype="bf16"),
                                  MoEConfig("t_dxdw_base_shape", N=4096, H=512, F=1024, E=8, K=2, dtype="bf16")],
                          ids=lambda c: c.name)
-def test_merged_dx_dw_launch_equals_separate_launches(cfg, monkeypatch):
+def test_merged_dx_dw_launch_equals_separate_launches(cfg):
     """moe_ffn_bwd_dx_dw (one launch: weight-gradient tiles first, dX tiles
     after) gives the same bytes as the separate 256 x 256 dX and dW launches,
     on poisoned outputs, with empty experts and ragged tails."""
     from mixture_experts_layer_sort_amd import _lib as L
     from mixture_experts_layer_sort_amd.layer import MoELayerRunner
-    monkeypatch.delenv("MOE_GEMM_TILES", raising=False)
     print(f"[dx_dw] {cfg.name}", flush=True)
     cpu, dev = gpu_inputs(cfg, 21, with_dy=True)
     r = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, "cuda", gather=False)
@@ -123,11 +131,10 @@ def test_merged_dx_dw_launch_equals_separate_launches(cfg, monkeypatch):
     sync()
     outs = []
     for forced in (None, "256"):
-        if forced is not None:
-            monkeypatch.setenv("MOE_GEMM_TILES", forced)
+        d = L.dims(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, L.dtype_code(cfg.torch_dtype), _family(forced))
         dxs = torch.full_like(r.dxs, float("nan"))
         dwg, dwu, dwd = (torch.full_like(t, float("nan")) for t in (r.dw_gate, r.dw_up, r.dw_down))
-        L.moe_ffn_bwd_dx_dw(r.d, r.dg, r.du, dev["w_gate"], dev["w_up"], r.tiles, r.num_tiles, dxs, r.xs, r.act,
+        L.moe_ffn_bwd_dx_dw(d, r.dg, r.du, dev["w_gate"], dev["w_up"], r.tiles, r.num_tiles, dxs, r.xs, r.act,
                             r.dys, r.offsets, dwg, dwu, dwd)
         sync()
         outs.append((dxs, dwg, dwu, dwd))
@@ -142,13 +149,12 @@ def test_merged_dx_dw_launch_equals_separate_launches(cfg, monkeypatch):
 
 @pytest.mark.parametrize("cfg", [TEST_CONFIGS["t_skew"], TEST_CONFIGS["t_ragged"], TEST_CONFIGS["t_f32"]],
                          ids=lambda c: c.name)
-def test_grouped_entry_points_equal_the_single_gemm_calls(cfg, monkeypatch):
+def test_grouped_entry_points_equal_the_single_gemm_calls(cfg):
     """moe_expert_ffn (gate/up + down) and moe_expert_ffn_bwd (dA, then dX
     and dW) give the same bytes as the per-GEMM calls the layer runner
     makes, on poisoned outputs."""
     from mixture_experts_layer_sort_amd import _lib as L
     from mixture_experts_layer_sort_amd.layer import MoELayerRunner
-    monkeypatch.delenv("MOE_GEMM_TILES", raising=False)
     cpu, dev = gpu_inputs(cfg, 22, with_dy=True)
     r = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, "cuda", gather=False)
     r.forward(dev["x"], dev["w_r"], dev["w_gate"], dev["w_up"], dev["w_down"], dev["bias"])
@@ -172,14 +178,13 @@ def test_grouped_entry_points_equal_the_single_gemm_calls(cfg, monkeypatch):
 
 @pytest.mark.parametrize("cfg", [TEST_CONFIGS["t_skew"], TEST_CONFIGS["t_bigtile"], TEST_CONFIGS["t_f32"]],
                          ids=lambda c: c.name)
-def test_separate_dx_and_dw_entries(cfg, monkeypatch):
+def test_separate_dx_and_dw_entries(cfg):
     """moe_ffn_bwd_dx and moe_ffn_bwd_dw called on their own: dW is the same
     bytes as the merged launch (same 256 x 256 kernel); dX, whose tile shape
     follows the per-stage choice, is checked against the oracle's dxs for
     the same dG, dU."""
     from mixture_experts_layer_sort_amd import _lib as L
     from mixture_experts_layer_sort_amd.layer import MoELayerRunner
-    monkeypatch.delenv("MOE_GEMM_TILES", raising=False)
     cpu, dev = gpu_inputs(cfg, 23, with_dy=True)
     r = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, "cuda", gather=False)
     r.forward(dev["x"], dev["w_r"], dev["w_gate"], dev["w_up"], dev["w_down"], dev["bias"])
@@ -213,18 +218,15 @@ def test_separate_dx_and_dw_entries(cfg, monkeypatch):
 @pytest.mark.parametrize("cfg", [TEST_CONFIGS["t_skew"], TEST_CONFIGS["t_ragged"], TEST_CONFIGS["t_f32"],
                                  MoEConfig("t_tiles_f640", N=1500, H=384, F=640, E=3, K=2, dtype="bf16")],
                          ids=lambda c: c.name)
-def test_gathered_weight_gradients_equal_the_xs_path(cfg, tiles, monkeypatch):
+def test_gathered_weight_gradients_equal_the_xs_path(cfg, tiles):
     """moe_ffn_bwd_dx_dw_gather (dW_gate and dW_up read x[sorted_flat / K])
     gives the same bytes as moe_permute + moe_ffn_bwd_dx_dw, for every tile
     family and the fp32 path, on poisoned outputs."""
     from mixture_experts_layer_sort_amd import _lib as L
     from mixture_experts_layer_sort_amd.layer import MoELayerRunner
-    if tiles is None:
-        monkeypatch.delenv("MOE_GEMM_TILES", raising=False)
-    else:
-        monkeypatch.setenv("MOE_GEMM_TILES", tiles)
     cpu, dev = gpu_inputs(cfg, 24, with_dy=True)
-    r = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, "cuda", gather=False)
+    r = MoELayerRunner(cfg.N, cfg.H, cfg.F, cfg.E, cfg.K, cfg.torch_dtype, "cuda", gather=False,
+                       gemm_tiles=_family(tiles))
     r.forward(dev["x"], dev["w_r"], dev["w_gate"], dev["w_up"], dev["w_down"], dev["bias"])
     r.backward(dev["dy"])
     sync()

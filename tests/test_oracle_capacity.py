@@ -192,7 +192,7 @@ def test_bands_with_capacity(cfg):
     b = O.backward(f, inp["dy"])
     band = O.rounding_bands(f, b, inp["dy"])
     dropped = f["inv"].reshape(cfg.N, cfg.K) < 0
-    assert dropped.any() and np.all(band["dgates"][dropped] == 0) and np.all(b["dgates"][dropped] == 0)
+    assert dropped.any() and np.all(b["dgates"][dropped] == 0)
     for k, v in band.items():
         assert np.all(np.isfinite(v)) and np.all(v >= 0), k
     # float32 combine of the kept rows (k ascending) stays inside the y band

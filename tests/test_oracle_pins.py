@@ -461,7 +461,7 @@ def test_forward_given_assignment_matches_bruteforce():
 
 @pytest.mark.parametrize("store", ["bf16", "f64"])
 def test_weight_grad_slices_match_whole_layer(store):
-    """Columns of dW_gate / dW_up and rows of dW_down (and their bands) from
+    """Columns of dW_gate / dW_up and rows of dW_down from
     weight_grad_slices equal the pinned whole-layer backward's, including an
     expert with no rows (exact zeros)."""
     cfg = TEST_CONFIGS["t_skew"]
@@ -470,7 +470,6 @@ def test_weight_grad_slices_match_whole_layer(store):
     f = O.forward(inp["x"], inp["w_r"], inp["w_gate"], inp["w_up"], inp["w_down"], cfg.K, bias=inp["bias"],
                   store=store)
     b = O.backward(f, inp_dy)
-    bands = O.rounding_bands(f, b, inp_dy) if store == "bf16" else None
     empty = int(np.where(f["counts"] == 0)[0][0])
     hot = int(np.argmax(f["counts"]))
     cols = [0, 7, cfg.F - 1]
@@ -482,10 +481,28 @@ def test_weight_grad_slices_match_whole_layer(store):
         assert np.allclose(s["dw_down"], b["dw_down"][e][cols, :], rtol=1e-12, atol=1e-12)
         if e == empty:
             assert not s["dw_gate"].any() and not s["dw_down"].any()
-        if bands is not None:
-            assert np.allclose(s["band_dw_gate"], bands["dw_gate"][e][:, cols], rtol=1e-9, atol=1e-15)
-            assert np.allclose(s["band_dw_up"], bands["dw_up"][e][:, cols], rtol=1e-9, atol=1e-15)
-            assert np.allclose(s["band_dw_down"], bands["dw_down"][e][cols, :], rtol=1e-9, atol=1e-15)
+
+
+@pytest.mark.parametrize("store", ["bf16", "f32"])
+def test_expert_rows_match_whole_layer(store):
+    """Any subset of one expert's rows from expert_rows equals the pinned
+    whole-layer forward and backward on those rows, bit for bit."""
+    cfg = TEST_CONFIGS["t_ragged"]
+    inp = _inputs(cfg, seed=4)
+    dy = O.as_f64(make_inputs(cfg, 4, with_dy=True)["dy"])
+    f = O.forward(inp["x"], inp["w_r"], inp["w_gate"], inp["w_up"], inp["w_down"], cfg.K, store=store)
+    b = O.backward(f, dy)
+    rng = np.random.default_rng(0)
+    for e in range(cfg.E):
+        r0, r1 = int(f["offsets"][e]), int(f["offsets"][e + 1])
+        rows = np.sort(rng.choice(np.arange(r0, r1), size=min(9, r1 - r0), replace=False))
+        sf = f["sorted_flat"][rows]
+        got = O.expert_rows(inp["x"][sf // cfg.K], f["gates"].reshape(-1)[sf], dy[sf // cfg.K], inp["w_gate"][e],
+                            inp["w_up"][e], inp["w_down"][e], store)
+        for k in ("xs", "G", "U", "A", "ys"):
+            assert np.array_equal(got[k], f[k][rows]), (e, k)
+        for k in ("dys", "dG", "dU", "dxs"):
+            assert np.array_equal(got[k], b[k][rows]), (e, k)
 
 
 def _pins_pass():

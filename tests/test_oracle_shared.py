@@ -158,5 +158,3 @@ def test_bands_cover_a_float32_backward_and_combine():
         assert np.all(np.abs(got.double().numpy() - b[name]) <= band[name] + 1e-30), name
     dxs = (t(b["dG_s"]) @ t(s["w_gate"]).T + t(b["dU_s"]) @ t(s["w_up"]).T).to(torch.bfloat16).double().numpy()
     assert np.all(np.abs(dxs - b["dxs_s"]) <= band["dxs_s"] + 1e-30)
-    for name in ("dw_gate_s", "dw_up_s", "dw_down_s"):
-        assert band[name].shape == b[name].shape and np.all(band[name] > 0), name
