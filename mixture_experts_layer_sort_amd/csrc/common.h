@@ -98,11 +98,12 @@ __device__ __forceinline__ float silu_f32(float g) { return g * sigmoid_f32(g); 
 // order still advances through all XCDs together.  The launch grid must be a
 // multiple of 8 * kXcdRun; returns -1 for blocks past `total`.
 constexpr int kXcdRun = 8;
+template <int RUN = kXcdRun>
 __device__ __forceinline__ int xcd_window_block(int b, int total) {
-  const int L = (b / (8 * kXcdRun)) * (8 * kXcdRun) + (b % 8) * kXcdRun + (b / 8) % kXcdRun;
+  const int L = (b / (8 * RUN)) * (8 * RUN) + (b % 8) * RUN + (b / 8) % RUN;
   return L < total ? L : -1;
 }
-__device__ __forceinline__ int xcd_window_block(int total) { return xcd_window_block(blockIdx.x, total); }
+__device__ __forceinline__ int xcd_window_block(int total) { return xcd_window_block<kXcdRun>(blockIdx.x, total); }
 
 // The expert of rank p when experts are ordered by row count, largest first
 // (equal counts: lower id first), from offsets [E+1].  The weight-gradient

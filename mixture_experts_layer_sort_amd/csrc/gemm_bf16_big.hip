@@ -159,6 +159,23 @@ __device__ __forceinline__ void grouped(int L, int nrow, int ncol, int& row, int
   col = r / gm;
 }
 
+// Weight-gradient tiles in patches: one XCD runs 32 workgroups at a time,
+// and a patch of kPatchM x kPatchN output tiles of one problem shares
+// kPatchM left panels and kPatchN right panels, each K step of which is
+// fetched into the XCD's L2 once for the patch (a 1 x 8 run of tiles shares
+// one left panel and fetches eight right panels).  Tile t of an mtiles x
+// ntiles problem, patch-major: row groups of kPatchM row tiles; inside a
+// group, column chunks of kPatchN; inside a chunk, the row tile fastest.
+constexpr int kPatchM = 4, kPatchN = 8, kDwRun = kPatchM * kPatchN;
+__device__ __forceinline__ void patch_tile(int t, int mtiles, int ntiles, int& mt, int& nt) {
+  const int per_group = kPatchM * ntiles;
+  const int g = t / per_group, r = t % per_group;
+  const int gm = min(kPatchM, mtiles - g * kPatchM);
+  const int chunk = r / (gm * kPatchN), rc = r % (gm * kPatchN);
+  mt = g * kPatchM + rc % gm;
+  nt = chunk * kPatchN + rc / gm;
+}
+
 // Row tile `sub` of the list tiles (C::SUB row tiles per list tile); rows <= 0
 // when the list tile is shorter.
 template <class C>
@@ -437,8 +454,8 @@ __device__ __forceinline__ void dw_tile(char* lds, int b, const bf16_t* __restri
   const int tpe2 = ((F + C::BM - 1) / C::BM) * th2;  // ... of problem 2
   const int per = 2 * tpe + tpe2;
   // experts largest first, each expert's tiles consecutive, dealt to the XCDs
-  // in runs of kXcdRun
-  const int blk = xcd_window_block(b, E * per);
+  // in runs of kDwRun (one patch)
+  const int blk = xcd_window_block<kDwRun>(b, E * per);
   if (blk < 0) return;
   const int e = expert_of_rank<C::NT>(offsets, E, blk / per, reinterpret_cast<int*>(lds));
   const int within = blk % per;
@@ -451,12 +468,12 @@ __device__ __forceinline__ void dw_tile(char* lds, int b, const bf16_t* __restri
     P = H; Q = F;
     Lm = xs; Rm = (prob == 0) ? dg : du;
     out = ((prob == 0) ? dwg : dwu) + (int64_t)e * H * F;
-    mt = t / tf; nt = t % tf;
+    patch_tile(t, tpe / tf, tf, mt, nt);
   } else {
     P = F; Q = H;
     Lm = act; Rm = dys;
     out = dwd + (int64_t)e * F * H;
-    mt = t / th2; nt = t % th2;
+    patch_tile(t, tpe2 / th2, th2, mt, nt);
   }
   const int prow = min(C::BM, P - mt * C::BM), qcol = min(C::BN, Q - nt * C::BN);
   const int w = threadIdx.x >> 6, wm = w / C::WN, wn = w % C::WN;
@@ -519,7 +536,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_dw(const bf16_t* __restrict_
 // weights), so their tiles are independent: the first dw_grid workgroups take
 // the weight-gradient tiles (longest contractions first), the rest the dX
 // tiles, which fill the CUs the weight gradients leave idle and their tail.
-// dw_grid is a multiple of 8 * kXcdRun, so both parts keep their XCD mapping.
+// dw_grid is a multiple of 8 * kDwRun, so both parts keep their XCD mapping.
 // CW: the weight-gradient tiles' shape; CX: the dX tiles' shape (same block
 // size; the launch gets the larger LDS of the two).
 template <class CW, class CX, bool GATHER = false>
@@ -628,7 +645,7 @@ static unsigned dw_grid(const Dims& d) {
   const int64_t tpe = ((d.H + C::BM - 1) / C::BM) * ((d.F + C::BN - 1) / C::BN);
   const int64_t tpe2 = ((d.F + C::BM - 1) / C::BM) * ((d.H + C::BN - 1) / C::BN);
   const int64_t total = d.E * (2 * tpe + tpe2);
-  const int64_t win = 8 * kXcdRun;
+  const int64_t win = 8 * kDwRun;
   return unsigned((total + win - 1) / win * win);
 }
 
