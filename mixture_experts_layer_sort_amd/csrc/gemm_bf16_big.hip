@@ -21,9 +21,8 @@
 // other LDS stage between the last k step's MFMAs; one barrier per step.
 // Spreading the requests keeps each wave's in-order issue from parking its
 // MFMAs behind a burst of loads, which is what held the LDS DMA version of
-// this loop near 0.8 PFLOP/s.  The SwiGLU backward keeps an 8-wave
-// configuration through the LDS DMA pipeline (BigDma): its G/U epilogue
-// wants more waves to issue loads.
+// this loop near 0.8 PFLOP/s.  The 8-wave form of the same loop (Big8) runs
+// dX, the weight gradients, down and the SwiGLU backward.
 //
 // A K-contiguous operand (token rows; weight rows in the backward) sits in
 // LDS as [rows][64 k] and is read with 16-byte fragment loads; an
@@ -54,15 +53,13 @@ using namespace moe_mma;
 
 using Big = TileCfg<256, 256, 2, 2, 1, 64, 2, true>;  // 4 waves, 128 x 128 per wave, register-staged
 // The same tile with 8 waves of 64 x 128 (two per SIMD, each covering the
-// other's issue stalls): used for dX, the weight gradients and down, where it
-// measured faster (merged dX/dW 866-870 -> 891-896 TFLOP/s at H = 512,
-// F = 1024, E = 8; 846-851 -> 881 at the skewed H = 2048, E = 64 workload);
-// gate/up keeps 4 waves (1.29 -> 1.31 ms and 5.49 -> 5.61 ms with 8).
+// other's issue stalls): used for dX, the weight gradients, down and dA, where
+// it measured faster (merged dX/dW 866-870 -> 891-896 TFLOP/s at H = 512,
+// F = 1024, E = 8; 846-851 -> 881 at the skewed H = 2048, E = 64 workload;
+// dA 4.84 -> 4.68 ms at H = 4096, F = 14336 against the 8-wave LDS DMA tile);
+// gate/up keeps 4 waves (1.29 -> 1.31 ms, 5.49 -> 5.61 ms and, at H = 4096,
+// F = 14336, 7.31 -> 7.40 ms with 8).
 using Big8 = TileCfg<256, 256, 4, 2, 1, 64, 2, true>;
-// 8 waves of 64 x 128 through the LDS DMA pipeline: kept for the SwiGLU
-// backward, whose G/U epilogue runs with twice as many waves to issue its
-// loads.
-using BigDma = TileCfg<256, 256, 4, 2, 1, 64, 2>;
 // 128 x 256 tiles through the same DMA pipeline, 32 k per stage, three stages
 // (72 KiB of LDS, two workgroups per CU): used by the SwiGLU backward on
 // short contractions, where its staged epilogue of G and U overlaps better
@@ -86,7 +83,7 @@ using SmallR64 = TileCfg<128, 128, 2, 2, 2, 64, 2, true>;
 // slower on every workload (221 -> 238 us there with 64 k per stage, 260 with
 // 32): the smaller tile's operand traffic per flop outweighs the balance.
 using DxInMerged = Big8;
-static_assert(MOE_TILE_M % Big::BM == 0 && MOE_TILE_M % Big8::BM == 0 && MOE_TILE_M % BigDma::BM == 0 && MOE_TILE_M % Mid::BM == 0 &&
+static_assert(MOE_TILE_M % Big::BM == 0 && MOE_TILE_M % Big8::BM == 0 && MOE_TILE_M % Mid::BM == 0 &&
                   MOE_TILE_M % MidR::BM == 0 && MOE_TILE_M % SmallR32::BM == 0 && MOE_TILE_M % SmallR64::BM == 0,
               "list tiles split into row tiles");
 
@@ -167,6 +164,21 @@ __device__ __forceinline__ void grouped(int L, int nrow, int ncol, int& row, int
 // ntiles problem, patch-major: row groups of kPatchM row tiles; inside a
 // group, column chunks of kPatchN; inside a chunk, the row tile fastest.
 constexpr int kPatchM = 4, kPatchN = 8, kDwRun = kPatchM * kPatchN;
+
+// Run length of the weight-gradient tiles per XCD window: one patch when
+// there are at least that many tiles per XCD, else an even eighth of them
+// (at H = 512, F = 1024, E = 8 the 192 tiles in runs of 32 would leave two
+// XCDs without any: 201 -> 245 us for the merged dX/dW launch), at least 8.
+__host__ __device__ __forceinline__ int dw_run(int64_t total) {
+  const int64_t per_xcd = (total + 7) / 8;
+  return int(per_xcd >= kDwRun ? kDwRun : (per_xcd < 8 ? 8 : per_xcd));
+}
+
+// xcd_window_block with a run length known at launch time.
+__device__ __forceinline__ int xcd_window_block_rt(int b, int total, int run) {
+  const int L = (b / (8 * run)) * (8 * run) + (b % 8) * run + (b / 8) % run;
+  return L < total ? L : -1;
+}
 __device__ __forceinline__ void patch_tile(int t, int mtiles, int ntiles, int& mt, int& nt) {
   const int per_group = kPatchM * ntiles;
   const int g = t / per_group, r = t % per_group;
@@ -454,8 +466,8 @@ __device__ __forceinline__ void dw_tile(char* lds, int b, const bf16_t* __restri
   const int tpe2 = ((F + C::BM - 1) / C::BM) * th2;  // ... of problem 2
   const int per = 2 * tpe + tpe2;
   // experts largest first, each expert's tiles consecutive, dealt to the XCDs
-  // in runs of kDwRun (one patch)
-  const int blk = xcd_window_block<kDwRun>(b, E * per);
+  // in runs of dw_run (one patch when there are enough tiles)
+  const int blk = xcd_window_block_rt(b, E * per, dw_run(int64_t(E) * per));
   if (blk < 0) return;
   const int e = expert_of_rank<C::NT>(offsets, E, blk / per, reinterpret_cast<int*>(lds));
   const int within = blk % per;
@@ -536,7 +548,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_dw(const bf16_t* __restrict_
 // weights), so their tiles are independent: the first dw_grid workgroups take
 // the weight-gradient tiles (longest contractions first), the rest the dX
 // tiles, which fill the CUs the weight gradients leave idle and their tail.
-// dw_grid is a multiple of 8 * kDwRun, so both parts keep their XCD mapping.
+// dw_grid is a multiple of 8 * dw_run, so both parts keep their XCD mapping.
 // CW: the weight-gradient tiles' shape; CX: the dX tiles' shape (same block
 // size; the launch gets the larger LDS of the two).
 template <class CW, class CX, bool GATHER = false>
@@ -613,7 +625,7 @@ static hipError_t dact_t(const Dims& d, const void* dys, const void* wd, const v
 
 hipError_t ffn_bwd_dact_big(const Dims& d, const void* dys, const void* wd, const void* g, const void* u,
                              const int32_t* tiles, const int32_t* num_tiles, void* dg, void* du, hipStream_t s) {
-  return dact_t<BigDma>(d, dys, wd, g, u, tiles, num_tiles, dg, du, s);
+  return dact_t<Big8>(d, dys, wd, g, u, tiles, num_tiles, dg, du, s);
 }
 
 hipError_t ffn_bwd_dact_mid(const Dims& d, const void* dys, const void* wd, const void* g, const void* u,
@@ -645,7 +657,7 @@ static unsigned dw_grid(const Dims& d) {
   const int64_t tpe = ((d.H + C::BM - 1) / C::BM) * ((d.F + C::BN - 1) / C::BN);
   const int64_t tpe2 = ((d.F + C::BM - 1) / C::BM) * ((d.H + C::BN - 1) / C::BN);
   const int64_t total = d.E * (2 * tpe + tpe2);
-  const int64_t win = 8 * kDwRun;
+  const int64_t win = 8 * dw_run(total);
   return unsigned((total + win - 1) / win * win);
 }
 

@@ -41,23 +41,23 @@ __host__ __device__ constexpr int tok_per_wave(int K) { return K <= 4 ? 2 : 1; }
 // y[n] = sum_k gates[n,k] * ys[inv[n*K+k]], k ascending, float32 accumulation;
 // dropped slots (inv < 0) add nothing.  add (optional, [N,H]): a row added
 // with weight 1 after the K terms (the shared expert's output).  One wave per
-// tok_per_wave(K) tokens, all row loads of a vector issued before the first
-// multiply; KT = K.
-template <typename T, int KT>
+// tok_per_wave(K) tokens; each lane takes U row vectors at a time (64 apart)
+// and issues every row load of them before the first multiply; KT = K.
+template <typename T, int KT, int U>
 __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ ys, const float* __restrict__ gates,
                                                  const int32_t* __restrict__ inv, const T* __restrict__ add,
                                                  T* __restrict__ y, int N, int vpr) {
   constexpr int V = Vec16<T>::n;
   constexpr int TW = tok_per_wave(KT);
   const int lane = lane_id();
-  const int64_t nbase = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * TW;
+  const int nbase = (blockIdx.x * 4 + (threadIdx.x >> 6)) * TW;
   if (nbase >= N) return;  // uniform across the wave
   int32_t r[TW][KT];
   float g[TW][KT];
   bool valid[TW];
 #pragma unroll
   for (int t = 0; t < TW; ++t) {
-    const int64_t n = nbase + t;
+    const int n = nbase + t;
     valid[t] = n < N;
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
@@ -66,55 +66,69 @@ __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ ys, const
     }
   }
   const uint4* ys4 = reinterpret_cast<const uint4*>(ys);
-  for (int c = lane; c < vpr; c += kWave) {
-    uint4 raw[TW][KT], ra[TW];
+  const uint4* add4 = reinterpret_cast<const uint4*>(add);
+  for (int c0 = lane; c0 < vpr; c0 += kWave * U) {
+    uint4 raw[U][TW][KT], ra[U][TW];
 #pragma unroll
-    for (int t = 0; t < TW; ++t) {
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * kWave;
+      if (c >= vpr) break;
 #pragma unroll
-      for (int k = 0; k < KT; ++k)
-        if (r[t][k] >= 0) raw[t][k] = ys4[(int64_t)r[t][k] * vpr + c];
-      if (add != nullptr && valid[t]) ra[t] = reinterpret_cast<const uint4*>(add)[(nbase + t) * vpr + c];
+      for (int t = 0; t < TW; ++t) {
+#pragma unroll
+        for (int k = 0; k < KT; ++k)
+          if (r[t][k] >= 0) raw[u][t][k] = ys4[(int64_t)r[t][k] * vpr + c];
+        if (add != nullptr && valid[t]) ra[u][t] = add4[(int64_t)(nbase + t) * vpr + c];
+      }
     }
 #pragma unroll
-    for (int t = 0; t < TW; ++t) {
-      if (!valid[t]) continue;
-      float acc[V];
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * kWave;
+      if (c >= vpr) break;
 #pragma unroll
-      for (int i = 0; i < V; ++i) acc[i] = 0.f;
+      for (int t = 0; t < TW; ++t) {
+        if (!valid[t]) continue;
+        float acc[V];
 #pragma unroll
-      for (int k = 0; k < KT; ++k)
-        if (r[t][k] >= 0) {
+        for (int i = 0; i < V; ++i) acc[i] = 0.f;
+#pragma unroll
+        for (int k = 0; k < KT; ++k)
+          if (r[t][k] >= 0) {
+            float val[V];
+            Vec16<T>::load(reinterpret_cast<const T*>(&raw[u][t][k]), val);
+#pragma unroll
+            for (int i = 0; i < V; ++i) acc[i] = fmaf(g[t][k], val[i], acc[i]);
+          }
+        if (add != nullptr) {
           float val[V];
-          Vec16<T>::load(reinterpret_cast<const T*>(&raw[t][k]), val);
+          Vec16<T>::load(reinterpret_cast<const T*>(&ra[u][t]), val);
 #pragma unroll
-          for (int i = 0; i < V; ++i) acc[i] = fmaf(g[t][k], val[i], acc[i]);
+          for (int i = 0; i < V; ++i) acc[i] += val[i];
         }
-      if (add != nullptr) {
-        float val[V];
-        Vec16<T>::load(reinterpret_cast<const T*>(&ra[t]), val);
-#pragma unroll
-        for (int i = 0; i < V; ++i) acc[i] += val[i];
+        Vec16<T>::store(y + ((int64_t)(nbase + t) * vpr + c) * V, acc);
       }
-      Vec16<T>::store(y + ((nbase + t) * vpr + c) * V, acc);
     }
   }
 }
 
-template <typename T, int KT>
+// dys[inv[n,k]] = gates[n,k] dy[n]; dgates[n,k] = <dy[n], ys[inv[n,k]]>
+// (fixed lane order, then a butterfly), dropped slots skipped.  Same wave and
+// chunk layout as k_combine.
+template <typename T, int KT, int U>
 __global__ __launch_bounds__(256) void k_combine_bwd(const T* __restrict__ dy, const T* __restrict__ ys,
                                                      const float* __restrict__ gates, const int32_t* __restrict__ inv,
                                                      T* __restrict__ dys, float* __restrict__ dgates, int N, int vpr) {
   constexpr int V = Vec16<T>::n;
   constexpr int TW = tok_per_wave(KT);
   const int lane = lane_id();
-  const int64_t nbase = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * TW;
+  const int nbase = (blockIdx.x * 4 + (threadIdx.x >> 6)) * TW;
   if (nbase >= N) return;  // uniform across the wave
   int32_t r[TW][KT];
   float g[TW][KT];
   bool valid[TW];
 #pragma unroll
   for (int t = 0; t < TW; ++t) {
-    const int64_t n = nbase + t;
+    const int n = nbase + t;
     valid[t] = n < N;
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
@@ -127,33 +141,45 @@ __global__ __launch_bounds__(256) void k_combine_bwd(const T* __restrict__ dy, c
   for (int t = 0; t < TW; ++t)
 #pragma unroll
     for (int k = 0; k < KT; ++k) dot[t][k] = 0.f;
-  for (int c = lane; c < vpr; c += kWave) {
-    uint4 rd[TW], raw[TW][KT];
+  const uint4* dy4 = reinterpret_cast<const uint4*>(dy);
+  const uint4* ys4 = reinterpret_cast<const uint4*>(ys);
+  for (int c0 = lane; c0 < vpr; c0 += kWave * U) {
+    uint4 rd[U][TW], raw[U][TW][KT];
 #pragma unroll
-    for (int t = 0; t < TW; ++t) {
-      if (valid[t]) rd[t] = *reinterpret_cast<const uint4*>(dy + ((nbase + t) * vpr + c) * V);
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * kWave;
+      if (c >= vpr) break;
 #pragma unroll
-      for (int k = 0; k < KT; ++k)
-        if (r[t][k] >= 0) raw[t][k] = *reinterpret_cast<const uint4*>(ys + ((int64_t)r[t][k] * vpr + c) * V);
+      for (int t = 0; t < TW; ++t) {
+        if (valid[t]) rd[u][t] = dy4[(int64_t)(nbase + t) * vpr + c];
+#pragma unroll
+        for (int k = 0; k < KT; ++k)
+          if (r[t][k] >= 0) raw[u][t][k] = ys4[(int64_t)r[t][k] * vpr + c];
+      }
     }
 #pragma unroll
-    for (int t = 0; t < TW; ++t) {
-      if (!valid[t]) continue;
-      float d[V];
-      Vec16<T>::load(reinterpret_cast<const T*>(&rd[t]), d);
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * kWave;
+      if (c >= vpr) break;
 #pragma unroll
-      for (int k = 0; k < KT; ++k) {
-        if (r[t][k] < 0) continue;
-        float yv[V], o[V];
-        Vec16<T>::load(reinterpret_cast<const T*>(&raw[t][k]), yv);
-        float s = dot[t][k];
+      for (int t = 0; t < TW; ++t) {
+        if (!valid[t]) continue;
+        float d[V];
+        Vec16<T>::load(reinterpret_cast<const T*>(&rd[u][t]), d);
 #pragma unroll
-        for (int i = 0; i < V; ++i) {
-          s = fmaf(d[i], yv[i], s);
-          o[i] = g[t][k] * d[i];
+        for (int k = 0; k < KT; ++k) {
+          if (r[t][k] < 0) continue;
+          float yv[V], o[V];
+          Vec16<T>::load(reinterpret_cast<const T*>(&raw[u][t][k]), yv);
+          float sdot = dot[t][k];
+#pragma unroll
+          for (int i = 0; i < V; ++i) {
+            sdot = fmaf(d[i], yv[i], sdot);
+            o[i] = g[t][k] * d[i];
+          }
+          dot[t][k] = sdot;
+          Vec16<T>::store(dys + ((int64_t)r[t][k] * vpr + c) * V, o);
         }
-        dot[t][k] = s;
-        Vec16<T>::store(dys + ((int64_t)r[t][k] * vpr + c) * V, o);
       }
     }
   }
@@ -162,8 +188,8 @@ __global__ __launch_bounds__(256) void k_combine_bwd(const T* __restrict__ dy, c
     if (!valid[t]) continue;  // uniform across the wave
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
-      const float s = wave_sum(dot[t][k]);
-      if (lane == 0) dgates[(nbase + t) * KT + k] = s;
+      const float sum = wave_sum(dot[t][k]);
+      if (lane == 0) dgates[(nbase + t) * KT + k] = sum;
     }
   }
 }
@@ -183,9 +209,9 @@ __global__ __launch_bounds__(256) void k_transpose_wr(const T* __restrict__ w_r,
 // rounding.  DENSE: the router term runs over all E experts in ascending
 // order (dlogits is dense when the load-balancing loss is on; used for
 // E <= 8).  add (optional): one more row added last.  One wave per
-// tok_per_wave(K) tokens with every row load of a vector issued together;
-// KT = K.
-template <typename T, bool DENSE, int KT>
+// tok_per_wave(K) tokens; each lane takes U row vectors at a time with every
+// row load of them issued together; KT = K.
+template <typename T, bool DENSE, int KT, int U>
 __global__ __launch_bounds__(256) void k_permute_bwd(const T* __restrict__ dxs, const int32_t* __restrict__ inv,
                                                      const int32_t* __restrict__ topk, const float* __restrict__ dl,
                                                      const T* __restrict__ w_rt, const T* __restrict__ add,
@@ -193,83 +219,94 @@ __global__ __launch_bounds__(256) void k_permute_bwd(const T* __restrict__ dxs, 
   constexpr int V = Vec16<T>::n;
   constexpr int TW = tok_per_wave(KT);
   const int lane = lane_id();
-  const int64_t nbase = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * TW;
+  const int nbase = (blockIdx.x * 4 + (threadIdx.x >> 6)) * TW;
   if (nbase >= N) return;  // uniform across the wave
   int32_t r[TW][KT], ex[TW][KT];
   float dk[TW][KT];
   bool valid[TW];
 #pragma unroll
   for (int t = 0; t < TW; ++t) {
-    const int64_t n = nbase + t;
+    const int n = nbase + t;
     valid[t] = n < N;
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
       r[t][k] = valid[t] ? inv[n * KT + k] : -1;
       ex[t][k] = valid[t] ? topk[n * KT + k] : 0;
-      dk[t][k] = (!DENSE && valid[t]) ? dl[n * E + ex[t][k]] : 0.f;
+      dk[t][k] = (!DENSE && valid[t]) ? dl[(int64_t)n * E + ex[t][k]] : 0.f;
     }
   }
   const uint4* xs4 = reinterpret_cast<const uint4*>(dxs);
   const uint4* wr4 = reinterpret_cast<const uint4*>(w_rt);
-  for (int c = lane; c < vpr; c += kWave) {
-    uint4 rx[TW][KT], rw[TW][KT], ra[TW];
+  const uint4* add4 = reinterpret_cast<const uint4*>(add);
+  for (int c0 = lane; c0 < vpr; c0 += kWave * U) {
+    uint4 rx[U][TW][KT], rw[U][TW][KT], ra[U][TW];
 #pragma unroll
-    for (int t = 0; t < TW; ++t) {
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * kWave;
+      if (c >= vpr) break;
 #pragma unroll
-      for (int k = 0; k < KT; ++k) {
-        if (r[t][k] >= 0) rx[t][k] = xs4[(int64_t)r[t][k] * vpr + c];
-        if (!DENSE && valid[t]) rw[t][k] = wr4[(int64_t)ex[t][k] * vpr + c];
+      for (int t = 0; t < TW; ++t) {
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+          if (r[t][k] >= 0) rx[u][t][k] = xs4[(int64_t)r[t][k] * vpr + c];
+          if (!DENSE && valid[t]) rw[u][t][k] = wr4[(int64_t)ex[t][k] * vpr + c];
+        }
+        if (add != nullptr && valid[t]) ra[u][t] = add4[(int64_t)(nbase + t) * vpr + c];
       }
-      if (add != nullptr && valid[t]) ra[t] = reinterpret_cast<const uint4*>(add)[(nbase + t) * vpr + c];
     }
-    float acc[TW][V];
 #pragma unroll
-    for (int t = 0; t < TW; ++t) {
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * kWave;
+      if (c >= vpr) break;
+      float acc[TW][V];
 #pragma unroll
-      for (int i = 0; i < V; ++i) acc[t][i] = 0.f;
+      for (int t = 0; t < TW; ++t) {
 #pragma unroll
-      for (int k = 0; k < KT; ++k)
-        if (r[t][k] >= 0) {
+        for (int i = 0; i < V; ++i) acc[t][i] = 0.f;
+#pragma unroll
+        for (int k = 0; k < KT; ++k)
+          if (r[t][k] >= 0) {
+            float val[V];
+            Vec16<T>::load(reinterpret_cast<const T*>(&rx[u][t][k]), val);
+#pragma unroll
+            for (int i = 0; i < V; ++i) acc[t][i] += val[i];
+          }
+        if (!DENSE) {
+#pragma unroll
+          for (int k = 0; k < KT; ++k) {
+            float wv[V];
+            Vec16<T>::load(reinterpret_cast<const T*>(&rw[u][t][k]), wv);
+#pragma unroll
+            for (int i = 0; i < V; ++i) acc[t][i] = fmaf(dk[t][k], wv[i], acc[t][i]);
+          }
+        }
+      }
+      if (DENSE) {
+        // every router logit has a gradient: all E experts, ascending; each
+        // W_r^T vector serves the wave's tokens
+        for (int e = 0; e < E; ++e) {
+          const uint4 raw = wr4[(int64_t)e * vpr + c];
+          float wv[V];
+          Vec16<T>::load(reinterpret_cast<const T*>(&raw), wv);
+#pragma unroll
+          for (int t = 0; t < TW; ++t) {
+            const float de = valid[t] ? dl[(int64_t)(nbase + t) * E + e] : 0.f;
+#pragma unroll
+            for (int i = 0; i < V; ++i) acc[t][i] = fmaf(de, wv[i], acc[t][i]);
+          }
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < TW; ++t) {
+        if (!valid[t]) continue;
+        if (add != nullptr) {
           float val[V];
-          Vec16<T>::load(reinterpret_cast<const T*>(&rx[t][k]), val);
+          Vec16<T>::load(reinterpret_cast<const T*>(&ra[u][t]), val);
 #pragma unroll
           for (int i = 0; i < V; ++i) acc[t][i] += val[i];
         }
-      if (!DENSE) {
-#pragma unroll
-        for (int k = 0; k < KT; ++k) {
-          float wv[V];
-          Vec16<T>::load(reinterpret_cast<const T*>(&rw[t][k]), wv);
-#pragma unroll
-          for (int i = 0; i < V; ++i) acc[t][i] = fmaf(dk[t][k], wv[i], acc[t][i]);
-        }
+        Vec16<T>::store(dx + ((int64_t)(nbase + t) * vpr + c) * V, acc[t]);
       }
-    }
-    if (DENSE) {
-      // every router logit has a gradient: all E experts, ascending; each
-      // W_r^T vector serves the wave's tokens
-      for (int e = 0; e < E; ++e) {
-        const uint4 raw = wr4[(int64_t)e * vpr + c];
-        float wv[V];
-        Vec16<T>::load(reinterpret_cast<const T*>(&raw), wv);
-#pragma unroll
-        for (int t = 0; t < TW; ++t) {
-          const float de = valid[t] ? dl[(nbase + t) * E + e] : 0.f;
-#pragma unroll
-          for (int i = 0; i < V; ++i) acc[t][i] = fmaf(de, wv[i], acc[t][i]);
-        }
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < TW; ++t) {
-      if (!valid[t]) continue;
-      if (add != nullptr) {
-        float val[V];
-        Vec16<T>::load(reinterpret_cast<const T*>(&ra[t]), val);
-#pragma unroll
-        for (int i = 0; i < V; ++i) acc[t][i] += val[i];
-      }
-      Vec16<T>::store(dx + ((nbase + t) * vpr + c) * V, acc[t]);
     }
   }
 }
@@ -391,6 +428,14 @@ unsigned grid_for(int64_t total, int64_t cap = 8192) {
 // Workgroups of 4 waves, one wave per row.
 unsigned waves4(int64_t rows) { return unsigned((rows + 3) / 4); }
 
+// Row vectors a lane takes at a time in the token-wise row kernels: two once
+// a row has at least two vectors per lane (more bytes in flight per wave),
+// else one.
+template <typename Fn>
+hipError_t with_u(int vpr, Fn&& f) {
+  return vpr >= 2 * kWave ? f(std::integral_constant<int, 2>{}) : f(std::integral_constant<int, 1>{});
+}
+
 template <typename T>
 int vpr_of(const moe_launch::Dims& d) {
   return int(d.H * int64_t(sizeof(T)) / 16);
@@ -423,9 +468,12 @@ hipError_t combine(const Dims& d, const void* ys, const float* gates, const int3
   auto run = [&](auto tag) {
     using T = decltype(tag);
     return with_k(int(d.K), [&](auto kt) {
-      hipLaunchKernelGGL((k_combine<T, decltype(kt)::value>), dim3(grid), dim3(256), 0, s, static_cast<const T*>(ys),
-                         gates, inv, static_cast<const T*>(add), static_cast<T*>(y), int(d.N), vpr_of<T>(d));
-      return hipGetLastError();
+      return with_u(vpr_of<T>(d), [&](auto u) {
+        hipLaunchKernelGGL((k_combine<T, decltype(kt)::value, decltype(u)::value>), dim3(grid), dim3(256), 0, s,
+                           static_cast<const T*>(ys), gates, inv, static_cast<const T*>(add), static_cast<T*>(y),
+                           int(d.N), vpr_of<T>(d));
+        return hipGetLastError();
+      });
     });
   };
   return d.dtype == MOE_BF16 ? run(moe::bf16_t{}) : run(float{});
@@ -438,10 +486,12 @@ hipError_t combine_bwd(const Dims& d, const void* dy, const void* ys, const floa
   auto run = [&](auto tag) {
     using T = decltype(tag);
     return with_k(int(d.K), [&](auto kt) {
-      hipLaunchKernelGGL((k_combine_bwd<T, decltype(kt)::value>), dim3(grid), dim3(256), 0, s,
-                         static_cast<const T*>(dy), static_cast<const T*>(ys), gates, inv, static_cast<T*>(dys),
-                         dgates, int(d.N), vpr_of<T>(d));
-      return hipGetLastError();
+      return with_u(vpr_of<T>(d), [&](auto u) {
+        hipLaunchKernelGGL((k_combine_bwd<T, decltype(kt)::value, decltype(u)::value>), dim3(grid), dim3(256), 0, s,
+                           static_cast<const T*>(dy), static_cast<const T*>(ys), gates, inv, static_cast<T*>(dys),
+                           dgates, int(d.N), vpr_of<T>(d));
+        return hipGetLastError();
+      });
     });
   };
   return d.dtype == MOE_BF16 ? run(moe::bf16_t{}) : run(float{});
@@ -471,15 +521,18 @@ hipError_t permute_bwd(const Dims& d, const void* dxs, const int32_t* inv, const
     }
     return with_k(int(d.K), [&](auto kt) {
       constexpr int KT = decltype(kt)::value;
-      if (dense)
-        hipLaunchKernelGGL((k_permute_bwd<T, true, KT>), dim3(grid), dim3(256), 0, s, static_cast<const T*>(dxs), inv,
-                           topk, dlogits, static_cast<const T*>(ws), static_cast<const T*>(add), static_cast<T*>(dx),
-                           int(d.N), vpr_of<T>(d), int(d.E));
-      else
-        hipLaunchKernelGGL((k_permute_bwd<T, false, KT>), dim3(grid), dim3(256), 0, s, static_cast<const T*>(dxs),
-                           inv, topk, dlogits, static_cast<const T*>(ws), static_cast<const T*>(add),
-                           static_cast<T*>(dx), int(d.N), vpr_of<T>(d), int(d.E));
-      return hipGetLastError();
+      return with_u(vpr_of<T>(d), [&](auto u) {
+        constexpr int UU = decltype(u)::value;
+        if (dense)
+          hipLaunchKernelGGL((k_permute_bwd<T, true, KT, UU>), dim3(grid), dim3(256), 0, s, static_cast<const T*>(dxs),
+                             inv, topk, dlogits, static_cast<const T*>(ws), static_cast<const T*>(add),
+                             static_cast<T*>(dx), int(d.N), vpr_of<T>(d), int(d.E));
+        else
+          hipLaunchKernelGGL((k_permute_bwd<T, false, KT, UU>), dim3(grid), dim3(256), 0, s,
+                             static_cast<const T*>(dxs), inv, topk, dlogits, static_cast<const T*>(ws),
+                             static_cast<const T*>(add), static_cast<T*>(dx), int(d.N), vpr_of<T>(d), int(d.E));
+        return hipGetLastError();
+      });
     });
   };
   if (d.dtype == MOE_BF16) return run(moe::bf16_t{});
