@@ -64,7 +64,8 @@ typedef enum moe_status {
   MOE_EINVAL = -1,       /* bad shape, null or misaligned pointer */
   MOE_EUNSUPPORTED = -2, /* outside the limits above, or unknown dtype */
   MOE_EWORKSPACE = -3,   /* workspace missing or smaller than required */
-  MOE_EHIP = -4          /* the HIP runtime reported a launch error */
+  MOE_EHIP = -4,         /* the HIP runtime reported a launch error */
+  MOE_ESCRATCH = -5      /* needs more than MOE_NOALLOC_SCRATCH_BYTES (no-allocation entry point) */
 } moe_status;
 
 typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
@@ -454,6 +455,33 @@ int moe_shared_ffn_bwd(const moe_dims* ds, const void* x, const void* dy, const 
 int moe_permute_bwd_add(const moe_dims* d, const void* dxs, const int32_t* inv, const int32_t* topk_idx,
                         const float* dlogits, const void* w_r, int32_t dense, const void* dx_add, void* dx, void* ws,
                         size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------- no-allocation entry point */
+
+/* Scratch held by the library for moe_route_meta_noalloc, per GPU, for the
+ * life of the process. */
+#define MOE_NOALLOC_SCRATCH_BYTES (4u << 20)
+
+/* moe_route_meta for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments and results as moe_route_meta minus
+ * (ws, ws_bytes): the scratch it needs lives in a file-scope device array of
+ * MOE_NOALLOC_SCRATCH_BYTES per GPU, whose address is looked up on the first
+ * call on each device (the current device; the stream must belong to it).
+ * No call allocates or frees memory.
+ * Limit: moe_workspace_bytes(d, MOE_ENTRY_ROUTE_META) <= 4 MiB, i.e.
+ * ceil(N/32)*E*4 bytes while the fused path runs (ceil(N/32)*E <= 32768,
+ * always within the limit) and (ceil(N*K/1024)*E + 2*E)*4 bytes otherwise
+ * (about N*K*E <= 2^30); beyond it the call returns MOE_ESCRATCH and
+ * enqueues nothing.  Every GPU's array is shared by all calls on that GPU
+ * and keeps the last call's contents: each call writes every scratch byte it
+ * reads before reading it, so nothing needs clearing, but calls that overlap
+ * on one GPU (two streams, or two threads) race and must be serialised by
+ * the caller.  Other errors: as moe_route_meta; MOE_EHIP if the device or
+ * the array's address cannot be queried. */
+int moe_route_meta_noalloc(const moe_dims* d, const void* x, const void* w_r, const float* logit_bias,
+                           int32_t capacity, int32_t* topk_idx, float* gates, int32_t* sorted_flat, int32_t* inv,
+                           int32_t* counts, int32_t* offsets, int32_t* tiles, int32_t* num_tiles, hipStream_t stream);
 
 #ifdef __cplusplus
 }

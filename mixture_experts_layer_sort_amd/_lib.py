@@ -17,7 +17,8 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_NAME = "libmoe_mi355x.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP, MOE_ESCRATCH = 0, -1, -2, -3, -4, -5
+MOE_NOALLOC_SCRATCH_BYTES = 4 << 20
 MOE_F32, MOE_BF16 = 0, 1
 MOE_ENTRY_PERMUTE_META, MOE_ENTRY_ROUTE_BWD, MOE_ENTRY_PERMUTE_BWD = 1, 2, 3
 MOE_ENTRY_AUX_LOSS, MOE_ENTRY_ROUTE_BWD_AUX = 4, 5
@@ -71,6 +72,7 @@ SIGNATURES = {
     "moe_permute_bwd_add": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
     "moe_ffn_bwd_dx_dw": (ctypes.c_int, [_DP] + [_P] * 14 + [_P]),
     "moe_route_meta": (ctypes.c_int, [_DP, _P, _P, _P, _I32] + [_P] * 9 + [_SZ, _P]),
+    "moe_route_meta_noalloc": (ctypes.c_int, [_DP, _P, _P, _P, _I32] + [_P] * 8 + [_P]),
     "moe_ffn_bwd_dx_dw_gather": (ctypes.c_int, [_DP] + [_P] * 15 + [_P]),
 }
 
@@ -292,6 +294,13 @@ def moe_route_meta(d, x, w_r, logit_bias, capacity, topk_idx, gates, sorted_flat
     _call("moe_route_meta", ctypes.byref(d), _ptr(x), _ptr(w_r), _ptr(logit_bias), int(capacity), _ptr(topk_idx),
           _ptr(gates), _ptr(sorted_flat), _ptr(inv), _ptr(counts), _ptr(offsets), _ptr(tiles), _ptr(num_tiles),
           _ptr(ws), _nbytes(ws), _stream(stream))
+
+
+def moe_route_meta_noalloc(d, x, w_r, logit_bias, capacity, topk_idx, gates, sorted_flat, inv, counts, offsets,
+                           tiles, num_tiles, stream=None):
+    _call("moe_route_meta_noalloc", ctypes.byref(d), _ptr(x), _ptr(w_r), _ptr(logit_bias), int(capacity),
+          _ptr(topk_idx), _ptr(gates), _ptr(sorted_flat), _ptr(inv), _ptr(counts), _ptr(offsets), _ptr(tiles),
+          _ptr(num_tiles), _stream(stream))
 
 
 def moe_ffn_bwd_dx_dw_gather(d, dg, du, w_gate, w_up, tiles, num_tiles, dxs, x, sorted_flat, act, dys, offsets,

@@ -72,6 +72,7 @@ const char* moe_status_str(int status) {
     case MOE_EUNSUPPORTED: return "unsupported configuration (limits or dtype)";
     case MOE_EWORKSPACE: return "workspace missing or too small";
     case MOE_EHIP: return "HIP runtime reported a launch error";
+    case MOE_ESCRATCH: return "problem needs more scratch than the no-allocation entry point holds (4 MiB)";
     default: return "unknown status";
   }
 }

@@ -239,3 +239,13 @@ def test_route_meta_workspace_follows_the_fusion_rule(lib, N, E, K, fused):
         assert got == blocks * E * 4
     else:
         assert got == L.moe_workspace_bytes(d, L.MOE_ENTRY_PERMUTE_META)
+
+
+def test_noalloc_rejects_a_problem_beyond_its_scratch(lib):
+    """moe_route_meta_noalloc refuses, on the host and before any launch, a
+    problem whose metadata scratch exceeds the library-held array."""
+    d = L.dims(600000, 128, 128, 256, 8, L.MOE_BF16)
+    assert L.moe_workspace_bytes(d, L.MOE_ENTRY_ROUTE_META) > L.MOE_NOALLOC_SCRATCH_BYTES
+    st = lib.moe_route_meta_noalloc(ctypes.byref(d), FAKE, FAKE, None, 2 ** 31 - 1, *([FAKE] * 8), None)
+    assert st == L.MOE_ESCRATCH
+    assert "scratch" in L.moe_status_str(st)
