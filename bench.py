@@ -40,12 +40,22 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # kernel sources whose hash is stored with them; once any source under csrc/
 # changes, the figure is reported as null until the counters are taken again.
 TRAFFIC = {
-    "sources": "2972a363a0b147fc",
+    "sources": "116cd43b8dc022a5",
     "bytes": {
-        ("bf16_n16384_h512_f1024_e8_k2", "gate_up"): 335674845,
-        ("bf16_n16384_h512_f1024_e8_k2", "down"): 148072799,
-        ("bf16_n16384_h512_f1024_e8_k2", "dact"): 339648836,
-        ("bf16_n16384_h512_f1024_e8_k2", "dx_dw"): 678808370,
+        ("bf16_fwd_n8192_h7168_f2048_e256_k8", "down"): 12005259351,
+        ("bf16_fwd_n8192_h7168_f2048_e256_k8", "gate_up"): 23556883135,
+        ("bf16_n16384_h4096_f14336_e8_k2", "dact"): 10623304890,
+        ("bf16_n16384_h4096_f14336_e8_k2", "down"): 7916025484,
+        ("bf16_n16384_h4096_f14336_e8_k2", "dx_dw"): 39398185601,
+        ("bf16_n16384_h4096_f14336_e8_k2", "gate_up"): 18305511794,
+        ("bf16_n16384_h512_f1024_e8_k2", "dact"): 339539102,
+        ("bf16_n16384_h512_f1024_e8_k2", "down"): 147934101,
+        ("bf16_n16384_h512_f1024_e8_k2", "dx_dw"): 656768682,
+        ("bf16_n16384_h512_f1024_e8_k2", "gate_up"): 334024750,
+        ("bf16_skewed_n16384_h2048_f1408_e64_k6", "dact"): 2966883518,
+        ("bf16_skewed_n16384_h2048_f1408_e64_k6", "down"): 1976919347,
+        ("bf16_skewed_n16384_h2048_f1408_e64_k6", "dx_dw"): 9317322511,
+        ("bf16_skewed_n16384_h2048_f1408_e64_k6", "gate_up"): 3716347510,
     },
 }
 
