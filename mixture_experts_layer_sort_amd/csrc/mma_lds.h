@@ -440,16 +440,16 @@ struct MnGather {
 // 0x008 MFMA, 0x020 VMEM read, 0x100 LDS read, 0x200 LDS write).  The
 // step's KK * MK MFMAs are the slots; after slot j come its share of
 //   - the next k step's fragment reads (FR per k step, k steps 0..KK-2),
-//   - the next K tile's global loads (GL, over the first max(1, KK/2) k steps),
+//   - the next K tile's global loads (GL, over the first LK k steps),
 //   - the LDS stores of those loads (GL, over the last k step),
 // each spread evenly over the slots it covers.  The first k step's fragment
 // reads open the step.
-template <int KK, int MK, int FR, int GL, int J = 0>
+template <int KK, int MK, int FR, int GL, int LK, int J = 0>
 __device__ __forceinline__ void reg_step_schedule() {
+  static_assert(LK >= 1 && LK <= KK, "loads spread over 1..KK k steps");
   if constexpr (J == 0) __builtin_amdgcn_sched_group_barrier(0x100, FR, 0);
   if constexpr (J < KK * MK) {
     constexpr int kk = J / MK, i = J % MK;
-    constexpr int LK = KK / 2 > 0 ? KK / 2 : 1;
     constexpr int r = kk + 1 < KK ? (i + 1) * FR / MK - i * FR / MK : 0;
     constexpr int g = kk < LK ? (J + 1) * GL / (LK * MK) - J * GL / (LK * MK) : 0;
     constexpr int w = kk == KK - 1 ? (i + 1) * GL / MK - i * GL / MK : 0;
@@ -457,14 +457,14 @@ __device__ __forceinline__ void reg_step_schedule() {
     if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
     if constexpr (g > 0) __builtin_amdgcn_sched_group_barrier(0x020, g, 0);
     if constexpr (w > 0) __builtin_amdgcn_sched_group_barrier(0x200, w, 0);
-    reg_step_schedule<KK, MK, FR, GL, J + 1>();
+    reg_step_schedule<KK, MK, FR, GL, LK, J + 1>();
   }
 }
 
 // Register-staged K loop over two LDS stages (KK = BK / 16 MFMA k steps per
 // stage).  Each step: the k-step-0 fragments of the current stage are read,
 // the next K tile's chunks are requested into registers, spread between the
-// MFMAs of the first half of the step, each later k step's fragments are
+// MFMAs of the first k step (8 waves) or the first half of the step (4), each later k step's fragments are
 // read while the previous k step multiplies, the chunks go to the other
 // stage between the last k step's MFMAs, and one barrier ends the step.  The
 // last step reloads its own tile (in bounds, never read).  Spreading the
@@ -479,6 +479,12 @@ __device__ __forceinline__ void k_loop_reg(char* lds, Acc<C>& acc, int nk, const
   constexpr int FR = C::FM * (A_MN ? 2 : 1) + C::FN * (B_MN ? 2 : 1);  // LDS reads per k step
   constexpr int MK = C::FM * C::FN;                                    // MFMAs per k step
   constexpr int GL = OA::N + OB::N;                                    // chunks per thread and tile
+  // k steps the next tile's loads are spread over: all in the first one with
+  // two waves per SIMD (the other wave covers the burst; more time for the
+  // loads to land: at H = 4096, F = 14336 merged dX/dW 17.64 -> 17.33 ms, dA
+  // 4.70 -> 4.56, down 3.64 -> 3.57), the first half with one wave per SIMD
+  // (gate/up 7.27 -> 7.42 ms when all in the first)
+  constexpr int LOAD_STEPS = C::NW >= 8 ? 1 : (KK / 2 > 0 ? KK / 2 : 1);
   static_assert(C::S == 2 && KK >= 2 && KK % 2 == 0, "two stages, an even number of k steps per stage");
   zero_acc(acc);
   if (nk <= 0) return;
@@ -514,7 +520,7 @@ __device__ __forceinline__ void k_loop_reg(char* lds, Acc<C>& acc, int nk, const
     }
     oa.store(va, nxt, kn);
     ob.store(vb, nxt + C::A_BYTES, kn);
-    reg_step_schedule<KK, MK, FR, GL>();
+    reg_step_schedule<KK, MK, FR, GL, LOAD_STEPS>();
     __syncthreads();
   }
 }
