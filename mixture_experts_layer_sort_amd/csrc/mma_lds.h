@@ -29,7 +29,7 @@ struct TileCfg {
   static constexpr int OP_BYTES = S * STAGE;
   static constexpr int PITCH = BN + 8;                       // bf16 per staged output row
   static constexpr int EPI_BYTES = BM * PITCH * 2;
-  static constexpr int DACT_BYTES = 2 * TM * PITCH * 2;      // G and U rows of one wave row
+  static constexpr int DACT_BYTES = TM * (BN + 4) * 4;       // float32 dA of one wave row
   static constexpr int LDS_A = OP_BYTES > EPI_BYTES ? OP_BYTES : EPI_BYTES;
   static constexpr int LDS = LDS_A > DACT_BYTES ? LDS_A : DACT_BYTES;
   static constexpr int SUB = MOE_TILE_M / BM;  // workgroup row tiles per list tile
