@@ -187,6 +187,32 @@ __device__ __forceinline__ void mma_stage(const char* sa, const char* sb, Acc<C>
   }
 }
 
+// Workgroup barrier without the memory fence of __syncthreads: with LDS DMA
+// in flight that fence waits for all of it (vmcnt 0), which drains the later
+// stages of the pipeline at every step.  The caller has waited for the DMA
+// it needs; the LDS accesses before it complete first (lgkmcnt 0), and the
+// clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt free
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// One step of the S-stage loop: the DMA of K tile nxt into stage wst (if
+// issue) and the MFMAs over stage rst.  The stages are distinct (restrict),
+// which lets the compiler keep its waits for LDS DMA per stage instead of
+// waiting for every DMA in flight before the first fragment read.
+template <class C, bool A_MN, bool B_MN, class IA, class IB>
+__device__ __forceinline__ void dma_mma_step(char* __restrict__ wst, const char* __restrict__ rst, int nxt, bool issue,
+                                             IA& ia, IB& ib, Acc<C>& acc, int wm, int wn) {
+  if (issue) {
+#pragma unroll
+    for (int j = 0; j < C::JA; ++j) ia(nxt, wst, j);
+#pragma unroll
+    for (int j = 0; j < C::JB; ++j) ib(nxt, wst + C::A_BYTES, j);
+  }
+  mma_stage<C, A_MN, B_MN>(rst, rst + C::A_BYTES, acc, wm, wn);
+}
+
 // S-stage K loop.  ia(kt, stage, j) / ib(kt, stage, j) issue the wave's
 // j-th LDS DMA instruction of K tile kt (j < C::JA resp. C::JB).  Tiles
 // 0 .. S-2 are issued up front; at step kt every wave waits until its own DMA
@@ -215,17 +241,15 @@ __device__ __forceinline__ void k_loop(char* lds, Acc<C>& acc, int nk, IA ia, IB
       wait_vm<C::DPT * (C::S - 2)>();
     else
       wait_vm<0>();
-    __syncthreads();
+    lds_barrier();
     const int nxt = kt + C::S - 1;
-    if (nxt < nk) {
-      char* st = lds + (nxt % C::S) * C::STAGE;
-#pragma unroll
-      for (int j = 0; j < C::JA; ++j) ia(nxt, st, j);
-#pragma unroll
-      for (int j = 0; j < C::JB; ++j) ib(nxt, st + C::A_BYTES, j);
-    }
     char* cur = lds + (kt % C::S) * C::STAGE;
-    if (A_MN && kt == nk - 1 && k_last < C::BK) {
+    if (!(A_MN && kt == nk - 1 && k_last < C::BK)) {
+      dma_mma_step<C, A_MN, B_MN>(lds + (nxt % C::S) * C::STAGE, cur, nxt, nxt < nk, ia, ib, acc, wm, wn);
+      continue;
+    }
+    // last tile with k_last valid k rows (weight gradients; no DMA left to issue)
+    {
       constexpr int ROWB = C::BM * 2;
       uint4* z = reinterpret_cast<uint4*>(cur + k_last * ROWB);
       for (int i = threadIdx.x; i < (C::BK - k_last) * ROWB / 16; i += C::NT) z[i] = make_uint4(0, 0, 0, 0);

@@ -476,12 +476,17 @@ __global__ __launch_bounds__(256) void k_route_small(const bf16_t* __restrict__ 
 }
 
 // Router tile shapes (tokens x padded experts): the MN-contiguous W_r tile
-// needs at least 128 columns for its swizzle.  Up to 128 experts: 32 tokens
-// per workgroup and four workgroups per CU (their two-stage rings fill the
-// 160 KB of LDS); measured at N = 16384 against 64 tokens with two per CU:
-// 9.1 vs 10.7 us (H = 512, E = 8) and 53.6 vs 56.6 us (H = 2048, E = 64).
-using RouteCfg128 = moe_mma::TileCfg<32, 128, 1, 4, 4, 64, 2>;
-using RouteCfg256 = moe_mma::TileCfg<32, 256, 1, 4, 2, 64, 2>;
+// needs at least 128 columns for its swizzle.  32 tokens per workgroup
+// (against 64 with two workgroups per CU: 9.1 vs 10.7 us at H = 512, E = 8
+// and 53.6 vs 56.6 us at H = 2048, E = 64, N = 16384).  Up to 128 experts:
+// four-stage rings, two workgroups per CU (160 KB of LDS), which keeps three
+// 64-deep stages in flight per workgroup; router + metadata went from 88 to
+// 61 us at N = 16384, H = 4096, E = 8 and from 87 to 74 us at H = 2048,
+// E = 64 against two-stage rings with four workgroups per CU (eight stages
+// per CU with one workgroup: 88 us).  256 experts: four stages, one
+// workgroup per CU (no change against two stages at H = 7168).
+using RouteCfg128 = moe_mma::TileCfg<32, 128, 1, 4, 2, 64, 4>;
+using RouteCfg256 = moe_mma::TileCfg<32, 256, 1, 4, 1, 64, 4>;
 static_assert(RouteCfg128::BM * (RouteCfg128::BN + 1) * 4 + MOE_MAX_EXPERTS * 4 <= RouteCfg128::LDS,
               "logits and the block histogram fit the staging space");
 static_assert(RouteCfg256::BM * (RouteCfg256::BN + 1) * 4 + MOE_MAX_EXPERTS * 4 <= RouteCfg256::LDS,
