@@ -36,26 +36,28 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # HBM bytes per launch of each GEMM stage, from two rocprofv3 --pmc runs of
 # this benchmark (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled
 # by what the same counter reads for the plain copy of --copy-calibration
-# (FETCH_SIZE x 2.0000, WRITE_SIZE x 1.0000).  The readings belong to the
-# kernel sources whose hash is stored with them; once any source under csrc/
-# changes, the figure is reported as null until the counters are taken again.
+# (FETCH_SIZE x 2.0000, WRITE_SIZE x 1.0000; FETCH_SIZE counts this GPU's
+# 128-byte read requests as 64 bytes, which the L2's read requests by size
+# confirm for every kernel).  The readings belong to the kernel sources whose
+# hash is stored with them; once any source under csrc/ changes, the figure
+# is reported as null until the counters are taken again.
 TRAFFIC = {
-    "sources": "116cd43b8dc022a5",
+    "sources": "42c17f1e0e6902d9",
     "bytes": {
-        ("bf16_fwd_n8192_h7168_f2048_e256_k8", "down"): 12005259351,
-        ("bf16_fwd_n8192_h7168_f2048_e256_k8", "gate_up"): 23556883135,
-        ("bf16_n16384_h4096_f14336_e8_k2", "dact"): 10623304890,
-        ("bf16_n16384_h4096_f14336_e8_k2", "down"): 7916025484,
-        ("bf16_n16384_h4096_f14336_e8_k2", "dx_dw"): 39398185601,
-        ("bf16_n16384_h4096_f14336_e8_k2", "gate_up"): 18305511794,
-        ("bf16_n16384_h512_f1024_e8_k2", "dact"): 339539102,
-        ("bf16_n16384_h512_f1024_e8_k2", "down"): 147934101,
-        ("bf16_n16384_h512_f1024_e8_k2", "dx_dw"): 656768682,
-        ("bf16_n16384_h512_f1024_e8_k2", "gate_up"): 334024750,
-        ("bf16_skewed_n16384_h2048_f1408_e64_k6", "dact"): 2966883518,
-        ("bf16_skewed_n16384_h2048_f1408_e64_k6", "down"): 1976919347,
-        ("bf16_skewed_n16384_h2048_f1408_e64_k6", "dx_dw"): 9317322511,
-        ("bf16_skewed_n16384_h2048_f1408_e64_k6", "gate_up"): 3716347510,
+        ('bf16_fwd_n8192_h7168_f2048_e256_k8', 'down'): 12405623639,
+        ('bf16_fwd_n8192_h7168_f2048_e256_k8', 'gate_up'): 23659174863,
+        ('bf16_n16384_h4096_f14336_e8_k2', 'dact'): 10545906595,
+        ('bf16_n16384_h4096_f14336_e8_k2', 'down'): 7839026300,
+        ('bf16_n16384_h4096_f14336_e8_k2', 'dx_dw'): 38304910637,
+        ('bf16_n16384_h4096_f14336_e8_k2', 'gate_up'): 18142643024,
+        ('bf16_n16384_h512_f1024_e8_k2', 'dact'): 351189903,
+        ('bf16_n16384_h512_f1024_e8_k2', 'down'): 148103396,
+        ('bf16_n16384_h512_f1024_e8_k2', 'dx_dw'): 657569808,
+        ('bf16_n16384_h512_f1024_e8_k2', 'gate_up'): 335892836,
+        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'dact'): 3171965101,
+        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'down'): 1922872081,
+        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'dx_dw'): 9183069487,
+        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'gate_up'): 3772060406,
     },
 }
 

@@ -195,9 +195,9 @@ hipError_t ffn_bwd_dx_dw_big(const Dims&, const void*, const void*, const void*,
 //   the register-staged loop (SmallR);
 //   down (contraction F): 256 x 256 from F = 1280 on, else 128 x 128 on the
 //   register-staged loop (SmallR);
-//   dA (contraction H): 256 x 256 (8 waves, LDS DMA) from H = 4096 on, below
-//   that 128 x 256 tiles through the LDS DMA pipeline (their staged SwiGLU
-//   epilogue overlaps across two workgroups per CU);
+//   dA (contraction H): 256 x 256 (8 waves, register-staged) from H = 4096
+//   on, below that 128 x 256 tiles through the LDS DMA pipeline (two
+//   workgroups per CU overlap one's SwiGLU epilogue with the other's loop);
 //   dX (contraction 2F): 256 x 256 from 2F = 2560 on;
 //   dW (contraction over an expert's rows): 256 x 256 throughout.
 // A forced family in Dims::tiles (moe_dims.gemm_tiles: 256, 128 x 256 or
