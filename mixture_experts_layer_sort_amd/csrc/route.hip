@@ -484,7 +484,10 @@ __global__ __launch_bounds__(256) void k_route_small(const bf16_t* __restrict__ 
 // 61 us at N = 16384, H = 4096, E = 8 and from 87 to 74 us at H = 2048,
 // E = 64 against two-stage rings with four workgroups per CU (eight stages
 // per CU with one workgroup: 88 us).  256 experts: four stages, one
-// workgroup per CU (no change against two stages at H = 7168).
+// workgroup per CU (no change against two stages at H = 7168, N = 8192,
+// where a timing-only copy without the W_r loads saved 70 of about 230 us
+// and one without the x loads 19: the rest is the latency of each 64-deep
+// step with one 4-wave workgroup per CU).
 using RouteCfg128 = moe_mma::TileCfg<32, 128, 1, 4, 2, 64, 4>;
 using RouteCfg256 = moe_mma::TileCfg<32, 256, 1, 4, 1, 64, 4>;
 static_assert(RouteCfg128::BM * (RouteCfg128::BN + 1) * 4 + MOE_MAX_EXPERTS * 4 <= RouteCfg128::LDS,
