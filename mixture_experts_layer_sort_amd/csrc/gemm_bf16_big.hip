@@ -58,7 +58,8 @@ using Big = TileCfg<256, 256, 2, 2, 1, 64, 2, true>;  // 4 waves, 128 x 128 per 
 // F = 1024, E = 8; 846-851 -> 881 at the skewed H = 2048, E = 64 workload;
 // dA 4.84 -> 4.68 ms at H = 4096, F = 14336 against the 8-wave LDS DMA tile);
 // gate/up keeps 4 waves (1.29 -> 1.31 ms, 5.49 -> 5.61 ms and, at H = 4096,
-// F = 14336, 7.31 -> 7.40 ms with 8).
+// F = 14336, 7.31 -> 7.40 ms with 8; equal within 0.3 % once the 8-wave loop
+// issued its loads in the first k step: 7.22 vs 7.20 ms).
 using Big8 = TileCfg<256, 256, 4, 2, 1, 64, 2, true>;
 // 128 x 256 tiles through the same DMA pipeline, 32 k per stage, three stages
 // (72 KiB of LDS, two workgroups per CU): used by the SwiGLU backward on
