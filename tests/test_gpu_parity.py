@@ -48,7 +48,11 @@ def _runner(cfg, backward=True, gather=None, dw_gather=False):
 # LDS-resident router at its largest shape (E = 32, H = 1024)
 ROUTER_PATHS = [MoEConfig("t_route_e64", N=300, H=256, F=128, E=64, K=4, dtype="bf16"),
                 MoEConfig("t_route_h1152", N=300, H=1152, F=128, E=8, K=2, dtype="bf16"),
-                MoEConfig("t_route_e32_h1024", N=300, H=1024, F=128, E=32, K=6, dtype="bf16")]
+                MoEConfig("t_route_e32_h1024", N=300, H=1024, F=128, E=32, K=6, dtype="bf16"),
+                # fewer 64-deep K steps (2) than the four-stage DMA rings issue up front (3), at 128
+                # and 256 padded expert columns
+                MoEConfig("t_route_e64_h128", N=300, H=128, F=128, E=64, K=4, dtype="bf16"),
+                MoEConfig("t_route_e256_h128", N=300, H=128, F=128, E=256, K=8, dtype="bf16")]
 
 
 @pytest.mark.parametrize("cfg", SMALL + ROUTER_PATHS, ids=lambda c: c.name)
