@@ -253,10 +253,12 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_gate_up(const bf16_t* __rest
     static_assert(C::REG, "the gathered A tile uses the register-staged loop");
     k_loop_reg<C, false, true>(lds, acc, H / C::BK,
                                KcGather<C::BM, C::BK, C::NT>(xs, sorted_flat + ti.row0, K, H, ti.rows),
-                               MnOp<C::BN, C::BK, C::NT>(b_g, b_u, HALF, F, C::BN), wm, wn);
+                               MnOp<C::BN, C::BK, C::NT>(b_g, b_u, HALF, F, C::BN), wm, wn, C::BK,
+                               wm * C::TM < ti.rows);
   } else if constexpr (C::REG) {
     k_loop_reg<C, false, true>(lds, acc, H / C::BK, KcOp<C::BM, C::BK, C::NT>(a_base, a_base, kNoSplit, H, ti.rows),
-                               MnOp<C::BN, C::BK, C::NT>(b_g, b_u, HALF, F, C::BN), wm, wn);
+                               MnOp<C::BN, C::BK, C::NT>(b_g, b_u, HALF, F, C::BN), wm, wn, C::BK,
+                               wm * C::TM < ti.rows);
   } else {
     k_loop<C, false, true>(
         lds, acc, H / C::BK,
@@ -317,7 +319,8 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_down(const bf16_t* __restric
   Acc<C> acc;
   if constexpr (C::REG) {
     k_loop_reg<C, false, true>(lds, acc, F / C::BK, KcOp<C::BM, C::BK, C::NT>(a_base, a_base, kNoSplit, F, ti.rows),
-                               MnBuf<C::BN, C::BK, C::NT>(b_base, H, ncols, F), wm, wn);
+                               MnBuf<C::BN, C::BK, C::NT>(b_base, H, ncols, F), wm, wn, C::BK,
+                               wm * C::TM < ti.rows);
   } else {
     k_loop<C, false, true>(
         lds, acc, F / C::BK,
@@ -376,7 +379,8 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_dact(const bf16_t* __restric
   Acc<C> acc;
   if constexpr (C::REG) {
     k_loop_reg<C, false, false>(lds, acc, H / C::BK, KcOp<C::BM, C::BK, C::NT>(a_base, a_base, kNoSplit, H, ti.rows),
-                                KcOp<C::BN, C::BK, C::NT>(b_base, b_base, kNoSplit, H, ncols), wm, wn);
+                                KcOp<C::BN, C::BK, C::NT>(b_base, b_base, kNoSplit, H, ncols), wm, wn, C::BK,
+                                wm * C::TM < ti.rows);
   } else {
     k_loop<C, false, false>(
         lds, acc, H / C::BK,
@@ -488,7 +492,8 @@ __device__ __forceinline__ void dx_tile(char* lds, int b, const bf16_t* __restri
     const int64_t aoff = (int64_t)ti.row0 * F;
     k_loop_reg<C, false, false>(lds, acc, 2 * nkf,
                                 KcOp<C::BM, C::BK, C::NT>(dg + aoff, du + aoff, nkf, F, ti.rows),
-                                KcOp<C::BN, C::BK, C::NT>(wg + woff, wu + woff, nkf, F, ncols), wm, wn);
+                                KcOp<C::BN, C::BK, C::NT>(wg + woff, wu + woff, nkf, F, ncols), wm, wn, C::BK,
+                                wm * C::TM < ti.rows);
   } else {
   k_loop<C, false, false>(
       lds, acc, 2 * nkf,

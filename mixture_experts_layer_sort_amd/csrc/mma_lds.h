@@ -485,20 +485,14 @@ __device__ __forceinline__ void reg_step_schedule() {
   }
 }
 
-// Register-staged K loop over two LDS stages (KK = BK / 16 MFMA k steps per
-// stage).  Each step: the k-step-0 fragments of the current stage are read,
-// the next K tile's chunks are requested into registers, spread between the
-// MFMAs of the first k step (8 waves) or the first half of the step (4), each later k step's fragments are
-// read while the previous k step multiplies, the chunks go to the other
-// stage between the last k step's MFMAs, and one barrier ends the step.  The
-// last step reloads its own tile (in bounds, never read).  Spreading the
-// requests keeps the wave's in-order issue from stalling its MFMAs behind a
-// burst of loads.  When the last tile holds only k_last valid k rows (weight
-// gradients), rows k_last.. of its A stage (an MN tile) are zeroed before it
-// is used.
-template <class C, bool A_MN, bool B_MN, class OA, class OB>
-__device__ __forceinline__ void k_loop_reg(char* lds, Acc<C>& acc, int nk, const OA& oa, const OB& ob, int wm,
-                                           int wn, int k_last = C::BK) {
+// Steps of the register-staged K loop (below).  MMA = false: a wave whose
+// tile rows all lie past the tile's valid rows only moves its share of the
+// operand chunks (its MFMAs and fragment reads would only make rows that are
+// never stored); the barriers are the same, so the workgroup stays in step.
+template <class C, bool A_MN, bool B_MN, bool MMA, class OA, class OB>
+__device__ __forceinline__ void k_steps_reg(char* lds, Acc<C>& acc, int nk, const OA& oa, const OB& ob,
+                                            u32x4_t (&va)[OA::N], u32x4_t (&vb)[OB::N], int wm, int wn,
+                                            int k_last) {
   constexpr int KK = C::BK / 16;
   constexpr int FR = C::FM * (A_MN ? 2 : 1) + C::FN * (B_MN ? 2 : 1);  // LDS reads per k step
   constexpr int MK = C::FM * C::FN;                                    // MFMAs per k step
@@ -509,15 +503,6 @@ __device__ __forceinline__ void k_loop_reg(char* lds, Acc<C>& acc, int nk, const
   // 4.70 -> 4.56, down 3.64 -> 3.57), the first half with one wave per SIMD
   // (gate/up 7.27 -> 7.42 ms when all in the first)
   constexpr int LOAD_STEPS = C::NW >= 8 ? 1 : (KK / 2 > 0 ? KK / 2 : 1);
-  static_assert(C::S == 2 && KK >= 2 && KK % 2 == 0, "two stages, an even number of k steps per stage");
-  zero_acc(acc);
-  if (nk <= 0) return;
-  u32x4_t va[OA::N], vb[OB::N];
-  oa.load(va, 0);
-  ob.load(vb, 0);
-  oa.store(va, lds, 0);
-  ob.store(vb, lds + C::A_BYTES, 0);
-  __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     char* cur = lds + (kt & 1) * C::STAGE;
     char* nxt = lds + ((kt + 1) & 1) * C::STAGE;
@@ -528,25 +513,67 @@ __device__ __forceinline__ void k_loop_reg(char* lds, Acc<C>& acc, int nk, const
       for (int i = threadIdx.x; i < (C::BK - k_last) * ROWB / 16; i += C::NT) z[i] = u32x4_t{0u, 0u, 0u, 0u};
       __syncthreads();
     }
-    bf16x8_t fa[2][C::FM], fb[2][C::FN];
-    load_frags<C, A_MN, B_MN>(cur, cur + C::A_BYTES, 0, wm, wn, fa[0], fb[0]);
-    oa.load(va, kn);
-    ob.load(vb, kn);
+    if constexpr (MMA) {
+      bf16x8_t fa[2][C::FM], fb[2][C::FN];
+      load_frags<C, A_MN, B_MN>(cur, cur + C::A_BYTES, 0, wm, wn, fa[0], fb[0]);
+      oa.load(va, kn);
+      ob.load(vb, kn);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const int cb = kk & 1;
-      if (kk + 1 < KK) load_frags<C, A_MN, B_MN>(cur, cur + C::A_BYTES, kk + 1, wm, wn, fa[cb ^ 1], fb[cb ^ 1]);
+      for (int kk = 0; kk < KK; ++kk) {
+        const int cb = kk & 1;
+        if (kk + 1 < KK) load_frags<C, A_MN, B_MN>(cur, cur + C::A_BYTES, kk + 1, wm, wn, fa[cb ^ 1], fb[cb ^ 1]);
 #pragma unroll
-      for (int mi = 0; mi < C::FM; ++mi)
+        for (int mi = 0; mi < C::FM; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < C::FN; ++ni)
-          acc.a[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cb][mi], fb[cb][ni], acc.a[mi][ni], 0, 0, 0);
+          for (int ni = 0; ni < C::FN; ++ni)
+            acc.a[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cb][mi], fb[cb][ni], acc.a[mi][ni], 0, 0, 0);
+      }
+      oa.store(va, nxt, kn);
+      ob.store(vb, nxt + C::A_BYTES, kn);
+      reg_step_schedule<KK, MK, FR, GL, LOAD_STEPS>();
+    } else {
+      oa.load(va, kn);
+      ob.load(vb, kn);
+      oa.store(va, nxt, kn);
+      ob.store(vb, nxt + C::A_BYTES, kn);
     }
-    oa.store(va, nxt, kn);
-    ob.store(vb, nxt + C::A_BYTES, kn);
-    reg_step_schedule<KK, MK, FR, GL, LOAD_STEPS>();
     __syncthreads();
   }
+}
+
+// Register-staged K loop over two LDS stages (KK = BK / 16 MFMA k steps per
+// stage).  Each step: the k-step-0 fragments of the current stage are read,
+// the next K tile's chunks are requested into registers, spread between the
+// MFMAs of the first k step (8 waves) or the first half of the step (4), each later k step's fragments are
+// read while the previous k step multiplies, the chunks go to the other
+// stage between the last k step's MFMAs, and one barrier ends the step.  The
+// last step reloads its own tile (in bounds, never read).  Spreading the
+// requests keeps the wave's in-order issue from stalling its MFMAs behind a
+// burst of loads.  When the last tile holds only k_last valid k rows (weight
+// gradients), rows k_last.. of its A stage (an MN tile) are zeroed before it
+// is used.  mma = false (wave-uniform): the wave's rows are all past the
+// tile's valid rows, so it moves operand chunks only and its accumulators
+// stay zero; with two waves per SIMD that halves the matrix-core work of a
+// SIMD on a tile of at most half its rows (skewed routing, H = 2048,
+// F = 1408, E = 64, where 36 of 64 experts have fewer than 128 rows: merged
+// dX/dW 3.376-3.414 -> 3.345-3.356 ms; no change where few tiles are ragged).
+template <class C, bool A_MN, bool B_MN, class OA, class OB>
+__device__ __forceinline__ void k_loop_reg(char* lds, Acc<C>& acc, int nk, const OA& oa, const OB& ob, int wm,
+                                           int wn, int k_last = C::BK, bool mma = true) {
+  constexpr int KK = C::BK / 16;
+  static_assert(C::S == 2 && KK >= 2 && KK % 2 == 0, "two stages, an even number of k steps per stage");
+  zero_acc(acc);
+  if (nk <= 0) return;
+  u32x4_t va[OA::N], vb[OB::N];
+  oa.load(va, 0);
+  ob.load(vb, 0);
+  oa.store(va, lds, 0);
+  ob.store(vb, lds + C::A_BYTES, 0);
+  __syncthreads();
+  if (__builtin_amdgcn_readfirstlane(mma ? 1 : 0))
+    k_steps_reg<C, A_MN, B_MN, true>(lds, acc, nk, oa, ob, va, vb, wm, wn, k_last);
+  else
+    k_steps_reg<C, A_MN, B_MN, false>(lds, acc, nk, oa, ob, va, vb, wm, wn, k_last);
 }
 
 // Accumulator element r of fragment (mi, ni): MFMA 32x32 result layout
