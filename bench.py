@@ -42,22 +42,22 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # hash is stored with them; once any source under csrc/ changes, the figure
 # is reported as null until the counters are taken again.
 TRAFFIC = {
-    "sources": "0b16435e48442d49",
+    "sources": "583d499a4bee38ac",
     "bytes": {
-        ('bf16_fwd_n8192_h7168_f2048_e256_k8', 'down'): 13826466289,
-        ('bf16_fwd_n8192_h7168_f2048_e256_k8', 'gate_up'): 27462323713,
-        ('bf16_n16384_h4096_f14336_e8_k2', 'dact'): 10688290205,
-        ('bf16_n16384_h4096_f14336_e8_k2', 'down'): 8065538848,
-        ('bf16_n16384_h4096_f14336_e8_k2', 'dx_dw'): 38858198948,
-        ('bf16_n16384_h4096_f14336_e8_k2', 'gate_up'): 19119919331,
-        ('bf16_n16384_h512_f1024_e8_k2', 'dact'): 351262000,
-        ('bf16_n16384_h512_f1024_e8_k2', 'down'): 148102604,
-        ('bf16_n16384_h512_f1024_e8_k2', 'dx_dw'): 658793621,
-        ('bf16_n16384_h512_f1024_e8_k2', 'gate_up'): 337468808,
-        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'dact'): 3157787638,
-        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'down'): 1947497117,
-        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'dx_dw'): 9138315559,
-        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'gate_up'): 3814309629,
+        ('bf16_fwd_n8192_h7168_f2048_e256_k8', 'down'): 13839061004,
+        ('bf16_fwd_n8192_h7168_f2048_e256_k8', 'gate_up'): 27190977552,
+        ('bf16_n16384_h4096_f14336_e8_k2', 'dact'): 10682656514,
+        ('bf16_n16384_h4096_f14336_e8_k2', 'down'): 8048195064,
+        ('bf16_n16384_h4096_f14336_e8_k2', 'dx_dw'): 39169343444,
+        ('bf16_n16384_h4096_f14336_e8_k2', 'gate_up'): 19480948491,
+        ('bf16_n16384_h512_f1024_e8_k2', 'dact'): 350465897,
+        ('bf16_n16384_h512_f1024_e8_k2', 'down'): 148076000,
+        ('bf16_n16384_h512_f1024_e8_k2', 'dx_dw'): 657192405,
+        ('bf16_n16384_h512_f1024_e8_k2', 'gate_up'): 338315464,
+        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'dact'): 3176457331,
+        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'down'): 1959397501,
+        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'dx_dw'): 9183985540,
+        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'gate_up'): 3818846063,
     },
 }
 
