@@ -105,6 +105,16 @@ __device__ __forceinline__ int xcd_window_block(int b, int total) {
 }
 __device__ __forceinline__ int xcd_window_block(int total) { return xcd_window_block<kXcdRun>(blockIdx.x, total); }
 
+// Largest row count of any expert, from offsets [E+1]; computed by each wave
+// on its own (the same value in every lane and wave).
+__device__ __forceinline__ int max_expert_rows(const int32_t* __restrict__ offsets, int E) {
+  int m = 0;
+  for (int e = lane_id(); e < E; e += kWave) m = max(m, offsets[e + 1] - offsets[e]);
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) m = max(m, __shfl_xor(m, off, kWave));
+  return m;
+}
+
 // The expert of rank p when experts are ordered by row count, largest first
 // (equal counts: lower id first), from offsets [E+1].  The weight-gradient
 // workgroups take their expert in this order, so the longest contractions
