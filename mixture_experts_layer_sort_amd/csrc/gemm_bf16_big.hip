@@ -159,16 +159,16 @@ __device__ __forceinline__ int xcd_block(int b, int total) {
 }
 __device__ __forceinline__ int xcd_block(int total) { return xcd_block(blockIdx.x, total); }
 
-// Logical block -> (row tile, n tile) in groups of kGroupM row tiles: inside
+// Logical block -> (row tile, n tile) in groups of gmax row tiles: inside
 // a group the row tile varies fastest, so the ~32 workgroups an XCD runs at
-// once cover a patch of kGroupM row tiles x 32/kGroupM n tiles and each
-// weight tile and each activation tile is fetched from HBM once per patch.
+// once cover a patch of gmax row tiles x 32/gmax n tiles and each weight
+// tile and each activation tile is fetched from HBM once per patch.
 constexpr int kGroupM = 8;
-__device__ __forceinline__ void grouped(int L, int nrow, int ncol, int& row, int& col) {
-  const int per_group = kGroupM * ncol;
+__device__ __forceinline__ void grouped(int L, int nrow, int ncol, int& row, int& col, int gmax) {
+  const int per_group = gmax * ncol;
   const int g = L / per_group, r = L % per_group;
-  const int first = g * kGroupM;
-  const int gm = min(kGroupM, nrow - first);
+  const int first = g * gmax;
+  const int gm = min(gmax, nrow - first);
   row = first + r % gm;
   col = r / gm;
 }
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_gate_up(const bf16_t* __rest
                                                    const bf16_t* __restrict__ wu, const int32_t* __restrict__ tiles,
                                                    const int32_t* __restrict__ num_tiles, bf16_t* __restrict__ g_out,
                                                    bf16_t* __restrict__ u_out, bf16_t* __restrict__ a_out, int H,
-                                                   int F) {
+                                                   int F, int gm) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   constexpr int HALF = C::BN / 2;
   const int ntn = F / HALF;
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_gate_up(const bf16_t* __rest
   const int L = xcd_block(nrow * ntn);
   if (L < 0) return;
   int rt, nt;
-  grouped(L, nrow, ntn, rt, nt);
+  grouped(L, nrow, ntn, rt, nt, gm);
   const TileInfo ti = row_tile<C>(tiles, rt);
   if (ti.rows <= 0) return;
   const int w = threadIdx.x >> 6, wm = w / C::WN, wn = w % C::WN;
@@ -302,14 +302,14 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_gate_up(const bf16_t* __rest
 template <class C>
 __global__ __launch_bounds__(C::NT, C::MINB) void k_down(const bf16_t* __restrict__ act, const bf16_t* __restrict__ wd,
                                                 const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles,
-                                                bf16_t* __restrict__ ys, int H, int F) {
+                                                bf16_t* __restrict__ ys, int H, int F, int gm) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int ntn = (H + C::BN - 1) / C::BN;
   const int nrow = *num_tiles * C::SUB;
   const int L = xcd_block(nrow * ntn);
   if (L < 0) return;
   int rt, nt;
-  grouped(L, nrow, ntn, rt, nt);
+  grouped(L, nrow, ntn, rt, nt, gm);
   const TileInfo ti = row_tile<C>(tiles, rt);
   if (ti.rows <= 0) return;
   const int ncols = min(C::BN, H - nt * C::BN);
@@ -361,14 +361,15 @@ template <class C>
 __global__ __launch_bounds__(C::NT, C::MINB) void k_dact(const bf16_t* __restrict__ dys, const bf16_t* __restrict__ wd,
                                                 const bf16_t* __restrict__ g_in, const bf16_t* __restrict__ u_in,
                                                 const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles,
-                                                bf16_t* __restrict__ dg, bf16_t* __restrict__ du, int H, int F) {
+                                                bf16_t* __restrict__ dg, bf16_t* __restrict__ du, int H, int F,
+                                                int gm) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int ntn = (F + C::BN - 1) / C::BN;
   const int nrow = *num_tiles * C::SUB;
   const int L = xcd_block(nrow * ntn);
   if (L < 0) return;
   int rt, nt;
-  grouped(L, nrow, ntn, rt, nt);
+  grouped(L, nrow, ntn, rt, nt, gm);
   const TileInfo ti = row_tile<C>(tiles, rt);
   if (ti.rows <= 0) return;
   const int ncols = min(C::BN, F - nt * C::BN);
@@ -473,13 +474,13 @@ __device__ __forceinline__ void dx_tile(char* lds, int b, const bf16_t* __restri
                                         const bf16_t* __restrict__ du, const bf16_t* __restrict__ wg,
                                         const bf16_t* __restrict__ wu, const int32_t* __restrict__ tiles,
                                         const int32_t* __restrict__ num_tiles, bf16_t* __restrict__ dxs, int H,
-                                        int F) {
+                                        int F, int gm) {
   const int ntn = (H + C::BN - 1) / C::BN;
   const int nrow = *num_tiles * C::SUB;
   const int L = xcd_block(b, nrow * ntn);
   if (L < 0) return;
   int rt, nt;
-  grouped(L, nrow, ntn, rt, nt);
+  grouped(L, nrow, ntn, rt, nt, gm);
   const TileInfo ti = row_tile<C>(tiles, rt);
   if (ti.rows <= 0) return;
   const int ncols = min(C::BN, H - nt * C::BN);
@@ -518,9 +519,9 @@ template <class C>
 __global__ __launch_bounds__(C::NT, C::MINB) void k_dx(const bf16_t* __restrict__ dg, const bf16_t* __restrict__ du,
                                               const bf16_t* __restrict__ wg, const bf16_t* __restrict__ wu,
                                               const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles,
-                                              bf16_t* __restrict__ dxs, int H, int F) {
+                                              bf16_t* __restrict__ dxs, int H, int F, int gm) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  dx_tile<C>(lds, blockIdx.x, dg, du, wg, wu, tiles, num_tiles, dxs, H, F);
+  dx_tile<C>(lds, blockIdx.x, dg, du, wg, wu, tiles, num_tiles, dxs, H, F, gm);
 }
 
 // Weight gradients, one workgroup per BM x BN output tile of one expert:
@@ -636,7 +637,7 @@ __global__ __launch_bounds__(CW::NT, CW::MINB) void k_dx_dw(
     bf16_t* __restrict__ dxs, const bf16_t* __restrict__ xs, const bf16_t* __restrict__ act,
     const bf16_t* __restrict__ dys, const int32_t* __restrict__ offsets, float* __restrict__ dwg,
     float* __restrict__ dwu, float* __restrict__ dwd, int H, int F, int E, int dw_grid, int dx_grid,
-    const int32_t* __restrict__ sorted_flat, int K) {
+    const int32_t* __restrict__ sorted_flat, int K, int gm) {
   static_assert(CW::NT == CX::NT, "one block size");
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int b = blockIdx.x;
@@ -652,7 +653,7 @@ __global__ __launch_bounds__(CW::NT, CW::MINB) void k_dx_dw(
   // would count as divergent and keep both tile paths live, spilling)
   const bool dx_first = __builtin_amdgcn_readfirstlane(2 * F >= max_expert_rows(offsets, E) ? 1 : 0) != 0;
   if (dx_first ? b < dx_grid : b >= dw_grid)
-    dx_tile<CX>(lds, dx_first ? b : b - dw_grid, dg, du, wg, wu, tiles, num_tiles, dxs, H, F);
+    dx_tile<CX>(lds, dx_first ? b : b - dw_grid, dg, du, wg, wu, tiles, num_tiles, dxs, H, F, gm);
   else
     dw_tile<CW, GATHER>(lds, dx_first ? b - dx_grid : b, xs, act, dys, dg, du, offsets, dwg, dwu, dwd, H, F, E,
                         sorted_flat, K);
@@ -665,6 +666,17 @@ namespace moe_launch {
 // grid size rounded up to whole XCD rounds
 static unsigned grid8(int64_t n) { return unsigned((n + kXcds - 1) / kXcds * kXcds); }
 
+// Row tiles per patch of the row-tile GEMMs: kGroupM when the experts average
+// more than one row tile of bm rows, so a patch's row tiles mostly belong to
+// one expert and share its weight tiles; else 1, so a patch covers all n
+// tiles of one row tile, which share its activation panel (row tiles of
+// different experts share nothing).  At N = 8192, H = 7168, F = 2048,
+// E = 256, K = 8 (256 rows per expert): gate/up 5.27-5.28 -> 5.13 ms and down
+// 2.71-2.72 -> 2.66 ms against patches of 8 row tiles (2 and 4: no gain).
+static int group_rows(const Dims& d, int bm) {
+  return int64_t(d.N) * d.K > int64_t(d.E) * bm ? kGroupM : 1;
+}
+
 template <class C, bool GATHER = false>
 static hipError_t gate_up_t(const Dims& d, const void* xs, const int32_t* sorted_flat, const void* wg, const void* wu,
                             const int32_t* tiles, const int32_t* num_tiles, void* g, void* u, void* a, hipStream_t s) {
@@ -674,7 +686,7 @@ static hipError_t gate_up_t(const Dims& d, const void* xs, const int32_t* sorted
   hipLaunchKernelGGL((k_gate_up<C, GATHER>), dim3(grid), dim3(C::NT), C::LDS, s, static_cast<const bf16_t*>(xs),
                      sorted_flat, int(d.K), static_cast<const bf16_t*>(wg), static_cast<const bf16_t*>(wu), tiles,
                      num_tiles, static_cast<bf16_t*>(g), static_cast<bf16_t*>(u), static_cast<bf16_t*>(a), int(d.H),
-                     int(d.F));
+                     int(d.F), group_rows(d, C::BM));
   return hipGetLastError();
 }
 
@@ -692,7 +704,8 @@ static hipError_t down_t(const Dims& d, const void* a, const void* wd, const int
   if (st != hipSuccess) return st;
   unsigned grid = grid8(max_tiles(d) * C::SUB * ((d.H + C::BN - 1) / C::BN));
   hipLaunchKernelGGL(k_down<C>, dim3(grid), dim3(C::NT), C::LDS, s, static_cast<const bf16_t*>(a),
-                     static_cast<const bf16_t*>(wd), tiles, num_tiles, static_cast<bf16_t*>(ys), int(d.H), int(d.F));
+                     static_cast<const bf16_t*>(wd), tiles, num_tiles, static_cast<bf16_t*>(ys), int(d.H), int(d.F),
+                     group_rows(d, C::BM));
   return hipGetLastError();
 }
 
@@ -709,7 +722,8 @@ static hipError_t dact_t(const Dims& d, const void* dys, const void* wd, const v
   unsigned grid = grid8(max_tiles(d) * C::SUB * ((d.F + C::BN - 1) / C::BN));
   hipLaunchKernelGGL(k_dact<C>, dim3(grid), dim3(C::NT), C::LDS, s, static_cast<const bf16_t*>(dys),
                      static_cast<const bf16_t*>(wd), static_cast<const bf16_t*>(g), static_cast<const bf16_t*>(u),
-                     tiles, num_tiles, static_cast<bf16_t*>(dg), static_cast<bf16_t*>(du), int(d.H), int(d.F));
+                     tiles, num_tiles, static_cast<bf16_t*>(dg), static_cast<bf16_t*>(du), int(d.H), int(d.F),
+                     group_rows(d, C::BM));
   return hipGetLastError();
 }
 
@@ -731,7 +745,7 @@ static hipError_t dx_t(const Dims& d, const void* dg, const void* du, const void
   unsigned grid = grid8(max_tiles(d) * C::SUB * ((d.H + C::BN - 1) / C::BN));
   hipLaunchKernelGGL(k_dx<C>, dim3(grid), dim3(C::NT), C::LDS, s, static_cast<const bf16_t*>(dg),
                      static_cast<const bf16_t*>(du), static_cast<const bf16_t*>(wg), static_cast<const bf16_t*>(wu),
-                     tiles, num_tiles, static_cast<bf16_t*>(dxs), int(d.H), int(d.F));
+                     tiles, num_tiles, static_cast<bf16_t*>(dxs), int(d.H), int(d.F), group_rows(d, C::BM));
   return hipGetLastError();
 }
 
@@ -794,7 +808,7 @@ hipError_t ffn_bwd_dx_dw_big(const Dims& d, const void* dg, const void* du, cons
                        static_cast<const bf16_t*>(wu), tiles, num_tiles, static_cast<bf16_t*>(dxs),
                        static_cast<const bf16_t*>(xs), static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(dys),
                        offsets, dwg, dwu, dwd, int(d.H), int(d.F), int(d.E), int(gw), int(gx), sorted_flat,
-                       int(d.K));
+                       int(d.K), group_rows(d, CX::BM));
     return hipGetLastError();
   };
   return sorted_flat ? run(std::true_type{}) : run(std::false_type{});
