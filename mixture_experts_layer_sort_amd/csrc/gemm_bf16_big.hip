@@ -21,8 +21,10 @@
 // other LDS stage between the last k step's MFMAs; one barrier per step.
 // Spreading the requests keeps each wave's in-order issue from parking its
 // MFMAs behind a burst of loads, which is what held the LDS DMA version of
-// this loop near 0.8 PFLOP/s.  The 8-wave form of the same loop (Big8) runs
-// dX, the weight gradients, down and the SwiGLU backward.
+// this loop near 0.8 PFLOP/s.  The 8-wave tile of the same shape (Big8)
+// runs dX, the weight gradients, down and the SwiGLU backward on the
+// mixed-depth LDS DMA loop (k_loop_dma2: operand A one K tile ahead, B two,
+// both through buffer-resource DMA, so nothing in flight occupies registers).
 //
 // A K-contiguous operand (token rows; weight rows in the backward) sits in
 // LDS as [rows][64 k] and is read with 16-byte fragment loads; an
@@ -46,6 +48,7 @@
 
 #include "mma_lds.h"
 
+
 namespace {
 using namespace moe;
 
@@ -59,7 +62,9 @@ using Big = TileCfg<256, 256, 2, 2, 1, 64, 2, true>;  // 4 waves, 128 x 128 per 
 // dA 4.84 -> 4.68 ms at H = 4096, F = 14336 against the 8-wave LDS DMA tile);
 // gate/up keeps 4 waves (1.29 -> 1.31 ms, 5.49 -> 5.61 ms and, at H = 4096,
 // F = 14336, 7.31 -> 7.40 ms with 8; equal within 0.3 % once the 8-wave loop
-// issued its loads in the first k step: 7.22 vs 7.20 ms).
+// issued its loads in the first k step: 7.22 vs 7.20 ms).  Those figures
+// are for the register-staged loop; the Big8 kernels now run k_loop_dma2
+// (mma_lds.h), whose 160 KiB of LDS slots the launches request.
 using Big8 = TileCfg<256, 256, 4, 2, 1, 64, 2, true>;
 // 128 x 256 tiles through the same DMA pipeline, 32 k per stage, three stages
 // (72 KiB of LDS, two workgroups per CU): used by the SwiGLU backward on
@@ -317,7 +322,10 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_down(const bf16_t* __restric
   const bf16_t* a_base = act + (int64_t)ti.row0 * F;
   const bf16_t* b_base = wd + (int64_t)ti.e * F * H + nt * C::BN;
   Acc<C> acc;
-  if constexpr (C::REG) {
+  if constexpr (C::REG && C::NW >= 8) {
+    k_loop_dma2<C, false, true>(lds, acc, F / C::BK, KcDma<C::BM, C::BK, C::NW>(a_base, F, ti.rows),
+                         MnDma<C::BN, C::BK, C::NW>(b_base, H, ncols), wm, wn, wm * C::TM < ti.rows);
+  } else if constexpr (C::REG) {
     k_loop_reg<C, false, true>(lds, acc, F / C::BK, KcOp<C::BM, C::BK, C::NT>(a_base, a_base, kNoSplit, F, ti.rows),
                                MnBuf<C::BN, C::BK, C::NT>(b_base, H, ncols, F), wm, wn, C::BK,
                                wm * C::TM < ti.rows);
@@ -378,7 +386,10 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_dact(const bf16_t* __restric
   // B[k = h][n = f] = W_down[e][f][h]: rows f of W_down[e] are k-contiguous
   const bf16_t* b_base = wd + (int64_t)ti.e * F * H + (int64_t)nt * C::BN * H;
   Acc<C> acc;
-  if constexpr (C::REG) {
+  if constexpr (C::REG && C::NW >= 8) {
+    k_loop_dma2<C, false, false>(lds, acc, H / C::BK, KcDma<C::BM, C::BK, C::NW>(a_base, H, ti.rows),
+                             KcDma<C::BN, C::BK, C::NW>(b_base, H, ncols), wm, wn, wm * C::TM < ti.rows);
+  } else if constexpr (C::REG) {
     k_loop_reg<C, false, false>(lds, acc, H / C::BK, KcOp<C::BM, C::BK, C::NT>(a_base, a_base, kNoSplit, H, ti.rows),
                                 KcOp<C::BN, C::BK, C::NT>(b_base, b_base, kNoSplit, H, ncols), wm, wn, C::BK,
                                 wm * C::TM < ti.rows);
@@ -489,7 +500,12 @@ __device__ __forceinline__ void dx_tile(char* lds, int b, const bf16_t* __restri
   const int64_t woff = (int64_t)ti.e * H * F + (int64_t)nt * C::BN * F;
   const int nkf = F / C::BK;
   Acc<C> acc;
-  if constexpr (C::REG) {
+  if constexpr (C::REG && C::NW >= 8) {
+    const int64_t aoff = (int64_t)ti.row0 * F;
+    k_loop_dma2<C, false, false>(lds, acc, 2 * nkf, KcDma<C::BM, C::BK, C::NW>(dg + aoff, du + aoff, nkf, F, ti.rows),
+                             KcDma<C::BN, C::BK, C::NW>(wg + woff, wu + woff, nkf, F, ncols), wm, wn,
+                             wm * C::TM < ti.rows);
+  } else if constexpr (C::REG) {
     const int64_t aoff = (int64_t)ti.row0 * F;
     k_loop_reg<C, false, false>(lds, acc, 2 * nkf,
                                 KcOp<C::BM, C::BK, C::NT>(dg + aoff, du + aoff, nkf, F, ti.rows),
@@ -582,6 +598,10 @@ __device__ __forceinline__ void dw_tile(char* lds, int b, const bf16_t* __restri
     else
       k_loop_reg<C, true, true>(lds, acc, nk, MnBuf<C::BM, C::BK, C::NT>(l_base, P, prow, cnt),
                                 MnBuf<C::BN, C::BK, C::NT>(r_base, Q, qcol, cnt), wm, wn, cnt - (nk - 1) * C::BK);
+  } else if constexpr (C::REG && C::NW >= 8) {
+    k_loop_dma2<C, true, true>(lds, acc, nk, MnDma<C::BM, C::BK, C::NW>(l_base, P, prow, cnt),
+                            MnDma<C::BN, C::BK, C::NW>(r_base, Q, qcol, cnt), wm, wn, true,
+                            cnt - (nk - 1) * C::BK);
   } else if constexpr (C::REG) {
     k_loop_reg<C, true, true>(lds, acc, nk, MnBuf<C::BM, C::BK, C::NT>(l_base, P, prow, cnt),
                               MnBuf<C::BN, C::BK, C::NT>(r_base, Q, qcol, cnt), wm, wn, cnt - (nk - 1) * C::BK);
@@ -663,6 +683,14 @@ __global__ __launch_bounds__(CW::NT, CW::MINB) void k_dx_dw(
 
 namespace moe_launch {
 
+// Dynamic LDS of a launch: the 8-wave register-staged tiles may run the
+// mixed-depth DMA loop, whose slots take 160 KiB (one workgroup per CU either
+// way).
+template <class C>
+constexpr int lds_bytes_of() {
+  return C::REG && C::NW >= 8 && C::BM == 256 ? Dma2Layout<C>::LDS : C::LDS;
+}
+
 // grid size rounded up to whole XCD rounds
 static unsigned grid8(int64_t n) { return unsigned((n + kXcds - 1) / kXcds * kXcds); }
 
@@ -680,13 +708,14 @@ static int group_rows(const Dims& d, int bm) {
 template <class C, bool GATHER = false>
 static hipError_t gate_up_t(const Dims& d, const void* xs, const int32_t* sorted_flat, const void* wg, const void* wu,
                             const int32_t* tiles, const int32_t* num_tiles, void* g, void* u, void* a, hipStream_t s) {
-  hipError_t st = allow_lds<k_gate_up<C, GATHER>>(C::LDS);
+  constexpr int lds_bytes = lds_bytes_of<C>();
+  hipError_t st = allow_lds<k_gate_up<C, GATHER>>(lds_bytes);
   if (st != hipSuccess) return st;
   unsigned grid = grid8(max_tiles(d) * C::SUB * (d.F / (C::BN / 2)));
-  hipLaunchKernelGGL((k_gate_up<C, GATHER>), dim3(grid), dim3(C::NT), C::LDS, s, static_cast<const bf16_t*>(xs),
-                     sorted_flat, int(d.K), static_cast<const bf16_t*>(wg), static_cast<const bf16_t*>(wu), tiles,
-                     num_tiles, static_cast<bf16_t*>(g), static_cast<bf16_t*>(u), static_cast<bf16_t*>(a), int(d.H),
-                     int(d.F), group_rows(d, C::BM));
+  hipLaunchKernelGGL((k_gate_up<C, GATHER>), dim3(grid), dim3(C::NT), lds_bytes, s,
+                     static_cast<const bf16_t*>(xs), sorted_flat, int(d.K), static_cast<const bf16_t*>(wg),
+                     static_cast<const bf16_t*>(wu), tiles, num_tiles, static_cast<bf16_t*>(g),
+                     static_cast<bf16_t*>(u), static_cast<bf16_t*>(a), int(d.H), int(d.F), group_rows(d, C::BM));
   return hipGetLastError();
 }
 
@@ -700,10 +729,11 @@ hipError_t ffn_gate_up_big(const Dims& d, const void* xs, const int32_t* sorted_
 template <class C>
 static hipError_t down_t(const Dims& d, const void* a, const void* wd, const int32_t* tiles, const int32_t* num_tiles,
                          void* ys, hipStream_t s) {
-  hipError_t st = allow_lds<k_down<C>>(C::LDS);
+  constexpr int lds_bytes = lds_bytes_of<C>();
+  hipError_t st = allow_lds<k_down<C>>(lds_bytes);
   if (st != hipSuccess) return st;
   unsigned grid = grid8(max_tiles(d) * C::SUB * ((d.H + C::BN - 1) / C::BN));
-  hipLaunchKernelGGL(k_down<C>, dim3(grid), dim3(C::NT), C::LDS, s, static_cast<const bf16_t*>(a),
+  hipLaunchKernelGGL(k_down<C>, dim3(grid), dim3(C::NT), lds_bytes, s, static_cast<const bf16_t*>(a),
                      static_cast<const bf16_t*>(wd), tiles, num_tiles, static_cast<bf16_t*>(ys), int(d.H), int(d.F),
                      group_rows(d, C::BM));
   return hipGetLastError();
@@ -717,10 +747,10 @@ hipError_t ffn_down_big(const Dims& d, const void* a, const void* wd, const int3
 template <class C>
 static hipError_t dact_t(const Dims& d, const void* dys, const void* wd, const void* g, const void* u,
                          const int32_t* tiles, const int32_t* num_tiles, void* dg, void* du, hipStream_t s) {
-  hipError_t st = allow_lds<k_dact<C>>(C::LDS);
+  hipError_t st = allow_lds<k_dact<C>>(lds_bytes_of<C>());
   if (st != hipSuccess) return st;
   unsigned grid = grid8(max_tiles(d) * C::SUB * ((d.F + C::BN - 1) / C::BN));
-  hipLaunchKernelGGL(k_dact<C>, dim3(grid), dim3(C::NT), C::LDS, s, static_cast<const bf16_t*>(dys),
+  hipLaunchKernelGGL(k_dact<C>, dim3(grid), dim3(C::NT), lds_bytes_of<C>(), s, static_cast<const bf16_t*>(dys),
                      static_cast<const bf16_t*>(wd), static_cast<const bf16_t*>(g), static_cast<const bf16_t*>(u),
                      tiles, num_tiles, static_cast<bf16_t*>(dg), static_cast<bf16_t*>(du), int(d.H), int(d.F),
                      group_rows(d, C::BM));
@@ -740,10 +770,10 @@ hipError_t ffn_bwd_dact_mid(const Dims& d, const void* dys, const void* wd, cons
 template <class C>
 static hipError_t dx_t(const Dims& d, const void* dg, const void* du, const void* wg, const void* wu,
                        const int32_t* tiles, const int32_t* num_tiles, void* dxs, hipStream_t s) {
-  hipError_t st = allow_lds<k_dx<C>>(C::LDS);
+  hipError_t st = allow_lds<k_dx<C>>(lds_bytes_of<C>());
   if (st != hipSuccess) return st;
   unsigned grid = grid8(max_tiles(d) * C::SUB * ((d.H + C::BN - 1) / C::BN));
-  hipLaunchKernelGGL(k_dx<C>, dim3(grid), dim3(C::NT), C::LDS, s, static_cast<const bf16_t*>(dg),
+  hipLaunchKernelGGL(k_dx<C>, dim3(grid), dim3(C::NT), lds_bytes_of<C>(), s, static_cast<const bf16_t*>(dg),
                      static_cast<const bf16_t*>(du), static_cast<const bf16_t*>(wg), static_cast<const bf16_t*>(wu),
                      tiles, num_tiles, static_cast<bf16_t*>(dxs), int(d.H), int(d.F), group_rows(d, C::BM));
   return hipGetLastError();
@@ -772,10 +802,10 @@ static hipError_t dw_t(const Dims& d, const void* xs, const int32_t* sorted_flat
                        hipStream_t s) {
   auto run = [&](auto gather) -> hipError_t {
     constexpr bool G = decltype(gather)::value;
-    hipError_t st = allow_lds<k_dw<C, G>>(C::LDS);
+    hipError_t st = allow_lds<k_dw<C, G>>(lds_bytes_of<C>());
     if (st != hipSuccess) return st;
     const unsigned grid = dw_grid<C>(d);
-    hipLaunchKernelGGL((k_dw<C, G>), dim3(grid), dim3(C::NT), C::LDS, s, static_cast<const bf16_t*>(xs),
+    hipLaunchKernelGGL((k_dw<C, G>), dim3(grid), dim3(C::NT), lds_bytes_of<C>(), s, static_cast<const bf16_t*>(xs),
                        static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(dys),
                        static_cast<const bf16_t*>(dg), static_cast<const bf16_t*>(du), offsets, dwg, dwu, dwd,
                        int(d.H), int(d.F), int(d.E), sorted_flat, int(d.K));
@@ -796,7 +826,7 @@ hipError_t ffn_bwd_dx_dw_big(const Dims& d, const void* dg, const void* du, cons
                              float* dwg, float* dwu, float* dwd, hipStream_t s) {
   using CW = Big8;
   using CX = DxInMerged;
-  constexpr int lds_bytes = CW::LDS > CX::LDS ? CW::LDS : CX::LDS;
+  constexpr int lds_bytes = lds_bytes_of<CW>() > lds_bytes_of<CX>() ? lds_bytes_of<CW>() : lds_bytes_of<CX>();
   auto run = [&](auto gather) -> hipError_t {
     constexpr bool G = decltype(gather)::value;
     hipError_t st = allow_lds<k_dx_dw<CW, CX, G>>(lds_bytes);

@@ -583,6 +583,236 @@ __device__ __forceinline__ void k_loop_reg(char* lds, Acc<C>& acc, int nk, const
     k_steps_reg<C, A_MN, B_MN, false>(lds, acc, nk, oa, ob, va, vb, wm, wn, k_last);
 }
 
+// ---- LDS DMA through buffer resources, and the mixed-depth DMA K loop
+//
+// The 8-wave 256 x 256 tiles (down, dA, dX and the weight gradients) move
+// both operands by LDS DMA instead of through registers: operand A one K
+// tile ahead into two LDS slots, operand B two K tiles ahead into three, so
+// 96 KB per CU are in flight without a register holding any of it (the
+// register-staged loop holds one 64 KB K tile, and a second register set
+// does not fit beside 128 accumulators per lane).  Each request is a buffer
+// load with a 32-bit lane offset fixed for the whole loop (the resource base
+// moves per K tile): one instruction and an M0 write, against ten address
+// instructions per request of the global-address LDS DMA.  Against the
+// register-staged loop at N = 16384, H = 4096, F = 14336, E = 8: down 3.58 ->
+// 3.46 ms, dA 3.99 -> 3.79 ms, merged dX / weight gradients 17.05 -> 16.27 ms
+// (one box, interleaved runs).  The 4-wave gate/up tile (B as two 128-column
+// sub-tiles, one per weight tensor) was slower this way (7.04 -> 7.13 ms),
+// so it keeps the register-staged loop.
+// LDS: A slots at [0, 2 * A_BYTES), B slots at [2 * A_BYTES, + 3 * B_BYTES).
+
+// 16 bytes per lane from a buffer resource into LDS: the wave's lanes fill
+// lds_wave[0 .. 1024) in lane order.
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, int off, char* lds_wave) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)lds_wave, 16, off, 0, 0, 0);
+}
+
+// K-contiguous operand by DMA: ROWS rows x BK k of a row-major matrix
+// (leading dimension ld) starting at base; K tile kt starts at k = kt * BK.
+// Rows at or past rows_valid read row rows_valid - 1 (never stored).  Same
+// LDS layout as dma_kc.  Byte offsets within a K tile must fit 31 bits.
+template <int ROWS, int BK, int NW>
+struct KcDma {
+  static constexpr int CPR = BK / 8, RPI = 1024 / (2 * BK), J = ROWS / RPI / NW;
+  static_assert((ROWS / RPI) % NW == 0, "instructions split evenly over the waves");
+  const bf16_t *base0, *base1;  // K tiles from nk0 on come from base1 (two stacked contractions)
+  int nk0;
+  int off[J];
+  __device__ __forceinline__ KcDma(const bf16_t* b0, const bf16_t* b1, int nk0_, int64_t ld, int rows_valid)
+      : base0(b0), base1(b1), nk0(nk0_) {
+    const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int row = (w + j * NW) * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ fk<BK>(row);
+      const int rs = row < rows_valid ? row : rows_valid - 1;
+      off[j] = int((rs * ld + c * 8) * 2);
+    }
+  }
+  __device__ __forceinline__ KcDma(const bf16_t* b, int64_t ld, int rows_valid) : KcDma(b, b, 1 << 30, ld, rows_valid) {}
+  __device__ __forceinline__ void issue(int kt, char* slot) const {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bf16_t* p = kt < nk0 ? base0 + kt * BK : base1 + (kt - nk0) * BK;
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(p), (short)0, 0x7fffffff, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < J; ++j) dma16_buf(r, off[j], slot + (w + j * NW) * 1024);
+  }
+};
+
+// MN-contiguous operand by DMA: BK k rows x COLS columns of a row-major slab
+// (leading dimension ld) whose row 0, column 0 is tile; K tile kt covers k
+// rows [kt * BK, kt * BK + BK) of which those below k_total are valid: the
+// resource of a tile ends after its last valid row, so rows past it read
+// zeros (k_loop_dma2 also zeroes them in LDS).  Columns at or past
+// cols_valid read a clamped column (results discarded).  Same LDS layout as
+// dma_mn.  Needs BK * ld * 2 < 2^31.
+template <int COLS, int BK, int NW>
+struct MnDma {
+  static constexpr int CPR = COLS / 8, RPI = 1024 / (COLS * 2), J = BK / RPI / NW;
+  static_assert((BK / RPI) % NW == 0, "instructions split evenly over the waves");
+  const char* tile;
+  int64_t ld;
+  int k_total;
+  int off[J];
+  __device__ __forceinline__ MnDma(const bf16_t* tile_, int64_t ld_, int cols_valid, int k_total_ = 1 << 30)
+      : tile(reinterpret_cast<const char*>(tile_)), ld(ld_), k_total(k_total_) {
+    const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int k = (w + j * NW) * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ fm(k);
+      const int cs = c * 8 < cols_valid ? c : (cols_valid >> 3) - 1;
+      off[j] = int(k * ld_ * 2) + cs * 16;
+    }
+  }
+  __device__ __forceinline__ void issue(int kt, char* slot) const {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int kv = k_total - kt * BK;
+    const int rows = kv < BK ? kv : BK;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(tile + (int64_t)kt * BK * ld * 2), (short)0, int(rows * ld * 2), 0x00020000);
+#pragma unroll
+    for (int j = 0; j < J; ++j) dma16_buf(r, off[j], slot + (w + j * NW) * 1024);
+  }
+};
+
+template <class C>
+struct Dma2Layout {
+  static constexpr int A0 = 0, B0 = 2 * C::A_BYTES;
+  static constexpr int BYTES = 2 * C::A_BYTES + 3 * C::B_BYTES;
+  static constexpr int LDS = BYTES > C::LDS_A ? BYTES : C::LDS_A;
+};
+
+// Instruction order of one step of k_loop_dma2 (masks as in
+// reg_step_schedule): the first k step's fragment reads open the step; after
+// each MFMA slot come its share of the next k step's fragment reads and of
+// the step's VL DMA requests (spread over the first LK k steps).
+template <int KK, int MK, int FR, int VL, int LK, int J = 0>
+__device__ __forceinline__ void dma2_schedule() {
+  if constexpr (J == 0) __builtin_amdgcn_sched_group_barrier(0x100, FR, 0);
+  if constexpr (J < KK * MK) {
+    constexpr int kk = J / MK, i = J % MK;
+    constexpr int r = kk + 1 < KK ? (i + 1) * FR / MK - i * FR / MK : 0;
+    constexpr int g = kk < LK ? (J + 1) * VL / (LK * MK) - J * VL / (LK * MK) : 0;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
+    if constexpr (g > 0) __builtin_amdgcn_sched_group_barrier(0x020, g, 0);
+    dma2_schedule<KK, MK, FR, VL, LK, J + 1>();
+  }
+}
+
+// One step: the DMA of A tile ka into slot wa and of B tile kb into slot wb
+// (A first: the end-of-step wait for it then leaves the B request in
+// flight), then the MFMAs over slots ra / rb.  The four regions are distinct
+// (restrict), so the compiler does not wait for the DMA before the fragment
+// reads.
+template <class C, bool A_MN, bool B_MN, bool MMA, class DA, class DB>
+__device__ __forceinline__ void dma2_step(const char* __restrict__ ra, const char* __restrict__ rb,
+                                          char* __restrict__ wa, char* __restrict__ wb, int ka, int kb,
+                                          const DA& da, const DB& db, Acc<C>& acc, int wm, int wn) {
+  if constexpr (!MMA) {
+    da.issue(ka, wa);
+    db.issue(kb, wb);
+  } else {
+    constexpr int KK = C::BK / 16;
+    constexpr int FR = C::FM * (A_MN ? 2 : 1) + C::FN * (B_MN ? 2 : 1);
+    constexpr int MK = C::FM * C::FN;
+    constexpr int LOAD_STEPS = C::NW >= 8 ? 1 : (KK / 2 > 0 ? KK / 2 : 1);
+    bf16x8_t fa[2][C::FM], fb[2][C::FN];
+#pragma unroll
+    for (int mi = 0; mi < C::FM; ++mi)
+      fa[0][mi] = A_MN ? frag_mn<C::BM>(ra, wm * C::TM + mi * 32, 0) : frag_kc<C::BK>(ra, wm * C::TM + mi * 32, 0);
+#pragma unroll
+    for (int ni = 0; ni < C::FN; ++ni)
+      fb[0][ni] = B_MN ? frag_mn<C::BN>(rb, wn * C::TN + ni * 32, 0) : frag_kc<C::BK>(rb, wn * C::TN + ni * 32, 0);
+    da.issue(ka, wa);
+    db.issue(kb, wb);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int cb = kk & 1;
+      if (kk + 1 < KK) {
+#pragma unroll
+        for (int mi = 0; mi < C::FM; ++mi)
+          fa[cb ^ 1][mi] = A_MN ? frag_mn<C::BM>(ra, wm * C::TM + mi * 32, kk + 1)
+                                : frag_kc<C::BK>(ra, wm * C::TM + mi * 32, kk + 1);
+#pragma unroll
+        for (int ni = 0; ni < C::FN; ++ni)
+          fb[cb ^ 1][ni] = B_MN ? frag_mn<C::BN>(rb, wn * C::TN + ni * 32, kk + 1)
+                                : frag_kc<C::BK>(rb, wn * C::TN + ni * 32, kk + 1);
+      }
+#pragma unroll
+      for (int mi = 0; mi < C::FM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < C::FN; ++ni)
+          acc.a[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cb][mi], fb[cb][ni], acc.a[mi][ni], 0, 0, 0);
+    }
+    dma2_schedule<KK, MK, FR, DA::J + DB::J, LOAD_STEPS>();
+    // every MFMA of the step is issued before the end-of-step wait and
+    // barrier (otherwise the scheduler sinks the last k step's MFMAs past
+    // them and a wave waits at the barrier with its matrix work undone)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <class C, bool A_MN, bool B_MN, bool MMA, class DA, class DB>
+__device__ __forceinline__ void k_steps_dma2(char* lds, Acc<C>& acc, int nk, const DA& da, const DB& db, int wm,
+                                             int wn, int k_last) {
+  using L = Dma2Layout<C>;
+  int rs = 0;  // B slot of tile kt
+  for (int kt = 0; kt < nk; ++kt) {
+    const int ka = kt + 1 < nk ? kt + 1 : kt;
+    const int kb = kt + 2 < nk ? kt + 2 : nk - 1;
+    const int ws = rs == 0 ? 2 : rs - 1;  // (kt + 2) % 3
+    char* ra = lds + L::A0 + (kt & 1) * C::A_BYTES;
+    char* rb = lds + L::B0 + rs * C::B_BYTES;
+    if (A_MN && kt == nk - 1 && k_last < C::BK) {
+      // ragged contraction tail (both operands MN: k rows are LDS rows)
+      static_assert(!A_MN || B_MN, "ragged tails with MN operands only");
+      u32x4_t* za = reinterpret_cast<u32x4_t*>(ra + k_last * C::BM * 2);
+      u32x4_t* zb = reinterpret_cast<u32x4_t*>(rb + k_last * C::BN * 2);
+      for (int i = threadIdx.x; i < (C::BK - k_last) * C::BM * 2 / 16; i += C::NT) za[i] = u32x4_t{0u, 0u, 0u, 0u};
+      for (int i = threadIdx.x; i < (C::BK - k_last) * C::BN * 2 / 16; i += C::NT) zb[i] = u32x4_t{0u, 0u, 0u, 0u};
+      __syncthreads();
+    }
+    dma2_step<C, A_MN, B_MN, MMA>(ra, rb, lds + L::A0 + ((kt + 1) & 1) * C::A_BYTES,
+                                     lds + L::B0 + ws * C::B_BYTES, ka, kb, da, db, acc, wm, wn);
+    wait_vm<C::JB>();
+    lds_barrier();
+    rs = rs == 2 ? 0 : rs + 1;
+  }
+}
+
+// Mixed-depth DMA K loop (see above).  Every step issues both requests (the
+// last steps re-fetch the last tiles into slots nobody reads), so each wait
+// is the same on every path: at the end of step kt only B tile kt + 2 may
+// still be in flight.  mma = false (wave-uniform): the wave's rows are all
+// past the tile's valid rows; it issues its requests and waits, no MFMAs.
+// Each operand is K-contiguous (KcDma) or MN-contiguous (MnDma); with both
+// MN-contiguous (the weight gradients) the last K tile may hold only k_last
+// valid k rows.
+template <class C, bool A_MN, bool B_MN, class DA, class DB>
+__device__ __forceinline__ void k_loop_dma2(char* lds, Acc<C>& acc, int nk, const DA& da, const DB& db, int wm,
+                                            int wn, bool mma = true, int k_last = C::BK) {
+  using L = Dma2Layout<C>;
+  static_assert(DA::J == C::JA && DB::J == C::JB, "one request per wave instruction");
+  zero_acc(acc);
+  if (nk <= 0) return;
+  da.issue(0, lds + L::A0);
+  db.issue(0, lds + L::B0);
+  db.issue(nk > 1 ? 1 : 0, lds + L::B0 + C::B_BYTES);
+  wait_vm<C::JB>();
+  lds_barrier();
+  if (__builtin_amdgcn_readfirstlane(mma ? 1 : 0))
+    k_steps_dma2<C, A_MN, B_MN, true>(lds, acc, nk, da, db, wm, wn, k_last);
+  else
+    k_steps_dma2<C, A_MN, B_MN, false>(lds, acc, nk, da, db, wm, wn, k_last);
+  // the last steps' requests land in slots nobody reads, but before the
+  // caller reuses the LDS
+  wait_vm<0>();
+  __syncthreads();
+}
+
 // Accumulator element r of fragment (mi, ni): MFMA 32x32 result layout
 // (column = lane % 32, rows in groups of 4 interleaved across the two lane
 // halves).  Offsets within the wave tile are compile-time constants added to
