@@ -42,22 +42,22 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # hash is stored with them; once any source under csrc/ changes, the figure
 # is reported as null until the counters are taken again.
 TRAFFIC = {
-    "sources": "b07e64cefd31f1fe",
+    "sources": "d6f36180db8d25c4",
     "bytes": {
-        ('bf16_fwd_n8192_h7168_f2048_e256_k8', 'down'): 12748825164,
-        ('bf16_fwd_n8192_h7168_f2048_e256_k8', 'gate_up'): 22298986034,
-        ('bf16_n16384_h4096_f14336_e8_k2', 'dact'): 11135979091,
-        ('bf16_n16384_h4096_f14336_e8_k2', 'down'): 8103742078,
-        ('bf16_n16384_h4096_f14336_e8_k2', 'dx_dw'): 45052244679,
-        ('bf16_n16384_h4096_f14336_e8_k2', 'gate_up'): 18800396819,
-        ('bf16_n16384_h512_f1024_e8_k2', 'dact'): 352225512,
-        ('bf16_n16384_h512_f1024_e8_k2', 'down'): 148145510,
-        ('bf16_n16384_h512_f1024_e8_k2', 'dx_dw'): 655010892,
-        ('bf16_n16384_h512_f1024_e8_k2', 'gate_up'): 338357273,
-        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'dact'): 3162016323,
-        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'down'): 1932473581,
-        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'dx_dw'): 9106589249,
-        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'gate_up'): 3905724080,
+        ('bf16_fwd_n8192_h7168_f2048_e256_k8', 'down'): 12797528192,
+        ('bf16_fwd_n8192_h7168_f2048_e256_k8', 'gate_up'): 22298201259,
+        ('bf16_n16384_h4096_f14336_e8_k2', 'dact'): 10812025941,
+        ('bf16_n16384_h4096_f14336_e8_k2', 'down'): 7883738368,
+        ('bf16_n16384_h4096_f14336_e8_k2', 'dx_dw'): 42735942571,
+        ('bf16_n16384_h4096_f14336_e8_k2', 'gate_up'): 18964363051,
+        ('bf16_n16384_h512_f1024_e8_k2', 'dact'): 352149035,
+        ('bf16_n16384_h512_f1024_e8_k2', 'down'): 148027221,
+        ('bf16_n16384_h512_f1024_e8_k2', 'dx_dw'): 665556629,
+        ('bf16_n16384_h512_f1024_e8_k2', 'gate_up'): 338058517,
+        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'dact'): 3139263701,
+        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'down'): 1895586837,
+        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'dx_dw'): 9136803008,
+        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'gate_up'): 3944301696,
     },
 }
 
