@@ -14,17 +14,17 @@
 // from L2 for 8.4 MFLOP.  Used for the long contractions;
 // gemm_bf16_small.hip holds the 128 x 128 shape for short ones.
 //
-// Main configuration (Big): 4 waves in a 2 x 2 arrangement, 128 x 128 per
-// wave (256 accumulator registers each, one workgroup per CU).  Each thread
-// requests its 16-byte chunks of the next K tile into registers, one request
-// per two MFMAs over the first half of the step, and stores them into the
-// other LDS stage between the last k step's MFMAs; one barrier per step.
-// Spreading the requests keeps each wave's in-order issue from parking its
-// MFMAs behind a burst of loads, which is what held the LDS DMA version of
-// this loop near 0.8 PFLOP/s.  The 8-wave tile of the same shape (Big8)
-// runs dX, the weight gradients, down and the SwiGLU backward on the
-// mixed-depth LDS DMA loop (k_loop_dma2: operand A one K tile ahead, B two,
-// both through buffer-resource DMA, so nothing in flight occupies registers).
+// Main configuration (Big8): 8 waves in a 4 x 2 arrangement, 64 x 128 per
+// wave (128 accumulator registers each, two waves per SIMD, one workgroup
+// per CU), on the mixed-depth LDS DMA loop of mma_lds.h (k_loop_dma2):
+// operand A one K tile ahead in two LDS slots, operand B two K tiles ahead in
+// three, both moved by buffer-resource LDS DMA, so 96 KB per CU are in flight
+// and none of it occupies registers.  Every GEMM stage on this tile runs it
+// (gate/up with its W_gate and W_up columns as two B sub-tiles, one per wave
+// column).  The register-staged loop (k_loop_reg: each thread's 16-byte
+// chunks of the next K tile requested into registers between the MFMAs and
+// stored into the other LDS stage) remains for the 128-row tiles and for the
+// weight gradients whose rows are gathered from x.
 //
 // A K-contiguous operand (token rows; weight rows in the backward) sits in
 // LDS as [rows][64 k] and is read with 16-byte fragment loads; an
@@ -54,17 +54,16 @@ using namespace moe;
 
 using namespace moe_mma;
 
-using Big = TileCfg<256, 256, 2, 2, 1, 64, 2, true>;  // 4 waves, 128 x 128 per wave, register-staged
-// The same tile with 8 waves of 64 x 128 (two per SIMD, each covering the
-// other's issue stalls): used for dX, the weight gradients, down and dA, where
-// it measured faster (merged dX/dW 866-870 -> 891-896 TFLOP/s at H = 512,
-// F = 1024, E = 8; 846-851 -> 881 at the skewed H = 2048, E = 64 workload;
-// dA 4.84 -> 4.68 ms at H = 4096, F = 14336 against the 8-wave LDS DMA tile);
-// gate/up keeps 4 waves (1.29 -> 1.31 ms, 5.49 -> 5.61 ms and, at H = 4096,
-// F = 14336, 7.31 -> 7.40 ms with 8; equal within 0.3 % once the 8-wave loop
-// issued its loads in the first k step: 7.22 vs 7.20 ms).  Those figures
-// are for the register-staged loop; the Big8 kernels now run k_loop_dma2
-// (mma_lds.h), whose 160 KiB of LDS slots the launches request.
+// 256 x 256 tiles with 8 waves of 64 x 128 (two per SIMD, each covering the
+// other's issue stalls).  On the register-staged loop 8 waves measured faster
+// than 4 waves of 128 x 128 for dX, the weight gradients, down and dA (merged
+// dX/dW 866-870 -> 891-896 TFLOP/s at H = 512, F = 1024, E = 8; 846-851 ->
+// 881 at the skewed H = 2048, E = 64 workload) and equal for gate/up (7.22 vs
+// 7.20 ms at H = 4096, F = 14336).  On k_loop_dma2, which the Big8 kernels
+// run (160 KiB of LDS slots, requested by the launches), gate/up gained
+// further against its 4-wave register-staged tile: 7.11-7.13 -> 6.92-6.95 ms
+// there, 5.12-5.18 -> 4.71 ms at H = 7168, E = 256 and 1.27-1.28 -> 1.19-1.20
+// ms at the skewed workload (interleaved runs, one box).
 using Big8 = TileCfg<256, 256, 4, 2, 1, 64, 2, true>;
 // 128 x 256 tiles through the same DMA pipeline, 32 k per stage, three stages
 // (72 KiB of LDS, two workgroups per CU): used by the SwiGLU backward on
@@ -90,7 +89,7 @@ using SmallR64 = TileCfg<128, 128, 2, 2, 2, 64, 2, true>;
 // slower on every workload (221 -> 238 us there with 64 k per stage, 260 with
 // 32): the smaller tile's operand traffic per flop outweighs the balance.
 using DxInMerged = Big8;
-static_assert(MOE_TILE_M % Big::BM == 0 && MOE_TILE_M % Big8::BM == 0 && MOE_TILE_M % Mid::BM == 0 &&
+static_assert(MOE_TILE_M % Big8::BM == 0 && MOE_TILE_M % Mid::BM == 0 &&
                   MOE_TILE_M % MidR::BM == 0 && MOE_TILE_M % SmallR32::BM == 0 && MOE_TILE_M % SmallR64::BM == 0,
               "list tiles split into row tiles");
 
@@ -254,7 +253,17 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_gate_up(const bf16_t* __rest
   const bf16_t* b_u = wu + eoff - HALF;
 
   Acc<C> acc;
-  if constexpr (GATHER) {
+  if constexpr (C::REG && C::NW >= 8) {
+    // mixed-depth DMA loop; W_gate and W_up as two B sub-tiles, one per wave column
+    const MnDma2<C::BN, C::BK, C::NW> wdma(b_g, b_u + HALF, F);
+    if constexpr (GATHER)
+      k_loop_dma2<C, false, true, KcGatherDma<C::BM, C::BK, C::NW>, MnDma2<C::BN, C::BK, C::NW>, true>(
+          lds, acc, H / C::BK, KcGatherDma<C::BM, C::BK, C::NW>(xs, sorted_flat + ti.row0, K, H, ti.rows), wdma, wm,
+          wn, wm * C::TM < ti.rows);
+    else
+      k_loop_dma2<C, false, true, KcDma<C::BM, C::BK, C::NW>, MnDma2<C::BN, C::BK, C::NW>, true>(
+          lds, acc, H / C::BK, KcDma<C::BM, C::BK, C::NW>(a_base, H, ti.rows), wdma, wm, wn, wm * C::TM < ti.rows);
+  } else if constexpr (GATHER) {
     static_assert(C::REG, "the gathered A tile uses the register-staged loop");
     k_loop_reg<C, false, true>(lds, acc, H / C::BK,
                                KcGather<C::BM, C::BK, C::NT>(xs, sorted_flat + ti.row0, K, H, ti.rows),
@@ -722,8 +731,8 @@ static hipError_t gate_up_t(const Dims& d, const void* xs, const int32_t* sorted
 // sorted_flat non-null: xs is x and the rows are gathered on load
 hipError_t ffn_gate_up_big(const Dims& d, const void* xs, const int32_t* sorted_flat, const void* wg, const void* wu,
                            const int32_t* tiles, const int32_t* num_tiles, void* g, void* u, void* a, hipStream_t s) {
-  return sorted_flat ? gate_up_t<Big, true>(d, xs, sorted_flat, wg, wu, tiles, num_tiles, g, u, a, s)
-                     : gate_up_t<Big>(d, xs, nullptr, wg, wu, tiles, num_tiles, g, u, a, s);
+  return sorted_flat ? gate_up_t<Big8, true>(d, xs, sorted_flat, wg, wu, tiles, num_tiles, g, u, a, s)
+                     : gate_up_t<Big8>(d, xs, nullptr, wg, wu, tiles, num_tiles, g, u, a, s);
 }
 
 template <class C>

@@ -184,8 +184,8 @@ hipError_t ffn_bwd_dx_dw_big(const Dims&, const void*, const void*, const void*,
                              const int32_t*, float*, float*, float*, hipStream_t);
 
 // Which bf16 tile shape each stage uses.  The 256 x 256 tiles (one workgroup
-// per CU: 4 waves of 128 x 128 with register-staged loads, or, for dA, 8
-// waves of 64 x 128 through the LDS DMA) win on long contractions; the
+// per CU: 8 waves of 64 x 128 on the mixed-depth LDS DMA loop) win on long
+// contractions; the
 // 128 x 128 tiles (2-3 workgroups per CU) hide latency better on short ones,
 // where a 256 x 256 tile spends a large share of its time in its prologue and
 // epilogue.  Measured on MI355X per stage over the shapes (H, F, rows per
@@ -195,8 +195,7 @@ hipError_t ffn_bwd_dx_dw_big(const Dims&, const void*, const void*, const void*,
 //   the register-staged loop (SmallR);
 //   down (contraction F): 256 x 256 from F = 1280 on, else 128 x 128 on the
 //   register-staged loop (SmallR);
-//   dA (contraction H): 256 x 256 (8 waves, register-staged) from H = 4096
-//   on, below that 128 x 256 tiles through the LDS DMA pipeline (two
+//   dA (contraction H): 256 x 256 from H = 4096 on, below that 128 x 256 tiles through the LDS DMA pipeline (two
 //   workgroups per CU overlap one's SwiGLU epilogue with the other's loop);
 //   dX (contraction 2F): 256 x 256 from 2F = 2560 on;
 //   dW (contraction over an expert's rows): 256 x 256 throughout.

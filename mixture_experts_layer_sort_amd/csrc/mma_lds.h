@@ -585,7 +585,7 @@ __device__ __forceinline__ void k_loop_reg(char* lds, Acc<C>& acc, int nk, const
 
 // ---- LDS DMA through buffer resources, and the mixed-depth DMA K loop
 //
-// The 8-wave 256 x 256 tiles (down, dA, dX and the weight gradients) move
+// The 8-wave 256 x 256 tiles (gate/up, down, dA, dX and the weight gradients) move
 // both operands by LDS DMA instead of through registers: operand A one K
 // tile ahead into two LDS slots, operand B two K tiles ahead into three, so
 // 96 KB per CU are in flight without a register holding any of it (the
@@ -596,9 +596,9 @@ __device__ __forceinline__ void k_loop_reg(char* lds, Acc<C>& acc, int nk, const
 // instructions per request of the global-address LDS DMA.  Against the
 // register-staged loop at N = 16384, H = 4096, F = 14336, E = 8: down 3.58 ->
 // 3.46 ms, dA 3.99 -> 3.79 ms, merged dX / weight gradients 17.05 -> 16.27 ms
-// (one box, interleaved runs).  The 4-wave gate/up tile (B as two 128-column
-// sub-tiles, one per weight tensor) was slower this way (7.04 -> 7.13 ms),
-// so it keeps the register-staged loop.
+// (one box, interleaved runs).  gate/up runs it too, on 8 waves with B as two
+// 128-column sub-tiles (one per weight tensor); with 4 waves (one per SIMD)
+// the loop was slower than the register-staged one (7.04 -> 7.13 ms).
 // LDS: A slots at [0, 2 * A_BYTES), B slots at [2 * A_BYTES, + 3 * B_BYTES).
 
 // 16 bytes per lane from a buffer resource into LDS: the wave's lanes fill
@@ -640,6 +640,35 @@ struct KcDma {
   }
 };
 
+// K-contiguous operand by DMA with gathered rows: tile row r is row
+// rows_src[r] / K of x (leading dimension ld), as KcGather.  Byte offsets are
+// 32-bit unsigned (callers keep x under 4 GiB).
+template <int ROWS, int BK, int NW>
+struct KcGatherDma {
+  static constexpr int CPR = BK / 8, RPI = 1024 / (2 * BK), J = ROWS / RPI / NW;
+  static_assert((ROWS / RPI) % NW == 0, "instructions split evenly over the waves");
+  const bf16_t* base;
+  unsigned off[J];
+  __device__ __forceinline__ KcGatherDma(const bf16_t* x, const int32_t* rows_src, int K, int64_t ld, int rows_valid)
+      : base(x) {
+    const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int row = (w + j * NW) * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ fk<BK>(row);
+      const int tok = rows_src[row < rows_valid ? row : rows_valid - 1] / K;
+      off[j] = unsigned(tok * ld + c * 8) * 2u;
+    }
+  }
+  __device__ __forceinline__ void issue(int kt, char* slot) const {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(base + kt * BK), (short)0, -1, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < J; ++j) dma16_buf(r, int(off[j]), slot + (w + j * NW) * 1024);
+  }
+};
+
 // MN-contiguous operand by DMA: BK k rows x COLS columns of a row-major slab
 // (leading dimension ld) whose row 0, column 0 is tile; K tile kt covers k
 // rows [kt * BK, kt * BK + BK) of which those below k_total are valid: the
@@ -677,6 +706,25 @@ struct MnDma {
   }
 };
 
+// Two MN-contiguous sources side by side (the W_gate and W_up halves of a
+// gate/up tile): B as two sub-tiles of COLS / 2 columns, [half][BK k][COLS /
+// 2], each moved by its own MnDma, so every DMA instruction reads one tensor.
+// A wave whose tile columns lie in one half reads that sub-tile as an MN tile
+// of COLS / 2 columns (k_loop_dma2 with B_HALVES).
+template <int COLS, int BK, int NW>
+struct MnDma2 {
+  using Half = MnDma<COLS / 2, BK, NW>;
+  static constexpr int J = 2 * Half::J;
+  static constexpr int HALF_BYTES = BK * COLS;  // bytes of one sub-tile
+  Half g, u;
+  __device__ __forceinline__ MnDma2(const bf16_t* t0, const bf16_t* t1, int64_t ld)
+      : g(t0, ld, COLS / 2), u(t1, ld, COLS / 2) {}
+  __device__ __forceinline__ void issue(int kt, char* slot) const {
+    g.issue(kt, slot);
+    u.issue(kt, slot + HALF_BYTES);
+  }
+};
+
 template <class C>
 struct Dma2Layout {
   static constexpr int A0 = 0, B0 = 2 * C::A_BYTES;
@@ -707,7 +755,7 @@ __device__ __forceinline__ void dma2_schedule() {
 // flight), then the MFMAs over slots ra / rb.  The four regions are distinct
 // (restrict), so the compiler does not wait for the DMA before the fragment
 // reads.
-template <class C, bool A_MN, bool B_MN, bool MMA, class DA, class DB>
+template <class C, bool A_MN, bool B_MN, bool MMA, bool B_HALVES, class DA, class DB>
 __device__ __forceinline__ void dma2_step(const char* __restrict__ ra, const char* __restrict__ rb,
                                           char* __restrict__ wa, char* __restrict__ wb, int ka, int kb,
                                           const DA& da, const DB& db, Acc<C>& acc, int wm, int wn) {
@@ -719,13 +767,18 @@ __device__ __forceinline__ void dma2_step(const char* __restrict__ ra, const cha
     constexpr int FR = C::FM * (A_MN ? 2 : 1) + C::FN * (B_MN ? 2 : 1);
     constexpr int MK = C::FM * C::FN;
     constexpr int LOAD_STEPS = C::NW >= 8 ? 1 : (KK / 2 > 0 ? KK / 2 : 1);
+    static_assert(!B_HALVES || (B_MN && C::WN == 2 && C::TN * 2 == C::BN), "one B half per wave column");
+    // the wave's B columns: its own half (B_HALVES, a TN-column MN tile) or the whole B tile
+    constexpr int BC = B_HALVES ? C::TN : C::BN;
+    const char* sb = B_HALVES ? rb + wn * (C::BK * C::TN * 2) : rb;
+    const int nb = B_HALVES ? 0 : wn * C::TN;
     bf16x8_t fa[2][C::FM], fb[2][C::FN];
 #pragma unroll
     for (int mi = 0; mi < C::FM; ++mi)
       fa[0][mi] = A_MN ? frag_mn<C::BM>(ra, wm * C::TM + mi * 32, 0) : frag_kc<C::BK>(ra, wm * C::TM + mi * 32, 0);
 #pragma unroll
     for (int ni = 0; ni < C::FN; ++ni)
-      fb[0][ni] = B_MN ? frag_mn<C::BN>(rb, wn * C::TN + ni * 32, 0) : frag_kc<C::BK>(rb, wn * C::TN + ni * 32, 0);
+      fb[0][ni] = B_MN ? frag_mn<BC>(sb, nb + ni * 32, 0) : frag_kc<C::BK>(sb, nb + ni * 32, 0);
     da.issue(ka, wa);
     db.issue(kb, wb);
 #pragma unroll
@@ -738,8 +791,7 @@ __device__ __forceinline__ void dma2_step(const char* __restrict__ ra, const cha
                                 : frag_kc<C::BK>(ra, wm * C::TM + mi * 32, kk + 1);
 #pragma unroll
         for (int ni = 0; ni < C::FN; ++ni)
-          fb[cb ^ 1][ni] = B_MN ? frag_mn<C::BN>(rb, wn * C::TN + ni * 32, kk + 1)
-                                : frag_kc<C::BK>(rb, wn * C::TN + ni * 32, kk + 1);
+          fb[cb ^ 1][ni] = B_MN ? frag_mn<BC>(sb, nb + ni * 32, kk + 1) : frag_kc<C::BK>(sb, nb + ni * 32, kk + 1);
       }
 #pragma unroll
       for (int mi = 0; mi < C::FM; ++mi)
@@ -755,7 +807,7 @@ __device__ __forceinline__ void dma2_step(const char* __restrict__ ra, const cha
   }
 }
 
-template <class C, bool A_MN, bool B_MN, bool MMA, class DA, class DB>
+template <class C, bool A_MN, bool B_MN, bool MMA, bool B_HALVES, class DA, class DB>
 __device__ __forceinline__ void k_steps_dma2(char* lds, Acc<C>& acc, int nk, const DA& da, const DB& db, int wm,
                                              int wn, int k_last) {
   using L = Dma2Layout<C>;
@@ -775,7 +827,7 @@ __device__ __forceinline__ void k_steps_dma2(char* lds, Acc<C>& acc, int nk, con
       for (int i = threadIdx.x; i < (C::BK - k_last) * C::BN * 2 / 16; i += C::NT) zb[i] = u32x4_t{0u, 0u, 0u, 0u};
       __syncthreads();
     }
-    dma2_step<C, A_MN, B_MN, MMA>(ra, rb, lds + L::A0 + ((kt + 1) & 1) * C::A_BYTES,
+    dma2_step<C, A_MN, B_MN, MMA, B_HALVES>(ra, rb, lds + L::A0 + ((kt + 1) & 1) * C::A_BYTES,
                                      lds + L::B0 + ws * C::B_BYTES, ka, kb, da, db, acc, wm, wn);
     wait_vm<C::JB>();
     lds_barrier();
@@ -790,8 +842,8 @@ __device__ __forceinline__ void k_steps_dma2(char* lds, Acc<C>& acc, int nk, con
 // past the tile's valid rows; it issues its requests and waits, no MFMAs.
 // Each operand is K-contiguous (KcDma) or MN-contiguous (MnDma); with both
 // MN-contiguous (the weight gradients) the last K tile may hold only k_last
-// valid k rows.
-template <class C, bool A_MN, bool B_MN, class DA, class DB>
+// valid k rows.  B_HALVES: B is two MN sub-tiles (MnDma2), one per wave column.
+template <class C, bool A_MN, bool B_MN, class DA, class DB, bool B_HALVES = false>
 __device__ __forceinline__ void k_loop_dma2(char* lds, Acc<C>& acc, int nk, const DA& da, const DB& db, int wm,
                                             int wn, bool mma = true, int k_last = C::BK) {
   using L = Dma2Layout<C>;
@@ -804,9 +856,9 @@ __device__ __forceinline__ void k_loop_dma2(char* lds, Acc<C>& acc, int nk, cons
   wait_vm<C::JB>();
   lds_barrier();
   if (__builtin_amdgcn_readfirstlane(mma ? 1 : 0))
-    k_steps_dma2<C, A_MN, B_MN, true>(lds, acc, nk, da, db, wm, wn, k_last);
+    k_steps_dma2<C, A_MN, B_MN, true, B_HALVES>(lds, acc, nk, da, db, wm, wn, k_last);
   else
-    k_steps_dma2<C, A_MN, B_MN, false>(lds, acc, nk, da, db, wm, wn, k_last);
+    k_steps_dma2<C, A_MN, B_MN, false, B_HALVES>(lds, acc, nk, da, db, wm, wn, k_last);
   // the last steps' requests land in slots nobody reads, but before the
   // caller reuses the LDS
   wait_vm<0>();
