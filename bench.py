@@ -42,22 +42,22 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # hash is stored with them; once any source under csrc/ changes, the figure
 # is reported as null until the counters are taken again.
 TRAFFIC = {
-    "sources": "e526fd488f61936e",
+    "sources": "796c79e94c338240",
     "bytes": {
-        ('bf16_fwd_n8192_h7168_f2048_e256_k8', 'down'): 12806192597,
-        ('bf16_fwd_n8192_h7168_f2048_e256_k8', 'gate_up'): 22516328469,
-        ('bf16_n16384_h4096_f14336_e8_k2', 'dact'): 10724456043,
-        ('bf16_n16384_h4096_f14336_e8_k2', 'down'): 7874631765,
-        ('bf16_n16384_h4096_f14336_e8_k2', 'dx_dw'): 43246696021,
-        ('bf16_n16384_h4096_f14336_e8_k2', 'gate_up'): 16891399253,
-        ('bf16_n16384_h512_f1024_e8_k2', 'dact'): 352650539,
-        ('bf16_n16384_h512_f1024_e8_k2', 'down'): 147899691,
-        ('bf16_n16384_h512_f1024_e8_k2', 'dx_dw'): 666970837,
-        ('bf16_n16384_h512_f1024_e8_k2', 'gate_up'): 338229291,
-        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'dact'): 3192955968,
-        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'down'): 1917794155,
-        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'dx_dw'): 9128497941,
-        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'gate_up'): 3804037141,
+        ('bf16_fwd_n8192_h7168_f2048_e256_k8', 'down'): 12798532352,
+        ('bf16_fwd_n8192_h7168_f2048_e256_k8', 'gate_up'): 22412608875,
+        ('bf16_n16384_h4096_f14336_e8_k2', 'dact'): 10669213845,
+        ('bf16_n16384_h4096_f14336_e8_k2', 'down'): 7973930219,
+        ('bf16_n16384_h4096_f14336_e8_k2', 'dx_dw'): 43713290709,
+        ('bf16_n16384_h4096_f14336_e8_k2', 'gate_up'): 17328258304,
+        ('bf16_n16384_h512_f1024_e8_k2', 'dact'): 352507051,
+        ('bf16_n16384_h512_f1024_e8_k2', 'down'): 148070208,
+        ('bf16_n16384_h512_f1024_e8_k2', 'dx_dw'): 665424448,
+        ('bf16_n16384_h512_f1024_e8_k2', 'gate_up'): 338989312,
+        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'dact'): 2834678187,
+        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'down'): 1911226091,
+        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'dx_dw'): 9183885568,
+        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'gate_up'): 3793338325,
     },
 }
 

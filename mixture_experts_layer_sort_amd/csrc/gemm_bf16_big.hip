@@ -257,11 +257,11 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_gate_up(const bf16_t* __rest
     // mixed-depth DMA loop; W_gate and W_up as two B sub-tiles, one per wave column
     const MnDma2<C::BN, C::BK, C::NW> wdma(b_g, b_u + HALF, F);
     if constexpr (GATHER)
-      k_loop_dma2<C, false, true, KcGatherDma<C::BM, C::BK, C::NW>, MnDma2<C::BN, C::BK, C::NW>, true>(
+      k_loop_dma2<C, false, true, KcGatherDma<C::BM, C::BK, C::NW>, MnDma2<C::BN, C::BK, C::NW>, true, true>(
           lds, acc, H / C::BK, KcGatherDma<C::BM, C::BK, C::NW>(xs, sorted_flat + ti.row0, K, H, ti.rows), wdma, wm,
           wn, wm * C::TM < ti.rows);
     else
-      k_loop_dma2<C, false, true, KcDma<C::BM, C::BK, C::NW>, MnDma2<C::BN, C::BK, C::NW>, true>(
+      k_loop_dma2<C, false, true, KcDma<C::BM, C::BK, C::NW>, MnDma2<C::BN, C::BK, C::NW>, true, true>(
           lds, acc, H / C::BK, KcDma<C::BM, C::BK, C::NW>(a_base, H, ti.rows), wdma, wm, wn, wm * C::TM < ti.rows);
   } else if constexpr (GATHER) {
     static_assert(C::REG, "the gathered A tile uses the register-staged loop");
@@ -332,8 +332,9 @@ __global__ __launch_bounds__(C::NT, C::MINB) void k_down(const bf16_t* __restric
   const bf16_t* b_base = wd + (int64_t)ti.e * F * H + nt * C::BN;
   Acc<C> acc;
   if constexpr (C::REG && C::NW >= 8) {
-    k_loop_dma2<C, false, true>(lds, acc, F / C::BK, KcDma<C::BM, C::BK, C::NW>(a_base, F, ti.rows),
-                         MnDma<C::BN, C::BK, C::NW>(b_base, H, ncols), wm, wn, wm * C::TM < ti.rows);
+    k_loop_dma2<C, false, true, KcDma<C::BM, C::BK, C::NW>, MnDma<C::BN, C::BK, C::NW>, false, true>(
+        lds, acc, F / C::BK, KcDma<C::BM, C::BK, C::NW>(a_base, F, ti.rows), MnDma<C::BN, C::BK, C::NW>(b_base, H, ncols),
+        wm, wn, wm * C::TM < ti.rows);
   } else if constexpr (C::REG) {
     k_loop_reg<C, false, true>(lds, acc, F / C::BK, KcOp<C::BM, C::BK, C::NT>(a_base, a_base, kNoSplit, F, ti.rows),
                                MnBuf<C::BN, C::BK, C::NT>(b_base, H, ncols, F), wm, wn, C::BK,

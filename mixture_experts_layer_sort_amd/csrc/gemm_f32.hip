@@ -195,8 +195,11 @@ hipError_t ffn_bwd_dx_dw_big(const Dims&, const void*, const void*, const void*,
 //   the register-staged loop (SmallR);
 //   down (contraction F): 256 x 256 from F = 1280 on, else 128 x 128 on the
 //   register-staged loop (SmallR);
-//   dA (contraction H): 256 x 256 from H = 4096 on, below that 128 x 256 tiles through the LDS DMA pipeline (two
-//   workgroups per CU overlap one's SwiGLU epilogue with the other's loop);
+//   dA (contraction H): 256 x 256 from H = 2048 on (at H = 2048, F = 1408,
+//   E = 64: 0.866-0.869 -> 0.819-0.821 ms on the mixed-depth DMA loop),
+//   below that 128 x 256 tiles through the LDS DMA pipeline (two workgroups
+//   per CU overlap one's SwiGLU epilogue with the other's loop; at H = 512
+//   the 256 x 256 tile takes 0.122 against 0.101 ms);
 //   dX (contraction 2F): 256 x 256 from 2F = 2560 on;
 //   dW (contraction over an expert's rows): 256 x 256 throughout.
 // A forced family in Dims::tiles (moe_dims.gemm_tiles: 256, 128 x 256 or
@@ -214,7 +217,7 @@ static Tiles pick(const Dims& d, Tiles measured) {
 }
 static Tiles tiles_gate_up(const Dims& d) { return pick(d, d.H >= 2048 ? Tiles::Big : Tiles::SmallR); }
 static Tiles tiles_down(const Dims& d) { return pick(d, d.F >= 1280 ? Tiles::Big : Tiles::SmallR); }
-static Tiles tiles_dact(const Dims& d) { return pick(d, d.H >= 4096 ? Tiles::Big : Tiles::Small); }
+static Tiles tiles_dact(const Dims& d) { return pick(d, d.H >= 2048 ? Tiles::Big : Tiles::Small); }
 static Tiles tiles_dx(const Dims& d) { return pick(d, 2 * d.F >= 2560 ? Tiles::Big : Tiles::Small); }
 static Tiles tiles_dw(const Dims& d) { return pick(d, Tiles::Big); }
 

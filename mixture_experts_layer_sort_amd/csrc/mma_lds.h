@@ -736,8 +736,18 @@ struct Dma2Layout {
 // reg_step_schedule): the first k step's fragment reads open the step; after
 // each MFMA slot come its share of the next k step's fragment reads and of
 // the step's VL DMA requests (spread over the first LK k steps).
-template <int KK, int MK, int FR, int VL, int LK, int J = 0>
+// EARLY: all VL requests open the step, before the first fragment reads (the
+// forward GEMMs: at N = 16384, H = 4096, F = 14336, E = 8 gate/up 6.92-6.93
+// -> 6.80-6.86 ms and down 3.51-3.55 -> 3.41-3.42 ms; dA and the merged dX /
+// weight-gradient launch were 1-2 % slower that way, so they keep the
+// requests spread over the first k step).
+template <int KK, int MK, int FR, int VL, int LK, bool EARLY = false, int J = 0>
 __device__ __forceinline__ void dma2_schedule() {
+  if constexpr (EARLY && J == 0 && VL > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x020, VL, 0);
+    dma2_schedule<KK, MK, FR, 0, LK>();
+    return;
+  }
   if constexpr (J == 0) __builtin_amdgcn_sched_group_barrier(0x100, FR, 0);
   if constexpr (J < KK * MK) {
     constexpr int kk = J / MK, i = J % MK;
@@ -746,7 +756,7 @@ __device__ __forceinline__ void dma2_schedule() {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
     if constexpr (g > 0) __builtin_amdgcn_sched_group_barrier(0x020, g, 0);
-    dma2_schedule<KK, MK, FR, VL, LK, J + 1>();
+    dma2_schedule<KK, MK, FR, VL, LK, false, J + 1>();
   }
 }
 
@@ -755,7 +765,7 @@ __device__ __forceinline__ void dma2_schedule() {
 // flight), then the MFMAs over slots ra / rb.  The four regions are distinct
 // (restrict), so the compiler does not wait for the DMA before the fragment
 // reads.
-template <class C, bool A_MN, bool B_MN, bool MMA, bool B_HALVES, class DA, class DB>
+template <class C, bool A_MN, bool B_MN, bool MMA, bool B_HALVES, bool EARLY, class DA, class DB>
 __device__ __forceinline__ void dma2_step(const char* __restrict__ ra, const char* __restrict__ rb,
                                           char* __restrict__ wa, char* __restrict__ wb, int ka, int kb,
                                           const DA& da, const DB& db, Acc<C>& acc, int wm, int wn) {
@@ -799,7 +809,7 @@ __device__ __forceinline__ void dma2_step(const char* __restrict__ ra, const cha
         for (int ni = 0; ni < C::FN; ++ni)
           acc.a[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cb][mi], fb[cb][ni], acc.a[mi][ni], 0, 0, 0);
     }
-    dma2_schedule<KK, MK, FR, DA::J + DB::J, LOAD_STEPS>();
+    dma2_schedule<KK, MK, FR, DA::J + DB::J, LOAD_STEPS, EARLY>();
     // every MFMA of the step is issued before the end-of-step wait and
     // barrier (otherwise the scheduler sinks the last k step's MFMAs past
     // them and a wave waits at the barrier with its matrix work undone)
@@ -807,7 +817,7 @@ __device__ __forceinline__ void dma2_step(const char* __restrict__ ra, const cha
   }
 }
 
-template <class C, bool A_MN, bool B_MN, bool MMA, bool B_HALVES, class DA, class DB>
+template <class C, bool A_MN, bool B_MN, bool MMA, bool B_HALVES, bool EARLY, class DA, class DB>
 __device__ __forceinline__ void k_steps_dma2(char* lds, Acc<C>& acc, int nk, const DA& da, const DB& db, int wm,
                                              int wn, int k_last) {
   using L = Dma2Layout<C>;
@@ -827,7 +837,7 @@ __device__ __forceinline__ void k_steps_dma2(char* lds, Acc<C>& acc, int nk, con
       for (int i = threadIdx.x; i < (C::BK - k_last) * C::BN * 2 / 16; i += C::NT) zb[i] = u32x4_t{0u, 0u, 0u, 0u};
       __syncthreads();
     }
-    dma2_step<C, A_MN, B_MN, MMA, B_HALVES>(ra, rb, lds + L::A0 + ((kt + 1) & 1) * C::A_BYTES,
+    dma2_step<C, A_MN, B_MN, MMA, B_HALVES, EARLY>(ra, rb, lds + L::A0 + ((kt + 1) & 1) * C::A_BYTES,
                                      lds + L::B0 + ws * C::B_BYTES, ka, kb, da, db, acc, wm, wn);
     wait_vm<C::JB>();
     lds_barrier();
@@ -843,7 +853,8 @@ __device__ __forceinline__ void k_steps_dma2(char* lds, Acc<C>& acc, int nk, con
 // Each operand is K-contiguous (KcDma) or MN-contiguous (MnDma); with both
 // MN-contiguous (the weight gradients) the last K tile may hold only k_last
 // valid k rows.  B_HALVES: B is two MN sub-tiles (MnDma2), one per wave column.
-template <class C, bool A_MN, bool B_MN, class DA, class DB, bool B_HALVES = false>
+// EARLY: each step's requests are issued before its first fragment reads.
+template <class C, bool A_MN, bool B_MN, class DA, class DB, bool B_HALVES = false, bool EARLY = false>
 __device__ __forceinline__ void k_loop_dma2(char* lds, Acc<C>& acc, int nk, const DA& da, const DB& db, int wm,
                                             int wn, bool mma = true, int k_last = C::BK) {
   using L = Dma2Layout<C>;
@@ -856,9 +867,9 @@ __device__ __forceinline__ void k_loop_dma2(char* lds, Acc<C>& acc, int nk, cons
   wait_vm<C::JB>();
   lds_barrier();
   if (__builtin_amdgcn_readfirstlane(mma ? 1 : 0))
-    k_steps_dma2<C, A_MN, B_MN, true, B_HALVES>(lds, acc, nk, da, db, wm, wn, k_last);
+    k_steps_dma2<C, A_MN, B_MN, true, B_HALVES, EARLY>(lds, acc, nk, da, db, wm, wn, k_last);
   else
-    k_steps_dma2<C, A_MN, B_MN, false, B_HALVES>(lds, acc, nk, da, db, wm, wn, k_last);
+    k_steps_dma2<C, A_MN, B_MN, false, B_HALVES, EARLY>(lds, acc, nk, da, db, wm, wn, k_last);
   // the last steps' requests land in slots nobody reads, but before the
   // caller reuses the LDS
   wait_vm<0>();
