@@ -42,22 +42,22 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # hash is stored with them; once any source under csrc/ changes, the figure
 # is reported as null until the counters are taken again.
 TRAFFIC = {
-    "sources": "796c79e94c338240",
+    "sources": "3416889ba7e8276e",
     "bytes": {
-        ('bf16_fwd_n8192_h7168_f2048_e256_k8', 'down'): 12798532352,
-        ('bf16_fwd_n8192_h7168_f2048_e256_k8', 'gate_up'): 22412608875,
-        ('bf16_n16384_h4096_f14336_e8_k2', 'dact'): 10669213845,
-        ('bf16_n16384_h4096_f14336_e8_k2', 'down'): 7973930219,
-        ('bf16_n16384_h4096_f14336_e8_k2', 'dx_dw'): 43713290709,
-        ('bf16_n16384_h4096_f14336_e8_k2', 'gate_up'): 17328258304,
-        ('bf16_n16384_h512_f1024_e8_k2', 'dact'): 352507051,
-        ('bf16_n16384_h512_f1024_e8_k2', 'down'): 148070208,
-        ('bf16_n16384_h512_f1024_e8_k2', 'dx_dw'): 665424448,
-        ('bf16_n16384_h512_f1024_e8_k2', 'gate_up'): 338989312,
-        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'dact'): 2834678187,
-        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'down'): 1911226091,
-        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'dx_dw'): 9183885568,
-        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'gate_up'): 3793338325,
+        ('bf16_fwd_n8192_h7168_f2048_e256_k8', 'down'): 12791171584,
+        ('bf16_fwd_n8192_h7168_f2048_e256_k8', 'gate_up'): 22410343765,
+        ('bf16_n16384_h4096_f14336_e8_k2', 'dact'): 10616806741,
+        ('bf16_n16384_h4096_f14336_e8_k2', 'down'): 7964579563,
+        ('bf16_n16384_h4096_f14336_e8_k2', 'dx_dw'): 42883770901,
+        ('bf16_n16384_h4096_f14336_e8_k2', 'gate_up'): 17380177856,
+        ('bf16_n16384_h512_f1024_e8_k2', 'dact'): 352213269,
+        ('bf16_n16384_h512_f1024_e8_k2', 'down'): 148100416,
+        ('bf16_n16384_h512_f1024_e8_k2', 'dx_dw'): 668934891,
+        ('bf16_n16384_h512_f1024_e8_k2', 'gate_up'): 338635456,
+        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'dact'): 2819030315,
+        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'down'): 1923069099,
+        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'dx_dw'): 9121219861,
+        ('bf16_skewed_n16384_h2048_f1408_e64_k6', 'gate_up'): 3910642133,
     },
 }
 

@@ -23,8 +23,7 @@
 // (gate/up with its W_gate and W_up columns as two B sub-tiles, one per wave
 // column).  The register-staged loop (k_loop_reg: each thread's 16-byte
 // chunks of the next K tile requested into registers between the MFMAs and
-// stored into the other LDS stage) remains for the 128-row tiles and for the
-// weight gradients whose rows are gathered from x.
+// stored into the other LDS stage) remains for the 128-row tiles.
 //
 // A K-contiguous operand (token rows; weight rows in the backward) sits in
 // LDS as [rows][64 k] and is read with 16-byte fragment loads; an
@@ -599,7 +598,18 @@ __device__ __forceinline__ void dw_tile(char* lds, int b, const bf16_t* __restri
   const bf16_t* r_base = Rm + (int64_t)r0 * Q + nt * C::BN;
   Acc<C> acc;
   const int nk = (cnt + C::BK - 1) / C::BK;
-  if constexpr (GATHER) {
+  if constexpr (GATHER && C::REG && C::NW >= 8) {
+    // dW_gate / dW_up: the k rows of xs gathered from x by DMA (their token numbers loaded a step ahead)
+    if (prob < 2)
+      k_loop_dma2<C, true, true>(lds, acc, nk,
+                                 MnGatherDma<C::BM, C::BK, C::NW>(xs + mt * C::BM, sorted_flat + r0, K, P, prow, cnt),
+                                 MnDma<C::BN, C::BK, C::NW>(r_base, Q, qcol, cnt), wm, wn, true,
+                                 cnt - (nk - 1) * C::BK);
+    else
+      k_loop_dma2<C, true, true>(lds, acc, nk, MnDma<C::BM, C::BK, C::NW>(l_base, P, prow, cnt),
+                                 MnDma<C::BN, C::BK, C::NW>(r_base, Q, qcol, cnt), wm, wn, true,
+                                 cnt - (nk - 1) * C::BK);
+  } else if constexpr (GATHER) {
     static_assert(C::REG, "the gathered rows use the register-staged loop");
     if (prob < 2)
       k_loop_reg<C, true, true>(lds, acc, nk,

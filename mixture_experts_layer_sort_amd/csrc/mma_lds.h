@@ -725,6 +725,65 @@ struct MnDma2 {
   }
 };
 
+// MN-contiguous operand by DMA whose k rows are gathered: k row r of the
+// contraction (r from 0 over the expert's rows) is token row rows_src[r] / K
+// of x (leading dimension ld), as MnGather; x_cols points at the tile's first
+// column.  The token numbers of K tile kt + 1 are loaded while tile kt is
+// requested (one index load per request, landing a step before they are
+// needed).  k rows at or past k_total read the last valid row (k_loop_dma2
+// zeroes them).  Byte offsets are 32-bit unsigned (callers keep x under 4 GiB).
+template <int COLS, int BK, int NW>
+struct MnGatherDma {
+  static constexpr int CPR = COLS / 8, RPI = 1024 / (COLS * 2), J = BK / RPI / NW;
+  static_assert((BK / RPI) % NW == 0, "instructions split evenly over the waves");
+  static_assert(RPI == 2 && NW % 2 == 0, "a lane's k row has the same k & 3 in every request");
+  const bf16_t* base;
+  const int32_t* rows_src;
+  int K, k_total;
+  int64_t ld;
+  unsigned coff;   // this lane's column chunk, in bytes
+  int src[J];      // token rows of the next tile to request (loaded one step ahead)
+  int ks[J];       // this lane's k row within a tile, per request
+  __device__ __forceinline__ MnGatherDma(const bf16_t* x_cols, const int32_t* rows_src_, int K_, int64_t ld_,
+                                         int cols_valid, int k_total_)
+      : base(x_cols), rows_src(rows_src_), K(K_), k_total(k_total_), ld(ld_) {
+    const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int j = 0; j < J; ++j) ks[j] = (w + j * NW) * RPI + lane / CPR;
+    // the chunk's XOR swizzle depends on the k row only through k & 3, the same for every request of a lane
+    const int c = (lane % CPR) ^ fm(ks[0]);
+    const int cs = c * 8 < cols_valid ? c : (cols_valid >> 3) - 1;
+    coff = unsigned(cs) * 16u;
+    load_rows(0);
+  }
+  __device__ __forceinline__ void load_rows(int kt) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int r = kt * BK + ks[j];
+      src[j] = rows_src[r < k_total ? r : k_total - 1];
+    }
+  }
+  // requests tile kt (whose rows were loaded by the previous call or the
+  // constructor), then loads the rows of tile kt + 1
+  __device__ __forceinline__ void issue(int kt, char* slot) {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(base), (short)0, -1, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+      dma16_buf(r, int(unsigned((src[j] / K) * ld) * 2u + coff), slot + (w + j * NW) * 1024);
+    load_rows(kt + 1);
+  }
+};
+
+// Keeps every memory request before it ahead of every one after it (other
+// instructions may still move across): the end-of-step wait of k_loop_dma2
+// counts on operand A's requests being older than B's (vmcnt retires loads
+// in issue order).
+__device__ __forceinline__ void dma_order_fence() {
+  __builtin_amdgcn_sched_barrier(0x0001 | 0x0002 | 0x0004 | 0x0008 | 0x0080 | 0x0100 | 0x0200 | 0x0400);
+}
+
 template <class C>
 struct Dma2Layout {
   static constexpr int A0 = 0, B0 = 2 * C::A_BYTES;
@@ -768,9 +827,10 @@ __device__ __forceinline__ void dma2_schedule() {
 template <class C, bool A_MN, bool B_MN, bool MMA, bool B_HALVES, bool EARLY, class DA, class DB>
 __device__ __forceinline__ void dma2_step(const char* __restrict__ ra, const char* __restrict__ rb,
                                           char* __restrict__ wa, char* __restrict__ wb, int ka, int kb,
-                                          const DA& da, const DB& db, Acc<C>& acc, int wm, int wn) {
+                                          DA& da, DB& db, Acc<C>& acc, int wm, int wn) {
   if constexpr (!MMA) {
     da.issue(ka, wa);
+    dma_order_fence();
     db.issue(kb, wb);
   } else {
     constexpr int KK = C::BK / 16;
@@ -790,6 +850,7 @@ __device__ __forceinline__ void dma2_step(const char* __restrict__ ra, const cha
     for (int ni = 0; ni < C::FN; ++ni)
       fb[0][ni] = B_MN ? frag_mn<BC>(sb, nb + ni * 32, 0) : frag_kc<C::BK>(sb, nb + ni * 32, 0);
     da.issue(ka, wa);
+    dma_order_fence();
     db.issue(kb, wb);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
@@ -818,7 +879,7 @@ __device__ __forceinline__ void dma2_step(const char* __restrict__ ra, const cha
 }
 
 template <class C, bool A_MN, bool B_MN, bool MMA, bool B_HALVES, bool EARLY, class DA, class DB>
-__device__ __forceinline__ void k_steps_dma2(char* lds, Acc<C>& acc, int nk, const DA& da, const DB& db, int wm,
+__device__ __forceinline__ void k_steps_dma2(char* lds, Acc<C>& acc, int nk, DA& da, DB& db, int wm,
                                              int wn, int k_last) {
   using L = Dma2Layout<C>;
   int rs = 0;  // B slot of tile kt
@@ -855,7 +916,7 @@ __device__ __forceinline__ void k_steps_dma2(char* lds, Acc<C>& acc, int nk, con
 // valid k rows.  B_HALVES: B is two MN sub-tiles (MnDma2), one per wave column.
 // EARLY: each step's requests are issued before its first fragment reads.
 template <class C, bool A_MN, bool B_MN, class DA, class DB, bool B_HALVES = false, bool EARLY = false>
-__device__ __forceinline__ void k_loop_dma2(char* lds, Acc<C>& acc, int nk, const DA& da, const DB& db, int wm,
+__device__ __forceinline__ void k_loop_dma2(char* lds, Acc<C>& acc, int nk, DA da, DB db, int wm,
                                             int wn, bool mma = true, int k_last = C::BK) {
   using L = Dma2Layout<C>;
   static_assert(DA::J == C::JA && DB::J == C::JB, "one request per wave instruction");
