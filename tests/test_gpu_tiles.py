@@ -2,8 +2,8 @@
 
 The dispatcher picks the GEMM tile shape per stage from the problem size, so
 at small sizes only the 128-wide kernels run.  moe_dims.gemm_tiles forces one
-family for every stage (256: the register-staged 256 x 256 kernels, 4 waves
-for gate/up and 8 for the others; 128x256: the register-staged 128 x 256
+family for every stage (256: the 256 x 256 kernels, 8 waves on the
+mixed-depth LDS DMA loop; 128x256: the register-staged 128 x 256
 kernels; 128: the 128 x 128 kernels and the 128 x 256 LDS DMA dA tiles);
 each is run here on inputs
 with ragged row tiles, partial column tiles, empty experts, K = E and a single
